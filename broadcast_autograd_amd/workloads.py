@@ -1,0 +1,91 @@
+"""Seeded synthetic inputs for the five workloads of the broadcasting path.
+
+This module only draws numbers: it holds none of the operators' arithmetic,
+so both the HIP path and the CPU oracle can be fed from it.  Every array is
+drawn on the host in float32 with numpy's PCG64 (``default_rng(seed)``):
+
+  N(mu, sigma) = standard_normal(float32) * sigma + mu   (sigma = std. dev.)
+  U(lo, hi)    = random(float32) * (hi - lo) + lo
+
+The causal mask follows the GPT chapter of the "Zero" book (section
+"attention"): 0 on and below the diagonal, a large negative constant above it
+(j > i).  The workloads use -1e9 as that constant.
+"""
+import numpy as np
+
+# workload name -> description
+WORKLOADS = {
+    "xy_plus_x": "z = x*y + x, x[64,128,256], y[128,1]",
+    "mlp_bias_gelu": "y = GeLU(act[4096,1024] + bias[1024])",
+    "attn_scale_mask": "scores[8,16,1024,1024] * scale[1,16,1,1] + mask[1,1,1024,1024]",
+    "strided_highrank": "a[4096,4096] strides [1,4096] * b[4096]; a[2..9] / b[1,3,1,5,1,7,1,9]",
+    "gpt_residual": "h[16,2048,4096] * gamma[4096] + resid[16,2048,4096]",
+}
+
+
+def normal(shape, seed, mu=0.0, sigma=1.0):
+    rng = np.random.default_rng(seed)
+    n = int(np.prod(shape, dtype=np.int64))
+    x = rng.standard_normal(n, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    if mu != 0.0:
+        x += np.float32(mu)
+    return x.reshape(shape)
+
+
+def uniform(shape, seed, lo, hi):
+    rng = np.random.default_rng(seed)
+    n = int(np.prod(shape, dtype=np.int64))
+    x = rng.random(n, dtype=np.float32)
+    x *= np.float32(hi - lo)
+    x += np.float32(lo)
+    return x.reshape(shape)
+
+
+def causal_mask(t, neg=-1e9):
+    """[1,1,t,t]: 0 where j <= i, ``neg`` where j > i."""
+    m = np.zeros((t, t), dtype=np.float32)
+    m[np.triu_indices(t, k=1)] = np.float32(neg)
+    return m.reshape(1, 1, t, t)
+
+
+def xy_plus_x(scale=1):
+    """x[64,128,256], y[128,1], g[64,128,256]; ``scale`` < 1 shrinks the
+    leading dim for quick checks."""
+    d0 = max(1, int(64 * scale))
+    return dict(x=normal((d0, 128, 256), 1001), y=normal((128, 1), 1002),
+                g=normal((d0, 128, 256), 1003))
+
+
+def mlp_bias_gelu(rows=4096, cols=1024):
+    return dict(act=normal((rows, cols), 2001),
+                bias=normal((cols,), 2002, 0.0, 0.02),
+                g=normal((rows, cols), 2003))
+
+
+def attn_scale_mask(b=8, h=16, t=1024):
+    return dict(scores=normal((b, h, t, t), 3001),
+                scale=uniform((1, h, 1, 1), 3002, 0.5, 2.0),
+                mask=causal_mask(t),
+                g=normal((b, h, t, t), 3003))
+
+
+def strided_transposed(n=4096):
+    """Storage S[n*n] U(-1,1); a = S viewed [n,n] and transposed, i.e.
+    sizes [n,n], strides [1,n]; b[n] U(-1,1); g[n,n] N(0,1)."""
+    return dict(a_storage=uniform((n * n,), 4001, -1.0, 1.0),
+                a_sizes=(n, n), a_strides=(1, n),
+                b=uniform((n,), 4002, -1.0, 1.0),
+                g=normal((n, n), 4003))
+
+
+def rank8(shape_a=(2, 3, 4, 5, 6, 7, 8, 9), shape_b=(1, 3, 1, 5, 1, 7, 1, 9)):
+    return dict(a=uniform(shape_a, 4101, 0.5, 2.0),
+                b=uniform(shape_b, 4102, 0.5, 2.0),
+                g=normal(shape_a, 4103))
+
+
+def gpt_residual(b=16, t=2048, c=4096):
+    return dict(h=normal((b, t, c), 5001), gamma=normal((c,), 5002, 1.0, 0.1),
+                resid=normal((b, t, c), 5003), g=normal((b, t, c), 5004))

@@ -1,0 +1,385 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for broadcasting binary operators and
+ * their backward.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and
+ * the benchmark's CPU-baseline leg call it; the product library never does.
+ * It shares no code, header or constant with the HIP library.
+ *
+ * What it computes follows the "Zero" book (ismantic.github.io/zero):
+ *   - strides count elements, offset = sum_k i_k * s_k
+ *       (Tensor chapter, "shape and strides" section)
+ *   - broadcast shape: right-align, each dim equal / one is 1 / one missing
+ *       (Operator chapter, "broadcast" section)
+ *   - broadcast forward: a size-1 input dim always reads coordinate 0
+ *       (Operator chapter, "broadcast" section)
+ *   - element-wise rules z = x*y -> (g*y, g*x); add passes g to both inputs
+ *       (Autograd chapter, "chain rule"; GPU chapter, "OpAdd" walkthrough)
+ *   - a broadcast input's gradient is the sum of the upstream gradient over
+ *     every output position it was repeated into; a tensor reached along
+ *     several paths gets the sum of the path gradients
+ *       (Operator chapter, "broadcast"; Autograd chapter, "chain rule")
+ * sub and div rules are not printed there; they are plain calculus.
+ *
+ * Precision (the pages fix none):
+ *   forward  : one IEEE binary32 operation per element, round-to-nearest-even
+ *              (built with -ffp-contract=off, SSE, no fast-math)
+ *   GeLU     : exact function h*Phi(h), Phi(h) = erfc(-h/sqrt2)/2, evaluated in
+ *              binary64 with libm erfc and rounded once to binary32
+ *   backward : every term in binary64 from the exact binary32 inputs, summed in
+ *              binary64 in row-major index order, rounded once to binary32;
+ *              the sum of |terms| is returned beside it for the tolerance.
+ *
+ * Loops are plain odometers over multi-indices.  OpenMP splits only the loop
+ * over OUTPUT elements, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_MAX_DIMS 8
+
+enum { OR_ADD = 0, OR_SUB = 1, OR_MUL = 2, OR_DIV = 3 };
+enum { OR_EPI_NONE = 0, OR_EPI_GELU = 1 };
+enum {
+  OR_OK = 0,
+  OR_ERR_BROADCAST = 1, /* shapes do not broadcast                   */
+  OR_ERR_RANK = 2,      /* rank < 0 or > 8                           */
+  OR_ERR_SIZE = 3,      /* negative size or stride                   */
+  OR_ERR_ARG = 4        /* bad op / epilogue / target shape          */
+};
+
+typedef struct {
+  int32_t rank;
+  int64_t sizes[OR_MAX_DIMS];
+  int64_t strides[OR_MAX_DIMS];
+} or_desc;
+
+static int g_threads = 1;
+
+void or_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int or_get_threads(void) { return g_threads; }
+
+/* ---------------------------------------------------------------- shapes */
+
+/* Broadcast rule, compared from the last dim backwards.  A missing dim acts
+ * as size 1.  Size 0 follows the same rule: 0 with 1 gives 0, 0 with n>1 is
+ * incompatible. */
+int or_broadcast_shape(int ra, const int64_t *na, int rb, const int64_t *nb,
+                       int *ro, int64_t *no) {
+  if (ra < 0 || rb < 0 || ra > OR_MAX_DIMS || rb > OR_MAX_DIMS) return OR_ERR_RANK;
+  for (int k = 0; k < ra; ++k) if (na[k] < 0) return OR_ERR_SIZE;
+  for (int k = 0; k < rb; ++k) if (nb[k] < 0) return OR_ERR_SIZE;
+  int r = ra > rb ? ra : rb;
+  int64_t tmp[OR_MAX_DIMS];
+  for (int k = 0; k < r; ++k) {
+    /* position counted from the right */
+    int ka = ra - r + k, kb = rb - r + k;
+    int64_t x = ka >= 0 ? na[ka] : 1;
+    int64_t y = kb >= 0 ? nb[kb] : 1;
+    if (x == y) tmp[k] = x;
+    else if (x == 1) tmp[k] = y;
+    else if (y == 1) tmp[k] = x;
+    else return OR_ERR_BROADCAST;
+  }
+  *ro = r;
+  for (int k = 0; k < r; ++k) no[k] = tmp[k];
+  return OR_OK;
+}
+
+static int64_t numel(int r, const int64_t *n) {
+  int64_t m = 1;
+  for (int k = 0; k < r; ++k) m *= n[k];
+  return m;
+}
+
+static int check_desc(const or_desc *d) {
+  if (d->rank < 0 || d->rank > OR_MAX_DIMS) return OR_ERR_RANK;
+  for (int k = 0; k < d->rank; ++k)
+    if (d->sizes[k] < 0 || d->strides[k] < 0) return OR_ERR_SIZE;
+  return OR_OK;
+}
+
+/* Offset of an operand element addressed by the OUTPUT multi-index idx
+ * (rank r).  The operand is right-aligned; a size-1 operand dim reads
+ * coordinate 0, which is what repeating it along that dim means. */
+static int64_t operand_offset(const or_desc *d, int r, const int64_t *idx) {
+  int64_t off = 0;
+  for (int k = 0; k < d->rank; ++k) {
+    int ko = r - d->rank + k;
+    int64_t i = d->sizes[k] == 1 ? 0 : idx[ko];
+    off += i * d->strides[k];
+  }
+  return off;
+}
+
+/* Row-major multi-index of flat position f in shape n (rank r). */
+static void unflatten(int64_t f, int r, const int64_t *n, int64_t *idx) {
+  for (int k = r - 1; k >= 0; --k) {
+    int64_t m = n[k];
+    idx[k] = m ? f % m : 0;
+    f = m ? f / m : 0;
+  }
+}
+
+/* ---------------------------------------------------------------- forward */
+
+static float op32(int op, float x, float y) {
+  switch (op) {
+  case OR_ADD: return x + y;
+  case OR_SUB: return x - y;
+  case OR_MUL: return x * y;
+  default:     return x / y;
+  }
+}
+
+/* Standard normal CDF and density, binary64. */
+double or_phi_cdf(double h) { return 0.5 * erfc(-h * M_SQRT1_2); }
+double or_phi_pdf(double h) { return exp(-0.5 * h * h) / sqrt(2.0 * M_PI); }
+
+/* GeLU(h) = h * Phi(h), evaluated in binary64, rounded once to binary32.
+ * The limits at +-inf are +inf and -0. */
+float or_gelu32(float h) {
+  if (isinf(h)) return h > 0 ? h : -0.0f;
+  double hd = (double)h;
+  return (float)(hd * or_phi_cdf(hd));
+}
+
+static float fwd_at(int op, int epi, const float *a, const or_desc *da,
+                    const float *b, const or_desc *db, int r,
+                    const int64_t *idx) {
+  float x = a[operand_offset(da, r, idx)];
+  float y = b[operand_offset(db, r, idx)];
+  float h = op32(op, x, y);
+  return epi == OR_EPI_GELU ? or_gelu32(h) : h;
+}
+
+int or_fwd(int op, int epi, const float *a, const or_desc *da, const float *b,
+           const or_desc *db, float *out) {
+  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_GELU) return OR_ERR_ARG;
+  int s;
+  if ((s = check_desc(da)) || (s = check_desc(db))) return s;
+  int r;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = or_broadcast_shape(da->rank, da->sizes, db->rank, db->sizes, &r, n)))
+    return s;
+  int64_t total = numel(r, n);
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t f = 0; f < total; ++f) {
+    int64_t idx[OR_MAX_DIMS];
+    unflatten(f, r, n, idx);
+    out[f] = fwd_at(op, epi, a, da, b, db, r, idx);
+  }
+  return OR_OK;
+}
+
+/* Forward at the listed flat output positions only (for spot checks of very
+ * large outputs). */
+int or_fwd_at(int op, int epi, const float *a, const or_desc *da,
+              const float *b, const or_desc *db, int64_t count,
+              const int64_t *pos, float *out) {
+  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_GELU) return OR_ERR_ARG;
+  int s;
+  if ((s = check_desc(da)) || (s = check_desc(db))) return s;
+  int r;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = or_broadcast_shape(da->rank, da->sizes, db->rank, db->sizes, &r, n)))
+    return s;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t t = 0; t < count; ++t) {
+    int64_t idx[OR_MAX_DIMS];
+    unflatten(pos[t], r, n, idx);
+    out[t] = fwd_at(op, epi, a, da, b, db, r, idx);
+  }
+  return OR_OK;
+}
+
+/* --------------------------------------------------------------- backward */
+
+/* Local gradient terms at one output position, binary64.
+ * which = 0 -> d/da, 1 -> d/db.  Up to two pieces are returned (the GeLU
+ * derivative Phi(h) + h*phi(h) is kept as two pieces so that the tolerance
+ * base sum|pieces| does not collapse where GeLU' crosses zero). */
+static int local_terms(int op, int epi, int which, double g, double x,
+                       double y, float h32, double *piece) {
+  int np = 1;
+  double gg[2];
+  gg[0] = g;
+  if (epi == OR_EPI_GELU) {
+    double h = (double)h32;
+    gg[0] = g * or_phi_cdf(h);
+    gg[1] = g * h * or_phi_pdf(h);
+    np = 2;
+  }
+  for (int p = 0; p < np; ++p) {
+    double u = gg[p], t;
+    switch (op) {
+    case OR_ADD: t = u; break;
+    case OR_SUB: t = which ? -u : u; break;
+    case OR_MUL: t = which ? u * x : u * y; break;
+    default:     t = which ? -u * x / (y * y) : u / y; break;
+    }
+    piece[p] = t;
+  }
+  return np;
+}
+
+/* Gradient of one operand at its dense row-major position j:
+ *   sum over every output index i that reads element j (row-major order of i)
+ * of the local terms, plus acc[j] when given.  Returns the binary64 sum and
+ * the sum of absolute pieces through *absum. */
+static double grad_at(int op, int epi, int which, const float *g,
+                      const float *a, const or_desc *da, const float *b,
+                      const or_desc *db, const float *acc, int r,
+                      const int64_t *n, int64_t j, double *absum) {
+  const or_desc *dx = which ? db : da;
+  int64_t xidx[OR_MAX_DIMS];
+  unflatten(j, dx->rank, dx->sizes, xidx);
+  /* Fixed output coordinates come from x; the others are free. */
+  int64_t lo[OR_MAX_DIMS], cnt[OR_MAX_DIMS];
+  for (int k = 0; k < r; ++k) {
+    int kx = k - (r - dx->rank);
+    if (kx >= 0 && dx->sizes[kx] != 1) {
+      lo[k] = xidx[kx];
+      cnt[k] = 1;
+    } else {
+      lo[k] = 0;
+      cnt[k] = n[k];
+    }
+  }
+  double sum = 0.0, as = 0.0;
+  if (acc) {
+    sum = (double)acc[j];
+    as = fabs(sum);
+  }
+  int64_t total = numel(r, cnt);
+  int64_t idx[OR_MAX_DIMS], sub[OR_MAX_DIMS];
+  int64_t gstr[OR_MAX_DIMS];
+  {
+    int64_t s = 1;
+    for (int k = r - 1; k >= 0; --k) { gstr[k] = s; s *= n[k]; }
+  }
+  for (int64_t t = 0; t < total; ++t) {
+    unflatten(t, r, cnt, sub);
+    int64_t goff = 0;
+    for (int k = 0; k < r; ++k) {
+      idx[k] = lo[k] + sub[k];
+      goff += idx[k] * gstr[k];
+    }
+    float xv = a[operand_offset(da, r, idx)];
+    float yv = b[operand_offset(db, r, idx)];
+    float h32 = epi == OR_EPI_GELU ? op32(op, xv, yv) : 0.0f;
+    double piece[2];
+    int np = local_terms(op, epi, which, (double)g[goff], (double)xv,
+                         (double)yv, h32, piece);
+    for (int p = 0; p < np; ++p) {
+      sum += piece[p];
+      as += fabs(piece[p]);
+    }
+  }
+  *absum = as;
+  return sum;
+}
+
+static int bwd_common(int op, int epi, const or_desc *da, const or_desc *db,
+                      int *r, int64_t *n) {
+  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_GELU) return OR_ERR_ARG;
+  int s;
+  if ((s = check_desc(da)) || (s = check_desc(db))) return s;
+  return or_broadcast_shape(da->rank, da->sizes, db->rank, db->sizes, r, n);
+}
+
+/* Full backward.  g is dense row-major in the broadcast shape; grad_a/grad_b
+ * are dense row-major in a's / b's shape (NULL = not wanted); *_64 receive
+ * the unrounded binary64 sums and abs_* the sums of |terms| (may be NULL). */
+int or_bwd(int op, int epi, const float *g, const float *a, const or_desc *da,
+           const float *b, const or_desc *db, const float *acc_a,
+           const float *acc_b, float *grad_a, double *grad_a64, double *abs_a,
+           float *grad_b, double *grad_b64, double *abs_b) {
+  int r, s;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = bwd_common(op, epi, da, db, &r, n))) return s;
+  for (int which = 0; which < 2; ++which) {
+    float *gx = which ? grad_b : grad_a;
+    double *gx64 = which ? grad_b64 : grad_a64;
+    double *ax = which ? abs_b : abs_a;
+    const float *acc = which ? acc_b : acc_a;
+    const or_desc *dx = which ? db : da;
+    if (!gx && !gx64) continue;
+    int64_t m = numel(dx->rank, dx->sizes);
+#pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads)
+    for (int64_t j = 0; j < m; ++j) {
+      double as;
+      double v = grad_at(op, epi, which, g, a, da, b, db, acc, r, n, j, &as);
+      if (gx) gx[j] = (float)v;
+      if (gx64) gx64[j] = v;
+      if (ax) ax[j] = as;
+    }
+  }
+  return OR_OK;
+}
+
+/* Backward of one operand (which: 0 = a, 1 = b) at listed dense positions. */
+int or_bwd_at(int op, int epi, int which, const float *g, const float *a,
+              const or_desc *da, const float *b, const or_desc *db,
+              const float *acc, int64_t count, const int64_t *pos, float *out,
+              double *out64, double *absout) {
+  int r, s;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = bwd_common(op, epi, da, db, &r, n))) return s;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(g_threads)
+  for (int64_t t = 0; t < count; ++t) {
+    double as;
+    double v = grad_at(op, epi, which, g, a, da, b, db, acc, r, n, pos[t], &as);
+    if (out) out[t] = (float)v;
+    if (out64) out64[t] = v;
+    if (absout) absout[t] = as;
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------- reduce to shape */
+
+/* out (dense, shape nout) = sum of `in` over every dim where the target is
+ * 1 or missing; the target must broadcast to in's shape.  This is the
+ * "sum back to the input shape" step of a broadcast backward. */
+int or_reduce(const float *in, const or_desc *din, int rout,
+              const int64_t *nout, float *out, double *out64, double *absout) {
+  int s;
+  if ((s = check_desc(din))) return s;
+  if (rout < 0 || rout > OR_MAX_DIMS) return OR_ERR_RANK;
+  for (int k = 0; k < rout; ++k) if (nout[k] < 0) return OR_ERR_SIZE;
+  int r;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = or_broadcast_shape(din->rank, din->sizes, rout, nout, &r, n))) return s;
+  if (r != din->rank) return OR_ERR_ARG;
+  for (int k = 0; k < r; ++k) if (n[k] != din->sizes[k]) return OR_ERR_ARG;
+  int64_t m = numel(rout, nout);
+#pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads)
+  for (int64_t j = 0; j < m; ++j) {
+    int64_t oidx[OR_MAX_DIMS], lo[OR_MAX_DIMS], cnt[OR_MAX_DIMS];
+    int64_t sub[OR_MAX_DIMS];
+    unflatten(j, rout, nout, oidx);
+    for (int k = 0; k < r; ++k) {
+      int ko = k - (r - rout);
+      if (ko >= 0 && nout[ko] != 1) { lo[k] = oidx[ko]; cnt[k] = 1; }
+      else { lo[k] = 0; cnt[k] = n[k]; }
+    }
+    double sum = 0.0, as = 0.0;
+    int64_t total = numel(r, cnt);
+    for (int64_t t = 0; t < total; ++t) {
+      unflatten(t, r, cnt, sub);
+      int64_t off = 0;
+      for (int k = 0; k < r; ++k) off += (lo[k] + sub[k]) * din->strides[k];
+      double v = (double)in[off];
+      sum += v;
+      as += fabs(v);
+    }
+    if (out) out[j] = (float)sum;
+    if (out64) out64[j] = sum;
+    if (absout) absout[j] = as;
+  }
+  return OR_OK;
+}

@@ -1,0 +1,413 @@
+"""Pins for the CPU oracle: facts fixed by the "Zero" book's worked examples,
+by calculus and by IEEE-754, checked independently of the oracle's own code.
+
+Each test names what it pins; together they are chosen so that a dropped term,
+a wrong sign, a wrong index or a transposed operand in the oracle fails one.
+"""
+import ast
+import itertools
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import GOLDEN
+
+F32 = np.float32
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def _kv(lines):
+    out = {}
+    for ln in lines:
+        k, v = ln.split("=")
+        out[k.strip()] = float(v)
+    return out
+
+
+def _scalar(v):
+    return np.array(v, dtype=np.float32)
+
+
+# --------------------------------------------------------------- P1 -------
+def test_chain_rule_worked_example(orc):
+    """Autograd chapter, "computation graph": z = x*y + x at x=3, y=2."""
+    v = _kv(_golden("chain_rule_example.txt"))
+    x, y = _scalar(v["x"]), _scalar(v["y"])
+    t = orc.fwd("mul", x, y)
+    z = orc.fwd("add", t, x)
+    assert float(t) == v["xy"] and float(z) == v["z"]
+    # backward, root gradient 1: Add passes it to both inputs ...
+    g = _scalar(v["dz_dz"])
+    g_t, g_x_add = orc.bwd("add", g, t, x)
+    # ... Mul's rule then gives x the second path, accumulated on the first.
+    g_x, g_y = orc.bwd("mul", g_t.f32, x, y, acc_a=g_x_add.f32)
+    assert float(g_x.f32) == v["dz_dx"]
+    assert float(g_y.f32) == v["dz_dy"]
+    # dropping the accumulated path gives y = 2, not 3
+    g_x_only, _ = orc.bwd("mul", g_t.f32, x, y)
+    assert float(g_x_only.f32) == 2.0
+
+
+# ----------------------------------------------------------- P2, P3, P4 ---
+def test_broadcast_worked_examples(orc):
+    """Operator chapter, "broadcast": shape rule, [3]->[2,3] and its sum."""
+    for ln in _golden("broadcast_examples.txt"):
+        if ln.startswith("shape"):
+            m = re.match(r"shape (\[.*\]) & (\[.*\]) -> (.*)", ln)
+            sa, sb = ast.literal_eval(m.group(1)), ast.literal_eval(m.group(2))
+            res = m.group(3).strip()
+            if res == "incompatible":
+                with pytest.raises(orc.OracleError) as e:
+                    orc.broadcast_shape(sa, sb)
+                assert e.value.code == orc.ERR_BROADCAST
+                with pytest.raises(orc.OracleError):
+                    orc.broadcast_shape(sb, sa)
+            else:
+                assert orc.broadcast_shape(sa, sb) == tuple(ast.literal_eval(res))
+                assert orc.broadcast_shape(sb, sa) == tuple(ast.literal_eval(res))
+        elif ln.startswith("expand"):
+            m = re.match(r"expand (\[.*\]) : (\[.*\]) -> (\[.*\]) = (.*)", ln)
+            vec = np.array(ast.literal_eval(m.group(1)), dtype=np.float32)
+            tgt = ast.literal_eval(m.group(3))
+            want = np.array(ast.literal_eval(m.group(4)), dtype=np.float32)
+            got = orc.fwd("add", np.zeros(tgt, np.float32), vec)
+            assert got.shape == tuple(tgt)
+            np.testing.assert_array_equal(got, want)
+        elif ln.startswith("reduce"):
+            m = re.match(r"reduce ones(\[.*\]) -> (\[.*\]) = (.*)", ln)
+            big = ast.literal_eval(m.group(1))
+            small = ast.literal_eval(m.group(2))
+            want = np.array(ast.literal_eval(m.group(3)), dtype=np.float32)
+            g = np.ones(big, np.float32)
+            _, gb = orc.bwd("add", g, np.zeros(big, np.float32),
+                            np.zeros(small, np.float32))
+            np.testing.assert_array_equal(gb.f32, want)
+            np.testing.assert_array_equal(orc.reduce_to_shape(g, small).f32, want)
+
+
+def test_broadcast_shape_edges(orc):
+    """Right alignment, missing dims, size 0 and the rank limit of 8."""
+    assert orc.broadcast_shape((), ()) == ()
+    assert orc.broadcast_shape((), (2, 3)) == (2, 3)
+    assert orc.broadcast_shape((3, 1), (1, 4)) == (3, 4)
+    assert orc.broadcast_shape((5, 1, 4), (3, 1)) == (5, 3, 4)
+    assert orc.broadcast_shape((0,), (1,)) == (0,)
+    assert orc.broadcast_shape((2, 0), (2, 1)) == (2, 0)
+    with pytest.raises(orc.OracleError):
+        orc.broadcast_shape((0,), (2,))
+    with pytest.raises(orc.OracleError):
+        orc.broadcast_shape((3,), (4,))
+    with pytest.raises(orc.OracleError) as e:
+        orc.broadcast_shape((1,) * 9, (1,))
+    assert e.value.code == orc.ERR_RANK
+    with pytest.raises(orc.OracleError) as e:
+        orc.broadcast_shape((-1,), (1,))
+    assert e.value.code == orc.ERR_SIZE
+
+
+# ------------------------------------------------------------------ P5 ----
+def test_strided_reads_worked_examples(orc):
+    """Tensor chapter, "shape and strides" / "zero-copy view"."""
+    lines = _golden("strides_examples.txt")
+    storage = np.array(ast.literal_eval(lines[0].split("=")[1]), np.float32)
+    for ln in lines[1:]:
+        if ln.startswith("view"):
+            m = re.match(r"view sizes=(\[.*\]) strides=(\[.*\]) at=(\(.*\)) "
+                         r"offset=(\d+) value=(\S+)", ln)
+            sizes = ast.literal_eval(m.group(1))
+            strides = ast.literal_eval(m.group(2))
+            at = ast.literal_eval(m.group(3))
+            assert sum(i * s for i, s in zip(at, strides)) == int(m.group(4))
+            v = orc.View(storage, sizes, strides)
+            out = orc.fwd("add", v, np.zeros(sizes, np.float32))
+            assert out[at] == float(m.group(5))
+            # the whole view agrees with an independent strided read
+            ref = np.lib.stride_tricks.as_strided(
+                storage, shape=sizes, strides=[4 * s for s in strides])
+            np.testing.assert_array_equal(out, ref)
+        elif ln.startswith("init_strides"):
+            m = re.match(r"init_strides (\[.*\]) = (\[.*\])", ln)
+            shape = ast.literal_eval(m.group(1))
+            want = ast.literal_eval(m.group(2))
+            arr = np.arange(np.prod(shape), dtype=np.float32)
+            # explicit row-major strides read the storage in flat order
+            out = orc.fwd("add", orc.View(arr, shape, want),
+                          np.zeros(shape, np.float32))
+            np.testing.assert_array_equal(out.reshape(-1), arr)
+            assert [s // 4 for s in arr.reshape(shape).strides] == want
+
+
+def test_transposed_operand_is_not_swapped(orc):
+    """A transposed view of a non-square matrix must read (i,j) at i*1+j*R."""
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal(6, dtype=np.float32)  # 2x3 storage
+    t = orc.View(s, (3, 2), (1, 3))
+    b = rng.standard_normal((2,), dtype=np.float32)
+    out = orc.fwd("sub", t, b)
+    want = s.reshape(2, 3).T - b
+    np.testing.assert_array_equal(out, want)
+
+
+# ------------------------------------------------------------------ P6 ----
+def test_ieee_identities(orc):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((4, 5), dtype=np.float32) * np.float32(1e3)
+    x[0, 0] = np.float32(1e-40)  # subnormal survives
+    np.testing.assert_array_equal(orc.fwd("add", x, np.zeros(1, np.float32)), x)
+    np.testing.assert_array_equal(orc.fwd("mul", x, np.ones(1, np.float32)), x)
+    np.testing.assert_array_equal(orc.fwd("div", x, np.ones((4, 1), np.float32)), x)
+    np.testing.assert_array_equal(orc.fwd("mul", x, np.full(5, 8.0, np.float32)),
+                                  x * np.float32(8))
+    np.testing.assert_array_equal(orc.fwd("div", x, np.full(5, 0.25, np.float32)),
+                                  x * np.float32(4))
+    d = orc.fwd("sub", x, x)
+    assert np.all(d == 0) and not np.any(np.signbit(d))
+    # reduce to the same shape is a bitwise copy; a size-1 dim likewise
+    np.testing.assert_array_equal(orc.reduce_to_shape(x, x.shape).f32, x)
+    x1 = x.reshape(4, 1, 5)
+    np.testing.assert_array_equal(orc.reduce_to_shape(x1, (4, 1, 5)).f32, x1)
+    np.testing.assert_array_equal(
+        orc.reduce_to_shape(x.reshape(1, 4, 5), (4, 5)).f32, x)
+
+
+def test_division_is_correctly_rounded(orc):
+    one = np.ones(1, np.float32)
+    three = np.full(1, 3.0, np.float32)
+    q = orc.fwd("div", one, three)
+    assert q.view(np.uint32)[0] == 0x3EAAAAAB  # RN(1/3)
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal(4096, dtype=np.float32)
+    b = rng.standard_normal(4096, dtype=np.float32)
+    a[:8] = [1e-38, 3e-39, 1.0, 3.4e38, 7.0, -0.0, 1e-45, 2.0]
+    b[:8] = [10.0, 3.0, 1e-39, 0.5, 2.0 ** -120, 5.0, 2.0, 3.0]
+    got = orc.fwd("div", a, b)
+    # exact quotient of two binary32 values, rounded once: float64 division
+    # of binary32 inputs followed by RN to binary32 is correctly rounded
+    # (53 >= 2*24+2), so it is an independent reference.
+    with np.errstate(over="ignore"):
+        want = (a.astype(np.float64) / b.astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------ P7, P8 ------
+def test_mass_invariant(orc):
+    rng = np.random.default_rng(3)
+    g = rng.standard_normal((7, 5, 6), dtype=np.float32)
+    x = rng.standard_normal((7, 5, 6), dtype=np.float32)
+    for tgt in [(5, 1), (1, 6), (7, 1, 1), (), (5, 6), (7, 5, 1)]:
+        r = orc.reduce_to_shape(g, tgt)
+        exact = math.fsum(g.astype(np.float64).ravel())
+        assert abs(math.fsum(r.f64.ravel()) - exact) <= 2e-6 * np.abs(g).sum()
+    # for mul, the small gradient carries sum(g * x)
+    y = rng.standard_normal((5, 1), dtype=np.float32)
+    _, gy = orc.bwd("mul", g, x, y)
+    exact = math.fsum((g.astype(np.float64) * x.astype(np.float64)).ravel())
+    assert abs(float(gy.f64.sum()) - exact) <= 2e-6 * float(gy.abs.sum())
+
+
+def test_reduce_special_cases(orc):
+    rng = np.random.default_rng(4)
+    G = rng.standard_normal((33, 17), dtype=np.float32)
+    G64 = G.astype(np.float64)
+    # to [] : the total, i.e. RN32 of the exact sum (within rounding of the
+    # binary64 accumulation)
+    tot = orc.reduce_to_shape(G, ())
+    exact = math.fsum(G64.ravel())
+    assert abs(tot.f64 - exact) <= 1e-13 * np.abs(G64).sum()
+    # [R,K] -> [K] : column sums, ones^T G
+    col = orc.reduce_to_shape(G, (17,))
+    np.testing.assert_allclose(col.f64, np.ones(33) @ G64, rtol=0, atol=1e-12)
+    # [K,R] -> [K,1] : row sums
+    row = orc.reduce_to_shape(G, (33, 1))
+    np.testing.assert_allclose(row.f64, G64 @ np.ones((17, 1)), rtol=0, atol=1e-12)
+    # summing a reduced axis of a broadcast is the multiplicity
+    ones = np.ones((4, 3), np.float32)
+    np.testing.assert_array_equal(orc.reduce_to_shape(ones, (3,)).f32, [4, 4, 4])
+    # strided input: a transposed view reduced to its columns
+    s = rng.standard_normal(12, dtype=np.float32)
+    v = orc.View(s, (4, 3), (1, 4))
+    want = s.reshape(3, 4).astype(np.float64).sum(axis=1)
+    np.testing.assert_allclose(orc.reduce_to_shape(v, (3,)).f64, want, atol=1e-12)
+    # empty reduction gives zeros
+    e = orc.reduce_to_shape(np.zeros((0, 3), np.float32), (3,))
+    np.testing.assert_array_equal(e.f32, [0, 0, 0])
+
+
+# ------------------------------------------------------------------ P9 ----
+def _f64(op, a, b):
+    return {"add": a + b, "sub": a - b, "mul": a * b, "div": a / b}[op]
+
+
+def _gelu64(h):
+    return h * 0.5 * np.vectorize(math.erfc)(-h / math.sqrt(2.0))
+
+
+@pytest.mark.parametrize("op", ["add", "sub", "mul", "div"])
+@pytest.mark.parametrize("gelu", [False, True])
+@pytest.mark.parametrize("shapes", [((2, 3), (3,)), ((3, 1), (1, 4)),
+                                    ((2, 1, 3), (2, 3))])
+def test_backward_rules_finite_differences(orc, op, gelu, shapes):
+    """Central differences of L = sum(g * f(a, b)) in binary64."""
+    sa, sb = shapes
+    rng = np.random.default_rng(hash((op, gelu, shapes)) % 2**32)
+    a = rng.uniform(0.5, 2.0, sa).astype(np.float32)
+    b = rng.uniform(0.5, 2.0, sb).astype(np.float32)
+    if op in ("add", "sub", "mul"):
+        a *= np.where(rng.random(sa) < 0.5, -1, 1).astype(np.float32)
+    out_shape = np.broadcast_shapes(sa, sb)
+    g = rng.standard_normal(out_shape).astype(np.float32)
+    epi = orc.EPI_GELU if gelu else orc.EPI_NONE
+    ga, gb = orc.bwd(op, g, a, b, epi=epi)
+
+    def L(a64, b64):
+        f = _f64(op, a64, b64)
+        if gelu:
+            f = _gelu64(f)
+        return math.fsum((g.astype(np.float64) * f).ravel())
+
+    for which, x, gx in ((0, a, ga), (1, b, gb)):
+        x64 = x.astype(np.float64)
+        for j in np.ndindex(x.shape):
+            h = 1e-4 * max(1.0, abs(x64[j]))
+            xp, xm = x64.copy(), x64.copy()
+            xp[j] += h
+            xm[j] -= h
+            if which == 0:
+                fd = (L(xp, b.astype(np.float64)) - L(xm, b.astype(np.float64))) / (2 * h)
+            else:
+                fd = (L(a.astype(np.float64), xp) - L(a.astype(np.float64), xm)) / (2 * h)
+            # bilinear rules are exact up to rounding; div and GeLU are O(h^2)
+            tol = 1e-6 * max(1.0, gx.abs[j]) if (op != "div" and not gelu) \
+                else 2e-5 * max(1.0, gx.abs[j])
+            assert abs(fd - gx.f64[j]) <= tol, (op, gelu, which, j, fd, gx.f64[j])
+
+
+def test_backward_sign_and_operand_roles(orc):
+    """Asymmetric ops must not swap roles: d(a-b)/db = -1, d(a/b)/da = 1/b."""
+    a = np.array([6.0], np.float32)
+    b = np.array([2.0], np.float32)
+    g = np.array([1.0], np.float32)
+    ga, gb = orc.bwd("sub", g, a, b)
+    assert ga.f64[0] == 1.0 and gb.f64[0] == -1.0
+    ga, gb = orc.bwd("div", g, a, b)
+    assert ga.f64[0] == 0.5 and gb.f64[0] == -1.5
+    ga, gb = orc.bwd("mul", g, a, b)
+    assert ga.f64[0] == 2.0 and gb.f64[0] == 6.0
+
+
+# ---------------------------------------------------- P10 (oracle side) ---
+def _all_shapes(max_rank=3, sizes=(1, 2, 3)):
+    for r in range(max_rank + 1):
+        for s in itertools.product(sizes, repeat=r):
+            yield s
+
+
+def test_forward_bruteforce_against_numpy(orc):
+    """Every shape pair of rank <= 3, sizes in {1,2,3}: numpy's float32
+    broadcasting ops (one IEEE op per element) agree bit for bit."""
+    rng = np.random.default_rng(9)
+    shapes = list(_all_shapes())
+    n = 0
+    for sa in shapes:
+        for sb in shapes:
+            try:
+                out_shape = np.broadcast_shapes(sa, sb)
+            except ValueError:
+                with pytest.raises(orc.OracleError):
+                    orc.broadcast_shape(sa, sb)
+                continue
+            a = rng.uniform(0.5, 2, sa).astype(np.float32)
+            b = rng.uniform(0.5, 2, sb).astype(np.float32)
+            for op, f in (("add", np.add), ("sub", np.subtract),
+                          ("mul", np.multiply), ("div", np.divide)):
+                got = orc.fwd(op, a, b)
+                want = f(a, b)
+                assert got.shape == out_shape
+                np.testing.assert_array_equal(got.view(np.uint32),
+                                              np.asarray(want).view(np.uint32))
+            n += 1
+    assert n > 300
+
+
+def test_reduce_bruteforce_against_numpy(orc):
+    rng = np.random.default_rng(10)
+    for sb in _all_shapes():
+        for st in _all_shapes():
+            try:
+                if np.broadcast_shapes(sb, st) != sb:
+                    continue
+            except ValueError:
+                continue
+            x = rng.standard_normal(sb).astype(np.float32)
+            # numpy: sum the leading extra dims, then the size-1 target dims
+            lead = len(sb) - len(st)
+            ref = x.astype(np.float64).sum(axis=tuple(range(lead)))
+            axes = tuple(k for k, n in enumerate(st) if n == 1 and ref.shape[k] != 1)
+            ref = ref.sum(axis=axes, keepdims=True).reshape(st)
+            got = orc.reduce_to_shape(x, st)
+            np.testing.assert_allclose(got.f64, ref, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- P12 ----
+def test_gelu_pins(orc):
+    # closed forms and textbook values of the standard normal CDF
+    assert orc.gelu32(0.0) == 0.0
+    assert abs(orc.phi_pdf(0.0) - 1 / math.sqrt(2 * math.pi)) < 1e-17
+    table = {1.0: 0.8413447460685429, -1.0: 0.15865525393145707,
+             1.959963984540054: 0.975, -3.0: 0.0013498980316300946,
+             0.5: 0.6914624612740131}
+    for h, p in table.items():
+        assert abs(orc.phi_cdf(h) - p) <= 1e-15 * max(1, p / 1e-3), h
+    # symmetry Phi(h) + Phi(-h) = 1, hence GeLU(h) - GeLU(-h) = h
+    for h in np.linspace(-8, 8, 161):
+        assert abs(orc.phi_cdf(h) + orc.phi_cdf(-h) - 1) < 1e-15
+    # Phi against Simpson integration of the density from -12
+    for h in (-6.0, -2.5, -0.7518, 0.0, 0.3, 1.7, 4.0):
+        xs = np.linspace(-12.0, h, 20001)
+        ys = np.exp(-0.5 * xs * xs) / math.sqrt(2 * math.pi)
+        w = np.ones_like(xs)
+        w[1:-1:2], w[2:-1:2] = 4, 2
+        simp = (xs[1] - xs[0]) / 3 * np.dot(w, ys)
+        assert abs(orc.phi_cdf(h) - simp) <= 1e-11 * max(simp, 1e-9), h
+    # gelu32 is the correctly rounded value of h*Phi(h) away from ties
+    rng = np.random.default_rng(12)
+    for h in rng.uniform(-10, 10, 2000).astype(np.float32):
+        v = float(h) * orc.phi_cdf(float(h))
+        got = float(orc.gelu32(h))
+        up = np.nextafter(np.float32(got), np.float32(np.inf))
+        dn = np.nextafter(np.float32(got), np.float32(-np.inf))
+        assert abs(v - got) <= 0.5 * (float(up) - float(dn)) / 2 + 1e-45
+    # limits
+    assert orc.gelu32(np.inf) == np.inf
+    z = orc.gelu32(-np.inf)
+    assert z == 0 and np.signbit(z)
+    assert np.isnan(orc.gelu32(np.nan))
+    # derivative pieces: Phi(h) + h*phi(h) equals the slope of h*Phi(h)
+    for h in (-3.0, -0.7518, 0.0, 0.4, 2.2):
+        d = 1e-5
+        fd = ((h + d) * orc.phi_cdf(h + d) - (h - d) * orc.phi_cdf(h - d)) / (2 * d)
+        assert abs(fd - (orc.phi_cdf(h) + h * orc.phi_pdf(h))) < 1e-9
+
+
+def test_sampled_paths_agree_with_full(orc):
+    """The point-wise entry points compute the same values as the full ones."""
+    rng = np.random.default_rng(13)
+    a = rng.standard_normal((6, 5, 4), dtype=np.float32)
+    b = rng.uniform(0.5, 2, (5, 1)).astype(np.float32)
+    g = rng.standard_normal((6, 5, 4), dtype=np.float32)
+    full = orc.fwd("div", a, b)
+    pos = np.array([0, 7, 33, 119], np.int64)
+    np.testing.assert_array_equal(orc.fwd_at("div", a, b, pos), full.reshape(-1)[pos])
+    ga, gb = orc.bwd("div", g, a, b)
+    pb = np.arange(5, dtype=np.int64)
+    s = orc.bwd_at("div", 1, g, a, b, pb)
+    np.testing.assert_array_equal(s.f64, gb.f64.reshape(-1))
+    s = orc.bwd_at("div", 0, g, a, b, pos)
+    np.testing.assert_array_equal(s.f32, ga.f32.reshape(-1)[pos])
