@@ -1,0 +1,352 @@
+// zk_api.cpp -- the extern "C" boundary (include/zk.h).
+//
+// Every argument is validated and the whole launch plan is built on the host
+// before the first HIP call; an error returns with nothing launched and no
+// output written.  The library keeps no state between calls.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "zk.h"
+#include "zk_kernels.h"
+#include "zk_plan.h"
+
+using namespace zk;
+
+namespace {
+
+bool valid_op(zk_op op) { return op >= ZK_ADD && op <= ZK_DIV; }
+bool valid_epi(zk_epi e) { return e == ZK_EPI_NONE || e == ZK_EPI_GELU; }
+
+int64_t numel(const zk_desc &d) {
+  int64_t m = 1;
+  for (int k = 0; k < d.rank; ++k) m *= d.sizes[k];
+  return m;
+}
+
+// The operand is dense row-major with exactly `n` elements in the broadcast
+// layout (sizes equal to the trailing out sizes, dense strides).
+bool dense_full(const zk_desc &d, int64_t out_numel) {
+  if (numel(d) != out_numel) return false;
+  int64_t s = 1;
+  for (int k = d.rank - 1; k >= 0; --k) {
+    if (d.sizes[k] != 1 && d.strides[k] != s) return false;
+    s *= d.sizes[k];
+  }
+  return true;
+}
+
+struct Ext {
+  uintptr_t lo = 0, hi = 0;
+};
+Ext ext_of(const void *p, const zk_desc &d) {
+  Ext e;
+  if (p) byte_extent(p, d, &e.lo, &e.hi);
+  return e;
+}
+Ext ext_dense(const void *p, int64_t n) {
+  Ext e;
+  if (p) byte_extent_dense(p, n, &e.lo, &e.hi);
+  return e;
+}
+bool ov(const Ext &a, const Ext &b) { return overlaps(a.lo, a.hi, b.lo, b.hi); }
+
+zk_status hip_status(hipError_t e) { return e == hipSuccess ? ZK_OK : ZK_ERR_HIP; }
+
+// Workspace a backward call needs, as a function of the shapes (and of which
+// gradients are requested) only: the larger of the plans for 16-byte aligned
+// and for misaligned pointers, since alignment picks between them.
+size_t bwd_workspace(zk_op op, zk_epi epi, const zk_desc &da,
+                     const zk_desc &db, bool wa, bool wb) {
+  size_t m = 0;
+  for (uintptr_t q : {(uintptr_t)0, (uintptr_t)4}) {
+    BwdPlan p;
+    if (plan_bwd(op, epi, da, db, wa, wb, q, q, q, q, q, q, q, &p) == ZK_OK)
+      m = p.workspace > m ? p.workspace : m;
+  }
+  return m;
+}
+
+size_t reduce_workspace(const zk_desc &din, int rout, const int64_t *nout) {
+  size_t m = 0;
+  for (uintptr_t q : {(uintptr_t)0, (uintptr_t)4}) {
+    BwdPlan p;
+    if (plan_reduce(din, rout, nout, q, q, &p) == ZK_OK)
+      m = p.workspace > m ? p.workspace : m;
+  }
+  return m;
+}
+
+// ------------------------------------------------ optional kernel timing
+struct Profiler {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<hipEvent_t> start, end;
+  std::vector<int32_t> ids;
+  int next = 0;
+};
+Profiler &prof() {
+  static Profiler p;
+  return p;
+}
+
+}  // namespace
+
+namespace zk {
+ProfScope::ProfScope(hipStream_t s, int32_t kernel) : slot(-1), st(s) {
+  Profiler &p = prof();
+  if (!p.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> g(p.mu);
+  if (p.next >= (int)p.start.size()) return;
+  slot = p.next++;
+  p.ids[slot] = kernel;
+  (void)hipEventRecord(p.start[slot], st);
+}
+ProfScope::~ProfScope() {
+  if (slot < 0) return;
+  (void)hipEventRecord(prof().end[slot], st);
+}
+}  // namespace zk
+
+extern "C" {
+
+zk_status zk_profile_start(int32_t capacity) {
+  Profiler &p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on = false;
+  for (auto e : p.start) (void)hipEventDestroy(e);
+  for (auto e : p.end) (void)hipEventDestroy(e);
+  p.start.clear();
+  p.end.clear();
+  p.ids.assign(capacity > 0 ? capacity : 0, -1);
+  p.next = 0;
+  for (int i = 0; i < capacity; ++i) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return ZK_ERR_HIP;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return ZK_ERR_HIP;
+    }
+    p.start.push_back(a);
+    p.end.push_back(b);
+  }
+  p.on = true;
+  return ZK_OK;
+}
+
+zk_status zk_profile_stop(void) {
+  prof().on = false;
+  return ZK_OK;
+}
+
+zk_status zk_profile_read(int32_t max, int32_t *kernel_ids, float *ms,
+                          int32_t *count) {
+  if (!count || (max > 0 && (!kernel_ids || !ms))) return ZK_ERR_NULL;
+  Profiler &p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  int n = p.next < max ? p.next : max;
+  for (int i = 0; i < n; ++i) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, p.start[i], p.end[i]) != hipSuccess) return ZK_ERR_HIP;
+    kernel_ids[i] = p.ids[i];
+    ms[i] = t;
+  }
+  *count = n;
+  return ZK_OK;
+}
+
+const char *zk_status_string(zk_status s) {
+  switch (s) {
+    case ZK_OK: return "ok";
+    case ZK_ERR_NULL: return "a required pointer is NULL";
+    case ZK_ERR_RANK: return "rank out of range [0, 8]";
+    case ZK_ERR_BAD_SIZE: return "negative size";
+    case ZK_ERR_BAD_STRIDE: return "negative stride";
+    case ZK_ERR_BROADCAST: return "shapes do not broadcast";
+    case ZK_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ZK_ERR_WORKSPACE: return "workspace too small";
+    case ZK_ERR_UNSUPPORTED: return "unsupported op or epilogue";
+    case ZK_ERR_HIP: return "HIP launch failed";
+    case ZK_ERR_SHAPE: return "target shape does not broadcast to the input";
+  }
+  return "unknown status";
+}
+
+const char *zk_kernel_name(int32_t k) { return kernel_name(k); }
+
+zk_status zk_broadcast_shape(int32_t rank_a, const int64_t *sizes_a,
+                             int32_t rank_b, const int64_t *sizes_b,
+                             int32_t *rank_out, int64_t sizes_out[ZK_MAX_DIMS]) {
+  if (!rank_out || !sizes_out) return ZK_ERR_NULL;
+  int r = 0;
+  int64_t n[kMaxDims];
+  zk_status s = broadcast_shape(rank_a, sizes_a, rank_b, sizes_b, &r, n);
+  if (s) return s;
+  *rank_out = r;
+  for (int k = 0; k < r; ++k) sizes_out[k] = n[k];
+  return ZK_OK;
+}
+
+zk_status zk_binary_fwd(zk_op op, zk_epi epi, const float *a, const zk_desc *da,
+                        const float *b, const zk_desc *db, float *out,
+                        void *stream) {
+  if (!valid_op(op) || !valid_epi(epi)) return ZK_ERR_UNSUPPORTED;
+  zk_status s;
+  if ((s = check_desc(da)) || (s = check_desc(db))) return s;
+  FwdPlan p;
+  if ((s = plan_fwd(op, epi, *da, *db, (uintptr_t)a, (uintptr_t)b,
+                    (uintptr_t)out, &p)))
+    return s;
+  if (p.empty) return ZK_OK;
+  if (!a || !b || !out) return ZK_ERR_NULL;
+  const int64_t n = p.c.numel;
+  Ext eo = ext_dense(out, n), ea = ext_of(a, *da), eb = ext_of(b, *db);
+  if (ov(eo, ea) && !(out == a && dense_full(*da, n))) return ZK_ERR_ALIAS;
+  if (ov(eo, eb) && !(out == b && dense_full(*db, n))) return ZK_ERR_ALIAS;
+  return hip_status(launch_fwd(p, op, epi, a, b, out, (hipStream_t)stream));
+}
+
+zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad, const float *a,
+                        const zk_desc *da, const float *b, const zk_desc *db,
+                        float *grad_a, const float *acc_a, float *grad_b,
+                        const float *acc_b, void *workspace,
+                        size_t *workspace_bytes, void *stream) {
+  if (!valid_op(op) || !valid_epi(epi)) return ZK_ERR_UNSUPPORTED;
+  if (!workspace_bytes) return ZK_ERR_NULL;
+  zk_status s;
+  if ((s = check_desc(da)) || (s = check_desc(db))) return s;
+  BwdPlan p;
+  if ((s = plan_bwd(op, epi, *da, *db, grad_a != nullptr, grad_b != nullptr,
+                    (uintptr_t)grad, (uintptr_t)a, (uintptr_t)b,
+                    (uintptr_t)grad_a, (uintptr_t)grad_b, (uintptr_t)acc_a,
+                    (uintptr_t)acc_b, &p)))
+    return s;
+  const size_t need = bwd_workspace(op, epi, *da, *db, grad_a != nullptr,
+                                    grad_b != nullptr);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return ZK_OK;
+  }
+  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  const int64_t n = p.c.numel;
+  const int64_t na = numel(*da), nb = numel(*db);
+  if (n > 0 && (!grad || !a || !b)) return ZK_ERR_NULL;
+  // Extents of everything written and read.
+  Ext eg = ext_dense(grad, n), ea = ext_of(a, *da), eb = ext_of(b, *db);
+  Ext ega = ext_dense(grad_a, na), egb = ext_dense(grad_b, nb);
+  Ext exa = ext_dense(acc_a, na), exb = ext_dense(acc_b, nb);
+  Ext ews;
+  if (need) ews = Ext{(uintptr_t)workspace, (uintptr_t)workspace + need};
+  const Ext outs[2] = {ega, egb};
+  const float *gp[2] = {grad_a, grad_b};
+  const float *accp[2] = {acc_a, acc_b};
+  const Ext accs[2] = {exa, exb};
+  if (ov(ega, egb)) return ZK_ERR_ALIAS;
+  for (int w = 0; w < 2; ++w) {
+    if (!gp[w]) continue;
+    const Ext &o = outs[w];
+    if (ov(o, eg) || ov(o, ea) || ov(o, eb) || ov(o, ews)) return ZK_ERR_ALIAS;
+    if (ov(o, accs[w]) && accp[w] != gp[w]) return ZK_ERR_ALIAS;
+    if (ov(o, accs[1 - w])) return ZK_ERR_ALIAS;
+  }
+  if (need && (ov(ews, eg) || ov(ews, ea) || ov(ews, eb) || ov(ews, exa) ||
+                      ov(ews, exb)))
+    return ZK_ERR_ALIAS;
+  return hip_status(launch_bwd(p, op, epi, grad, a, b, grad_a, acc_a, grad_b,
+                               acc_b, workspace, (hipStream_t)stream));
+}
+
+zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
+                             int32_t rank_out, const int64_t *sizes_out,
+                             float *out, void *workspace,
+                             size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes) return ZK_ERR_NULL;
+  zk_status s;
+  if ((s = check_desc(din))) return s;
+  if (rank_out < 0 || rank_out > kMaxDims) return ZK_ERR_RANK;
+  if (rank_out > 0 && !sizes_out) return ZK_ERR_NULL;
+  for (int k = 0; k < rank_out; ++k)
+    if (sizes_out[k] < 0) return ZK_ERR_BAD_SIZE;
+  BwdPlan p;
+  if ((s = plan_reduce(*din, rank_out, sizes_out, (uintptr_t)in, (uintptr_t)out, &p)))
+    return s;
+  const size_t need = reduce_workspace(*din, rank_out, sizes_out);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return ZK_OK;
+  }
+  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  int64_t nout = 1;
+  for (int k = 0; k < rank_out; ++k) nout *= sizes_out[k];
+  if (p.c.numel > 0 && !in) return ZK_ERR_NULL;
+  if (nout > 0 && !out) return ZK_ERR_NULL;
+  Ext ei = ext_of(in, *din), eo = ext_dense(out, nout);
+  Ext ews;
+  if (need) ews = Ext{(uintptr_t)workspace, (uintptr_t)workspace + need};
+  if (ov(eo, ei) || ov(eo, ews) || ov(ews, ei)) return ZK_ERR_ALIAS;
+  return hip_status(launch_reduce(p, in, out, workspace, (hipStream_t)stream));
+}
+
+zk_status zk_plan_describe(int32_t kind, zk_op op, zk_epi epi, const zk_desc *da,
+                           const zk_desc *db, zk_plan_info *info) {
+  if (!info) return ZK_ERR_NULL;
+  if (!valid_op(op) || !valid_epi(epi)) return ZK_ERR_UNSUPPORTED;
+  zk_status s;
+  if ((s = check_desc(da)) || (s = check_desc(db))) return s;
+  std::memset(info, 0, sizeof(*info));
+  info->kernel2 = K_NONE;
+  const Canon *c = nullptr;
+  if (kind == 0) {
+    static thread_local FwdPlan p;
+    p = FwdPlan();
+    if ((s = plan_fwd(op, epi, *da, *db, 0, 0, 0, &p))) return s;
+    info->kernel = p.kernel;
+    info->index64 = p.idx64;
+    info->vec = p.vec;
+    c = &p.c;
+    info->rank = c->rank;
+    for (int k = 0; k < c->rank; ++k) {
+      info->sizes[k] = c->n[k];
+      for (int o = 0; o < 3; ++o) info->strides[o][k] = c->s[o][k];
+    }
+    return ZK_OK;
+  }
+  static thread_local BwdPlan p;
+  p = BwdPlan();
+  if (kind == 1) {
+    if ((s = plan_bwd(op, epi, *da, *db, true, true, 0, 0, 0, 0, 0, 0, 0, &p))) return s;
+  } else if (kind == 2) {
+    if ((s = plan_reduce(*da, db->rank, db->sizes, 0, 0, &p))) return s;
+  } else {
+    return ZK_ERR_UNSUPPORTED;
+  }
+  c = &p.c;
+  info->kernel = p.ew_kernel;
+  if (p.nred > 0) {
+    if (info->kernel == K_NONE) info->kernel = p.red[0].kernel;
+    else info->kernel2 = p.red[0].kernel;
+    info->partials = p.red[0].partials;
+  }
+  if (p.nred > 1) info->kernel2 = p.red[1].kernel;
+  info->index64 = p.idx64;
+  info->vec = p.vec;
+  info->workspace_bytes = kind == 1 ? bwd_workspace(op, epi, *da, *db, true, true)
+                                    : reduce_workspace(*da, db->rank, db->sizes);
+  info->rank = c->rank;
+  for (int k = 0; k < c->rank; ++k) {
+    info->sizes[k] = c->n[k];
+    if (kind == 1) {
+      for (int o = 0; o < 3; ++o) info->strides[o][k] = c->s[o][k];
+    } else {  // [0] dense input layout, [1] input strides, [2] target
+      info->strides[0][k] = c->s[1][k];
+      info->strides[1][k] = c->s[0][k];
+      info->strides[2][k] = c->s[4][k];
+    }
+  }
+  return ZK_OK;
+}
+
+}  // extern "C"

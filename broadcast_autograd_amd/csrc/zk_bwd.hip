@@ -1,0 +1,756 @@
+// zk_bwd.hip -- backward kernels for gfx950 (wave64).
+//
+// Local rule per element, then the sum of each broadcast operand's gradient
+// over the positions it was repeated into (Operator chapter of the "Zero"
+// book, "broadcast").  The book's kernel adds into the small gradient with
+// atomics; here the sum is split by the shapes alone into partials:
+//   stage 1 (one fused kernel): stream the upstream grad and the operands the
+//     rule needs, write the full-shape gradient, and accumulate the small
+//     gradient's terms in binary64 per lane -> wave / LDS tree -> one binary64
+//     partial per (workgroup tile, kept element) in the caller's workspace;
+//   stage 2 (red_final): sum each kept element's partials in a fixed order,
+//     add its acc, round once to binary32.
+// No atomics, so every call on the same shapes returns the same bits.
+//
+// Stage-1 classes (canonical pattern, R = reduced dim, K = kept dim):
+//   red_col     [R, K]             column sums; lanes own 4 columns
+//   red_row     [R1, K, R0] / [K, R0] / [R0]  inner run reduced; a wave owns
+//               one chunk of one row and reduces it with a butterfly
+//   red_tile    [R, K] with the full-shape operand transposed; 64x64 tiles
+//               of it are staged through LDS
+//   red_generic any pattern, rank <= 8: one thread per (kept element,
+//               partial), offsets decoded per term
+#include <type_traits>
+
+#include "zk_device.h"
+
+namespace zk {
+
+constexpr int kBlk = 256;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <typename Fn>
+static hipError_t op_epi(zk_op op, zk_epi epi, Fn &&fn) {
+  switch ((int)op * 2 + (int)epi) {
+    case 0: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_NONE>{});
+    case 1: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_GELU>{});
+    case 2: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_NONE>{});
+    case 3: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_GELU>{});
+    case 4: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_NONE>{});
+    case 5: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_GELU>{});
+    case 6: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_NONE>{});
+    case 7: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_GELU>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename Fn>
+static hipError_t side_acc(int side, int acc, Fn &&fn) {
+  switch (side * 3 + acc) {
+    case 0: return fn(IC<0>{}, IC<0>{});
+    case 1: return fn(IC<0>{}, IC<1>{});
+    case 2: return fn(IC<0>{}, IC<2>{});
+    case 3: return fn(IC<1>{}, IC<0>{});
+    case 4: return fn(IC<1>{}, IC<1>{});
+    case 5: return fn(IC<1>{}, IC<2>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+// Does the rule of either gradient read the a-role (x) / b-role (y) value?
+template <int OP, int EPI>
+constexpr bool any_x() { return reads_x<OP, EPI, 0>() || reads_x<OP, EPI, 1>(); }
+template <int OP, int EPI>
+constexpr bool any_y() { return reads_y<OP, EPI, 0>() || reads_y<OP, EPI, 1>(); }
+
+// ---------------------------------------------------- element-wise, flat
+// Both gradients have the full shape: no reduction.  acc modes: 0 none,
+// 1 the upstream grad itself, 2 a separate buffer (or the gradient, in place).
+struct EwArgs {
+  int64_t n;
+  int32_t write_a, write_b, acc_a, acc_b, read_a, read_b;
+};
+
+template <int OP, int EPI>
+__device__ __forceinline__ void ew_one(float gv, float x, float y, float aa,
+                                       float ab, const EwArgs &ea, float &oa,
+                                       float &ob) {
+  if (ea.write_a) {
+    float t = term32<OP, EPI, 0>(gv, x, y);
+    oa = ea.acc_a == 1 ? gv + t : (ea.acc_a == 2 ? aa + t : t);
+  }
+  if (ea.write_b) {
+    float t = term32<OP, EPI, 1>(gv, x, y);
+    ob = ea.acc_b == 1 ? gv + t : (ea.acc_b == 2 ? ab + t : t);
+  }
+}
+
+template <int OP, int EPI, int VEC>
+__global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
+    const float *g, const float *a, const float *b, float *ga,
+    const float *acc_a, float *gb, const float *acc_b, EwArgs ea) {
+  constexpr int U = 4;
+  constexpr int64_t tile = (int64_t)kBlk * U * VEC;
+  if constexpr (VEC == 4) {
+    const int64_t base = (int64_t)blockIdx.x * tile + (int64_t)threadIdx.x * 4;
+    float4 vg[U], va[U], vb[U], xa[U], xb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t i = base + (int64_t)u * kBlk * 4;
+      if (i + 4 <= ea.n) {
+        vg[u] = ld4(g + i);
+        if (ea.read_a) va[u] = ld4(a + i);
+        if (ea.read_b) vb[u] = ld4(b + i);
+        if (ea.acc_a == 2) xa[u] = ld4(acc_a + i);
+        if (ea.acc_b == 2) xb[u] = ld4(acc_b + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t i = base + (int64_t)u * kBlk * 4;
+      if (i + 4 <= ea.n) {
+        float4 oa, ob;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          ew_one<OP, EPI>(el(vg[u], k), ea.read_a ? el(va[u], k) : 0.f,
+                          ea.read_b ? el(vb[u], k) : 0.f,
+                          ea.acc_a == 2 ? el(xa[u], k) : 0.f,
+                          ea.acc_b == 2 ? el(xb[u], k) : 0.f, ea, el(oa, k), el(ob, k));
+        if (ea.write_a) st4(ga + i, oa);
+        if (ea.write_b) st4(gb + i, ob);
+      } else if (i < ea.n) {
+        for (int64_t j = i; j < ea.n; ++j) {
+          float oa = 0.f, ob = 0.f;
+          ew_one<OP, EPI>(g[j], ea.read_a ? a[j] : 0.f, ea.read_b ? b[j] : 0.f,
+                          ea.acc_a == 2 ? acc_a[j] : 0.f, ea.acc_b == 2 ? acc_b[j] : 0.f,
+                          ea, oa, ob);
+          if (ea.write_a) ga[j] = oa;
+          if (ea.write_b) gb[j] = ob;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t j = (int64_t)blockIdx.x * tile + (int64_t)u * kBlk + threadIdx.x;
+      if (j < ea.n) {
+        float oa = 0.f, ob = 0.f;
+        ew_one<OP, EPI>(g[j], ea.read_a ? a[j] : 0.f, ea.read_b ? b[j] : 0.f,
+                        ea.acc_a == 2 ? acc_a[j] : 0.f, ea.acc_b == 2 ? acc_b[j] : 0.f,
+                        ea, oa, ob);
+        if (ea.write_a) ga[j] = oa;
+        if (ea.write_b) gb[j] = ob;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- element-wise, generic
+template <typename I>
+__device__ __forceinline__ void offs_ab(const Space &sp, I i, I &oa, I &ob) {
+  I rest = i;
+  oa = 0;
+  ob = 0;
+#pragma unroll
+  for (int k = kMaxDims - 1; k >= 1; --k) {
+    if (k < sp.rank) {
+      I q;
+      if constexpr (sizeof(I) == 4) q = (I)fdiv(sp.fd[k], (uint32_t)rest);
+      else q = rest / (I)sp.n[k];
+      I c = rest - q * (I)sp.n[k];
+      oa += c * (I)sp.s[1][k];
+      ob += c * (I)sp.s[2][k];
+      rest = q;
+    }
+  }
+  oa += rest * (I)sp.s[1][0];
+  ob += rest * (I)sp.s[2][0];
+}
+
+template <int OP, int EPI, typename I>
+__global__ __launch_bounds__(kBlk) void k_bwd_ew_generic(
+    const float *g, const float *a, const float *b, float *ga,
+    const float *acc_a, float *gb, const float *acc_b, EwArgs ea, Space sp) {
+  const I n = (I)ea.n;
+  const I i0 = ((I)blockIdx.x * kBlk + (I)threadIdx.x) * 4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    I i = i0 + k;
+    if (i < n) {
+      I oa, ob;
+      offs_ab<I>(sp, i, oa, ob);
+      float o1 = 0.f, o2 = 0.f;
+      ew_one<OP, EPI>(g[i], ea.read_a ? a[oa] : 0.f, ea.read_b ? b[ob] : 0.f,
+                      ea.acc_a == 2 ? acc_a[i] : 0.f, ea.acc_b == 2 ? acc_b[i] : 0.f,
+                      ea, o1, o2);
+      if (ea.write_a) ga[i] = o1;
+      if (ea.write_b) gb[i] = o2;
+    }
+  }
+}
+
+// --------------------------------------------------------------- red_col
+// g, the full operand and its gradient are dense [R, K]; the small operand
+// is read at column c with stride ss.  Block = 4 waves on the same 256
+// columns, rows of its chunk interleaved across the waves; each lane keeps 4
+// binary64 column sums; the 4 waves are combined through LDS in wave order.
+struct ColArgs {
+  int64_t R, K, rc, ss, colblocks;
+  int32_t write_big;
+};
+
+template <int OP, int EPI, int SIDE, int ACC>
+__global__ __launch_bounds__(kBlk) void k_red_col(
+    const float *g, const float *big, const float *small, float *gbig,
+    const float *accbig, double *part, ColArgs ca) {
+  constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
+  constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
+  constexpr int U = 4;
+  __shared__ double lds[4][64][4];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int64_t p = blockIdx.x / ca.colblocks;
+  const int64_t cb = blockIdx.x - p * ca.colblocks;
+  const int64_t c = cb * 256 + 4 * l;
+  const bool active = c < ca.K;
+  float sv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (NEED_SMALL && active) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sv[k] = small[(c + k) * ca.ss];
+  }
+  const int64_t r0 = p * ca.rc;
+  const int64_t r1 = r0 + ca.rc < ca.R ? r0 + ca.rc : ca.R;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  if (active) {
+    for (int64_t rb = r0 + w; rb < r1; rb += 4 * U) {
+      float4 vg[U], vb[U], va[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t r = rb + 4 * u;
+        if (r < r1) {
+          const int64_t i = r * ca.K + c;
+          vg[u] = ld4(g + i);
+          if constexpr (NEED_BIG) vb[u] = ld4(big + i);
+          if constexpr (ACC == 2) va[u] = ld4(accbig + i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t r = rb + 4 * u;
+        if (r < r1) {
+          const int64_t i = r * ca.K + c;
+          float4 ob;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float gv = el(vg[u], k);
+            const float bv = NEED_BIG ? el(vb[u], k) : 0.f;
+            const float x = SIDE == 0 ? sv[k] : bv;
+            const float y = SIDE == 0 ? bv : sv[k];
+            s[k] += term64<OP, EPI, SIDE>(gv, x, y);
+            float tb = term32<OP, EPI, 1 - SIDE>(gv, x, y);
+            if constexpr (ACC == 1) tb = gv + tb;
+            if constexpr (ACC == 2) tb = el(va[u], k) + tb;
+            el(ob, k) = tb;
+          }
+          if (ca.write_big) st4(gbig + i, ob);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) lds[w][l][k] = s[k];
+  __syncthreads();
+  if (w == 0 && active) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      double tot = ((lds[0][l][k] + lds[1][l][k]) + lds[2][l][k]) + lds[3][l][k];
+      part[p * ca.K + c + k] = tot;
+    }
+  }
+}
+
+// --------------------------------------------------------------- red_row
+// Rows of R0 contiguous reduced elements; row = r1 * K + k.  Work item =
+// (row, chunk of CL elements); one wave per item.
+struct RowRedArgs {
+  int64_t R0, K, NC, CL, items, ss;
+  int32_t write_big;
+};
+
+template <int OP, int EPI, int SIDE, int ACC>
+__global__ __launch_bounds__(kBlk) void k_red_row(
+    const float *g, const float *big, const float *small, float *gbig,
+    const float *accbig, double *part, RowRedArgs ra) {
+  constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
+  constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
+  constexpr int U = 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + w;
+  if (item >= ra.items) return;
+  const int64_t row = item / ra.NC, ch = item - row * ra.NC;
+  const int64_t r1 = row / ra.K, k = row - r1 * ra.K;
+  const float sv = NEED_SMALL ? small[k * ra.ss] : 0.f;
+  const int64_t e0 = row * ra.R0 + ch * ra.CL;
+  const int64_t lim = (ch + 1) * ra.CL < ra.R0 ? (ch + 1) * ra.CL : ra.R0;
+  const int64_t e1 = row * ra.R0 + lim;
+  double s = 0.0;
+  for (int64_t eb = e0 + 4 * l; eb < e1; eb += 256 * U) {
+    float4 vg[U], vb[U], va[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = eb + 256 * u;
+      if (i < e1) {
+        vg[u] = ld4(g + i);
+        if constexpr (NEED_BIG) vb[u] = ld4(big + i);
+        if constexpr (ACC == 2) va[u] = ld4(accbig + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = eb + 256 * u;
+      if (i < e1) {
+        float4 ob;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float gv = el(vg[u], q);
+          const float bv = NEED_BIG ? el(vb[u], q) : 0.f;
+          const float x = SIDE == 0 ? sv : bv;
+          const float y = SIDE == 0 ? bv : sv;
+          s += term64<OP, EPI, SIDE>(gv, x, y);
+          float tb = term32<OP, EPI, 1 - SIDE>(gv, x, y);
+          if constexpr (ACC == 1) tb = gv + tb;
+          if constexpr (ACC == 2) tb = el(va[u], q) + tb;
+          el(ob, q) = tb;
+        }
+        if (ra.write_big) st4(gbig + i, ob);
+      }
+    }
+  }
+  s = wave_sum(s);
+  if (l == 0) part[(r1 * ra.NC + ch) * ra.K + k] = s;
+}
+
+// -------------------------------------------------------------- red_tile
+// [R, K]; the full operand F[i, j] is at i + j*ld (transposed view); g and
+// the full operand's gradient are dense [R, K].  Block = 64 columns x a
+// chunk of rows walked in 64-row tiles.
+struct TileRedArgs {
+  int64_t R, K, ld, ss, rc, tiles_c;
+  int32_t write_big;
+};
+
+template <int OP, int EPI, int SIDE, int ACC>
+__global__ __launch_bounds__(kBlk) void k_red_tile(
+    const float *g, const float *big, const float *small, float *gbig,
+    const float *accbig, double *part, TileRedArgs ta) {
+  constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
+  constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
+  __shared__ float tile[64][65];
+  __shared__ double red[16][64];
+  const int t = threadIdx.x;
+  const int64_t p = blockIdx.x / ta.tiles_c;
+  const int64_t tj = blockIdx.x - p * ta.tiles_c;
+  const int64_t j0 = tj * 64;
+  const int m = t & 15, q = t >> 4;
+  const int64_t gj = j0 + 4 * m;
+  const bool colok = gj < ta.K;  // K % 4 == 0, so all 4 columns are in range
+  float sv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (NEED_SMALL && colok) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sv[k] = small[(gj + k) * ta.ss];
+  }
+  const int64_t r0 = p * ta.rc;
+  const int64_t r1 = r0 + ta.rc < ta.R ? r0 + ta.rc : ta.R;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t ti = r0; ti < r1; ti += 64) {
+    if constexpr (NEED_BIG) {
+      const int i = t & 63, jq = t >> 6;
+      const int64_t gi = ti + i;
+#pragma unroll
+      for (int pp = 0; pp < 16; ++pp) {
+        const int j = jq + 4 * pp;
+        float v = 0.f;
+        if (gi < r1 && j0 + j < ta.K) v = big[gi + (j0 + j) * ta.ld];
+        tile[j][i] = v;
+      }
+      __syncthreads();
+    }
+    if (colok) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int i = q + 16 * pp;
+        const int64_t gi = ti + i;
+        if (gi < r1) {
+          const int64_t off = gi * ta.K + gj;
+          const float4 vg = ld4(g + off);
+          float4 va;
+          if constexpr (ACC == 2) va = ld4(accbig + off);
+          float4 ob;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float gv = el(vg, k);
+            const float bv = NEED_BIG ? tile[4 * m + k][i] : 0.f;
+            const float x = SIDE == 0 ? sv[k] : bv;
+            const float y = SIDE == 0 ? bv : sv[k];
+            s[k] += term64<OP, EPI, SIDE>(gv, x, y);
+            float tb = term32<OP, EPI, 1 - SIDE>(gv, x, y);
+            if constexpr (ACC == 1) tb = gv + tb;
+            if constexpr (ACC == 2) tb = el(va, k) + tb;
+            el(ob, k) = tb;
+          }
+          if (ta.write_big) st4(gbig + off, ob);
+        }
+      }
+    }
+    if constexpr (NEED_BIG) __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) red[q][4 * m + k] = s[k];
+  __syncthreads();
+  if (t < 64 && j0 + t < ta.K) {
+    double tot = 0.0;
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) tot += red[qq][t];
+    part[p * ta.K + j0 + t] = tot;
+  }
+}
+
+// ----------------------------------------------------------- red_generic
+// One thread per (kept element k, partial p); p covers a contiguous range of
+// the row-major flattening of the reduced dims.  IDENT: the term is the
+// source value itself (reduce_to_shape).
+struct GenArgs {
+  int32_t nk, nr;
+  int64_t kn[kMaxDims], rn[kMaxDims];
+  int64_t ks[3][kMaxDims], rs[3][kMaxDims];  // strides of src/g, a, b
+  int64_t K, P, chunk, red;
+};
+
+template <int OP, int EPI, int WHICH, int IDENT, typename I>
+__global__ __launch_bounds__(kBlk) void k_red_generic(const float *g,
+                                                      const float *a,
+                                                      const float *b,
+                                                      double *part, GenArgs ga) {
+  const I gid = (I)blockIdx.x * kBlk + (I)threadIdx.x;
+  if (gid >= (I)(ga.K * ga.P)) return;
+  const I k = gid % (I)ga.K, p = gid / (I)ga.K;
+  I og = 0, oa = 0, ob = 0;
+  {
+    I rest = k;
+#pragma unroll
+    for (int d = kMaxDims - 1; d >= 0; --d) {
+      if (d < ga.nk) {
+        const I n = (I)ga.kn[d];
+        const I q = rest / n, c = rest - q * n;
+        og += c * (I)ga.ks[0][d];
+        oa += c * (I)ga.ks[1][d];
+        ob += c * (I)ga.ks[2][d];
+        rest = q;
+      }
+    }
+  }
+  const I lo = p * (I)ga.chunk;
+  const I hi = lo + (I)ga.chunk < (I)ga.red ? lo + (I)ga.chunk : (I)ga.red;
+  double s = 0.0;
+  for (I tt = lo; tt < hi; ++tt) {
+    I rest = tt, dg = 0, da = 0, db = 0;
+#pragma unroll
+    for (int d = kMaxDims - 1; d >= 0; --d) {
+      if (d < ga.nr) {
+        const I n = (I)ga.rn[d];
+        const I q = rest / n, c = rest - q * n;
+        dg += c * (I)ga.rs[0][d];
+        da += c * (I)ga.rs[1][d];
+        db += c * (I)ga.rs[2][d];
+        rest = q;
+      }
+    }
+    const float gv = g[og + dg];
+    if constexpr (IDENT) {
+      s += (double)gv;
+    } else {
+      const float x = reads_x<OP, EPI, WHICH>() ? a[oa + da] : 0.f;
+      const float y = reads_y<OP, EPI, WHICH>() ? b[ob + db] : 0.f;
+      s += term64<OP, EPI, WHICH>(gv, x, y);
+    }
+  }
+  part[p * (I)ga.K + k] = s;
+}
+
+// ------------------------------------------------------------- red_final
+// out[k] = RN32(sum_p part[p][k] + acc[k]).  tpk threads per kept element
+// each sum a fixed strided subset of p; the subsets are then added in order.
+struct FinArgs {
+  int64_t K, P;
+  int32_t tpk, kt, has_acc;
+};
+
+__global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
+                                                    const float *acc,
+                                                    float *out, FinArgs fa) {
+  __shared__ double sh[kBlk];
+  const int t = threadIdx.x;
+  const int kk = t % fa.kt, q = t / fa.kt;
+  const int64_t k = (int64_t)blockIdx.x * fa.kt + kk;
+  double s = 0.0;
+  if (k < fa.K) {
+    for (int64_t p = q; p < fa.P; p += fa.tpk) s += part[p * fa.K + k];
+  }
+  sh[t] = s;
+  __syncthreads();
+  if (q == 0 && k < fa.K) {
+    double tot = 0.0;
+    for (int qq = 0; qq < fa.tpk; ++qq) tot += sh[kk + qq * fa.kt];
+    if (fa.has_acc) tot += (double)acc[k];
+    out[k] = (float)tot;
+  }
+}
+
+// -------------------------------------------------------------- launchers
+static inline unsigned gridn(int64_t n, int64_t per) {
+  return (unsigned)((n + per - 1) / per);
+}
+
+static hipError_t launch_final(const RedPlan &rp, const double *part,
+                               const float *acc, float *out, hipStream_t st) {
+  if (rp.kept == 0) return hipSuccess;
+  FinArgs fa{};
+  fa.K = rp.kept;
+  fa.P = rp.partials;
+  int tpk = 1;
+  while (tpk < 256 && rp.partials > 16 * (int64_t)tpk) tpk *= 2;
+  fa.tpk = tpk;
+  fa.kt = kBlk / tpk;
+  fa.has_acc = acc != nullptr;
+  ProfScope prof(st, K_RED_FINAL);
+  hipLaunchKernelGGL(k_red_final, dim3(gridn(rp.kept, fa.kt)), dim3(kBlk), 0, st,
+                     part, acc, out, fa);
+  return hipGetLastError();
+}
+
+// Split the canonical dims into kept / reduced lists for the gather kernel.
+// kept_op: stride set of the reduced gradient (0 where reduced).
+static GenArgs make_gen(const Canon &c, int kept_op, int src_op, int a_op,
+                        int b_op, const RedPlan &rp) {
+  GenArgs ga{};
+  for (int d = 0; d < c.rank; ++d) {
+    const int ops[3] = {src_op, a_op, b_op};
+    if (c.s[kept_op][d] != 0) {
+      ga.kn[ga.nk] = c.n[d];
+      for (int o = 0; o < 3; ++o) ga.ks[o][ga.nk] = ops[o] >= 0 ? c.s[ops[o]][d] : 0;
+      ++ga.nk;
+    } else {
+      ga.rn[ga.nr] = c.n[d];
+      for (int o = 0; o < 3; ++o) ga.rs[o][ga.nr] = ops[o] >= 0 ? c.s[ops[o]][d] : 0;
+      ++ga.nr;
+    }
+  }
+  ga.K = rp.kept;
+  ga.P = rp.partials;
+  ga.chunk = rp.chunk;
+  ga.red = rp.red;
+  return ga;
+}
+
+static int acc_mode(const float *acc, const float *g) {
+  if (!acc) return 0;
+  return acc == g ? 1 : 2;
+}
+
+hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
+                      const float *a, const float *b, float *grad_a,
+                      const float *acc_a, float *grad_b, const float *acc_b,
+                      void *ws, hipStream_t st) {
+  const Canon &c = p.c;
+  hipError_t e = hipSuccess;
+  // Element-wise gradients of full-shape operands.
+  if (p.ew_kernel != K_NONE) {
+    EwArgs ea{};
+    ea.n = c.numel;
+    ea.write_a = p.ew_write[0];
+    ea.write_b = p.ew_write[1];
+    ea.acc_a = ea.write_a ? acc_mode(acc_a, g) : 0;
+    ea.acc_b = ea.write_b ? acc_mode(acc_b, g) : 0;
+    ea.read_a = (ea.write_a && rule_reads_a(op, epi, 0)) || (ea.write_b && rule_reads_a(op, epi, 1));
+    ea.read_b = (ea.write_a && rule_reads_b(op, epi, 0)) || (ea.write_b && rule_reads_b(op, epi, 1));
+    e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
+      constexpr int OP = decltype(OPc)::value;
+      constexpr int EPI = decltype(EPIc)::value;
+      ProfScope prof(st, p.ew_kernel);
+      if (p.ew_kernel == K_BWD_EW_FLAT) {
+        if (p.vec == 4)
+          hipLaunchKernelGGL((k_bwd_ew_flat<OP, EPI, 4>), dim3(gridn(c.numel, kBlk * 16)),
+                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
+        else
+          hipLaunchKernelGGL((k_bwd_ew_flat<OP, EPI, 1>), dim3(gridn(c.numel, kBlk * 4)),
+                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
+      } else {
+        Space sp = make_space(c);
+        if (p.idx64)
+          hipLaunchKernelGGL((k_bwd_ew_generic<OP, EPI, int64_t>), dim3(gridn(c.numel, kBlk * 4)),
+                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, sp);
+        else
+          hipLaunchKernelGGL((k_bwd_ew_generic<OP, EPI, int32_t>), dim3(gridn(c.numel, kBlk * 4)),
+                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, sp);
+      }
+      return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
+  }
+  for (int ri = 0; ri < p.nred; ++ri) {
+    const RedPlan &rp = p.red[ri];
+    const int sw = rp.which, bw = 1 - rp.which;
+    double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + rp.ws_offset);
+    const float *small = sw == 0 ? a : b;
+    const float *big = sw == 0 ? b : a;
+    float *gsmall = sw == 0 ? grad_a : grad_b;
+    float *gbig = sw == 0 ? grad_b : grad_a;
+    const float *accsmall = sw == 0 ? acc_a : acc_b;
+    const float *accbig = sw == 0 ? acc_b : acc_a;
+    const int amode = p.fused_big ? acc_mode(accbig, g) : 0;
+    if (rp.partials > 0) {
+      e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
+        constexpr int OP = decltype(OPc)::value;
+        constexpr int EPI = decltype(EPIc)::value;
+        ProfScope prof(st, rp.kernel);
+        switch (rp.kernel) {
+          case K_RED_COL: {
+            ColArgs ca{};
+            ca.R = c.n[0];
+            ca.K = c.n[1];
+            ca.rc = rp.chunk;
+            ca.ss = c.s[1 + sw][1];
+            ca.colblocks = (ca.K + 255) / 256;
+            ca.write_big = p.fused_big;
+            unsigned grid = (unsigned)(ca.colblocks * rp.partials);
+            return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
+              hipLaunchKernelGGL((k_red_col<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
+                                 dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
+                                 part, ca);
+              return hipGetLastError();
+            });
+          }
+          case K_RED_ROW: {
+            RowRedArgs ra{};
+            const int R = c.rank;
+            ra.R0 = c.n[R - 1];
+            ra.K = rp.kept;
+            ra.CL = rp.chunk;
+            ra.NC = (ra.R0 + ra.CL - 1) / ra.CL;
+            ra.items = (c.numel / ra.R0) * ra.NC;
+            ra.ss = R >= 2 ? c.s[1 + sw][R - 2] : 0;
+            ra.write_big = p.fused_big;
+            unsigned grid = gridn(ra.items, 4);
+            return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
+              hipLaunchKernelGGL((k_red_row<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
+                                 dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
+                                 part, ra);
+              return hipGetLastError();
+            });
+          }
+          case K_RED_TILE: {
+            TileRedArgs ta{};
+            ta.R = c.n[0];
+            ta.K = c.n[1];
+            ta.ld = c.s[1 + bw][1];
+            ta.ss = c.s[1 + sw][1];
+            ta.rc = rp.chunk;
+            ta.tiles_c = (ta.K + 63) / 64;
+            ta.write_big = p.fused_big;
+            unsigned grid = (unsigned)(ta.tiles_c * rp.partials);
+            return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
+              hipLaunchKernelGGL((k_red_tile<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
+                                 dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
+                                 part, ta);
+              return hipGetLastError();
+            });
+          }
+          default: {
+            GenArgs ga = make_gen(c, 3 + sw, 0, 1, 2, rp);
+            unsigned grid = gridn(rp.kept * rp.partials, kBlk);
+            if (sw == 0) {
+              if (p.idx64)
+                hipLaunchKernelGGL((k_red_generic<OP, EPI, 0, 0, int64_t>), dim3(grid), dim3(kBlk),
+                                   0, st, g, a, b, part, ga);
+              else
+                hipLaunchKernelGGL((k_red_generic<OP, EPI, 0, 0, int32_t>), dim3(grid), dim3(kBlk),
+                                   0, st, g, a, b, part, ga);
+            } else {
+              if (p.idx64)
+                hipLaunchKernelGGL((k_red_generic<OP, EPI, 1, 0, int64_t>), dim3(grid), dim3(kBlk),
+                                   0, st, g, a, b, part, ga);
+              else
+                hipLaunchKernelGGL((k_red_generic<OP, EPI, 1, 0, int32_t>), dim3(grid), dim3(kBlk),
+                                   0, st, g, a, b, part, ga);
+            }
+            return hipGetLastError();
+          }
+        }
+      });
+      if (e != hipSuccess) return e;
+    }
+    e = launch_final(rp, part, accsmall, gsmall, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
+                         void *ws, hipStream_t st) {
+  const Canon &c = p.c;
+  for (int ri = 0; ri < p.nred; ++ri) {
+    const RedPlan &rp = p.red[ri];
+    double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + rp.ws_offset);
+    if (rp.partials > 0) {
+      ProfScope prof(st, rp.kernel);
+      switch (rp.kernel) {
+        case K_RED_COL: {
+          ColArgs ca{};
+          ca.R = c.n[0];
+          ca.K = c.n[1];
+          ca.rc = rp.chunk;
+          ca.ss = 0;
+          ca.colblocks = (ca.K + 255) / 256;
+          ca.write_big = 0;
+          hipLaunchKernelGGL((k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0>),
+                             dim3((unsigned)(ca.colblocks * rp.partials)), dim3(kBlk), 0, st,
+                             in, nullptr, nullptr, nullptr, nullptr, part, ca);
+          break;
+        }
+        case K_RED_ROW: {
+          RowRedArgs ra{};
+          const int R = c.rank;
+          ra.R0 = c.n[R - 1];
+          ra.K = rp.kept;
+          ra.CL = rp.chunk;
+          ra.NC = (ra.R0 + ra.CL - 1) / ra.CL;
+          ra.items = (c.numel / ra.R0) * ra.NC;
+          ra.ss = 0;
+          ra.write_big = 0;
+          hipLaunchKernelGGL((k_red_row<ZK_ADD, ZK_EPI_NONE, 1, 0>), dim3(gridn(ra.items, 4)),
+                             dim3(kBlk), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ra);
+          break;
+        }
+        default: {
+          GenArgs ga = make_gen(c, 4, 0, -1, -1, rp);
+          unsigned grid = gridn(rp.kept * rp.partials, kBlk);
+          if (p.idx64)
+            hipLaunchKernelGGL((k_red_generic<ZK_ADD, ZK_EPI_NONE, 1, 1, int64_t>), dim3(grid),
+                               dim3(kBlk), 0, st, in, nullptr, nullptr, part, ga);
+          else
+            hipLaunchKernelGGL((k_red_generic<ZK_ADD, ZK_EPI_NONE, 1, 1, int32_t>), dim3(grid),
+                               dim3(kBlk), 0, st, in, nullptr, nullptr, part, ga);
+        }
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch_final(rp, part, nullptr, out, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace zk

@@ -1,0 +1,400 @@
+// zk_fwd.hip -- forward kernels for gfx950 (wave64).
+//
+// out[i] = epi(a[off_a(i)] (op) b[off_b(i)]) over the canonical iteration
+// space (Operator chapter of the "Zero" book, "broadcast": a repeated operand
+// dim reads coordinate 0, here a stride of 0).  The output is always dense.
+// Classes:
+//   flat    : a, b, out walk the same dense layout -> 128-bit streams
+//   row     : one dense operand, the other rank <= 3 with any strides; its
+//             inner dim is a broadcast scalar, a contiguous run, or a gather
+//   tile    : rank 2 with a transposed operand (x[i,j] at i + j*ld); 64x64
+//             tiles are staged through LDS so both HBM sides are coalesced
+//   generic : any rank <= 8, per-element offsets
+#include <type_traits>
+
+#include "zk_device.h"
+
+namespace zk {
+
+constexpr int kBlock = 256;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Calls fn(IC<op>, IC<epi>) for the runtime (op, epi).
+template <typename Fn>
+static hipError_t with_op_epi(zk_op op, zk_epi epi, Fn &&fn) {
+  switch ((int)op * 2 + (int)epi) {
+    case 0: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_NONE>{});
+    case 1: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_GELU>{});
+    case 2: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_NONE>{});
+    case 3: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_GELU>{});
+    case 4: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_NONE>{});
+    case 5: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_GELU>{});
+    case 6: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_NONE>{});
+    case 7: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_GELU>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+Space make_space(const Canon &c) {
+  Space s{};
+  s.rank = c.rank;
+  s.numel = c.numel;
+  for (int k = 0; k < kMaxDims; ++k) {
+    s.n[k] = k < c.rank ? c.n[k] : 1;
+    for (int o = 0; o < kMaxOps; ++o) s.s[o][k] = k < c.rank ? c.s[o][k] : 0;
+    uint32_t d = (s.n[k] >= 1 && s.n[k] < ((int64_t)1 << 31)) ? (uint32_t)s.n[k] : 1u;
+    s.fd[k] = make_fastdiv(d);
+  }
+  return s;
+}
+
+// ------------------------------------------------------------------ flat
+template <int OP, int EPI, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void k_fwd_flat(const float *a,
+                                                     const float *b,
+                                                     float *out, int64_t n) {
+  constexpr int64_t tile = (int64_t)kBlock * U * VEC;
+  int64_t base = (int64_t)blockIdx.x * tile + (int64_t)threadIdx.x * VEC;
+  if constexpr (VEC == 4) {
+    float4 va[U], vb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t i = base + (int64_t)u * kBlock * 4;
+      if (i + 4 <= n) {
+        va[u] = ld4(a + i);
+        vb[u] = ld4(b + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t i = base + (int64_t)u * kBlock * 4;
+      if (i + 4 <= n) {
+        float4 r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) el(r, k) = fwd32<OP, EPI>(el(va[u], k), el(vb[u], k));
+        st4(out + i, r);
+      } else if (i < n) {
+        for (int64_t j = i; j < n; ++j) out[j] = fwd32<OP, EPI>(a[j], b[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t i = (int64_t)blockIdx.x * tile + (int64_t)u * kBlock + threadIdx.x;
+      if (i < n) out[i] = fwd32<OP, EPI>(a[i], b[i]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------- row
+// Offset of a non-dense operand (strides ss) at flat output index i of a
+// rank <= 3 space.  Fully unrolled so kernel-argument arrays are indexed by
+// constants.
+struct RowArgs {
+  int32_t rank;
+  int64_t n[3];
+  int64_t ss[3];
+  FastDiv fd[3];
+  int64_t numel;
+};
+
+template <typename I>
+__device__ __forceinline__ I row_offset(const RowArgs &ra, I i) {
+  I off = 0;
+  I rest = i;
+#pragma unroll
+  for (int k = 2; k >= 1; --k) {
+    if (k < ra.rank) {
+      I q;
+      if constexpr (sizeof(I) == 4) q = (I)fdiv(ra.fd[k], (uint32_t)rest);
+      else q = rest / (I)ra.n[k];
+      I c = rest - q * (I)ra.n[k];
+      off += c * (I)ra.ss[k];
+      rest = q;
+    }
+  }
+  off += rest * (I)ra.ss[0];
+  return off;
+}
+
+template <int OP, int EPI, int VEC, int SMODE, bool SWAP, typename I>
+__global__ __launch_bounds__(kBlock) void k_fwd_row(const float *big,
+                                                    const float *small,
+                                                    float *out, RowArgs ra) {
+  constexpr int U = 4;
+  constexpr I tile = (I)kBlock * U * VEC;
+  const I n = (I)ra.numel;
+  const I sin = (I)ra.ss[ra.rank - 1];
+  I base = (I)blockIdx.x * tile + (I)threadIdx.x * VEC;
+  if constexpr (VEC == 4) {
+    float4 vb[U], vs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      I i = base + (I)u * kBlock * 4;
+      if (i < n) {
+        vb[u] = ld4(big + i);
+        I off = row_offset<I>(ra, i);
+        if constexpr (SMODE == SM_BCAST) {
+          float s = small[off];
+          vs[u] = make_float4(s, s, s, s);
+        } else if constexpr (SMODE == SM_CONTIG) {
+          vs[u] = ld4(small + off);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) el(vs[u], k) = small[off + (I)k * sin];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      I i = base + (I)u * kBlock * 4;
+      if (i < n) {
+        float4 r;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float x = SWAP ? el(vs[u], k) : el(vb[u], k);
+          float y = SWAP ? el(vb[u], k) : el(vs[u], k);
+          el(r, k) = fwd32<OP, EPI>(x, y);
+        }
+        st4(out + i, r);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      I i = (I)blockIdx.x * tile + (I)u * kBlock + (I)threadIdx.x;
+      if (i < n) {
+        float vbig = big[i];
+        float vsm = small[row_offset<I>(ra, i)];
+        out[i] = SWAP ? fwd32<OP, EPI>(vsm, vbig) : fwd32<OP, EPI>(vbig, vsm);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ tile
+// out[R, C] row-major; T[i, j] at i + j*ld (transposed view); O[i, j] at
+// i*os0 + j*os1.  One 64x64 tile per block: T is read down its contiguous
+// columns into LDS, then rows of the tile are combined with O and written
+// as 128-bit row segments.
+struct TileArgs {
+  int64_t R, C, ld, os0, os1;
+  int64_t tiles_c;
+};
+
+template <int OP, int EPI, int OMODE, bool SWAP>
+__global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
+                                                     const float *oth,
+                                                     float *out, TileArgs ta) {
+  __shared__ float tile[64][65];
+  const int t = threadIdx.x;
+  const int64_t tr_i = blockIdx.x / ta.tiles_c, tr_j = blockIdx.x % ta.tiles_c;
+  const int64_t i0 = tr_i * 64, j0 = tr_j * 64;
+  {
+    const int i = t & 63, jq = t >> 6;
+    const int64_t gi = i0 + i;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int j = jq + 4 * p;
+      const int64_t gj = j0 + j;
+      float v = 0.f;
+      if (gi < ta.R && gj < ta.C) v = tr[gi + gj * ta.ld];
+      tile[j][i] = v;
+    }
+  }
+  __syncthreads();
+  const int m = t & 15, q = t >> 4;
+  const int j = 4 * m;
+  const int64_t gj = j0 + j;
+  if (gj >= ta.C) return;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = q + 16 * p;
+    const int64_t gi = i0 + i;
+    if (gi >= ta.R) continue;
+    float4 vo;
+    const int64_t ooff = gi * ta.os0 + gj * ta.os1;
+    if constexpr (OMODE == SM_BCAST) {
+      float s = oth[ooff];
+      vo = make_float4(s, s, s, s);
+    } else if constexpr (OMODE == SM_CONTIG) {
+      vo = ld4(oth + ooff);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) el(vo, k) = oth[ooff + k * ta.os1];
+    }
+    float4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float vt = tile[j + k][i];
+      float x = SWAP ? el(vo, k) : vt;
+      float y = SWAP ? vt : el(vo, k);
+      el(r, k) = fwd32<OP, EPI>(x, y);
+    }
+    st4(out + gi * ta.C + gj, r);
+  }
+}
+
+// --------------------------------------------------------------- generic
+template <typename I>
+__device__ __forceinline__ void offsets_ab(const Space &sp, I i, I &oa, I &ob) {
+  I rest = i;
+  oa = 0;
+  ob = 0;
+#pragma unroll
+  for (int k = kMaxDims - 1; k >= 1; --k) {
+    if (k < sp.rank) {
+      I q;
+      if constexpr (sizeof(I) == 4) q = (I)fdiv(sp.fd[k], (uint32_t)rest);
+      else q = rest / (I)sp.n[k];
+      I c = rest - q * (I)sp.n[k];
+      oa += c * (I)sp.s[1][k];
+      ob += c * (I)sp.s[2][k];
+      rest = q;
+    }
+  }
+  oa += rest * (I)sp.s[1][0];
+  ob += rest * (I)sp.s[2][0];
+}
+
+template <int OP, int EPI, typename I>
+__global__ __launch_bounds__(kBlock) void k_fwd_generic(const float *a,
+                                                        const float *b,
+                                                        float *out, Space sp,
+                                                        int flat_a, int flat_b,
+                                                        int vec_out) {
+  const I n = (I)sp.numel;
+  const I i0 = ((I)blockIdx.x * kBlock + (I)threadIdx.x) * 4;
+  if (i0 >= n) return;
+  float r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    I i = i0 + k;
+    if (i < n) {
+      I oa, ob;
+      offsets_ab<I>(sp, i, oa, ob);
+      float x = a[flat_a ? i : oa];
+      float y = b[flat_b ? i : ob];
+      r[k] = fwd32<OP, EPI>(x, y);
+    }
+  }
+  if (vec_out && i0 + 4 <= n) {
+    st4(out + i0, make_float4(r[0], r[1], r[2], r[3]));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (i0 + k < n) out[i0 + k] = r[k];
+  }
+}
+
+// -------------------------------------------------------------- launcher
+static inline unsigned grid_of(int64_t n, int64_t per_block) {
+  return (unsigned)((n + per_block - 1) / per_block);
+}
+
+hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
+                      const float *b, float *out, hipStream_t st) {
+  if (p.empty) return hipSuccess;
+  const Canon &c = p.c;
+  return with_op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
+    constexpr int OP = decltype(OPc)::value;
+    constexpr int EPI = decltype(EPIc)::value;
+    ProfScope prof(st, p.kernel);
+    switch (p.kernel) {
+      case K_FWD_FLAT: {
+        constexpr int U = 4;
+        if (p.vec == 4)
+          hipLaunchKernelGGL((k_fwd_flat<OP, EPI, 4, U>), dim3(grid_of(c.numel, kBlock * U * 4)),
+                             dim3(kBlock), 0, st, a, b, out, c.numel);
+        else
+          hipLaunchKernelGGL((k_fwd_flat<OP, EPI, 1, U>), dim3(grid_of(c.numel, kBlock * U)),
+                             dim3(kBlock), 0, st, a, b, out, c.numel);
+        return hipGetLastError();
+      }
+      case K_FWD_ROW: {
+        RowArgs ra{};
+        ra.rank = c.rank;
+        ra.numel = c.numel;
+        int sm = p.swap ? 1 : 2;
+        for (int k = 0; k < 3; ++k) {
+          ra.n[k] = k < c.rank ? c.n[k] : 1;
+          ra.ss[k] = k < c.rank ? c.s[sm][k] : 0;
+          ra.fd[k] = make_fastdiv(ra.n[k] < ((int64_t)1 << 31) ? (uint32_t)ra.n[k] : 1u);
+        }
+        const float *big = p.swap ? b : a;
+        const float *small = p.swap ? a : b;
+        auto go = [&](auto VECc, auto SMc, auto SWc, auto Ic) -> hipError_t {
+          constexpr int VEC = decltype(VECc)::value;
+          constexpr int SM = decltype(SMc)::value;
+          constexpr bool SW = decltype(SWc)::value != 0;
+          using I = std::conditional_t<decltype(Ic)::value != 0, int64_t, int32_t>;
+          hipLaunchKernelGGL((k_fwd_row<OP, EPI, VEC, SM, SW, I>),
+                             dim3(grid_of(c.numel, kBlock * 4 * VEC)), dim3(kBlock), 0, st,
+                             big, small, out, ra);
+          return hipGetLastError();
+        };
+        auto go_i = [&](auto VECc, auto SMc, auto SWc) -> hipError_t {
+          return p.idx64 ? go(VECc, SMc, SWc, IC<1>{}) : go(VECc, SMc, SWc, IC<0>{});
+        };
+        auto go_sw = [&](auto VECc, auto SMc) -> hipError_t {
+          return p.swap ? go_i(VECc, SMc, IC<1>{}) : go_i(VECc, SMc, IC<0>{});
+        };
+        if (p.vec == 1) return go_sw(IC<1>{}, IC<SM_GATHER>{});
+        switch (p.small_mode) {
+          case SM_BCAST: return go_sw(IC<4>{}, IC<SM_BCAST>{});
+          case SM_CONTIG: return go_sw(IC<4>{}, IC<SM_CONTIG>{});
+          default: return go_sw(IC<4>{}, IC<SM_GATHER>{});
+        }
+      }
+      case K_FWD_TILE: {
+        int tr_op = p.swap ? 2 : 1, ot_op = p.swap ? 1 : 2;
+        const float *tr = p.swap ? b : a;
+        const float *ot = p.swap ? a : b;
+        TileArgs ta{};
+        ta.R = c.n[0];
+        ta.C = c.n[1];
+        ta.ld = c.s[tr_op][1];
+        ta.os0 = c.s[ot_op][0];
+        ta.os1 = c.s[ot_op][1];
+        ta.tiles_c = (ta.C + 63) / 64;
+        unsigned grid = (unsigned)(((ta.R + 63) / 64) * ta.tiles_c);
+        int om = SM_GATHER;
+        if (ta.os1 == 0) om = SM_BCAST;
+        else if (ta.os1 == 1 && ta.os0 % 4 == 0 && ((uintptr_t)ot & 15u) == 0) om = SM_CONTIG;
+        auto go = [&](auto OMc, auto SWc) -> hipError_t {
+          constexpr int OM = decltype(OMc)::value;
+          constexpr bool SW = decltype(SWc)::value != 0;
+          hipLaunchKernelGGL((k_fwd_tile<OP, EPI, OM, SW>), dim3(grid), dim3(kBlock), 0, st,
+                             tr, ot, out, ta);
+          return hipGetLastError();
+        };
+        auto go_sw = [&](auto OMc) -> hipError_t {
+          return p.swap ? go(OMc, IC<1>{}) : go(OMc, IC<0>{});
+        };
+        if (om == SM_BCAST) return go_sw(IC<SM_BCAST>{});
+        if (om == SM_CONTIG) return go_sw(IC<SM_CONTIG>{});
+        return go_sw(IC<SM_GATHER>{});
+      }
+      default: {
+        Space sp = make_space(c);
+        int fa = 1, fb = 1;
+        for (int k = 0; k < c.rank; ++k) {
+          if (c.s[1][k] != c.s[0][k]) fa = 0;
+          if (c.s[2][k] != c.s[0][k]) fb = 0;
+        }
+        unsigned grid = grid_of(c.numel, kBlock * 4);
+        if (p.idx64)
+          hipLaunchKernelGGL((k_fwd_generic<OP, EPI, int64_t>), dim3(grid), dim3(kBlock), 0, st,
+                             a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
+        else
+          hipLaunchKernelGGL((k_fwd_generic<OP, EPI, int32_t>), dim3(grid), dim3(kBlock), 0, st,
+                             a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
+        return hipGetLastError();
+      }
+    }
+  });
+}
+
+}  // namespace zk

@@ -1,0 +1,53 @@
+// zk_kernels.h -- kernel argument blocks (passed by value, like the book's
+// fixed 8-dim DimsArg in the GPU chapter, "kernel dispatch") and the host
+// launchers implemented in the .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zk.h"
+#include "zk_plan.h"
+
+namespace zk {
+
+// Canonical iteration space handed to a kernel.
+struct Space {
+  int32_t rank;
+  int64_t n[kMaxDims];
+  int64_t s[kMaxOps][kMaxDims];
+  FastDiv fd[kMaxDims];  // divisors n[k] (used when 32-bit indexing)
+  int64_t numel;
+};
+
+// A reduction's split of the canonical dims into kept (K) and reduced (R)
+// dims for the gather kernel; dims listed outer -> inner.
+struct RedDims {
+  int32_t nk, nr;
+  int32_t kdim[kMaxDims], rdim[kMaxDims];
+  FastDiv kfd[kMaxDims], rfd[kMaxDims];
+};
+
+Space make_space(const Canon &c);
+
+// Brackets one kernel launch with a HIP event pair on its stream while
+// zk_profile_start() is in effect; does nothing otherwise.
+struct ProfScope {
+  ProfScope(hipStream_t st, int32_t kernel);
+  ~ProfScope();
+  int slot;
+  hipStream_t st;
+};
+
+hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
+                      const float *b, float *out, hipStream_t st);
+
+hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
+                      const float *a, const float *b, float *grad_a,
+                      const float *acc_a, float *grad_b, const float *acc_b,
+                      void *ws, hipStream_t st);
+
+hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
+                         void *ws, hipStream_t st);
+
+}  // namespace zk

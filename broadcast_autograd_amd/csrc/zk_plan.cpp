@@ -1,0 +1,538 @@
+// zk_plan.cpp -- host-side canonicaliser and launch planner (see zk_plan.h).
+#include "zk_plan.h"
+
+#include <algorithm>
+#include <cstring>
+
+namespace zk {
+
+const char *kernel_name(int32_t k) {
+  static const char *names[K_COUNT] = {
+      "fwd_flat",       "fwd_row",       "fwd_tile",   "fwd_generic",
+      "bwd_ew_flat",    "bwd_ew_generic", "red_col",   "red_row",
+      "red_tile",       "red_generic",   "red_final"};
+  if (k < 0 || k >= K_COUNT) return "none";
+  return names[k];
+}
+
+FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{d, 0u, 0u};
+  if (d <= 1) return f;  // m = 0, l = 0: q = n
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;  // l = ceil(log2 d)
+  uint64_t m = ((((1ull << l) - d) << 32) / d) + 1;
+  f.m = (uint32_t)m;
+  f.l = l;
+  return f;
+}
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+zk_status check_desc(const zk_desc *d) {
+  if (!d) return ZK_ERR_NULL;
+  if (d->rank < 0 || d->rank > kMaxDims) return ZK_ERR_RANK;
+  for (int k = 0; k < d->rank; ++k)
+    if (d->sizes[k] < 0) return ZK_ERR_BAD_SIZE;
+  for (int k = 0; k < d->rank; ++k)
+    if (d->strides[k] < 0) return ZK_ERR_BAD_STRIDE;
+  return ZK_OK;
+}
+
+zk_status broadcast_shape(int ra, const int64_t *na, int rb, const int64_t *nb,
+                          int *ro, int64_t *no) {
+  if (ra < 0 || rb < 0 || ra > kMaxDims || rb > kMaxDims) return ZK_ERR_RANK;
+  if ((ra && !na) || (rb && !nb)) return ZK_ERR_NULL;
+  for (int k = 0; k < ra; ++k) if (na[k] < 0) return ZK_ERR_BAD_SIZE;
+  for (int k = 0; k < rb; ++k) if (nb[k] < 0) return ZK_ERR_BAD_SIZE;
+  int r = std::max(ra, rb);
+  int64_t tmp[kMaxDims];
+  for (int k = 0; k < r; ++k) {
+    int ka = k - (r - ra), kb = k - (r - rb);
+    int64_t x = ka >= 0 ? na[ka] : 1, y = kb >= 0 ? nb[kb] : 1;
+    if (x == y) tmp[k] = x;
+    else if (x == 1) tmp[k] = y;
+    else if (y == 1) tmp[k] = x;
+    else return ZK_ERR_BROADCAST;
+  }
+  *ro = r;
+  for (int k = 0; k < r; ++k) no[k] = tmp[k];
+  return ZK_OK;
+}
+
+void align_strides(const zk_desc &d, int r, int64_t *st) {
+  for (int k = 0; k < r; ++k) {
+    int kx = k - (r - d.rank);
+    st[k] = (kx < 0 || d.sizes[kx] == 1) ? 0 : d.strides[kx];
+  }
+}
+
+void align_dense(const zk_desc &d, int r, int64_t *st) {
+  int64_t dense[kMaxDims];
+  int64_t s = 1;
+  for (int k = d.rank - 1; k >= 0; --k) {
+    dense[k] = s;
+    s *= d.sizes[k];
+  }
+  for (int k = 0; k < r; ++k) {
+    int kx = k - (r - d.rank);
+    st[k] = (kx < 0 || d.sizes[kx] == 1) ? 0 : dense[kx];
+  }
+}
+
+Canon canonicalise(int r, const int64_t *n, int nops,
+                   const int64_t (*st)[kMaxDims]) {
+  Canon c;
+  c.nops = nops;
+  int64_t numel = 1;
+  for (int k = 0; k < r; ++k) numel *= n[k];
+  c.numel = numel;
+  if (numel == 0) {  // nothing to iterate: a single empty dim
+    c.rank = 1;
+    c.n[0] = 0;
+    return c;
+  }
+  // Walk from the innermost dim outwards, keeping dims of size > 1 and
+  // merging a dim into the current innermost kept one when every operand
+  // steps over it contiguously.
+  int64_t rn[kMaxDims], rs[kMaxOps][kMaxDims];
+  int m = 0;  // kept dims, stored inner -> outer
+  for (int k = r - 1; k >= 0; --k) {
+    if (n[k] == 1) continue;
+    if (m > 0) {
+      bool merge = true;
+      for (int o = 0; o < nops; ++o)
+        if (st[o][k] != rs[o][m - 1] * rn[m - 1]) { merge = false; break; }
+      if (merge) {
+        rn[m - 1] *= n[k];
+        continue;
+      }
+    }
+    rn[m] = n[k];
+    for (int o = 0; o < nops; ++o) rs[o][m] = st[o][k];
+    ++m;
+  }
+  if (m == 0) {  // all dims of size 1 (or rank 0): one element
+    c.rank = 1;
+    c.n[0] = 1;
+    for (int o = 0; o < nops; ++o) c.s[o][0] = 0;
+    c.s[0][0] = 1;
+    return c;
+  }
+  c.rank = m;
+  for (int k = 0; k < m; ++k) {
+    c.n[k] = rn[m - 1 - k];
+    for (int o = 0; o < nops; ++o) c.s[o][k] = rs[o][m - 1 - k];
+  }
+  return c;
+}
+
+void byte_extent(const void *p, const zk_desc &d, uintptr_t *lo, uintptr_t *hi) {
+  uintptr_t base = (uintptr_t)p;
+  int64_t last = 0;
+  for (int k = 0; k < d.rank; ++k) {
+    if (d.sizes[k] == 0) { *lo = *hi = base; return; }
+    last += (d.sizes[k] - 1) * d.strides[k];
+  }
+  *lo = base;
+  *hi = base + (uintptr_t)(last + 1) * 4u;
+}
+
+void byte_extent_dense(const void *p, int64_t numel, uintptr_t *lo,
+                       uintptr_t *hi) {
+  *lo = (uintptr_t)p;
+  *hi = (uintptr_t)p + (uintptr_t)numel * 4u;
+}
+
+bool overlaps(uintptr_t alo, uintptr_t ahi, uintptr_t blo, uintptr_t bhi) {
+  if (alo == ahi || blo == bhi) return false;
+  return alo < bhi && blo < ahi;
+}
+
+static int64_t numel_of(const zk_desc &d) {
+  int64_t m = 1;
+  for (int k = 0; k < d.rank; ++k) m *= d.sizes[k];
+  return m;
+}
+
+static bool is_flat(const Canon &c, int o) {
+  for (int k = 0; k < c.rank; ++k)
+    if (c.s[o][k] != c.s[0][k]) return false;
+  return true;
+}
+
+static int64_t max_offset(const Canon &c, int o) {
+  int64_t m = 0;
+  for (int k = 0; k < c.rank; ++k)
+    if (c.n[k] > 0) m += (c.n[k] - 1) * c.s[o][k];
+  return m;
+}
+
+static bool needs_idx64(const Canon &c) {
+  // margin: kernels form indices up to one tile past the end
+  const int64_t lim = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+  if (c.numel >= lim) return true;
+  for (int o = 0; o < c.nops; ++o)
+    if (max_offset(c, o) >= lim) return true;
+  return false;
+}
+
+static bool al16(uintptr_t p) { return (p & 15u) == 0; }
+
+// Transposed rank-2 operand: x[i, j] at i * 1 + j * ld.
+static bool is_transposed2(const Canon &c, int o) {
+  return c.rank == 2 && c.s[o][0] == 1 && c.s[o][1] >= c.n[0];
+}
+
+bool rule_reads_a(zk_op op, zk_epi epi, int which) {
+  if (epi == ZK_EPI_GELU) return true;
+  if (op == ZK_MUL) return which == 1;
+  if (op == ZK_DIV) return which == 1;
+  return false;
+}
+
+bool rule_reads_b(zk_op op, zk_epi epi, int which) {
+  if (epi == ZK_EPI_GELU) return true;
+  if (op == ZK_MUL) return which == 0;
+  if (op == ZK_DIV) return true;
+  return false;
+}
+
+// ------------------------------------------------------------- forward
+zk_status plan_fwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
+                   uintptr_t pa, uintptr_t pb, uintptr_t pout, FwdPlan *p) {
+  (void)op;
+  (void)epi;
+  int r;
+  int64_t n[kMaxDims];
+  zk_status s = broadcast_shape(da.rank, da.sizes, db.rank, db.sizes, &r, n);
+  if (s) return s;
+  int64_t st[kMaxOps][kMaxDims];
+  {
+    int64_t d = 1;
+    for (int k = r - 1; k >= 0; --k) { st[0][k] = d; d *= n[k]; }
+  }
+  align_strides(da, r, st[1]);
+  align_strides(db, r, st[2]);
+  p->c = canonicalise(r, n, 3, st);
+  const Canon &c = p->c;
+  if (c.numel == 0) {
+    p->empty = true;
+    p->kernel = K_NONE;
+    return ZK_OK;
+  }
+  p->idx64 = needs_idx64(c);
+  bool fa = is_flat(c, 1), fb = is_flat(c, 2);
+  int64_t inner = c.n[c.rank - 1];
+  if (fa && fb) {
+    p->kernel = K_FWD_FLAT;
+    p->vec = (al16(pa) && al16(pb) && al16(pout)) ? 4 : 1;
+    return ZK_OK;
+  }
+  if ((fa || fb) && c.rank <= 3) {
+    p->kernel = K_FWD_ROW;
+    p->swap = !fa;  // swap: the dense operand is b
+    int sm = p->swap ? 1 : 2;
+    uintptr_t psmall = p->swap ? pa : pb, pbig = p->swap ? pb : pa;
+    bool v4 = inner % 4 == 0 && al16(pbig) && al16(pout);
+    p->vec = v4 ? 4 : 1;
+    int64_t s0 = c.s[sm][c.rank - 1];
+    if (s0 == 0) {
+      p->small_mode = SM_BCAST;
+    } else {
+      bool contig = s0 == 1 && al16(psmall);
+      for (int k = 0; k + 1 < c.rank; ++k)
+        if (c.s[sm][k] % 4 != 0) contig = false;
+      p->small_mode = contig ? SM_CONTIG : SM_GATHER;
+    }
+    return ZK_OK;
+  }
+  if (is_transposed2(c, 1) || is_transposed2(c, 2)) {
+    p->kernel = K_FWD_TILE;
+    p->swap = !is_transposed2(c, 1);
+    p->vec = (c.n[1] % 4 == 0 && al16(pout)) ? 4 : 1;
+    if (p->vec == 4) return ZK_OK;
+  }
+  p->kernel = K_FWD_GENERIC;
+  p->swap = false;
+  p->vec = (al16(pout) && (!fa || al16(pa)) && (!fb || al16(pb))) ? 4 : 1;
+  return ZK_OK;
+}
+
+// ------------------------------------------------------------- backward
+
+// Reduction pattern of operand stride set `o` over the canonical dims:
+// bit k set when dim k is kept (stride != 0).
+static unsigned kept_mask(const Canon &c, int o) {
+  unsigned m = 0;
+  for (int k = 0; k < c.rank; ++k)
+    if (c.s[o][k] != 0) m |= 1u << k;
+  return m;
+}
+
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Sizing of a generic (gather) reduction: K kept elements, `red` reduced
+// elements each.  The split depends on the shapes only.
+static void size_generic(RedPlan *rp, int64_t K, int64_t red) {
+  rp->kernel = K_RED_GENERIC;
+  rp->kept = K;
+  rp->red = red;
+  if (red <= 0) {
+    rp->partials = 0;
+    rp->chunk = 0;
+    return;
+  }
+  int64_t P = std::max<int64_t>(1, ceil_div(65536, std::max<int64_t>(K, 1)));
+  P = std::min<int64_t>(P, ceil_div(red, 8));
+  P = std::max<int64_t>(P, 1);
+  int64_t chunk = ceil_div(red, P);
+  rp->chunk = chunk;
+  rp->partials = ceil_div(red, chunk);
+}
+
+// Try the fast stage-1 classes for the reduced operand stride set `o`
+// (grad layout) with `big` the dense operand id (or -1 if none is read).
+// Requires the source (op 0) to be dense.
+static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
+                      bool src_flat, bool aligned, RedPlan *rp) {
+  if (!src_flat || !aligned) return false;
+  unsigned km = kept_mask(c, o);
+  int R = c.rank;
+  int64_t inner = c.n[R - 1];
+  // [R, K] : column sums
+  if (R == 2 && km == 2u && c.s[o][1] == 1) {
+    if (big_transposed) {
+      if (c.n[1] % 4 != 0) return false;
+      rp->kernel = K_RED_TILE;
+      rp->kept = c.n[1];
+      rp->red = c.n[0];
+      int64_t tiles_c = ceil_div(c.n[1], 64);
+      int64_t rows64 = ceil_div(c.n[0], 64);
+      int64_t P = std::max<int64_t>(1, ceil_div(2048, tiles_c));
+      P = std::min<int64_t>(P, rows64);
+      int64_t rc = ceil_div(rows64, P) * 64;
+      rp->chunk = rc;
+      rp->partials = ceil_div(c.n[0], rc);
+      return true;
+    }
+    if (big_op >= 0 && !is_flat(c, big_op)) return false;
+    if (inner % 4 != 0) return false;
+    rp->kernel = K_RED_COL;
+    rp->kept = c.n[1];
+    rp->red = c.n[0];
+    int64_t colblocks = ceil_div(c.n[1], 256);
+    int64_t P = std::max<int64_t>(1, ceil_div(2048, colblocks));
+    P = std::min<int64_t>(P, std::max<int64_t>(1, ceil_div(c.n[0], 16)));
+    int64_t rc = ceil_div(c.n[0], P);
+    rp->chunk = rc;
+    rp->partials = ceil_div(c.n[0], rc);
+    return true;
+  }
+  if (big_transposed) return false;
+  if (big_op >= 0 && !is_flat(c, big_op)) return false;
+  // [R0], [K, R0], [R1, K, R0] : inner dim reduced
+  bool pat = (R == 1 && km == 0u) ||
+             (R == 2 && km == 1u && c.s[o][0] == 1) ||
+             (R == 3 && km == 2u && c.s[o][1] == 1);
+  if (!pat || inner % 4 != 0 || inner < 256) return false;
+  int64_t rows = c.numel / inner;               // (R1, K) rows
+  int64_t K = (R == 1) ? 1 : c.n[R - 2];
+  int64_t R1 = rows / K;
+  int64_t NC = std::max<int64_t>(1, ceil_div(8192, rows));
+  NC = std::min<int64_t>(NC, std::max<int64_t>(1, inner / 1024));
+  int64_t CL = ceil_div(ceil_div(inner, NC), 4) * 4;
+  NC = ceil_div(inner, CL);
+  rp->kernel = K_RED_ROW;
+  rp->kept = K;
+  rp->red = R1 * inner;
+  rp->chunk = CL;
+  rp->partials = R1 * NC;
+  return true;
+}
+
+static void finish_workspace(BwdPlan *p) {
+  size_t off = 0;
+  for (int i = 0; i < p->nred; ++i) {
+    p->red[i].ws_offset = off;
+    off += round256((size_t)p->red[i].partials * (size_t)p->red[i].kept * 8u);
+  }
+  p->workspace = off;
+}
+
+zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
+                   bool want_a, bool want_b, uintptr_t pg, uintptr_t pa,
+                   uintptr_t pb, uintptr_t pga, uintptr_t pgb,
+                   uintptr_t pacc_a, uintptr_t pacc_b, BwdPlan *p) {
+  int r;
+  int64_t n[kMaxDims];
+  zk_status s = broadcast_shape(da.rank, da.sizes, db.rank, db.sizes, &r, n);
+  if (s) return s;
+  int64_t st[kMaxOps][kMaxDims];
+  {
+    int64_t d = 1;
+    for (int k = r - 1; k >= 0; --k) { st[0][k] = d; d *= n[k]; }
+  }
+  align_strides(da, r, st[1]);
+  align_strides(db, r, st[2]);
+  align_dense(da, r, st[3]);
+  align_dense(db, r, st[4]);
+  p->c = canonicalise(r, n, 5, st);
+  const Canon &c = p->c;
+  p->want[0] = want_a;
+  p->want[1] = want_b;
+  int64_t ne[2] = {numel_of(da), numel_of(db)};
+  p->nred = 0;
+  if (c.numel == 0) {
+    // Sums over nothing: a non-empty gradient is its acc (or zeros).
+    p->empty_space = true;
+    for (int w = 0; w < 2; ++w) {
+      if (!p->want[w] || ne[w] == 0) continue;
+      RedPlan &rp = p->red[p->nred++];
+      size_generic(&rp, ne[w], 0);
+      rp.which = w;
+    }
+    finish_workspace(p);
+    return ZK_OK;
+  }
+  p->idx64 = needs_idx64(c);
+  for (int w = 0; w < 2; ++w) p->full[w] = ne[w] == c.numel;
+  bool reduced[2] = {want_a && !p->full[0], want_b && !p->full[1]};
+  bool fa = is_flat(c, 1), fb = is_flat(c, 2);
+
+  // Element-wise part: gradients of operands with the full shape.
+  auto ew_kernel = [&](bool wa, bool wb) {
+    bool ra = (wa && rule_reads_a(op, epi, 0)) || (wb && rule_reads_a(op, epi, 1));
+    bool rb = (wa && rule_reads_b(op, epi, 0)) || (wb && rule_reads_b(op, epi, 1));
+    bool flat = (!ra || fa) && (!rb || fb);
+    bool al = al16(pg) && (!ra || al16(pa)) && (!rb || al16(pb)) &&
+              (!wa || (al16(pga) && al16(pacc_a))) &&
+              (!wb || (al16(pgb) && al16(pacc_b)));
+    p->vec = al ? 4 : 1;
+    return flat ? K_BWD_EW_FLAT : K_BWD_EW_GENERIC;
+  };
+
+  if (!reduced[0] && !reduced[1]) {
+    if (want_a || want_b) {
+      p->ew_kernel = ew_kernel(want_a, want_b);
+      p->ew_write[0] = want_a;
+      p->ew_write[1] = want_b;
+    }
+    finish_workspace(p);
+    return ZK_OK;
+  }
+
+  if (reduced[0] != reduced[1]) {
+    int sw = reduced[0] ? 0 : 1;  // reduced operand
+    int bw = 1 - sw;              // the other (full, or not wanted)
+    bool big_full = p->full[bw];
+    bool big_read = rule_reads_a(op, epi, sw) && bw == 0;
+    big_read = big_read || (rule_reads_b(op, epi, sw) && bw == 1);
+    bool big_write = p->want[bw];
+    if (big_write) {
+      bool rd = (bw == 0) ? rule_reads_a(op, epi, 0) : rule_reads_b(op, epi, 1);
+      big_read = big_read || rd;
+    }
+    // The fused classes need the other operand to have the full shape
+    // (so its gradient and values walk with the upstream grad).
+    if (big_full || (!big_read && !big_write)) {
+      int big_op = (big_read && big_full) ? 1 + bw : -1;
+      bool big_tr = big_read && big_full && is_transposed2(c, 1 + bw);
+      uintptr_t pbig = bw == 0 ? pa : pb;
+      uintptr_t pgbig = bw == 0 ? pga : pgb;
+      uintptr_t paccbig = bw == 0 ? pacc_a : pacc_b;
+      bool aligned = al16(pg) && (!big_read || big_tr || al16(pbig)) &&
+                     (!big_write || (al16(pgbig) && al16(paccbig)));
+      RedPlan rp;
+      if (size_fast(c, 3 + sw, big_op, big_tr, true, aligned, &rp)) {
+        rp.which = sw;
+        p->red[p->nred++] = rp;
+        p->fused_big = big_write;
+        p->vec = 4;
+        finish_workspace(p);
+        return ZK_OK;
+      }
+    }
+    // Fallback: generic gather for the reduced gradient, element-wise
+    // kernel for the full one.
+    RedPlan &rp = p->red[p->nred++];
+    size_generic(&rp, ne[sw], c.numel / ne[sw]);
+    rp.which = sw;
+    if (big_write && big_full) {
+      p->ew_kernel = ew_kernel(bw == 0, bw == 1);
+      p->ew_write[bw] = true;
+    } else if (big_write) {
+      RedPlan &rq = p->red[p->nred++];
+      size_generic(&rq, ne[bw], c.numel / ne[bw]);
+      rq.which = bw;
+    }
+    finish_workspace(p);
+    return ZK_OK;
+  }
+  // Both operands broadcast: one gather reduction each.
+  for (int w = 0; w < 2; ++w) {
+    RedPlan &rp = p->red[p->nred++];
+    size_generic(&rp, ne[w], c.numel / ne[w]);
+    rp.which = w;
+  }
+  finish_workspace(p);
+  return ZK_OK;
+}
+
+zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
+                      uintptr_t pin, uintptr_t pout, BwdPlan *p) {
+  (void)pout;
+  int r;
+  int64_t n[kMaxDims];
+  zk_status s = broadcast_shape(din.rank, din.sizes, rout, nout, &r, n);
+  if (s == ZK_ERR_BROADCAST) return ZK_ERR_SHAPE;
+  if (s) return s;
+  if (r != din.rank) return ZK_ERR_SHAPE;
+  for (int k = 0; k < r; ++k)
+    if (n[k] != din.sizes[k]) return ZK_ERR_SHAPE;
+  zk_desc dt{};
+  dt.rank = rout;
+  for (int k = 0; k < rout; ++k) dt.sizes[k] = nout[k];
+  int64_t st[kMaxOps][kMaxDims] = {};
+  {
+    int64_t d = 1;
+    for (int k = r - 1; k >= 0; --k) { st[1][k] = d; d *= n[k]; }  // dense in
+  }
+  align_strides(din, r, st[0]);
+  align_dense(dt, r, st[4]);
+  // ops: 0 = input strides, 1 = dense layout of the input shape (to test
+  // flatness), 2/3 unused, 4 = target.
+  p->c = canonicalise(r, n, 5, st);
+  const Canon &c = p->c;
+  p->want[0] = false;
+  p->want[1] = true;
+  int64_t K = numel_of(dt);
+  p->nred = 0;
+  if (c.numel == 0) {
+    p->empty_space = true;
+    if (K > 0) {
+      RedPlan &rp = p->red[p->nred++];
+      size_generic(&rp, K, 0);
+      rp.which = 1;
+    }
+    finish_workspace(p);
+    return ZK_OK;
+  }
+  p->idx64 = needs_idx64(c);
+  bool src_flat = true;
+  for (int k = 0; k < c.rank; ++k)
+    if (c.s[0][k] != c.s[1][k]) src_flat = false;
+  RedPlan rp;
+  if (K < c.numel && size_fast(c, 4, -1, false, src_flat, al16(pin), &rp)) {
+    rp.which = 1;
+    p->red[p->nred++] = rp;
+    p->vec = 4;
+  } else {
+    RedPlan &q = p->red[p->nred++];
+    size_generic(&q, K, c.numel / K);
+    q.which = 1;
+  }
+  finish_workspace(p);
+  return ZK_OK;
+}
+
+}  // namespace zk

@@ -1,0 +1,139 @@
+// zk_plan.h -- host-side shape/stride canonicaliser and launch planner.
+//
+// Pure C++ (no HIP): it validates descriptors, computes the broadcast shape,
+// turns every operand into right-aligned strides over that shape (stride 0
+// where an operand is repeated), drops size-1 dims, merges adjacent dims that
+// every operand walks contiguously, and picks the kernel class for the
+// resulting canonical form.  Nothing here touches a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "zk.h"
+
+namespace zk {
+
+constexpr int kMaxDims = ZK_MAX_DIMS;
+constexpr int kMaxOps = 5;
+
+// Kernel classes (ids reported by zk_plan_describe).
+enum KernelClass : int32_t {
+  K_NONE = -1,
+  K_FWD_FLAT = 0,     // every operand dense in the output layout
+  K_FWD_ROW = 1,      // one dense operand, the other rank <= 3 strided
+  K_FWD_TILE = 2,     // a transposed rank-2 operand, staged through LDS
+  K_FWD_GENERIC = 3,  // anything (rank <= 8)
+  K_BWD_EW_FLAT = 4,  // backward, no reduction, dense operands
+  K_BWD_EW_GENERIC = 5,
+  K_RED_COL = 6,      // fused backward stage 1, pattern [R, K]
+  K_RED_ROW = 7,      // fused backward stage 1, pattern [.., K, R] (inner reduced)
+  K_RED_TILE = 8,     // fused backward stage 1, [R, K] with a transposed operand
+  K_RED_GENERIC = 9,  // gather stage 1, any pattern
+  K_RED_FINAL = 10,   // stage 2: fixed-order sum of the partials
+  K_COUNT = 11
+};
+
+const char *kernel_name(int32_t k);
+
+// Inner-dim access mode of a non-dense operand in the ROW classes.
+enum SmallMode : int32_t { SM_BCAST = 0, SM_CONTIG = 1, SM_GATHER = 2 };
+
+// Magic-number division for 0 <= n < 2^31 and 1 <= d < 2^31
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994, round-up variant):
+//   l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+//   q = (umulhi(n, m) + n) >> l.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+FastDiv make_fastdiv(uint32_t d);
+inline uint32_t fastdiv_eval(const FastDiv &f, uint32_t n) {
+  uint32_t hi = (uint32_t)(((uint64_t)n * f.m) >> 32);
+  return (hi + n) >> f.l;
+}
+
+// A canonical iteration space: rank dims, sizes n, one stride set per
+// operand (elements).  ops[0] is always the dense output / upstream grad.
+struct Canon {
+  int rank = 0;
+  int nops = 0;
+  int64_t n[kMaxDims] = {};
+  int64_t s[kMaxOps][kMaxDims] = {};
+  int64_t numel = 0;
+};
+
+// Right-aligns `d` to the rank-r shape `out`: stride 0 where d's dim is
+// missing or has size 1.
+void align_strides(const zk_desc &d, int r, int64_t *st);
+// Dense row-major strides of d's own shape, right-aligned the same way.
+void align_dense(const zk_desc &d, int r, int64_t *st);
+// Drop size-1 dims and merge dim k into k+1 when every operand has
+// s[k] == s[k+1] * n[k+1].  A zero-size or rank-0 space becomes rank 1.
+Canon canonicalise(int r, const int64_t *n, int nops,
+                   const int64_t (*st)[kMaxDims]);
+
+zk_status check_desc(const zk_desc *d);
+zk_status broadcast_shape(int ra, const int64_t *na, int rb, const int64_t *nb,
+                          int *ro, int64_t *no);
+// [lo, hi) byte extent an operand's elements span (hi == lo when empty).
+void byte_extent(const void *p, const zk_desc &d, uintptr_t *lo, uintptr_t *hi);
+void byte_extent_dense(const void *p, int64_t numel, uintptr_t *lo,
+                       uintptr_t *hi);
+bool overlaps(uintptr_t alo, uintptr_t ahi, uintptr_t blo, uintptr_t bhi);
+
+// ---------------------------------------------------------------- forward
+struct FwdPlan {
+  Canon c;            // ops: 0 out, 1 a, 2 b
+  int32_t kernel = K_NONE;
+  bool empty = false;
+  bool idx64 = false;
+  int vec = 1;
+  bool swap = false;  // ROW/TILE: the dense / transposed operand is b
+  int32_t small_mode = SM_GATHER;
+};
+zk_status plan_fwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
+                   uintptr_t pa, uintptr_t pb, uintptr_t pout, FwdPlan *p);
+
+// --------------------------------------------------------------- backward
+// One stage-1 reduction for one operand's gradient.
+struct RedPlan {
+  int32_t kernel = K_NONE;   // K_RED_*
+  int which = -1;            // 0 = a, 1 = b (reduce_to_shape: 1 = target)
+  int64_t kept = 0;          // K: elements of the reduced gradient
+  int64_t partials = 0;      // P: partial sums per kept element
+  int64_t chunk = 0;         // rows (COL/TILE) or elements (ROW/GENERIC) per partial
+  int64_t red = 0;           // reduced elements per kept element
+  size_t ws_offset = 0;      // byte offset of its partials in the workspace
+};
+
+struct BwdPlan {
+  Canon c;                 // ops: 0 grad, 1 a, 2 b, 3 grad_a, 4 grad_b
+  bool empty_space = false;  // broadcast shape has no elements
+  bool want[2] = {false, false};
+  bool full[2] = {false, false};   // operand has the full broadcast shape
+  bool idx64 = false;
+  int vec = 1;
+  int32_t ew_kernel = K_NONE;      // element-wise kernel for full grads
+  bool ew_write[2] = {false, false};
+  int nred = 0;
+  RedPlan red[2];
+  size_t workspace = 0;
+  // fused stage 1 writes the full operand's gradient too
+  bool fused_big = false;
+};
+zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
+                   bool want_a, bool want_b, uintptr_t pg, uintptr_t pa,
+                   uintptr_t pb, uintptr_t pga, uintptr_t pgb,
+                   uintptr_t pacc_a, uintptr_t pacc_b, BwdPlan *p);
+
+// reduce_to_shape: ops 0 = input (any strides), 1 = unused, 2 = unused,
+// 3 = unused, 4 = target dense-aligned.  Reuses BwdPlan with which = 1.
+zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
+                      uintptr_t pin, uintptr_t pout, BwdPlan *p);
+
+// Operands the local rule of `op` (with `epi`) reads for grad `which`.
+bool rule_reads_a(zk_op op, zk_epi epi, int which);
+bool rule_reads_b(zk_op op, zk_epi epi, int which);
+
+}  // namespace zk

@@ -1,0 +1,229 @@
+"""The five workloads as sequences of library calls (forward, then backward).
+
+Each workload holds its device inputs, preallocated outputs and workspaces, so
+a step only issues ``zk`` calls.  The backward replays by hand the graph the
+"Zero" book builds (Autograd chapter): add hands its upstream gradient to both
+inputs, so a gradient that passes through an add is the same buffer (no
+copy), and a tensor reached along two paths gets the second path accumulated
+onto the first (``acc``).
+
+Algorithmic bytes of a call = 4 x (distinct elements of every input the call
+reads + every element it writes); a repeated operand counts once, and an acc
+that is the same buffer as the upstream gradient is not counted twice.
+"""
+import numpy as np
+
+from . import workloads as W
+from . import zk
+
+
+def _n(shape):
+    return int(np.prod(shape, dtype=np.int64))
+
+
+class Call:
+    def __init__(self, name, kind, fn, reads, writes):
+        self.name, self.kind, self.fn = name, kind, fn
+        self.bytes = 4 * (sum(reads) + sum(writes))
+
+    def __call__(self):
+        return self.fn()
+
+
+class Workload:
+    """Base: ``calls`` lists Call objects in step order."""
+    name = ""
+
+    def run(self):
+        for c in self.calls:
+            c()
+
+    @property
+    def fwd_calls(self):
+        return [c for c in self.calls if c.kind == "fwd"]
+
+    @property
+    def bwd_calls(self):
+        return [c for c in self.calls if c.kind == "bwd"]
+
+    def step_bytes(self, kind=None):
+        return sum(c.bytes for c in self.calls if kind is None or c.kind == kind)
+
+
+def _ws(bytes_, torch):
+    return torch.empty(max(256, int(bytes_)), dtype=torch.uint8, device="cuda")
+
+
+class XYPlusX(Workload):
+    """z = x*y + x with x[64,128,256], y[128,1]."""
+    name = "xy_plus_x"
+
+    def __init__(self, host=None, scale=1):
+        import torch
+        h = host or W.xy_plus_x(scale)
+        self.host = h
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in h.items()}
+        self.x, self.y, self.g = d["x"], d["y"], d["g"]
+        e = torch.empty_like
+        self.t, self.z = e(self.x), e(self.x)
+        self.grad_x, self.grad_y = e(self.x), e(self.y)
+        self.ws = _ws(zk.bwd_workspace_bytes("mul", self.x, self.y), torch)
+        nx, ny = _n(self.x.shape), _n(self.y.shape)
+        self.calls = [
+            Call("mul(x,y)->t", "fwd",
+                 lambda: zk.binary_fwd("mul", self.x, self.y, out=self.t), [nx, ny], [nx]),
+            Call("add(t,x)->z", "fwd",
+                 lambda: zk.binary_fwd("add", self.t, self.x, out=self.z), [nx, nx], [nx]),
+            # add passes g to t and to x; mul's rule then adds x's second path
+            Call("mul_bwd(g;x,y)->grad_x(acc=g),grad_y", "bwd",
+                 lambda: zk.binary_bwd("mul", self.g, self.x, self.y, grad_a=self.grad_x,
+                                       grad_b=self.grad_y, acc_a=self.g, workspace=self.ws),
+                 [nx, nx, ny], [nx, ny]),
+        ]
+
+
+class MLPBiasGelu(Workload):
+    """y = GeLU(act[4096,1024] + bias[1024])."""
+    name = "mlp_bias_gelu"
+
+    def __init__(self, host=None, rows=4096, cols=1024):
+        import torch
+        h = host or W.mlp_bias_gelu(rows, cols)
+        self.host = h
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in h.items()}
+        self.act, self.bias, self.g = d["act"], d["bias"], d["g"]
+        self.y = torch.empty_like(self.act)
+        self.grad_act = torch.empty_like(self.act)
+        self.grad_bias = torch.empty_like(self.bias)
+        self.ws = _ws(zk.bwd_workspace_bytes("add", self.act, self.bias, epi="gelu"), torch)
+        na, nb = _n(self.act.shape), _n(self.bias.shape)
+        self.calls = [
+            Call("add+gelu(act,bias)->y", "fwd",
+                 lambda: zk.binary_fwd("add", self.act, self.bias, out=self.y, epi="gelu"),
+                 [na, nb], [na]),
+            Call("add_bwd+gelu(g;act,bias)->grad_act,grad_bias", "bwd",
+                 lambda: zk.binary_bwd("add", self.g, self.act, self.bias,
+                                       grad_a=self.grad_act, grad_b=self.grad_bias,
+                                       epi="gelu", workspace=self.ws),
+                 [na, na, nb], [na, nb]),
+        ]
+
+
+class AttnScaleMask(Workload):
+    """scores[8,16,1024,1024] * scale[1,16,1,1] + mask[1,1,1024,1024]."""
+    name = "attn_scale_mask"
+
+    def __init__(self, host=None, b=8, h=16, t=1024):
+        import torch
+        hh = host or W.attn_scale_mask(b, h, t)
+        self.host = hh
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in hh.items()}
+        self.scores, self.scale, self.mask, self.g = d["scores"], d["scale"], d["mask"], d["g"]
+        e = torch.empty_like
+        self.t, self.out = e(self.scores), e(self.scores)
+        self.grad_scores, self.grad_scale = e(self.scores), e(self.scale)
+        self.ws = _ws(zk.bwd_workspace_bytes("mul", self.scores, self.scale), torch)
+        ns, nc, nm = _n(self.scores.shape), _n(self.scale.shape), _n(self.mask.shape)
+        self.calls = [
+            Call("mul(scores,scale)->t", "fwd",
+                 lambda: zk.binary_fwd("mul", self.scores, self.scale, out=self.t),
+                 [ns, nc], [ns]),
+            Call("add(t,mask)->out", "fwd",
+                 lambda: zk.binary_fwd("add", self.t, self.mask, out=self.out),
+                 [ns, nm], [ns]),
+            # the gradient of t is g itself (add); mul's rule gives scores / scale
+            Call("mul_bwd(g;scores,scale)->grad_scores,grad_scale", "bwd",
+                 lambda: zk.binary_bwd("mul", self.g, self.scores, self.scale,
+                                       grad_a=self.grad_scores, grad_b=self.grad_scale,
+                                       workspace=self.ws),
+                 [ns, ns, nc], [ns, nc]),
+        ]
+
+
+class StridedTransposed(Workload):
+    """a[4096,4096] as a transposed view (strides [1,4096]) * b[4096]."""
+    name = "strided_transposed"
+
+    def __init__(self, host=None, n=4096):
+        import torch
+        h = host or W.strided_transposed(n)
+        self.host = h
+        self.a_storage = torch.from_numpy(h["a_storage"]).to("cuda")
+        self.a = torch.as_strided(self.a_storage, h["a_sizes"], h["a_strides"])
+        self.b = torch.from_numpy(h["b"]).to("cuda")
+        self.g = torch.from_numpy(h["g"]).to("cuda")
+        self.out = torch.empty(h["a_sizes"], dtype=torch.float32, device="cuda")
+        self.grad_a = torch.empty_like(self.out)
+        self.grad_b = torch.empty_like(self.b)
+        self.ws = _ws(zk.bwd_workspace_bytes("mul", self.a, self.b), torch)
+        na, nb = n * n, n
+        self.calls = [
+            Call("mul(aT,b)->out", "fwd",
+                 lambda: zk.binary_fwd("mul", self.a, self.b, out=self.out), [na, nb], [na]),
+            Call("mul_bwd(g;aT,b)->grad_a,grad_b", "bwd",
+                 lambda: zk.binary_bwd("mul", self.g, self.a, self.b, grad_a=self.grad_a,
+                                       grad_b=self.grad_b, workspace=self.ws),
+                 [na, na, nb], [na, nb]),
+        ]
+
+
+class Rank8(Workload):
+    """a[2,3,4,5,6,7,8,9] / b[1,3,1,5,1,7,1,9]."""
+    name = "rank8_div"
+
+    def __init__(self, host=None):
+        import torch
+        h = host or W.rank8()
+        self.host = h
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in h.items()}
+        self.a, self.b, self.g = d["a"], d["b"], d["g"]
+        e = torch.empty_like
+        self.out, self.grad_a, self.grad_b = e(self.a), e(self.a), e(self.b)
+        self.ws = _ws(zk.bwd_workspace_bytes("div", self.a, self.b), torch)
+        na, nb = _n(self.a.shape), _n(self.b.shape)
+        self.calls = [
+            Call("div(a,b)->out", "fwd",
+                 lambda: zk.binary_fwd("div", self.a, self.b, out=self.out), [na, nb], [na]),
+            Call("div_bwd(g;a,b)->grad_a,grad_b", "bwd",
+                 lambda: zk.binary_bwd("div", self.g, self.a, self.b, grad_a=self.grad_a,
+                                       grad_b=self.grad_b, workspace=self.ws),
+                 [na, na, nb], [na, nb]),
+        ]
+
+
+class GPTResidual(Workload):
+    """h[16,2048,4096] * gamma[4096] + resid[16,2048,4096]."""
+    name = "gpt_residual"
+
+    def __init__(self, host=None, b=16, t=2048, c=4096):
+        import torch
+        hh = host or W.gpt_residual(b, t, c)
+        self.host = hh
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in hh.items()}
+        self.h, self.gamma, self.resid, self.g = d["h"], d["gamma"], d["resid"], d["g"]
+        e = torch.empty_like
+        self.t, self.out = e(self.h), e(self.h)
+        self.grad_h, self.grad_gamma, self.grad_resid = e(self.h), e(self.gamma), e(self.h)
+        self.ws = _ws(zk.bwd_workspace_bytes("mul", self.h, self.gamma), torch)
+        self.ws2 = _ws(zk.bwd_workspace_bytes("add", self.t, self.resid, need_a=False), torch)
+        nh, ng = _n(self.h.shape), _n(self.gamma.shape)
+        self.calls = [
+            Call("mul(h,gamma)->t", "fwd",
+                 lambda: zk.binary_fwd("mul", self.h, self.gamma, out=self.t), [nh, ng], [nh]),
+            Call("add(t,resid)->out", "fwd",
+                 lambda: zk.binary_fwd("add", self.t, self.resid, out=self.out),
+                 [nh, nh], [nh]),
+            Call("mul_bwd(g;h,gamma)->grad_h,grad_gamma", "bwd",
+                 lambda: zk.binary_bwd("mul", self.g, self.h, self.gamma, grad_a=self.grad_h,
+                                       grad_b=self.grad_gamma, workspace=self.ws),
+                 [nh, nh, ng], [nh, ng]),
+            # add's gradient of t is g itself; resid's is materialised
+            Call("add_bwd(g)->grad_resid", "bwd",
+                 lambda: zk.binary_bwd("add", self.g, self.t, self.resid, need_a=False,
+                                       grad_b=self.grad_resid, workspace=self.ws2),
+                 [nh], [nh]),
+        ]
+
+
+WORKLOAD_CLASSES = {c.name: c for c in (XYPlusX, MLPBiasGelu, AttnScaleMask,
+                                        StridedTransposed, Rank8, GPTResidual)}

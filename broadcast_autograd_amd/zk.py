@@ -1,0 +1,281 @@
+"""ctypes binding of libzk.so (include/zk.h).
+
+Argument marshalling only: torch tensors supply device pointers, sizes and
+strides (in elements) and the current HIP stream; outputs and workspaces are
+allocated with torch when the caller does not pass them.  Every step of the
+computation runs in the library's gfx950 kernels.  There is no fallback: if
+libzk.so is missing, every call raises.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libzk.so")
+MAX_DIMS = 8
+
+OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3}
+EPIS = {"none": 0, "gelu": 1}
+
+STATUS = {0: "ZK_OK", 1: "ZK_ERR_NULL", 2: "ZK_ERR_RANK", 3: "ZK_ERR_BAD_SIZE",
+          4: "ZK_ERR_BAD_STRIDE", 5: "ZK_ERR_BROADCAST", 6: "ZK_ERR_ALIAS",
+          7: "ZK_ERR_WORKSPACE", 8: "ZK_ERR_UNSUPPORTED", 9: "ZK_ERR_HIP",
+          10: "ZK_ERR_SHAPE"}
+ERR = {v: k for k, v in STATUS.items()}
+
+# exported symbols declared in include/zk.h
+SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
+           "zk_reduce_to_shape", "zk_status_string", "zk_plan_describe",
+           "zk_kernel_name", "zk_profile_start", "zk_profile_stop",
+           "zk_profile_read")
+
+
+class ZkError(RuntimeError):
+    def __init__(self, code, what=""):
+        self.code = code
+        self.name = STATUS.get(code, str(code))
+        msg = f"{what}: {self.name}"
+        try:
+            msg += f" ({lib().zk_status_string(code).decode()})"
+        except Exception:  # noqa: BLE001 - message only
+            pass
+        super().__init__(msg)
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32),
+                ("sizes", ctypes.c_int64 * MAX_DIMS),
+                ("strides", ctypes.c_int64 * MAX_DIMS)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("kernel2", ctypes.c_int32),
+                ("rank", ctypes.c_int32),
+                ("sizes", ctypes.c_int64 * MAX_DIMS),
+                ("strides", (ctypes.c_int64 * MAX_DIMS) * 3),
+                ("index64", ctypes.c_int32), ("vec", ctypes.c_int32),
+                ("partials", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libzk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m broadcast_autograd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I32 = ctypes.c_int32
+        L.zk_broadcast_shape.argtypes = [I32, P, I32, P, P, P]
+        L.zk_binary_fwd.argtypes = [I32, I32, P, P, P, P, P, P]
+        L.zk_binary_bwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.zk_reduce_to_shape.argtypes = [P, P, I32, P, P, P, P, P]
+        L.zk_status_string.argtypes = [I32]
+        L.zk_status_string.restype = ctypes.c_char_p
+        L.zk_plan_describe.argtypes = [I32, I32, I32, P, P, P]
+        L.zk_profile_start.argtypes = [I32]
+        L.zk_profile_stop.argtypes = []
+        L.zk_profile_read.argtypes = [I32, P, P, P]
+        L.zk_kernel_name.argtypes = [I32]
+        L.zk_kernel_name.restype = ctypes.c_char_p
+        for name in SYMBOLS:
+            getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int32
+        L.zk_status_string.restype = ctypes.c_char_p
+        L.zk_kernel_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(code, what):
+    if code != 0:
+        raise ZkError(code, what)
+
+
+def make_desc(sizes, strides=None):
+    """zk_desc from sizes and strides (elements); dense row-major if no
+    strides are given."""
+    sizes = [int(s) for s in sizes]
+    if strides is None:
+        strides, s = [], 1
+        for n in reversed(sizes):
+            strides.append(s)
+            s *= n
+        strides = list(reversed(strides))
+    d = Desc()
+    d.rank = len(sizes)
+    for k, (n, s) in enumerate(zip(sizes, strides)):
+        if k < MAX_DIMS:
+            d.sizes[k] = n
+            d.strides[k] = int(s)
+    return d
+
+
+def desc_of(t):
+    return make_desc(t.shape, t.stride())
+
+
+def _i64(seq):
+    arr = (ctypes.c_int64 * max(1, len(seq)))()
+    for k, s in enumerate(seq):
+        arr[k] = int(s)
+    return arr
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _op(op):
+    return OPS[op] if isinstance(op, str) else int(op)
+
+
+def _epi(epi):
+    return EPIS[epi] if isinstance(epi, str) else int(epi)
+
+
+def broadcast_shape(sa, sb):
+    ro = ctypes.c_int32(0)
+    out = (ctypes.c_int64 * MAX_DIMS)()
+    _check(lib().zk_broadcast_shape(len(sa), _i64(sa), len(sb), _i64(sb),
+                                    ctypes.byref(ro), out), "zk_broadcast_shape")
+    return tuple(out[k] for k in range(ro.value))
+
+
+def binary_fwd(op, a, b, out=None, epi="none", stream=None):
+    """out = epi(a (op) b) in the broadcast shape (dense row-major)."""
+    import torch
+    if out is None:
+        shape = broadcast_shape(a.shape, b.shape)
+        out = torch.empty(shape, dtype=torch.float32, device=a.device)
+    da, db = desc_of(a), desc_of(b)
+    _check(lib().zk_binary_fwd(_op(op), _epi(epi), _ptr(a), ctypes.byref(da),
+                               _ptr(b), ctypes.byref(db), _ptr(out),
+                               _stream(stream)), "zk_binary_fwd")
+    return out
+
+
+def _workspace(nbytes, device):
+    import torch
+    return torch.empty(max(256, int(nbytes)), dtype=torch.uint8, device=device)
+
+
+def bwd_workspace_bytes(op, a, b, need_a=True, need_b=True, epi="none"):
+    """Workspace zk_binary_bwd needs for these operands (no launch)."""
+    da, db = desc_of(a), desc_of(b)
+    nbytes = ctypes.c_size_t(0)
+    # Any non-NULL marker pointer requests the gradient in the query.
+    mark = ctypes.c_void_p(16)
+    _check(lib().zk_binary_bwd(_op(op), _epi(epi), mark, mark, ctypes.byref(da),
+                               mark, ctypes.byref(db), mark if need_a else None,
+                               None, mark if need_b else None, None, None,
+                               ctypes.byref(nbytes), None), "zk_binary_bwd(query)")
+    return nbytes.value
+
+
+def binary_bwd(op, grad, a, b, need_a=True, need_b=True, grad_a=None,
+               grad_b=None, acc_a=None, acc_b=None, epi="none", workspace=None,
+               stream=None):
+    """Gradients of epi(a (op) b) for the upstream ``grad``; returns
+    (grad_a, grad_b), each dense in its operand's shape (None if not
+    requested)."""
+    import torch
+    if need_a and grad_a is None:
+        grad_a = torch.empty(a.shape, dtype=torch.float32, device=grad.device)
+    if need_b and grad_b is None:
+        grad_b = torch.empty(b.shape, dtype=torch.float32, device=grad.device)
+    if not need_a:
+        grad_a = None
+    if not need_b:
+        grad_b = None
+    da, db = desc_of(a), desc_of(b)
+    nbytes = ctypes.c_size_t(0)
+    L = lib()
+    args = (_op(op), _epi(epi), _ptr(grad), _ptr(a), ctypes.byref(da), _ptr(b),
+            ctypes.byref(db), _ptr(grad_a), _ptr(acc_a), _ptr(grad_b), _ptr(acc_b))
+    if workspace is None:
+        _check(L.zk_binary_bwd(*args, None, ctypes.byref(nbytes), None),
+               "zk_binary_bwd(query)")
+        workspace = _workspace(nbytes.value, grad.device)
+    nbytes.value = workspace.numel() * workspace.element_size()
+    _check(L.zk_binary_bwd(*args, _ptr(workspace), ctypes.byref(nbytes),
+                           _stream(stream)), "zk_binary_bwd")
+    return grad_a, grad_b
+
+
+def reduce_workspace_bytes(x, shape):
+    d = desc_of(x)
+    nbytes = ctypes.c_size_t(0)
+    _check(lib().zk_reduce_to_shape(ctypes.c_void_p(16), ctypes.byref(d), len(shape),
+                                    _i64(shape), ctypes.c_void_p(16), None,
+                                    ctypes.byref(nbytes), None),
+           "zk_reduce_to_shape(query)")
+    return nbytes.value
+
+
+def reduce_to_shape(x, shape, out=None, workspace=None, stream=None):
+    """Sum ``x`` back to ``shape`` (dense row-major)."""
+    import torch
+    shape = tuple(int(s) for s in shape)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    d = desc_of(x)
+    nbytes = ctypes.c_size_t(0)
+    L = lib()
+    if workspace is None:
+        _check(L.zk_reduce_to_shape(_ptr(x), ctypes.byref(d), len(shape), _i64(shape),
+                                    _ptr(out), None, ctypes.byref(nbytes), None),
+               "zk_reduce_to_shape(query)")
+        workspace = _workspace(nbytes.value, x.device)
+    nbytes.value = workspace.numel() * workspace.element_size()
+    _check(L.zk_reduce_to_shape(_ptr(x), ctypes.byref(d), len(shape), _i64(shape),
+                                _ptr(out), _ptr(workspace), ctypes.byref(nbytes),
+                                _stream(stream)), "zk_reduce_to_shape")
+    return out
+
+
+def plan_describe(kind, op, da, db, epi="none"):
+    """Launch plan a call would use (host only).  kind: "fwd", "bwd",
+    "reduce" (db = target shape)."""
+    info = PlanInfo()
+    k = {"fwd": 0, "bwd": 1, "reduce": 2}[kind]
+    _check(lib().zk_plan_describe(k, _op(op), _epi(epi), ctypes.byref(da),
+                                  ctypes.byref(db), ctypes.byref(info)),
+           "zk_plan_describe")
+    r = info.rank
+    return dict(kernel=lib().zk_kernel_name(info.kernel).decode(),
+                kernel2=lib().zk_kernel_name(info.kernel2).decode(),
+                rank=r, sizes=tuple(info.sizes[k] for k in range(r)),
+                strides=tuple(tuple(info.strides[o][k] for k in range(r))
+                              for o in range(3)),
+                index64=bool(info.index64), vec=info.vec,
+                partials=info.partials, workspace_bytes=info.workspace_bytes)
+
+
+def profile_start(capacity):
+    """Bracket every library kernel with HIP events (tooling; see zk.h)."""
+    _check(lib().zk_profile_start(int(capacity)), "zk_profile_start")
+
+
+def profile_stop():
+    _check(lib().zk_profile_stop(), "zk_profile_stop")
+
+
+def profile_read(max_records=1 << 16):
+    """[(kernel class name, milliseconds)] in launch order (after a sync)."""
+    ids = (ctypes.c_int32 * max_records)()
+    ms = (ctypes.c_float * max_records)()
+    n = ctypes.c_int32(0)
+    _check(lib().zk_profile_read(max_records, ids, ms, ctypes.byref(n)), "zk_profile_read")
+    L = lib()
+    return [(L.zk_kernel_name(ids[i]).decode(), ms[i]) for i in range(n.value)]

@@ -1,0 +1,221 @@
+/*
+ * zk.h -- C ABI of the MI355X (gfx950) broadcasting binary-operator library.
+ *
+ * The library computes, on one GPU, the N-d strided broadcasting element-wise
+ * operators add/sub/mul/div and their backward (the local gradient rule
+ * followed by the sum back to each input's shape), as described by the "Zero"
+ * book (ismantic.github.io/zero):
+ *   - Tensor chapter, "shape and strides": sizes and strides per dim, strides
+ *     counted in ELEMENTS, element offset = sum_k i_k * s_k.
+ *   - Operator chapter, "element-wise operators": same-shape add/sub/mul/div
+ *     and the mul rule dL/dx = g*y, dL/dy = g*x.
+ *   - Operator chapter, "broadcast": the shape rule (compare from the last
+ *     dim: equal, one is 1, or one missing) and the backward "repetition in
+ *     the forward is a sum in the backward" (SumToSize).
+ *   - GPU chapter, "kernel dispatch": at most 8 dims, passed by value.
+ *   - GPU chapter, "OpAdd": add's backward hands g to both inputs.
+ *   - GPU chapter, "asynchronous execution": work is queued on a stream and
+ *     the caller is not synchronised.
+ *
+ * Conventions shared by every call:
+ *   - Element type: IEEE binary32 (float) only.
+ *   - Dims are listed outer -> inner (row-major order).  A descriptor's
+ *     sizes and strides are int64 element counts; strides must be >= 0; a
+ *     stride on a size-1 dim is ignored.  Rank 0 (a scalar) is allowed.
+ *   - Every output is DENSE ROW-MAJOR: the forward result in the broadcast
+ *     shape, each gradient in its operand's logical shape.
+ *   - Pointers are device pointers on the device that owns `stream` (a
+ *     hipStream_t passed as void*; NULL means the default stream).  Host
+ *     arrays (sizes, descriptors) are read during the call only.
+ *   - The library allocates nothing on the device, keeps no pointer after
+ *     it returns and never synchronises: results are ready when the stream
+ *     reaches them.
+ *   - Every argument is validated before anything is launched; on an error
+ *     nothing is launched and no output is written.
+ *   - Forward results are one binary32 operation per element,
+ *     round-to-nearest-even, subnormals kept, no fused multiply-add.
+ *   - Backward reductions are deterministic: the same call on the same
+ *     shapes returns the same bits, on any device of the same kind.
+ */
+#ifndef ZK_H_
+#define ZK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Up to 8 dims per tensor (GPU chapter, "kernel dispatch"). */
+#define ZK_MAX_DIMS 8
+
+typedef enum {
+  ZK_OK = 0,
+  ZK_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  ZK_ERR_RANK = 2,        /* rank < 0 or > ZK_MAX_DIMS                      */
+  ZK_ERR_BAD_SIZE = 3,    /* a size is negative                             */
+  ZK_ERR_BAD_STRIDE = 4,  /* a stride is negative                           */
+  ZK_ERR_BROADCAST = 5,   /* shapes do not broadcast                        */
+  ZK_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
+  ZK_ERR_WORKSPACE = 7,   /* workspace smaller than required                */
+  ZK_ERR_UNSUPPORTED = 8, /* unknown op / epilogue value                    */
+  ZK_ERR_HIP = 9,         /* a kernel launch failed                         */
+  ZK_ERR_SHAPE = 10       /* reduce target does not broadcast to the input  */
+} zk_status;
+
+/* out = a (op) b.  Operator chapter, "element-wise operators". */
+typedef enum { ZK_ADD = 0, ZK_SUB = 1, ZK_MUL = 2, ZK_DIV = 3 } zk_op;
+
+/* Optional epilogue applied to the op's result: y = GeLU(a (op) b), with
+ * GeLU(h) = h * Phi(h) and Phi the standard normal CDF (the activation the
+ * GPU chapter, "element-wise" section, and the GPT chapter's FFN name).
+ * The forward value is GeLU evaluated in binary64 and rounded once to
+ * binary32; h = a (op) b is itself rounded to binary32 first. */
+typedef enum { ZK_EPI_NONE = 0, ZK_EPI_GELU = 1 } zk_epi;
+
+/* A strided tensor view (Tensor chapter, "shape and strides").
+ * sizes[k], strides[k] for k < rank; entries past rank are ignored. */
+typedef struct {
+  int32_t rank;
+  int64_t sizes[ZK_MAX_DIMS];
+  int64_t strides[ZK_MAX_DIMS];
+} zk_desc;
+
+/*
+ * Broadcast shape of two shapes (Operator chapter, "broadcast"): align the
+ * shapes at their last dim; per dim the sizes must be equal, or one is 1, or
+ * one is missing (counts as 1).  Size 0 obeys the same rule (0 with 1 gives
+ * 0; 0 with n > 1 is an error).
+ *   rank_a, sizes_a / rank_b, sizes_b : the two shapes (host arrays)
+ *   rank_out, sizes_out               : the result (host; ZK_MAX_DIMS slots)
+ * Errors: ZK_ERR_NULL, ZK_ERR_RANK, ZK_ERR_BAD_SIZE, ZK_ERR_BROADCAST.
+ * Pure host function: touches no GPU.
+ */
+zk_status zk_broadcast_shape(int32_t rank_a, const int64_t *sizes_a,
+                             int32_t rank_b, const int64_t *sizes_b,
+                             int32_t *rank_out,
+                             int64_t sizes_out[ZK_MAX_DIMS]);
+
+/*
+ * Forward: out[i] = epi(a[off_a(i)] (op) b[off_b(i)]) for every i of the
+ * broadcast shape (Operator chapter, "element-wise operators" and
+ * "broadcast": a size-1 or missing operand dim always reads coordinate 0).
+ *   a, da / b, db : inputs, any non-negative strides (views, stride 0 ok)
+ *   out           : dense row-major, broadcast shape, caller-allocated
+ *   stream        : hipStream_t or NULL
+ * Aliasing: out may be exactly a (or b) when that operand is dense row-major
+ * with the full broadcast shape (in-place); any other overlap of out with an
+ * input is ZK_ERR_ALIAS.
+ * An empty broadcast shape launches nothing and returns ZK_OK.
+ * Errors: ZK_ERR_NULL, ZK_ERR_RANK, ZK_ERR_BAD_SIZE, ZK_ERR_BAD_STRIDE,
+ *         ZK_ERR_BROADCAST, ZK_ERR_ALIAS, ZK_ERR_UNSUPPORTED, ZK_ERR_HIP.
+ */
+zk_status zk_binary_fwd(zk_op op, zk_epi epi, const float *a,
+                        const zk_desc *da, const float *b, const zk_desc *db,
+                        float *out, void *stream);
+
+/*
+ * Backward of y = epi(a (op) b) for the upstream gradient `grad` (dense
+ * row-major, broadcast shape).  Local rules (Autograd chapter, "chain rule";
+ * Operator chapter, "element-wise operators"; GPU chapter, "OpAdd"; sub and
+ * div by calculus):
+ *   add: (g, g)   sub: (g, -g)   mul: (g*b, g*a)   div: (g/b, -g*a/b^2)
+ * With ZK_EPI_GELU, g is first replaced by g * GeLU'(h), h = a (op) b
+ * recomputed in binary32, GeLU'(h) = Phi(h) + h*phi(h).
+ * Each input's gradient is then summed over every output position its
+ * elements were repeated into (Operator chapter, "broadcast"), and added to
+ * the matching acc buffer (Autograd chapter: a tensor reached along several
+ * paths gets the sum of the path gradients).
+ *   grad_a, grad_b : dense row-major in a's / b's logical shape; NULL = skip
+ *   acc_a, acc_b   : NULL (no accumulation), or a dense row-major buffer of
+ *                    the gradient's shape; it may be exactly the gradient
+ *                    pointer (in-place +=) or, when that operand has the full
+ *                    broadcast shape, exactly `grad` (folds an identity path
+ *                    without a copy)
+ *   workspace      : device scratch owned by the caller.  Pass NULL to query:
+ *                    the required size is written to *workspace_bytes and
+ *                    nothing is launched.  Otherwise *workspace_bytes is the
+ *                    size provided; too small -> ZK_ERR_WORKSPACE.  The size
+ *                    depends on the shapes only.  Contents need no
+ *                    initialisation and are garbage afterwards.
+ * Sums are accumulated in binary64 in an order fixed by the shapes and
+ * rounded once to binary32 (bitwise reproducible run to run).
+ * Aliasing: outputs may not overlap each other, `grad`, a, b or the
+ * workspace, except an output equal to its own acc (ZK_ERR_ALIAS).
+ * Errors: as zk_binary_fwd, plus ZK_ERR_WORKSPACE.
+ */
+zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad,
+                        const float *a, const zk_desc *da, const float *b,
+                        const zk_desc *db, float *grad_a, const float *acc_a,
+                        float *grad_b, const float *acc_b, void *workspace,
+                        size_t *workspace_bytes, void *stream);
+
+/*
+ * Sum `in` back to `sizes_out` (Operator chapter, "broadcast": SumToSize),
+ * i.e. over every dim where the target is 1 or missing.  The target must
+ * broadcast to in's shape with in's shape as the result (else ZK_ERR_SHAPE).
+ *   in, din   : input view, any non-negative strides
+ *   out       : dense row-major, target shape
+ *   workspace : as in zk_binary_bwd (NULL queries *workspace_bytes)
+ * An empty input writes zeros to a non-empty target.
+ * Errors: ZK_ERR_NULL, ZK_ERR_RANK, ZK_ERR_BAD_SIZE, ZK_ERR_BAD_STRIDE,
+ *         ZK_ERR_SHAPE, ZK_ERR_ALIAS, ZK_ERR_WORKSPACE, ZK_ERR_HIP.
+ */
+zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
+                             int32_t rank_out, const int64_t *sizes_out,
+                             float *out, void *workspace,
+                             size_t *workspace_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *zk_status_string(zk_status s);
+
+/*
+ * Host-only inspection of the launch plan a call would use, for tests and
+ * tooling.  kind: 0 = zk_binary_fwd, 1 = zk_binary_bwd (both grads
+ * requested), 2 = zk_reduce_to_shape (db holds the target shape, strides
+ * ignored).  Fills *info; touches no GPU.
+ */
+typedef struct {
+  int32_t kernel;              /* main kernel class, see zk_kernel_name   */
+  int32_t kernel2;             /* second kernel class, -1 if none         */
+  int32_t rank;                /* canonical rank after dropping/coalescing */
+  int64_t sizes[ZK_MAX_DIMS];  /* canonical sizes                         */
+  int64_t strides[3][ZK_MAX_DIMS]; /* canonical strides: [0] out/grad,
+                                      [1] a (or reduce input), [2] b (or
+                                      reduce target, dense, 0 = reduced)  */
+  int32_t index64;             /* 1 when 64-bit index math is used        */
+  int32_t vec;                 /* elements per vector access (4 or 1)     */
+  int64_t partials;            /* partial sums per reduced element        */
+  size_t workspace_bytes;      /* workspace the call needs                */
+} zk_plan_info;
+
+zk_status zk_plan_describe(int32_t kind, zk_op op, zk_epi epi,
+                           const zk_desc *da, const zk_desc *db,
+                           zk_plan_info *info);
+
+/* Name of a kernel class id reported by zk_plan_describe. */
+const char *zk_kernel_name(int32_t kernel);
+
+/*
+ * Optional per-kernel timing for measurement tools (off by default).
+ * zk_profile_start(capacity) creates `capacity` pairs of HIP events on the
+ * current device (a host call: make it before any timed or captured region)
+ * and clears the log.  While started, every kernel the library launches is
+ * bracketed by an event pair recorded on the kernel's own stream, until the
+ * pairs run out.  zk_profile_stop() stops recording.  After the caller has
+ * synchronised the streams, zk_profile_read() copies up to `max` records
+ * (kernel class id and elapsed milliseconds, in launch order) and writes
+ * their number to *count.  Not for concurrent use from several host threads
+ * while started.  Errors: ZK_ERR_NULL, ZK_ERR_HIP.
+ */
+zk_status zk_profile_start(int32_t capacity);
+zk_status zk_profile_stop(void);
+zk_status zk_profile_read(int32_t max, int32_t *kernel_ids, float *ms,
+                          int32_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZK_H_ */

@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: seeded views on both sides and the
+comparison rules.
+
+Forward: bit-exact (any NaN matches any NaN).  GeLU forward: bit-exact, except
+that one unit in the last place is accepted where the exact value lies within
+a relative 1e-12 of the midpoint between the two neighbouring binary32 values
+(both sides round a binary64 evaluation of GeLU; their libm erfc may differ by
+a few binary64 ulps, which only matters at such near-ties).
+Backward: |gpu - oracle| <= 2e-6 * sum|terms| per element, and exactly +-0
+where that sum is 0.
+"""
+import numpy as np
+
+BWD_TOL = 2e-6
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev(x):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+def strided_pair(storage, sizes, strides, offset=0):
+    """(oracle View, device tensor) reading the same storage the same way."""
+    import oracle
+    torch = torch_mod()
+    st = dev(storage.reshape(-1))
+    t = torch.as_strided(st, tuple(sizes), tuple(strides), offset)
+    return oracle.View(storage.reshape(-1), sizes, strides, offset), t, st
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def assert_bitexact(got, want, what=""):
+    got = np.asarray(got, dtype=np.float32)
+    want = np.asarray(want, dtype=np.float32)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    gb, wb = got.view(np.uint32), want.view(np.uint32)
+    nan = np.isnan(got) & np.isnan(want)
+    bad = (gb != wb) & ~nan
+    if bad.any():
+        i = np.flatnonzero(bad.reshape(-1))[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} differ; first at "
+                             f"{i}: got {got.reshape(-1)[i]} want {want.reshape(-1)[i]}")
+
+
+def assert_gelu_exact(got, want, hval):
+    """Bit-exact GeLU with the documented near-tie exception.  ``hval`` is the
+    binary32 argument h of each element."""
+    import oracle
+    got = np.asarray(got, dtype=np.float32).reshape(-1)
+    want = np.asarray(want, dtype=np.float32).reshape(-1)
+    h = np.asarray(hval, dtype=np.float32).reshape(-1)
+    diff = np.flatnonzero((got.view(np.uint32) != want.view(np.uint32)) &
+                          ~(np.isnan(got) & np.isnan(want)))
+    for i in diff:
+        gi, wi = got.view(np.int32)[i], want.view(np.int32)[i]
+        assert abs(int(gi) - int(wi)) == 1, (i, got[i], want[i], h[i])
+        exact = float(h[i]) * oracle.phi_cdf(float(h[i]))
+        mid = 0.5 * (float(got[i]) + float(want[i]))
+        assert abs(exact - mid) <= 1e-12 * abs(exact), (i, h[i], exact, mid)
+    return len(diff)
+
+
+def assert_bwd(got, ref, what=""):
+    """ref is an oracle.Grad."""
+    got = np.asarray(got, dtype=np.float32)
+    assert got.shape == ref.f32.shape, (what, got.shape, ref.f32.shape)
+    g64 = got.astype(np.float64)
+    err = np.abs(g64 - ref.f32.astype(np.float64))
+    lim = BWD_TOL * ref.abs
+    bad = err > lim
+    zero = ref.abs == 0
+    bad |= zero & (got != 0)
+    if bad.any():
+        i = np.flatnonzero(bad.reshape(-1))[:5]
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at {i}: "
+            f"got {got.reshape(-1)[i]} want {ref.f32.reshape(-1)[i]} "
+            f"abs {ref.abs.reshape(-1)[i]}")

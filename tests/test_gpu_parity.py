@@ -1,0 +1,494 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element, on seeded inputs.
+
+Forward: bit-exact.  Backward: |err| <= 2e-6 * sum|terms| per element.
+Small cases run the oracle on every element; the full-size workloads (the
+shapes and launch configuration the benchmark times) are checked on sampled
+positions of the large outputs and on every element of the reduced ones.
+"""
+import itertools
+import math
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from broadcast_autograd_amd import steps, workloads as W, zk  # noqa: E402
+from gpu_util import (assert_bitexact, assert_bwd, assert_gelu_exact, dev,  # noqa: E402
+                      host, strided_pair)
+
+OPS = ["add", "sub", "mul", "div"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    say(f"\n[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_fwd(op, ta, tb, epi="none"):
+    return host(zk.binary_fwd(op, ta, tb, epi=epi))
+
+
+def check_pair(orc, op, va, ta, vb, tb, g_np=None, epi="none", acc=None,
+               want=(True, True), seed=0):
+    """Forward bit-exact and backward within tolerance for one operand pair."""
+    e = orc.EPI_GELU if epi == "gelu" else orc.EPI_NONE
+    want_f = orc.fwd(op, va, vb, epi=e)
+    got_f = gpu_fwd(op, ta, tb, epi)
+    if epi == "gelu":
+        h = orc.fwd(op, va, vb)
+        assert_gelu_exact(got_f, want_f, h)
+    else:
+        assert_bitexact(got_f, want_f, f"fwd {op}")
+    if g_np is None:
+        g_np = np.random.default_rng(seed).standard_normal(want_f.shape).astype(np.float32)
+    g = dev(g_np)
+    acc_a = acc_b = None
+    acc_a_np = acc_b_np = None
+    if acc is not None:
+        acc_a_np, acc_b_np = acc
+        acc_a = None if acc_a_np is None else dev(acc_a_np)
+        acc_b = None if acc_b_np is None else dev(acc_b_np)
+    ga, gb = zk.binary_bwd(op, g, ta, tb, need_a=want[0], need_b=want[1],
+                           acc_a=acc_a, acc_b=acc_b, epi=epi)
+    ra, rb = orc.bwd(op, g_np, va, vb, acc_a=acc_a_np, acc_b=acc_b_np, want=want, epi=e)
+    if want[0]:
+        assert_bwd(host(ga), ra, f"grad_a {op}")
+    if want[1]:
+        assert_bwd(host(gb), rb, f"grad_b {op}")
+
+
+# ----------------------------------------------------------- worked examples
+def test_chain_rule_worked_example_on_gpu(orc):
+    """z = x*y + x at x=3, y=2: z = 9, dz/dx = 3, dz/dy = 3 (Autograd chapter)."""
+    x = dev(np.array(3.0, np.float32))
+    y = dev(np.array(2.0, np.float32))
+    t = zk.binary_fwd("mul", x, y)
+    z = zk.binary_fwd("add", t, x)
+    assert float(host(z)) == 9.0
+    g = dev(np.array(1.0, np.float32))
+    g_t, g_x1 = zk.binary_bwd("add", g, t, x)
+    g_x, g_y = zk.binary_bwd("mul", g_t, x, y, acc_a=g_x1)
+    assert float(host(g_x)) == 3.0 and float(host(g_y)) == 3.0
+
+
+def test_broadcast_worked_example_on_gpu():
+    """[10,20,30] broadcast from [3] to [2,3]; its gradient sums to [2,2,2]."""
+    v = dev(np.array([10, 20, 30], np.float32))
+    z = dev(np.zeros((2, 3), np.float32))
+    np.testing.assert_array_equal(host(zk.binary_fwd("add", z, v)),
+                                  [[10, 20, 30], [10, 20, 30]])
+    _, gb = zk.binary_bwd("add", dev(np.ones((2, 3), np.float32)), z, v)
+    np.testing.assert_array_equal(host(gb), [2, 2, 2])
+
+
+def test_strided_worked_example_on_gpu(orc):
+    """Transposed view of [[1,2,3],[4,5,6]]: element (0,1) reads 4."""
+    s = np.arange(1, 7, dtype=np.float32)
+    v, t, _ = strided_pair(s, (3, 2), (1, 3))
+    out = gpu_fwd("add", t, dev(np.zeros((3, 2), np.float32)))
+    assert out[0, 1] == 4.0
+    np.testing.assert_array_equal(out, [[1, 4], [2, 5], [3, 6]])
+
+
+# ------------------------------------------- workloads at reduced sizes
+def _rng_pair(shape_a, shape_b, seed, lo=0.5, hi=2.0, signed=True):
+    rng = np.random.default_rng(seed)
+    a = rng.uniform(lo, hi, shape_a).astype(np.float32)
+    b = rng.uniform(lo, hi, shape_b).astype(np.float32)
+    if signed:
+        a *= np.where(rng.random(shape_a) < 0.5, -1, 1).astype(np.float32)
+    return a, b
+
+
+@pytest.mark.parametrize("shapes", [
+    ((8, 128, 256), (128, 1)),        # config-1 layout, fewer batches
+    ((7, 33, 260), (33, 1)),          # ragged rows and inner run
+    ((3, 40, 1024), (40, 1)),
+])
+@pytest.mark.parametrize("op", OPS)
+def test_row_scalar_broadcast(orc, shapes, op):
+    a, b = _rng_pair(*shapes, seed=hash((shapes, op)) % 2**31)
+    check_pair(orc, op, a, dev(a), b, dev(b), seed=1)
+    # operand order swapped: the broadcast operand first
+    check_pair(orc, op, b, dev(b), a, dev(a), seed=2)
+
+
+@pytest.mark.parametrize("shapes", [
+    ((512, 1024), (1024,)),           # config-2/5 layout
+    ((300, 1000), (1000,)),           # ragged
+    ((37, 4100), (4100,)),
+    ((1, 4096), (4096,)),
+])
+@pytest.mark.parametrize("op", OPS)
+def test_column_broadcast(orc, shapes, op):
+    a, b = _rng_pair(*shapes, seed=hash((shapes, op)) % 2**31)
+    check_pair(orc, op, a, dev(a), b, dev(b), seed=3)
+    check_pair(orc, op, b, dev(b), a, dev(a), seed=4)
+
+
+@pytest.mark.parametrize("shapes", [((512, 1024), (1024,)), ((300, 1000), (1000,)),
+                                    ((64, 260), (64, 1))])
+@pytest.mark.parametrize("op", OPS)
+def test_gelu_epilogue(orc, shapes, op):
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal(shapes[0]).astype(np.float32)
+    b = (rng.standard_normal(shapes[1]) * 0.5 + (1.0 if op == "div" else 0.0)).astype(np.float32)
+    check_pair(orc, op, a, dev(a), b, dev(b), epi="gelu", seed=6)
+
+
+def test_mlp_bias_gelu_config_layout(orc):
+    h = W.mlp_bias_gelu(rows=512)
+    check_pair(orc, "add", h["act"], dev(h["act"]), h["bias"], dev(h["bias"]),
+               g_np=h["g"], epi="gelu")
+
+
+def test_attention_shaped_small(orc):
+    h = W.attn_scale_mask(b=2, h=16, t=128)
+    wl = steps.AttnScaleMask(host=h)
+    wl.run()
+    t = orc.fwd("mul", h["scores"], h["scale"])
+    assert_bitexact(host(wl.t), t, "scores*scale")
+    assert_bitexact(host(wl.out), orc.fwd("add", t, h["mask"]), "+mask")
+    ra, rb = orc.bwd("mul", h["g"], h["scores"], h["scale"])
+    assert_bwd(host(wl.grad_scores), ra, "grad_scores")
+    assert_bwd(host(wl.grad_scale), rb, "grad_scale")
+    # the mask's gradient would be g reduced to [1,1,T,T]
+    mg = zk.reduce_to_shape(wl.g, (1, 1, 128, 128))
+    assert_bwd(host(mg), orc.reduce_to_shape(h["g"], (1, 1, 128, 128)), "mask grad")
+
+
+@pytest.mark.parametrize("n,m", [(520, 392), (64, 64), (130, 260), (4096, 64)])
+@pytest.mark.parametrize("op", ["mul", "div", "sub"])
+def test_transposed_operand(orc, n, m, op):
+    """a is a transposed view: sizes [n, m], strides [1, n]."""
+    rng = np.random.default_rng(n * m)
+    s = rng.uniform(0.5, 2, n * m).astype(np.float32)
+    va, ta, _ = strided_pair(s, (n, m), (1, n))
+    b = rng.uniform(0.5, 2, (m,)).astype(np.float32)
+    check_pair(orc, op, va, ta, b, dev(b), seed=7)
+    check_pair(orc, op, b, dev(b), va, ta, seed=8)
+
+
+def test_strided_transposed_config_layout(orc):
+    h = W.strided_transposed(n=1024)
+    wl = steps.StridedTransposed(host=h)
+    wl.run()
+    va = orc.View(h["a_storage"], h["a_sizes"], h["a_strides"])
+    assert_bitexact(host(wl.out), orc.fwd("mul", va, h["b"]), "fwd")
+    ra, rb = orc.bwd("mul", h["g"], va, h["b"])
+    assert_bwd(host(wl.grad_a), ra, "grad_a")
+    assert_bwd(host(wl.grad_b), rb, "grad_b")
+
+
+def test_rank8_config_full(orc):
+    h = W.rank8()
+    wl = steps.Rank8(host=h)
+    wl.run()
+    assert_bitexact(host(wl.out), orc.fwd("div", h["a"], h["b"]), "fwd")
+    ra, rb = orc.bwd("div", h["g"], h["a"], h["b"])
+    assert_bwd(host(wl.grad_a), ra, "grad_a")
+    assert_bwd(host(wl.grad_b), rb, "grad_b")
+
+
+def test_xy_plus_x_small(orc):
+    h = W.xy_plus_x(scale=0.125)
+    wl = steps.XYPlusX(host=h)
+    wl.run()
+    t = orc.fwd("mul", h["x"], h["y"])
+    assert_bitexact(host(wl.t), t, "x*y")
+    assert_bitexact(host(wl.z), orc.fwd("add", t, h["x"]), "+x")
+    # graph by hand: add hands g to t and x; mul adds x's second path
+    rx, ry = orc.bwd("mul", h["g"], h["x"], h["y"], acc_a=h["g"])
+    assert_bwd(host(wl.grad_x), rx, "grad_x")
+    assert_bwd(host(wl.grad_y), ry, "grad_y")
+
+
+def test_gpt_residual_small(orc):
+    h = W.gpt_residual(b=2, t=64, c=4096)
+    wl = steps.GPTResidual(host=h)
+    wl.run()
+    t = orc.fwd("mul", h["h"], h["gamma"])
+    assert_bitexact(host(wl.t), t, "h*gamma")
+    assert_bitexact(host(wl.out), orc.fwd("add", t, h["resid"]), "+resid")
+    rh, rg = orc.bwd("mul", h["g"], h["h"], h["gamma"])
+    assert_bwd(host(wl.grad_h), rh, "grad_h")
+    assert_bwd(host(wl.grad_gamma), rg, "grad_gamma")
+    _, rr = orc.bwd("add", h["g"], t, h["resid"], want=(False, True))
+    assert_bwd(host(wl.grad_resid), rr, "grad_resid")
+
+
+# ------------------------------------------------- brute force and fuzz
+def _shapes(max_rank=3, sizes=(1, 2, 3)):
+    for r in range(max_rank + 1):
+        yield from itertools.product(sizes, repeat=r)
+
+
+def test_bruteforce_small_shapes(orc):
+    """Every shape pair of rank <= 3 with sizes in {1,2,3}, every op."""
+    shapes = list(_shapes())
+    rng = np.random.default_rng(21)
+    count = 0
+    for sa in shapes:
+        for sb in shapes:
+            try:
+                np.broadcast_shapes(sa, sb)
+            except ValueError:
+                continue
+            a = rng.uniform(0.5, 2, sa).astype(np.float32)
+            b = rng.uniform(0.5, 2, sb).astype(np.float32)
+            op = OPS[count % 4]
+            check_pair(orc, op, a, dev(a), b, dev(b), seed=count)
+            count += 1
+    say(f"  {count} shape pairs")
+
+
+def _random_view(rng, shape):
+    """A random strided view with the given logical shape: permuted storage,
+    stride-0 dims for size-1 dims, and a storage offset."""
+    r = len(shape)
+    perm = rng.permutation(r) if r else np.array([], int)
+    # dense strides in a permuted storage order
+    st = [0] * r
+    s = 1
+    for k in reversed(list(perm)):
+        st[k] = s
+        s *= max(shape[k], 1)
+    for k in range(r):
+        if shape[k] == 1 and rng.random() < 0.5:
+            st[k] = 0
+    off = int(rng.integers(0, 3))
+    extent = off + sum((n - 1) * x for n, x in zip(shape, st)) + 1 if all(shape) else off + 1
+    storage = rng.uniform(0.5, 2, max(extent, 1)).astype(np.float32)
+    return strided_pair(storage, shape, st, off)
+
+
+def test_fuzz_rank8_views(orc):
+    """Seeded fuzz: rank <= 8, sizes 1-5, random broadcast masks, permuted
+    views, zero strides, storage offsets (misaligned base pointers)."""
+    rng = np.random.default_rng(77)
+    for it in range(120):
+        r = int(rng.integers(0, 9))
+        out = [int(rng.integers(1, 6)) for _ in range(r)]
+        if np.prod(out) > 20000:
+            continue
+        ra_ = int(rng.integers(0, r + 1))
+        rb_ = int(rng.integers(0, r + 1))
+        sa = [n if rng.random() < 0.6 else 1 for n in out[r - ra_:]]
+        sb = [n if rng.random() < 0.6 else 1 for n in out[r - rb_:]]
+        va, ta, _ = _random_view(rng, sa)
+        vb, tb, _ = _random_view(rng, sb)
+        op = OPS[it % 4]
+        check_pair(orc, op, va, ta, vb, tb, seed=it)
+
+
+def test_reduce_to_shape_cases(orc):
+    rng = np.random.default_rng(31)
+    cases = [((64, 1000), (1000,)), ((64, 1000), (64, 1)), ((64, 1000), ()),
+             ((4, 5, 300), (5, 1)), ((4, 5, 300), (4, 1, 300)), ((3, 2048), (1, 1)),
+             ((2, 3, 4, 5, 6, 7, 8, 9), (3, 1, 5, 1, 7, 1, 9)), ((16, 4096), (16, 4096)),
+             ((0, 5), (5,)), ((6, 4096), (1,))]
+    for sin, sout in cases:
+        x = rng.standard_normal(sin).astype(np.float32)
+        got = host(zk.reduce_to_shape(dev(x), sout))
+        assert_bwd(got, orc.reduce_to_shape(x, sout), f"reduce {sin}->{sout}")
+    # strided input
+    s = rng.standard_normal(300 * 7).astype(np.float32)
+    v, t, _ = strided_pair(s, (300, 7), (1, 300))
+    assert_bwd(host(zk.reduce_to_shape(t, (7,))), orc.reduce_to_shape(v, (7,)), "strided")
+
+
+def test_acc_modes(orc):
+    rng = np.random.default_rng(41)
+    a = rng.uniform(0.5, 2, (96, 512)).astype(np.float32)
+    b = rng.uniform(0.5, 2, (512,)).astype(np.float32)
+    g = rng.standard_normal((96, 512)).astype(np.float32)
+    acc_a = rng.standard_normal((96, 512)).astype(np.float32)
+    acc_b = rng.standard_normal((512,)).astype(np.float32)
+    ta, tb, tg = dev(a), dev(b), dev(g)
+    for op in OPS:
+        # separate acc buffers
+        ga, gb = zk.binary_bwd(op, tg, ta, tb, acc_a=dev(acc_a), acc_b=dev(acc_b))
+        ra, rb = orc.bwd(op, g, a, b, acc_a=acc_a, acc_b=acc_b)
+        assert_bwd(host(ga), ra, f"{op} acc_a")
+        assert_bwd(host(gb), rb, f"{op} acc_b")
+        # in place: acc == the gradient buffer
+        xa, xb = dev(acc_a), dev(acc_b)
+        zk.binary_bwd(op, tg, ta, tb, grad_a=xa, acc_a=xa, grad_b=xb, acc_b=xb)
+        assert_bwd(host(xa), ra, f"{op} in-place a")
+        assert_bwd(host(xb), rb, f"{op} in-place b")
+        # acc == the upstream gradient itself
+        ga, _ = zk.binary_bwd(op, tg, ta, tb, acc_a=tg)
+        ra2, _ = orc.bwd(op, g, a, b, acc_a=g)
+        assert_bwd(host(ga), ra2, f"{op} acc=grad")
+
+
+def test_both_operands_broadcast(orc):
+    rng = np.random.default_rng(51)
+    for sa, sb in [((300, 1), (1, 200)), ((5, 1, 7), (1, 6, 1)), ((1, 64), (64, 1))]:
+        for op in OPS:
+            a, b = _rng_pair(sa, sb, seed=len(sa) * 7 + OPS.index(op))
+            check_pair(orc, op, a, dev(a), b, dev(b), seed=3)
+
+
+def test_edge_cases(orc):
+    # rank 0 with rank 0, empty broadcast shapes, empty reduction
+    for op in OPS:
+        check_pair(orc, op, np.array(1.5, np.float32), dev(np.array(1.5, np.float32)),
+                   np.array(0.75, np.float32), dev(np.array(0.75, np.float32)))
+    e = dev(np.zeros((0, 4), np.float32))
+    o = zk.binary_fwd("add", e, dev(np.ones((1, 4), np.float32)))
+    assert tuple(o.shape) == (0, 4)
+    _, gb = zk.binary_bwd("mul", dev(np.zeros((0, 4), np.float32)), e,
+                          dev(np.ones((4,), np.float32)))
+    np.testing.assert_array_equal(host(gb), np.zeros(4, np.float32))
+    # special values: x/0, 0/0, inf - inf, subnormals, signed zeros
+    a = np.array([1.0, 0.0, np.inf, 1e-40, -0.0, 3.0, -2.0, 1e38], np.float32)
+    b = np.array([0.0, 0.0, np.inf, 3.0, 0.0, -0.0, 1e-39, 1e-2], np.float32)
+    for op in OPS:
+        assert_bitexact(gpu_fwd(op, dev(a), dev(b)), orc.fwd(op, a, b), f"special {op}")
+
+
+def test_division_hard_cases(orc):
+    """Correctly rounded binary32 division on awkward quotients."""
+    rng = np.random.default_rng(61)
+    n = 1 << 20
+    a = (rng.standard_normal(n) * np.exp2(rng.integers(-126, 127, n))).astype(np.float32)
+    b = (rng.standard_normal(n) * np.exp2(rng.integers(-126, 127, n))).astype(np.float32)
+    b[::7] = np.exp2(rng.integers(-149, 128, b[::7].size).astype(np.float64)).astype(np.float32)
+    b[b == 0] = 1.0
+    assert_bitexact(gpu_fwd("div", dev(a), dev(b)), orc.fwd("div", a, b), "div")
+
+
+def test_gelu_forward_dense_sweep(orc):
+    """GeLU over 2^24 evenly spread binary32 values in [-12, 12]."""
+    h = np.linspace(-12, 12, 1 << 24, dtype=np.float32)
+    h[:16] = [0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -1e-45, 1e-38, -1e-38,
+              -0.7518, -5.5, 5.5, -9.4, -13.0, 6.0, -6.0]
+    z = np.zeros(1, np.float32)
+    got = gpu_fwd("add", dev(h), dev(z), epi="gelu")
+    want = orc.fwd("add", h, z, epi=orc.EPI_GELU)
+    nties = assert_gelu_exact(got, want, h)
+    say(f"  near-tie exceptions: {nties}")
+
+
+def test_determinism(orc):
+    """Two runs of the same backward give the same bits (no atomics)."""
+    h = W.gpt_residual(b=2, t=256, c=4096)
+    wl = steps.GPTResidual(host=h)
+    outs = []
+    for _ in range(2):
+        wl.run()
+        outs.append((host(wl.grad_h).copy(), host(wl.grad_gamma).copy()))
+    for x, y in zip(*outs):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    wl2 = steps.AttnScaleMask(host=W.attn_scale_mask(b=2, h=16, t=256))
+    r = []
+    for _ in range(2):
+        wl2.run()
+        r.append(host(wl2.grad_scale).copy())
+    assert np.array_equal(r[0].view(np.uint32), r[1].view(np.uint32))
+
+
+def test_mass_invariant_gpu():
+    rng = np.random.default_rng(71)
+    g = rng.standard_normal((64, 130, 64)).astype(np.float32)
+    for tgt in [(130, 1), (1, 64), (64, 1, 1), ()]:
+        r = host(zk.reduce_to_shape(dev(g), tgt)).astype(np.float64)
+        exact = math.fsum(g.astype(np.float64).ravel())
+        assert abs(r.sum() - exact) <= 2e-6 * np.abs(g).sum() + 1e-6 * r.size
+
+
+# --------------------------------------------- full sizes, sampled checks
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    s = rng.integers(0, n, k, dtype=np.int64)
+    return np.unique(np.concatenate([s, [0, n - 1]]))
+
+
+def _check_sampled_fwd(orc, op, a, b, got, seed, epi=0):
+    pos = _sample(got.size, 20000, seed)
+    want = orc.fwd_at(op, a, b, pos, epi=epi)
+    if epi:
+        h = orc.fwd_at(op, a, b, pos)
+        assert_gelu_exact(got.reshape(-1)[pos], want, h)
+    else:
+        assert_bitexact(got.reshape(-1)[pos], want, f"sampled fwd {op}")
+
+
+def _check_sampled_bwd(orc, op, which, g, a, b, got, seed, acc=None, epi=0, full=False):
+    n = got.size
+    pos = np.arange(n, dtype=np.int64) if full else _sample(n, 20000, seed)
+    ref = orc.bwd_at(op, which, g, a, b, pos, acc=acc, epi=epi)
+    assert_bwd(got.reshape(-1)[pos], ref, f"sampled bwd {op}/{which}")
+
+
+def test_full_size_xy_plus_x(orc):
+    wl = steps.XYPlusX()
+    h = wl.host
+    wl.run()
+    _check_sampled_fwd(orc, "mul", h["x"], h["y"], host(wl.t), 1)
+    t = host(wl.t)
+    _check_sampled_fwd(orc, "add", t, h["x"], host(wl.z), 2)
+    _check_sampled_bwd(orc, "mul", 0, h["g"], h["x"], h["y"], host(wl.grad_x), 3, acc=h["g"])
+    _check_sampled_bwd(orc, "mul", 1, h["g"], h["x"], h["y"], host(wl.grad_y), 4, full=True)
+
+
+def test_full_size_mlp_bias_gelu(orc):
+    wl = steps.MLPBiasGelu()
+    h = wl.host
+    wl.run()
+    y = host(wl.y)
+    want = orc.fwd("add", h["act"], h["bias"], epi=orc.EPI_GELU)
+    assert_gelu_exact(y, want, orc.fwd("add", h["act"], h["bias"]))
+    ra, rb = orc.bwd("add", h["g"], h["act"], h["bias"], epi=orc.EPI_GELU)
+    assert_bwd(host(wl.grad_act), ra, "grad_act")
+    assert_bwd(host(wl.grad_bias), rb, "grad_bias")
+
+
+def test_full_size_attn_scale_mask(orc):
+    wl = steps.AttnScaleMask()
+    h = wl.host
+    wl.run()
+    _check_sampled_fwd(orc, "mul", h["scores"], h["scale"], host(wl.t), 5)
+    _check_sampled_fwd(orc, "add", host(wl.t), h["mask"], host(wl.out), 6)
+    _check_sampled_bwd(orc, "mul", 0, h["g"], h["scores"], h["scale"],
+                       host(wl.grad_scores), 7)
+    _check_sampled_bwd(orc, "mul", 1, h["g"], h["scores"], h["scale"],
+                       host(wl.grad_scale), 8, full=True)
+
+
+def test_full_size_strided(orc):
+    wl = steps.StridedTransposed()
+    h = wl.host
+    wl.run()
+    va = orc.View(h["a_storage"], h["a_sizes"], h["a_strides"])
+    _check_sampled_fwd(orc, "mul", va, h["b"], host(wl.out), 9)
+    _check_sampled_bwd(orc, "mul", 0, h["g"], va, h["b"], host(wl.grad_a), 10)
+    _check_sampled_bwd(orc, "mul", 1, h["g"], va, h["b"], host(wl.grad_b), 11, full=True)
+
+
+def test_full_size_gpt_residual(orc):
+    wl = steps.GPTResidual()
+    h = wl.host
+    wl.run()
+    t = host(wl.t)
+    _check_sampled_fwd(orc, "mul", h["h"], h["gamma"], t, 12)
+    _check_sampled_fwd(orc, "add", t, h["resid"], host(wl.out), 13)
+    _check_sampled_bwd(orc, "mul", 0, h["g"], h["h"], h["gamma"], host(wl.grad_h), 14)
+    _check_sampled_bwd(orc, "mul", 1, h["g"], h["h"], h["gamma"], host(wl.grad_gamma), 15,
+                       full=True)
+    _check_sampled_bwd(orc, "add", 1, h["g"], t, h["resid"], host(wl.grad_resid), 16)
