@@ -21,7 +21,8 @@ def torch_mod():
 
 def dev(x):
     torch = torch_mod()
-    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    # np.array keeps 0-d arrays 0-d (ascontiguousarray would make them 1-d)
+    return torch.from_numpy(np.array(x, dtype=np.float32, order="C")).to("cuda")
 
 
 def strided_pair(storage, sizes, strides, offset=0):
