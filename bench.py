@@ -80,8 +80,13 @@ def capture(sets, torch):
         with torch.cuda.graph(g):
             s.run()
         graphs.append(g)
+    # all sets' steps back to back in one graph: fewer graph launches
+    chunk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chunk):
+        for s in sets:
+            s.run()
     torch.cuda.synchronize()
-    return graphs
+    return graphs, chunk
 
 
 def outputs(wl, torch):
@@ -106,16 +111,44 @@ def check_graph_replays(sets, graphs, torch):
         torch.cuda.synchronize()
 
 
-def time_steps(graphs, K, W, torch):
+def run_steps(graphs, chunk, K):
+    """Exactly K steps: whole chunks of len(graphs) steps, then single ones."""
     n = len(graphs)
-    for k in range(W):
-        graphs[k % n].replay()
+    for _ in range(K // n):
+        chunk.replay()
+    for k in range(K % n):
+        graphs[k].replay()
+
+
+def time_steps(graphs, chunk, K, W, torch):
+    run_steps(graphs, chunk, W)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(K):
-        graphs[k % n].replay()
+    run_steps(graphs, chunk, K)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def copy_ceiling(torch, nbytes=1 << 30, reps=20):
+    """Practical HBM ceiling: a plain 1 GiB device-to-device tensor copy
+    (read + write), timed the same way (graph, synchronised)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    g = torch.cuda.CUDAGraph()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        dst.copy_(src)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst, g
+    torch.cuda.empty_cache()
+    return 2 * nbytes / dt / 1e9
 
 
 def profile_calls(sets, reps, torch):
@@ -170,10 +203,10 @@ def spin_seconds(torch):
 def measure(name, host, K, W, torch, reps=None, check=True):
     from broadcast_autograd_amd import steps  # noqa: F401
     sets, fp = make_sets(name, host)
-    graphs = capture(sets, torch)
+    graphs, chunk = capture(sets, torch)
     if check:
         check_graph_replays(sets, graphs, torch)
-    secs = time_steps(graphs, K, W, torch)
+    secs = time_steps(graphs, chunk, K, W, torch)
     wl = sets[0]
     step_bytes = wl.step_bytes()
     if reps is None:
@@ -202,7 +235,7 @@ def measure(name, host, K, W, torch, reps=None, check=True):
     for k in ("step_gbs", "fwd_kernel_gbs", "bwd_kernel_gbs", "fwd_bwd_kernel_gbs"):
         if res[k] is not None:
             res[k.replace("gbs", "frac")] = res[k] * 1e9 / PEAK_HBM
-    del sets, graphs
+    del sets, graphs, chunk
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
@@ -253,6 +286,8 @@ def main():
            "gpt_residual": Wk.gpt_residual}
     log(f"[bench] device {torch.cuda.get_device_name(0)}; spin check "
         f"{spin_seconds(torch) * 1e3:.1f} ms")
+    ceiling = copy_ceiling(torch)
+    log(f"[bench] 1 GiB device copy: {ceiling:.1f} GB/s (read + write)")
     main_host = gen[args.workload]()
     log(f"[bench] main workload {args.workload}: {args.steps} steps")
     res = measure(args.workload, main_host, args.steps, args.warmup, torch)
@@ -318,7 +353,9 @@ def main():
                    "hbm_peak_frac": round(res["step_frac"], 4),
                    "fwd_kernel_gbs": round(res["fwd_kernel_gbs"], 1),
                    "bwd_kernel_gbs": round(res["bwd_kernel_gbs"], 1),
-                   "buffer_sets": res["buffer_sets"], "launch": "hip graph per step"},
+                   "buffer_sets": res["buffer_sets"],
+                   "launch": "hip graphs (one per rotation of buffer sets)",
+                   "copy_ceiling_gbs": round(ceiling, 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_config": {w: {k: (round(v, 4) if isinstance(v, float) else v)

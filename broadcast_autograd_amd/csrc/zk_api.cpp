@@ -124,9 +124,10 @@ zk_status zk_profile_start(int32_t capacity) {
   p.ids.assign(capacity > 0 ? capacity : 0, -1);
   p.next = 0;
   for (int i = 0; i < capacity; ++i) {
+    // No system-scope fence on record: the events only time device work.
     hipEvent_t a, b;
-    if (hipEventCreate(&a) != hipSuccess) return ZK_ERR_HIP;
-    if (hipEventCreate(&b) != hipSuccess) {
+    if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return ZK_ERR_HIP;
+    if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
       (void)hipEventDestroy(a);
       return ZK_ERR_HIP;
     }

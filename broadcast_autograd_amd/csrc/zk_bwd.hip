@@ -77,13 +77,20 @@ template <int OP, int EPI>
 __device__ __forceinline__ void ew_one(float gv, float x, float y, float aa,
                                        float ab, const EwArgs &ea, float &oa,
                                        float &ob) {
-  if (ea.write_a) {
-    float t = term32<OP, EPI, 0>(gv, x, y);
-    oa = ea.acc_a == 1 ? gv + t : (ea.acc_a == 2 ? aa + t : t);
-  }
-  if (ea.write_b) {
-    float t = term32<OP, EPI, 1>(gv, x, y);
-    ob = ea.acc_b == 1 ? gv + t : (ea.acc_b == 2 ? ab + t : t);
+  if constexpr (EPI == ZK_EPI_GELU) {
+    float ta, tb;
+    terms_ab<OP, EPI>(gv, x, y, ta, tb);
+    if (ea.write_a) oa = ea.acc_a == 1 ? gv + ta : (ea.acc_a == 2 ? aa + ta : ta);
+    if (ea.write_b) ob = ea.acc_b == 1 ? gv + tb : (ea.acc_b == 2 ? ab + tb : tb);
+  } else {
+    if (ea.write_a) {
+      float t = term32<OP, EPI, 0>(gv, x, y);
+      oa = ea.acc_a == 1 ? gv + t : (ea.acc_a == 2 ? aa + t : t);
+    }
+    if (ea.write_b) {
+      float t = term32<OP, EPI, 1>(gv, x, y);
+      ob = ea.acc_b == 1 ? gv + t : (ea.acc_b == 2 ? ab + t : t);
+    }
   }
 }
 
@@ -207,7 +214,9 @@ __global__ __launch_bounds__(kBlk) void k_red_col(
     const float *accbig, double *part, ColArgs ca) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
-  constexpr int U = 4;
+  // rows per loop trip: the GeLU epilogue is ALU-bound and wants fewer
+  // registers per wave; plain rules want more loads in flight
+  constexpr int U = EPI == ZK_EPI_GELU ? 1 : 4;
   __shared__ double lds[4][64][4];
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int64_t p = blockIdx.x / ca.colblocks;
@@ -223,8 +232,7 @@ __global__ __launch_bounds__(kBlk) void k_red_col(
   const int64_t r1 = r0 + ca.rc < ca.R ? r0 + ca.rc : ca.R;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
   if (active) {
-    for (int64_t rb = r0 + w; rb < r1; rb += 4 * U) {
-      float4 vg[U], vb[U], va[U];
+    auto load = [&](int64_t rb, float4 *vg, float4 *vb, float4 *va) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t r = rb + 4 * u;
@@ -235,23 +243,33 @@ __global__ __launch_bounds__(kBlk) void k_red_col(
           if constexpr (ACC == 2) va[u] = ld4(accbig + i);
         }
       }
+    };
+    for (int64_t rb = r0 + w; rb < r1; rb += 4 * U) {
+      float4 vg[U], vb[U], va[U];
+      load(rb, vg, vb, va);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t r = rb + 4 * u;
         if (r < r1) {
           const int64_t i = r * ca.K + c;
+          float gv[4], x[4], y[4], tb[4];
+          double ts[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            gv[k] = el(vg[u], k);
+            const float bv = NEED_BIG ? el(vb[u], k) : 0.f;
+            x[k] = SIDE == 0 ? sv[k] : bv;
+            y[k] = SIDE == 0 ? bv : sv[k];
+          }
+          terms2_w<OP, EPI, SIDE, 4>(gv, x, y, ts, tb);
           float4 ob;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const float gv = el(vg[u], k);
-            const float bv = NEED_BIG ? el(vb[u], k) : 0.f;
-            const float x = SIDE == 0 ? sv[k] : bv;
-            const float y = SIDE == 0 ? bv : sv[k];
-            s[k] += term64<OP, EPI, SIDE>(gv, x, y);
-            float tb = term32<OP, EPI, 1 - SIDE>(gv, x, y);
-            if constexpr (ACC == 1) tb = gv + tb;
-            if constexpr (ACC == 2) tb = el(va[u], k) + tb;
-            el(ob, k) = tb;
+            s[k] += ts[k];
+            float t = tb[k];
+            if constexpr (ACC == 1) t = gv[k] + t;
+            if constexpr (ACC == 2) t = el(va[u], k) + t;
+            el(ob, k) = t;
           }
           if (ca.write_big) st4(gbig + i, ob);
         }
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
     const float *accbig, double *part, RowRedArgs ra) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
-  constexpr int U = 4;
+  constexpr int U = EPI == ZK_EPI_GELU ? 1 : 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + w;
@@ -318,8 +336,10 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
           const float bv = NEED_BIG ? el(vb[u], q) : 0.f;
           const float x = SIDE == 0 ? sv : bv;
           const float y = SIDE == 0 ? bv : sv;
-          s += term64<OP, EPI, SIDE>(gv, x, y);
-          float tb = term32<OP, EPI, 1 - SIDE>(gv, x, y);
+          double ts;
+          float tb;
+          terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
+          s += ts;
           if constexpr (ACC == 1) tb = gv + tb;
           if constexpr (ACC == 2) tb = el(va[u], q) + tb;
           el(ob, q) = tb;
@@ -394,8 +414,10 @@ __global__ __launch_bounds__(kBlk) void k_red_tile(
             const float bv = NEED_BIG ? tile[4 * m + k][i] : 0.f;
             const float x = SIDE == 0 ? sv[k] : bv;
             const float y = SIDE == 0 ? bv : sv[k];
-            s[k] += term64<OP, EPI, SIDE>(gv, x, y);
-            float tb = term32<OP, EPI, 1 - SIDE>(gv, x, y);
+            double ts;
+            float tb;
+            terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
+            s[k] += ts;
             if constexpr (ACC == 1) tb = gv + tb;
             if constexpr (ACC == 2) tb = el(va, k) + tb;
             el(ob, k) = tb;
@@ -480,10 +502,12 @@ __global__ __launch_bounds__(kBlk) void k_red_generic(const float *g,
 }
 
 // ------------------------------------------------------------- red_final
-// out[k] = RN32(sum_p part[p][k] + acc[k]).  tpk threads per kept element
-// each sum a fixed strided subset of p; the subsets are then added in order.
+// out[k] = RN32(sum_p part[p][k] + acc[k]).  tpk (a power of two) threads
+// per kept element; thread q owns partials p = q + j*tpk, loads up to 8 of
+// them at once and adds them as a fixed tree, then the tpk subtotals meet in
+// an LDS tree.  Adjacent threads own adjacent k, so loads are coalesced.
 struct FinArgs {
-  int64_t K, P;
+  int64_t K, P, per;  // per: partials per thread
   int32_t tpk, kt, has_acc;
 };
 
@@ -494,15 +518,25 @@ __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
   const int t = threadIdx.x;
   const int kk = t % fa.kt, q = t / fa.kt;
   const int64_t k = (int64_t)blockIdx.x * fa.kt + kk;
+  const bool ok = k < fa.K;
   double s = 0.0;
-  if (k < fa.K) {
-    for (int64_t p = q; p < fa.P; p += fa.tpk) s += part[p * fa.K + k];
+  for (int64_t j0 = 0; j0 < fa.per; j0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t p = q + (j0 + j) * fa.tpk;
+      v[j] = (ok && j0 + j < fa.per && p < fa.P) ? part[p * fa.K + k] : 0.0;
+    }
+    s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
   }
   sh[t] = s;
   __syncthreads();
-  if (q == 0 && k < fa.K) {
-    double tot = 0.0;
-    for (int qq = 0; qq < fa.tpk; ++qq) tot += sh[kk + qq * fa.kt];
+  for (int off = fa.tpk >> 1; off >= 1; off >>= 1) {
+    if (q < off) sh[t] += sh[t + off * fa.kt];
+    __syncthreads();
+  }
+  if (q == 0 && ok) {
+    double tot = sh[kk];
     if (fa.has_acc) tot += (double)acc[k];
     out[k] = (float)tot;
   }
@@ -520,9 +554,10 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
   fa.K = rp.kept;
   fa.P = rp.partials;
   int tpk = 1;
-  while (tpk < 256 && rp.partials > 16 * (int64_t)tpk) tpk *= 2;
+  while (tpk < 256 && rp.partials > 8 * (int64_t)tpk) tpk *= 2;
   fa.tpk = tpk;
   fa.kt = kBlk / tpk;
+  fa.per = (rp.partials + tpk - 1) / tpk;
   fa.has_acc = acc != nullptr;
   ProfScope prof(st, K_RED_FINAL);
   hipLaunchKernelGGL(k_red_final, dim3(gridn(rp.kept, fa.kt)), dim3(kBlk), 0, st,

@@ -18,6 +18,15 @@ namespace zk {
 
 constexpr int kBlock = 256;
 
+// Vector accesses per thread of the streaming kernels: 4 keeps enough bytes
+// in flight for HBM; the GeLU epilogue is ALU-bound, where more waves with
+// one vector each schedule the long binary64 chains better.
+constexpr int row_unroll(int epi) { return epi == ZK_EPI_GELU ? 1 : 4; }
+
+// Launches give one block per tile; kernels loop over tiles with a grid
+// stride, so a grid capped here still covers any size.
+constexpr int64_t kMaxBlocks = (int64_t)1 << 30;
+
 template <int V>
 using IC = std::integral_constant<int, V>;
 
@@ -67,16 +76,28 @@ __global__ __launch_bounds__(kBlock) void k_fwd_flat(const float *a,
         vb[u] = ld4(b + i);
       }
     }
+    uint32_t redo_bits = 0;  // bit 4u+k: element needs the GeLU libm path
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int64_t i = base + (int64_t)u * kBlock * 4;
       if (i + 4 <= n) {
-        float4 r;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) el(r, k) = fwd32<OP, EPI>(el(va[u], k), el(vb[u], k));
-        st4(out + i, r);
+        const float x[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
+        const float y[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+        float r[4];
+        uint32_t redo;
+        fwd4_fast<OP, EPI>(x, y, r, redo);
+        redo_bits |= redo << (4 * u);
+        st4(out + i, make_float4(r[0], r[1], r[2], r[3]));
       } else if (i < n) {
         for (int64_t j = i; j < n; ++j) out[j] = fwd32<OP, EPI>(a[j], b[j]);
+      }
+    }
+    if constexpr (EPI == ZK_EPI_GELU) {
+      while (redo_bits) {  // rare: near a rounding tie
+        const int bit = __builtin_ctz(redo_bits);
+        redo_bits &= redo_bits - 1;
+        const int64_t j = base + (int64_t)(bit >> 2) * kBlock * 4 + (bit & 3);
+        out[j] = gelu32_libm_inl(op32<OP>(a[j], b[j]));
       }
     }
   } else {
@@ -123,53 +144,78 @@ template <int OP, int EPI, int VEC, int SMODE, bool SWAP, typename I>
 __global__ __launch_bounds__(kBlock) void k_fwd_row(const float *big,
                                                     const float *small,
                                                     float *out, RowArgs ra) {
-  constexpr int U = 4;
+  constexpr int U = row_unroll(EPI);
   constexpr I tile = (I)kBlock * U * VEC;
   const I n = (I)ra.numel;
   const I sin = (I)ra.ss[ra.rank - 1];
-  I base = (I)blockIdx.x * tile + (I)threadIdx.x * VEC;
   if constexpr (VEC == 4) {
-    float4 vb[U], vs[U];
+    // Tiles t = blockIdx.x, +gridDim.x, ... (the launch gives one per block).
+    const I ntiles = (n + tile - 1) / tile;
+    auto load = [&](I t, float4 *vb, float4 *vs) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      I i = base + (I)u * kBlock * 4;
-      if (i < n) {
-        vb[u] = ld4(big + i);
-        I off = row_offset<I>(ra, i);
-        if constexpr (SMODE == SM_BCAST) {
-          float s = small[off];
-          vs[u] = make_float4(s, s, s, s);
-        } else if constexpr (SMODE == SM_CONTIG) {
-          vs[u] = ld4(small + off);
-        } else {
+      for (int u = 0; u < U; ++u) {
+        const I i = t * tile + (I)threadIdx.x * 4 + (I)u * kBlock * 4;
+        if (i < n) {
+          vb[u] = ld4(big + i);
+          const I off = row_offset<I>(ra, i);
+          if constexpr (SMODE == SM_BCAST) {
+            const float s = small[off];
+            vs[u] = make_float4(s, s, s, s);
+          } else if constexpr (SMODE == SM_CONTIG) {
+            vs[u] = ld4(small + off);
+          } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) el(vs[u], k) = small[off + (I)k * sin];
+            for (int k = 0; k < 4; ++k) el(vs[u], k) = small[off + (I)k * sin];
+          }
         }
       }
-    }
+    };
+    for (I t = (I)blockIdx.x; t < ntiles; t += (I)gridDim.x) {
+      float4 vb[U], vs[U];
+      load(t, vb, vs);
+      const I base = t * tile + (I)threadIdx.x * 4;
+      uint32_t redo_bits = 0;  // bit 4u+k: element needs the GeLU libm path
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      I i = base + (I)u * kBlock * 4;
-      if (i < n) {
-        float4 r;
+      for (int u = 0; u < U; ++u) {
+        const I i = base + (I)u * kBlock * 4;
+        if (i < n) {
+          float x[4], y[4], r[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float x = SWAP ? el(vs[u], k) : el(vb[u], k);
-          float y = SWAP ? el(vb[u], k) : el(vs[u], k);
-          el(r, k) = fwd32<OP, EPI>(x, y);
+          for (int k = 0; k < 4; ++k) {
+            x[k] = SWAP ? el(vs[u], k) : el(vb[u], k);
+            y[k] = SWAP ? el(vb[u], k) : el(vs[u], k);
+          }
+          uint32_t redo;
+          fwd4_fast<OP, EPI>(x, y, r, redo);
+          redo_bits |= redo << (4 * u);
+          st4(out + i, make_float4(r[0], r[1], r[2], r[3]));
         }
-        st4(out + i, r);
+      }
+      if constexpr (EPI == ZK_EPI_GELU) {
+        while (redo_bits) {  // rare: near a rounding tie; reload the operands
+          const int bit = __builtin_ctz(redo_bits);
+          redo_bits &= redo_bits - 1;
+          const I i = base + (I)(bit >> 2) * kBlock * 4;
+          const I off = row_offset<I>(ra, i);
+          const int k = bit & 3;
+          float vsm;
+          if constexpr (SMODE == SM_BCAST) vsm = small[off];
+          else if constexpr (SMODE == SM_CONTIG) vsm = small[off + k];
+          else vsm = small[off + (I)k * sin];
+          const float vbig = big[i + k];
+          const float h = SWAP ? op32<OP>(vsm, vbig) : op32<OP>(vbig, vsm);
+          out[i + k] = gelu32_libm_inl(h);
+        }
       }
     }
   } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      I i = (I)blockIdx.x * tile + (I)u * kBlock + (I)threadIdx.x;
-      if (i < n) {
-        float vbig = big[i];
-        float vsm = small[row_offset<I>(ra, i)];
-        out[i] = SWAP ? fwd32<OP, EPI>(vsm, vbig) : fwd32<OP, EPI>(vbig, vsm);
-      }
+    // 64-bit loop counter: i + stride may pass 2^31 even when n does not
+    for (int64_t i64 = (int64_t)blockIdx.x * kBlock + threadIdx.x; i64 < (int64_t)n;
+         i64 += (int64_t)gridDim.x * kBlock) {
+      const I i = (I)i64;
+      const float vbig = big[i];
+      const float vsm = small[row_offset<I>(ra, i)];
+      out[i] = SWAP ? fwd32<OP, EPI>(vsm, vbig) : fwd32<OP, EPI>(vbig, vsm);
     }
   }
 }
@@ -304,7 +350,7 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
     ProfScope prof(st, p.kernel);
     switch (p.kernel) {
       case K_FWD_FLAT: {
-        constexpr int U = 4;
+        constexpr int U = row_unroll(EPI);
         if (p.vec == 4)
           hipLaunchKernelGGL((k_fwd_flat<OP, EPI, 4, U>), dim3(grid_of(c.numel, kBlock * U * 4)),
                              dim3(kBlock), 0, st, a, b, out, c.numel);
@@ -330,8 +376,10 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
           constexpr int SM = decltype(SMc)::value;
           constexpr bool SW = decltype(SWc)::value != 0;
           using I = std::conditional_t<decltype(Ic)::value != 0, int64_t, int32_t>;
-          hipLaunchKernelGGL((k_fwd_row<OP, EPI, VEC, SM, SW, I>),
-                             dim3(grid_of(c.numel, kBlock * 4 * VEC)), dim3(kBlock), 0, st,
+          int64_t blocks = grid_of(c.numel, kBlock * row_unroll(EPI) * VEC);
+          if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+          hipLaunchKernelGGL((k_fwd_row<OP, EPI, VEC, SM, SW, I>), dim3((unsigned)blocks),
+                             dim3(kBlock), 0, st,
                              big, small, out, ra);
           return hipGetLastError();
         };
