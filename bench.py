@@ -37,6 +37,46 @@ ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
        "rank8_div", "gpt_residual"]
 ROTATE_BYTES = 1 << 30  # per-workload footprint of the rotating buffer sets
 MAX_SETS = 32
+PEAK_FP64 = 78.6  # MI355X vector binary64, TFLOP/s (an FMA counts 2)
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "hbm_traffic.fetch_write_counters.txt")
+
+# Kernels bound by arithmetic rather than HBM: algorithmic binary64 flops per
+# output element of the path they run (an FMA counts 2).  The GeLU forward's
+# fast path: u, q and n (4), the exp reduction and degree-10 polynomial (22),
+# the reciprocal with two Newton steps (10), t and s (4), the degree-14
+# polynomial (28), E, Phi and y (5): 73.
+ALU_WORK = {("mlp_bias_gelu", "fwd_row"): 73}
+
+
+def source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    # device code, kernel argument blocks and the planner decide the traffic
+    for p in sorted(glob.glob(os.path.join(root, "broadcast_autograd_amd", "csrc", "*"))):
+        if p.endswith((".hip", ".h")) or p.endswith("zk_plan.cpp"):
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload, kernel):
+    """Counter-measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each
+    scaled by a plain copy of known size), or None when the kernels changed
+    since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    cur = source_hash()
+    for ln in lines:
+        p = ln.split()
+        if len(p) == 5 and p[0] == "traffic" and p[1] == workload and p[2] == kernel:
+            return int(p[3]) if p[4] == cur else None
+    return None
 
 
 def log(*a):
@@ -216,7 +256,7 @@ def measure(name, host, K, W, torch, reps=None, check=True):
     for i, c in enumerate(wl.calls):
         kern = {k: float(np.mean(v)) * 1e3 for k, v in prof[i].items()}  # us
         us = sum(kern.values())
-        calls.append(dict(name=c.name, kind=c.kind, bytes=c.bytes, us=us,
+        calls.append(dict(name=c.name, kind=c.kind, bytes=c.bytes, elements=c.elements, us=us,
                           kernels_us=kern, gbs=c.bytes / (us * 1e-6) / 1e9 if us else None))
     fwd_b = sum(c["bytes"] for c in calls if c["kind"] == "fwd")
     bwd_b = sum(c["bytes"] for c in calls if c["kind"] == "bwd")
@@ -270,6 +310,9 @@ def main():
                     help="comma list of other workloads to report, 'all' or 'none'")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--other-steps", type=int, default=None,
+                    help="timed steps of each other workload (default 40 for the "
+                         "1 GB-scale ones, 400 for the small ones)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -303,7 +346,7 @@ def main():
         else [w for w in args.others.split(",") if w and w != args.workload])
     for w in others:
         big = w in ("attn_scale_mask", "gpt_residual", "strided_transposed")
-        K = 40 if big else 400
+        K = args.other_steps or (40 if big else 400)
         log(f"[bench] workload {w}: {K} steps")
         r = measure(w, gen[w](), K, K // 10, torch)
         log(f"[bench]   {r['ms_per_step'] * 1e3:.2f} us/step, {r['step_gbs']:.1f} GB/s; "
@@ -317,11 +360,23 @@ def main():
             if best is None or us > best[2]:
                 best = (c, k, us)
     c, kname, kus = best
-    achieved = c["bytes"] / (kus * 1e-6) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
-            "unit": "GB/s", "frac": round(achieved * 1e9 / PEAK_HBM, 4),
-            "traffic": None, "kernel": kname, "call": c["name"],
-            "bytes_per_launch": c["bytes"], "us_per_launch": round(kus, 3)}
+    hbm = c["bytes"] / (kus * 1e-6) / 1e9
+    traffic = read_traffic(args.workload, kname)
+    alu = ALU_WORK.get((args.workload, kname))
+    if alu is not None:
+        flops = alu * c["elements"]
+        achieved = flops / (kus * 1e-6) / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP64,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP64, 4),
+                "traffic": traffic, "kernel": kname, "call": c["name"],
+                "flops_per_launch": flops, "flops_per_element": alu,
+                "bytes_per_launch": c["bytes"], "us_per_launch": round(kus, 3),
+                "hbm_gbs": round(hbm, 1), "hbm_frac": round(hbm * 1e9 / PEAK_HBM, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(hbm * 1e9 / PEAK_HBM, 4),
+                "traffic": traffic, "kernel": kname, "call": c["name"],
+                "bytes_per_launch": c["bytes"], "us_per_launch": round(kus, 3)}
 
     cpu = None
     if not args.no_cpu:

@@ -124,10 +124,12 @@ zk_status zk_profile_start(int32_t capacity) {
   p.ids.assign(capacity > 0 ? capacity : 0, -1);
   p.next = 0;
   for (int i = 0; i < capacity; ++i) {
-    // No system-scope fence on record: the events only time device work.
+    // Only device-scope release on record, no system-scope fence: the events
+    // only time device work, and cache write-backs would distort it.
+    const unsigned fl = hipEventDisableSystemFence | hipEventReleaseToDevice;
     hipEvent_t a, b;
-    if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return ZK_ERR_HIP;
-    if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
+    if (hipEventCreateWithFlags(&a, fl) != hipSuccess) return ZK_ERR_HIP;
+    if (hipEventCreateWithFlags(&b, fl) != hipSuccess) {
       (void)hipEventDestroy(a);
       return ZK_ERR_HIP;
     }

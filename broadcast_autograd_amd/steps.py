@@ -25,6 +25,7 @@ class Call:
     def __init__(self, name, kind, fn, reads, writes):
         self.name, self.kind, self.fn = name, kind, fn
         self.bytes = 4 * (sum(reads) + sum(writes))
+        self.elements = max(writes)  # elements of the largest output
 
     def __call__(self):
         return self.fn()
