@@ -96,18 +96,15 @@ Profiler &prof() {
 }  // namespace
 
 namespace zk {
-ProfScope::ProfScope(hipStream_t s, int32_t kernel) : slot(-1), st(s) {
+ProfScope::ProfScope(int32_t kernel) : slot(-1), ev_start(nullptr), ev_end(nullptr) {
   Profiler &p = prof();
   if (!p.on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> g(p.mu);
   if (p.next >= (int)p.start.size()) return;
   slot = p.next++;
   p.ids[slot] = kernel;
-  (void)hipEventRecord(p.start[slot], st);
-}
-ProfScope::~ProfScope() {
-  if (slot < 0) return;
-  (void)hipEventRecord(prof().end[slot], st);
+  ev_start = p.start[slot];
+  ev_end = p.end[slot];
 }
 }  // namespace zk
 
@@ -124,9 +121,8 @@ zk_status zk_profile_start(int32_t capacity) {
   p.ids.assign(capacity > 0 ? capacity : 0, -1);
   p.next = 0;
   for (int i = 0; i < capacity; ++i) {
-    // Only device-scope release on record, no system-scope fence: the events
-    // only time device work, and cache write-backs would distort it.
-    const unsigned fl = hipEventDisableSystemFence | hipEventReleaseToDevice;
+    // No system-scope fence: the events only time device work.
+    const unsigned fl = hipEventDisableSystemFence;
     hipEvent_t a, b;
     if (hipEventCreateWithFlags(&a, fl) != hipSuccess) return ZK_ERR_HIP;
     if (hipEventCreateWithFlags(&b, fl) != hipSuccess) {

@@ -559,9 +559,9 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
   fa.kt = kBlk / tpk;
   fa.per = (rp.partials + tpk - 1) / tpk;
   fa.has_acc = acc != nullptr;
-  ProfScope prof(st, K_RED_FINAL);
-  hipLaunchKernelGGL(k_red_final, dim3(gridn(rp.kept, fa.kt)), dim3(kBlk), 0, st,
-                     part, acc, out, fa);
+  ProfScope prof(K_RED_FINAL);
+  ZK_LAUNCH(prof, k_red_final, dim3(gridn(rp.kept, fa.kt)), dim3(kBlk), 0, st,
+            part, acc, out, fa);
   return hipGetLastError();
 }
 
@@ -613,22 +613,22 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
     e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
       constexpr int OP = decltype(OPc)::value;
       constexpr int EPI = decltype(EPIc)::value;
-      ProfScope prof(st, p.ew_kernel);
+      ProfScope prof(p.ew_kernel);
       if (p.ew_kernel == K_BWD_EW_FLAT) {
         if (p.vec == 4)
-          hipLaunchKernelGGL((k_bwd_ew_flat<OP, EPI, 4>), dim3(gridn(c.numel, kBlk * 16)),
-                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
+          ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 4>), dim3(gridn(c.numel, kBlk * 16)),
+                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
         else
-          hipLaunchKernelGGL((k_bwd_ew_flat<OP, EPI, 1>), dim3(gridn(c.numel, kBlk * 4)),
-                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
+          ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 1>), dim3(gridn(c.numel, kBlk * 4)),
+                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
       } else {
         Space sp = make_space(c);
         if (p.idx64)
-          hipLaunchKernelGGL((k_bwd_ew_generic<OP, EPI, int64_t>), dim3(gridn(c.numel, kBlk * 4)),
-                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, sp);
+          ZK_LAUNCH(prof, (k_bwd_ew_generic<OP, EPI, int64_t>), dim3(gridn(c.numel, kBlk * 4)),
+                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, sp);
         else
-          hipLaunchKernelGGL((k_bwd_ew_generic<OP, EPI, int32_t>), dim3(gridn(c.numel, kBlk * 4)),
-                             dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, sp);
+          ZK_LAUNCH(prof, (k_bwd_ew_generic<OP, EPI, int32_t>), dim3(gridn(c.numel, kBlk * 4)),
+                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, sp);
       }
       return hipGetLastError();
     });
@@ -649,7 +649,7 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
       e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
         constexpr int OP = decltype(OPc)::value;
         constexpr int EPI = decltype(EPIc)::value;
-        ProfScope prof(st, rp.kernel);
+        ProfScope prof(rp.kernel);
         switch (rp.kernel) {
           case K_RED_COL: {
             ColArgs ca{};
@@ -661,9 +661,9 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ca.write_big = p.fused_big;
             unsigned grid = (unsigned)(ca.colblocks * rp.partials);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
-              hipLaunchKernelGGL((k_red_col<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
-                                 dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
-                                 part, ca);
+              ZK_LAUNCH(prof, (k_red_col<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
+                        dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
+                        part, ca);
               return hipGetLastError();
             });
           }
@@ -679,9 +679,9 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ra.write_big = p.fused_big;
             unsigned grid = gridn(ra.items, 4);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
-              hipLaunchKernelGGL((k_red_row<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
-                                 dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
-                                 part, ra);
+              ZK_LAUNCH(prof, (k_red_row<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
+                        dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
+                        part, ra);
               return hipGetLastError();
             });
           }
@@ -696,9 +696,9 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ta.write_big = p.fused_big;
             unsigned grid = (unsigned)(ta.tiles_c * rp.partials);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
-              hipLaunchKernelGGL((k_red_tile<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
-                                 dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
-                                 part, ta);
+              ZK_LAUNCH(prof, (k_red_tile<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
+                        dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
+                        part, ta);
               return hipGetLastError();
             });
           }
@@ -707,18 +707,18 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             unsigned grid = gridn(rp.kept * rp.partials, kBlk);
             if (sw == 0) {
               if (p.idx64)
-                hipLaunchKernelGGL((k_red_generic<OP, EPI, 0, 0, int64_t>), dim3(grid), dim3(kBlk),
-                                   0, st, g, a, b, part, ga);
+                ZK_LAUNCH(prof, (k_red_generic<OP, EPI, 0, 0, int64_t>), dim3(grid), dim3(kBlk),
+                          0, st, g, a, b, part, ga);
               else
-                hipLaunchKernelGGL((k_red_generic<OP, EPI, 0, 0, int32_t>), dim3(grid), dim3(kBlk),
-                                   0, st, g, a, b, part, ga);
+                ZK_LAUNCH(prof, (k_red_generic<OP, EPI, 0, 0, int32_t>), dim3(grid), dim3(kBlk),
+                          0, st, g, a, b, part, ga);
             } else {
               if (p.idx64)
-                hipLaunchKernelGGL((k_red_generic<OP, EPI, 1, 0, int64_t>), dim3(grid), dim3(kBlk),
-                                   0, st, g, a, b, part, ga);
+                ZK_LAUNCH(prof, (k_red_generic<OP, EPI, 1, 0, int64_t>), dim3(grid), dim3(kBlk),
+                          0, st, g, a, b, part, ga);
               else
-                hipLaunchKernelGGL((k_red_generic<OP, EPI, 1, 0, int32_t>), dim3(grid), dim3(kBlk),
-                                   0, st, g, a, b, part, ga);
+                ZK_LAUNCH(prof, (k_red_generic<OP, EPI, 1, 0, int32_t>), dim3(grid), dim3(kBlk),
+                          0, st, g, a, b, part, ga);
             }
             return hipGetLastError();
           }
@@ -739,7 +739,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
     const RedPlan &rp = p.red[ri];
     double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + rp.ws_offset);
     if (rp.partials > 0) {
-      ProfScope prof(st, rp.kernel);
+      ProfScope prof(rp.kernel);
       switch (rp.kernel) {
         case K_RED_COL: {
           ColArgs ca{};
@@ -749,9 +749,9 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ca.ss = 0;
           ca.colblocks = (ca.K + 255) / 256;
           ca.write_big = 0;
-          hipLaunchKernelGGL((k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0>),
-                             dim3((unsigned)(ca.colblocks * rp.partials)), dim3(kBlk), 0, st,
-                             in, nullptr, nullptr, nullptr, nullptr, part, ca);
+          ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0>),
+                    dim3((unsigned)(ca.colblocks * rp.partials)), dim3(kBlk), 0, st,
+                    in, nullptr, nullptr, nullptr, nullptr, part, ca);
           break;
         }
         case K_RED_ROW: {
@@ -764,19 +764,19 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ra.items = (c.numel / ra.R0) * ra.NC;
           ra.ss = 0;
           ra.write_big = 0;
-          hipLaunchKernelGGL((k_red_row<ZK_ADD, ZK_EPI_NONE, 1, 0>), dim3(gridn(ra.items, 4)),
-                             dim3(kBlk), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ra);
+          ZK_LAUNCH(prof, (k_red_row<ZK_ADD, ZK_EPI_NONE, 1, 0>), dim3(gridn(ra.items, 4)),
+                    dim3(kBlk), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ra);
           break;
         }
         default: {
           GenArgs ga = make_gen(c, 4, 0, -1, -1, rp);
           unsigned grid = gridn(rp.kept * rp.partials, kBlk);
           if (p.idx64)
-            hipLaunchKernelGGL((k_red_generic<ZK_ADD, ZK_EPI_NONE, 1, 1, int64_t>), dim3(grid),
-                               dim3(kBlk), 0, st, in, nullptr, nullptr, part, ga);
+            ZK_LAUNCH(prof, (k_red_generic<ZK_ADD, ZK_EPI_NONE, 1, 1, int64_t>), dim3(grid),
+                      dim3(kBlk), 0, st, in, nullptr, nullptr, part, ga);
           else
-            hipLaunchKernelGGL((k_red_generic<ZK_ADD, ZK_EPI_NONE, 1, 1, int32_t>), dim3(grid),
-                               dim3(kBlk), 0, st, in, nullptr, nullptr, part, ga);
+            ZK_LAUNCH(prof, (k_red_generic<ZK_ADD, ZK_EPI_NONE, 1, 1, int32_t>), dim3(grid),
+                      dim3(kBlk), 0, st, in, nullptr, nullptr, part, ga);
         }
       }
       hipError_t e = hipGetLastError();

@@ -347,16 +347,16 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
   return with_op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
     constexpr int OP = decltype(OPc)::value;
     constexpr int EPI = decltype(EPIc)::value;
-    ProfScope prof(st, p.kernel);
+    ProfScope prof(p.kernel);
     switch (p.kernel) {
       case K_FWD_FLAT: {
         constexpr int U = row_unroll(EPI);
         if (p.vec == 4)
-          hipLaunchKernelGGL((k_fwd_flat<OP, EPI, 4, U>), dim3(grid_of(c.numel, kBlock * U * 4)),
-                             dim3(kBlock), 0, st, a, b, out, c.numel);
+          ZK_LAUNCH(prof, (k_fwd_flat<OP, EPI, 4, U>), dim3(grid_of(c.numel, kBlock * U * 4)),
+                    dim3(kBlock), 0, st, a, b, out, c.numel);
         else
-          hipLaunchKernelGGL((k_fwd_flat<OP, EPI, 1, U>), dim3(grid_of(c.numel, kBlock * U)),
-                             dim3(kBlock), 0, st, a, b, out, c.numel);
+          ZK_LAUNCH(prof, (k_fwd_flat<OP, EPI, 1, U>), dim3(grid_of(c.numel, kBlock * U)),
+                    dim3(kBlock), 0, st, a, b, out, c.numel);
         return hipGetLastError();
       }
       case K_FWD_ROW: {
@@ -378,9 +378,9 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
           using I = std::conditional_t<decltype(Ic)::value != 0, int64_t, int32_t>;
           int64_t blocks = grid_of(c.numel, kBlock * row_unroll(EPI) * VEC);
           if (blocks > kMaxBlocks) blocks = kMaxBlocks;
-          hipLaunchKernelGGL((k_fwd_row<OP, EPI, VEC, SM, SW, I>), dim3((unsigned)blocks),
-                             dim3(kBlock), 0, st,
-                             big, small, out, ra);
+          ZK_LAUNCH(prof, (k_fwd_row<OP, EPI, VEC, SM, SW, I>), dim3((unsigned)blocks),
+                    dim3(kBlock), 0, st,
+                    big, small, out, ra);
           return hipGetLastError();
         };
         auto go_i = [&](auto VECc, auto SMc, auto SWc) -> hipError_t {
@@ -414,8 +414,8 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         auto go = [&](auto OMc, auto SWc) -> hipError_t {
           constexpr int OM = decltype(OMc)::value;
           constexpr bool SW = decltype(SWc)::value != 0;
-          hipLaunchKernelGGL((k_fwd_tile<OP, EPI, OM, SW>), dim3(grid), dim3(kBlock), 0, st,
-                             tr, ot, out, ta);
+          ZK_LAUNCH(prof, (k_fwd_tile<OP, EPI, OM, SW>), dim3(grid), dim3(kBlock), 0, st,
+                    tr, ot, out, ta);
           return hipGetLastError();
         };
         auto go_sw = [&](auto OMc) -> hipError_t {
@@ -434,11 +434,11 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         }
         unsigned grid = grid_of(c.numel, kBlock * 4);
         if (p.idx64)
-          hipLaunchKernelGGL((k_fwd_generic<OP, EPI, int64_t>), dim3(grid), dim3(kBlock), 0, st,
-                             a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
+          ZK_LAUNCH(prof, (k_fwd_generic<OP, EPI, int64_t>), dim3(grid), dim3(kBlock), 0, st,
+                    a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
         else
-          hipLaunchKernelGGL((k_fwd_generic<OP, EPI, int32_t>), dim3(grid), dim3(kBlock), 0, st,
-                             a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
+          ZK_LAUNCH(prof, (k_fwd_generic<OP, EPI, int32_t>), dim3(grid), dim3(kBlock), 0, st,
+                    a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
         return hipGetLastError();
       }
     }

@@ -3,6 +3,7 @@
 // launchers implemented in the .hip files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,14 +31,24 @@ struct RedDims {
 
 Space make_space(const Canon &c);
 
-// Brackets one kernel launch with a HIP event pair on its stream while
-// zk_profile_start() is in effect; does nothing otherwise.
+// Reserves a HIP event pair for the one kernel launched in its scope while
+// zk_profile_start() is in effect (slot < 0 otherwise).  ZK_LAUNCH hands the
+// pair to hipExtLaunchKernel, so the events carry the kernel's own begin and
+// end timestamps from its dispatch packet, not those of separate markers.
 struct ProfScope {
-  ProfScope(hipStream_t st, int32_t kernel);
-  ~ProfScope();
+  explicit ProfScope(int32_t kernel);
   int slot;
-  hipStream_t st;
+  hipEvent_t ev_start, ev_end;
 };
+
+#define ZK_LAUNCH(ps, kernel, grid, block, shmem, st, ...)                    \
+  do {                                                                     \
+    if ((ps).slot >= 0)                                                    \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, (ps).ev_start,   \
+                            (ps).ev_end, 0, __VA_ARGS__);                  \
+    else                                                                   \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);      \
+  } while (0)
 
 hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
                       const float *b, float *out, hipStream_t st);
