@@ -27,6 +27,8 @@
 namespace zk {
 
 constexpr int kBlk = 256;
+// Waves per red_col block when its waves combine their sums in LDS.
+constexpr int kColWaves = 16;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -98,37 +100,53 @@ template <int OP, int EPI, int VEC>
 __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
     const float *g, const float *a, const float *b, float *ga,
     const float *acc_a, float *gb, const float *acc_b, EwArgs ea) {
-  constexpr int U = 4;
+  constexpr int U = 1;  // one vector per lane, one tile per block: streams best
   constexpr int64_t tile = (int64_t)kBlk * U * VEC;
-  if constexpr (VEC == 4) {
-    const int64_t base = (int64_t)blockIdx.x * tile + (int64_t)threadIdx.x * 4;
-    float4 vg[U], va[U], vb[U], xa[U], xb[U];
+  const int64_t ntiles = (ea.n + tile - 1) / tile;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    if constexpr (VEC == 4) {
+      const int64_t base = t * tile + (int64_t)threadIdx.x * 4;
+      float4 vg[U], va[U], vb[U], xa[U], xb[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t i = base + (int64_t)u * kBlk * 4;
-      if (i + 4 <= ea.n) {
-        vg[u] = ld4(g + i);
-        if (ea.read_a) va[u] = ld4(a + i);
-        if (ea.read_b) vb[u] = ld4(b + i);
-        if (ea.acc_a == 2) xa[u] = ld4(acc_a + i);
-        if (ea.acc_b == 2) xb[u] = ld4(acc_b + i);
+      for (int u = 0; u < U; ++u) {
+        int64_t i = base + (int64_t)u * kBlk * 4;
+        if (i + 4 <= ea.n) {
+          vg[u] = ld4_nt(g + i);
+          if (ea.read_a) va[u] = ld4_nt(a + i);
+          if (ea.read_b) vb[u] = ld4_nt(b + i);
+          if (ea.acc_a == 2) xa[u] = ld4_nt(acc_a + i);
+          if (ea.acc_b == 2) xb[u] = ld4_nt(acc_b + i);
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t i = base + (int64_t)u * kBlk * 4;
-      if (i + 4 <= ea.n) {
-        float4 oa, ob;
+      for (int u = 0; u < U; ++u) {
+        int64_t i = base + (int64_t)u * kBlk * 4;
+        if (i + 4 <= ea.n) {
+          float4 oa, ob;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          ew_one<OP, EPI>(el(vg[u], k), ea.read_a ? el(va[u], k) : 0.f,
-                          ea.read_b ? el(vb[u], k) : 0.f,
-                          ea.acc_a == 2 ? el(xa[u], k) : 0.f,
-                          ea.acc_b == 2 ? el(xb[u], k) : 0.f, ea, el(oa, k), el(ob, k));
-        if (ea.write_a) st4(ga + i, oa);
-        if (ea.write_b) st4(gb + i, ob);
-      } else if (i < ea.n) {
-        for (int64_t j = i; j < ea.n; ++j) {
+          for (int k = 0; k < 4; ++k)
+            ew_one<OP, EPI>(el(vg[u], k), ea.read_a ? el(va[u], k) : 0.f,
+                            ea.read_b ? el(vb[u], k) : 0.f,
+                            ea.acc_a == 2 ? el(xa[u], k) : 0.f,
+                            ea.acc_b == 2 ? el(xb[u], k) : 0.f, ea, el(oa, k), el(ob, k));
+          if (ea.write_a) st4_nt(ga + i, oa);
+          if (ea.write_b) st4_nt(gb + i, ob);
+        } else if (i < ea.n) {
+          for (int64_t j = i; j < ea.n; ++j) {
+            float oa = 0.f, ob = 0.f;
+            ew_one<OP, EPI>(g[j], ea.read_a ? a[j] : 0.f, ea.read_b ? b[j] : 0.f,
+                            ea.acc_a == 2 ? acc_a[j] : 0.f, ea.acc_b == 2 ? acc_b[j] : 0.f,
+                            ea, oa, ob);
+            if (ea.write_a) ga[j] = oa;
+            if (ea.write_b) gb[j] = ob;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int64_t j = t * tile + (int64_t)u * kBlk + threadIdx.x;
+        if (j < ea.n) {
           float oa = 0.f, ob = 0.f;
           ew_one<OP, EPI>(g[j], ea.read_a ? a[j] : 0.f, ea.read_b ? b[j] : 0.f,
                           ea.acc_a == 2 ? acc_a[j] : 0.f, ea.acc_b == 2 ? acc_b[j] : 0.f,
@@ -136,19 +154,6 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
           if (ea.write_a) ga[j] = oa;
           if (ea.write_b) gb[j] = ob;
         }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t j = (int64_t)blockIdx.x * tile + (int64_t)u * kBlk + threadIdx.x;
-      if (j < ea.n) {
-        float oa = 0.f, ob = 0.f;
-        ew_one<OP, EPI>(g[j], ea.read_a ? a[j] : 0.f, ea.read_b ? b[j] : 0.f,
-                        ea.acc_a == 2 ? acc_a[j] : 0.f, ea.acc_b == 2 ? acc_b[j] : 0.f,
-                        ea, oa, ob);
-        if (ea.write_a) ga[j] = oa;
-        if (ea.write_b) gb[j] = ob;
       }
     }
   }
@@ -181,44 +186,50 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_generic(
     const float *g, const float *a, const float *b, float *ga,
     const float *acc_a, float *gb, const float *acc_b, EwArgs ea, Space sp) {
   const I n = (I)ea.n;
-  const I i0 = ((I)blockIdx.x * kBlk + (I)threadIdx.x) * 4;
+  // 64-bit loop counter: i0 + stride may pass 2^31 even when n does not
+  for (int64_t j0 = ((int64_t)blockIdx.x * kBlk + threadIdx.x) * 4; j0 < (int64_t)n;
+       j0 += (int64_t)gridDim.x * kBlk * 4) {
+    const I i0 = (I)j0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    I i = i0 + k;
-    if (i < n) {
-      I oa, ob;
-      offs_ab<I>(sp, i, oa, ob);
-      float o1 = 0.f, o2 = 0.f;
-      ew_one<OP, EPI>(g[i], ea.read_a ? a[oa] : 0.f, ea.read_b ? b[ob] : 0.f,
-                      ea.acc_a == 2 ? acc_a[i] : 0.f, ea.acc_b == 2 ? acc_b[i] : 0.f,
-                      ea, o1, o2);
-      if (ea.write_a) ga[i] = o1;
-      if (ea.write_b) gb[i] = o2;
+    for (int k = 0; k < 4; ++k) {
+      I i = i0 + k;
+      if (i < n) {
+        I oa, ob;
+        offs_ab<I>(sp, i, oa, ob);
+        float o1 = 0.f, o2 = 0.f;
+        ew_one<OP, EPI>(g[i], ea.read_a ? a[oa] : 0.f, ea.read_b ? b[ob] : 0.f,
+                        ea.acc_a == 2 ? acc_a[i] : 0.f, ea.acc_b == 2 ? acc_b[i] : 0.f,
+                        ea, o1, o2);
+        if (ea.write_a) ga[i] = o1;
+        if (ea.write_b) gb[i] = o2;
+      }
     }
   }
 }
 
 // --------------------------------------------------------------- red_col
 // g, the full operand and its gradient are dense [R, K]; the small operand
-// is read at column c with stride ss.  Block = 4 waves on the same 256
-// columns, rows of its chunk interleaved across the waves; each lane keeps 4
-// binary64 column sums; the 4 waves are combined through LDS in wave order.
+// is read at column c with stride ss.  Each wave owns 256 columns (4 per
+// lane, 128-bit accesses) and walks rcw consecutive rows, keeping 4 binary64
+// column sums per lane.  NW waves of a block share the same columns and
+// consecutive row ranges; with NW > 1 their sums meet in LDS in wave order,
+// so one partial covers NW * rcw rows.
 struct ColArgs {
-  int64_t R, K, rc, ss, colblocks;
+  int64_t R, K, rcw, ss, colblocks;
   int32_t write_big;
 };
 
-template <int OP, int EPI, int SIDE, int ACC>
-__global__ __launch_bounds__(kBlk) void k_red_col(
+template <int OP, int EPI, int SIDE, int ACC, int NW>
+__global__ __launch_bounds__(64 * NW) void k_red_col(
     const float *g, const float *big, const float *small, float *gbig,
     const float *accbig, double *part, ColArgs ca) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
-  // rows per loop trip: the GeLU epilogue is ALU-bound and wants fewer
+  // rows in flight per wave: the GeLU epilogue is ALU-bound and wants fewer
   // registers per wave; plain rules want more loads in flight
-  constexpr int U = EPI == ZK_EPI_GELU ? 1 : 4;
-  __shared__ double lds[4][64][4];
-  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  constexpr int U = EPI == ZK_EPI_GELU ? 1 : 2;
+  const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int l = threadIdx.x & 63;
   const int64_t p = blockIdx.x / ca.colblocks;
   const int64_t cb = blockIdx.x - p * ca.colblocks;
   const int64_t c = cb * 256 + 4 * l;
@@ -228,28 +239,25 @@ __global__ __launch_bounds__(kBlk) void k_red_col(
 #pragma unroll
     for (int k = 0; k < 4; ++k) sv[k] = small[(c + k) * ca.ss];
   }
-  const int64_t r0 = p * ca.rc;
-  const int64_t r1 = r0 + ca.rc < ca.R ? r0 + ca.rc : ca.R;
+  const int64_t r0 = (p * NW + w) * ca.rcw;
+  const int64_t r1 = r0 + ca.rcw < ca.R ? r0 + ca.rcw : ca.R;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
   if (active) {
-    auto load = [&](int64_t rb, float4 *vg, float4 *vb, float4 *va) {
+    for (int64_t rb = r0; rb < r1; rb += U) {
+      float4 vg[U], vb[U], va[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t r = rb + 4 * u;
+        const int64_t r = rb + u;
         if (r < r1) {
           const int64_t i = r * ca.K + c;
-          vg[u] = ld4(g + i);
-          if constexpr (NEED_BIG) vb[u] = ld4(big + i);
-          if constexpr (ACC == 2) va[u] = ld4(accbig + i);
+          vg[u] = ld4_nt(g + i);
+          if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
+          if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
         }
       }
-    };
-    for (int64_t rb = r0 + w; rb < r1; rb += 4 * U) {
-      float4 vg[U], vb[U], va[U];
-      load(rb, vg, vb, va);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t r = rb + 4 * u;
+        const int64_t r = rb + u;
         if (r < r1) {
           const int64_t i = r * ca.K + c;
           float gv[4], x[4], y[4], tb[4];
@@ -271,19 +279,29 @@ __global__ __launch_bounds__(kBlk) void k_red_col(
             if constexpr (ACC == 2) t = el(va[u], k) + t;
             el(ob, k) = t;
           }
-          if (ca.write_big) st4(gbig + i, ob);
+          if (ca.write_big) st4_nt(gbig + i, ob);
         }
       }
     }
   }
+  if constexpr (NW == 1) {
+    if (active) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) lds[w][l][k] = s[k];
-  __syncthreads();
-  if (w == 0 && active) {
+      for (int k = 0; k < 4; ++k) part[p * ca.K + c + k] = s[k];
+    }
+  } else {
+    __shared__ double lds[NW][4][64];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      double tot = ((lds[0][l][k] + lds[1][l][k]) + lds[2][l][k]) + lds[3][l][k];
-      part[p * ca.K + c + k] = tot;
+    for (int k = 0; k < 4; ++k) lds[w][k][l] = s[k];
+    __syncthreads();
+    if (w == 0 && active) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        double tot = lds[0][k][l];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) tot += lds[ww][k][l];
+        part[p * ca.K + c + k] = tot;
+      }
     }
   }
 }
@@ -302,54 +320,57 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
     const float *accbig, double *part, RowRedArgs ra) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
-  constexpr int U = EPI == ZK_EPI_GELU ? 1 : 4;
+  // one vector per lane per trip over short chunks (many waves) streams best
+  constexpr int U = 1;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + w;
-  if (item >= ra.items) return;
-  const int64_t row = item / ra.NC, ch = item - row * ra.NC;
-  const int64_t r1 = row / ra.K, k = row - r1 * ra.K;
-  const float sv = NEED_SMALL ? small[k * ra.ss] : 0.f;
-  const int64_t e0 = row * ra.R0 + ch * ra.CL;
-  const int64_t lim = (ch + 1) * ra.CL < ra.R0 ? (ch + 1) * ra.CL : ra.R0;
-  const int64_t e1 = row * ra.R0 + lim;
-  double s = 0.0;
-  for (int64_t eb = e0 + 4 * l; eb < e1; eb += 256 * U) {
-    float4 vg[U], vb[U], va[U];
+  // items (row, chunk) item = 4 * blockIdx.x + w, then with a grid stride
+  for (int64_t item = (int64_t)blockIdx.x * 4 + w; item < ra.items;
+       item += (int64_t)gridDim.x * 4) {
+    const int64_t row = item / ra.NC, ch = item - row * ra.NC;
+    const int64_t r1 = row / ra.K, k = row - r1 * ra.K;
+    const float sv = NEED_SMALL ? small[k * ra.ss] : 0.f;
+    const int64_t e0 = row * ra.R0 + ch * ra.CL;
+    const int64_t lim = (ch + 1) * ra.CL < ra.R0 ? (ch + 1) * ra.CL : ra.R0;
+    const int64_t e1 = row * ra.R0 + lim;
+    double s = 0.0;
+    for (int64_t eb = e0 + 4 * l; eb < e1; eb += 256 * U) {
+      float4 vg[U], vb[U], va[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = eb + 256 * u;
-      if (i < e1) {
-        vg[u] = ld4(g + i);
-        if constexpr (NEED_BIG) vb[u] = ld4(big + i);
-        if constexpr (ACC == 2) va[u] = ld4(accbig + i);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = eb + 256 * u;
-      if (i < e1) {
-        float4 ob;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float gv = el(vg[u], q);
-          const float bv = NEED_BIG ? el(vb[u], q) : 0.f;
-          const float x = SIDE == 0 ? sv : bv;
-          const float y = SIDE == 0 ? bv : sv;
-          double ts;
-          float tb;
-          terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
-          s += ts;
-          if constexpr (ACC == 1) tb = gv + tb;
-          if constexpr (ACC == 2) tb = el(va[u], q) + tb;
-          el(ob, q) = tb;
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = eb + 256 * u;
+        if (i < e1) {
+          vg[u] = ld4_nt(g + i);
+          if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
+          if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
         }
-        if (ra.write_big) st4(gbig + i, ob);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = eb + 256 * u;
+        if (i < e1) {
+          float4 ob;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float gv = el(vg[u], q);
+            const float bv = NEED_BIG ? el(vb[u], q) : 0.f;
+            const float x = SIDE == 0 ? sv : bv;
+            const float y = SIDE == 0 ? bv : sv;
+            double ts;
+            float tb;
+            terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
+            s += ts;
+            if constexpr (ACC == 1) tb = gv + tb;
+            if constexpr (ACC == 2) tb = el(va[u], q) + tb;
+            el(ob, q) = tb;
+          }
+          if (ra.write_big) st4_nt(gbig + i, ob);
+        }
       }
     }
+    s = wave_sum(s);
+    if (l == 0) part[(r1 * ra.NC + ch) * ra.K + k] = s;
   }
-  s = wave_sum(s);
-  if (l == 0) part[(r1 * ra.NC + ch) * ra.K + k] = s;
 }
 
 // -------------------------------------------------------------- red_tile
@@ -357,7 +378,7 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
 // the full operand's gradient are dense [R, K].  Block = 64 columns x a
 // chunk of rows walked in 64-row tiles.
 struct TileRedArgs {
-  int64_t R, K, ld, ss, rc, tiles_c;
+  int64_t R, K, ld, ss, rc, tiles_c, items;
   int32_t write_big;
 };
 
@@ -370,72 +391,76 @@ __global__ __launch_bounds__(kBlk) void k_red_tile(
   __shared__ float tile[64][65];
   __shared__ double red[16][64];
   const int t = threadIdx.x;
-  const int64_t p = blockIdx.x / ta.tiles_c;
-  const int64_t tj = blockIdx.x - p * ta.tiles_c;
-  const int64_t j0 = tj * 64;
-  const int m = t & 15, q = t >> 4;
-  const int64_t gj = j0 + 4 * m;
-  const bool colok = gj < ta.K;  // K % 4 == 0, so all 4 columns are in range
-  float sv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (NEED_SMALL && colok) {
+  // (row chunk p, 64-column tile tj) items, one per block up to the grid cap
+  for (int64_t bt = blockIdx.x; bt < ta.items; bt += gridDim.x) {
+    const int64_t p = bt / ta.tiles_c;
+    const int64_t tj = bt - p * ta.tiles_c;
+    const int64_t j0 = tj * 64;
+    const int m = t & 15, q = t >> 4;
+    const int64_t gj = j0 + 4 * m;
+    const bool colok = gj < ta.K;  // K % 4 == 0, so all 4 columns are in range
+    float sv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (NEED_SMALL && colok) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sv[k] = small[(gj + k) * ta.ss];
-  }
-  const int64_t r0 = p * ta.rc;
-  const int64_t r1 = r0 + ta.rc < ta.R ? r0 + ta.rc : ta.R;
-  double s[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int64_t ti = r0; ti < r1; ti += 64) {
-    if constexpr (NEED_BIG) {
-      const int i = t & 63, jq = t >> 6;
-      const int64_t gi = ti + i;
-#pragma unroll
-      for (int pp = 0; pp < 16; ++pp) {
-        const int j = jq + 4 * pp;
-        float v = 0.f;
-        if (gi < r1 && j0 + j < ta.K) v = big[gi + (j0 + j) * ta.ld];
-        tile[j][i] = v;
-      }
-      __syncthreads();
+      for (int k = 0; k < 4; ++k) sv[k] = small[(gj + k) * ta.ss];
     }
-    if (colok) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int i = q + 16 * pp;
+    const int64_t r0 = p * ta.rc;
+    const int64_t r1 = r0 + ta.rc < ta.R ? r0 + ta.rc : ta.R;
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int64_t ti = r0; ti < r1; ti += 64) {
+      if constexpr (NEED_BIG) {
+        const int i = t & 63, jq = t >> 6;
         const int64_t gi = ti + i;
-        if (gi < r1) {
-          const int64_t off = gi * ta.K + gj;
-          const float4 vg = ld4(g + off);
-          float4 va;
-          if constexpr (ACC == 2) va = ld4(accbig + off);
-          float4 ob;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float gv = el(vg, k);
-            const float bv = NEED_BIG ? tile[4 * m + k][i] : 0.f;
-            const float x = SIDE == 0 ? sv[k] : bv;
-            const float y = SIDE == 0 ? bv : sv[k];
-            double ts;
-            float tb;
-            terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
-            s[k] += ts;
-            if constexpr (ACC == 1) tb = gv + tb;
-            if constexpr (ACC == 2) tb = el(va, k) + tb;
-            el(ob, k) = tb;
+        for (int pp = 0; pp < 16; ++pp) {
+          const int j = jq + 4 * pp;
+          float v = 0.f;
+          if (gi < r1 && j0 + j < ta.K) v = big[gi + (j0 + j) * ta.ld];
+          tile[j][i] = v;
+        }
+        __syncthreads();
+      }
+      if (colok) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int i = q + 16 * pp;
+          const int64_t gi = ti + i;
+          if (gi < r1) {
+            const int64_t off = gi * ta.K + gj;
+            const float4 vg = ld4_nt(g + off);
+            float4 va;
+            if constexpr (ACC == 2) va = ld4_nt(accbig + off);
+            float4 ob;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float gv = el(vg, k);
+              const float bv = NEED_BIG ? tile[4 * m + k][i] : 0.f;
+              const float x = SIDE == 0 ? sv[k] : bv;
+              const float y = SIDE == 0 ? bv : sv[k];
+              double ts;
+              float tb;
+              terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
+              s[k] += ts;
+              if constexpr (ACC == 1) tb = gv + tb;
+              if constexpr (ACC == 2) tb = el(va, k) + tb;
+              el(ob, k) = tb;
+            }
+            if (ta.write_big) st4_nt(gbig + off, ob);
           }
-          if (ta.write_big) st4(gbig + off, ob);
         }
       }
+      if constexpr (NEED_BIG) __syncthreads();
     }
-    if constexpr (NEED_BIG) __syncthreads();
-  }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) red[q][4 * m + k] = s[k];
-  __syncthreads();
-  if (t < 64 && j0 + t < ta.K) {
-    double tot = 0.0;
+    for (int k = 0; k < 4; ++k) red[q][4 * m + k] = s[k];
+    __syncthreads();
+    if (t < 64 && j0 + t < ta.K) {
+      double tot = 0.0;
 #pragma unroll
-    for (int qq = 0; qq < 16; ++qq) tot += red[qq][t];
-    part[p * ta.K + j0 + t] = tot;
+      for (int qq = 0; qq < 16; ++qq) tot += red[qq][t];
+      part[p * ta.K + j0 + t] = tot;
+    }
+    __syncthreads();  // red and tile are rewritten by the next item
   }
 }
 
@@ -455,50 +480,52 @@ __global__ __launch_bounds__(kBlk) void k_red_generic(const float *g,
                                                       const float *a,
                                                       const float *b,
                                                       double *part, GenArgs ga) {
-  const I gid = (I)blockIdx.x * kBlk + (I)threadIdx.x;
-  if (gid >= (I)(ga.K * ga.P)) return;
-  const I k = gid % (I)ga.K, p = gid / (I)ga.K;
-  I og = 0, oa = 0, ob = 0;
-  {
-    I rest = k;
+  for (int64_t gid64 = (int64_t)blockIdx.x * kBlk + threadIdx.x; gid64 < ga.K * ga.P;
+       gid64 += (int64_t)gridDim.x * kBlk) {
+    const I gid = (I)gid64;
+    const I k = gid % (I)ga.K, p = gid / (I)ga.K;
+    I og = 0, oa = 0, ob = 0;
+    {
+      I rest = k;
 #pragma unroll
-    for (int d = kMaxDims - 1; d >= 0; --d) {
-      if (d < ga.nk) {
-        const I n = (I)ga.kn[d];
-        const I q = rest / n, c = rest - q * n;
-        og += c * (I)ga.ks[0][d];
-        oa += c * (I)ga.ks[1][d];
-        ob += c * (I)ga.ks[2][d];
-        rest = q;
+      for (int d = kMaxDims - 1; d >= 0; --d) {
+        if (d < ga.nk) {
+          const I n = (I)ga.kn[d];
+          const I q = rest / n, c = rest - q * n;
+          og += c * (I)ga.ks[0][d];
+          oa += c * (I)ga.ks[1][d];
+          ob += c * (I)ga.ks[2][d];
+          rest = q;
+        }
       }
     }
-  }
-  const I lo = p * (I)ga.chunk;
-  const I hi = lo + (I)ga.chunk < (I)ga.red ? lo + (I)ga.chunk : (I)ga.red;
-  double s = 0.0;
-  for (I tt = lo; tt < hi; ++tt) {
-    I rest = tt, dg = 0, da = 0, db = 0;
+    const I lo = p * (I)ga.chunk;
+    const I hi = lo + (I)ga.chunk < (I)ga.red ? lo + (I)ga.chunk : (I)ga.red;
+    double s = 0.0;
+    for (I tt = lo; tt < hi; ++tt) {
+      I rest = tt, dg = 0, da = 0, db = 0;
 #pragma unroll
-    for (int d = kMaxDims - 1; d >= 0; --d) {
-      if (d < ga.nr) {
-        const I n = (I)ga.rn[d];
-        const I q = rest / n, c = rest - q * n;
-        dg += c * (I)ga.rs[0][d];
-        da += c * (I)ga.rs[1][d];
-        db += c * (I)ga.rs[2][d];
-        rest = q;
+      for (int d = kMaxDims - 1; d >= 0; --d) {
+        if (d < ga.nr) {
+          const I n = (I)ga.rn[d];
+          const I q = rest / n, c = rest - q * n;
+          dg += c * (I)ga.rs[0][d];
+          da += c * (I)ga.rs[1][d];
+          db += c * (I)ga.rs[2][d];
+          rest = q;
+        }
+      }
+      const float gv = g[og + dg];
+      if constexpr (IDENT) {
+        s += (double)gv;
+      } else {
+        const float x = reads_x<OP, EPI, WHICH>() ? a[oa + da] : 0.f;
+        const float y = reads_y<OP, EPI, WHICH>() ? b[ob + db] : 0.f;
+        s += term64<OP, EPI, WHICH>(gv, x, y);
       }
     }
-    const float gv = g[og + dg];
-    if constexpr (IDENT) {
-      s += (double)gv;
-    } else {
-      const float x = reads_x<OP, EPI, WHICH>() ? a[oa + da] : 0.f;
-      const float y = reads_y<OP, EPI, WHICH>() ? b[ob + db] : 0.f;
-      s += term64<OP, EPI, WHICH>(gv, x, y);
-    }
+    part[p * (I)ga.K + k] = s;
   }
-  part[p * (I)ga.K + k] = s;
 }
 
 // ------------------------------------------------------------- red_final
@@ -517,34 +544,42 @@ __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
   __shared__ double sh[kBlk];
   const int t = threadIdx.x;
   const int kk = t % fa.kt, q = t / fa.kt;
-  const int64_t k = (int64_t)blockIdx.x * fa.kt + kk;
-  const bool ok = k < fa.K;
-  double s = 0.0;
-  for (int64_t j0 = 0; j0 < fa.per; j0 += 8) {
-    double v[8];
+  const int64_t groups = (fa.K + fa.kt - 1) / fa.kt;
+  for (int64_t kg = blockIdx.x; kg < groups; kg += gridDim.x) {
+    const int64_t k = kg * fa.kt + kk;
+    const bool ok = k < fa.K;
+    double s = 0.0;
+    for (int64_t j0 = 0; j0 < fa.per; j0 += 8) {
+      double v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t p = q + (j0 + j) * fa.tpk;
-      v[j] = (ok && j0 + j < fa.per && p < fa.P) ? part[p * fa.K + k] : 0.0;
+      for (int j = 0; j < 8; ++j) {
+        const int64_t p = q + (j0 + j) * fa.tpk;
+        v[j] = (ok && j0 + j < fa.per && p < fa.P) ? part[p * fa.K + k] : 0.0;
+      }
+      s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     }
-    s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-  }
-  sh[t] = s;
-  __syncthreads();
-  for (int off = fa.tpk >> 1; off >= 1; off >>= 1) {
-    if (q < off) sh[t] += sh[t + off * fa.kt];
+    sh[t] = s;
     __syncthreads();
-  }
-  if (q == 0 && ok) {
-    double tot = sh[kk];
-    if (fa.has_acc) tot += (double)acc[k];
-    out[k] = (float)tot;
+    for (int off = fa.tpk >> 1; off >= 1; off >>= 1) {
+      if (q < off) sh[t] += sh[t + off * fa.kt];
+      __syncthreads();
+    }
+    if (q == 0 && ok) {
+      double tot = sh[kk];
+      if (fa.has_acc) tot += (double)acc[k];
+      out[k] = (float)tot;
+    }
+    __syncthreads();  // sh is rewritten by the next group
   }
 }
 
 // -------------------------------------------------------------- launchers
+// Grids are capped (a dispatch counts work-items with 32 bits); kernels
+// launched through gridn loop over their work with a grid stride.
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 static inline unsigned gridn(int64_t n, int64_t per) {
-  return (unsigned)((n + per - 1) / per);
+  const int64_t g = (n + per - 1) / per;
+  return (unsigned)(g < kMaxGrid ? g : kMaxGrid);
 }
 
 static hipError_t launch_final(const RedPlan &rp, const double *part,
@@ -553,8 +588,12 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
   FinArgs fa{};
   fa.K = rp.kept;
   fa.P = rp.partials;
+  // Threads per kept element: enough that each loads about 8 partials, but
+  // at most 16 once there are many kept elements, so that a wave still reads
+  // runs of >= 16 consecutive k (128 B) from each partial row.
+  const int max_tpk = rp.kept >= 1024 ? 16 : 256;
   int tpk = 1;
-  while (tpk < 256 && rp.partials > 8 * (int64_t)tpk) tpk *= 2;
+  while (tpk < max_tpk && rp.partials > 8 * (int64_t)tpk) tpk *= 2;
   fa.tpk = tpk;
   fa.kt = kBlk / tpk;
   fa.per = (rp.partials + tpk - 1) / tpk;
@@ -616,10 +655,10 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
       ProfScope prof(p.ew_kernel);
       if (p.ew_kernel == K_BWD_EW_FLAT) {
         if (p.vec == 4)
-          ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 4>), dim3(gridn(c.numel, kBlk * 16)),
+          ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 4>), dim3(gridn(c.numel, kBlk * 4)),
                     dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
         else
-          ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 1>), dim3(gridn(c.numel, kBlk * 4)),
+          ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 1>), dim3(gridn(c.numel, kBlk)),
                     dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
       } else {
         Space sp = make_space(c);
@@ -655,15 +694,19 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ColArgs ca{};
             ca.R = c.n[0];
             ca.K = c.n[1];
-            ca.rc = rp.chunk;
+            ca.rcw = rp.chunk;
             ca.ss = c.s[1 + sw][1];
             ca.colblocks = (ca.K + 255) / 256;
             ca.write_big = p.fused_big;
             unsigned grid = (unsigned)(ca.colblocks * rp.partials);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
-              ZK_LAUNCH(prof, (k_red_col<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
-                        dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
-                        part, ca);
+              constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
+              if (rp.nw == 1)
+                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, 1>), dim3(grid), dim3(64), 0, st, g,
+                          big, small, gbig, accbig, part, ca);
+              else
+                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, kColWaves>), dim3(grid),
+                          dim3(64 * kColWaves), 0, st, g, big, small, gbig, accbig, part, ca);
               return hipGetLastError();
             });
           }
@@ -693,8 +736,9 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ta.ss = c.s[1 + sw][1];
             ta.rc = rp.chunk;
             ta.tiles_c = (ta.K + 63) / 64;
+            ta.items = ta.tiles_c * rp.partials;
             ta.write_big = p.fused_big;
-            unsigned grid = (unsigned)(ta.tiles_c * rp.partials);
+            unsigned grid = gridn(ta.items, 1);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               ZK_LAUNCH(prof, (k_red_tile<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
                         dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
@@ -745,13 +789,18 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ColArgs ca{};
           ca.R = c.n[0];
           ca.K = c.n[1];
-          ca.rc = rp.chunk;
+          ca.rcw = rp.chunk;
           ca.ss = 0;
           ca.colblocks = (ca.K + 255) / 256;
           ca.write_big = 0;
-          ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0>),
-                    dim3((unsigned)(ca.colblocks * rp.partials)), dim3(kBlk), 0, st,
-                    in, nullptr, nullptr, nullptr, nullptr, part, ca);
+          const unsigned grid = (unsigned)(ca.colblocks * rp.partials);
+          if (rp.nw == 1)
+            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, 1>), dim3(grid), dim3(64), 0,
+                      st, in, nullptr, nullptr, nullptr, nullptr, part, ca);
+          else
+            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, kColWaves>), dim3(grid),
+                      dim3(64 * kColWaves), 0, st, in, nullptr, nullptr, nullptr, nullptr, part,
+                      ca);
           break;
         }
         case K_RED_ROW: {

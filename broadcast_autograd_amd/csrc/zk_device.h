@@ -141,10 +141,16 @@ __device__ __forceinline__ void gelu32_fast_w(const float (&h)[W], float (&f)[W]
     // or zero) always take the libm path.
     const uint32_t lo = (uint32_t)__double_as_longlong(y);
     const uint32_t dist = (lo & 0x1fffffffu) - (0x10000000u - 0x8000u);
+    uint32_t near = (uint32_t)(dist < 0x10000u || fabs(y) < 0x1p-126);
+    float fy = (float)y;
+    // Keep the fast value unconditional: left alone, the compiler turns the
+    // select below into a branch per element around the whole evaluation,
+    // which serialises the W independent chains.
+    asm volatile("" : "+v"(fy), "+v"(near));
     const bool fin = __builtin_isfinite(h[k]);
-    redo |= (uint32_t)(fin && (dist < 0x10000u || fabs(y) < 0x1p-126)) << k;
+    redo |= (fin ? near : 0u) << k;
     // limits: +inf -> +inf, -inf -> -0, NaN -> NaN
-    f[k] = fin ? (float)y : (__builtin_isnan(h[k]) || h[k] > 0.f ? h[k] : -0.0f);
+    f[k] = fin ? fy : (__builtin_isnan(h[k]) || h[k] > 0.f ? h[k] : -0.0f);
   }
 }
 
@@ -188,6 +194,34 @@ __device__ __forceinline__ void phi_pair_f32(float h, double &Phi, double &pdf) 
   const double E = (double)(g * rc) * eq;
   Phi = h < 0.f ? 0.5 * E : fma(-0.5, E, 1.0);
   pdf = eq * 0.39894228040143267794;
+}
+
+// g * GeLU'(h) = g*Phi(h) + (g*h)*phi(h) entirely in binary32, valid for
+// |h| <= kGeluGradFastMax, where exp(-h^2/2) >= 2^-60 and every intermediate
+// is a normal binary32 number.  Same steps as phi_pair_f32: relative error
+// of Phi and phi below ~8e-7, plus three binary32 roundings of the products,
+// i.e. within ~1.1e-6 of the sum of the magnitudes of the two terms.
+constexpr float kGeluGradFastMax = 9.0f;
+__device__ __forceinline__ float gelu_grad_f32(float g, float h) {
+  const float hh = 0.5f * h;
+  const float qh = hh * h;
+  const float ql = fmaf(hh, h, -qh);  // exact remainder of h^2/2
+  const float n = rintf(qh * 1.44269504f);
+  float r = fmaf(-n, 0.693359375f, qh);  // exact
+  r = fmaf(-n, -2.12194440e-4f, r);      // ln2 - head
+  float e = __builtin_amdgcn_exp2f(-r * 1.44269504f);
+  e = fmaf(-ql, e, e);
+  e = ldexpf(e, -(int)n);  // exp(-h^2/2)
+  const float u = fabsf(h) * 0.707106781f;
+  const float rc = __builtin_amdgcn_rcpf(u + (float)kErfcxK);
+  const float sv = fmaf((u - (float)kErfcxK) * rc, kErfcxABF32[0], kErfcxABF32[1]);
+  float gp = kErfcxF32[9];
+#pragma unroll
+  for (int j = 8; j >= 0; --j) gp = fmaf(gp, sv, kErfcxF32[j]);
+  const float E = (gp * rc) * e;  // erfc(|h|/sqrt2)
+  const float Phi = h < 0.f ? 0.5f * E : fmaf(-0.5f, E, 1.0f);
+  const float pdf = e * 0.398942280f;
+  return fmaf(g * h, pdf, g * Phi);
 }
 
 // Phi(h) and the density phi(h) for W arguments (LO accuracy, backward).
@@ -239,16 +273,31 @@ __device__ __forceinline__ void fwd4_fast(const float (&x)[4], const float (&y)[
 template <int OP, int EPI, int W>
 __device__ __forceinline__ void gscale_w(const float (&g)[W], const float (&x)[W],
                                          const float (&y)[W], double (&gd)[W]) {
-#pragma unroll
-  for (int k = 0; k < W; ++k) gd[k] = (double)g[k];
   if constexpr (EPI == ZK_EPI_GELU) {
+    // binary32 for |h| <= kGeluGradFastMax; the rare larger, infinite or NaN
+    // arguments take the binary64-scaled path afterwards
+    float h[W];
+    uint32_t slow = 0;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
-      const float h = op32<OP>(x[k], y[k]);
-      double Phi, pdf;
-      phi_pair_f32(h, Phi, pdf);
-      gd[k] = gd[k] * Phi + (gd[k] * (double)h) * pdf;
+      h[k] = op32<OP>(x[k], y[k]);
+      slow |= (uint32_t)!(fabsf(h[k]) <= kGeluGradFastMax) << k;
+      gd[k] = (double)gelu_grad_f32(g[k], h[k]);
     }
+    if (slow) {
+#pragma unroll
+      for (int k = 0; k < W; ++k) {
+        if ((slow >> k) & 1u) {
+          double Phi, pdf;
+          phi_pair_f32(h[k], Phi, pdf);
+          const double gk = (double)g[k];
+          gd[k] = gk * Phi + (gk * (double)h[k]) * pdf;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < W; ++k) gd[k] = (double)g[k];
   }
 }
 

@@ -320,12 +320,19 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
     rp->kernel = K_RED_COL;
     rp->kept = c.n[1];
     rp->red = c.n[0];
-    int64_t colblocks = ceil_div(c.n[1], 256);
-    int64_t P = std::max<int64_t>(1, ceil_div(2048, colblocks));
-    P = std::min<int64_t>(P, std::max<int64_t>(1, ceil_div(c.n[0], 16)));
-    int64_t rc = ceil_div(c.n[0], P);
-    rp->chunk = rc;
-    rp->partials = ceil_div(c.n[0], rc);
+    // A wave owns 256 columns and walks rcw rows: enough waves to fill the
+    // chip (~8192), at most 64 rows each.  Below 64 rows per wave, 16 waves
+    // of a block combine their sums, so a partial always covers >= 64 rows
+    // (binary64 partials stay near 1% of the call's bytes).  The grid
+    // (column groups x partials) stays within the dispatch limit.
+    const int64_t R0 = c.n[0];
+    const int64_t colblocks = ceil_div(c.n[1], 256);
+    int64_t rcw = std::min<int64_t>(64, std::max<int64_t>(4, R0 * colblocks / 8192));
+    const int nw = rcw >= 64 ? 1 : 16;
+    while (colblocks * ceil_div(R0, nw * rcw) > kMaxGridBlocks) rcw *= 2;
+    rp->chunk = rcw;
+    rp->nw = nw;
+    rp->partials = ceil_div(R0, nw * rcw);
     return true;
   }
   if (big_transposed) return false;
@@ -338,10 +345,12 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
   int64_t rows = c.numel / inner;               // (R1, K) rows
   int64_t K = (R == 1) ? 1 : c.n[R - 2];
   int64_t R1 = rows / K;
-  int64_t NC = std::max<int64_t>(1, ceil_div(8192, rows));
-  NC = std::min<int64_t>(NC, std::max<int64_t>(1, inner / 1024));
-  int64_t CL = ceil_div(ceil_div(inner, NC), 4) * 4;
-  NC = ceil_div(inner, CL);
+  // Chunks of 256..2048 elements (whole wave trips), about 8192 of them:
+  // short chunks over many waves stream best; partials stay < 0.1% of bytes.
+  int64_t CL = std::min<int64_t>(2048, std::max<int64_t>(256, c.numel / 8192));
+  CL = ceil_div(CL, 256) * 256;
+  if (CL >= inner) CL = inner;
+  int64_t NC = ceil_div(inner, CL);
   rp->kernel = K_RED_ROW;
   rp->kept = K;
   rp->red = R1 * inner;

@@ -16,6 +16,9 @@ namespace zk {
 
 constexpr int kMaxDims = ZK_MAX_DIMS;
 constexpr int kMaxOps = 5;
+// Largest grid the planner sizes a non-looping launch for: a dispatch counts
+// work-items with 32 bits, and blocks have at most 1024 threads.
+constexpr int64_t kMaxGridBlocks = (int64_t)1 << 22;
 
 // Kernel classes (ids reported by zk_plan_describe).
 enum KernelClass : int32_t {
@@ -102,7 +105,9 @@ struct RedPlan {
   int which = -1;            // 0 = a, 1 = b (reduce_to_shape: 1 = target)
   int64_t kept = 0;          // K: elements of the reduced gradient
   int64_t partials = 0;      // P: partial sums per kept element
-  int64_t chunk = 0;         // rows (COL/TILE) or elements (ROW/GENERIC) per partial
+  int64_t chunk = 0;         // rows per wave (COL), rows (TILE) or elements
+                             // (ROW/GENERIC) per partial
+  int32_t nw = 1;            // COL: waves of a block that share one partial
   int64_t red = 0;           // reduced elements per kept element
   size_t ws_offset = 0;      // byte offset of its partials in the workspace
 };

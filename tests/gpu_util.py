@@ -6,12 +6,16 @@ that one unit in the last place is accepted where the exact value lies within
 a relative 1e-12 of the midpoint between the two neighbouring binary32 values
 (both sides round a binary64 evaluation of GeLU; their libm erfc may differ by
 a few binary64 ulps, which only matters at such near-ties).
-Backward: |gpu - oracle| <= 2e-6 * sum|terms| per element, and exactly +-0
-where that sum is 0.
+Backward: |gpu - oracle| <= 2e-6 * sum|terms| + 2^-149 per element, and
+exactly +-0 where that sum is 0.  The 2^-149 term is the spacing of binary32
+subnormals: a binary32 result below 2^-126 cannot carry the relative accuracy
+2e-6, so there the bound also admits the neighbouring subnormal of the
+correctly rounded value.
 """
 import numpy as np
 
 BWD_TOL = 2e-6
+F32_SUBNORMAL_STEP = 2.0 ** -149
 
 
 def torch_mod():
@@ -75,7 +79,7 @@ def assert_bwd(got, ref, what=""):
     assert got.shape == ref.f32.shape, (what, got.shape, ref.f32.shape)
     g64 = got.astype(np.float64)
     err = np.abs(g64 - ref.f32.astype(np.float64))
-    lim = BWD_TOL * ref.abs
+    lim = BWD_TOL * ref.abs + F32_SUBNORMAL_STEP
     bad = err > lim
     zero = ref.abs == 0
     bad |= zero & (got != 0)
@@ -85,3 +89,8 @@ def assert_bwd(got, ref, what=""):
             f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at {i}: "
             f"got {got.reshape(-1)[i]} want {ref.f32.reshape(-1)[i]} "
             f"abs {ref.abs.reshape(-1)[i]}")
+    # largest error as a fraction of its allowance (the tolerance margin)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r = err / lim
+    r = r[np.isfinite(r)]
+    return float(r.max()) if r.size else 0.0
