@@ -37,17 +37,8 @@ ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
        "rank8_div", "gpt_residual"]
 ROTATE_BYTES = 1 << 30  # per-workload footprint of the rotating buffer sets
 MAX_SETS = 32
-PEAK_FP64 = 78.6  # MI355X vector binary64, TFLOP/s (an FMA counts 2)
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "hbm_traffic.fetch_write_counters.txt")
-
-# Kernels bound by arithmetic rather than HBM: algorithmic binary64 flops per
-# output element of the path they run (an FMA counts 2).  The GeLU forward's
-# fast path: u, q and n (4), the exp reduction and degree-10 polynomial (22),
-# the reciprocal with two Newton steps (10), t and s (4), the degree-14
-# polynomial (28), E, Phi and y (5): 73.
-ALU_WORK = {("mlp_bias_gelu", "fwd_row"): 73}
-
 
 def source_hash():
     import glob
@@ -362,21 +353,10 @@ def main():
     c, kname, kus = best
     hbm = c["bytes"] / (kus * 1e-6) / 1e9
     traffic = read_traffic(args.workload, kname)
-    alu = ALU_WORK.get((args.workload, kname))
-    if alu is not None:
-        flops = alu * c["elements"]
-        achieved = flops / (kus * 1e-6) / 1e12
-        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP64,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP64, 4),
-                "traffic": traffic, "kernel": kname, "call": c["name"],
-                "flops_per_launch": flops, "flops_per_element": alu,
-                "bytes_per_launch": c["bytes"], "us_per_launch": round(kus, 3),
-                "hbm_gbs": round(hbm, 1), "hbm_frac": round(hbm * 1e9 / PEAK_HBM, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s", "frac": round(hbm * 1e9 / PEAK_HBM, 4),
-                "traffic": traffic, "kernel": kname, "call": c["name"],
-                "bytes_per_launch": c["bytes"], "us_per_launch": round(kus, 3)}
+    roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s", "frac": round(hbm * 1e9 / PEAK_HBM, 4),
+            "traffic": traffic, "kernel": kname, "call": c["name"],
+            "bytes_per_launch": c["bytes"], "us_per_launch": round(kus, 3)}
 
     cpu = None
     if not args.no_cpu:

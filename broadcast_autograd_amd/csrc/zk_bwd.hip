@@ -213,7 +213,9 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_generic(
 // lane, 128-bit accesses) and walks rcw consecutive rows, keeping 4 binary64
 // column sums per lane.  NW waves of a block share the same columns and
 // consecutive row ranges; with NW > 1 their sums meet in LDS in wave order,
-// so one partial covers NW * rcw rows.
+// so one partial covers NW * rcw rows.  (Finishing the sum in the last block
+// to arrive, behind an atomic ticket, was measured 6-15x slower on MI355X:
+// the device-scope fences it needs cost more than the second launch.)
 struct ColArgs {
   int64_t R, K, rcw, ss, colblocks;
   int32_t write_big;
@@ -225,8 +227,9 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
     const float *accbig, double *part, ColArgs ca) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
-  // rows in flight per wave: the GeLU epilogue is ALU-bound and wants fewer
-  // registers per wave; plain rules want more loads in flight
+  // rows in flight per wave: two for the plain rules; one with the GeLU
+  // epilogue, whose arithmetic is long enough per row (measured: the
+  // [4096, 1024] GeLU step is ~10% faster than with two)
   constexpr int U = EPI == ZK_EPI_GELU ? 1 : 2;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l = threadIdx.x & 63;

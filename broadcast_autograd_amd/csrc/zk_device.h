@@ -27,8 +27,11 @@ __device__ __forceinline__ double phi_cdf(double h) {
   return 0.5 * erfc(-h * 0.70710678118654752440);
 }
 
-// GeLU through phi_cdf (the path taken near rounding ties).
+// GeLU through phi_cdf (the path taken near rounding ties, for results
+// below 2^-126 and for arguments outside the table).  Limits: +inf -> +inf,
+// -inf -> -0 (the product inf * 0 would be NaN), NaN -> NaN.
 __device__ __forceinline__ float gelu32_libm_inl(float h) {
+  if (__builtin_isinf(h)) return h > 0.f ? h : -0.0f;
   const double hd = (double)h;
   return (float)(hd * phi_cdf(hd));
 }
@@ -37,128 +40,89 @@ __device__ __attribute__((noinline)) float gelu32_libm(float h) {
   return gelu32_libm_inl(h);
 }
 
-// a*b + c with c a wave-uniform binary64 constant held in scalar registers:
-// one VOP3 v_fma_f64.  (Binary64 constants have no literal encoding; left
-// to itself the compiler copies c into vector registers for every v_fmac.)
-__device__ __forceinline__ double fma_s(double a, double b, double c) {
-  double r;
-  asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
-  return r;
+// ------------------------------------------------------------- GeLU fwd
+// GeLU(h) = h Phi(h) = max(h, 0) - |h E(|h|)|/2 with E(a) = erfc(a/sqrt2)
+// (for h < 0, Phi(h) = E/2; for h >= 0, Phi(h) = 1 - E/2).  E comes from
+// the piecewise polynomials of zk_gelu_coeffs.h, copied into LDS by each
+// block: piece i = floor(a^2 + kGeluTabK a) of a = |h| (computed exactly in
+// binary64; a piece stays accurate a little past its ends, so the rounding
+// of the index does not matter), E = sum c_k d^k, d = a - mid_i, Horner in
+// binary64.  Error of the binary64 result: fit ~9e-15 plus ~12 binary64
+// roundings, below 2^-46 relative.
+constexpr int kGeluTabLen = kGeluTabN * kGeluTabW;
+
+// Copies the table into the block's LDS; every thread of the block calls it.
+__device__ __forceinline__ void gelu_tab_load(double *lds) {
+  for (int j = threadIdx.x; j < kGeluTabLen; j += blockDim.x) lds[j] = kGeluTab[j];
+  __syncthreads();
 }
 
-// Horner over W independent arguments: each coefficient is applied to all W
-// before the next, so one scalar-register copy of it feeds W fused
-// multiply-adds and the W dependency chains interleave.
-template <int N, int W>
-__device__ __forceinline__ void horner_w(const double (&c)[N], const double (&x)[W],
-                                         double (&p)[W]) {
-  double top[W];
-#pragma unroll
-  for (int k = 0; k < W; ++k) top[k] = c[N - 1];
-#pragma unroll
-  for (int k = 0; k < W; ++k) p[k] = fma_s(top[k], x[k], c[N - 2]);
-#pragma unroll
-  for (int j = N - 3; j >= 0; --j) {
-#pragma unroll
-    for (int k = 0; k < W; ++k) p[k] = fma_s(p[k], x[k], c[j]);
-  }
-}
-
-// 1/d for d in a modest range (no scaling): hardware estimate and two
-// Newton-Raphson steps.
-__device__ __forceinline__ double rcp64(double d) {
-  double r = __builtin_amdgcn_rcp(d);
-  double e = fma(-d, r, 1.0);
-  r = fma(r, e, r);
-  e = fma(-d, r, 1.0);
-  return fma(r, e, r);
-}
-
-// Phi(h) and exp(-h^2/2) for W finite arguments, branch-free binary64:
-//   u = |h|/sqrt2, q = h^2/2 (exact: h is binary32),
-//   exp(-q) = 2^-n exp(-r), n = rint(q/ln2), r = q - n ln2, polynomial in -r,
-//   erfc(u) = erfcx(u) exp(-q), erfcx from the rational substitution
-//   t = (u-K)/(u+K) (one reciprocal), Phi = erfc/2 or 1 - erfc/2.
-// HI: relative error ~4e-13; LO: ~2e-8 (coefficients: zk_gelu_coeffs.h).
-template <int W, bool HI>
-__device__ __forceinline__ void phi_fast_w(const double (&hd)[W], double (&Phi)[W],
-                                           double (&eq)[W]) {
-  double u[W], n[W], mr[W], pe[W], s[W], rc[W], g[W];
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-    u[k] = fmin(fabs(hd[k]) * 0.70710678118654752440, kErfcxUmax);
-    const double q = fmin(0.5 * (hd[k] * hd[k]), 1000.0);
-    n[k] = rint(q * 1.4426950408889634074);
-    mr[k] = fma(n[k], 0.69314718055994530942, -q);  // -(q - n ln2)
-  }
-  if constexpr (HI) horner_w(kExpHI, mr, pe);
-  else horner_w(kExpLO, mr, pe);
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-    eq[k] = ldexp(pe[k], -(int)n[k]);
-    rc[k] = rcp64(u[k] + kErfcxK);  // u + K in [3.75, 14.35]
-    const double t = (u[k] - kErfcxK) * rc[k];
-    s[k] = HI ? fma(t, kErfcxABHI[0], kErfcxABHI[1]) : fma(t, kErfcxABLO[0], kErfcxABLO[1]);
-  }
-  if constexpr (HI) horner_w(kErfcxHI, s, g);
-  else horner_w(kErfcxLO, s, g);
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-    const double E = (g[k] * rc[k]) * eq[k];
-    Phi[k] = hd[k] < 0.0 ? 0.5 * E : fma(-0.5, E, 1.0);
-  }
-}
-
-// Relative distance from a binary32 rounding boundary below which the fast
-// forward value is not trusted: 2^-37 ~ 7.3e-12, about twenty times the HI
-// error bound.  (Distances are measured in binary64 ulps of y, which are at
-// most 2^-52 |y| and at least 2^-53 |y|.)
-constexpr double kGeluTieMargin = 0x1p-37;
-
-// GeLU(h) = h * Phi(h) rounded once to binary32.  The fast binary64 value is
-// rounded when it lies farther than kGeluTieMargin (relative) from the
-// midpoint between the two binary32 neighbours, which makes the result the
-// correctly rounded exact value; otherwise the libm erfc path decides.
-// Limits at +-inf are +inf and -0; NaN propagates.
-// Fast part for W arguments: the rounded fast values, and bit k of *redo
-// set when value k is too close to a rounding boundary to be trusted (the
-// caller then recomputes it with gelu32_libm).
+// GeLU(h) rounded once to binary32 for W arguments.  The binary64 value y
+// is rounded when it lies farther than 2^-40 (relative, 2^6 times the error
+// bound) from the midpoint between its two binary32 neighbours, which makes
+// the result the correctly rounded exact value; otherwise bit k of *redo is
+// set and the caller recomputes element k with gelu32_libm.  Also sent
+// there: results below 2^-126 (binary32 subnormals or zero, including
+// h = +-0) and negative h beyond the table.  Positive h beyond the table
+// gives y = h exactly (GeLU(h) = h (1 - 1e-10) rounds to h); +inf gives
+// +inf and NaN gives NaN; -inf is sent to the libm path.
 template <int W>
-__device__ __forceinline__ void gelu32_fast_w(const float (&h)[W], float (&f)[W],
-                                              uint32_t &redo) {
-  double hd[W], Phi[W], eq[W];
+__device__ __forceinline__ void gelu32_fast_w(const double *tab, const float (&h)[W],
+                                              float (&f)[W], uint32_t &redo) {
+  // The W evaluations are interleaved step by step (table reads for all,
+  // then each Horner step for all) so that their LDS reads and dependent
+  // binary64 FMAs overlap instead of running one element after another.
+  double hd[W], ad[W], d[W], e[W];
+  bool beyond[W];
+  const double *t[W];
 #pragma unroll
-  for (int k = 0; k < W; ++k) hd[k] = __builtin_isfinite(h[k]) ? (double)h[k] : 0.0;
-  phi_fast_w<W, true>(hd, Phi, eq);
+  for (int k = 0; k < W; ++k) {
+    hd[k] = (double)h[k];
+    ad[k] = fabs(hd[k]);
+    const double a2 = hd[k] * hd[k];  // exact
+    beyond[k] = a2 > kGeluTabAmax2;
+    int i = (int)fma(ad[k], kGeluTabK, a2);  // NaN -> 0, +inf -> INT_MAX
+    i = i < kGeluTabN - 1 ? i : kGeluTabN - 1;
+    t[k] = tab + i * kGeluTabW;
+  }
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    d[k] = ad[k] - t[k][0];
+    e[k] = t[k][kGeluTabW - 1];
+  }
+#pragma unroll
+  for (int j = kGeluTabW - 2; j >= 1; --j) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) e[k] = fma(e[k], d[k], t[k][j]);
+  }
   redo = 0;
 #pragma unroll
   for (int k = 0; k < W; ++k) {
-    const double y = hd[k] * Phi[k];
-    // Rounding y to binary32 discards the low 29 of its 52 mantissa bits;
-    // a midpoint between binary32 neighbours has exactly 2^28 there.  y is
-    // trusted when those bits are more than 2^15 units (2^-37 relative,
-    // kGeluTieMargin) from 2^28.  Results below 2^-126 (binary32 subnormals
-    // or zero) always take the libm path.
+    double th = hd[k] * e[k];
+    th = beyond[k] ? 0.0 : th;
+    const double y = fma(-0.5, fabs(th), fmax(hd[k], 0.0));  // NaN: fmax gives 0, y NaN
+    // Rounding y to binary32 discards the low 29 of its 52 mantissa bits; a
+    // midpoint between binary32 neighbours has exactly 2^28 there.  y is
+    // trusted when those bits are more than 2^12 units (2^-40 relative) from
+    // 2^28.
     const uint32_t lo = (uint32_t)__double_as_longlong(y);
-    const uint32_t dist = (lo & 0x1fffffffu) - (0x10000000u - 0x8000u);
-    uint32_t near = (uint32_t)(dist < 0x10000u || fabs(y) < 0x1p-126);
+    const uint32_t dist = (lo & 0x1fffffffu) - (0x10000000u - 0x1000u);
+    uint32_t near = (uint32_t)(dist < 0x2000u || fabs(y) < 0x1p-126);
     float fy = (float)y;
-    // Keep the fast value unconditional: left alone, the compiler turns the
-    // select below into a branch per element around the whole evaluation,
-    // which serialises the W independent chains.
+    // Keep the fast value unconditional: left alone, the compiler turns a
+    // select on it into a branch per element around the whole evaluation.
     asm volatile("" : "+v"(fy), "+v"(near));
-    const bool fin = __builtin_isfinite(h[k]);
-    redo |= (fin ? near : 0u) << k;
-    // limits: +inf -> +inf, -inf -> -0, NaN -> NaN
-    f[k] = fin ? fy : (__builtin_isnan(h[k]) || h[k] > 0.f ? h[k] : -0.0f);
+    redo |= near << k;
+    f[k] = fy;
   }
 }
 
-__device__ __forceinline__ float gelu32(float h) {
+// One element, with the rare libm path inline.
+__device__ __forceinline__ float gelu32(const double *tab, float h) {
   const float hv[1] = {h};
   float f[1];
   uint32_t redo;
-  gelu32_fast_w<1>(hv, f, redo);
+  gelu32_fast_w<1>(tab, hv, f, redo);
   return redo ? gelu32_libm(h) : f[0];
 }
 
@@ -224,28 +188,11 @@ __device__ __forceinline__ float gelu_grad_f32(float g, float h) {
   return fmaf(g * h, pdf, g * Phi);
 }
 
-// Phi(h) and the density phi(h) for W arguments (LO accuracy, backward).
-template <int W>
-__device__ __forceinline__ void phi_pair_lo_w(const double (&h)[W], double (&Phi)[W],
-                                              double (&pdf)[W]) {
-  double hd[W], eq[W];
-#pragma unroll
-  for (int k = 0; k < W; ++k) hd[k] = __builtin_isfinite(h[k]) ? h[k] : 0.0;
-  phi_fast_w<W, false>(hd, Phi, eq);
-#pragma unroll
-  for (int k = 0; k < W; ++k) {
-    pdf[k] = eq[k] * 0.39894228040143267794;
-    if (!__builtin_isfinite(h[k])) {  // limits: Phi(+-inf) = 1 / 0, phi = 0
-      Phi[k] = h[k] > 0.0 ? 1.0 : (h[k] < 0.0 ? 0.0 : h[k]);
-      pdf[k] = h[k] == h[k] ? 0.0 : h[k];
-    }
-  }
-}
-
+// r = epi(x (op) y); tab: the GeLU table in LDS (unused without GeLU).
 template <int OP, int EPI>
-__device__ __forceinline__ float fwd32(float x, float y) {
+__device__ __forceinline__ float fwd32(float x, float y, const double *tab) {
   float h = op32<OP>(x, y);
-  if constexpr (EPI == ZK_EPI_GELU) return gelu32(h);
+  if constexpr (EPI == ZK_EPI_GELU) return gelu32(tab, h);
   else return h;
 }
 
@@ -254,12 +201,13 @@ __device__ __forceinline__ float fwd32(float x, float y) {
 // its stores and so keeps that code out of the hot loop.
 template <int OP, int EPI>
 __device__ __forceinline__ void fwd4_fast(const float (&x)[4], const float (&y)[4],
-                                          float (&r)[4], uint32_t &redo) {
+                                          float (&r)[4], uint32_t &redo,
+                                          const double *tab) {
   float h[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) h[k] = op32<OP>(x[k], y[k]);
   if constexpr (EPI == ZK_EPI_GELU) {
-    gelu32_fast_w<4>(h, r, redo);
+    gelu32_fast_w<4>(tab, h, r, redo);
   } else {
     redo = 0;
 #pragma unroll

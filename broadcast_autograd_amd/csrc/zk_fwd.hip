@@ -22,8 +22,10 @@ constexpr int kBlock = 256;
 // 128-bit vector per lane and one tile per block, over a grid as large as
 // the data, streams fastest (measured: a dense a+b reaches ~6.4 TB/s this
 // way against ~5.7 TB/s with four vectors per lane); the operands that are
-// read or written once also carry the non-temporal hint.
-constexpr int row_unroll(int) { return 1; }
+// read or written once also carry the non-temporal hint.  With the GeLU
+// epilogue each block first copies the 5.4 KB erfc table into LDS, so a
+// block takes two vectors per lane to halve that traffic.
+constexpr int row_unroll(int epi) { return epi == ZK_EPI_GELU ? 2 : 1; }
 
 // Launches give one block per tile; kernels loop over tiles with a grid
 // stride, so a grid capped here still covers any size.  (A dispatch counts
@@ -69,6 +71,8 @@ template <int OP, int EPI, int VEC, int U>
 __global__ __launch_bounds__(kBlock) void k_fwd_flat(const float *a,
                                                      const float *b,
                                                      float *out, int64_t n) {
+  __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
+  if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   constexpr int64_t tile = (int64_t)kBlock * U * VEC;
   const int64_t ntiles = (n + tile - 1) / tile;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
@@ -92,11 +96,11 @@ __global__ __launch_bounds__(kBlock) void k_fwd_flat(const float *a,
           const float y[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
           float r[4];
           uint32_t redo;
-          fwd4_fast<OP, EPI>(x, y, r, redo);
+          fwd4_fast<OP, EPI>(x, y, r, redo, s_gelu);
           redo_bits |= redo << (4 * u);
           st4_nt(out + i, make_float4(r[0], r[1], r[2], r[3]));
         } else if (i < n) {
-          for (int64_t j = i; j < n; ++j) out[j] = fwd32<OP, EPI>(a[j], b[j]);
+          for (int64_t j = i; j < n; ++j) out[j] = fwd32<OP, EPI>(a[j], b[j], s_gelu);
         }
       }
       if constexpr (EPI == ZK_EPI_GELU) {
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void k_fwd_flat(const float *a,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t i = t * tile + (int64_t)u * kBlock + threadIdx.x;
-        if (i < n) out[i] = fwd32<OP, EPI>(a[i], b[i]);
+        if (i < n) out[i] = fwd32<OP, EPI>(a[i], b[i], s_gelu);
       }
     }
   }
@@ -152,6 +156,8 @@ template <int OP, int EPI, int VEC, int SMODE, bool SWAP, typename I>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_fwd_row(const float *big,
                                                     const float *small,
                                                     float *out, RowArgs ra) {
+  __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
+  if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   constexpr int U = row_unroll(EPI);
   constexpr I tile = (I)kBlock * U * VEC;
   const I n = (I)ra.numel;
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
             y[k] = SWAP ? el(vb[u], k) : el(vs[u], k);
           }
           uint32_t redo;
-          fwd4_fast<OP, EPI>(x, y, r, redo);
+          fwd4_fast<OP, EPI>(x, y, r, redo, s_gelu);
           redo_bits |= redo << (4 * u);
           res[u] = make_float4(r[0], r[1], r[2], r[3]);
         }
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
       const I i = (I)i64;
       const float vbig = big[i];
       const float vsm = small[row_offset<I>(ra, i)];
-      out[i] = SWAP ? fwd32<OP, EPI>(vsm, vbig) : fwd32<OP, EPI>(vbig, vsm);
+      out[i] = SWAP ? fwd32<OP, EPI>(vsm, vbig, s_gelu) : fwd32<OP, EPI>(vbig, vsm, s_gelu);
     }
   }
 }
@@ -252,6 +258,8 @@ __global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
                                                      const float *oth,
                                                      float *out, TileArgs ta) {
   __shared__ float tile[64][65];
+  __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
+  if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   const int t = threadIdx.x;
   for (int64_t bt = blockIdx.x; bt < ta.ntiles; bt += gridDim.x) {
     const int64_t tr_i = bt / ta.tiles_c, tr_j = bt % ta.tiles_c;
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
           float vt = tile[j + k][i];
           float x = SWAP ? el(vo, k) : vt;
           float y = SWAP ? vt : el(vo, k);
-          el(r, k) = fwd32<OP, EPI>(x, y);
+          el(r, k) = fwd32<OP, EPI>(x, y, s_gelu);
         }
         st4_nt(out + gi * ta.C + gj, r);
       }
@@ -332,6 +340,8 @@ __global__ __launch_bounds__(kBlock) void k_fwd_generic(const float *a,
                                                         float *out, Space sp,
                                                         int flat_a, int flat_b,
                                                         int vec_out) {
+  __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
+  if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   const I n = (I)sp.numel;
   // 64-bit loop counter: i0 + stride may pass 2^31 even when n does not
   for (int64_t j0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4; j0 < (int64_t)n;
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(kBlock) void k_fwd_generic(const float *a,
         offsets_ab<I>(sp, i, oa, ob);
         float x = a[flat_a ? i : oa];
         float y = b[flat_b ? i : ob];
-        r[k] = fwd32<OP, EPI>(x, y);
+        r[k] = fwd32<OP, EPI>(x, y, s_gelu);
       }
     }
     if (vec_out && i0 + 4 <= n) {

@@ -89,8 +89,10 @@ def assert_bwd(got, ref, what=""):
             f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at {i}: "
             f"got {got.reshape(-1)[i]} want {ref.f32.reshape(-1)[i]} "
             f"abs {ref.abs.reshape(-1)[i]}")
-    # largest error as a fraction of its allowance (the tolerance margin)
+    # largest error as a fraction of 2e-6*sum|terms| over the results in the
+    # binary32 normal range (the tolerance margin)
+    normal = np.abs(ref.f32) >= np.float32(2.0 ** -126)
     with np.errstate(invalid="ignore", divide="ignore"):
-        r = err / lim
+        r = err[normal] / (BWD_TOL * ref.abs[normal])
     r = r[np.isfinite(r)]
     return float(r.max()) if r.size else 0.0
