@@ -383,6 +383,7 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
 struct TileRedArgs {
   int64_t R, K, ld, ss, rc, tiles_c, items;
   int32_t write_big;
+  int32_t tv;  // the transposed operand's columns start 16-byte aligned
 };
 
 template <int OP, int EPI, int SIDE, int ACC>
@@ -396,6 +397,8 @@ __global__ __launch_bounds__(kBlk) void k_red_tile(
   const int t = threadIdx.x;
   // (row chunk p, 64-column tile tj) items, one per block up to the grid cap
   for (int64_t bt = blockIdx.x; bt < ta.items; bt += gridDim.x) {
+    // (Unlike the forward tile kernel, a diagonal order of the items
+    // measured slower here: the row-major gradient streams dominate.)
     const int64_t p = bt / ta.tiles_c;
     const int64_t tj = bt - p * ta.tiles_c;
     const int64_t j0 = tj * 64;
@@ -411,15 +414,65 @@ __global__ __launch_bounds__(kBlk) void k_red_tile(
     const int64_t r1 = r0 + ta.rc < ta.R ? r0 + ta.rc : ta.R;
     double s[4] = {0.0, 0.0, 0.0, 0.0};
     for (int64_t ti = r0; ti < r1; ti += 64) {
+      // Issue every load of this tile first (the transposed operand's column
+      // runs and the upstream gradient's row runs), so that both latencies
+      // overlap; then stage the transposed operand through LDS.
+      float4 av[4];
+      float4 vg[4], va[4];
+      // 128-bit loads down the transposed operand's columns when they start
+      // 16-byte aligned: lane (t & 15) takes rows 4(t&15)..+3 of columns
+      // t/16 + 16pp; else 32-bit loads, lane (t & 63) one row of columns
+      // t/64 + 4k.
+      const int i4 = ta.tv ? (t & 15) * 4 : (t & 63);
+      const int jq = ta.tv ? t >> 4 : t >> 6;
       if constexpr (NEED_BIG) {
-        const int i = t & 63, jq = t >> 6;
-        const int64_t gi = ti + i;
+        const int64_t gi = ti + i4;
 #pragma unroll
-        for (int pp = 0; pp < 16; ++pp) {
-          const int j = jq + 4 * pp;
-          float v = 0.f;
-          if (gi < r1 && j0 + j < ta.K) v = big[gi + (j0 + j) * ta.ld];
-          tile[j][i] = v;
+        for (int pp = 0; pp < 4; ++pp) {
+          av[pp] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (ta.tv) {
+            const int64_t gj = j0 + jq + 16 * pp;
+            if (gj < ta.K) {
+              const float *src = big + gi + gj * ta.ld;
+              if (gi + 3 < r1) {
+                av[pp] = ld4_nt(src);
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                  if (gi + k < r1) el(av[pp], k) = src[k];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int64_t gj = j0 + jq + 4 * (4 * pp + k);
+              if (gi < r1 && gj < ta.K) el(av[pp], k) = big[gi + gj * ta.ld];
+            }
+          }
+        }
+      }
+      if (colok) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int64_t gi = ti + q + 16 * pp;
+          if (gi < r1) {
+            const int64_t off = gi * ta.K + gj;
+            vg[pp] = ld4_nt(g + off);
+            if constexpr (ACC == 2) va[pp] = ld4_nt(accbig + off);
+          }
+        }
+      }
+      if constexpr (NEED_BIG) {
+        if (ta.tv) {
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tile[jq + 16 * pp][i4 + k] = el(av[pp], k);
+        } else {
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tile[jq + 4 * (4 * pp + k)][i4] = el(av[pp], k);
         }
         __syncthreads();
       }
@@ -430,13 +483,10 @@ __global__ __launch_bounds__(kBlk) void k_red_tile(
           const int64_t gi = ti + i;
           if (gi < r1) {
             const int64_t off = gi * ta.K + gj;
-            const float4 vg = ld4_nt(g + off);
-            float4 va;
-            if constexpr (ACC == 2) va = ld4_nt(accbig + off);
             float4 ob;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              const float gv = el(vg, k);
+              const float gv = el(vg[pp], k);
               const float bv = NEED_BIG ? tile[4 * m + k][i] : 0.f;
               const float x = SIDE == 0 ? sv[k] : bv;
               const float y = SIDE == 0 ? bv : sv[k];
@@ -445,7 +495,7 @@ __global__ __launch_bounds__(kBlk) void k_red_tile(
               terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
               s[k] += ts;
               if constexpr (ACC == 1) tb = gv + tb;
-              if constexpr (ACC == 2) tb = el(va, k) + tb;
+              if constexpr (ACC == 2) tb = el(va[pp], k) + tb;
               el(ob, k) = tb;
             }
             if (ta.write_big) st4_nt(gbig + off, ob);
@@ -741,6 +791,7 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ta.tiles_c = (ta.K + 63) / 64;
             ta.items = ta.tiles_c * rp.partials;
             ta.write_big = p.fused_big;
+            ta.tv = ta.ld % 4 == 0 && ((uintptr_t)big & 15u) == 0;
             unsigned grid = gridn(ta.items, 1);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               ZK_LAUNCH(prof, (k_red_tile<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),

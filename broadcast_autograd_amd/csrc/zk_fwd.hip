@@ -251,6 +251,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 struct TileArgs {
   int64_t R, C, ld, os0, os1;
   int64_t tiles_c, ntiles;
+  int32_t tv;  // T's columns start 16-byte aligned: 128-bit loads
 };
 
 template <int OP, int EPI, int OMODE, bool SWAP>
@@ -262,9 +263,39 @@ __global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
   if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   const int t = threadIdx.x;
   for (int64_t bt = blockIdx.x; bt < ta.ntiles; bt += gridDim.x) {
-    const int64_t tr_i = bt / ta.tiles_c, tr_j = bt % ta.tiles_c;
+    // Diagonal order: blocks running together take different row tiles, so
+    // their column runs of T start at different offsets within the column
+    // stride (with one row tile for all, every concurrent read would share
+    // its low address bits, and with them the same few HBM channels).
+    const int64_t tiles_r = ta.ntiles / ta.tiles_c;
+    const int64_t tr_j = bt % ta.tiles_c;
+    const int64_t tr_i = (bt / ta.tiles_c + tr_j) % tiles_r;
     const int64_t i0 = tr_i * 64, j0 = tr_j * 64;
-    {
+    if (ta.tv) {
+      // 128-bit loads down T's columns: lane (t & 15) takes rows 4(t&15)..+3
+      const int i4 = (t & 15) * 4, jq = t >> 4;
+      const int64_t gi = i0 + i4;
+      float4 v[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int64_t gj = j0 + jq + 16 * p;
+        v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gj < ta.C) {
+          const float *src = tr + gi + gj * ta.ld;
+          if (gi + 3 < ta.R) {
+            v[p] = ld4_nt(src);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (gi + k < ta.R) el(v[p], k) = src[k];
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tile[jq + 16 * p][i4 + k] = el(v[p], k);
+    } else {
       const int i = t & 63, jq = t >> 6;
       const int64_t gi = i0 + i;
 #pragma unroll
@@ -443,6 +474,7 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         ta.os1 = c.s[ot_op][1];
         ta.tiles_c = (ta.C + 63) / 64;
         ta.ntiles = ((ta.R + 63) / 64) * ta.tiles_c;
+        ta.tv = ta.ld % 4 == 0 && ((uintptr_t)tr & 15u) == 0;
         unsigned grid = (unsigned)(ta.ntiles < kMaxBlocks ? ta.ntiles : kMaxBlocks);
         int om = SM_GATHER;
         if (ta.os1 == 0) om = SM_BCAST;

@@ -306,13 +306,9 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
       rp->kernel = K_RED_TILE;
       rp->kept = c.n[1];
       rp->red = c.n[0];
-      int64_t tiles_c = ceil_div(c.n[1], 64);
-      int64_t rows64 = ceil_div(c.n[0], 64);
-      int64_t P = std::max<int64_t>(1, ceil_div(2048, tiles_c));
-      P = std::min<int64_t>(P, rows64);
-      int64_t rc = ceil_div(rows64, P) * 64;
-      rp->chunk = rc;
-      rp->partials = ceil_div(c.n[0], rc);
+      // one 64 x 64 tile per block and partial (partials ~1% of the bytes)
+      rp->chunk = 64;
+      rp->partials = ceil_div(c.n[0], 64);
       return true;
     }
     if (big_op >= 0 && !is_flat(c, big_op)) return false;

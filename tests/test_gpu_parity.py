@@ -172,13 +172,16 @@ def test_attention_shaped_small(orc):
     assert_bwd(host(mg), orc.reduce_to_shape(h["g"], (1, 1, 128, 128)), "mask grad")
 
 
-@pytest.mark.parametrize("n,m", [(520, 392), (64, 64), (130, 260), (4096, 64)])
+@pytest.mark.parametrize("n,m,ld,off", [(520, 392, 520, 0), (64, 64, 64, 0), (130, 260, 130, 0),
+                                        (4096, 64, 4096, 0), (130, 260, 132, 0), (61, 128, 64, 0),
+                                        (128, 96, 128, 1)])
 @pytest.mark.parametrize("op", ["mul", "div", "sub"])
-def test_transposed_operand(orc, n, m, op):
-    """a is a transposed view: sizes [n, m], strides [1, n]."""
-    rng = np.random.default_rng(n * m)
-    s = rng.uniform(0.5, 2, n * m).astype(np.float32)
-    va, ta, _ = strided_pair(s, (n, m), (1, n))
+def test_transposed_operand(orc, n, m, ld, off, op):
+    """a is a transposed view: sizes [n, m], strides [1, ld], storage offset
+    off (column starts 16-byte aligned or not; rows a multiple of 4 or not)."""
+    rng = np.random.default_rng(n * m + ld + off)
+    s = rng.uniform(0.5, 2, off + ld * m).astype(np.float32)
+    va, ta, _ = strided_pair(s, (n, m), (1, ld), off)
     b = rng.uniform(0.5, 2, (m,)).astype(np.float32)
     check_pair(orc, op, va, ta, b, dev(b), seed=7)
     check_pair(orc, op, b, dev(b), va, ta, seed=8)
