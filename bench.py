@@ -34,7 +34,10 @@ PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 METRIC = "effective HBM GB/s (fwd, fwd+bwd) and % of MI355X HBM peak per config"
 MAIN = "mlp_bias_gelu"
 ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
-       "rank8_div", "gpt_residual"]
+       "rank8_div", "gpt_residual",
+       # the three two-operator expressions again, each as one fused call per
+       # direction (fewer bytes: the intermediate is never stored)
+       "xy_plus_x_fused", "attn_scale_mask_fused", "gpt_residual_fused"]
 ROTATE_BYTES = 1 << 30  # per-workload footprint of the rotating buffer sets
 MAX_SETS = 32
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -318,6 +321,8 @@ def main():
            "attn_scale_mask": Wk.attn_scale_mask,
            "strided_transposed": Wk.strided_transposed, "rank8_div": Wk.rank8,
            "gpt_residual": Wk.gpt_residual}
+    for w in ("xy_plus_x", "attn_scale_mask", "gpt_residual"):
+        gen[w + "_fused"] = gen[w]
     log(f"[bench] device {torch.cuda.get_device_name(0)}; spin check "
         f"{spin_seconds(torch) * 1e3:.1f} ms")
     ceiling = copy_ceiling(torch)
@@ -336,7 +341,8 @@ def main():
         [w for w in ALL if w != args.workload] if args.others == "all"
         else [w for w in args.others.split(",") if w and w != args.workload])
     for w in others:
-        big = w in ("attn_scale_mask", "gpt_residual", "strided_transposed")
+        big = w.replace("_fused", "") in ("attn_scale_mask", "gpt_residual",
+                                          "strided_transposed")
         K = args.other_steps or (40 if big else 400)
         log(f"[bench] workload {w}: {K} steps")
         r = measure(w, gen[w](), K, K // 10, torch)

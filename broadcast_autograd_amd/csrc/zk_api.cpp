@@ -70,6 +70,57 @@ size_t bwd_workspace(zk_op op, zk_epi epi, const zk_desc &da,
   return m;
 }
 
+bool valid_op2(zk_op op) { return op == ZK_ADD || op == ZK_SUB; }
+
+// Dense row-major descriptor of a shape.
+zk_desc dense_desc(int r, const int64_t *n) {
+  zk_desc d{};
+  d.rank = r;
+  int64_t s = 1;
+  for (int k = r - 1; k >= 0; --k) {
+    d.sizes[k] = n[k];
+    d.strides[k] = s;
+    s *= n[k];
+  }
+  return d;
+}
+
+bool same_view(const zk_desc &x, const zk_desc &y) {
+  if (x.rank != y.rank) return false;
+  for (int k = 0; k < x.rank; ++k)
+    if (x.sizes[k] != y.sizes[k] || (x.sizes[k] != 1 && x.strides[k] != y.strides[k]))
+      return false;
+  return true;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t reduce_workspace(const zk_desc &din, int rout, const int64_t *nout);
+
+// Layout of the fused backward's workspace (shapes only):
+//   [op1 backward][c reduction][t gradient buffer][t reduction]
+struct Bwd2Layout {
+  size_t op1 = 0, cred = 0, tbuf = 0, tred = 0;
+  size_t total() const { return op1 + cred + tbuf + tred; }
+};
+Bwd2Layout bwd2_layout(zk_op op1, const zk_desc &da, const zk_desc &db,
+                       const zk_desc &dc, int r, const int64_t *n, bool wa, bool wb,
+                       bool wc) {
+  Bwd2Layout L;
+  int rab;
+  int64_t nab[kMaxDims];
+  broadcast_shape(da.rank, da.sizes, db.rank, db.sizes, &rab, nab);
+  const zk_desc ds = dense_desc(r, n);
+  const int64_t ns = numel(ds), nab_el = numel(dense_desc(rab, nab));
+  L.op1 = round256(bwd_workspace(op1, ZK_EPI_NONE, da, db, wa, wb));
+  if (wc && numel(dc) < ns) L.cred = round256(reduce_workspace(ds, dc.rank, dc.sizes));
+  if (nab_el < ns && (wa || wb)) {
+    L.tbuf = round256((size_t)nab_el * 4u);
+    L.tred = round256(reduce_workspace(ds, rab, nab));
+  }
+  return L;
+}
+
 size_t reduce_workspace(const zk_desc &din, int rout, const int64_t *nout) {
   size_t m = 0;
   for (uintptr_t q : {(uintptr_t)0, (uintptr_t)4}) {
@@ -287,6 +338,145 @@ zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
   if (need) ews = Ext{(uintptr_t)workspace, (uintptr_t)workspace + need};
   if (ov(eo, ei) || ov(eo, ews) || ov(ews, ei)) return ZK_ERR_ALIAS;
   return hip_status(launch_reduce(p, in, out, workspace, (hipStream_t)stream));
+}
+
+zk_status zk_binary2_fwd(zk_op op1, zk_op op2, const float *a, const zk_desc *da,
+                         const float *b, const zk_desc *db, const float *c,
+                         const zk_desc *dc, float *out, void *stream) {
+  if (!valid_op(op1) || !valid_op2(op2)) return ZK_ERR_UNSUPPORTED;
+  zk_status s;
+  if ((s = check_desc(da)) || (s = check_desc(db)) || (s = check_desc(dc))) return s;
+  Fwd2Plan p;
+  if ((s = plan_fwd2(*da, *db, *dc, (uintptr_t)a, (uintptr_t)b, (uintptr_t)c,
+                     (uintptr_t)out, &p)))
+    return s;
+  if (p.empty) return ZK_OK;
+  if (!a || !b || !c || !out) return ZK_ERR_NULL;
+  const int64_t n = p.c.numel;
+  Ext eo = ext_dense(out, n);
+  const float *in[3] = {a, b, c};
+  const zk_desc *din[3] = {da, db, dc};
+  for (int x = 0; x < 3; ++x)
+    if (ov(eo, ext_of(in[x], *din[x])) && !(out == in[x] && dense_full(*din[x], n)))
+      return ZK_ERR_ALIAS;
+  return hip_status(launch_fwd2(p, op1, op2, a, b, c, out, (hipStream_t)stream));
+}
+
+zk_status zk_binary2_bwd(zk_op op1, zk_op op2, const float *grad, const float *a,
+                         const zk_desc *da, const float *b, const zk_desc *db,
+                         const float *c, const zk_desc *dc, float *grad_a,
+                         const float *acc_a, float *grad_b, const float *acc_b,
+                         float *grad_c, const float *acc_c, void *workspace,
+                         size_t *workspace_bytes, void *stream) {
+  if (!valid_op(op1) || !valid_op2(op2)) return ZK_ERR_UNSUPPORTED;
+  if (!workspace_bytes) return ZK_ERR_NULL;
+  zk_status s;
+  if ((s = check_desc(da)) || (s = check_desc(db)) || (s = check_desc(dc))) return s;
+  int r, rab;
+  int64_t n[kMaxDims], nab[kMaxDims];
+  if ((s = broadcast_shape3(*da, *db, *dc, &r, n))) return s;
+  if ((s = broadcast_shape(da->rank, da->sizes, db->rank, db->sizes, &rab, nab))) return s;
+  const zk_desc ds = dense_desc(r, n), dab = dense_desc(rab, nab);
+  const int64_t ns = numel(ds), nt = numel(dab);
+  const int64_t na = numel(*da), nb = numel(*db), nc = numel(*dc);
+  // A tensor used twice: c is a (or b) and one buffer takes both paths.
+  int tie = -1;
+  if (grad_c && grad_c == grad_a) tie = 0;
+  else if (grad_c && grad_c == grad_b) tie = 1;
+  if (tie >= 0) {
+    const zk_desc &dt = tie == 0 ? *da : *db;
+    const float *pt = tie == 0 ? a : b;
+    const float *acct = tie == 0 ? acc_a : acc_b;
+    if (op2 != ZK_ADD || c != pt || !same_view(*dc, dt) || numel(dt) != ns || acct || acc_c)
+      return ZK_ERR_UNSUPPORTED;
+  }
+  const bool wa = grad_a != nullptr, wb = grad_b != nullptr;
+  const bool wc = grad_c != nullptr && tie < 0;
+  const bool split = nt < ns;  // t = a op1 b is repeated into out
+  const Bwd2Layout L = bwd2_layout(op1, *da, *db, *dc, r, n, wa, wb, wc);
+  const size_t need = L.total();
+  if (!workspace) {
+    *workspace_bytes = need;
+    return ZK_OK;
+  }
+  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(workspace);
+  float *tbuf = split && (wa || wb) ? reinterpret_cast<float *>(ws + L.op1 + L.cred) : nullptr;
+  const float *up = tbuf ? tbuf : grad;  // upstream gradient of t
+  const float *acc_a1 = tie == 0 ? up : acc_a;
+  const float *acc_b1 = tie == 1 ? up : acc_b;
+  BwdPlan p1, pc, pt;
+  if ((wa || wb) &&
+      (s = plan_bwd(op1, ZK_EPI_NONE, *da, *db, wa, wb, (uintptr_t)up, (uintptr_t)a,
+                    (uintptr_t)b, (uintptr_t)grad_a, (uintptr_t)grad_b,
+                    (uintptr_t)acc_a1, (uintptr_t)acc_b1, &p1)))
+    return s;
+  if (wc && nc < ns &&
+      (s = plan_reduce(ds, dc->rank, dc->sizes, (uintptr_t)grad, (uintptr_t)grad_c, &pc)))
+    return s;
+  if (tbuf && (s = plan_reduce(ds, rab, nab, (uintptr_t)grad, (uintptr_t)tbuf, &pt)))
+    return s;
+  if (ns > 0 && (!grad || !a || !b || !c)) return ZK_ERR_NULL;
+  // Aliasing: outputs against each other, the inputs, the accs and the
+  // workspace (an output may be its own acc; a tied pair is one output).
+  Ext eg = ext_dense(grad, ns), ea = ext_of(a, *da), eb = ext_of(b, *db), ec = ext_of(c, *dc);
+  Ext ews;
+  if (need) ews = Ext{(uintptr_t)workspace, (uintptr_t)workspace + need};
+  float *outs[3] = {grad_a, grad_b, tie < 0 ? grad_c : nullptr};
+  const float *accs[3] = {acc_a, acc_b, acc_c};
+  const int64_t cnt[3] = {na, nb, nc};
+  Ext eo[3], ex[3];
+  for (int w = 0; w < 3; ++w) {
+    eo[w] = ext_dense(outs[w], cnt[w]);
+    ex[w] = ext_dense(accs[w], cnt[w]);
+  }
+  for (int w = 0; w < 3; ++w) {
+    if (!outs[w]) continue;
+    if (ov(eo[w], eg) || ov(eo[w], ea) || ov(eo[w], eb) || ov(eo[w], ec) || ov(eo[w], ews))
+      return ZK_ERR_ALIAS;
+    for (int v = 0; v < 3; ++v) {
+      if (v != w && outs[v] && ov(eo[w], eo[v])) return ZK_ERR_ALIAS;
+      if (ov(eo[w], ex[v]) && !(v == w && accs[v] == outs[w])) return ZK_ERR_ALIAS;
+    }
+  }
+  if (need)
+    for (int w = 0; w < 3; ++w)
+      if (ov(ews, eg) || ov(ews, ea) || ov(ews, eb) || ov(ews, ec) || ov(ews, ex[w]))
+        return ZK_ERR_ALIAS;
+  const hipStream_t st = (hipStream_t)stream;
+  const float sign = op2 == ZK_SUB ? -1.f : 1.f;
+  hipError_t e = hipSuccess;
+  if (ns == 0) {
+    // Sums over nothing: each requested gradient is its acc, or zeros.
+    const zk_desc *dw[3] = {da, db, dc};
+    float *gw[3] = {grad_a, grad_b, wc ? grad_c : nullptr};
+    const float *aw[3] = {acc_a, acc_b, acc_c};
+    for (int w = 0; w < 3; ++w) {
+      if (!gw[w] || cnt[w] == 0) continue;
+      BwdPlan pz;
+      if ((s = plan_reduce(ds, dw[w]->rank, dw[w]->sizes, 0, 0, &pz))) return s;
+      e = launch_reduce(pz, grad, gw[w], ws, st, aw[w]);
+      if (e != hipSuccess) return ZK_ERR_HIP;
+    }
+    return ZK_OK;
+  }
+  if (tbuf) {
+    e = launch_reduce(pt, grad, tbuf, ws + L.op1 + L.cred + L.tbuf, st);
+    if (e != hipSuccess) return ZK_ERR_HIP;
+  }
+  // c's gradient rides with the op1 backward when both walk the full layout
+  const bool gc_in_op1 = wc && nc == ns && !split && (wa || wb);
+  if (wa || wb) {
+    e = launch_bwd(p1, op1, ZK_EPI_NONE, up, a, b, grad_a, acc_a1, grad_b, acc_b1, ws, st,
+                   gc_in_op1 ? grad_c : nullptr, acc_c, sign);
+    if (e != hipSuccess) return ZK_ERR_HIP;
+  }
+  if (wc && !gc_in_op1) {
+    if (nc == ns) e = launch_signed(grad, ns, grad_c, acc_c, sign, st);
+    else e = launch_reduce(pc, grad, grad_c, ws + L.op1, st, acc_c, op2 == ZK_SUB);
+    if (e != hipSuccess) return ZK_ERR_HIP;
+  }
+  return ZK_OK;
 }
 
 zk_status zk_plan_describe(int32_t kind, zk_op op, zk_epi epi, const zk_desc *da,

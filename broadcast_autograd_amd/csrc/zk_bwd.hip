@@ -33,6 +33,31 @@ constexpr int kColWaves = 16;
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// Optional extra output of the fused two-operator backward: the gradient of
+// the second operator's c, +-g (+ acc), written by the stage-1 kernel that
+// streams g anyway.  p == nullptr: off.  Dense in the output layout.
+struct GcOut {
+  float *p;
+  const float *acc;
+  float sign;  // +1 (add) or -1 (sub): exact
+};
+__device__ __forceinline__ void gc_store4(const GcOut &o, int64_t i, float4 vg) {
+  float4 v;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) el(v, k) = o.sign * el(vg, k);
+  if (o.acc) {
+    const float4 x = ld4_nt(o.acc + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) el(v, k) = el(x, k) + el(v, k);
+  }
+  st4_nt(o.p + i, v);
+}
+__device__ __forceinline__ void gc_store1(const GcOut &o, int64_t i, float g) {
+  float v = o.sign * g;
+  if (o.acc) v = o.acc[i] + v;
+  o.p[i] = v;
+}
+
 template <typename Fn>
 static hipError_t op_epi(zk_op op, zk_epi epi, Fn &&fn) {
   switch ((int)op * 2 + (int)epi) {
@@ -99,7 +124,7 @@ __device__ __forceinline__ void ew_one(float gv, float x, float y, float aa,
 template <int OP, int EPI, int VEC>
 __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
     const float *g, const float *a, const float *b, float *ga,
-    const float *acc_a, float *gb, const float *acc_b, EwArgs ea) {
+    const float *acc_a, float *gb, const float *acc_b, EwArgs ea, GcOut gco) {
   constexpr int U = 1;  // one vector per lane, one tile per block: streams best
   constexpr int64_t tile = (int64_t)kBlk * U * VEC;
   const int64_t ntiles = (ea.n + tile - 1) / tile;
@@ -131,6 +156,7 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
                             ea.acc_b == 2 ? el(xb[u], k) : 0.f, ea, el(oa, k), el(ob, k));
           if (ea.write_a) st4_nt(ga + i, oa);
           if (ea.write_b) st4_nt(gb + i, ob);
+          if (gco.p) gc_store4(gco, i, vg[u]);
         } else if (i < ea.n) {
           for (int64_t j = i; j < ea.n; ++j) {
             float oa = 0.f, ob = 0.f;
@@ -139,6 +165,7 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
                             ea, oa, ob);
             if (ea.write_a) ga[j] = oa;
             if (ea.write_b) gb[j] = ob;
+            if (gco.p) gc_store1(gco, j, g[j]);
           }
         }
       }
@@ -153,6 +180,7 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
                           ea, oa, ob);
           if (ea.write_a) ga[j] = oa;
           if (ea.write_b) gb[j] = ob;
+          if (gco.p) gc_store1(gco, j, g[j]);
         }
       }
     }
@@ -224,7 +252,7 @@ struct ColArgs {
 template <int OP, int EPI, int SIDE, int ACC, int NW>
 __global__ __launch_bounds__(64 * NW) void k_red_col(
     const float *g, const float *big, const float *small, float *gbig,
-    const float *accbig, double *part, ColArgs ca) {
+    const float *accbig, double *part, ColArgs ca, GcOut gco) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
   // rows in flight per wave: two for the plain rules; one with the GeLU
@@ -283,6 +311,7 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
             el(ob, k) = t;
           }
           if (ca.write_big) st4_nt(gbig + i, ob);
+          if (gco.p) gc_store4(gco, i, vg[u]);
         }
       }
     }
@@ -320,7 +349,7 @@ struct RowRedArgs {
 template <int OP, int EPI, int SIDE, int ACC>
 __global__ __launch_bounds__(kBlk) void k_red_row(
     const float *g, const float *big, const float *small, float *gbig,
-    const float *accbig, double *part, RowRedArgs ra) {
+    const float *accbig, double *part, RowRedArgs ra, GcOut gco) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
   // one vector per lane per trip over short chunks (many waves) streams best
@@ -368,6 +397,7 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
             el(ob, q) = tb;
           }
           if (ra.write_big) st4_nt(gbig + i, ob);
+          if (gco.p) gc_store4(gco, i, vg[u]);
         }
       }
     }
@@ -589,6 +619,7 @@ __global__ __launch_bounds__(kBlk) void k_red_generic(const float *g,
 struct FinArgs {
   int64_t K, P, per;  // per: partials per thread
   int32_t tpk, kt, has_acc;
+  int32_t neg;  // the terms are the negated partials (exact)
 };
 
 __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
@@ -618,11 +649,33 @@ __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
       __syncthreads();
     }
     if (q == 0 && ok) {
-      double tot = sh[kk];
+      double tot = fa.neg ? -sh[kk] : sh[kk];
       if (fa.has_acc) tot += (double)acc[k];
       out[k] = (float)tot;
     }
     __syncthreads();  // sh is rewritten by the next group
+  }
+}
+
+// ------------------------------------------------------------ bwd_signed
+// gc[i] = sign * g[i] (+ acc[i]) over the dense output layout: the gradient
+// of the second operator's c when no stage-1 kernel streams g for it.
+template <int VEC>
+__global__ __launch_bounds__(kBlk) void k_bwd_signed(const float *g, GcOut gco, int64_t n) {
+  constexpr int64_t tile = (int64_t)kBlk * VEC;
+  const int64_t ntiles = (n + tile - 1) / tile;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    if constexpr (VEC == 4) {
+      const int64_t i = t * tile + (int64_t)threadIdx.x * 4;
+      if (i + 4 <= n) {
+        gc_store4(gco, i, ld4_nt(g + i));
+      } else {
+        for (int64_t j = i; j < n; ++j) gc_store1(gco, j, g[j]);
+      }
+    } else {
+      const int64_t j = t * tile + threadIdx.x;
+      if (j < n) gc_store1(gco, j, g[j]);
+    }
   }
 }
 
@@ -636,9 +689,11 @@ static inline unsigned gridn(int64_t n, int64_t per) {
 }
 
 static hipError_t launch_final(const RedPlan &rp, const double *part,
-                               const float *acc, float *out, hipStream_t st) {
+                               const float *acc, float *out, hipStream_t st,
+                               bool neg = false) {
   if (rp.kept == 0) return hipSuccess;
   FinArgs fa{};
+  fa.neg = neg ? 1 : 0;
   fa.K = rp.kept;
   fa.P = rp.partials;
   // Threads per kept element: enough that each loads about 8 partials, but
@@ -686,12 +741,34 @@ static int acc_mode(const float *acc, const float *g) {
   return acc == g ? 1 : 2;
 }
 
+static bool al16p(const void *q) { return ((uintptr_t)q & 15u) == 0; }
+
+hipError_t launch_signed(const float *g, int64_t n, float *gc, const float *acc,
+                         float sign, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const GcOut gco{gc, acc, sign};
+  ProfScope prof(K_BWD_SIGNED);
+  if (al16p(g) && al16p(gc) && al16p(acc))
+    ZK_LAUNCH(prof, (k_bwd_signed<4>), dim3(gridn(n, kBlk * 4)), dim3(kBlk), 0, st, g, gco, n);
+  else
+    ZK_LAUNCH(prof, (k_bwd_signed<1>), dim3(gridn(n, kBlk)), dim3(kBlk), 0, st, g, gco, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
                       const float *a, const float *b, float *grad_a,
                       const float *acc_a, float *grad_b, const float *acc_b,
-                      void *ws, hipStream_t st) {
+                      void *ws, hipStream_t st, float *grad_c, const float *acc_c,
+                      float c_sign) {
   const Canon &c = p.c;
   hipError_t e = hipSuccess;
+  // The c gradient of the fused backward rides along with the first stage-1
+  // kernel that streams all of g in the output layout with 128-bit accesses
+  // (or any layout for the scalar element-wise kernel); otherwise it gets a
+  // pass of its own at the end.
+  GcOut gco{nullptr, nullptr, c_sign};
+  bool gc_done = grad_c == nullptr;
+  const bool gc_al = al16p(grad_c) && al16p(acc_c);
   // Element-wise gradients of full-shape operands.
   if (p.ew_kernel != K_NONE) {
     EwArgs ea{};
@@ -707,12 +784,17 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
       constexpr int EPI = decltype(EPIc)::value;
       ProfScope prof(p.ew_kernel);
       if (p.ew_kernel == K_BWD_EW_FLAT) {
+        GcOut go{nullptr, nullptr, c_sign};
+        if (!gc_done && (p.vec == 1 || gc_al)) {
+          go = GcOut{grad_c, acc_c, c_sign};
+          gc_done = true;
+        }
         if (p.vec == 4)
           ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 4>), dim3(gridn(c.numel, kBlk * 4)),
-                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
+                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, go);
         else
           ZK_LAUNCH(prof, (k_bwd_ew_flat<OP, EPI, 1>), dim3(gridn(c.numel, kBlk)),
-                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea);
+                    dim3(kBlk), 0, st, g, a, b, grad_a, acc_a, grad_b, acc_b, ea, go);
       } else {
         Space sp = make_space(c);
         if (p.idx64)
@@ -737,6 +819,13 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
     const float *accsmall = sw == 0 ? acc_a : acc_b;
     const float *accbig = sw == 0 ? acc_b : acc_a;
     const int amode = p.fused_big ? acc_mode(accbig, g) : 0;
+    // red_col and red_row stream all of g in the output layout
+    GcOut go{nullptr, nullptr, c_sign};
+    if (!gc_done && gc_al && rp.partials > 0 &&
+        (rp.kernel == K_RED_COL || rp.kernel == K_RED_ROW)) {
+      go = GcOut{grad_c, acc_c, c_sign};
+      gc_done = true;
+    }
     if (rp.partials > 0) {
       e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
         constexpr int OP = decltype(OPc)::value;
@@ -756,10 +845,11 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
               constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
               if (rp.nw == 1)
                 ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, 1>), dim3(grid), dim3(64), 0, st, g,
-                          big, small, gbig, accbig, part, ca);
+                          big, small, gbig, accbig, part, ca, go);
               else
                 ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, kColWaves>), dim3(grid),
-                          dim3(64 * kColWaves), 0, st, g, big, small, gbig, accbig, part, ca);
+                          dim3(64 * kColWaves), 0, st, g, big, small, gbig, accbig, part, ca,
+                          go);
               return hipGetLastError();
             });
           }
@@ -777,7 +867,7 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               ZK_LAUNCH(prof, (k_red_row<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
                         dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
-                        part, ra);
+                        part, ra, go);
               return hipGetLastError();
             });
           }
@@ -827,11 +917,13 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
     e = launch_final(rp, part, accsmall, gsmall, st);
     if (e != hipSuccess) return e;
   }
+  if (!gc_done) return launch_signed(g, c.numel, grad_c, acc_c, c_sign, st);
   return hipSuccess;
 }
 
 hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
-                         void *ws, hipStream_t st) {
+                         void *ws, hipStream_t st, const float *acc, bool neg) {
+  const GcOut none{nullptr, nullptr, 1.f};
   const Canon &c = p.c;
   for (int ri = 0; ri < p.nred; ++ri) {
     const RedPlan &rp = p.red[ri];
@@ -850,11 +942,11 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           const unsigned grid = (unsigned)(ca.colblocks * rp.partials);
           if (rp.nw == 1)
             ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, 1>), dim3(grid), dim3(64), 0,
-                      st, in, nullptr, nullptr, nullptr, nullptr, part, ca);
+                      st, in, nullptr, nullptr, nullptr, nullptr, part, ca, none);
           else
             ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, kColWaves>), dim3(grid),
                       dim3(64 * kColWaves), 0, st, in, nullptr, nullptr, nullptr, nullptr, part,
-                      ca);
+                      ca, none);
           break;
         }
         case K_RED_ROW: {
@@ -868,7 +960,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ra.ss = 0;
           ra.write_big = 0;
           ZK_LAUNCH(prof, (k_red_row<ZK_ADD, ZK_EPI_NONE, 1, 0>), dim3(gridn(ra.items, 4)),
-                    dim3(kBlk), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ra);
+                    dim3(kBlk), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ra, none);
           break;
         }
         default: {
@@ -885,7 +977,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipError_t e = launch_final(rp, part, nullptr, out, st);
+    hipError_t e = launch_final(rp, part, acc, out, st, neg);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

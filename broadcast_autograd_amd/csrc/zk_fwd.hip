@@ -400,6 +400,122 @@ __global__ __launch_bounds__(kBlock) void k_fwd_generic(const float *a,
   }
 }
 
+// ------------------------------------------------------ fused forward
+// out = (a op1 b) op2 c, each operator one binary32 operation (Operator
+// chapter, "fusion": the same math in one pass; the intermediate is never
+// stored).  ROW: canonical rank <= 3, inner dim a multiple of 4; each input
+// walks the output's layout (IM_FLAT), repeats the first input (IM_SAME_A),
+// or is read at its decoded offset with its own inner-dim mode.
+struct In3 {
+  const float *p;
+  int64_t s[3];  // canonical strides (rank <= 3; unused dims 0)
+  int32_t mode;
+};
+struct Space3 {
+  int32_t rank;
+  int64_t n[3];
+  FastDiv fd[3];
+  int64_t numel;
+};
+
+template <typename I>
+__device__ __forceinline__ float4 load_in3(const In3 &x, I i, I c0, I c1, I c2) {
+  if (x.mode == IM_FLAT) return ld4_nt(x.p + i);
+  const I off = c0 * (I)x.s[0] + c1 * (I)x.s[1] + c2 * (I)x.s[2];
+  if (x.mode == IM_BCAST) {
+    const float v = x.p[off];
+    return make_float4(v, v, v, v);
+  }
+  if (x.mode == IM_CONTIG) return ld4(x.p + off);
+  float4 v;
+  const I si = (I)x.s[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) el(v, k) = x.p[off + (I)k * si];
+  return v;
+}
+
+template <int OP1, int OP2, typename I>
+__global__ __launch_bounds__(kBlock) void k_fwd2_row(In3 a, In3 b, In3 c, float *out,
+                                                     Space3 sp) {
+  const I n = (I)sp.numel;
+  const bool dec = a.mode != IM_FLAT || b.mode != IM_FLAT ||
+                   (c.mode != IM_FLAT && c.mode != IM_SAME_A);
+  // 64-bit loop counter: i + stride may pass 2^31 even when n does not
+  for (int64_t j = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4; j < (int64_t)n;
+       j += (int64_t)gridDim.x * kBlock * 4) {
+    const I i = (I)j;
+    // coordinates of element i over the (up to) 3 canonical dims
+    I c0 = 0, c1 = 0, c2 = i;
+    if (dec && sp.rank >= 2) {
+      I q;
+      if constexpr (sizeof(I) == 4) q = (I)fdiv(sp.fd[sp.rank - 1], (uint32_t)i);
+      else q = i / (I)sp.n[sp.rank - 1];
+      c2 = i - q * (I)sp.n[sp.rank - 1];
+      if (sp.rank == 3) {
+        I q2;
+        if constexpr (sizeof(I) == 4) q2 = (I)fdiv(sp.fd[1], (uint32_t)q);
+        else q2 = q / (I)sp.n[1];
+        c1 = q - q2 * (I)sp.n[1];
+        c0 = q2;
+      } else {
+        c1 = q;
+      }
+    }
+    // the kernel's In3 strides are aligned to (c0, c1, c2) by the launcher
+    const float4 va = load_in3<I>(a, i, c0, c1, c2);
+    const float4 vb = load_in3<I>(b, i, c0, c1, c2);
+    const float4 vc = c.mode == IM_SAME_A ? va : load_in3<I>(c, i, c0, c1, c2);
+    float4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      el(r, k) = op32<OP2>(op32<OP1>(el(va, k), el(vb, k)), el(vc, k));
+    st4_nt(out + i, r);
+  }
+}
+
+template <int OP1, int OP2, typename I>
+__global__ __launch_bounds__(kBlock) void k_fwd2_generic(const float *a, const float *b,
+                                                         const float *c, float *out,
+                                                         Space sp, int vec_out) {
+  const I n = (I)sp.numel;
+  for (int64_t j0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4; j0 < (int64_t)n;
+       j0 += (int64_t)gridDim.x * kBlock * 4) {
+    const I i0 = (I)j0;
+    float r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const I i = i0 + k;
+      if (i < n) {
+        I rest = i, oa = 0, ob = 0, oc = 0;
+#pragma unroll
+        for (int d = kMaxDims - 1; d >= 1; --d) {
+          if (d < sp.rank) {
+            I q;
+            if constexpr (sizeof(I) == 4) q = (I)fdiv(sp.fd[d], (uint32_t)rest);
+            else q = rest / (I)sp.n[d];
+            const I cd = rest - q * (I)sp.n[d];
+            oa += cd * (I)sp.s[1][d];
+            ob += cd * (I)sp.s[2][d];
+            oc += cd * (I)sp.s[3][d];
+            rest = q;
+          }
+        }
+        oa += rest * (I)sp.s[1][0];
+        ob += rest * (I)sp.s[2][0];
+        oc += rest * (I)sp.s[3][0];
+        r[k] = op32<OP2>(op32<OP1>(a[oa], b[ob]), c[oc]);
+      }
+    }
+    if (vec_out && i0 + 4 <= n) {
+      st4(out + i0, make_float4(r[0], r[1], r[2], r[3]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < n) out[i0 + k] = r[k];
+    }
+  }
+}
+
 // -------------------------------------------------------------- launcher
 static inline unsigned grid_of(int64_t n, int64_t per_block) {
   const int64_t g = (n + per_block - 1) / per_block;
@@ -510,6 +626,70 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         return hipGetLastError();
       }
     }
+  });
+}
+
+// Calls fn(IC<op1>, IC<op2>) for op1 in add..div, op2 in add/sub.
+template <typename Fn>
+static hipError_t with_op2(zk_op op1, zk_op op2, Fn &&fn) {
+  switch ((int)op1 * 2 + (op2 == ZK_SUB ? 1 : 0)) {
+    case 0: return fn(IC<ZK_ADD>{}, IC<ZK_ADD>{});
+    case 1: return fn(IC<ZK_ADD>{}, IC<ZK_SUB>{});
+    case 2: return fn(IC<ZK_SUB>{}, IC<ZK_ADD>{});
+    case 3: return fn(IC<ZK_SUB>{}, IC<ZK_SUB>{});
+    case 4: return fn(IC<ZK_MUL>{}, IC<ZK_ADD>{});
+    case 5: return fn(IC<ZK_MUL>{}, IC<ZK_SUB>{});
+    case 6: return fn(IC<ZK_DIV>{}, IC<ZK_ADD>{});
+    case 7: return fn(IC<ZK_DIV>{}, IC<ZK_SUB>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd2(const Fwd2Plan &p, zk_op op1, zk_op op2, const float *a,
+                       const float *b, const float *c, float *out, hipStream_t st) {
+  if (p.empty) return hipSuccess;
+  const Canon &cn = p.c;
+  return with_op2(op1, op2, [&](auto O1, auto O2) -> hipError_t {
+    constexpr int OP1 = decltype(O1)::value;
+    constexpr int OP2 = decltype(O2)::value;
+    ProfScope prof(p.kernel);
+    const unsigned grid = grid_of(cn.numel, kBlock * 4);
+    if (p.kernel == K_FWD2_ROW) {
+      // canonical dims right-aligned onto (c0, c1, c2)
+      Space3 sp{};
+      sp.rank = cn.rank;
+      sp.numel = cn.numel;
+      for (int k = 0; k < 3; ++k) {
+        sp.n[k] = k < cn.rank ? cn.n[k] : 1;
+        sp.fd[k] = make_fastdiv(sp.n[k] < ((int64_t)1 << 31) ? (uint32_t)sp.n[k] : 1u);
+      }
+      In3 in[3];
+      const float *ptr[3] = {a, b, c};
+      for (int x = 0; x < 3; ++x) {
+        in[x].p = ptr[x];
+        in[x].mode = p.mode[x];
+        for (int k = 0; k < 3; ++k) in[x].s[k] = 0;
+        // rank 1: (c2); rank 2: (c1, c2); rank 3: (c0, c1, c2)
+        for (int k = 0; k < cn.rank; ++k) in[x].s[3 - cn.rank + k] = cn.s[1 + x][k];
+      }
+      // sp.n / sp.fd are indexed by canonical dim; the kernel divides by the
+      // innermost (rank-1) and, for rank 3, by dim 1.
+      if (p.idx64)
+        ZK_LAUNCH(prof, (k_fwd2_row<OP1, OP2, int64_t>), dim3(grid), dim3(kBlock), 0, st,
+                  in[0], in[1], in[2], out, sp);
+      else
+        ZK_LAUNCH(prof, (k_fwd2_row<OP1, OP2, int32_t>), dim3(grid), dim3(kBlock), 0, st,
+                  in[0], in[1], in[2], out, sp);
+      return hipGetLastError();
+    }
+    Space sp = make_space(cn);
+    if (p.idx64)
+      ZK_LAUNCH(prof, (k_fwd2_generic<OP1, OP2, int64_t>), dim3(grid), dim3(kBlock), 0, st,
+                a, b, c, out, sp, p.vec == 4 ? 1 : 0);
+    else
+      ZK_LAUNCH(prof, (k_fwd2_generic<OP1, OP2, int32_t>), dim3(grid), dim3(kBlock), 0, st,
+                a, b, c, out, sp, p.vec == 4 ? 1 : 0);
+    return hipGetLastError();
   });
 }
 

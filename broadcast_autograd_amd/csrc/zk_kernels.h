@@ -53,12 +53,24 @@ struct ProfScope {
 hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
                       const float *b, float *out, hipStream_t st);
 
+hipError_t launch_fwd2(const Fwd2Plan &p, zk_op op1, zk_op op2, const float *a,
+                       const float *b, const float *c, float *out, hipStream_t st);
+
+// grad_c (optional): also write c_sign * g (+ acc_c) over the dense output
+// layout, the gradient of a fused expression's second operand c.
 hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
                       const float *a, const float *b, float *grad_a,
                       const float *acc_a, float *grad_b, const float *acc_b,
-                      void *ws, hipStream_t st);
+                      void *ws, hipStream_t st, float *grad_c = nullptr,
+                      const float *acc_c = nullptr, float c_sign = 1.f);
 
+// gc[i] = sign * g[i] (+ acc[i]) for i < n.
+hipError_t launch_signed(const float *g, int64_t n, float *gc, const float *acc,
+                         float sign, hipStream_t st);
+
+// acc (optional) is added to each sum; neg negates the sum first.
 hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
-                         void *ws, hipStream_t st);
+                         void *ws, hipStream_t st, const float *acc = nullptr,
+                         bool neg = false);
 
 }  // namespace zk

@@ -10,7 +10,8 @@ const char *kernel_name(int32_t k) {
   static const char *names[K_COUNT] = {
       "fwd_flat",       "fwd_row",       "fwd_tile",   "fwd_generic",
       "bwd_ew_flat",    "bwd_ew_generic", "red_col",   "red_row",
-      "red_tile",       "red_generic",   "red_final"};
+      "red_tile",       "red_generic",   "red_final",  "fwd2_row",
+      "fwd2_generic",   "bwd_signed"};
   if (k < 0 || k >= K_COUNT) return "none";
   return names[k];
 }
@@ -255,6 +256,74 @@ zk_status plan_fwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
   p->kernel = K_FWD_GENERIC;
   p->swap = false;
   p->vec = (al16(pout) && (!fa || al16(pa)) && (!fb || al16(pb))) ? 4 : 1;
+  return ZK_OK;
+}
+
+// ------------------------------------------------------- fused forward
+zk_status broadcast_shape3(const zk_desc &da, const zk_desc &db, const zk_desc &dc,
+                           int *r, int64_t *n) {
+  int r1;
+  int64_t n1[kMaxDims];
+  zk_status s = broadcast_shape(da.rank, da.sizes, db.rank, db.sizes, &r1, n1);
+  if (s) return s;
+  return broadcast_shape(r1, n1, dc.rank, dc.sizes, r, n);
+}
+
+static bool same_view(const zk_desc &x, const zk_desc &y) {
+  if (x.rank != y.rank) return false;
+  for (int k = 0; k < x.rank; ++k)
+    if (x.sizes[k] != y.sizes[k] || (x.sizes[k] != 1 && x.strides[k] != y.strides[k]))
+      return false;
+  return true;
+}
+
+zk_status plan_fwd2(const zk_desc &da, const zk_desc &db, const zk_desc &dc,
+                    uintptr_t pa, uintptr_t pb, uintptr_t pc, uintptr_t pout,
+                    Fwd2Plan *p) {
+  int r;
+  int64_t n[kMaxDims];
+  zk_status s = broadcast_shape3(da, db, dc, &r, n);
+  if (s) return s;
+  int64_t st[kMaxOps][kMaxDims];
+  {
+    int64_t d = 1;
+    for (int k = r - 1; k >= 0; --k) { st[0][k] = d; d *= n[k]; }
+  }
+  align_strides(da, r, st[1]);
+  align_strides(db, r, st[2]);
+  align_strides(dc, r, st[3]);
+  p->c = canonicalise(r, n, 4, st);
+  const Canon &c = p->c;
+  if (c.numel == 0) {
+    p->empty = true;
+    p->kernel = K_NONE;
+    return ZK_OK;
+  }
+  p->idx64 = needs_idx64(c);
+  const int64_t inner = c.n[c.rank - 1];
+  if (c.rank <= 3 && inner % 4 == 0 && al16(pout)) {
+    p->kernel = K_FWD2_ROW;
+    p->vec = 4;
+    const uintptr_t ptr[3] = {pa, pb, pc};
+    for (int x = 0; x < 3; ++x) {
+      const int o = 1 + x;
+      if (x == 2 && pc == pa && same_view(dc, da)) {
+        p->mode[x] = IM_SAME_A;
+      } else if (is_flat(c, o) && al16(ptr[x])) {
+        p->mode[x] = IM_FLAT;
+      } else if (c.s[o][c.rank - 1] == 0) {
+        p->mode[x] = IM_BCAST;
+      } else {
+        bool contig = c.s[o][c.rank - 1] == 1 && al16(ptr[x]);
+        for (int k = 0; k + 1 < c.rank; ++k)
+          if (c.s[o][k] % 4 != 0) contig = false;
+        p->mode[x] = contig ? IM_CONTIG : IM_GATHER;
+      }
+    }
+    return ZK_OK;
+  }
+  p->kernel = K_FWD2_GENERIC;
+  p->vec = al16(pout) ? 4 : 1;
   return ZK_OK;
 }
 

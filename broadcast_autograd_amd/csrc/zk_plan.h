@@ -34,7 +34,10 @@ enum KernelClass : int32_t {
   K_RED_TILE = 8,     // fused backward stage 1, [R, K] with a transposed operand
   K_RED_GENERIC = 9,  // gather stage 1, any pattern
   K_RED_FINAL = 10,   // stage 2: fixed-order sum of the partials
-  K_COUNT = 11
+  K_FWD2_ROW = 11,    // fused (a op1 b) op2 c, rank <= 3, 128-bit output
+  K_FWD2_GENERIC = 12,  // fused (a op1 b) op2 c, anything (rank <= 8)
+  K_BWD_SIGNED = 13,  // +-g (+ acc) element-wise: the gradient of op2's c
+  K_COUNT = 14
 };
 
 const char *kernel_name(int32_t k);
@@ -86,6 +89,15 @@ void byte_extent_dense(const void *p, int64_t numel, uintptr_t *lo,
 bool overlaps(uintptr_t alo, uintptr_t ahi, uintptr_t blo, uintptr_t bhi);
 
 // ---------------------------------------------------------------- forward
+// Access mode of one input of the fused forward (K_FWD2_ROW).
+enum InMode : int32_t {
+  IM_FLAT = 0,    // walks the output's dense layout (128-bit, aligned)
+  IM_BCAST = 1,   // decoded offset; inner dim repeated (stride 0)
+  IM_CONTIG = 2,  // decoded offset; inner dim contiguous, 128-bit aligned
+  IM_GATHER = 3,  // decoded offset; inner dim any stride
+  IM_SAME_A = 4   // the same tensor as input a (read once)
+};
+
 struct FwdPlan {
   Canon c;            // ops: 0 out, 1 a, 2 b
   int32_t kernel = K_NONE;
@@ -97,6 +109,22 @@ struct FwdPlan {
 };
 zk_status plan_fwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
                    uintptr_t pa, uintptr_t pb, uintptr_t pout, FwdPlan *p);
+
+// Fused out = (a op1 b) op2 c.  Canon ops: 0 out, 1 a, 2 b, 3 c.
+struct Fwd2Plan {
+  Canon c;
+  int32_t kernel = K_NONE;  // K_FWD2_ROW or K_FWD2_GENERIC
+  bool empty = false;
+  bool idx64 = false;
+  int vec = 1;
+  int32_t mode[3] = {IM_GATHER, IM_GATHER, IM_GATHER};  // a, b, c (ROW)
+};
+// Broadcast shape of three shapes (a with b, then with c).
+zk_status broadcast_shape3(const zk_desc &da, const zk_desc &db, const zk_desc &dc,
+                           int *r, int64_t *n);
+zk_status plan_fwd2(const zk_desc &da, const zk_desc &db, const zk_desc &dc,
+                    uintptr_t pa, uintptr_t pb, uintptr_t pc, uintptr_t pout,
+                    Fwd2Plan *p);
 
 // --------------------------------------------------------------- backward
 // One stage-1 reduction for one operand's gradient.

@@ -226,5 +226,99 @@ class GPTResidual(Workload):
         ]
 
 
+# ------------------------------------------------------------------ fused
+# The same expressions as one fused call each way (Operator chapter, "fusion":
+# merged operators, same math): out = (a op1 b) op2 c forward, and the
+# backward of all inputs from one pass over g.
+
+
+class XYPlusXFused(Workload):
+    """z = x*y + x as one fused call; x's two paths land in one buffer."""
+    name = "xy_plus_x_fused"
+
+    def __init__(self, host=None, scale=1):
+        import torch
+        h = host or W.xy_plus_x(scale)
+        self.host = h
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in h.items()}
+        self.x, self.y, self.g = d["x"], d["y"], d["g"]
+        e = torch.empty_like
+        self.z, self.grad_x, self.grad_y = e(self.x), e(self.x), e(self.y)
+        self.ws = _ws(zk.bwd2_workspace_bytes("mul", "add", self.x, self.y, self.x,
+                                              tie="a"), torch)
+        nx, ny = _n(self.x.shape), _n(self.y.shape)
+        self.calls = [
+            Call("fused mul,add(x,y,x)->z", "fwd",
+                 lambda: zk.binary2_fwd("mul", "add", self.x, self.y, self.x, out=self.z),
+                 [nx, ny], [nx]),
+            Call("fused bwd(g;x,y,x)->grad_x(both paths),grad_y", "bwd",
+                 lambda: zk.binary2_bwd("mul", "add", self.g, self.x, self.y, self.x,
+                                        need=(True, True, True),
+                                        grads=(self.grad_x, self.grad_y, None), tie="a",
+                                        workspace=self.ws),
+                 [nx, nx, ny], [nx, ny]),
+        ]
+
+
+class AttnScaleMaskFused(Workload):
+    """scores * scale + mask as one fused call; the mask gets no gradient."""
+    name = "attn_scale_mask_fused"
+
+    def __init__(self, host=None, b=8, h=16, t=1024):
+        import torch
+        hh = host or W.attn_scale_mask(b, h, t)
+        self.host = hh
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in hh.items()}
+        self.scores, self.scale, self.mask, self.g = d["scores"], d["scale"], d["mask"], d["g"]
+        e = torch.empty_like
+        self.out, self.grad_scores, self.grad_scale = e(self.scores), e(self.scores), e(self.scale)
+        self.ws = _ws(zk.bwd2_workspace_bytes("mul", "add", self.scores, self.scale, self.mask,
+                                              need=(True, True, False)), torch)
+        ns, nc, nm = _n(self.scores.shape), _n(self.scale.shape), _n(self.mask.shape)
+        self.calls = [
+            Call("fused mul,add(scores,scale,mask)->out", "fwd",
+                 lambda: zk.binary2_fwd("mul", "add", self.scores, self.scale, self.mask,
+                                        out=self.out),
+                 [ns, nc, nm], [ns]),
+            Call("fused bwd(g;scores,scale,mask)->grad_scores,grad_scale", "bwd",
+                 lambda: zk.binary2_bwd("mul", "add", self.g, self.scores, self.scale,
+                                        self.mask, need=(True, True, False),
+                                        grads=(self.grad_scores, self.grad_scale, None),
+                                        workspace=self.ws),
+                 [ns, ns, nc], [ns, nc]),
+        ]
+
+
+class GPTResidualFused(Workload):
+    """h * gamma + resid as one fused call; grad_resid from the same pass."""
+    name = "gpt_residual_fused"
+
+    def __init__(self, host=None, b=16, t=2048, c=4096):
+        import torch
+        hh = host or W.gpt_residual(b, t, c)
+        self.host = hh
+        d = {k: torch.from_numpy(v).to("cuda") for k, v in hh.items()}
+        self.h, self.gamma, self.resid, self.g = d["h"], d["gamma"], d["resid"], d["g"]
+        e = torch.empty_like
+        self.out, self.grad_h, self.grad_gamma = e(self.h), e(self.h), e(self.gamma)
+        self.grad_resid = e(self.h)
+        self.ws = _ws(zk.bwd2_workspace_bytes("mul", "add", self.h, self.gamma, self.resid),
+                      torch)
+        nh, ng = _n(self.h.shape), _n(self.gamma.shape)
+        self.calls = [
+            Call("fused mul,add(h,gamma,resid)->out", "fwd",
+                 lambda: zk.binary2_fwd("mul", "add", self.h, self.gamma, self.resid,
+                                        out=self.out),
+                 [nh, ng, nh], [nh]),
+            Call("fused bwd(g;h,gamma,resid)->grad_h,grad_gamma,grad_resid", "bwd",
+                 lambda: zk.binary2_bwd("mul", "add", self.g, self.h, self.gamma, self.resid,
+                                        grads=(self.grad_h, self.grad_gamma, self.grad_resid),
+                                        workspace=self.ws),
+                 [nh, nh, ng], [nh, ng, nh]),
+        ]
+
+
 WORKLOAD_CLASSES = {c.name: c for c in (XYPlusX, MLPBiasGelu, AttnScaleMask,
-                                        StridedTransposed, Rank8, GPTResidual)}
+                                        StridedTransposed, Rank8, GPTResidual,
+                                        XYPlusXFused, AttnScaleMaskFused,
+                                        GPTResidualFused)}

@@ -24,9 +24,9 @@ ERR = {v: k for k, v in STATUS.items()}
 
 # exported symbols declared in include/zk.h
 SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
-           "zk_reduce_to_shape", "zk_status_string", "zk_plan_describe",
-           "zk_kernel_name", "zk_profile_start", "zk_profile_stop",
-           "zk_profile_read")
+           "zk_reduce_to_shape", "zk_binary2_fwd", "zk_binary2_bwd",
+           "zk_status_string", "zk_plan_describe", "zk_kernel_name",
+           "zk_profile_start", "zk_profile_stop", "zk_profile_read")
 
 
 class ZkError(RuntimeError):
@@ -75,6 +75,8 @@ def lib():
         L.zk_binary_fwd.argtypes = [I32, I32, P, P, P, P, P, P]
         L.zk_binary_bwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, P, P]
         L.zk_reduce_to_shape.argtypes = [P, P, I32, P, P, P, P, P]
+        L.zk_binary2_fwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P]
+        L.zk_binary2_bwd.argtypes = [I32, I32] + [P] * 16
         L.zk_status_string.argtypes = [I32]
         L.zk_status_string.restype = ctypes.c_char_p
         L.zk_plan_describe.argtypes = [I32, I32, I32, P, P, P]
@@ -211,6 +213,74 @@ def binary_bwd(op, grad, a, b, need_a=True, need_b=True, grad_a=None,
     _check(L.zk_binary_bwd(*args, _ptr(workspace), ctypes.byref(nbytes),
                            _stream(stream)), "zk_binary_bwd")
     return grad_a, grad_b
+
+
+def broadcast_shape3(sa, sb, sc):
+    return broadcast_shape(broadcast_shape(sa, sb), sc)
+
+
+def binary2_fwd(op1, op2, a, b, c, out=None, stream=None):
+    """out = (a (op1) b) (op2) c in the broadcast shape of a, b and c, one
+    pass, each operator rounded on its own (op2: "add" or "sub")."""
+    import torch
+    if out is None:
+        shape = broadcast_shape3(a.shape, b.shape, c.shape)
+        out = torch.empty(shape, dtype=torch.float32, device=a.device)
+    da, db, dc = desc_of(a), desc_of(b), desc_of(c)
+    _check(lib().zk_binary2_fwd(_op(op1), _op(op2), _ptr(a), ctypes.byref(da), _ptr(b),
+                                ctypes.byref(db), _ptr(c), ctypes.byref(dc), _ptr(out),
+                                _stream(stream)), "zk_binary2_fwd")
+    return out
+
+
+def bwd2_workspace_bytes(op1, op2, a, b, c, need=(True, True, True), tie=None):
+    """Workspace zk_binary2_bwd needs for these operands (no launch)."""
+    da, db, dc = desc_of(a), desc_of(b), desc_of(c)
+    nbytes = ctypes.c_size_t(0)
+    m = [ctypes.c_void_p(16 + 64 * k) if need[k] else None for k in range(3)]
+    if tie is not None:
+        m[2] = m[0] if tie == "a" else m[1]
+    mark = ctypes.c_void_p(16)
+    cp = mark if tie is None else mark
+    _check(lib().zk_binary2_bwd(_op(op1), _op(op2), mark, mark, ctypes.byref(da), mark,
+                                ctypes.byref(db), cp, ctypes.byref(dc), m[0], None, m[1],
+                                None, m[2], None, None, ctypes.byref(nbytes), None),
+           "zk_binary2_bwd(query)")
+    return nbytes.value
+
+
+def binary2_bwd(op1, op2, grad, a, b, c, need=(True, True, True), grads=(None, None, None),
+                accs=(None, None, None), tie=None, workspace=None, stream=None):
+    """Gradients of (a (op1) b) (op2) c for the upstream ``grad``; returns
+    (grad_a, grad_b, grad_c), each dense in its operand's shape (None if not
+    requested).  tie "a" / "b": c is that same tensor and one buffer takes
+    both paths (returned for that operand; grad_c is then None)."""
+    import torch
+    ops = (a, b, c)
+    out = []
+    for k in range(3):
+        g = grads[k]
+        if need[k] and g is None and not (k == 2 and tie is not None):
+            g = torch.empty(ops[k].shape, dtype=torch.float32, device=grad.device)
+        out.append(g if need[k] else None)
+    if tie is not None:
+        out[2] = out[0] if tie == "a" else out[1]
+    da, db, dc = desc_of(a), desc_of(b), desc_of(c)
+    nbytes = ctypes.c_size_t(0)
+    L = lib()
+    args = (_op(op1), _op(op2), _ptr(grad), _ptr(a), ctypes.byref(da), _ptr(b),
+            ctypes.byref(db), _ptr(c), ctypes.byref(dc), _ptr(out[0]), _ptr(accs[0]),
+            _ptr(out[1]), _ptr(accs[1]), _ptr(out[2]), _ptr(accs[2]))
+    if workspace is None:
+        _check(L.zk_binary2_bwd(*args, None, ctypes.byref(nbytes), None),
+               "zk_binary2_bwd(query)")
+        workspace = _workspace(nbytes.value, grad.device)
+    nbytes.value = workspace.numel() * workspace.element_size()
+    _check(L.zk_binary2_bwd(*args, _ptr(workspace), ctypes.byref(nbytes), _stream(stream)),
+           "zk_binary2_bwd")
+    if tie is not None:
+        out[2] = None
+    return tuple(out)
 
 
 def reduce_workspace_bytes(x, shape):

@@ -167,6 +167,58 @@ zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
                              float *out, void *workspace,
                              size_t *workspace_bytes, void *stream);
 
+/*
+ * Fused two-operator expression (Operator chapter, "fusion": several small
+ * element-wise operators merged into one execution unit, with the usual
+ * forward/backward interface and without changing the math):
+ *   out = (a (op1) b) (op2) c,  op1 in {add, sub, mul, div}, op2 in {add, sub}
+ * over the broadcast shape of a, b and c (a with b, then with c).  Each
+ * operator is still one binary32 operation with its own rounding (no fused
+ * multiply-add), so the result equals zk_binary_fwd(op1, a, b) followed by
+ * zk_binary_fwd(op2, ., c) bit for bit; the intermediate is never stored.
+ *   a, da / b, db / c, dc : inputs, any non-negative strides; c may be the
+ *                           same tensor as a (then read once)
+ *   out                   : dense row-major, broadcast shape
+ * Aliasing: out may be exactly an input that is dense row-major with the
+ * full broadcast shape; any other overlap is ZK_ERR_ALIAS.
+ * Errors: as zk_binary_fwd; op2 other than add or sub is
+ * ZK_ERR_UNSUPPORTED.
+ */
+zk_status zk_binary2_fwd(zk_op op1, zk_op op2, const float *a,
+                         const zk_desc *da, const float *b, const zk_desc *db,
+                         const float *c, const zk_desc *dc, float *out,
+                         void *stream);
+
+/*
+ * Backward of out = (a (op1) b) (op2) c for the upstream gradient `grad`
+ * (dense row-major, broadcast shape).  op2 hands g to t = a (op1) b and +g
+ * (add) or -g (sub) to c (GPU chapter, "OpAdd"; sub by calculus), so
+ *   grad_a, grad_b : zk_binary_bwd's op1 rules applied to the gradient of t,
+ *                    which is g summed to t's shape (g itself when t has the
+ *                    full broadcast shape), then summed to a's / b's shape
+ *   grad_c         : +-g summed to c's shape
+ * Each requested gradient is added to its acc as in zk_binary_bwd; NULL
+ * gradients are skipped.  When c's gradient has the full shape it is
+ * written by the pass that streams g for a and b.
+ * A tensor used twice (Autograd chapter, "chain rule", z = x*y + x): when c
+ * is the same tensor as a (same pointer and descriptor) with the full
+ * broadcast shape and op2 is add, grad_c may be exactly grad_a, with acc_a
+ * and acc_c NULL; that buffer receives the sum of both paths.  Likewise for
+ * b.  Any other shared gradient buffer is ZK_ERR_UNSUPPORTED (if it is
+ * grad_a or grad_b) or ZK_ERR_ALIAS.
+ * Workspace protocol as in zk_binary_bwd (NULL queries; size depends on the
+ * shapes and on which gradients are requested).
+ * Errors: as zk_binary_bwd; op2 other than add or sub is
+ * ZK_ERR_UNSUPPORTED.
+ */
+zk_status zk_binary2_bwd(zk_op op1, zk_op op2, const float *grad,
+                         const float *a, const zk_desc *da, const float *b,
+                         const zk_desc *db, const float *c, const zk_desc *dc,
+                         float *grad_a, const float *acc_a, float *grad_b,
+                         const float *acc_b, float *grad_c, const float *acc_c,
+                         void *workspace, size_t *workspace_bytes,
+                         void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *zk_status_string(zk_status s);
 

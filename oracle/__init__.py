@@ -73,6 +73,12 @@ def lib():
         L.or_bwd_at.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                 P, P, P, I64, P, P, P, P]
         L.or_reduce.argtypes = [P, P, ctypes.c_int, P, P, P, P]
+        L.or_fwd2.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P]
+        L.or_fwd2_at.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, I64, P, P]
+        L.or_bwd2.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
+                              P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.or_bwd2_at.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 P, P, P, P, P, P, P, P, I64, P, P, P, P]
         L.or_gelu32.argtypes = [ctypes.c_float]
         L.or_gelu32.restype = ctypes.c_float
         L.or_phi_cdf.argtypes = [ctypes.c_double]
@@ -258,6 +264,86 @@ def reduce_to_shape(x, shape):
 
     _check(lib().or_reduce(_ptr(v), ctypes.byref(d), len(shape), _i64(shape),
                            p(f32), p(f64), p(ab)))
+    return Grad(f32, f64, ab)
+
+
+def broadcast_shape3(sa, sb, sc):
+    return broadcast_shape(broadcast_shape(sa, sb), sc)
+
+
+def fwd2(op1, op2, a, b, c):
+    """out = (a (op1) b) (op2) c in the broadcast shape of a, b and c: the two
+    operators one after the other, each one binary32 operation."""
+    va, vb, vc = _as_view(a), _as_view(b), _as_view(c)
+    shape = broadcast_shape3(va.sizes, vb.sizes, vc.sizes)
+    out = np.empty(shape, dtype=np.float32)
+    da, db, dc = _desc(va), _desc(vb), _desc(vc)
+    _check(lib().or_fwd2(_op(op1), _op(op2), _ptr(va), ctypes.byref(da), _ptr(vb),
+                         ctypes.byref(db), _ptr(vc), ctypes.byref(dc),
+                         out.ctypes.data if out.size else None))
+    return out
+
+
+def fwd2_at(op1, op2, a, b, c, pos):
+    """Fused forward at flat output positions ``pos`` only."""
+    va, vb, vc = _as_view(a), _as_view(b), _as_view(c)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    out = np.empty(pos.shape, dtype=np.float32)
+    da, db, dc = _desc(va), _desc(vb), _desc(vc)
+    _check(lib().or_fwd2_at(_op(op1), _op(op2), _ptr(va), ctypes.byref(da), _ptr(vb),
+                            ctypes.byref(db), _ptr(vc), ctypes.byref(dc), pos.size,
+                            pos.ctypes.data, out.ctypes.data))
+    return out
+
+
+_TIE = {None: -1, "a": 0, "b": 1}
+
+
+def bwd2(op1, op2, g, a, b, c, acc=(None, None, None), want=(True, True, True), tie=None):
+    """Gradients of sum(g * ((a op1 b) op2 c)) w.r.t. a, b and c (dense, in
+    each operand's shape), each accumulated onto its acc when given.  tie
+    "a" / "b": c is the same tensor as a / b; that operand's gradient then
+    has both paths and the c gradient is None."""
+    va, vb, vc = _as_view(a), _as_view(b), _as_view(c)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    da, db, dc = _desc(va), _desc(vb), _desc(vc)
+    t = _TIE[tie]
+    bufs = []
+    for k, (v, w) in enumerate(((va, want[0]), (vb, want[1]), (vc, want[2] and t < 0))):
+        if not w:
+            bufs.append((None, None, None))
+            continue
+        bufs.append((np.empty(v.sizes, dtype=np.float32), np.empty(v.sizes, dtype=np.float64),
+                     np.empty(v.sizes, dtype=np.float64)))
+
+    def p(x):
+        return None if x is None or x.size == 0 else x.ctypes.data
+
+    accs = [None if x is None else np.ascontiguousarray(x, dtype=np.float32) for x in acc]
+    _check(lib().or_bwd2(_op(op1), _op(op2), t, p(g), _ptr(va), ctypes.byref(da), _ptr(vb),
+                         ctypes.byref(db), _ptr(vc), ctypes.byref(dc), p(accs[0]),
+                         p(accs[1]), p(accs[2]), *[p(x) for buf in bufs for x in buf]))
+    return tuple(None if f32 is None else Grad(f32, f64, ab) for f32, f64, ab in bufs)
+
+
+def bwd2_at(op1, op2, which, g, a, b, c, pos, acc=None, tie=None):
+    """One gradient of the fused expression (which: 0 = a, 1 = b, 2 = c) at
+    dense positions ``pos``."""
+    va, vb, vc = _as_view(a), _as_view(b), _as_view(c)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    da, db, dc = _desc(va), _desc(vb), _desc(vc)
+    f32 = np.empty(pos.shape, dtype=np.float32)
+    f64 = np.empty(pos.shape, dtype=np.float64)
+    ab = np.empty(pos.shape, dtype=np.float64)
+    accp = None
+    if acc is not None:
+        acc = np.ascontiguousarray(acc, dtype=np.float32)
+        accp = acc.ctypes.data
+    _check(lib().or_bwd2_at(_op(op1), _op(op2), which, _TIE[tie], g.ctypes.data, _ptr(va),
+                            ctypes.byref(da), _ptr(vb), ctypes.byref(db), _ptr(vc),
+                            ctypes.byref(dc), accp, pos.size, pos.ctypes.data,
+                            f32.ctypes.data, f64.ctypes.data, ab.ctypes.data))
     return Grad(f32, f64, ab)
 
 

@@ -18,6 +18,10 @@
  *     several paths gets the sum of the path gradients
  *       (Operator chapter, "broadcast"; Autograd chapter, "chain rule")
  * sub and div rules are not printed there; they are plain calculus.
+ *   - a fused operator merges several operators into one unit without
+ *     changing their math (Operator chapter, "fusion" section): the fused
+ *     expression (a op1 b) op2 c is computed here as the two operators one
+ *     after the other
  *
  * Precision (the pages fix none):
  *   forward  : one IEEE binary32 operation per element, round-to-nearest-even
@@ -380,6 +384,178 @@ int or_reduce(const float *in, const or_desc *din, int rout,
     if (out) out[j] = (float)sum;
     if (out64) out64[j] = sum;
     if (absout) absout[j] = as;
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------- fused two-operator expression */
+
+static int check3(int op1, int op2, const or_desc *da, const or_desc *db,
+                  const or_desc *dc, int *r, int64_t *n) {
+  if (op1 < OR_ADD || op1 > OR_DIV || (op2 != OR_ADD && op2 != OR_SUB)) return OR_ERR_ARG;
+  int s;
+  if ((s = check_desc(da)) || (s = check_desc(db)) || (s = check_desc(dc))) return s;
+  int r1;
+  int64_t n1[OR_MAX_DIMS];
+  if ((s = or_broadcast_shape(da->rank, da->sizes, db->rank, db->sizes, &r1, n1))) return s;
+  return or_broadcast_shape(r1, n1, dc->rank, dc->sizes, r, n);
+}
+
+/* t = a (op1) b rounded to binary32, then t (op2) c rounded to binary32. */
+static float fwd2_at(int op1, int op2, const float *a, const or_desc *da,
+                     const float *b, const or_desc *db, const float *c,
+                     const or_desc *dc, int r, const int64_t *idx) {
+  float t = op32(op1, a[operand_offset(da, r, idx)], b[operand_offset(db, r, idx)]);
+  return op32(op2, t, c[operand_offset(dc, r, idx)]);
+}
+
+/* out (dense, broadcast shape of a, b, c) = (a op1 b) op2 c. */
+int or_fwd2(int op1, int op2, const float *a, const or_desc *da, const float *b,
+            const or_desc *db, const float *c, const or_desc *dc, float *out) {
+  int r, s;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = check3(op1, op2, da, db, dc, &r, n))) return s;
+  int64_t total = numel(r, n);
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t f = 0; f < total; ++f) {
+    int64_t idx[OR_MAX_DIMS];
+    unflatten(f, r, n, idx);
+    out[f] = fwd2_at(op1, op2, a, da, b, db, c, dc, r, idx);
+  }
+  return OR_OK;
+}
+
+int or_fwd2_at(int op1, int op2, const float *a, const or_desc *da, const float *b,
+               const or_desc *db, const float *c, const or_desc *dc, int64_t count,
+               const int64_t *pos, float *out) {
+  int r, s;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = check3(op1, op2, da, db, dc, &r, n))) return s;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t t = 0; t < count; ++t) {
+    int64_t idx[OR_MAX_DIMS];
+    unflatten(pos[t], r, n, idx);
+    out[t] = fwd2_at(op1, op2, a, da, b, db, c, dc, r, idx);
+  }
+  return OR_OK;
+}
+
+/* Gradient of operand `which` (0 = a, 1 = b, 2 = c) of L = sum_i g_i out_i,
+ * out = (a op1 b) op2 c, at its dense position j.  op2 (add or sub) hands
+ * g_i to t = a op1 b and +-g_i to c (GPU chapter, "OpAdd"; sub by calculus);
+ * op1's local rule turns the former into the terms of a and b.  Every
+ * output position i reading element j contributes, in row-major order of i.
+ * tie = which (0 or 1): c is the same tensor as this operand, and the c-path
+ * term +-g_i of the same positions is added too (Autograd chapter: a tensor
+ * reached along two paths gets the sum of the path gradients). */
+static double grad2_at(int op1, int op2, int which, int tie, const float *g,
+                       const float *a, const or_desc *da, const float *b,
+                       const or_desc *db, const float *c, const or_desc *dc,
+                       const float *acc, int r, const int64_t *n, int64_t j,
+                       double *absum) {
+  const or_desc *dx = which == 0 ? da : (which == 1 ? db : dc);
+  int64_t xidx[OR_MAX_DIMS];
+  unflatten(j, dx->rank, dx->sizes, xidx);
+  int64_t lo[OR_MAX_DIMS], cnt[OR_MAX_DIMS];
+  for (int k = 0; k < r; ++k) {
+    int kx = k - (r - dx->rank);
+    if (kx >= 0 && dx->sizes[kx] != 1) {
+      lo[k] = xidx[kx];
+      cnt[k] = 1;
+    } else {
+      lo[k] = 0;
+      cnt[k] = n[k];
+    }
+  }
+  double sum = 0.0, as = 0.0;
+  if (acc) {
+    sum = (double)acc[j];
+    as = fabs(sum);
+  }
+  int64_t gstr[OR_MAX_DIMS];
+  {
+    int64_t s = 1;
+    for (int k = r - 1; k >= 0; --k) { gstr[k] = s; s *= n[k]; }
+  }
+  int64_t total = numel(r, cnt);
+  int64_t idx[OR_MAX_DIMS], sub[OR_MAX_DIMS];
+  for (int64_t t = 0; t < total; ++t) {
+    unflatten(t, r, cnt, sub);
+    int64_t goff = 0;
+    for (int k = 0; k < r; ++k) {
+      idx[k] = lo[k] + sub[k];
+      goff += idx[k] * gstr[k];
+    }
+    double gi = (double)g[goff];
+    double cpath = op2 == OR_SUB ? -gi : gi;
+    if (which == 2 || tie == which) {
+      sum += cpath;
+      as += fabs(cpath);
+    }
+    if (which < 2) {
+      float xv = a[operand_offset(da, r, idx)];
+      float yv = b[operand_offset(db, r, idx)];
+      double piece[2];
+      int np = local_terms(op1, OR_EPI_NONE, which, gi, (double)xv, (double)yv, 0.0f, piece);
+      for (int p = 0; p < np; ++p) {
+        sum += piece[p];
+        as += fabs(piece[p]);
+      }
+    }
+  }
+  *absum = as;
+  return sum;
+}
+
+/* Full backward of the fused expression; outputs as in or_bwd, three of
+ * them (NULL = not wanted).  tie: -1, or 0 / 1 when c is the same tensor as
+ * a / b (then grad_c is ignored and that operand's gradient has both paths). */
+int or_bwd2(int op1, int op2, int tie, const float *g, const float *a,
+            const or_desc *da, const float *b, const or_desc *db, const float *c,
+            const or_desc *dc, const float *acc_a, const float *acc_b,
+            const float *acc_c, float *grad_a, double *grad_a64, double *abs_a,
+            float *grad_b, double *grad_b64, double *abs_b, float *grad_c,
+            double *grad_c64, double *abs_c) {
+  int r, s;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = check3(op1, op2, da, db, dc, &r, n))) return s;
+  if (tie < -1 || tie > 1) return OR_ERR_ARG;
+  for (int which = 0; which < 3; ++which) {
+    float *gx = which == 0 ? grad_a : (which == 1 ? grad_b : grad_c);
+    double *gx64 = which == 0 ? grad_a64 : (which == 1 ? grad_b64 : grad_c64);
+    double *ax = which == 0 ? abs_a : (which == 1 ? abs_b : abs_c);
+    const float *acc = which == 0 ? acc_a : (which == 1 ? acc_b : acc_c);
+    const or_desc *dx = which == 0 ? da : (which == 1 ? db : dc);
+    if ((!gx && !gx64) || (which == 2 && tie >= 0)) continue;
+    int64_t m = numel(dx->rank, dx->sizes);
+#pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads)
+    for (int64_t j = 0; j < m; ++j) {
+      double as;
+      double v = grad2_at(op1, op2, which, tie, g, a, da, b, db, c, dc, acc, r, n, j, &as);
+      if (gx) gx[j] = (float)v;
+      if (gx64) gx64[j] = v;
+      if (ax) ax[j] = as;
+    }
+  }
+  return OR_OK;
+}
+
+/* One gradient of the fused expression at listed dense positions. */
+int or_bwd2_at(int op1, int op2, int which, int tie, const float *g, const float *a,
+               const or_desc *da, const float *b, const or_desc *db, const float *c,
+               const or_desc *dc, const float *acc, int64_t count, const int64_t *pos,
+               float *out, double *out64, double *absout) {
+  int r, s;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = check3(op1, op2, da, db, dc, &r, n))) return s;
+  if (which < 0 || which > 2 || tie < -1 || tie > 1) return OR_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(g_threads)
+  for (int64_t t = 0; t < count; ++t) {
+    double as;
+    double v = grad2_at(op1, op2, which, tie, g, a, da, b, db, c, dc, acc, r, n, pos[t], &as);
+    if (out) out[t] = (float)v;
+    if (out64) out64[t] = v;
+    if (absout) absout[t] = as;
   }
   return OR_OK;
 }

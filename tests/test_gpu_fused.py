@@ -1,0 +1,217 @@
+"""GPU parity of the fused two-operator expression out = (a op1 b) op2 c
+(Operator chapter, "fusion") against the CPU oracle, through the C ABI.
+
+Forward: bit-exact (the same two binary32 roundings as the unfused pair).
+Backward: |err| <= 2e-6 * sum|terms| (+ one binary32 subnormal step).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from broadcast_autograd_amd import steps, workloads as W, zk  # noqa: E402
+from gpu_util import assert_bitexact, assert_bwd, dev, host, strided_pair  # noqa: E402
+
+OPS1 = ["add", "sub", "mul", "div"]
+OPS2 = ["add", "sub"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    say(f"\n[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+
+
+def _vals(rng, shape, lo=0.5, hi=2.0, signed=True):
+    x = rng.uniform(lo, hi, shape).astype(np.float32)
+    if signed:
+        x *= np.where(rng.random(shape) < 0.5, -1, 1).astype(np.float32)
+    return x
+
+
+def check3(orc, op1, op2, a, b, c, ta, tb, tc, seed=0, need=(True, True, True), accs=None):
+    want = orc.fwd2(op1, op2, a, b, c)
+    got = host(zk.binary2_fwd(op1, op2, ta, tb, tc))
+    assert_bitexact(got, want, f"fwd2 {op1},{op2}")
+    g = np.random.default_rng(seed).standard_normal(want.shape).astype(np.float32)
+    accs = accs or (None, None, None)
+    dacc = tuple(None if x is None else dev(x) for x in accs)
+    ga = zk.binary2_bwd(op1, op2, dev(g), ta, tb, tc, need=need, accs=dacc)
+    ref = orc.bwd2(op1, op2, g, a, b, c, acc=accs, want=need)
+    for k, name in enumerate("abc"):
+        if need[k]:
+            assert_bwd(host(ga[k]), ref[k], f"grad_{name} {op1},{op2}")
+
+
+SHAPES = [
+    ((64, 256), (256,), (64, 256)),          # residual-like, c dense
+    ((4, 16, 64), (16, 1), (4, 16, 64)),     # x*y + z with y a column
+    ((8, 4, 128), (1, 4, 1), (1, 1, 128)),   # attention-like: scale and mask
+    ((32, 96), (96,), (1, 96)),              # c a broadcast row
+    ((30, 70), (70,), (30, 1)),              # inner dim not a multiple of 4
+    ((2, 3, 4, 5, 6), (1, 3, 1, 5, 1), (4, 5, 6)),  # rank 5: generic kernels
+    ((3, 1), (1, 4), (2, 3, 4)),             # t repeated into out (split path)
+    ((), (5,), (2, 5)),                      # scalar a
+]
+
+
+@pytest.mark.parametrize("shapes", SHAPES)
+@pytest.mark.parametrize("op1", OPS1)
+@pytest.mark.parametrize("op2", OPS2)
+def test_fused_shapes(orc, shapes, op1, op2):
+    sa, sb, sc = shapes
+    rng = np.random.default_rng(abs(hash((shapes, op1, op2))) % 2**32)
+    a, b, c = _vals(rng, sa), _vals(rng, sb), _vals(rng, sc)
+    check3(orc, op1, op2, a, b, c, dev(a), dev(b), dev(c), seed=3)
+
+
+def test_fused_accumulate(orc):
+    rng = np.random.default_rng(11)
+    a, b, c = _vals(rng, (48, 64)), _vals(rng, (64,)), _vals(rng, (48, 64))
+    accs = tuple(rng.standard_normal(s).astype(np.float32) for s in ((48, 64), (64,), (48, 64)))
+    check3(orc, "mul", "sub", a, b, c, dev(a), dev(b), dev(c), seed=4, accs=accs)
+    # c broadcast: its gradient is a (negated) sum plus acc
+    c1 = _vals(rng, (1, 64))
+    accs1 = (accs[0], accs[1], rng.standard_normal((1, 64)).astype(np.float32))
+    check3(orc, "div", "sub", a, b, c1, dev(a), dev(b), dev(c1), seed=5, accs=accs1)
+
+
+@pytest.mark.parametrize("need", [(True, False, True), (False, True, False),
+                                  (False, False, True), (True, True, False)])
+def test_fused_partial_requests(orc, need):
+    rng = np.random.default_rng(12)
+    a, b, c = _vals(rng, (16, 128)), _vals(rng, (128,)), _vals(rng, (16, 128))
+    check3(orc, "mul", "add", a, b, c, dev(a), dev(b), dev(c), seed=6, need=need)
+
+
+def test_fused_strided_views(orc):
+    """Transposed and stride-0 views on every input (generic and gather
+    paths of the fused kernels)."""
+    rng = np.random.default_rng(13)
+    s = rng.uniform(0.5, 2, 40 * 24).astype(np.float32)
+    va, ta, _ = strided_pair(s, (24, 40), (1, 24))  # transposed
+    b = _vals(rng, (40,))
+    sc = rng.uniform(0.5, 2, 24 * 3).astype(np.float32)
+    vc, tc, _ = strided_pair(sc, (24, 40), (3, 0))  # stride-0 inner
+    for op1 in OPS1:
+        check3(orc, op1, "add", va, b, vc, ta, dev(b), tc, seed=7)
+
+
+def test_fused_tie_xy_plus_x(orc):
+    """z = x*y + x (Autograd chapter worked example, config layout at a small
+    size): x's two paths accumulate into one buffer."""
+    h = W.xy_plus_x()
+    x, y, g = h["x"][:4], h["y"], h["g"][:4]
+    tx, ty = dev(x), dev(y)
+    z = host(zk.binary2_fwd("mul", "add", tx, ty, tx))
+    assert_bitexact(z, orc.fwd2("mul", "add", x, y, x), "fwd2 tie")
+    gx, gy, gc = zk.binary2_bwd("mul", "add", dev(g), tx, ty, tx, tie="a")
+    assert gc is None
+    rx, ry, _ = orc.bwd2("mul", "add", g, x, y, x, tie="a")
+    assert_bwd(host(gx), rx, "grad_x (both paths)")
+    assert_bwd(host(gy), ry, "grad_y")
+    # the worked example itself
+    one = dev(np.array([1.0], np.float32))
+    x3, y2 = dev(np.array([3.0], np.float32)), dev(np.array([2.0], np.float32))
+    assert float(host(zk.binary2_fwd("mul", "add", x3, y2, x3))[0]) == 9.0
+    gx, gy, _ = zk.binary2_bwd("mul", "add", one, x3, y2, x3, tie="a")
+    assert float(host(gx)[0]) == 3.0 and float(host(gy)[0]) == 3.0
+
+
+def test_fused_matches_unfused_pair_bitwise():
+    """The fused forward equals zk_binary_fwd(op1) then zk_binary_fwd(op2)."""
+    rng = np.random.default_rng(14)
+    a, b, c = _vals(rng, (8, 16, 256)), _vals(rng, (16, 1)), _vals(rng, (8, 16, 256))
+    ta, tb, tc = dev(a), dev(b), dev(c)
+    for op1 in OPS1:
+        for op2 in OPS2:
+            t = zk.binary_fwd(op1, ta, tb)
+            want = host(zk.binary_fwd(op2, t, tc))
+            got = host(zk.binary2_fwd(op1, op2, ta, tb, tc))
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (op1, op2)
+
+
+def test_fused_empty_and_zero_sizes(orc):
+    a = np.zeros((3, 0), np.float32)
+    b = np.ones((1,), np.float32)
+    c = np.ones((3, 1), np.float32)
+    out = zk.binary2_fwd("mul", "add", dev(a), dev(b), dev(c))
+    assert tuple(out.shape) == (3, 0)
+    # out is empty: every gradient is a sum over nothing (its acc, or 0)
+    g = dev(np.zeros((3, 0), np.float32))
+    acc_b = np.array([2.5], np.float32)
+    ga, gb, gc = zk.binary2_bwd("mul", "add", g, dev(a), dev(b), dev(c),
+                                accs=(None, dev(acc_b), None))
+    assert host(gb)[0] == 2.5 and np.all(host(gc) == 0)
+
+
+def test_fused_determinism():
+    h = W.gpt_residual(b=2, t=128, c=4096)
+    wl = steps.GPTResidualFused(host=h)
+    outs = []
+    for _ in range(2):
+        wl.run()
+        outs.append([host(getattr(wl, k)).copy() for k in ("out", "grad_h", "grad_gamma",
+                                                            "grad_resid")])
+    for x, y in zip(*outs):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+# ----------------------------------------- full sizes of the fused workloads
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.integers(0, n, k, dtype=np.int64), [0, n - 1]]))
+
+
+def test_full_size_fused_gpt_residual(orc):
+    wl = steps.GPTResidualFused()
+    h = wl.host
+    wl.run()
+    pos = _sample(wl.out.numel(), 20000, 21)
+    assert_bitexact(host(wl.out).reshape(-1)[pos],
+                    orc.fwd2_at("mul", "add", h["h"], h["gamma"], h["resid"], pos), "out")
+    for which, name in ((0, "grad_h"), (2, "grad_resid")):
+        ref = orc.bwd2_at("mul", "add", which, h["g"], h["h"], h["gamma"], h["resid"], pos)
+        assert_bwd(host(getattr(wl, name)).reshape(-1)[pos], ref, name)
+    kpos = np.arange(wl.grad_gamma.numel(), dtype=np.int64)
+    ref = orc.bwd2_at("mul", "add", 1, h["g"], h["h"], h["gamma"], h["resid"], kpos)
+    assert_bwd(host(wl.grad_gamma).reshape(-1), ref, "grad_gamma")
+
+
+def test_full_size_fused_attn_scale_mask(orc):
+    wl = steps.AttnScaleMaskFused()
+    h = wl.host
+    wl.run()
+    pos = _sample(wl.out.numel(), 20000, 22)
+    assert_bitexact(host(wl.out).reshape(-1)[pos],
+                    orc.fwd2_at("mul", "add", h["scores"], h["scale"], h["mask"], pos), "out")
+    ref = orc.bwd2_at("mul", "add", 0, h["g"], h["scores"], h["scale"], h["mask"], pos)
+    assert_bwd(host(wl.grad_scores).reshape(-1)[pos], ref, "grad_scores")
+    kpos = np.arange(wl.grad_scale.numel(), dtype=np.int64)
+    ref = orc.bwd2_at("mul", "add", 1, h["g"], h["scores"], h["scale"], h["mask"], kpos)
+    assert_bwd(host(wl.grad_scale).reshape(-1), ref, "grad_scale")
+
+
+def test_full_size_fused_xy_plus_x(orc):
+    wl = steps.XYPlusXFused()
+    h = wl.host
+    wl.run()
+    assert_bitexact(host(wl.z), orc.fwd2("mul", "add", h["x"], h["y"], h["x"]), "z")
+    pos = _sample(wl.grad_x.numel(), 20000, 23)
+    ref = orc.bwd2_at("mul", "add", 0, h["g"], h["x"], h["y"], h["x"], pos, tie="a")
+    assert_bwd(host(wl.grad_x).reshape(-1)[pos], ref, "grad_x")
+    kpos = np.arange(wl.grad_y.numel(), dtype=np.int64)
+    ref = orc.bwd2_at("mul", "add", 1, h["g"], h["x"], h["y"], h["x"], kpos, tie="a")
+    assert_bwd(host(wl.grad_y).reshape(-1), ref, "grad_y")

@@ -139,6 +139,50 @@ def test_backward_validation_errors(L):
                                      FO, None, FW, None, None, None, None)] == "ZK_ERR_NULL"
 
 
+FC = ctypes.c_void_p(9 << 20)  # distinct from the addresses above
+
+
+def _fwd2(op1, op2, da, db, dc, a=FA, b=FB, c=FC, out=FO):
+    return zk.STATUS[zk.lib().zk_binary2_fwd(op1, op2, a, ctypes.byref(da), b,
+                                              ctypes.byref(db), c, ctypes.byref(dc), out,
+                                              None)]
+
+
+def _bwd2(op1, op2, da, db, dc, ga=None, gb=None, gc=None, acc=(None, None, None),
+          g=FG, a=FA, b=FB, c=FC, ws=None, wsb=1 << 30):
+    n = ctypes.c_size_t(wsb)
+    return zk.STATUS[zk.lib().zk_binary2_bwd(op1, op2, g, a, ctypes.byref(da), b,
+                                              ctypes.byref(db), c, ctypes.byref(dc), ga,
+                                              acc[0], gb, acc[1], gc, acc[2], ws,
+                                              ctypes.byref(n), None)], n.value
+
+
+def test_fused_validation_errors(L):
+    d = zk.make_desc((4, 8))
+    r = zk.make_desc((8,))
+    assert _fwd2(2, 2, d, r, d) == "ZK_ERR_UNSUPPORTED"  # op2 must be add or sub
+    assert _fwd2(5, 0, d, r, d) == "ZK_ERR_UNSUPPORTED"
+    assert _fwd2(2, 0, d, r, zk.make_desc((5,))) == "ZK_ERR_BROADCAST"
+    assert _fwd2(2, 0, d, r, d, c=None) == "ZK_ERR_NULL"
+    assert _fwd2(2, 0, d, r, d, out=ctypes.c_void_p(FC.value + 4)) == "ZK_ERR_ALIAS"
+    # the backward workspace query launches nothing
+    st, need = _bwd2(2, 0, d, r, d, ga=FO, gb=FW, gc=ctypes.c_void_p(7 << 20))
+    assert st == "ZK_OK" and need > 0
+    ws = ctypes.c_void_p(6 << 20)
+    gc = ctypes.c_void_p(7 << 20)
+    assert _bwd2(2, 0, d, r, d, ga=FO, gb=FW, gc=gc, ws=ws, wsb=need - 1)[0] == "ZK_ERR_WORKSPACE"
+    # shared gradient buffer: only grad_c == grad_a with c the same tensor as a
+    assert _bwd2(2, 0, d, r, d, ga=FO, gc=FO, ws=ws)[0] == "ZK_ERR_UNSUPPORTED"   # c != a
+    assert _bwd2(2, 1, d, r, d, ga=FO, gc=FO, c=FA, ws=ws)[0] == "ZK_ERR_UNSUPPORTED"  # sub
+    assert _bwd2(2, 0, d, r, d, ga=FO, gc=FO, c=FA, ws=ws,
+                 acc=(FW, None, None))[0] == "ZK_ERR_UNSUPPORTED"  # acc with a tie
+    # grad_c overlapping another output, an input or the upstream gradient
+    assert _bwd2(2, 0, d, r, d, ga=FO, gc=ctypes.c_void_p(FO.value + 8), ws=ws)[0] == "ZK_ERR_ALIAS"
+    assert _bwd2(2, 0, d, r, d, gc=FA, ws=ws)[0] == "ZK_ERR_ALIAS"
+    assert _bwd2(2, 0, d, r, d, gc=FG, ws=ws)[0] == "ZK_ERR_ALIAS"
+    assert _bwd2(2, 0, d, r, d, gc=gc, acc=(None, None, FO), ga=FO, ws=ws)[0] == "ZK_ERR_ALIAS"
+
+
 def test_reduce_validation_errors(L):
     d = zk.make_desc((4, 6))
 

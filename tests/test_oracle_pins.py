@@ -411,3 +411,97 @@ def test_sampled_paths_agree_with_full(orc):
     np.testing.assert_array_equal(s.f64, gb.f64.reshape(-1))
     s = orc.bwd_at("div", 0, g, a, b, pos)
     np.testing.assert_array_equal(s.f32, ga.f32.reshape(-1)[pos])
+
+
+# ------------------------------------------ fused (a op1 b) op2 c (f1) -----
+def test_fused_chain_rule_worked_example(orc):
+    """Autograd chapter, "computation graph": z = x*y + x at x=3, y=2, as one
+    fused expression with x used twice (both paths into one gradient)."""
+    v = _kv(_golden("chain_rule_example.txt"))
+    x, y = _scalar([v["x"]]), _scalar([v["y"]])
+    z = orc.fwd2("mul", "add", x, y, x)
+    assert float(z[0]) == v["z"]
+    g = _scalar([v["dz_dz"]])
+    gx, gy, gc = orc.bwd2("mul", "add", g, x, y, x, tie="a")
+    assert gc is None
+    assert float(gx.f32[0]) == v["dz_dx"] and float(gy.f32[0]) == v["dz_dy"]
+    # without the tie the two paths stay apart: 2 through x*y, 1 through + x
+    ga, gb, gc = orc.bwd2("mul", "add", g, x, y, x)
+    assert float(ga.f32[0]) == 2.0 and float(gc.f32[0]) == 1.0 and float(gb.f32[0]) == 3.0
+
+
+@pytest.mark.parametrize("op1", ["add", "sub", "mul", "div"])
+@pytest.mark.parametrize("op2", ["add", "sub"])
+@pytest.mark.parametrize("shapes", [((2, 3), (3,), (2, 3)), ((3, 1), (1, 4), (4,)),
+                                    ((2, 1, 3), (2, 3), (1, 2, 1))])
+def test_fused_backward_finite_differences(orc, op1, op2, shapes):
+    """Central differences of L = sum(g * ((a op1 b) op2 c)) in binary64 pin
+    every rule, sign and broadcast sum of the fused backward, c included."""
+    sa, sb, sc = shapes
+    rng = np.random.default_rng(hash((op1, op2, shapes)) % 2**32)
+    a = rng.uniform(0.5, 2.0, sa).astype(np.float32)
+    b = rng.uniform(0.5, 2.0, sb).astype(np.float32)
+    c = rng.uniform(-2.0, 2.0, sc).astype(np.float32)
+    if op1 in ("add", "sub", "mul"):
+        a *= np.where(rng.random(sa) < 0.5, -1, 1).astype(np.float32)
+    out_shape = np.broadcast_shapes(sa, sb, sc)
+    g = rng.standard_normal(out_shape).astype(np.float32)
+    grads = orc.bwd2(op1, op2, g, a, b, c)
+
+    def L(a64, b64, c64):
+        f = _f64(op2, _f64(op1, a64, b64), c64)
+        return math.fsum((g.astype(np.float64) * f).ravel())
+
+    xs = [a.astype(np.float64), b.astype(np.float64), c.astype(np.float64)]
+    for which in range(3):
+        gx = grads[which]
+        for j in np.ndindex(xs[which].shape):
+            h = 1e-4 * max(1.0, abs(xs[which][j]))
+            xp = [x.copy() for x in xs]
+            xm = [x.copy() for x in xs]
+            xp[which][j] += h
+            xm[which][j] -= h
+            fd = (L(*xp) - L(*xm)) / (2 * h)
+            tol = (2e-5 if op1 == "div" else 1e-6) * max(1.0, gx.abs[j])
+            assert abs(fd - gx.f64[j]) <= tol, (op1, op2, which, j, fd, gx.f64[j])
+
+
+def test_fused_forward_is_two_roundings(orc):
+    """The fused forward rounds after each operator: it equals the unfused
+    pair of forwards bit for bit, and differs from a single rounding of the
+    exact a*b + c on inputs chosen so that the two disagree."""
+    rng = np.random.default_rng(31)
+    a = rng.standard_normal((5, 7)).astype(np.float32)
+    b = rng.standard_normal((7,)).astype(np.float32)
+    c = rng.standard_normal((5, 1)).astype(np.float32)
+    for op1 in ("add", "sub", "mul", "div"):
+        for op2 in ("add", "sub"):
+            want = orc.fwd(op2, orc.fwd(op1, a, b), c)
+            got = orc.fwd2(op1, op2, a, b, c)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # (1 + 2^-23) * (1 - 2^-23) = 1 - 2^-46 rounds to 1; minus 1 gives 0,
+    # while a fused multiply-add would give -2^-46.
+    x = np.array([1 + 2.0 ** -23], np.float32)
+    y = np.array([1 - 2.0 ** -23], np.float32)
+    one = np.array([1.0], np.float32)
+    assert orc.fwd2("mul", "sub", x, y, one)[0] == 0.0
+
+
+def test_fused_mass_and_tie_identities(orc):
+    """sum(grad_c) = +-sum(g) (Operator chapter, "broadcast": a repeated
+    operand's gradient is the sum); a tied gradient is the sum of the two
+    untied path gradients (Autograd chapter, "chain rule")."""
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((6, 8)).astype(np.float32)
+    b = rng.standard_normal((8,)).astype(np.float32)
+    c = rng.standard_normal((1, 8)).astype(np.float32)
+    g = rng.standard_normal((6, 8)).astype(np.float32)
+    exact = math.fsum(g.astype(np.float64).ravel())
+    for op2, sgn in (("add", 1.0), ("sub", -1.0)):
+        _, _, gc = orc.bwd2("mul", op2, g, a, b, c)
+        assert abs(math.fsum(gc.f64.ravel()) - sgn * exact) <= 1e-12 * np.abs(g).sum()
+    ga, gb, gc = orc.bwd2("mul", "add", g, a, b, a)
+    gt, gbt, none = orc.bwd2("mul", "add", g, a, b, a, tie="a")
+    assert none is None
+    assert np.allclose(gt.f64, ga.f64 + gc.f64, rtol=0, atol=1e-12)
+    assert np.array_equal(gbt.f64, gb.f64)
