@@ -340,6 +340,22 @@ zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
   return hip_status(launch_reduce(p, in, out, workspace, (hipStream_t)stream));
 }
 
+zk_status zk_materialize(const float *in, const zk_desc *din, int32_t rank_out,
+                         const int64_t *sizes_out, float *out, void *stream) {
+  zk_status s;
+  if ((s = check_desc(din))) return s;
+  if (rank_out < 0 || rank_out > kMaxDims) return ZK_ERR_RANK;
+  if (rank_out > 0 && !sizes_out) return ZK_ERR_NULL;
+  for (int k = 0; k < rank_out; ++k)
+    if (sizes_out[k] < 0) return ZK_ERR_BAD_SIZE;
+  CopyPlan p;
+  if ((s = plan_copy(*din, rank_out, sizes_out, (uintptr_t)in, (uintptr_t)out, &p))) return s;
+  if (p.empty) return ZK_OK;
+  if (!in || !out) return ZK_ERR_NULL;
+  if (ov(ext_dense(out, p.c.numel), ext_of(in, *din))) return ZK_ERR_ALIAS;
+  return hip_status(launch_copy(p, in, out, (hipStream_t)stream));
+}
+
 zk_status zk_binary2_fwd(zk_op op1, zk_op op2, const float *a, const zk_desc *da,
                          const float *b, const zk_desc *db, const float *c,
                          const zk_desc *dc, float *out, void *stream) {

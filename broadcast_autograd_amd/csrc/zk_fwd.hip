@@ -516,6 +516,136 @@ __global__ __launch_bounds__(kBlock) void k_fwd2_generic(const float *a, const f
   }
 }
 
+// ---------------------------------------------------------- materialise
+// out (dense, target shape) = in read through its strides, broadcast to the
+// target (Operator chapter, "view backward": the stride-aware copy that turns
+// a view into contiguous storage).  A copy: no arithmetic, bit-exact.
+template <typename I>
+__global__ __launch_bounds__(kBlock) void k_copy_row(In3 x, float *out, Space3 sp) {
+  const I n = (I)sp.numel;
+  for (int64_t j = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4; j < (int64_t)n;
+       j += (int64_t)gridDim.x * kBlock * 4) {
+    const I i = (I)j;
+    I c0 = 0, c1 = 0, c2 = i;
+    if (x.mode != IM_FLAT && sp.rank >= 2) {
+      I q;
+      if constexpr (sizeof(I) == 4) q = (I)fdiv(sp.fd[sp.rank - 1], (uint32_t)i);
+      else q = i / (I)sp.n[sp.rank - 1];
+      c2 = i - q * (I)sp.n[sp.rank - 1];
+      if (sp.rank == 3) {
+        I q2;
+        if constexpr (sizeof(I) == 4) q2 = (I)fdiv(sp.fd[1], (uint32_t)q);
+        else q2 = q / (I)sp.n[1];
+        c1 = q - q2 * (I)sp.n[1];
+        c0 = q2;
+      } else {
+        c1 = q;
+      }
+    }
+    st4_nt(out + i, load_in3<I>(x, i, c0, c1, c2));
+  }
+}
+
+// T[i, j] at i + j*ld (a transposed view) -> out[R, C] row-major, through a
+// 64x64 LDS tile (the layout of k_fwd_tile without the second operand).
+__global__ __launch_bounds__(kBlock) void k_copy_tile(const float *tr, float *out, TileArgs ta) {
+  __shared__ float tile[64][65];
+  const int t = threadIdx.x;
+  for (int64_t bt = blockIdx.x; bt < ta.ntiles; bt += gridDim.x) {
+    const int64_t tiles_r = ta.ntiles / ta.tiles_c;
+    const int64_t tr_j = bt % ta.tiles_c;
+    const int64_t tr_i = (bt / ta.tiles_c + tr_j) % tiles_r;  // diagonal order
+    const int64_t i0 = tr_i * 64, j0 = tr_j * 64;
+    if (ta.tv) {
+      const int i4 = (t & 15) * 4, jq = t >> 4;
+      const int64_t gi = i0 + i4;
+      float4 v[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int64_t gj = j0 + jq + 16 * p;
+        v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gj < ta.C) {
+          const float *src = tr + gi + gj * ta.ld;
+          if (gi + 3 < ta.R) {
+            v[p] = ld4_nt(src);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (gi + k < ta.R) el(v[p], k) = src[k];
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tile[jq + 16 * p][i4 + k] = el(v[p], k);
+    } else {
+      const int i = t & 63, jq = t >> 6;
+      const int64_t gi = i0 + i;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int j = jq + 4 * p;
+        const int64_t gj = j0 + j;
+        tile[j][i] = (gi < ta.R && gj < ta.C) ? tr[gi + gj * ta.ld] : 0.f;
+      }
+    }
+    __syncthreads();
+    const int m = t & 15, q = t >> 4;
+    const int64_t gj = j0 + 4 * m;
+    if (gj < ta.C) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int i = q + 16 * p;
+        const int64_t gi = i0 + i;
+        if (gi < ta.R) {
+          float4 r;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) el(r, k) = tile[4 * m + k][i];
+          st4_nt(out + gi * ta.C + gj, r);
+        }
+      }
+    }
+    __syncthreads();  // the tile is refilled by the next trip
+  }
+}
+
+template <typename I>
+__global__ __launch_bounds__(kBlock) void k_copy_generic(const float *in, float *out, Space sp,
+                                                         int vec_out) {
+  const I n = (I)sp.numel;
+  for (int64_t j0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4; j0 < (int64_t)n;
+       j0 += (int64_t)gridDim.x * kBlock * 4) {
+    const I i0 = (I)j0;
+    float r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const I i = i0 + k;
+      if (i < n) {
+        I rest = i, off = 0;
+#pragma unroll
+        for (int d = kMaxDims - 1; d >= 1; --d) {
+          if (d < sp.rank) {
+            I q;
+            if constexpr (sizeof(I) == 4) q = (I)fdiv(sp.fd[d], (uint32_t)rest);
+            else q = rest / (I)sp.n[d];
+            off += (rest - q * (I)sp.n[d]) * (I)sp.s[1][d];
+            rest = q;
+          }
+        }
+        off += rest * (I)sp.s[1][0];
+        r[k] = in[off];
+      }
+    }
+    if (vec_out && i0 + 4 <= n) {
+      st4(out + i0, make_float4(r[0], r[1], r[2], r[3]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < n) out[i0 + k] = r[k];
+    }
+  }
+}
+
 // -------------------------------------------------------------- launcher
 static inline unsigned grid_of(int64_t n, int64_t per_block) {
   const int64_t g = (n + per_block - 1) / per_block;
@@ -691,6 +821,51 @@ hipError_t launch_fwd2(const Fwd2Plan &p, zk_op op1, zk_op op2, const float *a,
                 a, b, c, out, sp, p.vec == 4 ? 1 : 0);
     return hipGetLastError();
   });
+}
+
+hipError_t launch_copy(const CopyPlan &p, const float *in, float *out, hipStream_t st) {
+  if (p.empty) return hipSuccess;
+  const Canon &cn = p.c;
+  ProfScope prof(p.kernel);
+  if (p.kernel == K_COPY_TILE) {
+    TileArgs ta{};
+    ta.R = cn.n[0];
+    ta.C = cn.n[1];
+    ta.ld = cn.s[1][1];
+    ta.tiles_c = (ta.C + 63) / 64;
+    ta.ntiles = ((ta.R + 63) / 64) * ta.tiles_c;
+    ta.tv = ta.ld % 4 == 0 && ((uintptr_t)in & 15u) == 0;
+    const unsigned grid = (unsigned)(ta.ntiles < kMaxBlocks ? ta.ntiles : kMaxBlocks);
+    ZK_LAUNCH(prof, k_copy_tile, dim3(grid), dim3(kBlock), 0, st, in, out, ta);
+    return hipGetLastError();
+  }
+  const unsigned grid = grid_of(cn.numel, kBlock * 4);
+  if (p.kernel == K_COPY_ROW) {
+    Space3 sp{};
+    sp.rank = cn.rank;
+    sp.numel = cn.numel;
+    for (int k = 0; k < 3; ++k) {
+      sp.n[k] = k < cn.rank ? cn.n[k] : 1;
+      sp.fd[k] = make_fastdiv(sp.n[k] < ((int64_t)1 << 31) ? (uint32_t)sp.n[k] : 1u);
+    }
+    In3 x{};
+    x.p = in;
+    x.mode = p.mode;
+    for (int k = 0; k < cn.rank; ++k) x.s[3 - cn.rank + k] = cn.s[1][k];
+    if (p.idx64)
+      ZK_LAUNCH(prof, (k_copy_row<int64_t>), dim3(grid), dim3(kBlock), 0, st, x, out, sp);
+    else
+      ZK_LAUNCH(prof, (k_copy_row<int32_t>), dim3(grid), dim3(kBlock), 0, st, x, out, sp);
+    return hipGetLastError();
+  }
+  Space sp = make_space(cn);
+  if (p.idx64)
+    ZK_LAUNCH(prof, (k_copy_generic<int64_t>), dim3(grid), dim3(kBlock), 0, st, in, out, sp,
+              p.vec == 4 ? 1 : 0);
+  else
+    ZK_LAUNCH(prof, (k_copy_generic<int32_t>), dim3(grid), dim3(kBlock), 0, st, in, out, sp,
+              p.vec == 4 ? 1 : 0);
+  return hipGetLastError();
 }
 
 }  // namespace zk

@@ -53,6 +53,8 @@ struct ProfScope {
 hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
                       const float *b, float *out, hipStream_t st);
 
+hipError_t launch_copy(const CopyPlan &p, const float *in, float *out, hipStream_t st);
+
 hipError_t launch_fwd2(const Fwd2Plan &p, zk_op op1, zk_op op2, const float *a,
                        const float *b, const float *c, float *out, hipStream_t st);
 

@@ -11,7 +11,8 @@ const char *kernel_name(int32_t k) {
       "fwd_flat",       "fwd_row",       "fwd_tile",   "fwd_generic",
       "bwd_ew_flat",    "bwd_ew_generic", "red_col",   "red_row",
       "red_tile",       "red_generic",   "red_final",  "fwd2_row",
-      "fwd2_generic",   "bwd_signed"};
+      "fwd2_generic",   "bwd_signed",    "copy_row",   "copy_tile",
+      "copy_generic"};
   if (k < 0 || k >= K_COUNT) return "none";
   return names[k];
 }
@@ -323,6 +324,57 @@ zk_status plan_fwd2(const zk_desc &da, const zk_desc &db, const zk_desc &dc,
     return ZK_OK;
   }
   p->kernel = K_FWD2_GENERIC;
+  p->vec = al16(pout) ? 4 : 1;
+  return ZK_OK;
+}
+
+// --------------------------------------------------------- materialise
+zk_status plan_copy(const zk_desc &din, int rout, const int64_t *nout, uintptr_t pin,
+                    uintptr_t pout, CopyPlan *p) {
+  int r;
+  int64_t n[kMaxDims];
+  zk_status s = broadcast_shape(din.rank, din.sizes, rout, nout, &r, n);
+  if (s == ZK_ERR_BROADCAST) return ZK_ERR_SHAPE;
+  if (s) return s;
+  // the result of the broadcast must be the target itself
+  if (r != rout) return ZK_ERR_SHAPE;
+  for (int k = 0; k < r; ++k)
+    if (n[k] != nout[k]) return ZK_ERR_SHAPE;
+  int64_t st[kMaxOps][kMaxDims];
+  {
+    int64_t d = 1;
+    for (int k = r - 1; k >= 0; --k) { st[0][k] = d; d *= n[k]; }
+  }
+  align_strides(din, r, st[1]);
+  p->c = canonicalise(r, n, 2, st);
+  const Canon &c = p->c;
+  if (c.numel == 0) {
+    p->empty = true;
+    return ZK_OK;
+  }
+  p->idx64 = needs_idx64(c);
+  const int64_t inner = c.n[c.rank - 1];
+  if (is_transposed2(c, 1) && c.n[1] % 4 == 0 && al16(pout)) {
+    p->kernel = K_COPY_TILE;
+    p->vec = 4;
+    return ZK_OK;
+  }
+  if (c.rank <= 3 && inner % 4 == 0 && al16(pout)) {
+    p->kernel = K_COPY_ROW;
+    p->vec = 4;
+    if (is_flat(c, 1) && al16(pin)) {
+      p->mode = IM_FLAT;
+    } else if (c.s[1][c.rank - 1] == 0) {
+      p->mode = IM_BCAST;
+    } else {
+      bool contig = c.s[1][c.rank - 1] == 1 && al16(pin);
+      for (int k = 0; k + 1 < c.rank; ++k)
+        if (c.s[1][k] % 4 != 0) contig = false;
+      p->mode = contig ? IM_CONTIG : IM_GATHER;
+    }
+    return ZK_OK;
+  }
+  p->kernel = K_COPY_GENERIC;
   p->vec = al16(pout) ? 4 : 1;
   return ZK_OK;
 }

@@ -37,7 +37,10 @@ enum KernelClass : int32_t {
   K_FWD2_ROW = 11,    // fused (a op1 b) op2 c, rank <= 3, 128-bit output
   K_FWD2_GENERIC = 12,  // fused (a op1 b) op2 c, anything (rank <= 8)
   K_BWD_SIGNED = 13,  // +-g (+ acc) element-wise: the gradient of op2's c
-  K_COUNT = 14
+  K_COPY_ROW = 14,    // materialise a view, rank <= 3, 128-bit output
+  K_COPY_TILE = 15,   // materialise a transposed rank-2 view through LDS
+  K_COPY_GENERIC = 16,  // materialise anything (rank <= 8)
+  K_COUNT = 17
 };
 
 const char *kernel_name(int32_t k);
@@ -119,6 +122,19 @@ struct Fwd2Plan {
   int vec = 1;
   int32_t mode[3] = {IM_GATHER, IM_GATHER, IM_GATHER};  // a, b, c (ROW)
 };
+// Materialise a view into dense row-major storage of a target shape the
+// view broadcasts to.  Canon ops: 0 out, 1 in.
+struct CopyPlan {
+  Canon c;
+  int32_t kernel = K_NONE;  // K_COPY_ROW, K_COPY_TILE or K_COPY_GENERIC
+  bool empty = false;
+  bool idx64 = false;
+  int vec = 1;
+  int32_t mode = IM_GATHER;  // ROW: input access mode
+};
+zk_status plan_copy(const zk_desc &din, int rout, const int64_t *nout, uintptr_t pin,
+                    uintptr_t pout, CopyPlan *p);
+
 // Broadcast shape of three shapes (a with b, then with c).
 zk_status broadcast_shape3(const zk_desc &da, const zk_desc &db, const zk_desc &dc,
                            int *r, int64_t *n);

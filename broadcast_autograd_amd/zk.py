@@ -24,7 +24,7 @@ ERR = {v: k for k, v in STATUS.items()}
 
 # exported symbols declared in include/zk.h
 SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
-           "zk_reduce_to_shape", "zk_binary2_fwd", "zk_binary2_bwd",
+           "zk_reduce_to_shape", "zk_materialize", "zk_binary2_fwd", "zk_binary2_bwd",
            "zk_status_string", "zk_plan_describe", "zk_kernel_name",
            "zk_profile_start", "zk_profile_stop", "zk_profile_read")
 
@@ -75,6 +75,7 @@ def lib():
         L.zk_binary_fwd.argtypes = [I32, I32, P, P, P, P, P, P]
         L.zk_binary_bwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, P, P]
         L.zk_reduce_to_shape.argtypes = [P, P, I32, P, P, P, P, P]
+        L.zk_materialize.argtypes = [P, P, I32, P, P, P]
         L.zk_binary2_fwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P]
         L.zk_binary2_bwd.argtypes = [I32, I32] + [P] * 16
         L.zk_status_string.argtypes = [I32]
@@ -213,6 +214,19 @@ def binary_bwd(op, grad, a, b, need_a=True, need_b=True, grad_a=None,
     _check(L.zk_binary_bwd(*args, _ptr(workspace), ctypes.byref(nbytes),
                            _stream(stream)), "zk_binary_bwd")
     return grad_a, grad_b
+
+
+def materialize(x, shape=None, out=None, stream=None):
+    """Dense row-major copy of the view ``x``, broadcast to ``shape`` (default:
+    x's own shape)."""
+    import torch
+    shape = tuple(x.shape) if shape is None else tuple(int(s) for s in shape)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    d = desc_of(x)
+    _check(lib().zk_materialize(_ptr(x), ctypes.byref(d), len(shape), _i64(shape), _ptr(out),
+                                _stream(stream)), "zk_materialize")
+    return out
 
 
 def broadcast_shape3(sa, sb, sc):

@@ -168,6 +168,25 @@ zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
                              size_t *workspace_bytes, void *stream);
 
 /*
+ * Stride-aware materialisation (Operator chapter, "view backward": the
+ * broadcast-to copy that turns a view, e.g. a transposed gradient, into
+ * contiguous storage; a View of a non-contiguous input first makes such a
+ * row-major copy):
+ *   out[i] = in[off(i)] for every i of the target shape (rank_out,
+ *   sizes_out), with in broadcast to it (a size-1 or missing input dim
+ *   repeats).  With the target equal to in's shape this is a contiguous copy.
+ *   in, din : any non-negative strides
+ *   out     : dense row-major, target shape, caller-allocated
+ * No arithmetic: the copy is bit-exact.  The target must be the broadcast of
+ * in's shape with itself, else ZK_ERR_SHAPE.  An empty target launches
+ * nothing.  Any overlap of out with in is ZK_ERR_ALIAS.
+ * Errors: ZK_ERR_NULL, ZK_ERR_RANK, ZK_ERR_BAD_SIZE, ZK_ERR_BAD_STRIDE,
+ *         ZK_ERR_SHAPE, ZK_ERR_ALIAS, ZK_ERR_HIP.
+ */
+zk_status zk_materialize(const float *in, const zk_desc *din, int32_t rank_out,
+                         const int64_t *sizes_out, float *out, void *stream);
+
+/*
  * Fused two-operator expression (Operator chapter, "fusion": several small
  * element-wise operators merged into one execution unit, with the usual
  * forward/backward interface and without changing the math):

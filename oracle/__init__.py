@@ -79,6 +79,7 @@ def lib():
                               P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.or_bwd2_at.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  P, P, P, P, P, P, P, P, I64, P, P, P, P]
+        L.or_materialize.argtypes = [P, P, ctypes.c_int, P, P]
         L.or_gelu32.argtypes = [ctypes.c_float]
         L.or_gelu32.restype = ctypes.c_float
         L.or_phi_cdf.argtypes = [ctypes.c_double]
@@ -265,6 +266,17 @@ def reduce_to_shape(x, shape):
     _check(lib().or_reduce(_ptr(v), ctypes.byref(d), len(shape), _i64(shape),
                            p(f32), p(f64), p(ab)))
     return Grad(f32, f64, ab)
+
+
+def materialize(x, shape=None):
+    """Dense row-major copy of the view ``x`` broadcast to ``shape``."""
+    v = _as_view(x)
+    shape = tuple(v.sizes) if shape is None else tuple(int(s) for s in shape)
+    out = np.empty(shape, dtype=np.float32)
+    d = _desc(v)
+    _check(lib().or_materialize(_ptr(v), ctypes.byref(d), len(shape), _i64(shape),
+                                out.ctypes.data if out.size else None))
+    return out
 
 
 def broadcast_shape3(sa, sb, sc):

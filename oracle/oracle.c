@@ -559,3 +559,29 @@ int or_bwd2_at(int op1, int op2, int which, int tie, const float *g, const float
   }
   return OR_OK;
 }
+
+/* ------------------------------------------------------------ materialise */
+
+/* out (dense, shape nout) = in read through its strides, broadcast to nout
+ * (Operator chapter, "view backward": a stride-aware copy into contiguous
+ * storage).  nout must be the broadcast of in's shape with itself. */
+int or_materialize(const float *in, const or_desc *din, int rout, const int64_t *nout,
+                   float *out) {
+  int s;
+  if ((s = check_desc(din))) return s;
+  if (rout < 0 || rout > OR_MAX_DIMS) return OR_ERR_RANK;
+  for (int k = 0; k < rout; ++k) if (nout[k] < 0) return OR_ERR_SIZE;
+  int r;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = or_broadcast_shape(din->rank, din->sizes, rout, nout, &r, n))) return s;
+  if (r != rout) return OR_ERR_ARG;
+  for (int k = 0; k < r; ++k) if (n[k] != nout[k]) return OR_ERR_ARG;
+  int64_t total = numel(r, n);
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t f = 0; f < total; ++f) {
+    int64_t idx[OR_MAX_DIMS];
+    unflatten(f, r, n, idx);
+    out[f] = in[operand_offset(din, r, idx)];
+  }
+  return OR_OK;
+}

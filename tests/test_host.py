@@ -183,6 +183,21 @@ def test_fused_validation_errors(L):
     assert _bwd2(2, 0, d, r, d, gc=gc, acc=(None, None, FO), ga=FO, ws=ws)[0] == "ZK_ERR_ALIAS"
 
 
+def test_materialize_validation_errors(L):
+    def call(din, shape, inp=FA, out=FO):
+        return zk.STATUS[L.zk_materialize(inp, ctypes.byref(din), len(shape),
+                                          zk._i64(shape), out, None)]
+    d = zk.make_desc((4, 8))
+    assert call(d, (3, 8)) == "ZK_ERR_SHAPE"          # 4 does not broadcast to 3
+    assert call(d, (8,)) == "ZK_ERR_SHAPE"            # the target must be the result
+    assert call(d, (2, 4, 8), inp=None) == "ZK_ERR_NULL"
+    assert call(d, (4, 8), out=ctypes.c_void_p(FA.value + 16)) == "ZK_ERR_ALIAS"
+    bad = zk.make_desc((4, 8), (8, -1))
+    assert call(bad, (4, 8)) == "ZK_ERR_BAD_STRIDE"
+    d0 = zk.make_desc((0, 8))
+    assert call(d0, (0, 8), inp=None, out=None) == "ZK_OK"  # empty: nothing launched
+
+
 def test_reduce_validation_errors(L):
     d = zk.make_desc((4, 6))
 

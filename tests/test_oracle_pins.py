@@ -505,3 +505,40 @@ def test_fused_mass_and_tie_identities(orc):
     assert none is None
     assert np.allclose(gt.f64, ga.f64 + gc.f64, rtol=0, atol=1e-12)
     assert np.array_equal(gbt.f64, gb.f64)
+
+
+# ------------------------------------------------ materialise a view (f2) --
+def test_materialize_worked_examples(orc):
+    """Tensor chapter, "zero-copy view": the transposed view of
+    [[1,2,3],[4,5,6]] (sizes [3,2], strides [1,3]) made contiguous is the
+    transpose; Operator chapter, "broadcast": [10,20,30] broadcast to [2,3]."""
+    storage = np.arange(1, 7, dtype=np.float32)
+    tv = orc.View(storage, (3, 2), (1, 3))
+    got = orc.materialize(tv)
+    assert got.tolist() == [[1, 4], [2, 5], [3, 6]]
+    assert orc.materialize(tv)[0, 1] == 4  # element (0,1) of the view is storage[3]
+    b = np.array([10, 20, 30], np.float32)
+    assert orc.materialize(b, (2, 3)).tolist() == [[10, 20, 30], [10, 20, 30]]
+
+
+def test_materialize_against_numpy(orc):
+    """Random strided views (transposes, stride-0 repeats, offsets) against
+    numpy's as_strided + broadcast_to + ascontiguousarray, bit for bit."""
+    rng = np.random.default_rng(17)
+    for trial in range(60):
+        r = int(rng.integers(0, 5))
+        sizes = tuple(int(x) for x in rng.integers(1, 5, r))
+        strides = tuple(int(x) for x in rng.integers(0, 7, r))
+        off = int(rng.integers(0, 4))
+        span = off + sum((n - 1) * s for n, s in zip(sizes, strides)) + 1
+        st = rng.standard_normal(span).astype(np.float32)
+        v = orc.View(st, sizes, strides, off)
+        lead = tuple(int(x) for x in rng.integers(1, 3, int(rng.integers(0, 2))))
+        shape = lead + tuple(n if rng.random() < 0.7 or n != 1 else int(rng.integers(1, 4))
+                             for n in sizes)
+        ref = np.lib.stride_tricks.as_strided(st[off:], sizes, tuple(4 * s for s in strides))
+        want = np.array(np.broadcast_to(ref, shape), order="C")  # keeps 0-d arrays 0-d
+        got = orc.materialize(v, shape)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (sizes, strides, shape)
+    with pytest.raises(orc.OracleError):
+        orc.materialize(np.ones((2, 3), np.float32), (3, 3))
