@@ -19,7 +19,9 @@ using namespace zk;
 namespace {
 
 bool valid_op(zk_op op) { return op >= ZK_ADD && op <= ZK_DIV; }
-bool valid_epi(zk_epi e) { return e == ZK_EPI_NONE || e == ZK_EPI_GELU; }
+bool valid_epi(zk_epi e) {
+  return e == ZK_EPI_NONE || e == ZK_EPI_GELU || e == ZK_EPI_RELU;
+}
 
 int64_t numel(const zk_desc &d) {
   int64_t m = 1;
@@ -338,6 +340,81 @@ zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
   if (need) ews = Ext{(uintptr_t)workspace, (uintptr_t)workspace + need};
   if (ov(eo, ei) || ov(eo, ews) || ov(ews, ei)) return ZK_ERR_ALIAS;
   return hip_status(launch_reduce(p, in, out, workspace, (hipStream_t)stream));
+}
+
+zk_status zk_scalar_fwd(zk_op op, zk_epi epi, const float *t, const zk_desc *dt,
+                        float sv, int32_t scalar_first, float *out, void *stream) {
+  if (!valid_op(op) || !valid_epi(epi)) return ZK_ERR_UNSUPPORTED;
+  zk_status s;
+  if ((s = check_desc(dt))) return s;
+  const zk_desc d0{};  // the scalar as a rank-0 operand
+  const bool sf = scalar_first != 0;
+  const zk_desc &da = sf ? d0 : *dt, &db = sf ? *dt : d0;
+  const float *pa = sf ? nullptr : t, *pb = sf ? t : nullptr;
+  FwdPlan p;
+  if ((s = plan_fwd(op, epi, da, db, (uintptr_t)pa, (uintptr_t)pb, (uintptr_t)out, &p)))
+    return s;
+  if (p.empty) return ZK_OK;
+  if (!t || !out) return ZK_ERR_NULL;
+  if (p.kernel == K_FWD_ROW) {
+    p.small_mode = SM_ARG;  // the tensor is the dense operand
+  } else if (p.kernel != K_FWD_GENERIC) {
+    p.kernel = K_FWD_GENERIC;
+    p.vec = ((uintptr_t)out & 15u) == 0 ? 4 : 1;
+  }
+  const int64_t n = p.c.numel;
+  if (ov(ext_dense(out, n), ext_of(t, *dt)) && !(out == t && dense_full(*dt, n)))
+    return ZK_ERR_ALIAS;
+  const ScalarArg sa{sf ? 0 : 1, sv};
+  return hip_status(launch_fwd(p, op, epi, pa, pb, out, (hipStream_t)stream, &sa));
+}
+
+zk_status zk_scalar_bwd(zk_op op, zk_epi epi, const float *grad, const float *t,
+                        const zk_desc *dt, float sv, int32_t scalar_first,
+                        float *grad_t, const float *acc_t, void *stream) {
+  if (!valid_op(op) || !valid_epi(epi)) return ZK_ERR_UNSUPPORTED;
+  zk_status s;
+  if ((s = check_desc(dt))) return s;
+  const zk_desc d0{};
+  const bool sf = scalar_first != 0;
+  const zk_desc &da = sf ? d0 : *dt, &db = sf ? *dt : d0;
+  const float *pa = sf ? nullptr : t, *pb = sf ? t : nullptr;
+  float *ga = sf ? nullptr : grad_t, *gb = sf ? grad_t : nullptr;
+  const float *xa = sf ? nullptr : acc_t, *xb = sf ? acc_t : nullptr;
+  BwdPlan p;
+  if ((s = plan_bwd(op, epi, da, db, !sf && grad_t, sf && grad_t, (uintptr_t)grad,
+                    (uintptr_t)pa, (uintptr_t)pb, (uintptr_t)ga, (uintptr_t)gb,
+                    (uintptr_t)xa, (uintptr_t)xb, &p)))
+    return s;
+  const int64_t n = p.c.numel;
+  if (!grad_t || n == 0) return ZK_OK;
+  if (!grad || !t) return ZK_ERR_NULL;
+  // The tensor has the full shape: one element-wise pass.  The scalar needs
+  // no layout, so the flat kernel applies whenever the tensor is dense.
+  if (canon_is_flat(p.c, sf ? 2 : 1)) {
+    p.ew_kernel = K_BWD_EW_FLAT;
+    auto al = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
+    p.vec = al(grad) && al(t) && al(grad_t) && al(acc_t) ? 4 : 1;
+  }
+  Ext eg = ext_dense(grad, n), et = ext_of(t, *dt), eo = ext_dense(grad_t, n);
+  Ext ex = ext_dense(acc_t, n);
+  if (ov(eo, eg) || ov(eo, et)) return ZK_ERR_ALIAS;
+  if (ov(eo, ex) && acc_t != grad_t) return ZK_ERR_ALIAS;
+  const ScalarArg sa{sf ? 0 : 1, sv};
+  return hip_status(launch_bwd(p, op, epi, grad, pa, pb, ga, xa, gb, xb, nullptr,
+                               (hipStream_t)stream, nullptr, nullptr, 1.f, &sa));
+}
+
+zk_status zk_unary_fwd(zk_epi f, const float *x, const zk_desc *dx, float *out,
+                       void *stream) {
+  if (f != ZK_EPI_GELU && f != ZK_EPI_RELU) return ZK_ERR_UNSUPPORTED;
+  return zk_scalar_fwd(ZK_SUB, f, x, dx, 0.0f, 0, out, stream);  // x - 0 == x
+}
+
+zk_status zk_unary_bwd(zk_epi f, const float *grad, const float *x, const zk_desc *dx,
+                       float *grad_x, const float *acc_x, void *stream) {
+  if (f != ZK_EPI_GELU && f != ZK_EPI_RELU) return ZK_ERR_UNSUPPORTED;
+  return zk_scalar_bwd(ZK_SUB, f, grad, x, dx, 0.0f, 0, grad_x, acc_x, stream);
 }
 
 zk_status zk_materialize(const float *in, const zk_desc *din, int32_t rank_out,

@@ -60,15 +60,19 @@ __device__ __forceinline__ void gc_store1(const GcOut &o, int64_t i, float g) {
 
 template <typename Fn>
 static hipError_t op_epi(zk_op op, zk_epi epi, Fn &&fn) {
-  switch ((int)op * 2 + (int)epi) {
+  switch ((int)op * 3 + (int)epi) {
     case 0: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_NONE>{});
     case 1: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_GELU>{});
-    case 2: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_NONE>{});
-    case 3: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_GELU>{});
-    case 4: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_NONE>{});
-    case 5: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_GELU>{});
-    case 6: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_NONE>{});
-    case 7: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_GELU>{});
+    case 2: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_RELU>{});
+    case 3: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_NONE>{});
+    case 4: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_GELU>{});
+    case 5: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_RELU>{});
+    case 6: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_NONE>{});
+    case 7: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_GELU>{});
+    case 8: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_RELU>{});
+    case 9: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_NONE>{});
+    case 10: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_GELU>{});
+    case 11: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_RELU>{});
   }
   return hipErrorInvalidValue;
 }
@@ -95,16 +99,19 @@ constexpr bool any_y() { return reads_y<OP, EPI, 0>() || reads_y<OP, EPI, 1>(); 
 // ---------------------------------------------------- element-wise, flat
 // Both gradients have the full shape: no reduction.  acc modes: 0 none,
 // 1 the upstream grad itself, 2 a separate buffer (or the gradient, in place).
+// a_arg / b_arg: that operand is a host scalar passed by value (av / bv).
 struct EwArgs {
   int64_t n;
   int32_t write_a, write_b, acc_a, acc_b, read_a, read_b;
+  int32_t a_arg, b_arg;
+  float av, bv;
 };
 
 template <int OP, int EPI>
 __device__ __forceinline__ void ew_one(float gv, float x, float y, float aa,
                                        float ab, const EwArgs &ea, float &oa,
                                        float &ob) {
-  if constexpr (EPI == ZK_EPI_GELU) {
+  if constexpr (EPI != ZK_EPI_NONE) {
     float ta, tb;
     terms_ab<OP, EPI>(gv, x, y, ta, tb);
     if (ea.write_a) oa = ea.acc_a == 1 ? gv + ta : (ea.acc_a == 2 ? aa + ta : ta);
@@ -137,8 +144,10 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
         int64_t i = base + (int64_t)u * kBlk * 4;
         if (i + 4 <= ea.n) {
           vg[u] = ld4_nt(g + i);
-          if (ea.read_a) va[u] = ld4_nt(a + i);
-          if (ea.read_b) vb[u] = ld4_nt(b + i);
+          if (ea.read_a)
+            va[u] = ea.a_arg ? make_float4(ea.av, ea.av, ea.av, ea.av) : ld4_nt(a + i);
+          if (ea.read_b)
+            vb[u] = ea.b_arg ? make_float4(ea.bv, ea.bv, ea.bv, ea.bv) : ld4_nt(b + i);
           if (ea.acc_a == 2) xa[u] = ld4_nt(acc_a + i);
           if (ea.acc_b == 2) xb[u] = ld4_nt(acc_b + i);
         }
@@ -160,7 +169,8 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
         } else if (i < ea.n) {
           for (int64_t j = i; j < ea.n; ++j) {
             float oa = 0.f, ob = 0.f;
-            ew_one<OP, EPI>(g[j], ea.read_a ? a[j] : 0.f, ea.read_b ? b[j] : 0.f,
+            ew_one<OP, EPI>(g[j], ea.read_a ? (ea.a_arg ? ea.av : a[j]) : 0.f,
+                            ea.read_b ? (ea.b_arg ? ea.bv : b[j]) : 0.f,
                             ea.acc_a == 2 ? acc_a[j] : 0.f, ea.acc_b == 2 ? acc_b[j] : 0.f,
                             ea, oa, ob);
             if (ea.write_a) ga[j] = oa;
@@ -175,7 +185,8 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_flat(
         int64_t j = t * tile + (int64_t)u * kBlk + threadIdx.x;
         if (j < ea.n) {
           float oa = 0.f, ob = 0.f;
-          ew_one<OP, EPI>(g[j], ea.read_a ? a[j] : 0.f, ea.read_b ? b[j] : 0.f,
+          ew_one<OP, EPI>(g[j], ea.read_a ? (ea.a_arg ? ea.av : a[j]) : 0.f,
+                          ea.read_b ? (ea.b_arg ? ea.bv : b[j]) : 0.f,
                           ea.acc_a == 2 ? acc_a[j] : 0.f, ea.acc_b == 2 ? acc_b[j] : 0.f,
                           ea, oa, ob);
           if (ea.write_a) ga[j] = oa;
@@ -225,7 +236,8 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_generic(
         I oa, ob;
         offs_ab<I>(sp, i, oa, ob);
         float o1 = 0.f, o2 = 0.f;
-        ew_one<OP, EPI>(g[i], ea.read_a ? a[oa] : 0.f, ea.read_b ? b[ob] : 0.f,
+        ew_one<OP, EPI>(g[i], ea.read_a ? (ea.a_arg ? ea.av : a[oa]) : 0.f,
+                        ea.read_b ? (ea.b_arg ? ea.bv : b[ob]) : 0.f,
                         ea.acc_a == 2 ? acc_a[i] : 0.f, ea.acc_b == 2 ? acc_b[i] : 0.f,
                         ea, o1, o2);
         if (ea.write_a) ga[i] = o1;
@@ -759,7 +771,7 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
                       const float *a, const float *b, float *grad_a,
                       const float *acc_a, float *grad_b, const float *acc_b,
                       void *ws, hipStream_t st, float *grad_c, const float *acc_c,
-                      float c_sign) {
+                      float c_sign, const ScalarArg *sa) {
   const Canon &c = p.c;
   hipError_t e = hipSuccess;
   // The c gradient of the fused backward rides along with the first stage-1
@@ -779,6 +791,11 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
     ea.acc_b = ea.write_b ? acc_mode(acc_b, g) : 0;
     ea.read_a = (ea.write_a && rule_reads_a(op, epi, 0)) || (ea.write_b && rule_reads_a(op, epi, 1));
     ea.read_b = (ea.write_a && rule_reads_b(op, epi, 0)) || (ea.write_b && rule_reads_b(op, epi, 1));
+    if (sa) {
+      ea.a_arg = sa->side == 0;
+      ea.b_arg = sa->side == 1;
+      ea.av = ea.bv = sa->value;
+    }
     e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
       constexpr int OP = decltype(OPc)::value;
       constexpr int EPI = decltype(EPIc)::value;

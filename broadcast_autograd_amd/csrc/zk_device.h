@@ -188,11 +188,17 @@ __device__ __forceinline__ float gelu_grad_f32(float g, float h) {
   return fmaf(g * h, pdf, g * Phi);
 }
 
+// ReLU(h): h for h > 0, NaN for NaN (propagated), +0 otherwise.
+__device__ __forceinline__ float relu32(float h) {
+  return h > 0.f ? h : (h != h ? h : 0.f);
+}
+
 // r = epi(x (op) y); tab: the GeLU table in LDS (unused without GeLU).
 template <int OP, int EPI>
 __device__ __forceinline__ float fwd32(float x, float y, const double *tab) {
   float h = op32<OP>(x, y);
   if constexpr (EPI == ZK_EPI_GELU) return gelu32(tab, h);
+  else if constexpr (EPI == ZK_EPI_RELU) return relu32(h);
   else return h;
 }
 
@@ -211,7 +217,7 @@ __device__ __forceinline__ void fwd4_fast(const float (&x)[4], const float (&y)[
   } else {
     redo = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = h[k];
+    for (int k = 0; k < 4; ++k) r[k] = EPI == ZK_EPI_RELU ? relu32(h[k]) : h[k];
   }
 }
 
@@ -243,6 +249,10 @@ __device__ __forceinline__ void gscale_w(const float (&g)[W], const float (&x)[W
         }
       }
     }
+  } else if constexpr (EPI == ZK_EPI_RELU) {
+    // ReLU'(h) = 1 for h > 0, else 0 (NaN included)
+#pragma unroll
+    for (int k = 0; k < W; ++k) gd[k] = op32<OP>(x[k], y[k]) > 0.f ? (double)g[k] : 0.0;
   } else {
 #pragma unroll
     for (int k = 0; k < W; ++k) gd[k] = (double)g[k];
@@ -280,7 +290,7 @@ __device__ __forceinline__ double term64(float g, float x, float y) {
 // Cheap single-precision forms where the rule is one product or quotient.
 template <int OP, int EPI, int WHICH>
 __device__ __forceinline__ float term32(float g, float x, float y) {
-  if constexpr (EPI == ZK_EPI_GELU) {
+  if constexpr (EPI != ZK_EPI_NONE) {
     return (float)term64<OP, EPI, WHICH>(g, x, y);
   } else if constexpr (OP == ZK_ADD) {
     return g;
@@ -300,7 +310,7 @@ __device__ __forceinline__ float term32(float g, float x, float y) {
 template <int OP, int EPI, int SMALL>
 __device__ __forceinline__ void terms2(float g, float x, float y, double &ts,
                                        float &tb) {
-  if constexpr (EPI == ZK_EPI_GELU) {
+  if constexpr (EPI != ZK_EPI_NONE) {
     const double gd = gscale<OP, EPI>(g, x, y);
     ts = rule64<OP, SMALL>(gd, x, y);
     tb = (float)rule64<OP, 1 - SMALL>(gd, x, y);
@@ -315,7 +325,7 @@ template <int OP, int EPI, int SMALL, int W>
 __device__ __forceinline__ void terms2_w(const float (&g)[W], const float (&x)[W],
                                          const float (&y)[W], double (&ts)[W],
                                          float (&tb)[W]) {
-  if constexpr (EPI == ZK_EPI_GELU) {
+  if constexpr (EPI != ZK_EPI_NONE) {
     double gd[W];
     gscale_w<OP, EPI, W>(g, x, y, gd);
 #pragma unroll
@@ -333,7 +343,7 @@ __device__ __forceinline__ void terms2_w(const float (&g)[W], const float (&x)[W
 template <int OP, int EPI>
 __device__ __forceinline__ void terms_ab(float g, float x, float y, float &ta,
                                          float &tb) {
-  if constexpr (EPI == ZK_EPI_GELU) {
+  if constexpr (EPI != ZK_EPI_NONE) {
     const double gd = gscale<OP, EPI>(g, x, y);
     ta = (float)rule64<OP, 0>(gd, x, y);
     tb = (float)rule64<OP, 1>(gd, x, y);
@@ -346,11 +356,11 @@ __device__ __forceinline__ void terms_ab(float g, float x, float y, float &ta,
 // Whether the rule for grad WHICH reads a (x) / b (y).
 template <int OP, int EPI, int WHICH>
 __host__ __device__ constexpr bool reads_x() {
-  return EPI == ZK_EPI_GELU || ((OP == ZK_MUL || OP == ZK_DIV) && WHICH == 1);
+  return EPI != ZK_EPI_NONE || ((OP == ZK_MUL || OP == ZK_DIV) && WHICH == 1);
 }
 template <int OP, int EPI, int WHICH>
 __host__ __device__ constexpr bool reads_y() {
-  return EPI == ZK_EPI_GELU || (OP == ZK_MUL && WHICH == 0) || OP == ZK_DIV;
+  return EPI != ZK_EPI_NONE || (OP == ZK_MUL && WHICH == 0) || OP == ZK_DIV;
 }
 
 // ------------------------------------------------------------ index math

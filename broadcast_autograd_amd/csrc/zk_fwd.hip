@@ -38,15 +38,19 @@ using IC = std::integral_constant<int, V>;
 // Calls fn(IC<op>, IC<epi>) for the runtime (op, epi).
 template <typename Fn>
 static hipError_t with_op_epi(zk_op op, zk_epi epi, Fn &&fn) {
-  switch ((int)op * 2 + (int)epi) {
+  switch ((int)op * 3 + (int)epi) {
     case 0: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_NONE>{});
     case 1: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_GELU>{});
-    case 2: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_NONE>{});
-    case 3: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_GELU>{});
-    case 4: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_NONE>{});
-    case 5: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_GELU>{});
-    case 6: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_NONE>{});
-    case 7: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_GELU>{});
+    case 2: return fn(IC<ZK_ADD>{}, IC<ZK_EPI_RELU>{});
+    case 3: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_NONE>{});
+    case 4: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_GELU>{});
+    case 5: return fn(IC<ZK_SUB>{}, IC<ZK_EPI_RELU>{});
+    case 6: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_NONE>{});
+    case 7: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_GELU>{});
+    case 8: return fn(IC<ZK_MUL>{}, IC<ZK_EPI_RELU>{});
+    case 9: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_NONE>{});
+    case 10: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_GELU>{});
+    case 11: return fn(IC<ZK_DIV>{}, IC<ZK_EPI_RELU>{});
   }
   return hipErrorInvalidValue;
 }
@@ -131,6 +135,7 @@ struct RowArgs {
   int64_t ss[3];
   FastDiv fd[3];
   int64_t numel;
+  float sval;  // SM_ARG: the scalar operand
 };
 
 template <typename I>
@@ -171,13 +176,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         const I i = t * tile + (I)threadIdx.x * 4 + (I)u * kBlock * 4;
         if (i < n) {
           vb[u] = ld4_nt(big + i);
-          const I off = row_offset<I>(ra, i);
-          if constexpr (SMODE == SM_BCAST) {
-            const float s = small[off];
+          if constexpr (SMODE == SM_ARG) {
+            vs[u] = make_float4(ra.sval, ra.sval, ra.sval, ra.sval);
+          } else if constexpr (SMODE == SM_BCAST) {
+            const float s = small[row_offset<I>(ra, i)];
             vs[u] = make_float4(s, s, s, s);
           } else if constexpr (SMODE == SM_CONTIG) {
-            vs[u] = ld4(small + off);
+            vs[u] = ld4(small + row_offset<I>(ra, i));
           } else {
+            const I off = row_offset<I>(ra, i);
 #pragma unroll
             for (int k = 0; k < 4; ++k) el(vs[u], k) = small[off + (I)k * sin];
           }
@@ -214,10 +221,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
           const int bit = __builtin_ctz(redo_bits);
           redo_bits &= redo_bits - 1;
           const I i = base + (I)(bit >> 2) * kBlock * 4;
-          const I off = row_offset<I>(ra, i);
+          const I off = SMODE == SM_ARG ? (I)0 : row_offset<I>(ra, i);
           const int k = bit & 3;
           float vsm;
-          if constexpr (SMODE == SM_BCAST) vsm = small[off];
+          if constexpr (SMODE == SM_ARG) vsm = ra.sval;
+          else if constexpr (SMODE == SM_BCAST) vsm = small[off];
           else if constexpr (SMODE == SM_CONTIG) vsm = small[off + k];
           else vsm = small[off + (I)k * sin];
           const float vbig = big[i + k];
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
          i64 += (int64_t)gridDim.x * kBlock) {
       const I i = (I)i64;
       const float vbig = big[i];
-      const float vsm = small[row_offset<I>(ra, i)];
+      const float vsm = SMODE == SM_ARG ? ra.sval : small[row_offset<I>(ra, i)];
       out[i] = SWAP ? fwd32<OP, EPI>(vsm, vbig, s_gelu) : fwd32<OP, EPI>(vbig, vsm, s_gelu);
     }
   }
@@ -365,12 +373,13 @@ __device__ __forceinline__ void offsets_ab(const Space &sp, I i, I &oa, I &ob) {
   ob += rest * (I)sp.s[2][0];
 }
 
+// side: -1, or which operand (0 = a, 1 = b) is the host scalar sv.
 template <int OP, int EPI, typename I>
 __global__ __launch_bounds__(kBlock) void k_fwd_generic(const float *a,
                                                         const float *b,
                                                         float *out, Space sp,
                                                         int flat_a, int flat_b,
-                                                        int vec_out) {
+                                                        int vec_out, ScalarArg sa) {
   __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
   if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   const I n = (I)sp.numel;
@@ -385,8 +394,8 @@ __global__ __launch_bounds__(kBlock) void k_fwd_generic(const float *a,
       if (i < n) {
         I oa, ob;
         offsets_ab<I>(sp, i, oa, ob);
-        float x = a[flat_a ? i : oa];
-        float y = b[flat_b ? i : ob];
+        float x = sa.side == 0 ? sa.value : a[flat_a ? i : oa];
+        float y = sa.side == 1 ? sa.value : b[flat_b ? i : ob];
         r[k] = fwd32<OP, EPI>(x, y, s_gelu);
       }
     }
@@ -653,7 +662,9 @@ static inline unsigned grid_of(int64_t n, int64_t per_block) {
 }
 
 hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
-                      const float *b, float *out, hipStream_t st) {
+                      const float *b, float *out, hipStream_t st, const ScalarArg *sa) {
+  const ScalarArg no_scalar{-1, 0.f};
+  const ScalarArg sarg = sa ? *sa : no_scalar;
   if (p.empty) return hipSuccess;
   const Canon &c = p.c;
   return with_op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
@@ -675,6 +686,7 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         RowArgs ra{};
         ra.rank = c.rank;
         ra.numel = c.numel;
+        ra.sval = sarg.value;
         int sm = p.swap ? 1 : 2;
         for (int k = 0; k < 3; ++k) {
           ra.n[k] = k < c.rank ? c.n[k] : 1;
@@ -701,6 +713,8 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         auto go_sw = [&](auto VECc, auto SMc) -> hipError_t {
           return p.swap ? go_i(VECc, SMc, IC<1>{}) : go_i(VECc, SMc, IC<0>{});
         };
+        if (p.small_mode == SM_ARG)
+          return p.vec == 1 ? go_sw(IC<1>{}, IC<SM_ARG>{}) : go_sw(IC<4>{}, IC<SM_ARG>{});
         if (p.vec == 1) return go_sw(IC<1>{}, IC<SM_GATHER>{});
         switch (p.small_mode) {
           case SM_BCAST: return go_sw(IC<4>{}, IC<SM_BCAST>{});
@@ -749,10 +763,10 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         unsigned grid = grid_of(c.numel, kBlock * 4);
         if (p.idx64)
           ZK_LAUNCH(prof, (k_fwd_generic<OP, EPI, int64_t>), dim3(grid), dim3(kBlock), 0, st,
-                    a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
+                    a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0, sarg);
         else
           ZK_LAUNCH(prof, (k_fwd_generic<OP, EPI, int32_t>), dim3(grid), dim3(kBlock), 0, st,
-                    a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0);
+                    a, b, out, sp, fa, fb, p.vec == 4 ? 1 : 0, sarg);
         return hipGetLastError();
       }
     }

@@ -31,6 +31,12 @@ struct RedDims {
 
 Space make_space(const Canon &c);
 
+// A host scalar operand passed by value: side 0 = operand a, 1 = operand b.
+struct ScalarArg {
+  int32_t side;
+  float value;
+};
+
 // Reserves a HIP event pair for the one kernel launched in its scope while
 // zk_profile_start() is in effect (slot < 0 otherwise).  ZK_LAUNCH hands the
 // pair to hipExtLaunchKernel, so the events carry the kernel's own begin and
@@ -50,8 +56,10 @@ struct ProfScope {
       hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);      \
   } while (0)
 
+// sa (optional): one operand is a host scalar; its pointer is unused.
 hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
-                      const float *b, float *out, hipStream_t st);
+                      const float *b, float *out, hipStream_t st,
+                      const ScalarArg *sa = nullptr);
 
 hipError_t launch_copy(const CopyPlan &p, const float *in, float *out, hipStream_t st);
 
@@ -64,7 +72,8 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
                       const float *a, const float *b, float *grad_a,
                       const float *acc_a, float *grad_b, const float *acc_b,
                       void *ws, hipStream_t st, float *grad_c = nullptr,
-                      const float *acc_c = nullptr, float c_sign = 1.f);
+                      const float *acc_c = nullptr, float c_sign = 1.f,
+                      const ScalarArg *sa = nullptr);
 
 // gc[i] = sign * g[i] (+ acc[i]) for i < n.
 hipError_t launch_signed(const float *g, int64_t n, float *gc, const float *acc,

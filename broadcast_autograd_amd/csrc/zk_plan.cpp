@@ -162,6 +162,8 @@ static bool is_flat(const Canon &c, int o) {
   return true;
 }
 
+bool canon_is_flat(const Canon &c, int o) { return is_flat(c, o); }
+
 static int64_t max_offset(const Canon &c, int o) {
   int64_t m = 0;
   for (int k = 0; k < c.rank; ++k)
@@ -186,14 +188,14 @@ static bool is_transposed2(const Canon &c, int o) {
 }
 
 bool rule_reads_a(zk_op op, zk_epi epi, int which) {
-  if (epi == ZK_EPI_GELU) return true;
+  if (epi != ZK_EPI_NONE) return true;
   if (op == ZK_MUL) return which == 1;
   if (op == ZK_DIV) return which == 1;
   return false;
 }
 
 bool rule_reads_b(zk_op op, zk_epi epi, int which) {
-  if (epi == ZK_EPI_GELU) return true;
+  if (epi != ZK_EPI_NONE) return true;
   if (op == ZK_MUL) return which == 0;
   if (op == ZK_DIV) return true;
   return false;

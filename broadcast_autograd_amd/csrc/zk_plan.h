@@ -46,7 +46,8 @@ enum KernelClass : int32_t {
 const char *kernel_name(int32_t k);
 
 // Inner-dim access mode of a non-dense operand in the ROW classes.
-enum SmallMode : int32_t { SM_BCAST = 0, SM_CONTIG = 1, SM_GATHER = 2 };
+// SM_ARG: the operand is a host scalar passed by value in the kernel arguments.
+enum SmallMode : int32_t { SM_BCAST = 0, SM_CONTIG = 1, SM_GATHER = 2, SM_ARG = 3 };
 
 // Magic-number division for 0 <= n < 2^31 and 1 <= d < 2^31
 // (Granlund & Montgomery, "Division by invariant integers using
@@ -180,6 +181,9 @@ zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
 // 3 = unused, 4 = target dense-aligned.  Reuses BwdPlan with which = 1.
 zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
                       uintptr_t pin, uintptr_t pout, BwdPlan *p);
+
+// Operand o walks the canonical space exactly like the dense output (op 0).
+bool canon_is_flat(const Canon &c, int o);
 
 // Operands the local rule of `op` (with `epi`) reads for grad `which`.
 bool rule_reads_a(zk_op op, zk_epi epi, int which);

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(PKG, "libzk.so")
 MAX_DIMS = 8
 
 OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3}
-EPIS = {"none": 0, "gelu": 1}
+EPIS = {"none": 0, "gelu": 1, "relu": 2}
 
 STATUS = {0: "ZK_OK", 1: "ZK_ERR_NULL", 2: "ZK_ERR_RANK", 3: "ZK_ERR_BAD_SIZE",
           4: "ZK_ERR_BAD_STRIDE", 5: "ZK_ERR_BROADCAST", 6: "ZK_ERR_ALIAS",
@@ -25,6 +25,7 @@ ERR = {v: k for k, v in STATUS.items()}
 # exported symbols declared in include/zk.h
 SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
            "zk_reduce_to_shape", "zk_materialize", "zk_binary2_fwd", "zk_binary2_bwd",
+           "zk_scalar_fwd", "zk_scalar_bwd", "zk_unary_fwd", "zk_unary_bwd",
            "zk_status_string", "zk_plan_describe", "zk_kernel_name",
            "zk_profile_start", "zk_profile_stop", "zk_profile_read")
 
@@ -76,6 +77,11 @@ def lib():
         L.zk_binary_bwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, P, P]
         L.zk_reduce_to_shape.argtypes = [P, P, I32, P, P, P, P, P]
         L.zk_materialize.argtypes = [P, P, I32, P, P, P]
+        F32 = ctypes.c_float
+        L.zk_scalar_fwd.argtypes = [I32, I32, P, P, F32, I32, P, P]
+        L.zk_scalar_bwd.argtypes = [I32, I32, P, P, P, F32, I32, P, P, P]
+        L.zk_unary_fwd.argtypes = [I32, P, P, P, P]
+        L.zk_unary_bwd.argtypes = [I32, P, P, P, P, P, P]
         L.zk_binary2_fwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P]
         L.zk_binary2_bwd.argtypes = [I32, I32] + [P] * 16
         L.zk_status_string.argtypes = [I32]
@@ -214,6 +220,53 @@ def binary_bwd(op, grad, a, b, need_a=True, need_b=True, grad_a=None,
     _check(L.zk_binary_bwd(*args, _ptr(workspace), ctypes.byref(nbytes),
                            _stream(stream)), "zk_binary_bwd")
     return grad_a, grad_b
+
+
+def scalar_fwd(op, t, s, scalar_first=False, out=None, epi="none", stream=None):
+    """out = epi(t (op) s), or epi(s (op) t), s a host float (by value)."""
+    import torch
+    if out is None:
+        out = torch.empty(tuple(t.shape), dtype=torch.float32, device=t.device)
+    d = desc_of(t)
+    _check(lib().zk_scalar_fwd(_op(op), _epi(epi), _ptr(t), ctypes.byref(d), float(s),
+                               1 if scalar_first else 0, _ptr(out), _stream(stream)),
+           "zk_scalar_fwd")
+    return out
+
+
+def scalar_bwd(op, grad, t, s, scalar_first=False, grad_t=None, acc_t=None, epi="none",
+               stream=None):
+    """Gradient of epi(t (op) s) (or epi(s (op) t)) w.r.t. the tensor t."""
+    import torch
+    if grad_t is None:
+        grad_t = torch.empty(tuple(t.shape), dtype=torch.float32, device=grad.device)
+    d = desc_of(t)
+    _check(lib().zk_scalar_bwd(_op(op), _epi(epi), _ptr(grad), _ptr(t), ctypes.byref(d),
+                               float(s), 1 if scalar_first else 0, _ptr(grad_t), _ptr(acc_t),
+                               _stream(stream)), "zk_scalar_bwd")
+    return grad_t
+
+
+def unary_fwd(f, x, out=None, stream=None):
+    """out = f(x), f "gelu" or "relu"."""
+    import torch
+    if out is None:
+        out = torch.empty(tuple(x.shape), dtype=torch.float32, device=x.device)
+    d = desc_of(x)
+    _check(lib().zk_unary_fwd(_epi(f), _ptr(x), ctypes.byref(d), _ptr(out), _stream(stream)),
+           "zk_unary_fwd")
+    return out
+
+
+def unary_bwd(f, grad, x, grad_x=None, acc_x=None, stream=None):
+    """grad_x = grad * f'(x) (+ acc_x)."""
+    import torch
+    if grad_x is None:
+        grad_x = torch.empty(tuple(x.shape), dtype=torch.float32, device=grad.device)
+    d = desc_of(x)
+    _check(lib().zk_unary_bwd(_epi(f), _ptr(grad), _ptr(x), ctypes.byref(d), _ptr(grad_x),
+                              _ptr(acc_x), _stream(stream)), "zk_unary_bwd")
+    return grad_x
 
 
 def materialize(x, shape=None, out=None, stream=None):

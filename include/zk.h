@@ -67,12 +67,16 @@ typedef enum {
 /* out = a (op) b.  Operator chapter, "element-wise operators". */
 typedef enum { ZK_ADD = 0, ZK_SUB = 1, ZK_MUL = 2, ZK_DIV = 3 } zk_op;
 
-/* Optional epilogue applied to the op's result: y = GeLU(a (op) b), with
- * GeLU(h) = h * Phi(h) and Phi the standard normal CDF (the activation the
- * GPU chapter, "element-wise" section, and the GPT chapter's FFN name).
- * The forward value is GeLU evaluated in binary64 and rounded once to
- * binary32; h = a (op) b is itself rounded to binary32 first. */
-typedef enum { ZK_EPI_NONE = 0, ZK_EPI_GELU = 1 } zk_epi;
+/* Optional epilogue applied to the op's result h = a (op) b (itself rounded
+ * to binary32 first):
+ *   ZK_EPI_GELU: y = GeLU(h) = h * Phi(h), Phi the standard normal CDF (the
+ *                activation the GPU chapter, "element-wise" section, and the
+ *                GPT chapter's FFN name), evaluated in binary64 and rounded
+ *                once to binary32; GeLU' = Phi(h) + h*phi(h).
+ *   ZK_EPI_RELU: y = ReLU(h) = h for h > 0, NaN for NaN, +0 otherwise (the
+ *                activation of the Module chapter's example MLP); ReLU'(h) = 1 for
+ *                h > 0, else 0. */
+typedef enum { ZK_EPI_NONE = 0, ZK_EPI_GELU = 1, ZK_EPI_RELU = 2 } zk_epi;
 
 /* A strided tensor view (Tensor chapter, "shape and strides").
  * sizes[k], strides[k] for k < rank; entries past rank are ignored. */
@@ -166,6 +170,46 @@ zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
                              int32_t rank_out, const int64_t *sizes_out,
                              float *out, void *workspace,
                              size_t *workspace_bytes, void *stream);
+
+/*
+ * A tensor and a host scalar (Operator chapter, "element-wise operators":
+ * the same operators with one operand a constant):
+ *   out = epi(t (op) s), or epi(s (op) t) when scalar_first != 0,
+ * for every element of t; out is dense row-major in t's shape.  The
+ * scalar travels by value in the kernel arguments (no device copy).
+ *   t, dt : tensor, any non-negative strides
+ * Aliasing: out may be exactly t when t is dense row-major; other overlaps
+ * are ZK_ERR_ALIAS.  Errors: as zk_binary_fwd.
+ */
+zk_status zk_scalar_fwd(zk_op op, zk_epi epi, const float *t, const zk_desc *dt,
+                        float s, int32_t scalar_first, float *out, void *stream);
+
+/*
+ * Backward of zk_scalar_fwd w.r.t. the tensor: grad_t = rule(g) (+ acc_t),
+ * the operand-t rules of zk_binary_bwd with the scalar as the other operand.
+ * A host scalar is a constant and gets no gradient (pass a rank-0 device
+ * tensor to zk_binary_bwd when it needs one).  No reduction, no workspace.
+ *   grad   : dense row-major, t's shape
+ *   grad_t : dense row-major, t's shape; acc_t NULL, a buffer, exactly
+ *            grad_t (in place) or exactly grad
+ * Errors: as zk_binary_bwd (no ZK_ERR_WORKSPACE).
+ */
+zk_status zk_scalar_bwd(zk_op op, zk_epi epi, const float *grad, const float *t,
+                        const zk_desc *dt, float s, int32_t scalar_first,
+                        float *grad_t, const float *acc_t, void *stream);
+
+/*
+ * Stand-alone activation y = f(x), f = ZK_EPI_GELU or ZK_EPI_RELU (the
+ * epilogues above applied to x itself), and its backward
+ * grad_x = g * f'(x) (+ acc_x).  Computed as zk_scalar_fwd / _bwd of
+ * x - 0, which is x for every binary32 x (-0, NaN and infinities included).
+ * Errors: as zk_scalar_fwd / _bwd; f = ZK_EPI_NONE is ZK_ERR_UNSUPPORTED.
+ */
+zk_status zk_unary_fwd(zk_epi f, const float *x, const zk_desc *dx, float *out,
+                       void *stream);
+zk_status zk_unary_bwd(zk_epi f, const float *grad, const float *x,
+                       const zk_desc *dx, float *grad_x, const float *acc_x,
+                       void *stream);
 
 /*
  * Stride-aware materialisation (Operator chapter, "view backward": the

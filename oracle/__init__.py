@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "liboracle.so")
 SRC_PATH = os.path.join(HERE, "oracle.c")
 
 ADD, SUB, MUL, DIV = 0, 1, 2, 3
-EPI_NONE, EPI_GELU = 0, 1
+EPI_NONE, EPI_GELU, EPI_RELU = 0, 1, 2
 OPS = {"add": ADD, "sub": SUB, "mul": MUL, "div": DIV}
 
 OK, ERR_BROADCAST, ERR_RANK, ERR_SIZE, ERR_ARG = 0, 1, 2, 3, 4
@@ -80,6 +80,8 @@ def lib():
         L.or_bwd2_at.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  P, P, P, P, P, P, P, P, I64, P, P, P, P]
         L.or_materialize.argtypes = [P, P, ctypes.c_int, P, P]
+        L.or_relu32.argtypes = [ctypes.c_float]
+        L.or_relu32.restype = ctypes.c_float
         L.or_gelu32.argtypes = [ctypes.c_float]
         L.or_gelu32.restype = ctypes.c_float
         L.or_phi_cdf.argtypes = [ctypes.c_double]
@@ -357,6 +359,10 @@ def bwd2_at(op1, op2, which, g, a, b, c, pos, acc=None, tie=None):
                             ctypes.byref(dc), accp, pos.size, pos.ctypes.data,
                             f32.ctypes.data, f64.ctypes.data, ab.ctypes.data))
     return Grad(f32, f64, ab)
+
+
+def relu32(h):
+    return np.float32(lib().or_relu32(float(h)))
 
 
 def gelu32(h):

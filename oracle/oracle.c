@@ -28,6 +28,8 @@
  *              (built with -ffp-contract=off, SSE, no fast-math)
  *   GeLU     : exact function h*Phi(h), Phi(h) = erfc(-h/sqrt2)/2, evaluated in
  *              binary64 with libm erfc and rounded once to binary32
+ *   ReLU     : h for h > 0, NaN for NaN, +0 otherwise; derivative 1 for h > 0,
+ *              else 0 (the pages name the activation without a formula)
  *   backward : every term in binary64 from the exact binary32 inputs, summed in
  *              binary64 in row-major index order, rounded once to binary32;
  *              the sum of |terms| is returned beside it for the tolerance.
@@ -46,7 +48,7 @@
 #define OR_MAX_DIMS 8
 
 enum { OR_ADD = 0, OR_SUB = 1, OR_MUL = 2, OR_DIV = 3 };
-enum { OR_EPI_NONE = 0, OR_EPI_GELU = 1 };
+enum { OR_EPI_NONE = 0, OR_EPI_GELU = 1, OR_EPI_RELU = 2 };
 enum {
   OR_OK = 0,
   OR_ERR_BROADCAST = 1, /* shapes do not broadcast                   */
@@ -151,18 +153,26 @@ float or_gelu32(float h) {
   return (float)(hd * or_phi_cdf(hd));
 }
 
+/* ReLU(h): h for h > 0, NaN stays NaN, +0 otherwise. */
+float or_relu32(float h) {
+  if (isnan(h)) return h;
+  return h > 0.0f ? h : 0.0f;
+}
+
 static float fwd_at(int op, int epi, const float *a, const or_desc *da,
                     const float *b, const or_desc *db, int r,
                     const int64_t *idx) {
   float x = a[operand_offset(da, r, idx)];
   float y = b[operand_offset(db, r, idx)];
   float h = op32(op, x, y);
-  return epi == OR_EPI_GELU ? or_gelu32(h) : h;
+  if (epi == OR_EPI_GELU) return or_gelu32(h);
+  if (epi == OR_EPI_RELU) return or_relu32(h);
+  return h;
 }
 
 int or_fwd(int op, int epi, const float *a, const or_desc *da, const float *b,
            const or_desc *db, float *out) {
-  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_GELU) return OR_ERR_ARG;
+  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_RELU) return OR_ERR_ARG;
   int s;
   if ((s = check_desc(da)) || (s = check_desc(db))) return s;
   int r;
@@ -184,7 +194,7 @@ int or_fwd(int op, int epi, const float *a, const or_desc *da, const float *b,
 int or_fwd_at(int op, int epi, const float *a, const or_desc *da,
               const float *b, const or_desc *db, int64_t count,
               const int64_t *pos, float *out) {
-  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_GELU) return OR_ERR_ARG;
+  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_RELU) return OR_ERR_ARG;
   int s;
   if ((s = check_desc(da)) || (s = check_desc(db))) return s;
   int r;
@@ -216,6 +226,8 @@ static int local_terms(int op, int epi, int which, double g, double x,
     gg[0] = g * or_phi_cdf(h);
     gg[1] = g * h * or_phi_pdf(h);
     np = 2;
+  } else if (epi == OR_EPI_RELU) {
+    gg[0] = h32 > 0.0f ? g : 0.0;
   }
   for (int p = 0; p < np; ++p) {
     double u = gg[p], t;
@@ -274,7 +286,7 @@ static double grad_at(int op, int epi, int which, const float *g,
     }
     float xv = a[operand_offset(da, r, idx)];
     float yv = b[operand_offset(db, r, idx)];
-    float h32 = epi == OR_EPI_GELU ? op32(op, xv, yv) : 0.0f;
+    float h32 = epi != OR_EPI_NONE ? op32(op, xv, yv) : 0.0f;
     double piece[2];
     int np = local_terms(op, epi, which, (double)g[goff], (double)xv,
                          (double)yv, h32, piece);
@@ -289,7 +301,7 @@ static double grad_at(int op, int epi, int which, const float *g,
 
 static int bwd_common(int op, int epi, const or_desc *da, const or_desc *db,
                       int *r, int64_t *n) {
-  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_GELU) return OR_ERR_ARG;
+  if (op < OR_ADD || op > OR_DIV || epi < 0 || epi > OR_EPI_RELU) return OR_ERR_ARG;
   int s;
   if ((s = check_desc(da)) || (s = check_desc(db))) return s;
   return or_broadcast_shape(da->rank, da->sizes, db->rank, db->sizes, r, n);

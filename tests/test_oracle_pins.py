@@ -542,3 +542,68 @@ def test_materialize_against_numpy(orc):
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (sizes, strides, shape)
     with pytest.raises(orc.OracleError):
         orc.materialize(np.ones((2, 3), np.float32), (3, 3))
+
+
+# ------------------------------------------- ReLU epilogue, scalars (f3) --
+def test_relu_pins(orc):
+    """ReLU(h) = h for h > 0, NaN for NaN, +0 otherwise (the reading for the
+    activation the Module chapter's example MLP uses); numpy.maximum agrees
+    away from -0 and NaN."""
+    assert orc.relu32(2.5) == np.float32(2.5)
+    assert orc.relu32(-3.0) == 0.0
+    z = orc.relu32(-0.0)
+    assert z == 0.0 and not np.signbit(z)
+    assert orc.relu32(np.inf) == np.inf and orc.relu32(-np.inf) == 0.0
+    assert np.isnan(orc.relu32(np.nan))
+    x = np.random.default_rng(3).standard_normal(1000).astype(np.float32)
+    y = orc.fwd("add", x, np.zeros((), np.float32), epi=orc.EPI_RELU)
+    assert np.array_equal(y, np.maximum(x, np.float32(0)))
+
+
+@pytest.mark.parametrize("op", ["add", "sub", "mul", "div"])
+def test_relu_backward_finite_differences(orc, op):
+    """d/dx of sum(g * ReLU(a op b)) by central differences at points away
+    from the kink; at h exactly 0 the rule gives 0 (subgradient, reading)."""
+    rng = np.random.default_rng(hash(op) % 2**32)
+    a = rng.uniform(0.5, 2.0, (3, 4)).astype(np.float32)
+    a *= np.where(rng.random((3, 4)) < 0.5, -1, 1).astype(np.float32)
+    b = rng.uniform(0.5, 2.0, (4,)).astype(np.float32)
+    g = rng.standard_normal((3, 4)).astype(np.float32)
+    ga, gb = orc.bwd(op, g, a, b, epi=orc.EPI_RELU)
+
+    def L(a64, b64):
+        return math.fsum((g.astype(np.float64) * np.maximum(_f64(op, a64, b64), 0.0)).ravel())
+
+    for which, x, gx in ((0, a, ga), (1, b, gb)):
+        x64 = x.astype(np.float64)
+        for j in np.ndindex(x.shape):
+            h = 1e-4 * max(1.0, abs(x64[j]))
+            xp, xm = x64.copy(), x64.copy()
+            xp[j] += h
+            xm[j] -= h
+            if which == 0:
+                fd = (L(xp, b.astype(np.float64)) - L(xm, b.astype(np.float64))) / (2 * h)
+            else:
+                fd = (L(a.astype(np.float64), xp) - L(a.astype(np.float64), xm)) / (2 * h)
+            tol = (2e-5 if op == "div" else 1e-6) * max(1.0, gx.abs[j])
+            assert abs(fd - gx.f64[j]) <= tol, (op, which, j, fd, gx.f64[j])
+    zero = np.zeros((2,), np.float32)
+    gz, _ = orc.bwd("add", np.ones(2, np.float32), zero, zero, epi=orc.EPI_RELU)
+    assert np.all(gz.f64 == 0.0)
+
+
+def test_scalar_operand_is_rank0_broadcast(orc):
+    """A scalar operand is the rank-0 case of the broadcast rule (Operator
+    chapter, "broadcast"): t op s reads s at every position; s op t too."""
+    t = np.array([[1.0, -2.0, 3.0], [4.0, 0.5, -6.0]], np.float32)
+    s = np.array(2.0, np.float32)
+    assert orc.fwd("sub", t, s).tolist() == [[-1.0, -4.0, 1.0], [2.0, -1.5, -8.0]]
+    assert orc.fwd("sub", s, t).tolist() == [[1.0, 4.0, -1.0], [-2.0, 1.5, 8.0]]
+    # operand roles of div against numpy's correctly rounded binary32 division
+    assert np.array_equal(orc.fwd("div", s, t), np.float32(2.0) / t)
+    assert np.array_equal(orc.fwd("div", t, s), t / np.float32(2.0))
+    g = np.ones((2, 3), np.float32)
+    gt, gs = orc.bwd("div", g, s, t)
+    # d(s/t)/dt = -s/t^2
+    assert np.allclose(gs.f64, -2.0 / t.astype(np.float64) ** 2, rtol=1e-15, atol=0)
+    assert gt.f64 == pytest.approx(float(np.sum(1.0 / t.astype(np.float64))), rel=1e-15)
