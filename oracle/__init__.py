@@ -80,6 +80,12 @@ def lib():
         L.or_bwd2_at.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  P, P, P, P, P, P, P, P, I64, P, P, P, P]
         L.or_materialize.argtypes = [P, P, ctypes.c_int, P, P]
+        L.or_mean.argtypes = [P, P, ctypes.c_int, P, P, P, P]
+        L.or_mean_bwd.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, P]
+        L.or_grad_norm.argtypes = [ctypes.c_int, P, P]
+        L.or_grad_norm.restype = ctypes.c_double
+        L.or_clip_grad_norm.argtypes = [ctypes.c_int, P, P, ctypes.c_double, P, P]
+        L.or_clip_grad_norm.restype = ctypes.c_double
         L.or_relu32.argtypes = [ctypes.c_float]
         L.or_relu32.restype = ctypes.c_float
         L.or_gelu32.argtypes = [ctypes.c_float]
@@ -268,6 +274,65 @@ def reduce_to_shape(x, shape):
     _check(lib().or_reduce(_ptr(v), ctypes.byref(d), len(shape), _i64(shape),
                            p(f32), p(f64), p(ab)))
     return Grad(f32, f64, ab)
+
+
+def mean_to_shape(x, shape):
+    """Mean of ``x`` over the dims where ``shape`` (which must broadcast to
+    x's shape) is 1 or missing.  Returns a Grad: fp32 value, binary64 value
+    and sum|x| / count (the tolerance base)."""
+    v = _as_view(x)
+    d = _desc(v)
+    shape = tuple(int(s) for s in shape)
+    f32 = np.empty(shape, dtype=np.float32)
+    f64 = np.empty(shape, dtype=np.float64)
+    ab = np.empty(shape, dtype=np.float64)
+
+    def p(z):
+        return None if z.size == 0 else z.ctypes.data
+
+    _check(lib().or_mean(_ptr(v), ctypes.byref(d), len(shape), _i64(shape),
+                         p(f32), p(f64), p(ab)))
+    return Grad(f32, f64, ab)
+
+
+def mean_bwd(g, shape_in):
+    """Gradient of mean_to_shape: g (dense, the reduced shape) divided by the
+    count and repeated over ``shape_in``."""
+    g = np.array(g, dtype=np.float32, order="C")
+    shape_in = tuple(int(s) for s in shape_in)
+    out = np.empty(shape_in, dtype=np.float32)
+    _check(lib().or_mean_bwd(g.ctypes.data if g.size else None, g.ndim, _i64(g.shape),
+                             len(shape_in), _i64(shape_in),
+                             out.ctypes.data if out.size else None))
+    return out
+
+
+def _tensor_list(gs):
+    arrs = [np.array(x, dtype=np.float32, order="C") for x in gs]
+    ptrs = (ctypes.c_void_p * max(1, len(arrs)))(
+        *[a.ctypes.data if a.size else None for a in arrs])
+    ns = _i64([a.size for a in arrs])
+    return arrs, ptrs, ns
+
+
+def grad_norm(gs):
+    """Global L2 norm (binary64) of a list of gradients."""
+    arrs, ptrs, ns = _tensor_list(gs)
+    return float(lib().or_grad_norm(len(arrs), ptrs, ns))
+
+
+def clip_grad_norm(gs, max_norm):
+    """ClipGradNorm on copies of ``gs``: returns (scaled copies, norm as
+    binary64, whether it scaled, the binary32 factor)."""
+    arrs, ptrs, ns = _tensor_list(gs)
+    arrs = [a.copy() for a in arrs]
+    ptrs = (ctypes.c_void_p * max(1, len(arrs)))(
+        *[a.ctypes.data if a.size else None for a in arrs])
+    clipped = ctypes.c_int(0)
+    factor = ctypes.c_float(0.0)
+    norm = lib().or_clip_grad_norm(len(arrs), ptrs, ns, float(max_norm),
+                                   ctypes.byref(clipped), ctypes.byref(factor))
+    return arrs, float(norm), bool(clipped.value), np.float32(factor.value)
 
 
 def materialize(x, shape=None):

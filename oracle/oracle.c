@@ -22,6 +22,9 @@
  *     changing their math (Operator chapter, "fusion" section): the fused
  *     expression (a op1 b) op2 c is computed here as the two operators one
  *     after the other
+ *   - the mean, and the global L2 norm of all parameter gradients with the
+ *     ClipGradNorm scaling g <- g * c / (||g||_2 + 1e-6) applied when the
+ *     norm exceeds c (GPU chapter, "reduction"; GPT chapter, "training loop")
  *
  * Precision (the pages fix none):
  *   forward  : one IEEE binary32 operation per element, round-to-nearest-even
@@ -33,6 +36,13 @@
  *   backward : every term in binary64 from the exact binary32 inputs, summed in
  *              binary64 in row-major index order, rounded once to binary32;
  *              the sum of |terms| is returned beside it for the tolerance.
+ *   mean     : the binary64 sum divided by the count in binary64, rounded once;
+ *              its gradient g / count is one binary32 division by the count
+ *              rounded to binary32
+ *   L2 norm  : squares summed in binary64 (exact squares), square root in
+ *              binary64; the clip decision and factor are taken in binary64,
+ *              the factor rounded once to binary32 and applied with one
+ *              binary32 multiply per element.
  *
  * Loops are plain odometers over multi-indices.  OpenMP splits only the loop
  * over OUTPUT elements, so results do not depend on the thread count.
@@ -596,4 +606,102 @@ int or_materialize(const float *in, const or_desc *din, int rout, const int64_t 
     out[f] = in[operand_offset(din, r, idx)];
   }
   return OR_OK;
+}
+
+/* ------------------------------------------------------- other reductions */
+
+/* Mean back to a shape: out_j = RN32(S_j / count), S_j the binary64 sum in
+ * index order of the `count` input elements that map to j (the elements
+ * or_reduce sums), count the product of the input sizes over the reduced
+ * dims.  An empty reduced dim gives count 0 and 0/0 = NaN.  out64 gets
+ * S_j / count and absout sum|in_i| / count (the tolerance base). */
+int or_mean(const float *in, const or_desc *din, int rout, const int64_t *nout,
+            float *out, double *out64, double *absout) {
+  int64_t m = numel(rout < 0 ? 0 : rout, nout);
+  double *s64 = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+  double *sab = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+  int s = or_reduce(in, din, rout, nout, NULL, s64, sab);
+  if (s == OR_OK) {
+    int r = din->rank;
+    int64_t count = 1;
+    for (int k = 0; k < r; ++k) {
+      int ko = k - (r - rout);
+      if (ko < 0 || nout[ko] == 1) count *= din->sizes[k];
+    }
+    for (int64_t j = 0; j < m; ++j) {
+      double v = s64[j] / (double)count;
+      if (out) out[j] = (float)v;
+      if (out64) out64[j] = v;
+      if (absout) absout[j] = sab[j] / (double)count;
+    }
+  }
+  free(s64);
+  free(sab);
+  return s;
+}
+
+/* Gradient of the mean: each input element (shape nin) receives the upstream
+ * gradient of the output it was averaged into (g dense in shape nout, which
+ * broadcasts to nin), divided by the count: grad_in_i = RN32(g_j /
+ * RN32(count)), one binary32 division. */
+int or_mean_bwd(const float *g, int rout, const int64_t *nout, int rin,
+                const int64_t *nin, float *grad_in) {
+  if (rout < 0 || rout > OR_MAX_DIMS || rin < 0 || rin > OR_MAX_DIMS) return OR_ERR_RANK;
+  for (int k = 0; k < rout; ++k) if (nout[k] < 0) return OR_ERR_SIZE;
+  for (int k = 0; k < rin; ++k) if (nin[k] < 0) return OR_ERR_SIZE;
+  int r, s;
+  int64_t n[OR_MAX_DIMS];
+  if ((s = or_broadcast_shape(rin, nin, rout, nout, &r, n))) return s;
+  if (r != rin) return OR_ERR_ARG;
+  for (int k = 0; k < r; ++k) if (n[k] != nin[k]) return OR_ERR_ARG;
+  int64_t count = 1;
+  for (int k = 0; k < r; ++k) {
+    int ko = k - (r - rout);
+    if (ko < 0 || nout[ko] == 1) count *= nin[k];
+  }
+  const float c32 = (float)count;
+  int64_t total = numel(r, nin);
+  for (int64_t f = 0; f < total; ++f) {
+    int64_t idx[OR_MAX_DIMS];
+    unflatten(f, r, nin, idx);
+    int64_t j = 0;
+    for (int ko = 0; ko < rout; ++ko) {
+      int k = ko + (r - rout);
+      j = j * nout[ko] + (nout[ko] == 1 ? 0 : idx[k]);
+    }
+    grad_in[f] = g[j] / c32;
+  }
+  return OR_OK;
+}
+
+/* Global L2 norm of a list of dense gradients: the square root, in binary64,
+ * of the binary64 sum of g^2 over every element of every tensor, in list
+ * order then index order (each square of a binary32 value is exact). */
+double or_grad_norm(int count, const float *const *g, const int64_t *n) {
+  double s = 0.0;
+  for (int t = 0; t < count; ++t)
+    for (int64_t i = 0; i < n[t]; ++i) {
+      double v = (double)g[t][i];
+      s += v * v;
+    }
+  return sqrt(s);
+}
+
+/* ClipGradNorm: when the global norm exceeds c, every gradient element is
+ * scaled by the one factor c / (norm + 1e-6).  The decision and the factor
+ * are taken in binary64 from the binary64 norm; the factor is rounded once
+ * to binary32 and each element becomes RN32(g * factor).  Scales in place;
+ * returns the norm, and through the pointers whether it scaled and the
+ * binary32 factor (1 when it did not). */
+double or_clip_grad_norm(int count, float *const *g, const int64_t *n, double c,
+                         int *clipped, float *factor) {
+  double norm = or_grad_norm(count, (const float *const *)g, n);
+  int clip = norm > c;
+  float f = clip ? (float)(c / (norm + 1e-6)) : 1.0f;
+  if (clip)
+    for (int t = 0; t < count; ++t)
+      for (int64_t i = 0; i < n[t]; ++i) g[t][i] = g[t][i] * f;
+  if (clipped) *clipped = clip;
+  if (factor) *factor = f;
+  return norm;
 }

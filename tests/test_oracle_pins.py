@@ -607,3 +607,141 @@ def test_scalar_operand_is_rank0_broadcast(orc):
     # d(s/t)/dt = -s/t^2
     assert np.allclose(gs.f64, -2.0 / t.astype(np.float64) ** 2, rtol=1e-15, atol=0)
     assert gt.f64 == pytest.approx(float(np.sum(1.0 / t.astype(np.float64))), rel=1e-15)
+
+
+# ------------------------------------------------------- other reductions
+# The mean and the global gradient norm are the reductions the pages list
+# beside the sum (GPU chapter, "reduction"); the training loop averages the
+# per-token loss over dim 0 and clips the gradients to a global L2 norm of
+# 1.0 with g <- g * c / (||g||_2 + 1e-6) (GPT chapter, "training loop").
+
+
+def test_mean_closed_forms(orc):
+    """Mean of a constant is that constant (bitwise); the mean of
+    x[i, j] = 10 i + j over i is j + 5 (R - 1), over j it is 10 i + (K - 1)/2."""
+    R, K = 7, 6
+    v = np.float32(0.3)
+    c = np.full((R, K), v, np.float32)
+    for shape in ((), (K,), (R, 1), (1, K)):
+        got = orc.mean_to_shape(c, shape).f32
+        assert np.all(got.view(np.uint32) == np.full(shape, v, np.float32).view(np.uint32))
+    x = (10 * np.arange(R)[:, None] + np.arange(K)[None, :]).astype(np.float32)
+    assert orc.mean_to_shape(x, (K,)).f32.tolist() == [j + 5.0 * (R - 1) for j in range(K)]
+    assert orc.mean_to_shape(x, (R, 1)).f32.ravel().tolist() == [
+        10.0 * i + (K - 1) / 2 for i in range(R)]
+    # the whole mean of x: 5 (R - 1) + (K - 1) / 2
+    assert float(orc.mean_to_shape(x, ()).f32) == 5.0 * (R - 1) + (K - 1) / 2
+
+
+def test_mean_library_cases_and_edges(orc):
+    """Against numpy's binary64 mean; a size-1 (or unreduced) dim is a copy;
+    an empty reduced dim gives NaN (0 / 0); the divisor is the count of the
+    reduced dims only."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((5, 3, 8)).astype(np.float32)
+    x64 = x.astype(np.float64)
+    for shape, axes in (((), (0, 1, 2)), ((8,), (0, 1)), ((3, 1), (0, 2)),
+                        ((5, 1, 1), (1, 2)), ((1, 3, 8), (0,))):
+        want = x64.mean(axis=axes).reshape(shape)
+        got = orc.mean_to_shape(x, shape)
+        assert np.allclose(got.f64, want, rtol=1e-14, atol=1e-16), shape
+        assert np.allclose(got.abs, np.abs(x64).mean(axis=axes).reshape(shape), rtol=1e-14)
+        # rounded once from the binary64 mean
+        assert np.array_equal(got.f32, got.f64.astype(np.float32))
+    assert np.array_equal(orc.mean_to_shape(x, x.shape).f32, x)
+    y = x[:, :1, :]
+    assert np.array_equal(orc.mean_to_shape(y, (5, 1, 8)).f32, y)
+    e = orc.mean_to_shape(np.zeros((0, 4), np.float32), (4,)).f32
+    assert e.shape == (4,) and np.all(np.isnan(e))
+    assert orc.mean_to_shape(np.zeros((0, 4), np.float32), (0, 1)).f32.shape == (0, 1)
+    with pytest.raises(orc.OracleError):
+        orc.mean_to_shape(x, (4,))
+
+
+def test_mean_backward(orc):
+    """d/dx_i of sum_j g_j mean(x)_j is g_j / count for the output j that
+    x_i is averaged into (finite differences of the linear form); with a
+    power-of-two count the division is exact and the gradient's mass equals
+    the upstream gradient's."""
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((3, 5, 4)).astype(np.float32)
+    for shape in ((5, 1), (), (1, 5, 4), (4,)):
+        g = rng.standard_normal(shape).astype(np.float32)
+        gx = orc.mean_bwd(g, x.shape)
+        assert gx.shape == x.shape
+
+        def L(x64):
+            m = x64.mean(axis=tuple(k for k in range(3) if _reduced(k, x.shape, shape)),
+                         keepdims=True).reshape(shape)
+            return math.fsum((g.astype(np.float64) * m).ravel())
+
+        x64 = x.astype(np.float64)
+        for j in [(0, 0, 0), (2, 4, 3), (1, 2, 1)]:
+            h = 1e-3
+            xp, xm = x64.copy(), x64.copy()
+            xp[j] += h
+            xm[j] -= h
+            fd = (L(xp) - L(xm)) / (2 * h)
+            assert abs(fd - float(gx[j])) <= 1e-6 * max(1e-3, abs(fd)), (shape, j)
+    g = rng.standard_normal((3, 1, 4)).astype(np.float32)
+    gx = orc.mean_bwd(g, (3, 8, 4))  # count 8: exact division
+    assert np.array_equal(gx * np.float32(8), np.broadcast_to(g, (3, 8, 4)))
+    assert math.fsum(gx.astype(np.float64).ravel()) == math.fsum(g.astype(np.float64).ravel())
+    with pytest.raises(orc.OracleError):
+        orc.mean_bwd(g, (3, 8, 5))
+
+
+def _reduced(k, shape_in, shape_out):
+    ko = k - (len(shape_in) - len(shape_out))
+    return ko < 0 or (shape_out[ko] == 1 and shape_in[k] != 1)
+
+
+def test_grad_norm_pins(orc):
+    """Closed form for constants (0.5 repeated 64 times has norm 4 exactly),
+    additivity of squared norms over the list, numpy's binary64 norm of the
+    concatenation, and empty tensors / lists contributing nothing."""
+    assert orc.grad_norm([np.full(64, 0.5, np.float32)]) == 4.0
+    assert orc.grad_norm([np.full(9, -3.0, np.float32), np.full(16, 0.0, np.float32)]) == 9.0
+    assert orc.grad_norm([]) == 0.0
+    assert orc.grad_norm([np.zeros(0, np.float32)]) == 0.0
+    rng = np.random.default_rng(33)
+    gs = [rng.standard_normal(n).astype(np.float32) * np.float32(s)
+          for n, s in ((1000, 0.01), (3, 5.0), (0, 1.0), (4097, 0.1))]
+    whole = np.linalg.norm(np.concatenate([g.astype(np.float64) for g in gs]))
+    assert orc.grad_norm(gs) == pytest.approx(whole, rel=1e-14)
+    parts = math.fsum(orc.grad_norm([g]) ** 2 for g in gs)
+    assert orc.grad_norm(gs) ** 2 == pytest.approx(parts, rel=1e-14)
+    # scaling by a power of two scales the norm exactly
+    assert orc.grad_norm([g * np.float32(4) for g in gs]) == 4 * orc.grad_norm(gs)
+
+
+def test_clip_grad_norm_pins(orc):
+    """Below or at the threshold nothing changes (the pages scale only when
+    the norm exceeds c); above it every element is multiplied by the same
+    factor, the direction is kept, the new norm is c * n / (n + 1e-6), and
+    the 1e-6 sits beside the norm (visible when the norm is small)."""
+    rng = np.random.default_rng(34)
+    gs = [rng.standard_normal(n).astype(np.float32) * np.float32(0.01) for n in (50, 7)]
+    n = orc.grad_norm(gs)
+    out, norm, clipped, f = orc.clip_grad_norm(gs, 2 * n)
+    assert not clipped and norm == n and f == 1.0
+    assert all(np.array_equal(a, b) for a, b in zip(out, gs))
+    # norm exactly equal to the threshold: [3, 4] has norm 5
+    out, norm, clipped, _ = orc.clip_grad_norm([np.array([3.0, 4.0], np.float32)], 5.0)
+    assert norm == 5.0 and not clipped and out[0].tolist() == [3.0, 4.0]
+    # small norm: c = 1e-3, ||g|| = 5e-3 -> factor 1e-3 / (5e-3 + 1e-6)
+    g = np.array([3e-3, 4e-3], np.float32)
+    out, norm, clipped, f = orc.clip_grad_norm([g], 1e-3)
+    n64 = math.sqrt(float(g[0]) ** 2 + float(g[1]) ** 2)
+    assert clipped and norm == pytest.approx(n64, rel=1e-15)
+    want = 1e-3 * n64 / (n64 + 1e-6)
+    got = math.sqrt(float(out[0][0]) ** 2 + float(out[0][1]) ** 2)
+    assert got == pytest.approx(want, rel=3e-7)
+    assert abs(got - 1e-3) > 1e-7  # without the 1e-6 the new norm would be c
+    # one factor for every element of every tensor, direction kept
+    out, norm, clipped, f = orc.clip_grad_norm(gs, 0.5 * n)
+    assert clipped and 0.49 < f < 0.5
+    for a, b in zip(out, gs):
+        r = a.astype(np.float64) / b.astype(np.float64)
+        assert np.all(np.abs(r - float(f)) <= float(f) * 2.0 ** -23)
+    assert orc.grad_norm(out) == pytest.approx(0.5 * n * n / (n + 1e-6), rel=1e-6)
