@@ -37,7 +37,10 @@ ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
        "rank8_div", "gpt_residual",
        # the three two-operator expressions again, each as one fused call per
        # direction (fewer bytes: the intermediate is never stored)
-       "xy_plus_x_fused", "attn_scale_mask_fused", "gpt_residual_fused"]
+       "xy_plus_x_fused", "attn_scale_mask_fused", "gpt_residual_fused",
+       # the other reductions: mean of the per-token loss and its gradient,
+       # ClipGradNorm over the GPT configuration's parameter gradients
+       "gpt_loss_mean_clip"]
 ROTATE_BYTES = 1 << 30  # per-workload footprint of the rotating buffer sets
 MAX_SETS = 32
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -215,13 +218,18 @@ def profile_calls(sets, reps, torch):
     spin_total = time.perf_counter() - t0
     recs = zk.profile_read(cap)
     zk.profile_stop()
+    # per call and kernel name: the summed duration of that kernel's launches
+    # in one step (a call may launch one kernel several times)
     out = {i: {} for i in range(ncalls)}
     it = iter(recs)
     for _ in range(reps * len(sets)):
         for i, ks in enumerate(per_call):
+            step = {}
             for k in ks:
                 name, ms = next(it)
                 assert name == k, (name, k)
+                step[k] = step.get(k, 0.0) + ms
+            for k, ms in step.items():
                 out[i].setdefault(k, []).append(ms)
     return out, per_call, enq, spin_total
 
@@ -323,6 +331,7 @@ def main():
            "gpt_residual": Wk.gpt_residual}
     for w in ("xy_plus_x", "attn_scale_mask", "gpt_residual"):
         gen[w + "_fused"] = gen[w]
+    gen["gpt_loss_mean_clip"] = Wk.gpt_loss_mean_clip
     log(f"[bench] device {torch.cuda.get_device_name(0)}; spin check "
         f"{spin_seconds(torch) * 1e3:.1f} ms")
     ceiling = copy_ceiling(torch)

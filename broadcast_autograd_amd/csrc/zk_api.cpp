@@ -5,6 +5,7 @@
 // output written.  The library keeps no state between calls.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -311,10 +312,23 @@ zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad, const float *a,
                                acc_b, workspace, (hipStream_t)stream));
 }
 
-zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
-                             int32_t rank_out, const int64_t *sizes_out,
-                             float *out, void *workspace,
-                             size_t *workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// Product of in's sizes over the dims where the target is 1 or missing:
+// the number of input elements each target element sums.
+int64_t reduced_count(int rin, const int64_t *nin, int rout, const int64_t *nout) {
+  int64_t c = 1;
+  for (int k = 0; k < rin; ++k) {
+    const int ko = k - (rin - rout);
+    if (ko < 0 || nout[ko] == 1) c *= nin[k];
+  }
+  return c;
+}
+
+zk_status reduce_common(const float *in, const zk_desc *din, int32_t rank_out,
+                        const int64_t *sizes_out, float *out, void *workspace,
+                        size_t *workspace_bytes, void *stream, bool mean) {
   if (!workspace_bytes) return ZK_ERR_NULL;
   zk_status s;
   if ((s = check_desc(din))) return s;
@@ -339,7 +353,129 @@ zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
   Ext ews;
   if (need) ews = Ext{(uintptr_t)workspace, (uintptr_t)workspace + need};
   if (ov(eo, ei) || ov(eo, ews) || ov(ews, ei)) return ZK_ERR_ALIAS;
-  return hip_status(launch_reduce(p, in, out, workspace, (hipStream_t)stream));
+  const double count =
+      mean ? (double)reduced_count(din->rank, din->sizes, rank_out, sizes_out) : -1.0;
+  return hip_status(launch_reduce(p, in, out, workspace, (hipStream_t)stream, nullptr, false,
+                                  count));
+}
+
+// Tensor list of zk_grad_norm / zk_clip_grad_norm: sizes non-negative;
+// with `ptrs`, pointers present for non-empty tensors and no two tensors
+// overlapping.
+zk_status check_grad_list(int32_t count, const void *const *grads, const int64_t *numels,
+                          bool ptrs) {
+  if (count < 0) return ZK_ERR_BAD_SIZE;
+  if (count > 0 && !numels) return ZK_ERR_NULL;
+  for (int t = 0; t < count; ++t)
+    if (numels[t] < 0) return ZK_ERR_BAD_SIZE;
+  if (!ptrs) return ZK_OK;
+  if (count > 0 && !grads) return ZK_ERR_NULL;
+  std::vector<std::pair<uintptr_t, uintptr_t>> ext;
+  ext.reserve(count);
+  for (int t = 0; t < count; ++t) {
+    if (numels[t] == 0) continue;
+    if (!grads[t]) return ZK_ERR_NULL;
+    Ext e = ext_dense(grads[t], numels[t]);
+    ext.emplace_back(e.lo, e.hi);
+  }
+  std::sort(ext.begin(), ext.end());
+  for (size_t k = 1; k < ext.size(); ++k)
+    if (ext[k].first < ext[k - 1].second) return ZK_ERR_ALIAS;
+  return ZK_OK;
+}
+
+zk_status norm_common(int32_t count, float *const *grads, const int64_t *numels, bool clip,
+                      float max_norm, float *norm_out, void *workspace,
+                      size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes) return ZK_ERR_NULL;
+  zk_status s;
+  if ((s = check_grad_list(count, (const void *const *)grads, numels, workspace != nullptr)))
+    return s;
+  if (clip && !(max_norm >= 0.0f)) return ZK_ERR_UNSUPPORTED;  // NaN or negative
+  const size_t need = norm_workspace(count, numels);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return ZK_OK;
+  }
+  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  if (!norm_out) return ZK_ERR_NULL;
+  const Ext ew{(uintptr_t)workspace, (uintptr_t)workspace + need};
+  const Ext en = ext_dense(norm_out, 1);
+  if (ov(ew, en)) return ZK_ERR_ALIAS;
+  for (int t = 0; t < count; ++t) {
+    if (numels[t] == 0) continue;
+    const Ext e = ext_dense(grads[t], numels[t]);
+    if (ov(e, ew) || ov(e, en)) return ZK_ERR_ALIAS;
+  }
+  return hip_status(launch_grad_norm(count, grads, numels, norm_out, workspace, clip,
+                                     (double)max_norm, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+zk_status zk_reduce_to_shape(const float *in, const zk_desc *din,
+                             int32_t rank_out, const int64_t *sizes_out,
+                             float *out, void *workspace,
+                             size_t *workspace_bytes, void *stream) {
+  return reduce_common(in, din, rank_out, sizes_out, out, workspace, workspace_bytes, stream,
+                       false);
+}
+
+zk_status zk_mean_to_shape(const float *in, const zk_desc *din, int32_t rank_out,
+                           const int64_t *sizes_out, float *out, void *workspace,
+                           size_t *workspace_bytes, void *stream) {
+  return reduce_common(in, din, rank_out, sizes_out, out, workspace, workspace_bytes, stream,
+                       true);
+}
+
+zk_status zk_mean_bwd(const float *grad, int32_t rank_out, const int64_t *sizes_out,
+                      int32_t rank_in, const int64_t *sizes_in, float *grad_in,
+                      void *stream) {
+  if (rank_out < 0 || rank_out > kMaxDims || rank_in < 0 || rank_in > kMaxDims)
+    return ZK_ERR_RANK;
+  if ((rank_out > 0 && !sizes_out) || (rank_in > 0 && !sizes_in)) return ZK_ERR_NULL;
+  for (int k = 0; k < rank_out; ++k)
+    if (sizes_out[k] < 0) return ZK_ERR_BAD_SIZE;
+  for (int k = 0; k < rank_in; ++k)
+    if (sizes_in[k] < 0) return ZK_ERR_BAD_SIZE;
+  int r;
+  int64_t n[kMaxDims];
+  zk_status s = broadcast_shape(rank_in, sizes_in, rank_out, sizes_out, &r, n);
+  if (s == ZK_ERR_BROADCAST) return ZK_ERR_SHAPE;
+  if (s) return s;
+  if (r != rank_in) return ZK_ERR_SHAPE;
+  for (int k = 0; k < r; ++k)
+    if (n[k] != sizes_in[k]) return ZK_ERR_SHAPE;
+  // grad read as a view of the input's shape: stride 0 on the reduced dims
+  const zk_desc dout = dense_desc(rank_out, sizes_out);
+  zk_desc dg{};
+  dg.rank = rank_in;
+  for (int k = 0; k < rank_in; ++k) {
+    const int ko = k - (rank_in - rank_out);
+    dg.sizes[k] = sizes_in[k];
+    dg.strides[k] = (ko < 0 || sizes_out[ko] == 1) ? 0 : dout.strides[ko];
+  }
+  const int64_t nin = numel(dg);
+  if (nin == 0) return ZK_OK;
+  if (!grad || !grad_in) return ZK_ERR_NULL;
+  if (ov(ext_dense(grad_in, nin), ext_dense(grad, numel(dout)))) return ZK_ERR_ALIAS;
+  const float c32 = (float)reduced_count(rank_in, sizes_in, rank_out, sizes_out);
+  return zk_scalar_fwd(ZK_DIV, ZK_EPI_NONE, grad, &dg, c32, 0, grad_in, stream);
+}
+
+zk_status zk_grad_norm(int32_t count, const float *const *grads, const int64_t *numels,
+                       float *norm_out, void *workspace, size_t *workspace_bytes,
+                       void *stream) {
+  return norm_common(count, const_cast<float *const *>(grads), numels, false, 0.0f, norm_out,
+                     workspace, workspace_bytes, stream);
+}
+
+zk_status zk_clip_grad_norm(int32_t count, float *const *grads, const int64_t *numels,
+                            float max_norm, float *norm_out, void *workspace,
+                            size_t *workspace_bytes, void *stream) {
+  return norm_common(count, grads, numels, true, max_norm, norm_out, workspace,
+                     workspace_bytes, stream);
 }
 
 zk_status zk_scalar_fwd(zk_op op, zk_epi epi, const float *t, const zk_desc *dt,

@@ -632,6 +632,8 @@ struct FinArgs {
   int64_t K, P, per;  // per: partials per thread
   int32_t tpk, kt, has_acc;
   int32_t neg;  // the terms are the negated partials (exact)
+  int32_t has_div;
+  double div;  // has_div: the result is the sum divided by div (a mean)
 };
 
 __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
@@ -663,6 +665,7 @@ __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
     if (q == 0 && ok) {
       double tot = fa.neg ? -sh[kk] : sh[kk];
       if (fa.has_acc) tot += (double)acc[k];
+      if (fa.has_div) tot = tot / fa.div;
       out[k] = (float)tot;
     }
     __syncthreads();  // sh is rewritten by the next group
@@ -702,7 +705,7 @@ static inline unsigned gridn(int64_t n, int64_t per) {
 
 static hipError_t launch_final(const RedPlan &rp, const double *part,
                                const float *acc, float *out, hipStream_t st,
-                               bool neg = false) {
+                               bool neg = false, double mean_count = -1.0) {
   if (rp.kept == 0) return hipSuccess;
   FinArgs fa{};
   fa.neg = neg ? 1 : 0;
@@ -718,6 +721,8 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
   fa.kt = kBlk / tpk;
   fa.per = (rp.partials + tpk - 1) / tpk;
   fa.has_acc = acc != nullptr;
+  fa.has_div = mean_count >= 0.0;
+  fa.div = mean_count;
   ProfScope prof(K_RED_FINAL);
   ZK_LAUNCH(prof, k_red_final, dim3(gridn(rp.kept, fa.kt)), dim3(kBlk), 0, st,
             part, acc, out, fa);
@@ -939,7 +944,8 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
 }
 
 hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
-                         void *ws, hipStream_t st, const float *acc, bool neg) {
+                         void *ws, hipStream_t st, const float *acc, bool neg,
+                         double mean_count) {
   const GcOut none{nullptr, nullptr, 1.f};
   const Canon &c = p.c;
   for (int ri = 0; ri < p.nred; ++ri) {
@@ -994,7 +1000,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipError_t e = launch_final(rp, part, acc, out, st, neg);
+    hipError_t e = launch_final(rp, part, acc, out, st, neg, mean_count);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

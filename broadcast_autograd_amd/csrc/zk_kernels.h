@@ -79,9 +79,34 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
 hipError_t launch_signed(const float *g, int64_t n, float *gc, const float *acc,
                          float sign, hipStream_t st);
 
-// acc (optional) is added to each sum; neg negates the sum first.
+// acc (optional) is added to each sum; neg negates the sum first; a
+// mean_count >= 0 divides each sum by it in binary64 (the mean).
 hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
                          void *ws, hipStream_t st, const float *acc = nullptr,
-                         bool neg = false);
+                         bool neg = false, double mean_count = -1.0);
+
+// ---- global L2 norm / ClipGradNorm (zk_norm.hip)
+constexpr int kNormTab = 128;  // tensors per launch, passed in the kernel arguments
+// Up to kNormTab non-empty dense tensors and the first block of each
+// (2.5 KB of kernel arguments).
+struct NormTab {
+  float *p[kNormTab];
+  int64_t n[kNormTab];
+  uint32_t b0[kNormTab + 1];  // b0[nt] = blocks of this launch
+  int32_t nt;
+  int64_t part0;  // index of this launch's first partial
+};
+// Workspace: one binary64 partial per block of the tensor list.
+struct NormFinArgs {
+  int64_t P;  // partials
+  double max_norm;
+};
+// Most blocks one launch of a table may hold (b0 is 32-bit).
+constexpr int64_t kNormMaxTableBlocks = (int64_t)1 << 30;
+size_t norm_workspace(int count, const int64_t *numels);
+// norm_out: device float.  clip: also scale every tensor in place when the
+// norm exceeds max_norm.
+hipError_t launch_grad_norm(int count, float *const *g, const int64_t *numels, float *norm_out,
+                            void *ws, bool clip, double max_norm, hipStream_t st);
 
 }  // namespace zk

@@ -12,7 +12,7 @@ const char *kernel_name(int32_t k) {
       "bwd_ew_flat",    "bwd_ew_generic", "red_col",   "red_row",
       "red_tile",       "red_generic",   "red_final",  "fwd2_row",
       "fwd2_generic",   "bwd_signed",    "copy_row",   "copy_tile",
-      "copy_generic"};
+      "copy_generic",   "norm_part",     "norm_final", "clip_scale"};
   if (k < 0 || k >= K_COUNT) return "none";
   return names[k];
 }

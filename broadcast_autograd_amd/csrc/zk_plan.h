@@ -40,7 +40,10 @@ enum KernelClass : int32_t {
   K_COPY_ROW = 14,    // materialise a view, rank <= 3, 128-bit output
   K_COPY_TILE = 15,   // materialise a transposed rank-2 view through LDS
   K_COPY_GENERIC = 16,  // materialise anything (rank <= 8)
-  K_COUNT = 17
+  K_NORM_PART = 17,   // global L2 norm: binary64 partial sums of squares
+  K_NORM_FINAL = 18,  // global L2 norm: fixed-order total, sqrt, clip factor
+  K_CLIP_SCALE = 19,  // ClipGradNorm: in-place scaling by the factor
+  K_COUNT = 20
 };
 
 const char *kernel_name(int32_t k);

@@ -318,7 +318,52 @@ class GPTResidualFused(Workload):
         ]
 
 
+# ------------------------------------------------------ other reductions
+
+
+class GPTLossMeanClip(Workload):
+    """The tail of the GPT chapter's training loop: the per-token loss
+    averaged to a scalar and its gradient, then ClipGradNorm(1.0) over every
+    parameter gradient.  The gradients live in one flat buffer (one tensor
+    view per parameter); each step first rewrites them from a pristine copy,
+    standing in for the backward pass that produces them, so that every
+    step's clip scales (the clip leaves the norm just under the threshold)."""
+    name = "gpt_loss_mean_clip"
+
+    def __init__(self, host=None, b=64, t=256, max_norm=1.0):
+        import torch
+        hh = host or W.gpt_loss_mean_clip(b, t)
+        self.host = hh
+        self.loss = torch.from_numpy(hh["loss"]).to("cuda")
+        self.g = torch.from_numpy(np.array(hh["g"], dtype=np.float32)).to("cuda")
+        self.pristine = torch.from_numpy(hh["grads"]).to("cuda")
+        self.grad_params = torch.empty_like(self.pristine)
+        shapes = W.gpt_param_shapes(ctx=t)
+        offs, _ = W.grad_arena_offsets(shapes)
+        self.views = [self.grad_params[o:o + _n(s)].view(s) for o, s in zip(offs, shapes)]
+        self.out = torch.empty((), dtype=torch.float32, device="cuda")
+        self.grad_loss = torch.empty_like(self.loss)
+        self.norm = torch.empty((), dtype=torch.float32, device="cuda")
+        self.ws = _ws(zk.reduce_workspace_bytes(self.loss, ()), torch)
+        self.ws_norm = _ws(zk.norm_workspace_bytes([v.numel() for v in self.views]), torch)
+        nl, na = _n(self.loss.shape), _n(self.pristine.shape)
+        npar = sum(v.numel() for v in self.views)
+        self.calls = [
+            Call("mean(per_token_loss[%d])->loss" % nl, "fwd",
+                 lambda: zk.mean_to_shape(self.loss, (), out=self.out, workspace=self.ws),
+                 [nl], [1]),
+            Call("mean_bwd(g[])->grad_per_token_loss", "bwd",
+                 lambda: zk.mean_bwd(self.g, self.loss.shape, out=self.grad_loss), [1], [nl]),
+            Call("gradients rewritten from a pristine copy (stands in for backward)", "aux",
+                 lambda: zk.materialize(self.pristine, out=self.grad_params), [na], [na]),
+            Call("clip_grad_norm(%d grads, %g)" % (len(self.views), max_norm), "bwd",
+                 lambda: zk.clip_grad_norm(self.views, max_norm, norm_out=self.norm,
+                                           workspace=self.ws_norm),
+                 [npar, npar], [npar, 1]),
+        ]
+
+
 WORKLOAD_CLASSES = {c.name: c for c in (XYPlusX, MLPBiasGelu, AttnScaleMask,
                                         StridedTransposed, Rank8, GPTResidual,
                                         XYPlusXFused, AttnScaleMaskFused,
-                                        GPTResidualFused)}
+                                        GPTResidualFused, GPTLossMeanClip)}

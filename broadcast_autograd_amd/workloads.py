@@ -20,6 +20,8 @@ WORKLOADS = {
     "attn_scale_mask": "scores[8,16,1024,1024] * scale[1,16,1,1] + mask[1,1,1024,1024]",
     "strided_highrank": "a[4096,4096] strides [1,4096] * b[4096]; a[2..9] / b[1,3,1,5,1,7,1,9]",
     "gpt_residual": "h[16,2048,4096] * gamma[4096] + resid[16,2048,4096]",
+    "gpt_loss_mean_clip": "mean of the per-token loss[64*256] and its gradient; "
+                          "ClipGradNorm(1.0) over the GPT configuration's 76 gradients",
 }
 
 
@@ -89,3 +91,42 @@ def rank8(shape_a=(2, 3, 4, 5, 6, 7, 8, 9), shape_b=(1, 3, 1, 5, 1, 7, 1, 9)):
 def gpt_residual(b=16, t=2048, c=4096):
     return dict(h=normal((b, t, c), 5001), gamma=normal((c,), 5002, 1.0, 0.1),
                 resid=normal((b, t, c), 5003), g=normal((b, t, c), 5004))
+
+
+def gpt_param_shapes(vocab=4096, ctx=256, c=384, blocks=6):
+    """Parameter shapes of the GPT training configuration of the GPT chapter
+    ("training configuration": hidden size 384, 6 blocks, sequence length
+    256), in list order: token embedding [V, C] (the output layer reuses it
+    transposed), position embedding [T, C]; per block LayerNorm weight and
+    bias, the attention's QKV projection [C, 3C] and bias, its output
+    projection [C, C] and bias, a second LayerNorm, the FFN's [C, 4C] and
+    bias and [4C, C] and bias; a final LayerNorm.  The vocabulary size is
+    the corpus's and is not printed; 4096 is assumed."""
+    shapes = [(vocab, c), (ctx, c)]
+    for _ in range(blocks):
+        shapes += [(c,), (c,), (c, 3 * c), (3 * c,), (c, c), (c,),
+                   (c,), (c,), (c, 4 * c), (4 * c,), (4 * c, c), (c,)]
+    shapes += [(c,), (c,)]
+    return shapes
+
+
+def grad_arena_offsets(shapes, align=64):
+    """Element offsets of each tensor in one flat gradient buffer, each
+    rounded up to ``align`` elements (256 bytes), and the buffer's size."""
+    offs, pos = [], 0
+    for s in shapes:
+        offs.append(pos)
+        n = int(np.prod(s, dtype=np.int64))
+        pos += (n + align - 1) // align * align
+    return offs, pos
+
+
+def gpt_loss_mean_clip(b=64, t=256):
+    """Per-token loss[b*t] U(0, 10) (positive, like cross-entropy values);
+    the parameter gradients as one flat buffer N(0, 0.01) laid out by
+    grad_arena_offsets (padding included); the loss's upstream gradient 1."""
+    shapes = gpt_param_shapes(ctx=t)
+    _, total = grad_arena_offsets(shapes)
+    return dict(loss=uniform((b * t,), 6001, 0.0, 10.0),
+                grads=normal((total,), 6002, 0.0, 0.01),
+                g=np.array(1.0, dtype=np.float32))

@@ -26,6 +26,7 @@ ERR = {v: k for k, v in STATUS.items()}
 SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
            "zk_reduce_to_shape", "zk_materialize", "zk_binary2_fwd", "zk_binary2_bwd",
            "zk_scalar_fwd", "zk_scalar_bwd", "zk_unary_fwd", "zk_unary_bwd",
+           "zk_mean_to_shape", "zk_mean_bwd", "zk_grad_norm", "zk_clip_grad_norm",
            "zk_status_string", "zk_plan_describe", "zk_kernel_name",
            "zk_profile_start", "zk_profile_stop", "zk_profile_read")
 
@@ -84,6 +85,10 @@ def lib():
         L.zk_unary_bwd.argtypes = [I32, P, P, P, P, P, P]
         L.zk_binary2_fwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P]
         L.zk_binary2_bwd.argtypes = [I32, I32] + [P] * 16
+        L.zk_mean_to_shape.argtypes = [P, P, I32, P, P, P, P, P]
+        L.zk_mean_bwd.argtypes = [P, I32, P, I32, P, P, P]
+        L.zk_grad_norm.argtypes = [I32, P, P, P, P, P, P]
+        L.zk_clip_grad_norm.argtypes = [I32, P, P, F32, P, P, P, P]
         L.zk_status_string.argtypes = [I32]
         L.zk_status_string.restype = ctypes.c_char_p
         L.zk_plan_describe.argtypes = [I32, I32, I32, P, P, P]
@@ -379,6 +384,85 @@ def reduce_to_shape(x, shape, out=None, workspace=None, stream=None):
                                 _ptr(out), _ptr(workspace), ctypes.byref(nbytes),
                                 _stream(stream)), "zk_reduce_to_shape")
     return out
+
+
+def mean_to_shape(x, shape, out=None, workspace=None, stream=None):
+    """Mean of ``x`` over the dims where ``shape`` is 1 or missing (dense
+    row-major result); the workspace is the one reduce_to_shape needs."""
+    import torch
+    shape = tuple(int(s) for s in shape)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    d = desc_of(x)
+    nbytes = ctypes.c_size_t(0)
+    L = lib()
+    if workspace is None:
+        workspace = _workspace(reduce_workspace_bytes(x, shape), x.device)
+    nbytes.value = workspace.numel() * workspace.element_size()
+    _check(L.zk_mean_to_shape(_ptr(x), ctypes.byref(d), len(shape), _i64(shape),
+                              _ptr(out), _ptr(workspace), ctypes.byref(nbytes),
+                              _stream(stream)), "zk_mean_to_shape")
+    return out
+
+
+def mean_bwd(g, shape_in, out=None, stream=None):
+    """Gradient of mean_to_shape: ``g`` (dense, the reduced shape) divided by
+    the count and repeated over ``shape_in``."""
+    import torch
+    shape_in = tuple(int(s) for s in shape_in)
+    if out is None:
+        out = torch.empty(shape_in, dtype=torch.float32, device=g.device)
+    gs = tuple(g.shape)
+    _check(lib().zk_mean_bwd(_ptr(g), len(gs), _i64(gs), len(shape_in), _i64(shape_in),
+                             _ptr(out), _stream(stream)), "zk_mean_bwd")
+    return out
+
+
+def _grad_list(tensors):
+    ptrs = (ctypes.c_void_p * max(1, len(tensors)))(
+        *[t.data_ptr() if t.numel() else None for t in tensors])
+    return ptrs, _i64([t.numel() for t in tensors])
+
+
+def norm_workspace_bytes(numels):
+    """Workspace zk_grad_norm / zk_clip_grad_norm need for these element
+    counts (no launch)."""
+    nbytes = ctypes.c_size_t(0)
+    _check(lib().zk_grad_norm(len(numels), None, _i64(numels), None, None,
+                              ctypes.byref(nbytes), None), "zk_grad_norm(query)")
+    return nbytes.value
+
+
+def _norm_call(tensors, clip, max_norm, norm_out, workspace, stream):
+    import torch
+    dev = tensors[0].device if tensors else torch.device("cuda")
+    if norm_out is None:
+        norm_out = torch.empty((), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _workspace(norm_workspace_bytes([t.numel() for t in tensors]), dev)
+    ptrs, ns = _grad_list(tensors)
+    nbytes = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    L = lib()
+    if clip:
+        _check(L.zk_clip_grad_norm(len(tensors), ptrs, ns, float(max_norm), _ptr(norm_out),
+                                   _ptr(workspace), ctypes.byref(nbytes), _stream(stream)),
+               "zk_clip_grad_norm")
+    else:
+        _check(L.zk_grad_norm(len(tensors), ptrs, ns, _ptr(norm_out), _ptr(workspace),
+                              ctypes.byref(nbytes), _stream(stream)), "zk_grad_norm")
+    return norm_out
+
+
+def grad_norm(tensors, norm_out=None, workspace=None, stream=None):
+    """Global L2 norm of dense fp32 tensors, as a 0-d device tensor."""
+    return _norm_call(tensors, False, 0.0, norm_out, workspace, stream)
+
+
+def clip_grad_norm(tensors, max_norm, norm_out=None, workspace=None, stream=None):
+    """ClipGradNorm in place: scales every tensor by max_norm / (norm + 1e-6)
+    when the global norm exceeds max_norm.  Returns the norm (0-d device
+    tensor; nothing is synchronised)."""
+    return _norm_call(tensors, True, max_norm, norm_out, workspace, stream)
 
 
 def plan_describe(kind, op, da, db, epi="none"):

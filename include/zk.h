@@ -282,6 +282,74 @@ zk_status zk_binary2_bwd(zk_op op1, zk_op op2, const float *grad,
                          void *workspace, size_t *workspace_bytes,
                          void *stream);
 
+/*
+ * Mean back to a shape (GPU chapter, "reduction": the mean is one of the
+ * reductions that combine many inputs into few outputs; GPT chapter,
+ * "training loop": the per-token loss is averaged over dim 0):
+ *   out[j] = (sum of the in elements that map to j) / count,
+ * count = the product of in's sizes over the dims where the target is 1 or
+ * missing.  The sum is accumulated in binary64 in an order fixed by the
+ * shapes, divided by the count in binary64 and rounded once to binary32.
+ * An empty reduced dim gives NaN (0 / 0).  Arguments, workspace protocol
+ * (the same size as zk_reduce_to_shape), aliasing and errors as
+ * zk_reduce_to_shape.
+ */
+zk_status zk_mean_to_shape(const float *in, const zk_desc *din, int32_t rank_out,
+                           const int64_t *sizes_out, float *out, void *workspace,
+                           size_t *workspace_bytes, void *stream);
+
+/*
+ * Gradient of zk_mean_to_shape (Autograd chapter, "chain rule": upstream
+ * gradient times the local derivative 1 / count):
+ *   grad_in[i] = grad[j(i)] / count,
+ * one binary32 division by the count rounded to binary32, j(i) the output
+ * element that input element i is averaged into.
+ *   grad    : dense row-major, shape (rank_out, sizes_out); that shape must
+ *             broadcast to (rank_in, sizes_in) with the latter as the
+ *             result, else ZK_ERR_SHAPE
+ *   grad_in : dense row-major, shape (rank_in, sizes_in), caller-allocated
+ * No workspace.  An empty grad_in launches nothing.  Any overlap of grad_in
+ * with grad is ZK_ERR_ALIAS.
+ * Errors: ZK_ERR_NULL, ZK_ERR_RANK, ZK_ERR_BAD_SIZE, ZK_ERR_SHAPE,
+ *         ZK_ERR_ALIAS, ZK_ERR_HIP.
+ */
+zk_status zk_mean_bwd(const float *grad, int32_t rank_out, const int64_t *sizes_out,
+                      int32_t rank_in, const int64_t *sizes_in, float *grad_in,
+                      void *stream);
+
+/*
+ * Global L2 norm of a list of gradients (GPT chapter, "training loop": the
+ * norm of all parameter gradients taken together), and ClipGradNorm: when
+ * that norm exceeds max_norm, every gradient is multiplied by the one factor
+ * max_norm / (norm + 1e-6), which keeps the overall direction.
+ *   count     : number of tensors, >= 0
+ *   grads     : host array of `count` device pointers, each a dense binary32
+ *               tensor of numels[t] elements (any 4-byte alignment)
+ *   numels    : host array of element counts, each >= 0
+ *   norm_out  : device pointer to one float: the norm, rounded to binary32
+ *   workspace : device scratch owned by the caller; NULL queries
+ *               *workspace_bytes (the size depends on numels only; grads
+ *               and norm_out are not read then), as in zk_binary_bwd
+ * Squares are summed in binary64 in an order fixed by numels, the square
+ * root taken in binary64 (bitwise reproducible).  zk_clip_grad_norm then
+ * decides on the device, without a host synchronisation: if the binary64
+ * norm is greater than max_norm, factor = max_norm / (norm + 1e-6) computed
+ * in binary64 and rounded to binary32, and every element becomes
+ * g * factor (one binary32 multiply) in place; otherwise nothing is
+ * written to the gradients.
+ * Aliasing: the tensors may not overlap each other, norm_out or the
+ * workspace (ZK_ERR_ALIAS).
+ * Errors: ZK_ERR_NULL, ZK_ERR_BAD_SIZE (negative count or numel),
+ *         ZK_ERR_ALIAS, ZK_ERR_WORKSPACE, ZK_ERR_HIP; zk_clip_grad_norm
+ *         also ZK_ERR_UNSUPPORTED for a max_norm that is negative or NaN.
+ */
+zk_status zk_grad_norm(int32_t count, const float *const *grads, const int64_t *numels,
+                       float *norm_out, void *workspace, size_t *workspace_bytes,
+                       void *stream);
+zk_status zk_clip_grad_norm(int32_t count, float *const *grads, const int64_t *numels,
+                            float max_norm, float *norm_out, void *workspace,
+                            size_t *workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *zk_status_string(zk_status s);
 

@@ -218,6 +218,74 @@ def test_reduce_validation_errors(L):
     assert red((6,), ws=FW, out=ctypes.c_void_p(FW.value + 8))[0] == "ZK_ERR_ALIAS"
 
 
+def test_mean_validation_errors(L):
+    """zk_mean_to_shape shares zk_reduce_to_shape's checks and workspace size;
+    zk_mean_bwd checks the shapes before anything is launched."""
+    d = zk.make_desc((4, 6))
+
+    def mean(shape, ws=None, wsb=1 << 30, out=FO):
+        n = ctypes.c_size_t(wsb)
+        arr = (ctypes.c_int64 * max(8, len(shape)))(*shape)
+        return zk.STATUS[L.zk_mean_to_shape(FA, ctypes.byref(d), len(shape), arr, out,
+                                            ws, ctypes.byref(n), None)], n.value
+
+    assert mean((5,))[0] == "ZK_ERR_SHAPE"
+    st, need = mean((6,))
+    n2 = ctypes.c_size_t(0)
+    L.zk_reduce_to_shape(FA, ctypes.byref(d), 1, zk._i64((6,)), FO, None, ctypes.byref(n2),
+                         None)
+    assert st == "ZK_OK" and need == n2.value
+    assert mean((6,), ws=FW, wsb=need - 1)[0] == "ZK_ERR_WORKSPACE"
+    assert mean((6,), ws=FW, out=FA)[0] == "ZK_ERR_ALIAS"
+
+    def mbwd(sout, sin, g=FG, out=FO):
+        return zk.STATUS[L.zk_mean_bwd(g, len(sout), zk._i64(sout), len(sin), zk._i64(sin),
+                                       out, None)]
+
+    assert mbwd((5,), (4, 6)) == "ZK_ERR_SHAPE"
+    assert mbwd((2, 4, 6), (4, 6)) == "ZK_ERR_SHAPE"    # the target grows the shape
+    assert mbwd((6,), (1,) * 9) == "ZK_ERR_RANK"
+    assert mbwd((-1,), (4, 6)) == "ZK_ERR_BAD_SIZE"
+    assert mbwd((6,), (4, 6), g=None) == "ZK_ERR_NULL"
+    assert mbwd((6,), (4, 6), out=ctypes.c_void_p(FG.value + 8)) == "ZK_ERR_ALIAS"
+    assert mbwd((6,), (0, 6), g=None, out=None) == "ZK_OK"  # empty: nothing launched
+
+
+def test_grad_norm_validation_errors(L):
+    """Queries need only the counts; every error returns before a launch."""
+    def q(ns):
+        n = ctypes.c_size_t(0)
+        st = L.zk_grad_norm(len(ns), None, zk._i64(ns), None, None, ctypes.byref(n), None)
+        return zk.STATUS[st], n.value
+
+    st, need = q([12, 8192, 8193, 0])
+    assert st == "ZK_OK" and need == 8 * 4
+    assert q([])[1] == 8
+    assert q([-1])[0] == "ZK_ERR_BAD_SIZE"
+
+    def call(ptrs, ns, ws=FW, wsb=1 << 30, norm=FO, clip=None):
+        arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[p.value if p else None for p in ptrs])
+        n = ctypes.c_size_t(wsb)
+        if clip is None:
+            st = L.zk_grad_norm(len(ptrs), arr, zk._i64(ns), norm, ws, ctypes.byref(n), None)
+        else:
+            st = L.zk_clip_grad_norm(len(ptrs), arr, zk._i64(ns), clip, norm, ws,
+                                     ctypes.byref(n), None)
+        return zk.STATUS[st]
+
+    assert call([FA, FB], [100, 100], wsb=8) == "ZK_ERR_WORKSPACE"
+    assert call([FA, None], [100, 100]) == "ZK_ERR_NULL"
+    assert call([FA, FB], [100, 100], norm=None) == "ZK_ERR_NULL"
+    # overlapping tensors, a tensor over the workspace or over norm_out
+    assert call([FA, ctypes.c_void_p(FA.value + 396)], [100, 100]) == "ZK_ERR_ALIAS"
+    assert call([FA, FB], [100, 100], ws=ctypes.c_void_p(FB.value + 64)) == "ZK_ERR_ALIAS"
+    assert call([FA, FB], [100, 100], norm=ctypes.c_void_p(FA.value + 4)) == "ZK_ERR_ALIAS"
+    assert call([FA, FB], [100, 100], clip=-1.0) == "ZK_ERR_UNSUPPORTED"
+    assert call([FA, FB], [100, 100], clip=float("nan")) == "ZK_ERR_UNSUPPORTED"
+    assert L.zk_grad_norm(-1, None, None, FO, FW, ctypes.byref(ctypes.c_size_t(1 << 20)),
+                          None) == zk.ERR["ZK_ERR_BAD_SIZE"]
+
+
 WORKLOAD_PLANS = [
     # (kind, op, epi, a (sizes, strides), b (sizes, strides), kernel, canonical sizes, b strides)
     ("fwd", "mul", "none", ((64, 128, 256), None), ((128, 1), None), "fwd_row",
