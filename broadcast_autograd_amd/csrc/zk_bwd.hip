@@ -27,8 +27,6 @@
 namespace zk {
 
 constexpr int kBlk = 256;
-// Waves per red_col block when its waves combine their sums in LDS.
-constexpr int kColWaves = 16;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -271,6 +269,7 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   // epilogue, whose arithmetic is long enough per row (measured: the
   // [4096, 1024] GeLU step is ~10% faster than with two)
   constexpr int U = EPI == ZK_EPI_GELU ? 1 : 2;
+  constexpr bool PF = false;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l = threadIdx.x & 63;
   const int64_t p = blockIdx.x / ca.colblocks;
@@ -285,46 +284,68 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   const int64_t r0 = (p * NW + w) * ca.rcw;
   const int64_t r1 = r0 + ca.rcw < ca.R ? r0 + ca.rcw : ca.R;
   double s[4] = {0.0, 0.0, 0.0, 0.0};
-  if (active) {
-    for (int64_t rb = r0; rb < r1; rb += U) {
-      float4 vg[U], vb[U], va[U];
+  auto load = [&](int64_t rb, float4 *vg, float4 *vb, float4 *va) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t r = rb + u;
-        if (r < r1) {
-          const int64_t i = r * ca.K + c;
-          vg[u] = ld4_nt(g + i);
-          if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
-          if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = rb + u;
+      if (r < r1) {
+        const int64_t i = r * ca.K + c;
+        vg[u] = ld4_nt(g + i);
+        if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
+        if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
+      }
+    }
+  };
+  auto process = [&](int64_t rb, const float4 *vg, const float4 *vb, const float4 *va) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = rb + u;
+      if (r < r1) {
+        const int64_t i = r * ca.K + c;
+        float gv[4], x[4], y[4], tb[4];
+        double ts[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          gv[k] = el(vg[u], k);
+          const float bv = NEED_BIG ? el(vb[u], k) : 0.f;
+          x[k] = SIDE == 0 ? sv[k] : bv;
+          y[k] = SIDE == 0 ? bv : sv[k];
+        }
+        terms2_w<OP, EPI, SIDE, 4>(gv, x, y, ts, tb);
+        float4 ob;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          s[k] += ts[k];
+          float t = tb[k];
+          if constexpr (ACC == 1) t = gv[k] + t;
+          if constexpr (ACC == 2) t = el(va[u], k) + t;
+          el(ob, k) = t;
+        }
+        if (ca.write_big) st4_nt(gbig + i, ob);
+        if (gco.p) gc_store4(gco, i, vg[u]);
+      }
+    }
+  };
+  if (active) {
+    float4 vg[U], vb[U], va[U];
+    if constexpr (PF) {
+      // the next rows' loads are issued before this row's arithmetic
+      if (r0 < r1) load(r0, vg, vb, va);
+      for (int64_t rb = r0; rb < r1; rb += U) {
+        float4 ng[U], nb[U], na[U];
+        if (rb + U < r1) load(rb + U, ng, nb, na);
+        process(rb, vg, vb, va);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          vg[u] = ng[u];
+          if constexpr (NEED_BIG) vb[u] = nb[u];
+          if constexpr (ACC == 2) va[u] = na[u];
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t r = rb + u;
-        if (r < r1) {
-          const int64_t i = r * ca.K + c;
-          float gv[4], x[4], y[4], tb[4];
-          double ts[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            gv[k] = el(vg[u], k);
-            const float bv = NEED_BIG ? el(vb[u], k) : 0.f;
-            x[k] = SIDE == 0 ? sv[k] : bv;
-            y[k] = SIDE == 0 ? bv : sv[k];
-          }
-          terms2_w<OP, EPI, SIDE, 4>(gv, x, y, ts, tb);
-          float4 ob;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            s[k] += ts[k];
-            float t = tb[k];
-            if constexpr (ACC == 1) t = gv[k] + t;
-            if constexpr (ACC == 2) t = el(va[u], k) + t;
-            el(ob, k) = t;
-          }
-          if (ca.write_big) st4_nt(gbig + i, ob);
-          if (gco.p) gc_store4(gco, i, vg[u]);
-        }
+    } else {
+      for (int64_t rb = r0; rb < r1; rb += U) {
+        load(rb, vg, vb, va);
+        process(rb, vg, vb, va);
       }
     }
   }
@@ -703,6 +724,17 @@ static inline unsigned gridn(int64_t n, int64_t per) {
   return (unsigned)(g < kMaxGrid ? g : kMaxGrid);
 }
 
+// red_col waves per block, as planned (kColWavesFew / kColWavesMany).
+template <class Fn>
+static hipError_t with_col_waves(int nw, Fn fn) {
+  switch (nw) {
+    case 1: return fn(IC<1>{});
+    case 4: return fn(IC<4>{});
+    case 16: return fn(IC<16>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
 static hipError_t launch_final(const RedPlan &rp, const double *part,
                                const float *acc, float *out, hipStream_t st,
                                bool neg = false, double mean_count = -1.0) {
@@ -865,14 +897,12 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             unsigned grid = (unsigned)(ca.colblocks * rp.partials);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
-              if (rp.nw == 1)
-                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, 1>), dim3(grid), dim3(64), 0, st, g,
-                          big, small, gbig, accbig, part, ca, go);
-              else
-                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, kColWaves>), dim3(grid),
-                          dim3(64 * kColWaves), 0, st, g, big, small, gbig, accbig, part, ca,
-                          go);
-              return hipGetLastError();
+              return with_col_waves(rp.nw, [&](auto Wc) -> hipError_t {
+                constexpr int NW = decltype(Wc)::value;
+                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, NW>), dim3(grid), dim3(64 * NW), 0,
+                          st, g, big, small, gbig, accbig, part, ca, go);
+                return hipGetLastError();
+              });
             });
           }
           case K_RED_ROW: {
@@ -963,13 +993,14 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ca.colblocks = (ca.K + 255) / 256;
           ca.write_big = 0;
           const unsigned grid = (unsigned)(ca.colblocks * rp.partials);
-          if (rp.nw == 1)
-            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, 1>), dim3(grid), dim3(64), 0,
-                      st, in, nullptr, nullptr, nullptr, nullptr, part, ca, none);
-          else
-            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, kColWaves>), dim3(grid),
-                      dim3(64 * kColWaves), 0, st, in, nullptr, nullptr, nullptr, nullptr, part,
-                      ca, none);
+          hipError_t e = with_col_waves(rp.nw, [&](auto Wc) -> hipError_t {
+            constexpr int NW = decltype(Wc)::value;
+            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, NW>), dim3(grid),
+                      dim3(64 * NW), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ca,
+                      none);
+            return hipGetLastError();
+          });
+          if (e != hipSuccess) return e;
           break;
         }
         case K_RED_ROW: {

@@ -25,7 +25,14 @@ constexpr int kBlock = 256;
 // read or written once also carry the non-temporal hint.  With the GeLU
 // epilogue each block first copies the 5.4 KB erfc table into LDS, so a
 // block takes two vectors per lane to halve that traffic.
-constexpr int row_unroll(int epi) { return epi == ZK_EPI_GELU ? 2 : 1; }
+constexpr int row_unroll(int epi) { (void)epi; return 1; }
+// The GeLU row kernel (long arithmetic per element, 64 VGPRs) runs a grid of
+// 8 blocks per CU (all resident at once) that loops over the tiles and
+// issues the next tile's loads before the current tile's arithmetic.
+// Measured on the [4096, 1024] step against one tile per block with two
+// vectors per lane: 10.1 against 11.0 us.
+constexpr bool kRowPrefetch = true;
+constexpr int kRowGeluBlocksPerCU = 8;
 
 // Launches give one block per tile; kernels loop over tiles with a grid
 // stride, so a grid capped here still covers any size.  (A dispatch counts
@@ -162,7 +169,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
                                                     const float *small,
                                                     float *out, RowArgs ra) {
   __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
-  if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   constexpr int U = row_unroll(EPI);
   constexpr I tile = (I)kBlock * U * VEC;
   const I n = (I)ra.numel;
@@ -234,12 +240,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
       }
     };
-    for (I t = (I)blockIdx.x; t < ntiles; t += (I)gridDim.x) {
-      float4 vb[U], vs[U];
-      load(t, vb, vs);
-      process(t, vb, vs);
+    // The first tile's loads are issued before the GeLU table is staged in
+    // LDS, so the two latencies overlap.
+    float4 vb[U], vs[U];
+    I t = (I)blockIdx.x;
+    if (t < ntiles) load(t, vb, vs);
+    if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
+    for (; t < ntiles; t += (I)gridDim.x) {
+      if constexpr (kRowPrefetch && EPI == ZK_EPI_GELU) {
+        // the next tile's loads are issued before this tile's arithmetic
+        float4 nb[U], ns[U];
+        const I tn = t + (I)gridDim.x;
+        if (tn < ntiles) load(tn, nb, ns);
+        process(t, vb, vs);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          vb[u] = nb[u];
+          vs[u] = ns[u];
+        }
+      } else {
+        if (t != (I)blockIdx.x) load(t, vb, vs);
+        process(t, vb, vs);
+      }
     }
   } else {
+    if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
     // 64-bit loop counter: i + stride may pass 2^31 even when n does not
     for (int64_t i64 = (int64_t)blockIdx.x * kBlock + threadIdx.x; i64 < (int64_t)n;
          i64 += (int64_t)gridDim.x * kBlock) {
@@ -656,6 +681,21 @@ __global__ __launch_bounds__(kBlock) void k_copy_generic(const float *in, float 
 }
 
 // -------------------------------------------------------------- launcher
+// Compute units of the current device (queried once per process).
+static int cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 static inline unsigned grid_of(int64_t n, int64_t per_block) {
   const int64_t g = (n + per_block - 1) / per_block;
   return (unsigned)(g < kMaxBlocks ? g : kMaxBlocks);
@@ -702,6 +742,10 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
           using I = std::conditional_t<decltype(Ic)::value != 0, int64_t, int32_t>;
           int64_t blocks = grid_of(c.numel, kBlock * row_unroll(EPI) * VEC);
           if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+          if (EPI == ZK_EPI_GELU && kRowGeluBlocksPerCU > 0) {
+            const int64_t cap = (int64_t)kRowGeluBlocksPerCU * cu_count();
+            if (blocks > cap) blocks = cap;
+          }
           ZK_LAUNCH(prof, (k_fwd_row<OP, EPI, VEC, SM, SW, I>), dim3((unsigned)blocks),
                     dim3(kBlock), 0, st,
                     big, small, out, ra);
