@@ -439,6 +439,92 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
   }
 }
 
+// ------------------------------------------------------------- red_rowd
+// The [R1, K, R0] pattern of red_row in one pass when a kept element has
+// few terms (T = R1 * R0, 2048..16384): block k owns kept element k, its
+// 1024 lanes hold every term's loads at once (U vectors each), and the
+// block's fixed-order sum is finished in place (sign, acc, divisor) and
+// rounded once, so no partials and no stage-2 launch.
+struct RowDirArgs {
+  int64_t R0, K, T, ss;
+  int32_t write_big;
+  int32_t neg, has_div;
+  double div;
+};
+constexpr int kDirBlk = 1024;
+
+template <int OP, int EPI, int SIDE, int ACC, int U>
+__global__ __launch_bounds__(kDirBlk) void k_red_rowd(
+    const float *g, const float *big, const float *small, float *gbig,
+    const float *accbig, float *out, const float *acc, RowDirArgs ra, GcOut gco) {
+  constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
+  constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
+  __shared__ double sh[kDirBlk / 64];
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int64_t k = blockIdx.x; k < ra.K; k += gridDim.x) {
+    const float sv = NEED_SMALL ? small[k * ra.ss] : 0.f;
+    double s = 0.0;
+    for (int64_t t0 = 0; t0 < ra.T; t0 += (int64_t)kDirBlk * 4 * U) {
+      float4 vg[U], vb[U], va[U];
+      int64_t idx[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t t = t0 + 4 * ((int64_t)threadIdx.x + (int64_t)kDirBlk * u);
+        idx[u] = -1;
+        if (t < ra.T) {
+          // R0 % 4 == 0, so the 4 terms t..t+3 lie in one row r1
+          const int64_t r1 = t / ra.R0;
+          const int64_t i = (r1 * ra.K + k) * ra.R0 + (t - r1 * ra.R0);
+          idx[u] = i;
+          vg[u] = ld4_nt(g + i);
+          if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
+          if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (idx[u] >= 0) {
+          const int64_t i = idx[u];
+          float gv[4], x[4], y[4], tb[4];
+          double ts[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gv[q] = el(vg[u], q);
+            const float bv = NEED_BIG ? el(vb[u], q) : 0.f;
+            x[q] = SIDE == 0 ? sv : bv;
+            y[q] = SIDE == 0 ? bv : sv;
+          }
+          terms2_w<OP, EPI, SIDE, 4>(gv, x, y, ts, tb);
+          float4 ob;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            s += ts[q];
+            float tq = tb[q];
+            if constexpr (ACC == 1) tq = gv[q] + tq;
+            if constexpr (ACC == 2) tq = el(va[u], q) + tq;
+            el(ob, q) = tq;
+          }
+          if (ra.write_big) st4_nt(gbig + i, ob);
+          if (gco.p) gc_store4(gco, i, vg[u]);
+        }
+      }
+    }
+    s = wave_sum(s);
+    if (l == 0) sh[w] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double tot = 0.0;
+#pragma unroll
+      for (int j = 0; j < kDirBlk / 64; ++j) tot += sh[j];
+      if (ra.neg) tot = -tot;
+      if (acc) tot += (double)acc[k];
+      if (ra.has_div) tot = tot / ra.div;
+      out[k] = (float)tot;
+    }
+    __syncthreads();  // sh is rewritten for the next kept element
+  }
+}
+
 // -------------------------------------------------------------- red_tile
 // [R, K]; the full operand F[i, j] is at i + j*ld (transposed view); g and
 // the full operand's gradient are dense [R, K].  Block = 64 columns x a
@@ -735,6 +821,45 @@ static hipError_t with_col_waves(int nw, Fn fn) {
   }
 }
 
+// One-pass row reduction (red_rowd): stage 1 and the final rounding.
+template <int OP, int EPI, int S, int A>
+static hipError_t launch_rowd(const RedPlan &rp, const Canon &c, int sw, const float *g,
+                              const float *big, const float *small, float *gbig,
+                              const float *accbig, float *out, const float *acc,
+                              bool write_big, bool neg, double mean_count, GcOut go,
+                              hipStream_t st) {
+  if (rp.kept == 0) return hipSuccess;
+  RowDirArgs ra{};
+  const int R = c.rank;
+  ra.R0 = c.n[R - 1];
+  ra.K = rp.kept;
+  ra.T = rp.red;
+  ra.ss = (R >= 2 && small) ? c.s[1 + sw][R - 2] : 0;
+  ra.write_big = write_big ? 1 : 0;
+  ra.neg = neg ? 1 : 0;
+  ra.has_div = mean_count >= 0.0 ? 1 : 0;
+  ra.div = mean_count;
+  const unsigned grid = gridn(rp.kept, 1);
+  ProfScope prof(K_RED_ROWD);
+  switch (rp.chunk) {
+    case 1:
+      ZK_LAUNCH(prof, (k_red_rowd<OP, EPI, S, A, 1>), dim3(grid), dim3(kDirBlk), 0, st, g, big,
+                small, gbig, accbig, out, acc, ra, go);
+      break;
+    case 2:
+      ZK_LAUNCH(prof, (k_red_rowd<OP, EPI, S, A, 2>), dim3(grid), dim3(kDirBlk), 0, st, g, big,
+                small, gbig, accbig, out, acc, ra, go);
+      break;
+    case 4:
+      ZK_LAUNCH(prof, (k_red_rowd<OP, EPI, S, A, 4>), dim3(grid), dim3(kDirBlk), 0, st, g, big,
+                small, gbig, accbig, out, acc, ra, go);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 static hipError_t launch_final(const RedPlan &rp, const double *part,
                                const float *acc, float *out, hipStream_t st,
                                bool neg = false, double mean_count = -1.0) {
@@ -763,6 +888,132 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
 
 // Split the canonical dims into kept / reduced lists for the gather kernel.
 // kept_op: stride set of the reduced gradient (0 where reduced).
+// ------------------------------------------------------------- red_gend
+// Any reduction pattern in one pass when a kept element has 32..4096 terms:
+// WPK waves per kept element (one wave, or the whole 4-wave block beyond 128
+// terms) walk its terms (thread j takes terms j, j + 64 WPK, ...), decoding
+// offsets as red_generic does, write the full-shape operand's gradient at
+// the elements they visit when asked (each element of the output space
+// belongs to exactly one kept element), and finish the sum themselves
+// (sign, acc, divisor; rounded once): no partials, no stage 2, no separate
+// element-wise pass.
+struct GenDirArgs {
+  GenArgs ga;
+  int32_t write_big, big_acc;  // big_acc: 0 none, 1 acc is g, 2 a buffer
+  int32_t neg, has_div;
+  double div;
+};
+
+template <int OP, int EPI, int WHICH, int IDENT, int WPK, typename I>
+__global__ __launch_bounds__(kBlk) void k_red_gend(const float *g, const float *a,
+                                                   const float *b, float *gbig,
+                                                   const float *accbig, float *out,
+                                                   const float *acc, GenDirArgs da) {
+  const GenArgs &ga = da.ga;
+  // operands either rule reads (the full operand's gradient may be written)
+  constexpr bool RA = !IDENT && (reads_x<OP, EPI, 0>() || reads_x<OP, EPI, 1>());
+  constexpr bool RB = !IDENT && (reads_y<OP, EPI, 0>() || reads_y<OP, EPI, 1>());
+  constexpr int KPB = (kBlk / 64) / WPK;  // kept elements per block
+  constexpr int TPK = 64 * WPK;           // threads per kept element
+  __shared__ double sh[kBlk / 64];
+  const int w = threadIdx.x >> 6;
+  const int j = threadIdx.x % TPK;  // thread within its kept element
+  auto decode_r = [&](I tt, I &dg, I &dA, I &dB) {
+    I rest = tt;
+    dg = 0;
+    dA = 0;
+    dB = 0;
+#pragma unroll
+    for (int d = kMaxDims - 1; d >= 0; --d) {
+      if (d < ga.nr) {
+        const I n = (I)ga.rn[d];
+        const I q = rest / n, c = rest - q * n;
+        dg += c * (I)ga.rs[0][d];
+        dA += c * (I)ga.rs[1][d];
+        dB += c * (I)ga.rs[2][d];
+        rest = q;
+      }
+    }
+  };
+  for (int64_t kb = (int64_t)blockIdx.x * KPB; kb < ga.K; kb += (int64_t)gridDim.x * KPB) {
+    const int64_t k64 = kb + threadIdx.x / TPK;
+    const bool kok = k64 < ga.K;
+    const I k = (I)(kok ? k64 : 0);
+    I og = 0, oa = 0, ob = 0;
+    {
+      I rest = k;
+#pragma unroll
+      for (int d = kMaxDims - 1; d >= 0; --d) {
+        if (d < ga.nk) {
+          const I n = (I)ga.kn[d];
+          const I q = rest / n, c = rest - q * n;
+          og += c * (I)ga.ks[0][d];
+          oa += c * (I)ga.ks[1][d];
+          ob += c * (I)ga.ks[2][d];
+          rest = q;
+        }
+      }
+    }
+    double s = 0.0;
+    // two terms per trip, their loads issued together
+    for (I t0 = (I)j; kok && t0 < (I)ga.red; t0 += 2 * TPK) {
+      I ig[2], ia[2], ib[2];
+      float gv[2], x[2], y[2];
+      bool ok[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const I tt = t0 + (I)(u * TPK);
+        ok[u] = tt < (I)ga.red;
+        I dg, dA, dB;
+        decode_r(ok[u] ? tt : (I)0, dg, dA, dB);
+        ig[u] = og + dg;
+        ia[u] = oa + dA;
+        ib[u] = ob + dB;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (ok[u]) {
+          gv[u] = g[ig[u]];
+          x[u] = RA ? a[ia[u]] : 0.f;
+          y[u] = RB ? b[ib[u]] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!ok[u]) continue;
+        if constexpr (IDENT) {
+          s += (double)gv[u];
+        } else {
+          double ts;
+          float tb;
+          terms2<OP, EPI, WHICH>(gv[u], x[u], y[u], ts, tb);
+          s += ts;
+          if (da.write_big) {
+            if (da.big_acc == 1) tb = gv[u] + tb;
+            else if (da.big_acc == 2) tb = accbig[ig[u]] + tb;
+            gbig[ig[u]] = tb;
+          }
+        }
+      }
+    }
+    s = wave_sum(s);
+    if constexpr (WPK > 1) {
+      if ((threadIdx.x & 63) == 0) sh[w] = s;
+      __syncthreads();
+      s = 0.0;
+#pragma unroll
+      for (int q = 0; q < WPK; ++q) s += sh[q];
+      __syncthreads();  // sh is rewritten for the next kept element
+    }
+    if (j == 0 && kok) {
+      double tot = da.neg ? -s : s;
+      if (acc) tot += (double)acc[k];
+      if (da.has_div) tot = tot / da.div;
+      out[k] = (float)tot;
+    }
+  }
+}
+
 static GenArgs make_gen(const Canon &c, int kept_op, int src_op, int a_op,
                         int b_op, const RedPlan &rp) {
   GenArgs ga{};
@@ -783,6 +1034,50 @@ static GenArgs make_gen(const Canon &c, int kept_op, int src_op, int a_op,
   ga.chunk = rp.chunk;
   ga.red = rp.red;
   return ga;
+}
+
+// One-pass gather reduction (red_gend).
+static hipError_t launch_gend(const RedPlan &rp, const Canon &c, bool idx64, int kept_op,
+                              int a_op, int b_op, zk_op op, zk_epi epi, bool ident, int which,
+                              const float *g, const float *a, const float *b, float *gbig,
+                              const float *accbig, int big_acc, bool write_big, float *out,
+                              const float *acc, bool neg, double mean_count, hipStream_t st) {
+  if (rp.kept == 0) return hipSuccess;
+  GenDirArgs da{};
+  da.ga = make_gen(c, kept_op, 0, a_op, b_op, rp);
+  da.write_big = write_big ? 1 : 0;
+  da.big_acc = big_acc;
+  da.neg = neg ? 1 : 0;
+  da.has_div = mean_count >= 0.0 ? 1 : 0;
+  da.div = mean_count;
+  // the whole block per kept element beyond 128 terms, else a wave
+  const bool whole = rp.red > 128;
+  const unsigned grid = gridn(rp.kept, whole ? 1 : kBlk / 64);
+  ProfScope prof(K_RED_GEND);
+  auto go = [&](auto OPc, auto EPIc, auto Wc, auto IDc) -> hipError_t {
+    constexpr int OP = decltype(OPc)::value, EPI = decltype(EPIc)::value;
+    constexpr int W = decltype(Wc)::value, ID = decltype(IDc)::value;
+    if (idx64) {
+      if (whole)
+        ZK_LAUNCH(prof, (k_red_gend<OP, EPI, W, ID, kBlk / 64, int64_t>), dim3(grid),
+                  dim3(kBlk), 0, st, g, a, b, gbig, accbig, out, acc, da);
+      else
+        ZK_LAUNCH(prof, (k_red_gend<OP, EPI, W, ID, 1, int64_t>), dim3(grid), dim3(kBlk), 0,
+                  st, g, a, b, gbig, accbig, out, acc, da);
+    } else {
+      if (whole)
+        ZK_LAUNCH(prof, (k_red_gend<OP, EPI, W, ID, kBlk / 64, int32_t>), dim3(grid),
+                  dim3(kBlk), 0, st, g, a, b, gbig, accbig, out, acc, da);
+      else
+        ZK_LAUNCH(prof, (k_red_gend<OP, EPI, W, ID, 1, int32_t>), dim3(grid), dim3(kBlk), 0,
+                  st, g, a, b, gbig, accbig, out, acc, da);
+    }
+    return hipGetLastError();
+  };
+  if (ident) return go(IC<ZK_ADD>{}, IC<ZK_EPI_NONE>{}, IC<1>{}, IC<1>{});
+  return op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
+    return which == 0 ? go(OPc, EPIc, IC<0>{}, IC<0>{}) : go(OPc, EPIc, IC<1>{}, IC<0>{});
+  });
 }
 
 static int acc_mode(const float *acc, const float *g) {
@@ -875,10 +1170,31 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
     const int amode = p.fused_big ? acc_mode(accbig, g) : 0;
     // red_col and red_row stream all of g in the output layout
     GcOut go{nullptr, nullptr, c_sign};
-    if (!gc_done && gc_al && rp.partials > 0 &&
-        (rp.kernel == K_RED_COL || rp.kernel == K_RED_ROW)) {
+    if (!gc_done && gc_al &&
+        ((rp.partials > 0 && (rp.kernel == K_RED_COL || rp.kernel == K_RED_ROW)) ||
+         (rp.kernel == K_RED_ROWD && rp.kept > 0))) {
       go = GcOut{grad_c, acc_c, c_sign};
       gc_done = true;
+    }
+    if (rp.kernel == K_RED_GEND) {
+      e = launch_gend(rp, c, p.idx64, 3 + sw, 1, 2, op, epi, false, sw, g, a, b, gbig, accbig,
+                      p.fused_big ? acc_mode(accbig, g) : 0, p.fused_big, gsmall, accsmall,
+                      false, -1.0, st);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (rp.kernel == K_RED_ROWD) {
+      e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
+        constexpr int OP = decltype(OPc)::value;
+        constexpr int EPI = decltype(EPIc)::value;
+        return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
+          return launch_rowd<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>(
+              rp, c, sw, g, big, small, gbig, accbig, gsmall, accsmall, p.fused_big, false,
+              -1.0, go, st);
+        });
+      });
+      if (e != hipSuccess) return e;
+      continue;
     }
     if (rp.partials > 0) {
       e = op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
@@ -981,6 +1297,20 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
   for (int ri = 0; ri < p.nred; ++ri) {
     const RedPlan &rp = p.red[ri];
     double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + rp.ws_offset);
+    if (rp.kernel == K_RED_GEND) {
+      hipError_t e = launch_gend(rp, c, p.idx64, 4, -1, -1, ZK_ADD, ZK_EPI_NONE, true, 1, in,
+                                 nullptr, nullptr, nullptr, nullptr, 0, false, out, acc, neg,
+                                 mean_count, st);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (rp.kernel == K_RED_ROWD) {
+      hipError_t e = launch_rowd<ZK_ADD, ZK_EPI_NONE, 1, 0>(rp, c, 1, in, nullptr, nullptr,
+                                                            nullptr, nullptr, out, acc, false,
+                                                            neg, mean_count, none, st);
+      if (e != hipSuccess) return e;
+      continue;
+    }
     if (rp.partials > 0) {
       ProfScope prof(rp.kernel);
       switch (rp.kernel) {

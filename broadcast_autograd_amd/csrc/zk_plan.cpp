@@ -12,7 +12,8 @@ const char *kernel_name(int32_t k) {
       "bwd_ew_flat",    "bwd_ew_generic", "red_col",   "red_row",
       "red_tile",       "red_generic",   "red_final",  "fwd2_row",
       "fwd2_generic",   "bwd_signed",    "copy_row",   "copy_tile",
-      "copy_generic",   "norm_part",     "norm_final", "clip_scale"};
+      "copy_generic",   "norm_part",     "norm_final", "clip_scale",
+      "red_rowd",       "red_gend"};
   if (k < 0 || k >= K_COUNT) return "none";
   return names[k];
 }
@@ -413,6 +414,18 @@ static void size_generic(RedPlan *rp, int64_t K, int64_t red) {
   rp->partials = ceil_div(red, chunk);
 }
 
+// The one-pass gather (red_gend) when each kept element has a moderate
+// number of terms; false leaves rp alone.
+static bool size_gend(RedPlan *rp, int64_t K, int64_t red) {
+  if (K <= 0 || red < kGenDirMinTerms || red > kGenDirMaxTerms) return false;
+  rp->kernel = K_RED_GEND;
+  rp->kept = K;
+  rp->red = red;
+  rp->chunk = 0;
+  rp->partials = 0;
+  return true;
+}
+
 // Try the fast stage-1 classes for the reduced operand stride set `o`
 // (grad layout) with `big` the dense operand id (or -1 if none is read).
 // Requires the source (op 0) to be dense.
@@ -472,6 +485,17 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
   CL = ceil_div(CL, 256) * 256;
   if (CL >= inner) CL = inner;
   int64_t NC = ceil_div(inner, CL);
+  // Few terms per kept element: one block per kept element finishes its sum
+  // itself (no partials, no stage-2 launch).
+  const int64_t T = R1 * inner;
+  if (T >= kDirMinTerms && T <= kDirMaxTerms) {
+    rp->kernel = K_RED_ROWD;
+    rp->kept = K;
+    rp->red = T;
+    rp->chunk = T <= 4096 ? 1 : (T <= 8192 ? 2 : 4);  // vectors per lane
+    rp->partials = 0;
+    return true;
+  }
   rp->kernel = K_RED_ROW;
   rp->kept = K;
   rp->red = R1 * inner;
@@ -582,6 +606,18 @@ zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
         return ZK_OK;
       }
     }
+    // Moderate term counts: one gather pass that also writes the full
+    // operand's gradient.
+    {
+      RedPlan rd;
+      if (size_gend(&rd, ne[sw], c.numel / ne[sw]) && (big_full || !big_write)) {
+        rd.which = sw;
+        p->red[p->nred++] = rd;
+        p->fused_big = big_write;
+        finish_workspace(p);
+        return ZK_OK;
+      }
+    }
     // Fallback: generic gather for the reduced gradient, element-wise
     // kernel for the full one.
     RedPlan &rp = p->red[p->nred++];
@@ -601,7 +637,7 @@ zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
   // Both operands broadcast: one gather reduction each.
   for (int w = 0; w < 2; ++w) {
     RedPlan &rp = p->red[p->nred++];
-    size_generic(&rp, ne[w], c.numel / ne[w]);
+    if (!size_gend(&rp, ne[w], c.numel / ne[w])) size_generic(&rp, ne[w], c.numel / ne[w]);
     rp.which = w;
   }
   finish_workspace(p);
@@ -658,7 +694,7 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
     p->vec = 4;
   } else {
     RedPlan &q = p->red[p->nred++];
-    size_generic(&q, K, c.numel / K);
+    if (!size_gend(&q, K, c.numel / K)) size_generic(&q, K, c.numel / K);
     q.which = 1;
   }
   finish_workspace(p);

@@ -25,6 +25,13 @@ constexpr int64_t kMaxGridBlocks = (int64_t)1 << 22;
 // instantiated for 1, 4 and 16.  Measured on the [32768, 4096] backward:
 // 16 waves 270 us, 4 waves 289 us, 1 wave (no LDS combine) 296 us.
 constexpr int kColRowsMany = 64;
+// red_rowd: terms per kept element it takes (a 1024-lane block holds up to 4
+// vectors per lane in flight).
+constexpr int64_t kDirMinTerms = 2048;
+constexpr int64_t kDirMaxTerms = 16384;
+// red_gend: terms per kept element it takes (a wave walks them, 64 at a time).
+constexpr int64_t kGenDirMinTerms = 32;
+constexpr int64_t kGenDirMaxTerms = 4096;
 constexpr int kColWavesFew = 16;
 constexpr int kColWavesMany = 16;
 
@@ -51,7 +58,9 @@ enum KernelClass : int32_t {
   K_NORM_PART = 17,   // global L2 norm: binary64 partial sums of squares
   K_NORM_FINAL = 18,  // global L2 norm: fixed-order total, sqrt, clip factor
   K_CLIP_SCALE = 19,  // ClipGradNorm: in-place scaling by the factor
-  K_COUNT = 20
+  K_RED_ROWD = 20,    // red_row's pattern in one pass: a block per kept element
+  K_RED_GEND = 21,    // any pattern in one pass: a wave per kept element
+  K_COUNT = 22
 };
 
 const char *kernel_name(int32_t k);

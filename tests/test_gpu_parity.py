@@ -517,3 +517,128 @@ def test_full_size_gpt_residual(orc):
     _check_sampled_bwd(orc, "mul", 1, h["g"], h["h"], h["gamma"], host(wl.grad_gamma), 15,
                        full=True)
     _check_sampled_bwd(orc, "add", 1, h["g"], t, h["resid"], host(wl.grad_resid), 16)
+
+
+# One-pass row reductions (2048..16384 terms per kept element): a block per
+# kept element finishes the sum itself.  Term counts at and between the
+# limits of 1, 2 and 4 vectors per lane, ragged last vectors, every op with
+# and without GeLU, the acc modes, and the plain reduction.
+ROWD_SHAPES = [((64, 128, 256), (128, 1)),   # the x*y + x workload's y: T = 16384
+               ((2, 7, 1024), (7, 1)),       # T = 2048, U = 1
+               ((4096,), ()),                # T = 4096: one kept element
+               ((3, 5, 1372), (5, 1)),       # T = 4116: U = 2, ragged vectors
+               ((31, 2, 264), (2, 1)),       # T = 8184: U = 2
+               ((4, 9, 2052), (9, 1)),       # T = 8208: U = 4
+               ((16384,), (1,))]             # T = 16384, rank 1
+
+
+@pytest.mark.parametrize("shapes", ROWD_SHAPES)
+@pytest.mark.parametrize("op", OPS)
+def test_one_pass_row_reduction(orc, shapes, op):
+    sa, sb = shapes
+    info = zk.plan_describe("bwd", op, zk.make_desc(sa), zk.make_desc(sb))
+    assert info["kernel"] == "red_rowd", info
+    a, b = _rng_pair(sa, sb, seed=sum(sa) + OPS.index(op))
+    check_pair(orc, op, a, dev(a), b, dev(b), seed=5)
+    if op in ("add", "mul"):
+        check_pair(orc, op, a, dev(a), b, dev(b), seed=6, epi="gelu")
+    rng = np.random.default_rng(sum(sa))
+    g = rng.standard_normal(sa).astype(np.float32)
+    acc_b = rng.standard_normal(sb).astype(np.float32)
+    ga, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), acc_a=dev(g), acc_b=dev(acc_b))
+    ra, rb = orc.bwd(op, g, a, b, acc_a=g, acc_b=acc_b)
+    assert_bwd(host(ga), ra, f"{op} acc_a=g")
+    assert_bwd(host(gb), rb, f"{op} acc_b")
+    x = rng.standard_normal(sa).astype(np.float32)
+    assert_bwd(host(zk.reduce_to_shape(dev(x), sb)), orc.reduce_to_shape(x, sb), "reduce")
+    m = host(zk.mean_to_shape(dev(x), sb))
+    assert_bwd(m, orc.mean_to_shape(x, sb), "mean")
+
+
+@pytest.mark.parametrize("op2", ["add", "sub"])
+def test_one_pass_row_reduction_fused(orc, op2):
+    """The fused expression's c gradient through the one-pass kernels: c with
+    the full shape (written beside a's gradient) and c broadcast (a signed
+    one-pass reduction of g)."""
+    rng = np.random.default_rng(61)
+    a = rng.standard_normal((16, 96, 256)).astype(np.float32)
+    b = rng.uniform(0.5, 2.0, (96, 1)).astype(np.float32)
+    g = rng.standard_normal((16, 96, 256)).astype(np.float32)
+    for c in (rng.standard_normal((16, 96, 256)).astype(np.float32),
+              rng.standard_normal((96, 1)).astype(np.float32)):
+        grads = zk.binary2_bwd("mul", op2, dev(g), dev(a), dev(b), dev(c))
+        want = orc.bwd2("mul", op2, g, a, b, c)
+        for got, ref, name in zip(grads, want, "abc"):
+            assert_bwd(host(got), ref, f"fused {op2} grad_{name} c{c.shape}")
+
+
+# One-pass gather reductions (32..4096 terms per kept element on patterns
+# the streaming classes do not take): a wave per kept element, also writing
+# the full operand's gradient.
+GEND_SHAPES = [((2, 3, 4, 5, 6, 7, 8, 9), (1, 3, 1, 5, 1, 7, 1, 9)),  # the rank-8 workload
+               ((40, 3, 7), (1, 3, 1)),       # T = 280, inner dim reduced but short
+               ((5, 64, 3), (5, 1, 3)),       # middle dim reduced: T = 64
+               ((4096, 3), (1, 3)),           # T = 4096, inner 3
+               ((33, 5), (1, 5))]             # T = 33
+
+
+@pytest.mark.parametrize("shapes", GEND_SHAPES)
+@pytest.mark.parametrize("op", OPS)
+def test_one_pass_gather_reduction(orc, shapes, op):
+    sa, sb = shapes
+    info = zk.plan_describe("bwd", op, zk.make_desc(sa), zk.make_desc(sb))
+    assert info["kernel"] == "red_gend", info
+    a, b = _rng_pair(sa, sb, seed=sum(sa) + OPS.index(op))
+    check_pair(orc, op, a, dev(a), b, dev(b), seed=7)
+    if op in ("add", "mul"):
+        check_pair(orc, op, a, dev(a), b, dev(b), seed=8, epi="gelu")
+    rng = np.random.default_rng(sum(sa) + 1)
+    g = rng.standard_normal(sa).astype(np.float32)
+    acc_a = rng.standard_normal(sa).astype(np.float32)
+    acc_b = rng.standard_normal(sb).astype(np.float32)
+    # acc == g for the full gradient, a separate acc for the reduced one
+    ga, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), acc_a=dev(g), acc_b=dev(acc_b))
+    ra, rb = orc.bwd(op, g, a, b, acc_a=g, acc_b=acc_b)
+    assert_bwd(host(ga), ra, f"{op} acc_a=g")
+    assert_bwd(host(gb), rb, f"{op} acc_b")
+    # separate acc buffers, in place
+    xa, xb = dev(acc_a), dev(acc_b)
+    zk.binary_bwd(op, dev(g), dev(a), dev(b), grad_a=xa, acc_a=xa, grad_b=xb, acc_b=xb)
+    ra, rb = orc.bwd(op, g, a, b, acc_a=acc_a, acc_b=acc_b)
+    assert_bwd(host(xa), ra, f"{op} in-place a")
+    assert_bwd(host(xb), rb, f"{op} in-place b")
+    # only the reduced gradient
+    _, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), need_a=False)
+    _, rb = orc.bwd(op, g, a, b, want=(False, True))
+    assert_bwd(host(gb), rb, f"{op} b only")
+
+
+def test_one_pass_gather_reduce_mean_and_fused(orc):
+    rng = np.random.default_rng(71)
+    # transposed views reduced and averaged
+    for sizes, strides, target in (((300, 7), (1, 300), (7,)), ((64, 40), (1, 64), (1, 40)),
+                                   ((9, 10, 11), (110, 1, 10), (1, 10, 1))):
+        span = sum((n - 1) * st for n, st in zip(sizes, strides)) + 1
+        stor = rng.standard_normal(span).astype(np.float32)
+        v, t, _ = strided_pair(stor, sizes, strides)
+        info = zk.plan_describe("reduce", "add", zk.desc_of(t), zk.make_desc(target))
+        assert info["kernel"] == "red_gend", info
+        assert_bwd(host(zk.reduce_to_shape(t, target)), orc.reduce_to_shape(v, target),
+                   f"reduce {sizes}")
+        assert_bwd(host(zk.mean_to_shape(t, target)), orc.mean_to_shape(v, target),
+                   f"mean {sizes}")
+    # both operands broadcast
+    for sa, sb in (((300, 1), (1, 200)), ((40, 1, 7), (1, 30, 1))):
+        for op in OPS:
+            a, b = _rng_pair(sa, sb, seed=len(sa) + OPS.index(op))
+            check_pair(orc, op, a, dev(a), b, dev(b), seed=9)
+    # fused expression whose c is reduced on a gather pattern, with a sign
+    a = rng.standard_normal((40, 3, 7)).astype(np.float32)
+    b = rng.uniform(0.5, 2.0, (1, 3, 1)).astype(np.float32)
+    c = rng.standard_normal((1, 3, 7)).astype(np.float32)
+    g = rng.standard_normal((40, 3, 7)).astype(np.float32)
+    for op2 in ("add", "sub"):
+        grads = zk.binary2_bwd("mul", op2, dev(g), dev(a), dev(b), dev(c))
+        want = orc.bwd2("mul", op2, g, a, b, c)
+        for got, ref, name in zip(grads, want, "abc"):
+            assert_bwd(host(got), ref, f"fused {op2} grad_{name}")

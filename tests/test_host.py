@@ -292,7 +292,7 @@ WORKLOAD_PLANS = [
      (64, 128, 256), (0, 1, 0)),
     ("fwd", "add", "none", ((64, 128, 256), None), ((64, 128, 256), None), "fwd_flat",
      (2097152,), (1,)),
-    ("bwd", "mul", "none", ((64, 128, 256), None), ((128, 1), None), "red_row",
+    ("bwd", "mul", "none", ((64, 128, 256), None), ((128, 1), None), "red_rowd",
      (64, 128, 256), (0, 1, 0)),
     ("fwd", "add", "gelu", ((4096, 1024), None), ((1024,), None), "fwd_row",
      (4096, 1024), (0, 1)),
@@ -311,7 +311,7 @@ WORKLOAD_PLANS = [
     ("fwd", "div", "none", ((2, 3, 4, 5, 6, 7, 8, 9), None), ((1, 3, 1, 5, 1, 7, 1, 9), None),
      "fwd_generic", (2, 3, 4, 5, 6, 7, 8, 9), (0, 315, 0, 63, 0, 9, 0, 1)),
     ("bwd", "div", "none", ((2, 3, 4, 5, 6, 7, 8, 9), None), ((1, 3, 1, 5, 1, 7, 1, 9), None),
-     "bwd_ew_generic", (2, 3, 4, 5, 6, 7, 8, 9), (0, 315, 0, 63, 0, 9, 0, 1)),
+     "red_gend", (2, 3, 4, 5, 6, 7, 8, 9), (0, 315, 0, 63, 0, 9, 0, 1)),
     ("fwd", "mul", "none", ((16, 2048, 4096), None), ((4096,), None), "fwd_row",
      (32768, 4096), (0, 1)),
     ("fwd", "add", "none", ((16, 2048, 4096), None), ((16, 2048, 4096), None), "fwd_flat",
@@ -342,6 +342,21 @@ def test_reduce_plans(L):
     assert info["kernel"] == "red_col" and info["sizes"] == (128, 1048576)
     info = zk.plan_describe("reduce", "add", zk.make_desc((6, 4), (1, 6)), zk.make_desc((4,)))
     assert info["kernel"] == "red_generic"
+    # 32..4096 terms per kept element on a gather pattern: one pass
+    info = zk.plan_describe("reduce", "add", zk.make_desc((64, 4), (1, 64)), zk.make_desc((4,)))
+    assert info["kernel"] == "red_gend" and info["partials"] == 0
+    info = zk.plan_describe("reduce", "add", zk.make_desc((4097, 4), (1, 4097)),
+                            zk.make_desc((4,)))
+    assert info["kernel"] == "red_generic"
+    # 2048..16384 terms per kept element: one pass, no partials
+    for shape, target, kern in (((16384,), (), "red_rowd"), ((8192,), (), "red_rowd"),
+                                ((4096,), (1,), "red_rowd"), ((2, 1024), (1, 1), "red_rowd"),
+                                ((16, 1024), (16, 1), "red_row"),
+                                ((32768,), (), "red_row"), ((7, 4, 4096), (1, 4, 1), "red_row")):
+        info = zk.plan_describe("reduce", "add", zk.make_desc(shape), zk.make_desc(target))
+        assert info["kernel"] == kern, (shape, target, info["kernel"])
+        if kern == "red_rowd":
+            assert info["partials"] == 0
 
 
 def test_index64_threshold(L):
