@@ -86,6 +86,8 @@ def lib():
         L.or_grad_norm.restype = ctypes.c_double
         L.or_clip_grad_norm.argtypes = [ctypes.c_int, P, P, ctypes.c_double, P, P]
         L.or_clip_grad_norm.restype = ctypes.c_double
+        L.or_row_moments.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+        L.or_row_softmax_stats.argtypes = [P, I64, I64, I64, P, P, P]
         L.or_relu32.argtypes = [ctypes.c_float]
         L.or_relu32.restype = ctypes.c_float
         L.or_gelu32.argtypes = [ctypes.c_float]
@@ -333,6 +335,46 @@ def clip_grad_norm(gs, max_norm):
     norm = lib().or_clip_grad_norm(len(arrs), ptrs, ns, float(max_norm),
                                    ctypes.byref(clipped), ctypes.byref(factor))
     return arrs, float(norm), bool(clipped.value), np.float32(factor.value)
+
+
+def _rows(x, cols=None, ld=None):
+    """A [rows, cols] matrix given as 2-D array, or as flat storage with an
+    explicit row pitch ``ld``."""
+    x = np.array(x, dtype=np.float32, order="C")
+    if ld is None:
+        rows, cols = x.shape
+        ld = cols
+    else:
+        rows = (x.size - cols) // ld + 1 if x.size else 0
+    return x.reshape(-1), int(rows), int(cols), int(ld)
+
+
+def row_moments(x, cols=None, ld=None):
+    """Per-row mean and biased variance: (Grad of the mean with sum|x|/cols as
+    its tolerance base, Grad of the variance with its own value as base)."""
+    flat, rows, cols, ld = _rows(x, cols, ld)
+    m32, v32 = np.empty(rows, np.float32), np.empty(rows, np.float32)
+    m64, v64, am = np.empty(rows), np.empty(rows), np.empty(rows)
+
+    def p(z):
+        return z.ctypes.data if z.size else None
+
+    _check(lib().or_row_moments(p(flat), rows, cols, ld, p(m32), p(v32), p(m64), p(v64),
+                                p(am)))
+    return Grad(m32, m64, am), Grad(v32, v64, v64.copy())
+
+
+def row_softmax_stats(x, cols=None, ld=None):
+    """Per-row max (binary32, exact) and Grad of sum exp(x - max) (its own
+    value as the tolerance base: every term is positive)."""
+    flat, rows, cols, ld = _rows(x, cols, ld)
+    mx, s32, s64 = np.empty(rows, np.float32), np.empty(rows, np.float32), np.empty(rows)
+
+    def p(z):
+        return z.ctypes.data if z.size else None
+
+    _check(lib().or_row_softmax_stats(p(flat), rows, cols, ld, p(mx), p(s32), p(s64)))
+    return mx, Grad(s32, s64, s64.copy())
 
 
 def materialize(x, shape=None):

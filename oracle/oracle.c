@@ -705,3 +705,68 @@ double or_clip_grad_norm(int count, float *const *g, const int64_t *n, double c,
   if (factor) *factor = f;
   return norm;
 }
+
+/* ----------------------------------------------------- row statistics */
+
+/* Per-row mean and (biased) variance, the statistics a LayerNorm takes of
+ * each row (GPU chapter, "reduction": mean and variance are reductions;
+ * Operator chapter, "fusion": LayerNorm computes them inside one operator).
+ * Row r is x[r*ld .. r*ld + cols).  mean = sum x / cols and var = sum (x -
+ * mean)^2 / cols, both in binary64 (two passes, index order), rounded once;
+ * cols = 0 gives NaN.  abs_mean gets sum|x| / cols (the mean's tolerance
+ * base); the variance's terms are its own squares. */
+int or_row_moments(const float *x, int64_t rows, int64_t cols, int64_t ld, float *mean,
+                   float *var, double *mean64, double *var64, double *abs_mean) {
+  if (rows < 0 || cols < 0 || ld < cols) return OR_ERR_SIZE;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float *row = x + r * ld;
+    double s = 0.0, a = 0.0;
+    for (int64_t j = 0; j < cols; ++j) {
+      s += (double)row[j];
+      a += fabs((double)row[j]);
+    }
+    const double m = s / (double)cols;
+    double q = 0.0;
+    for (int64_t j = 0; j < cols; ++j) {
+      const double d = (double)row[j] - m;
+      q += d * d;
+    }
+    const double v = q / (double)cols;
+    if (mean) mean[r] = (float)m;
+    if (var) var[r] = (float)v;
+    if (mean64) mean64[r] = m;
+    if (var64) var64[r] = v;
+    if (abs_mean) abs_mean[r] = a / (double)cols;
+  }
+  return OR_OK;
+}
+
+/* Per-row softmax statistics (GPU chapter, "reduction": Softmax is one of
+ * the reductions; the GPT chapter's attention takes a softmax over each row
+ * of the masked scores): rowmax = max_j x (exact; NaN if the row holds a
+ * NaN, -inf for an empty row) and sumexp = sum_j exp(x - rowmax), each
+ * exponent of the exact binary64 difference with libm exp, summed in
+ * binary64 in index order and rounded once (0 for an empty row). */
+int or_row_softmax_stats(const float *x, int64_t rows, int64_t cols, int64_t ld,
+                         float *rowmax, float *sumexp, double *sumexp64) {
+  if (rows < 0 || cols < 0 || ld < cols) return OR_ERR_SIZE;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float *row = x + r * ld;
+    float m = -INFINITY;
+    int nan = 0;
+    for (int64_t j = 0; j < cols; ++j) {
+      if (isnan(row[j])) nan = 1;
+      else if (row[j] > m) m = row[j];
+    }
+    if (nan) m = NAN;
+    double s = 0.0;
+    for (int64_t j = 0; j < cols; ++j) s += exp((double)row[j] - (double)m);
+    if (cols == 0) s = 0.0;
+    if (rowmax) rowmax[r] = m;
+    if (sumexp) sumexp[r] = (float)s;
+    if (sumexp64) sumexp64[r] = s;
+  }
+  return OR_OK;
+}

@@ -745,3 +745,74 @@ def test_clip_grad_norm_pins(orc):
         r = a.astype(np.float64) / b.astype(np.float64)
         assert np.all(np.abs(r - float(f)) <= float(f) * 2.0 ** -23)
     assert orc.grad_norm(out) == pytest.approx(0.5 * n * n / (n + 1e-6), rel=1e-6)
+
+
+# ------------------------------------------------------- row statistics
+# Mean, variance and softmax are the reductions the GPU chapter lists beside
+# the gradient norm; LayerNorm takes the first two of each row, the
+# attention's softmax the row max and the sum of exponentials.
+
+
+def test_row_moments_pins(orc):
+    """Constant rows: mean exact, variance 0; an arithmetic sequence a + d j
+    (j < n): mean a + d (n - 1)/2, variance d^2 (n^2 - 1)/12; numpy's
+    binary64 mean and var (ddof 0); the variance is shift invariant; a row
+    pitch beyond the row is skipped."""
+    c = np.full((3, 384), np.float32(0.7), np.float32)
+    m, v = orc.row_moments(c)
+    assert np.all(m.f32 == np.float32(0.7)) and np.all(v.f64 == 0.0)
+    n, a, d = 384, np.float32(-3.0), np.float32(0.5)
+    x = (a + d * np.arange(n, dtype=np.float32))[None, :]
+    m, v = orc.row_moments(x)
+    assert m.f64[0] == float(a) + float(d) * (n - 1) / 2
+    assert v.f64[0] == pytest.approx(float(d) ** 2 * (n * n - 1) / 12, rel=1e-14)
+    rng = np.random.default_rng(81)
+    y = rng.standard_normal((17, 300)).astype(np.float32) * np.float32(3) + np.float32(1)
+    m, v = orc.row_moments(y)
+    y64 = y.astype(np.float64)
+    assert np.allclose(m.f64, y64.mean(axis=1), rtol=1e-14, atol=1e-15)
+    assert np.allclose(v.f64, y64.var(axis=1), rtol=1e-13)
+    assert np.array_equal(m.f32, m.f64.astype(np.float32))
+    assert np.allclose(m.abs, np.abs(y64).mean(axis=1), rtol=1e-14)
+    # on a 2^-10 grid, adding 64 is exact in binary32 (|y| < 64)
+    yq = (np.round(y * 1024) / 1024).astype(np.float32)
+    _, vq = orc.row_moments(yq)
+    _, v2 = orc.row_moments(yq + np.float32(64))
+    assert np.allclose(v2.f64, vq.f64, rtol=1e-12)
+    # pitch: rows of 300 inside a buffer with rows of 320
+    buf = np.zeros((17, 320), np.float32)
+    buf[:, :300] = y
+    mp, vp = orc.row_moments(buf.reshape(-1)[:16 * 320 + 300], cols=300, ld=320)
+    assert np.array_equal(mp.f32, m.f32) and np.array_equal(vp.f32, v.f32)
+    e, ev = orc.row_moments(np.zeros((2, 0), np.float32))
+    assert np.all(np.isnan(e.f32)) and np.all(np.isnan(ev.f32))
+
+
+def test_row_softmax_stats_pins(orc):
+    """The max is exact (numpy's); a constant row sums to its length; x_j =
+    -j t is a geometric series (1 - e^(-n t)) / (1 - e^(-t)); log(sum) + max
+    equals scipy's binary64 logsumexp; NaN rows give NaN, a row of -inf gives
+    NaN (exp of -inf minus -inf), an empty row gives max -inf and sum 0."""
+    from scipy.special import logsumexp
+    mx, s = orc.row_softmax_stats(np.full((2, 256), np.float32(-1e9), np.float32))
+    assert np.all(mx == np.float32(-1e9)) and np.all(s.f64 == 256.0)
+    t = 0.25
+    x = (-t * np.arange(100)).astype(np.float32)[None, :]  # exact in binary32
+    mx, s = orc.row_softmax_stats(x)
+    assert mx[0] == 0.0
+    assert s.f64[0] == pytest.approx((1 - math.exp(-100 * t)) / (1 - math.exp(-t)), rel=1e-14)
+    rng = np.random.default_rng(82)
+    y = rng.standard_normal((9, 256)).astype(np.float32) * np.float32(4)
+    y[3, 100:] = np.float32(-1e9)  # a causal-mask style row
+    mx, s = orc.row_softmax_stats(y)
+    assert np.array_equal(mx, y.max(axis=1))
+    lse = logsumexp(y.astype(np.float64), axis=1)
+    assert np.allclose(np.log(s.f64) + mx.astype(np.float64), lse, rtol=0, atol=1e-13)
+    z = y.copy()
+    z[1, 7] = np.nan
+    z[2, :] = -np.inf
+    mz, sz = orc.row_softmax_stats(z)
+    assert np.isnan(mz[1]) and np.isnan(sz.f32[1])
+    assert mz[2] == -np.inf and np.isnan(sz.f32[2])
+    me, se = orc.row_softmax_stats(np.zeros((2, 0), np.float32))
+    assert np.all(me == -np.inf) and np.all(se.f32 == 0)
