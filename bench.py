@@ -40,7 +40,9 @@ ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
        "xy_plus_x_fused", "attn_scale_mask_fused", "gpt_residual_fused",
        # the other reductions: mean of the per-token loss and its gradient,
        # ClipGradNorm over the GPT configuration's parameter gradients
-       "gpt_loss_mean_clip"]
+       "gpt_loss_mean_clip",
+       # per-row statistics: LayerNorm mean / variance, softmax max / sum exp
+       "gpt_row_stats"]
 ROTATE_BYTES = 1 << 30  # per-workload footprint of the rotating buffer sets
 MAX_SETS = 32
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -128,7 +130,7 @@ def capture(sets, torch):
 
 def outputs(wl, torch):
     names = [k for k, v in vars(wl).items() if isinstance(v, torch.Tensor)
-             and (k.startswith("grad_") or k in ("t", "z", "y", "out"))]
+             and (k.startswith(("grad_", "out")) or k in ("t", "z", "y"))]
     return {k: getattr(wl, k).detach().clone() for k in sorted(names)}
 
 
@@ -332,6 +334,7 @@ def main():
     for w in ("xy_plus_x", "attn_scale_mask", "gpt_residual"):
         gen[w + "_fused"] = gen[w]
     gen["gpt_loss_mean_clip"] = Wk.gpt_loss_mean_clip
+    gen["gpt_row_stats"] = Wk.gpt_row_stats
     log(f"[bench] device {torch.cuda.get_device_name(0)}; spin check "
         f"{spin_seconds(torch) * 1e3:.1f} ms")
     ceiling = copy_ceiling(torch)
@@ -355,8 +358,11 @@ def main():
         K = args.other_steps or (40 if big else 400)
         log(f"[bench] workload {w}: {K} steps")
         r = measure(w, gen[w](), K, K // 10, torch)
+        def gbs(v):
+            return "-" if v is None else f"{v:.1f}"
         log(f"[bench]   {r['ms_per_step'] * 1e3:.2f} us/step, {r['step_gbs']:.1f} GB/s; "
-            f"fwd kernels {r['fwd_kernel_gbs']:.1f} GB/s, bwd kernels {r['bwd_kernel_gbs']:.1f} GB/s")
+            f"fwd kernels {gbs(r['fwd_kernel_gbs'])} GB/s, bwd kernels "
+            f"{gbs(r['bwd_kernel_gbs'])} GB/s")
         per[w] = r
 
     # dominant kernel of the main step: the largest total kernel time

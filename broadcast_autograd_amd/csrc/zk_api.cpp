@@ -478,6 +478,32 @@ zk_status zk_clip_grad_norm(int32_t count, float *const *grads, const int64_t *n
                      workspace_bytes, stream);
 }
 
+namespace {
+zk_status row_stats_common(int mode, const float *x, int64_t rows, int64_t cols, int64_t ld,
+                           float *o1, float *o2, void *stream) {
+  if (rows < 0 || cols < 0) return ZK_ERR_BAD_SIZE;
+  if (ld < cols || (rows > 1 && ld < 1)) return ZK_ERR_BAD_STRIDE;
+  if (rows == 0) return ZK_OK;
+  if (!o1 || !o2) return ZK_ERR_NULL;
+  if (cols > 0 && !x) return ZK_ERR_NULL;
+  const Ext e1 = ext_dense(o1, rows), e2 = ext_dense(o2, rows);
+  Ext ex;
+  if (cols > 0) ex = ext_dense(x, (rows - 1) * ld + cols);
+  if (ov(e1, e2) || ov(e1, ex) || ov(e2, ex)) return ZK_ERR_ALIAS;
+  return hip_status(launch_row_stats(mode, x, rows, cols, ld, o1, o2, (hipStream_t)stream));
+}
+}  // namespace
+
+zk_status zk_row_moments(const float *x, int64_t rows, int64_t cols, int64_t ld, float *mean,
+                         float *var, void *stream) {
+  return row_stats_common(0, x, rows, cols, ld, mean, var, stream);
+}
+
+zk_status zk_row_softmax_stats(const float *x, int64_t rows, int64_t cols, int64_t ld,
+                               float *rowmax, float *sumexp, void *stream) {
+  return row_stats_common(1, x, rows, cols, ld, rowmax, sumexp, stream);
+}
+
 zk_status zk_scalar_fwd(zk_op op, zk_epi epi, const float *t, const zk_desc *dt,
                         float sv, int32_t scalar_first, float *out, void *stream) {
   if (!valid_op(op) || !valid_epi(epi)) return ZK_ERR_UNSUPPORTED;

@@ -13,7 +13,7 @@ const char *kernel_name(int32_t k) {
       "red_tile",       "red_generic",   "red_final",  "fwd2_row",
       "fwd2_generic",   "bwd_signed",    "copy_row",   "copy_tile",
       "copy_generic",   "norm_part",     "norm_final", "clip_scale",
-      "red_rowd",       "red_gend"};
+      "red_rowd",       "red_gend",      "row_moments", "row_softmax"};
   if (k < 0 || k >= K_COUNT) return "none";
   return names[k];
 }

@@ -60,7 +60,9 @@ enum KernelClass : int32_t {
   K_CLIP_SCALE = 19,  // ClipGradNorm: in-place scaling by the factor
   K_RED_ROWD = 20,    // red_row's pattern in one pass: a block per kept element
   K_RED_GEND = 21,    // any pattern in one pass: a wave per kept element
-  K_COUNT = 22
+  K_ROW_MOMENTS = 22,  // per-row mean and variance, a wave per row
+  K_ROW_SOFTMAX = 23,  // per-row max and sum of exponentials, a wave per row
+  K_COUNT = 24
 };
 
 const char *kernel_name(int32_t k);

@@ -363,7 +363,35 @@ class GPTLossMeanClip(Workload):
         ]
 
 
+class GPTRowStats(Workload):
+    """Per-row statistics of the GPT configuration: a LayerNorm's row mean
+    and variance of x[64*256, 384] and a softmax's row max and sum of
+    exponentials over the causal attention scores [64*6*256, 256]."""
+    name = "gpt_row_stats"
+
+    def __init__(self, host=None):
+        import torch
+        hh = host or W.gpt_row_stats()
+        self.host = hh
+        self.x = torch.from_numpy(hh["x"]).to("cuda")
+        self.scores = torch.from_numpy(hh["scores"]).to("cuda")
+        rx, cx = self.x.shape
+        rs, cs = self.scores.shape
+        e = torch.empty
+        self.out_mean, self.out_var = e(rx, device="cuda"), e(rx, device="cuda")
+        self.out_max, self.out_sumexp = e(rs, device="cuda"), e(rs, device="cuda")
+        self.calls = [
+            Call("row_moments(x[%d,%d])->mean,var" % (rx, cx), "fwd",
+                 lambda: zk.row_moments(self.x, mean=self.out_mean, var=self.out_var),
+                 [rx * cx], [rx, rx]),
+            Call("row_softmax_stats(scores[%d,%d])->max,sumexp" % (rs, cs), "fwd",
+                 lambda: zk.row_softmax_stats(self.scores, rowmax=self.out_max,
+                                              sumexp=self.out_sumexp),
+                 [rs * cs], [rs, rs]),
+        ]
+
+
 WORKLOAD_CLASSES = {c.name: c for c in (XYPlusX, MLPBiasGelu, AttnScaleMask,
                                         StridedTransposed, Rank8, GPTResidual,
                                         XYPlusXFused, AttnScaleMaskFused,
-                                        GPTResidualFused, GPTLossMeanClip)}
+                                        GPTResidualFused, GPTLossMeanClip, GPTRowStats)}

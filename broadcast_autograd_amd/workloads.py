@@ -22,6 +22,8 @@ WORKLOADS = {
     "gpt_residual": "h[16,2048,4096] * gamma[4096] + resid[16,2048,4096]",
     "gpt_loss_mean_clip": "mean of the per-token loss[64*256] and its gradient; "
                           "ClipGradNorm(1.0) over the GPT configuration's 76 gradients",
+    "gpt_row_stats": "LayerNorm row mean/variance of x[64*256, 384]; softmax row max / "
+                     "sum exp of causal scores[64*6*256, 256]",
 }
 
 
@@ -130,3 +132,13 @@ def gpt_loss_mean_clip(b=64, t=256):
     return dict(loss=uniform((b * t,), 6001, 0.0, 10.0),
                 grads=normal((total,), 6002, 0.0, 0.01),
                 g=np.array(1.0, dtype=np.float32))
+
+
+def gpt_row_stats(b=64, t=256, c=384, heads=6):
+    """LayerNorm input x[b*t, c] N(0,1) and attention scores [b*heads*t, t]
+    N(0,1) with the causal mask added (row i of each t x t block: -1e9 for
+    j > i), i.e. the masked scores the softmax reduces."""
+    x = normal((b * t, c), 7001)
+    s = normal((b * heads, t, t), 7002)
+    s += causal_mask(t).reshape(1, t, t)
+    return dict(x=x, scores=s.reshape(b * heads * t, t))

@@ -27,6 +27,7 @@ SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
            "zk_reduce_to_shape", "zk_materialize", "zk_binary2_fwd", "zk_binary2_bwd",
            "zk_scalar_fwd", "zk_scalar_bwd", "zk_unary_fwd", "zk_unary_bwd",
            "zk_mean_to_shape", "zk_mean_bwd", "zk_grad_norm", "zk_clip_grad_norm",
+           "zk_row_moments", "zk_row_softmax_stats",
            "zk_status_string", "zk_plan_describe", "zk_kernel_name",
            "zk_profile_start", "zk_profile_stop", "zk_profile_read")
 
@@ -89,6 +90,9 @@ def lib():
         L.zk_mean_bwd.argtypes = [P, I32, P, I32, P, P, P]
         L.zk_grad_norm.argtypes = [I32, P, P, P, P, P, P]
         L.zk_clip_grad_norm.argtypes = [I32, P, P, F32, P, P, P, P]
+        I64 = ctypes.c_int64
+        L.zk_row_moments.argtypes = [P, I64, I64, I64, P, P, P]
+        L.zk_row_softmax_stats.argtypes = [P, I64, I64, I64, P, P, P]
         L.zk_status_string.argtypes = [I32]
         L.zk_status_string.restype = ctypes.c_char_p
         L.zk_plan_describe.argtypes = [I32, I32, I32, P, P, P]
@@ -463,6 +467,39 @@ def clip_grad_norm(tensors, max_norm, norm_out=None, workspace=None, stream=None
     when the global norm exceeds max_norm.  Returns the norm (0-d device
     tensor; nothing is synchronised)."""
     return _norm_call(tensors, True, max_norm, norm_out, workspace, stream)
+
+
+def _row_view(x):
+    """(rows, cols, ld) of a 2-D tensor whose rows are contiguous."""
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("row statistics take a 2-D tensor with contiguous rows")
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else max(cols, 1)
+    return rows, cols, ld
+
+
+def row_moments(x, mean=None, var=None, stream=None):
+    """Per-row mean and biased variance of a 2-D tensor with contiguous rows."""
+    import torch
+    rows, cols, ld = _row_view(x)
+    mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
+    var = torch.empty(rows, dtype=torch.float32, device=x.device) if var is None else var
+    _check(lib().zk_row_moments(_ptr(x), rows, cols, ld, _ptr(mean), _ptr(var),
+                                _stream(stream)), "zk_row_moments")
+    return mean, var
+
+
+def row_softmax_stats(x, rowmax=None, sumexp=None, stream=None):
+    """Per-row max and sum of exp(x - max) of a 2-D tensor with contiguous rows."""
+    import torch
+    rows, cols, ld = _row_view(x)
+    if rowmax is None:
+        rowmax = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if sumexp is None:
+        sumexp = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().zk_row_softmax_stats(_ptr(x), rows, cols, ld, _ptr(rowmax), _ptr(sumexp),
+                                      _stream(stream)), "zk_row_softmax_stats")
+    return rowmax, sumexp
 
 
 def plan_describe(kind, op, da, db, epi="none"):

@@ -350,6 +350,34 @@ zk_status zk_clip_grad_norm(int32_t count, float *const *grads, const int64_t *n
                             float max_norm, float *norm_out, void *workspace,
                             size_t *workspace_bytes, void *stream);
 
+/*
+ * Per-row statistics of a [rows, cols] binary32 matrix whose row r starts at
+ * x + r*ld (elements of a row contiguous, ld >= cols), reduced over each row
+ * (GPU chapter, "reduction": mean, variance and softmax are reductions;
+ * Operator chapter, "fusion": a LayerNorm computes its row statistics inside
+ * one operator; GPT chapter, "attention": a softmax over each row of the
+ * masked scores).
+ * zk_row_moments:        mean[r] = sum_j x[r,j] / cols,
+ *                        var[r]  = sum_j (x[r,j] - mean)^2 / cols (biased),
+ *                        both in binary64 (two passes), rounded once; an empty
+ *                        row gives NaN.
+ * zk_row_softmax_stats:  rowmax[r] = max_j x[r,j] (exact; NaN if the row holds
+ *                        a NaN; -inf for an empty row),
+ *                        sumexp[r] = sum_j exp(x[r,j] - rowmax[r]), each term
+ *                        with relative error below 2e-7, summed in binary64,
+ *                        rounded once (0 for an empty row; NaN for a row of
+ *                        -inf).
+ * Outputs are dense float vectors of `rows` elements, caller-allocated.  Rows
+ * of up to 4096 elements are read once, longer rows twice.  No workspace.
+ * Aliasing: the outputs may not overlap each other or the extent of x
+ * (ZK_ERR_ALIAS).  Errors: ZK_ERR_BAD_SIZE (negative rows or cols),
+ * ZK_ERR_BAD_STRIDE (ld < cols), ZK_ERR_NULL, ZK_ERR_ALIAS, ZK_ERR_HIP.
+ */
+zk_status zk_row_moments(const float *x, int64_t rows, int64_t cols, int64_t ld, float *mean,
+                         float *var, void *stream);
+zk_status zk_row_softmax_stats(const float *x, int64_t rows, int64_t cols, int64_t ld,
+                               float *rowmax, float *sumexp, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *zk_status_string(zk_status s);
 

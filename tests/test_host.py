@@ -286,6 +286,22 @@ def test_grad_norm_validation_errors(L):
                           None) == zk.ERR["ZK_ERR_BAD_SIZE"]
 
 
+def test_row_stats_validation_errors(L):
+    """Row statistics check sizes, pitch, pointers and overlaps before any
+    launch; no rows launches nothing."""
+    for fn in (L.zk_row_moments, L.zk_row_softmax_stats):
+        def call(x=FA, rows=4, cols=8, ld=8, o1=FO, o2=FB):
+            return zk.STATUS[fn(x, rows, cols, ld, o1, o2, None)]
+        assert call(rows=-1) == "ZK_ERR_BAD_SIZE"
+        assert call(cols=-1) == "ZK_ERR_BAD_SIZE"
+        assert call(ld=7) == "ZK_ERR_BAD_STRIDE"
+        assert call(x=None) == "ZK_ERR_NULL"
+        assert call(o2=None) == "ZK_ERR_NULL"
+        assert call(o1=ctypes.c_void_p(FA.value + 64)) == "ZK_ERR_ALIAS"
+        assert call(o2=ctypes.c_void_p(FO.value + 8)) == "ZK_ERR_ALIAS"
+        assert call(rows=0, x=None, o1=None, o2=None) == "ZK_OK"
+
+
 WORKLOAD_PLANS = [
     # (kind, op, epi, a (sizes, strides), b (sizes, strides), kernel, canonical sizes, b strides)
     ("fwd", "mul", "none", ((64, 128, 256), None), ((128, 1), None), "fwd_row",
