@@ -160,22 +160,28 @@ __device__ __forceinline__ void phi_pair_f32(float h, double &Phi, double &pdf) 
   pdf = eq * 0.39894228040143267794;
 }
 
-// g * GeLU'(h) = g*Phi(h) + (g*h)*phi(h) entirely in binary32, valid for
+// g * GeLU'(h) = g * (Phi(h) + h*phi(h)) entirely in binary32, valid for
 // |h| <= kGeluGradFastMax, where exp(-h^2/2) >= 2^-60 and every intermediate
-// is a normal binary32 number.  Same steps as phi_pair_f32: relative error
-// of Phi and phi below ~8e-7, plus three binary32 roundings of the products,
+// is a normal binary32 number.  The erfcx step is phi_pair_f32's; the
+// exponential takes the unreduced argument (below): relative error of Phi
+// and phi below ~8e-7, plus two binary32 roundings of the combination,
 // i.e. within ~1.1e-6 of the sum of the magnitudes of the two terms.
 constexpr float kGeluGradFastMax = 9.0f;
 __device__ __forceinline__ float gelu_grad_f32(float g, float h) {
   const float hh = 0.5f * h;
   const float qh = hh * h;
   const float ql = fmaf(hh, h, -qh);  // exact remainder of h^2/2
-  const float n = rintf(qh * 1.44269504f);
-  float r = fmaf(-n, 0.693359375f, qh);  // exact
-  r = fmaf(-n, -2.12194440e-4f, r);      // ln2 - head
-  float e = __builtin_amdgcn_exp2f(-r * 1.44269504f);
-  e = fmaf(-ql, e, e);
-  e = ldexpf(e, -(int)n);  // exp(-h^2/2)
+  // exp(-(qh + ql)) = 2^-p * exp(-t): p = qh*L1 rounded (L1 = log2(e) to
+  // binary32), pe = qh*L1 - p exactly, and since log2(e)*ln2 = 1,
+  // t = pe*ln2 + qh*(log2(e) - L1)*ln2 + ql, |t| < 5e-6, so exp(-t) = 1 - t
+  // to 1e-11; 2^-p >= 2^-59 comes from the hardware exp2 over its whole
+  // argument.
+  const float p = qh * 1.44269502f;
+  const float pe = fmaf(qh, 1.44269502f, -p);
+  float t = fmaf(qh, 1.33497582e-8f, ql);
+  t = fmaf(pe, 0.693147182f, t);
+  float e = __builtin_amdgcn_exp2f(-p);
+  e = fmaf(-t, e, e);  // exp(-h^2/2)
   const float u = fabsf(h) * 0.707106781f;
   const float rc = __builtin_amdgcn_rcpf(u + (float)kErfcxK);
   const float sv = fmaf((u - (float)kErfcxK) * rc, kErfcxABF32[0], kErfcxABF32[1]);
@@ -185,7 +191,7 @@ __device__ __forceinline__ float gelu_grad_f32(float g, float h) {
   const float E = (gp * rc) * e;  // erfc(|h|/sqrt2)
   const float Phi = h < 0.f ? 0.5f * E : fmaf(-0.5f, E, 1.0f);
   const float pdf = e * 0.398942280f;
-  return fmaf(g * h, pdf, g * Phi);
+  return g * fmaf(h, pdf, Phi);
 }
 
 // ReLU(h): h for h > 0, NaN for NaN (propagated), +0 otherwise.

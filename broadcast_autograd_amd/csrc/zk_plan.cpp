@@ -455,10 +455,9 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
     // A wave owns 256 columns and walks rcw rows: enough waves to fill the
     // chip (~8192), between 4 and 64 rows each.  The waves of a block
     // combine their sums (kColWavesFew / kColWavesMany), so a partial covers
-    // >= 64 rows and binary64 partials stay near 1% of the call's bytes
-    // (measured on the [4096, 1024] GeLU step: 16 waves x 4 rows as fast as
-    // 8 x 4, 4 x 4, 8 x 2 or 16 x 2 within the step's noise).  The grid
-    // (column groups x partials) stays within the dispatch limit.
+    // >= 16 rows and binary64 partials stay within a few % of the call's
+    // bytes.  The grid (column groups x partials) stays within the dispatch
+    // limit.
     const int64_t R0 = c.n[0];
     const int64_t colblocks = ceil_div(c.n[1], 256);
     int64_t rcw = std::min<int64_t>(kColRowsMany, std::max<int64_t>(4, R0 * colblocks / 8192));

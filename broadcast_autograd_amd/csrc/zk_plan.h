@@ -22,9 +22,14 @@ constexpr int64_t kMaxGridBlocks = (int64_t)1 << 22;
 
 // Waves per red_col block (they combine their column sums in LDS): with
 // fewer than kColRowsMany rows per wave, and with that many.  The kernel is
-// instantiated for 1, 4 and 16.  Measured on the [32768, 4096] backward:
-// 16 waves 270 us, 4 waves 289 us, 1 wave (no LDS combine) 296 us.
+// instantiated for 1, 4 and 16.  Measured: on the [4096, 1024] GeLU
+// backward, 4 waves x 4 rows 10.8-11.0 us against 12.1-15.2 us for 16 x 4
+// (the larger blocks vary from one machine to the next); on the
+// [32768, 4096] backward, 16 waves 270 us, 4 waves 289 us, 1 wave (no LDS
+// combine) 296 us.
 constexpr int kColRowsMany = 64;
+constexpr int kColWavesFew = 4;
+constexpr int kColWavesMany = 16;
 // red_rowd: terms per kept element it takes (a 1024-lane block holds up to 4
 // vectors per lane in flight).
 constexpr int64_t kDirMinTerms = 2048;
@@ -32,8 +37,6 @@ constexpr int64_t kDirMaxTerms = 16384;
 // red_gend: terms per kept element it takes (a wave walks them, 64 at a time).
 constexpr int64_t kGenDirMinTerms = 32;
 constexpr int64_t kGenDirMaxTerms = 4096;
-constexpr int kColWavesFew = 16;
-constexpr int kColWavesMany = 16;
 
 // Kernel classes (ids reported by zk_plan_describe).
 enum KernelClass : int32_t {

@@ -356,10 +356,12 @@ class GPTLossMeanClip(Workload):
                  lambda: zk.mean_bwd(self.g, self.loss.shape, out=self.grad_loss), [1], [nl]),
             Call("gradients rewritten from a pristine copy (stands in for backward)", "aux",
                  lambda: zk.materialize(self.pristine, out=self.grad_params), [na], [na]),
+            # distinct elements: each gradient read (the kernels read it twice)
+            # and written once, plus the norm
             Call("clip_grad_norm(%d grads, %g)" % (len(self.views), max_norm), "bwd",
                  lambda: zk.clip_grad_norm(self.views, max_norm, norm_out=self.norm,
                                            workspace=self.ws_norm),
-                 [npar, npar], [npar, 1]),
+                 [npar], [npar, 1]),
         ]
 
 
