@@ -81,7 +81,7 @@ __device__ __forceinline__ void gelu32_fast_w(const double *tab, const float (&h
     ad[k] = fabs(hd[k]);
     const double a2 = hd[k] * hd[k];  // exact
     beyond[k] = a2 > kGeluTabAmax2;
-    int i = (int)fma(ad[k], kGeluTabK, a2);  // NaN -> 0, +inf -> INT_MAX
+    int i = (int)(fma(ad[k], kGeluTabK, a2) * kGeluTabS);  // NaN -> 0, +inf -> INT_MAX
     i = i < kGeluTabN - 1 ? i : kGeluTabN - 1;
     t[k] = tab + i * kGeluTabW;
   }

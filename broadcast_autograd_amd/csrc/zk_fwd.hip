@@ -27,12 +27,18 @@ constexpr int kBlock = 256;
 // block takes two vectors per lane to halve that traffic.
 constexpr int row_unroll(int epi) { (void)epi; return 1; }
 // The GeLU row kernel (long arithmetic per element, 64 VGPRs) runs a grid of
-// 8 blocks per CU (all resident at once) that loops over the tiles and
-// issues the next tile's loads before the current tile's arithmetic.
-// Measured on the [4096, 1024] step against one tile per block with two
-// vectors per lane: 10.1 against 11.0 us.
+// 2 blocks of 1024 lanes per CU (all resident at once, 8 waves per SIMD)
+// that loops over the tiles and issues the next tile's loads before the
+// current tile's arithmetic.  Each block stages the GeLU table in LDS once,
+// so few large blocks stage it least often.  Measured on the [4096, 1024]
+// step: 9.9 us, against 10.5 us with 8 blocks of 256 lanes per CU and
+// 11.0 us with one tile per block.
 constexpr bool kRowPrefetch = true;
-constexpr int kRowGeluBlocksPerCU = 8;
+// Rows (along the transposed operand's contiguous columns) per fwd_tile tile
+// (128 and 256 measured slower on the [4096, 4096] transposed product).
+constexpr int kTileRows = 64;
+constexpr int kRowGeluBlocksPerCU = 2;
+constexpr int kRowGeluBlk = 1024;  // threads per block of the GeLU row kernel
 
 // Launches give one block per tile; kernels loop over tiles with a grid
 // stride, so a grid capped here still covers any size.  (A dispatch counts
@@ -164,13 +170,13 @@ __device__ __forceinline__ I row_offset(const RowArgs &ra, I i) {
   return off;
 }
 
-template <int OP, int EPI, int VEC, int SMODE, bool SWAP, typename I>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_fwd_row(const float *big,
+template <int OP, int EPI, int VEC, int SMODE, bool SWAP, typename I, int BLK>
+__global__ __launch_bounds__(BLK) __attribute__((amdgpu_waves_per_eu(4))) void k_fwd_row(const float *big,
                                                     const float *small,
                                                     float *out, RowArgs ra) {
   __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
   constexpr int U = row_unroll(EPI);
-  constexpr I tile = (I)kBlock * U * VEC;
+  constexpr I tile = (I)BLK * U * VEC;
   const I n = (I)ra.numel;
   const I sin = (I)ra.ss[ra.rank - 1];
   if constexpr (VEC == 4) {
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     auto load = [&](I t, float4 *vb, float4 *vs) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const I i = t * tile + (I)threadIdx.x * 4 + (I)u * kBlock * 4;
+        const I i = t * tile + (I)threadIdx.x * 4 + (I)u * BLK * 4;
         if (i < n) {
           vb[u] = ld4_nt(big + i);
           if constexpr (SMODE == SM_ARG) {
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
       float4 res[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const I i = base + (I)u * kBlock * 4;
+        const I i = base + (I)u * BLK * 4;
         if (i < n) {
           float x[4], y[4], r[4];
 #pragma unroll
@@ -219,14 +225,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const I i = base + (I)u * kBlock * 4;
+        const I i = base + (I)u * BLK * 4;
         if (i < n) st4_nt(out + i, res[u]);
       }
       if constexpr (EPI == ZK_EPI_GELU) {
         while (redo_bits) {  // rare: near a rounding tie; reload the operands
           const int bit = __builtin_ctz(redo_bits);
           redo_bits &= redo_bits - 1;
-          const I i = base + (I)(bit >> 2) * kBlock * 4;
+          const I i = base + (I)(bit >> 2) * BLK * 4;
           const I off = SMODE == SM_ARG ? (I)0 : row_offset<I>(ra, i);
           const int k = bit & 3;
           float vsm;
@@ -266,8 +272,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   } else {
     if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
     // 64-bit loop counter: i + stride may pass 2^31 even when n does not
-    for (int64_t i64 = (int64_t)blockIdx.x * kBlock + threadIdx.x; i64 < (int64_t)n;
-         i64 += (int64_t)gridDim.x * kBlock) {
+    for (int64_t i64 = (int64_t)blockIdx.x * BLK + threadIdx.x; i64 < (int64_t)n;
+         i64 += (int64_t)gridDim.x * BLK) {
       const I i = (I)i64;
       const float vbig = big[i];
       const float vsm = SMODE == SM_ARG ? ra.sval : small[row_offset<I>(ra, i)];
@@ -287,11 +293,12 @@ struct TileArgs {
   int32_t tv;  // T's columns start 16-byte aligned: 128-bit loads
 };
 
-template <int OP, int EPI, int OMODE, bool SWAP>
+template <int OP, int EPI, int OMODE, bool SWAP, int TI>
 __global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
                                                      const float *oth,
                                                      float *out, TileArgs ta) {
-  __shared__ float tile[64][65];
+  // TI rows (along T's contiguous columns) x 64 columns per tile
+  __shared__ float tile[64][TI + 1];
   __shared__ double s_gelu[EPI == ZK_EPI_GELU ? kGeluTabLen : 1];
   if constexpr (EPI == ZK_EPI_GELU) gelu_tab_load(s_gelu);
   const int t = threadIdx.x;
@@ -303,15 +310,16 @@ __global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
     const int64_t tiles_r = ta.ntiles / ta.tiles_c;
     const int64_t tr_j = bt % ta.tiles_c;
     const int64_t tr_i = (bt / ta.tiles_c + tr_j) % tiles_r;
-    const int64_t i0 = tr_i * 64, j0 = tr_j * 64;
+    const int64_t i0 = tr_i * TI, j0 = tr_j * 64;
     if (ta.tv) {
-      // 128-bit loads down T's columns: lane (t & 15) takes rows 4(t&15)..+3
-      const int i4 = (t & 15) * 4, jq = t >> 4;
+      // 128-bit loads down T's columns: TI/4 lanes cover one column's run
+      constexpr int LPC = TI / 4, CPT = kBlock / LPC;  // lanes per column, columns per trip
+      const int i4 = (t % LPC) * 4, jq = t / LPC;
       const int64_t gi = i0 + i4;
-      float4 v[4];
+      float4 v[64 / CPT];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int64_t gj = j0 + jq + 16 * p;
+      for (int p = 0; p < 64 / CPT; ++p) {
+        const int64_t gj = j0 + jq + CPT * p;
         v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (gj < ta.C) {
           const float *src = tr + gi + gj * ta.ld;
@@ -325,15 +333,16 @@ __global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
         }
       }
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
+      for (int p = 0; p < 64 / CPT; ++p)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) tile[jq + 16 * p][i4 + k] = el(v[p], k);
+        for (int k = 0; k < 4; ++k) tile[jq + CPT * p][i4 + k] = el(v[p], k);
     } else {
-      const int i = t & 63, jq = t >> 6;
+      constexpr int CPT = kBlock / TI;
+      const int i = t % TI, jq = t / TI;
       const int64_t gi = i0 + i;
 #pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        const int j = jq + 4 * p;
+      for (int p = 0; p < 64 / CPT; ++p) {
+        const int j = jq + CPT * p;
         const int64_t gj = j0 + j;
         float v = 0.f;
         if (gi < ta.R && gj < ta.C) v = __builtin_nontemporal_load(tr + gi + gj * ta.ld);
@@ -346,7 +355,7 @@ __global__ __launch_bounds__(kBlock) void k_fwd_tile(const float *tr,
     const int64_t gj = j0 + j;
     if (gj < ta.C) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      for (int p = 0; p < TI / 16; ++p) {
         const int i = q + 16 * p;
         const int64_t gi = i0 + i;
         if (gi >= ta.R) continue;
@@ -740,14 +749,16 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
           constexpr int SM = decltype(SMc)::value;
           constexpr bool SW = decltype(SWc)::value != 0;
           using I = std::conditional_t<decltype(Ic)::value != 0, int64_t, int32_t>;
-          int64_t blocks = grid_of(c.numel, kBlock * row_unroll(EPI) * VEC);
-          if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+          constexpr int BLK = EPI == ZK_EPI_GELU ? kRowGeluBlk : kBlock;
+          int64_t blocks = grid_of(c.numel, BLK * row_unroll(EPI) * VEC);
+          // a dispatch counts work-items with 32 bits
+          if (blocks > kMaxBlocks * kBlock / BLK) blocks = kMaxBlocks * kBlock / BLK;
           if (EPI == ZK_EPI_GELU && kRowGeluBlocksPerCU > 0) {
             const int64_t cap = (int64_t)kRowGeluBlocksPerCU * cu_count();
             if (blocks > cap) blocks = cap;
           }
-          ZK_LAUNCH(prof, (k_fwd_row<OP, EPI, VEC, SM, SW, I>), dim3((unsigned)blocks),
-                    dim3(kBlock), 0, st,
+          ZK_LAUNCH(prof, (k_fwd_row<OP, EPI, VEC, SM, SW, I, BLK>), dim3((unsigned)blocks),
+                    dim3(BLK), 0, st,
                     big, small, out, ra);
           return hipGetLastError();
         };
@@ -777,7 +788,7 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         ta.os0 = c.s[ot_op][0];
         ta.os1 = c.s[ot_op][1];
         ta.tiles_c = (ta.C + 63) / 64;
-        ta.ntiles = ((ta.R + 63) / 64) * ta.tiles_c;
+        ta.ntiles = ((ta.R + kTileRows - 1) / kTileRows) * ta.tiles_c;
         ta.tv = ta.ld % 4 == 0 && ((uintptr_t)tr & 15u) == 0;
         unsigned grid = (unsigned)(ta.ntiles < kMaxBlocks ? ta.ntiles : kMaxBlocks);
         int om = SM_GATHER;
@@ -786,8 +797,8 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         auto go = [&](auto OMc, auto SWc) -> hipError_t {
           constexpr int OM = decltype(OMc)::value;
           constexpr bool SW = decltype(SWc)::value != 0;
-          ZK_LAUNCH(prof, (k_fwd_tile<OP, EPI, OM, SW>), dim3(grid), dim3(kBlock), 0, st,
-                    tr, ot, out, ta);
+          ZK_LAUNCH(prof, (k_fwd_tile<OP, EPI, OM, SW, kTileRows>), dim3(grid), dim3(kBlock),
+                    0, st, tr, ot, out, ta);
           return hipGetLastError();
         };
         auto go_sw = [&](auto OMc) -> hipError_t {
