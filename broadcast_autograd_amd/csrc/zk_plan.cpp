@@ -481,6 +481,8 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
   // Chunks of 256..2048 elements (whole wave trips), about 8192 of them:
   // short chunks over many waves stream best; partials stay < 0.1% of bytes.
   int64_t CL = std::min<int64_t>(2048, std::max<int64_t>(256, c.numel / 8192));
+  // at most 65536 partials per kept element, so that stage 2 stays short
+  CL = std::max<int64_t>(CL, ceil_div(R1 * inner, 65536));
   CL = ceil_div(CL, 256) * 256;
   if (CL >= inner) CL = inner;
   int64_t NC = ceil_div(inner, CL);

@@ -10,6 +10,7 @@ positions of the large outputs and on every element of the reduced ones.
 import itertools
 import math
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -122,7 +123,7 @@ def _rng_pair(shape_a, shape_b, seed, lo=0.5, hi=2.0, signed=True):
 ])
 @pytest.mark.parametrize("op", OPS)
 def test_row_scalar_broadcast(orc, shapes, op):
-    a, b = _rng_pair(*shapes, seed=hash((shapes, op)) % 2**31)
+    a, b = _rng_pair(*shapes, seed=zlib.crc32(repr((shapes, op)).encode()))
     check_pair(orc, op, a, dev(a), b, dev(b), seed=1)
     # operand order swapped: the broadcast operand first
     check_pair(orc, op, b, dev(b), a, dev(a), seed=2)
@@ -136,7 +137,7 @@ def test_row_scalar_broadcast(orc, shapes, op):
 ])
 @pytest.mark.parametrize("op", OPS)
 def test_column_broadcast(orc, shapes, op):
-    a, b = _rng_pair(*shapes, seed=hash((shapes, op)) % 2**31)
+    a, b = _rng_pair(*shapes, seed=zlib.crc32(repr((shapes, op)).encode()))
     check_pair(orc, op, a, dev(a), b, dev(b), seed=3)
     check_pair(orc, op, b, dev(b), a, dev(a), seed=4)
 
