@@ -320,8 +320,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(the per-GPU kernels are the same at 1/N of the rows; see the "
-              "sharding note in DESIGN.md).", file=sys.stderr)
+              "(sharded, each GPU would run the same kernels on 1/N of the rows, "
+              "then gather the small reduced gradients).", file=sys.stderr)
         sys.exit(2)
     import torch
     from broadcast_autograd_amd import zk, workloads as Wk
