@@ -42,6 +42,21 @@ def test_exports_every_declared_symbol(L):
             assert re.search(rf"\bT {name}$", out, re.M), name
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/zk.h compiles as C99 (and C++17): plain pointers, sizes and
+    enums only, usable from any language with a C FFI."""
+    gcc = shutil.which("gcc")
+    if not gcc:
+        pytest.skip("no gcc")
+    src = tmp_path / "use.c"
+    src.write_text('#include "zk.h"\nint main(void) { return (int)ZK_OK; }\n')
+    for lang, std in (("c", "-std=c99"), ("c++", "-std=c++17")):
+        r = subprocess.run([gcc, "-x", lang, std, "-Wall", "-Wextra", "-Werror",
+                            "-I", os.path.dirname(HEADER), "-fsyntax-only", str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
 def test_broadcast_shape_matches_oracle(L, orc):
     shapes = [s for r in range(4) for s in itertools.product((0, 1, 2, 3), repeat=r)]
     for sa in shapes:
