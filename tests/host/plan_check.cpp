@@ -3,7 +3,10 @@
 //  1. magic-number division agrees with '/' for random and edge operands;
 //  2. the canonical iteration space visits exactly the same per-operand
 //     offsets, in the same row-major order, as the uncanonicalised space,
-//     for random shapes, broadcasts and strides.
+//     for random shapes, broadcasts and strides;
+//  3. every reduction plan of random backward and reduce calls meets the
+//     shape assumptions its stage-1 kernel and launch are written for
+//     (patterns, divisibility, partial counts, grid limits, workspace).
 #include <cstdio>
 #include <cstdlib>
 #include <random>
@@ -98,6 +101,103 @@ int main() {
     for (int k = 0; k < c.rank; ++k)
       if (c.n[k] == 1 && c.rank > 1) return fail("size-1 kept", k, c.rank);
   }
+  // 3. reduction plans against the assumptions of their kernels
+  const int64_t sizes[] = {1, 2, 3, 4, 7, 9, 16, 64, 256, 260, 1024, 2048, 4096};
+  int seen[K_COUNT] = {0};
+  for (int t = 0; t < 20000; ++t) {
+    zk_desc da{}, db{};
+    const int r = 1 + (int)(rng() % 4);
+    da.rank = r;
+    int64_t numel = 1;
+    for (int k = 0; k < r; ++k) {
+      int64_t v = sizes[rng() % 13];
+      if (numel * v > ((int64_t)1 << 26)) v = 1;
+      da.sizes[k] = v;
+      numel *= v;
+    }
+    // b: a's shape with random dims set to 1, possibly fewer leading dims
+    const int rb = 1 + (int)(rng() % r);
+    db.rank = rb;
+    for (int k = 0; k < rb; ++k) {
+      const int64_t v = da.sizes[r - rb + k];
+      db.sizes[k] = (rng() % 2) ? v : 1;
+    }
+    for (zk_desc *d : {&da, &db}) {
+      int64_t s = 1;
+      for (int k = d->rank - 1; k >= 0; --k) { d->strides[k] = s; s *= d->sizes[k]; }
+    }
+    if (rng() % 2) std::swap(da, db);
+    const uintptr_t q = (rng() % 4) ? 0 : 4;  // aligned or not
+    BwdPlan p;
+    const zk_op op = (zk_op)(rng() % 4);
+    const zk_epi epi = (zk_epi)(rng() % 3);
+    const bool wa = rng() % 4 != 0, wb = rng() % 4 != 0;
+    zk_status st;
+    if (rng() % 3 == 0) {
+      st = plan_reduce(db.rank <= da.rank ? da : db, db.rank <= da.rank ? db.rank : da.rank,
+                       db.rank <= da.rank ? db.sizes : da.sizes, q, q, &p);
+    } else {
+      st = plan_bwd(op, epi, da, db, wa, wb, q, q, q, q, q, q, q, &p);
+    }
+    if (st != ZK_OK) continue;
+    const Canon &c = p.c;
+    size_t need = 0;
+    for (int i = 0; i < p.nred; ++i) {
+      const RedPlan &rp = p.red[i];
+      if (rp.kernel >= 0 && rp.kernel < K_COUNT) ++seen[rp.kernel];
+      need += (size_t)rp.partials * (size_t)rp.kept * 8u;
+      const int64_t inner = c.rank > 0 ? c.n[c.rank - 1] : 1;
+      switch (rp.kernel) {
+        case K_RED_COL: {
+          if (c.rank != 2 || rp.kept != c.n[1] || rp.red != c.n[0]) return fail("col shape", rp.kept, c.rank);
+          if (c.n[1] % 4 != 0) return fail("col K%4", c.n[1], 0);
+          if (!(rp.nw == 1 || rp.nw == 4 || rp.nw == 16)) return fail("col nw", rp.nw, 0);
+          if (rp.chunk < 1) return fail("col rcw", rp.chunk, 0);
+          const int64_t P = (c.n[0] + rp.nw * rp.chunk - 1) / (rp.nw * rp.chunk);
+          if (rp.partials != P) return fail("col partials", rp.partials, P);
+          if (((c.n[1] + 255) / 256) * P > kMaxGridBlocks) return fail("col grid", P, 0);
+          break;
+        }
+        case K_RED_ROW: {
+          if (inner % 4 != 0 || inner < 256) return fail("row inner", inner, 0);
+          if (rp.chunk != inner && rp.chunk % 256 != 0) return fail("row chunk", rp.chunk, inner);
+          const int64_t R1 = c.numel / inner / rp.kept;
+          const int64_t NC = (inner + rp.chunk - 1) / rp.chunk;
+          if (R1 * inner * rp.kept != c.numel) return fail("row cover", R1, rp.kept);
+          if (rp.partials != R1 * NC) return fail("row partials", rp.partials, R1 * NC);
+          break;
+        }
+        case K_RED_ROWD: {
+          if (rp.partials != 0 || inner % 4 != 0) return fail("rowd", rp.partials, inner);
+          if (rp.kept * rp.red != c.numel) return fail("rowd cover", rp.kept, rp.red);
+          if (rp.red < kDirMinTerms || rp.red > kDirMaxTerms) return fail("rowd terms", rp.red, 0);
+          if (!(rp.chunk == 1 || rp.chunk == 2 || rp.chunk == 4) || rp.red > 4096 * rp.chunk)
+            return fail("rowd vectors", rp.chunk, rp.red);
+          break;
+        }
+        case K_RED_GEND: {
+          if (rp.partials != 0 || rp.kept * rp.red != c.numel) return fail("gend", rp.kept, rp.red);
+          if (rp.red < kGenDirMinTerms || rp.red > kGenDirMaxTerms) return fail("gend terms", rp.red, 0);
+          break;
+        }
+        case K_RED_TILE: {
+          if (c.rank != 2 || c.n[1] % 4 != 0) return fail("tile shape", c.rank, c.n[1]);
+          if (rp.partials != (c.n[0] + 63) / 64) return fail("tile partials", rp.partials, 0);
+          break;
+        }
+        case K_RED_GENERIC: {
+          if (rp.red > 0 && rp.partials * rp.chunk < rp.red) return fail("gen cover", rp.partials, rp.red);
+          if (!p.empty_space && rp.kept * rp.red != c.numel) return fail("gen count", rp.kept, rp.red);
+          break;
+        }
+        default:
+          return fail("kernel", rp.kernel, 0);
+      }
+    }
+    if (p.workspace < need) return fail("workspace", (long long)p.workspace, (long long)need);
+  }
+  for (int k : {K_RED_COL, K_RED_ROW, K_RED_ROWD, K_RED_GEND, K_RED_TILE, K_RED_GENERIC})
+    if (k != K_RED_TILE && seen[k] == 0) return fail("class never planned", k, 0);
   std::printf("OK\n");
   return 0;
 }
