@@ -198,6 +198,62 @@ int main() {
   }
   for (int k : {K_RED_COL, K_RED_ROW, K_RED_ROWD, K_RED_GEND, K_RED_TILE, K_RED_GENERIC})
     if (k != K_RED_TILE && seen[k] == 0) return fail("class never planned", k, 0);
+  // 4. forward plans: the dense operand of fwd_row walks the output layout,
+  //    128-bit paths only on multiples of 4 and aligned pointers, rank <= 3
+  for (int t = 0; t < 20000; ++t) {
+    zk_desc da{}, db{};
+    const int r = 1 + (int)(rng() % 4);
+    da.rank = r;
+    int64_t numel = 1;
+    for (int k = 0; k < r; ++k) {
+      int64_t v = sizes[rng() % 13];
+      if (numel * v > ((int64_t)1 << 26)) v = 1;
+      da.sizes[k] = v;
+      numel *= v;
+    }
+    const int rb = (int)(rng() % (r + 1));
+    db.rank = rb;
+    for (int k = 0; k < rb; ++k) db.sizes[k] = (rng() % 2) ? da.sizes[r - rb + k] : 1;
+    for (zk_desc *d : {&da, &db}) {
+      int64_t s2 = 1;
+      for (int k = d->rank - 1; k >= 0; --k) { d->strides[k] = s2; s2 *= d->sizes[k]; }
+    }
+    if (r == 2 && rng() % 3 == 0) {  // a transposed view
+      std::swap(da.sizes[0], da.sizes[1]);
+      da.strides[0] = 1;
+      da.strides[1] = da.sizes[0];
+    }
+    if (rng() % 2) std::swap(da, db);
+    const uintptr_t pa = (rng() % 4) ? 0 : 4, pb = (rng() % 4) ? 0 : 4, po = (rng() % 4) ? 0 : 4;
+    FwdPlan f;
+    if (plan_fwd((zk_op)(rng() % 4), (zk_epi)(rng() % 3), da, db, pa, pb, po, &f) != ZK_OK)
+      continue;
+    if (f.empty) continue;
+    const Canon &c = f.c;
+    const int64_t inner = c.n[c.rank - 1];
+    switch (f.kernel) {
+      case K_FWD_FLAT:
+        if (f.vec == 4 && (pa || pb || po)) return fail("flat vec align", f.vec, 0);
+        break;
+      case K_FWD_ROW: {
+        if (c.rank > 3) return fail("row rank", c.rank, 0);
+        const int big = f.swap ? 2 : 1;
+        for (int k = 0; k < c.rank; ++k)
+          if (c.n[k] > 1 && c.s[big][k] != c.s[0][k]) return fail("row dense", k, c.s[big][k]);
+        if (f.vec == 4 && (inner % 4 != 0 || po || (f.swap ? pb : pa)))
+          return fail("row vec", inner, 0);
+        break;
+      }
+      case K_FWD_TILE:
+        if (c.rank != 2 || f.vec != 4 || c.n[1] % 4 != 0 || po) return fail("tile", c.rank, c.n[1]);
+        break;
+      case K_FWD_GENERIC:
+        if (f.vec == 4 && po) return fail("generic vec align", 0, 0);
+        break;
+      default:
+        return fail("fwd kernel", f.kernel, 0);
+    }
+  }
   std::printf("OK\n");
   return 0;
 }
