@@ -242,3 +242,35 @@ def test_clip_gpt_parameter_list(orc):
     norm = zk.clip_grad_norm(ts, 1.0)
     _check_norm(host(norm), want[1], "gpt norm")
     _check_clip(ts, hs, want, "gpt clip")
+
+
+def test_clip_threshold_edges(orc):
+    """max_norm = 0 scales by 0 (any nonzero norm exceeds it) and leaves all
+    zeros untouched; max_norm = inf never scales; rank-0 and empty tensors in
+    the list."""
+    h = np.random.default_rng(21).standard_normal(1000).astype(np.float32)
+    for c in (0.0, float("inf")):
+        t = dev(h)
+        s = dev(np.array(2.5, np.float32))
+        e = torch.zeros(0, device="cuda")
+        norm = float(host(zk.clip_grad_norm([t, s.reshape(1), e], c)))
+        outs, n64, clipped, f = orc.clip_grad_norm([h, np.array([2.5], np.float32)], c)
+        assert np.float32(norm) == np.float32(n64)
+        assert_bitexact(host(t), outs[0], f"clip c={c}")
+        assert_bitexact(host(s).reshape(1), outs[1], f"clip scalar c={c}")
+        assert clipped == (c == 0.0)
+    z = torch.zeros(100, device="cuda")
+    assert float(host(zk.clip_grad_norm([z], 0.0))) == 0.0
+    assert np.all(host(z) == 0)
+
+
+def test_mean_rank0_and_size1(orc):
+    """Means over nothing (rank 0, all size-1 dims) are copies; the gradient
+    through them is the upstream gradient itself."""
+    x = np.array(3.25, np.float32)
+    assert float(host(zk.mean_to_shape(dev(x), ()))) == 3.25
+    y = np.random.default_rng(22).standard_normal((1, 1, 5)).astype(np.float32)
+    assert_bitexact(host(zk.mean_to_shape(dev(y), (1, 5))), y.reshape(1, 5))
+    g = np.random.default_rng(23).standard_normal((1, 5)).astype(np.float32)
+    assert_bitexact(host(zk.mean_bwd(dev(g), (1, 1, 5))), g.reshape(1, 1, 5))
+    assert_bitexact(host(zk.mean_bwd(dev(x), ())), x)
