@@ -366,8 +366,12 @@ zk_status check_grad_list(int32_t count, const void *const *grads, const int64_t
                           bool ptrs) {
   if (count < 0) return ZK_ERR_BAD_SIZE;
   if (count > 0 && !numels) return ZK_ERR_NULL;
-  for (int t = 0; t < count; ++t)
-    if (numels[t] < 0) return ZK_ERR_BAD_SIZE;
+  int64_t total = 0;
+  for (int t = 0; t < count; ++t) {
+    if (numels[t] < 0 || numels[t] > kMaxExtent) return ZK_ERR_BAD_SIZE;
+    if (__builtin_add_overflow(total, numels[t], &total) || total > kMaxExtent)
+      return ZK_ERR_BAD_SIZE;
+  }
   if (!ptrs) return ZK_OK;
   if (count > 0 && !grads) return ZK_ERR_NULL;
   std::vector<std::pair<uintptr_t, uintptr_t>> ext;
@@ -481,9 +485,13 @@ zk_status zk_clip_grad_norm(int32_t count, float *const *grads, const int64_t *n
 namespace {
 zk_status row_stats_common(int mode, const float *x, int64_t rows, int64_t cols, int64_t ld,
                            float *o1, float *o2, void *stream) {
-  if (rows < 0 || cols < 0) return ZK_ERR_BAD_SIZE;
+  if (rows < 0 || cols < 0 || rows > kMaxExtent || cols > kMaxExtent) return ZK_ERR_BAD_SIZE;
   if (ld < cols || (rows > 1 && ld < 1)) return ZK_ERR_BAD_STRIDE;
   if (rows == 0) return ZK_OK;
+  int64_t last = 0;  // one past the last element read
+  if (cols > 0 && (__builtin_mul_overflow(rows - 1, ld, &last) ||
+                   __builtin_add_overflow(last, cols, &last) || last > kMaxExtent))
+    return ZK_ERR_BAD_STRIDE;
   if (!o1 || !o2) return ZK_ERR_NULL;
   if (cols > 0 && !x) return ZK_ERR_NULL;
   const Ext e1 = ext_dense(o1, rows), e2 = ext_dense(o2, rows);

@@ -34,10 +34,26 @@ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 zk_status check_desc(const zk_desc *d) {
   if (!d) return ZK_ERR_NULL;
   if (d->rank < 0 || d->rank > kMaxDims) return ZK_ERR_RANK;
-  for (int k = 0; k < d->rank; ++k)
+  bool empty = false;
+  for (int k = 0; k < d->rank; ++k) {
     if (d->sizes[k] < 0) return ZK_ERR_BAD_SIZE;
+    empty = empty || d->sizes[k] == 0;
+  }
   for (int k = 0; k < d->rank; ++k)
     if (d->strides[k] < 0) return ZK_ERR_BAD_STRIDE;
+  if (empty) return ZK_OK;  // nothing is read or written
+  // The element count and the largest element offset stay below kMaxExtent,
+  // so every count, offset and byte extent formed from them fits in int64.
+  int64_t numel = 1, last = 0;
+  for (int k = 0; k < d->rank; ++k) {
+    if (__builtin_mul_overflow(numel, d->sizes[k], &numel) || numel > kMaxExtent)
+      return ZK_ERR_BAD_SIZE;
+    int64_t span = 0;
+    if (d->sizes[k] > 1 &&
+        (__builtin_mul_overflow(d->sizes[k] - 1, d->strides[k], &span) ||
+         __builtin_add_overflow(last, span, &last) || last > kMaxExtent))
+      return ZK_ERR_BAD_STRIDE;
+  }
   return ZK_OK;
 }
 
@@ -57,6 +73,13 @@ zk_status broadcast_shape(int ra, const int64_t *na, int rb, const int64_t *nb,
     else if (y == 1) tmp[k] = x;
     else return ZK_ERR_BROADCAST;
   }
+  // the broadcast shape may hold more elements than either operand
+  int64_t numel = 1;
+  bool empty = false;
+  for (int k = 0; k < r; ++k) empty = empty || tmp[k] == 0;
+  for (int k = 0; k < r && !empty; ++k)
+    if (__builtin_mul_overflow(numel, tmp[k], &numel) || numel > kMaxExtent)
+      return ZK_ERR_BAD_SIZE;
   *ro = r;
   for (int k = 0; k < r; ++k) no[k] = tmp[k];
   return ZK_OK;

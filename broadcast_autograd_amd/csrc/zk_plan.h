@@ -19,6 +19,8 @@ constexpr int kMaxOps = 5;
 // Largest grid the planner sizes a non-looping launch for: a dispatch counts
 // work-items with 32 bits, and blocks have at most 1024 threads.
 constexpr int64_t kMaxGridBlocks = (int64_t)1 << 22;
+// Largest element count, and largest element offset, of any view (2^62).
+constexpr int64_t kMaxExtent = (int64_t)1 << 62;
 
 // Waves per red_col block (they combine their column sums in LDS): with
 // fewer than kColRowsMany rows per wave, and with that many.  The kernel is

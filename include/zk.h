@@ -54,8 +54,10 @@ typedef enum {
   ZK_OK = 0,
   ZK_ERR_NULL = 1,        /* a required pointer is NULL                     */
   ZK_ERR_RANK = 2,        /* rank < 0 or > ZK_MAX_DIMS                      */
-  ZK_ERR_BAD_SIZE = 3,    /* a size is negative                             */
-  ZK_ERR_BAD_STRIDE = 4,  /* a stride is negative                           */
+  ZK_ERR_BAD_SIZE = 3,    /* a size is negative, or a view, a broadcast     */
+                          /* shape or a tensor holds more than 2^62 elements */
+  ZK_ERR_BAD_STRIDE = 4,  /* a stride is negative, or a view's largest     */
+                          /* element offset exceeds 2^62                   */
   ZK_ERR_BROADCAST = 5,   /* shapes do not broadcast                        */
   ZK_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
   ZK_ERR_WORKSPACE = 7,   /* workspace smaller than required                */
@@ -339,7 +341,8 @@ zk_status zk_mean_bwd(const float *grad, int32_t rank_out, const int64_t *sizes_
  * written to the gradients.
  * Aliasing: the tensors may not overlap each other, norm_out or the
  * workspace (ZK_ERR_ALIAS).
- * Errors: ZK_ERR_NULL, ZK_ERR_BAD_SIZE (negative count or numel),
+ * Errors: ZK_ERR_NULL, ZK_ERR_BAD_SIZE (negative count or numel, or more
+ *         than 2^62 elements in all),
  *         ZK_ERR_ALIAS, ZK_ERR_WORKSPACE, ZK_ERR_HIP; zk_clip_grad_norm
  *         also ZK_ERR_UNSUPPORTED for a max_norm that is negative or NaN.
  */
@@ -371,7 +374,8 @@ zk_status zk_clip_grad_norm(int32_t count, float *const *grads, const int64_t *n
  * of up to 4096 elements are read once, longer rows twice.  No workspace.
  * Aliasing: the outputs may not overlap each other or the extent of x
  * (ZK_ERR_ALIAS).  Errors: ZK_ERR_BAD_SIZE (negative rows or cols),
- * ZK_ERR_BAD_STRIDE (ld < cols), ZK_ERR_NULL, ZK_ERR_ALIAS, ZK_ERR_HIP.
+ * ZK_ERR_BAD_STRIDE (ld < cols, or (rows - 1) * ld + cols above 2^62),
+ * ZK_ERR_NULL, ZK_ERR_ALIAS, ZK_ERR_HIP.
  */
 zk_status zk_row_moments(const float *x, int64_t rows, int64_t cols, int64_t ld, float *mean,
                          float *var, void *stream);

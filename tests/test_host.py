@@ -115,6 +115,22 @@ def test_forward_validation_errors(L):
     negs = zk.make_desc((2, 3), (-3, 1))
     assert _fwd(0, negs, d23) == "ZK_ERR_BAD_STRIDE"
     assert _fwd(0, zk.make_desc((2, 3, 4)), zk.make_desc((2, 4, 5))) == "ZK_ERR_BROADCAST"
+    # int64 extents: element counts and largest offsets above 2^62 are refused
+    huge = zk.make_desc((1 << 31, 1 << 32), (0, 0))
+    assert _fwd(0, huge, zk.make_desc((1,))) == "ZK_ERR_BAD_SIZE"
+    far = zk.make_desc((2, 3), (1 << 62, 1))
+    assert _fwd(0, far, d23) == "ZK_ERR_BAD_STRIDE"
+    wrap = zk.make_desc((3, 3), (1 << 62, 1 << 62))
+    assert _fwd(0, wrap, zk.make_desc((3, 3))) == "ZK_ERR_BAD_STRIDE"
+    col = zk.make_desc((1 << 31, 1), (1, 0))
+    row = zk.make_desc((1, 1 << 32), (0, 1))
+    assert _fwd(0, col, row) == "ZK_ERR_BAD_SIZE"  # each fits, their broadcast does not
+    with pytest.raises(zk.ZkError) as e:
+        zk.broadcast_shape((1 << 31, 1), (1, 1 << 32))
+    assert e.value.name == "ZK_ERR_BAD_SIZE"
+    # an empty view reads nothing: its strides may be anything non-negative
+    empty = zk.make_desc((0, 3), (1 << 62, 1 << 62))
+    assert _fwd(0, empty, zk.make_desc((3,))) == "ZK_OK"
     assert _fwd(0, d23, d23, a=None) == "ZK_ERR_NULL"
     assert _fwd(0, d23, d23, out=None) == "ZK_ERR_NULL"
     assert zk.STATUS[L.zk_binary_fwd(0, 0, FA, None, FB, ctypes.byref(d23), FO, None)] == "ZK_ERR_NULL"
@@ -277,6 +293,8 @@ def test_grad_norm_validation_errors(L):
     assert st == "ZK_OK" and need == 8 * 4
     assert q([])[1] == 8
     assert q([-1])[0] == "ZK_ERR_BAD_SIZE"
+    assert q([1 << 62, 1])[0] == "ZK_ERR_BAD_SIZE"  # more than 2^62 elements in all
+    assert q([(1 << 63) - 1])[0] == "ZK_ERR_BAD_SIZE"
 
     def call(ptrs, ns, ws=FW, wsb=1 << 30, norm=FO, clip=None):
         arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[p.value if p else None for p in ptrs])
@@ -310,6 +328,7 @@ def test_row_stats_validation_errors(L):
         assert call(rows=-1) == "ZK_ERR_BAD_SIZE"
         assert call(cols=-1) == "ZK_ERR_BAD_SIZE"
         assert call(ld=7) == "ZK_ERR_BAD_STRIDE"
+        assert call(rows=1 << 40, ld=1 << 30) == "ZK_ERR_BAD_STRIDE"  # offset above 2^62
         assert call(x=None) == "ZK_ERR_NULL"
         assert call(o2=None) == "ZK_ERR_NULL"
         assert call(o1=ctypes.c_void_p(FA.value + 64)) == "ZK_ERR_ALIAS"
