@@ -111,6 +111,14 @@ def main():
     print(f"forward table: {len(rows)} pieces of degree {TAB_DEG}, erfc rel err {terr:.2e}")
     me, a, b = fit_erfcx(9)
     e32 = report_f32(me, a, b)
+    # Rows are padded with zeros to a stride of an odd number of 16-byte
+    # units: lanes reading random rows with 128-bit LDS reads then start in
+    # all 16 of the LDS's 16-byte bank groups (a stride of 64 bytes would
+    # use 4 of them, and its reads would conflict four times as often).
+    stride = TAB_DEG + 2 + (TAB_DEG % 2)
+    if (stride // 2) % 2 == 0:
+        stride += 2
+    rows = [list(r) + [0.0] * (stride - len(r)) for r in rows]
     tab = ",\n    ".join(", ".join(float(v).hex() for v in r) for r in rows)
     hdr = ("// zk_gelu_coeffs.h -- generated by gen_gelu_coeffs.py; do not edit.\n"
            "// Forward: erfc(a/sqrt2), a = |h| with a^2 <= kGeluTabAmax2, as piecewise\n"
@@ -121,10 +129,11 @@ def main():
            f"// forward table: erfc rel. error {terr:.2e} (dense-grid maximum at fit time)\n"
            f"static constexpr int kGeluTabN = {len(rows)};\n"
            f"static constexpr int kGeluTabW = {TAB_DEG + 2};  // mid, c_0 .. c_{TAB_DEG}\n"
+           f"static constexpr int kGeluTabStride = {stride};  // doubles per row (zero padded)\n"
            f"static constexpr double kGeluTabK = {float(TAB_K).hex()};\n"
            f"static constexpr double kGeluTabS = {float(TAB_S).hex()};  // pieces per unit of w\n"
            f"static constexpr double kGeluTabAmax2 = {float(TAB_AMAX * TAB_AMAX).hex()};\n"
-           f"static constexpr double kGeluTab[{len(rows) * (TAB_DEG + 2)}] = {{\n    {tab}}};\n\n"
+           f"static constexpr double kGeluTab[{len(rows) * stride}] = {{\n    {tab}}};\n\n"
            f"static constexpr double kErfcxK = {float(K).hex()};\n"
            f"static constexpr double kErfcxUmax = {float(UMAX).hex()};\n\n"
            f"// F32: erfcx rel. error {e32:.2e} evaluated in binary32\n"

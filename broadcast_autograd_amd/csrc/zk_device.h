@@ -49,7 +49,7 @@ __device__ __attribute__((noinline)) float gelu32_libm(float h) {
 // of the index does not matter), E = sum c_k d^k, d = a - mid_i, Horner in
 // binary64.  Error of the binary64 result: fit ~9e-15 plus ~12 binary64
 // roundings, below 2^-46 relative.
-constexpr int kGeluTabLen = kGeluTabN * kGeluTabW;
+constexpr int kGeluTabLen = kGeluTabN * kGeluTabStride;
 
 // Copies the table into the block's LDS; every thread of the block calls it.
 __device__ __forceinline__ void gelu_tab_load(double *lds) {
@@ -83,7 +83,7 @@ __device__ __forceinline__ void gelu32_fast_w(const double *tab, const float (&h
     beyond[k] = a2 > kGeluTabAmax2;
     int i = (int)(fma(ad[k], kGeluTabK, a2) * kGeluTabS);  // NaN -> 0, +inf -> INT_MAX
     i = i < kGeluTabN - 1 ? i : kGeluTabN - 1;
-    t[k] = tab + i * kGeluTabW;
+    t[k] = tab + i * kGeluTabStride;
   }
 #pragma unroll
   for (int k = 0; k < W; ++k) {
