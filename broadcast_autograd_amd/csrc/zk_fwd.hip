@@ -10,6 +10,7 @@
 //   tile    : rank 2 with a transposed operand (x[i,j] at i + j*ld); 64x64
 //             tiles are staged through LDS so both HBM sides are coalesced
 //   generic : any rank <= 8, per-element offsets
+#include <atomic>
 #include <type_traits>
 
 #include "zk_device.h"
@@ -691,18 +692,23 @@ __global__ __launch_bounds__(kBlock) void k_copy_generic(const float *in, float 
 
 // -------------------------------------------------------------- launcher
 // Compute units of the current device (queried once per process).
+// Compute units of the current device, looked up once per device (a relaxed
+// atomic cache: concurrent first calls store the same value).  It sizes the
+// resident GeLU grid only; no result depends on it.
 static int cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        n > 0)
-      cus = n;
-    else
-      cus = 256;
+  constexpr int kDevCache = 64;
+  static std::atomic<int> cache[kDevCache] = {};
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kDevCache) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
   }
-  return cus;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev < kDevCache) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 static inline unsigned grid_of(int64_t n, int64_t per_block) {
