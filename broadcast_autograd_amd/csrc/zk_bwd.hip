@@ -906,6 +906,10 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
 // belongs to exactly one kept element), and finish the sum themselves
 // (sign, acc, divisor; rounded once): no partials, no stage 2, no separate
 // element-wise pass.
+// Terms per lane and trip, their loads issued together (rank-8 workload,
+// 384 terms a kept element: 10.0 us with 2, 10.6 with 4, 11.3 with 8).
+constexpr int kGendU = 2;
+
 struct GenDirArgs {
   GenArgs ga;
   int32_t write_big, big_acc;  // big_acc: 0 none, 1 acc is g, 2 a buffer
@@ -964,13 +968,13 @@ __global__ __launch_bounds__(kBlk) void k_red_gend(const float *g, const float *
       }
     }
     double s = 0.0;
-    // two terms per trip, their loads issued together
-    for (I t0 = (I)j; kok && t0 < (I)ga.red; t0 += 2 * TPK) {
-      I ig[2], ia[2], ib[2];
-      float gv[2], x[2], y[2];
-      bool ok[2];
+    // kGendU terms per trip, their loads issued together
+    for (I t0 = (I)j; kok && t0 < (I)ga.red; t0 += kGendU * TPK) {
+      I ig[kGendU], ia[kGendU], ib[kGendU];
+      float gv[kGendU], x[kGendU], y[kGendU];
+      bool ok[kGendU];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kGendU; ++u) {
         const I tt = t0 + (I)(u * TPK);
         ok[u] = tt < (I)ga.red;
         I dg, dA, dB;
@@ -980,7 +984,7 @@ __global__ __launch_bounds__(kBlk) void k_red_gend(const float *g, const float *
         ib[u] = ob + dB;
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kGendU; ++u) {
         if (ok[u]) {
           gv[u] = g[ig[u]];
           x[u] = RA ? a[ia[u]] : 0.f;
@@ -988,7 +992,7 @@ __global__ __launch_bounds__(kBlk) void k_red_gend(const float *g, const float *
         }
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kGendU; ++u) {
         if (!ok[u]) continue;
         if constexpr (IDENT) {
           s += (double)gv[u];
