@@ -906,6 +906,7 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
 // belongs to exactly one kept element), and finish the sum themselves
 // (sign, acc, divisor; rounded once): no partials, no stage 2, no separate
 // element-wise pass.
+
 // Terms per lane and trip, their loads issued together (rank-8 workload,
 // 384 terms a kept element: 10.0 us with 2, 10.6 with 4, 11.3 with 8).
 constexpr int kGendU = 2;
