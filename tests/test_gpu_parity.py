@@ -428,6 +428,44 @@ def test_determinism(orc):
     assert np.array_equal(r[0].view(np.uint32), r[1].view(np.uint32))
 
 
+@pytest.mark.parametrize("case", ["red_col", "red_col_gelu", "red_rowd"])
+def test_determinism_concurrent_streams(orc, case):
+    """The partition depends on the shapes only: a backward run alone and two
+    copies of it running at once on two streams (other occupancy, other
+    timing) give the same bits, within tolerance of the oracle."""
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    if case == "red_col":
+        op, epi, sa, sb = "mul", "none", (2048, 4096), (4096,)
+    elif case == "red_col_gelu":
+        op, epi, sa, sb = "add", "gelu", (1024, 1024), (1024,)
+    else:
+        op, epi, sa, sb = "mul", "none", (64, 128, 256), (128, 1)
+    a_np = rng.standard_normal(sa).astype(np.float32)
+    b_np = rng.standard_normal(sb).astype(np.float32)
+    g_np = rng.standard_normal(sa).astype(np.float32)
+    a, b, g = dev(a_np), dev(b_np), dev(g_np)
+    nb = zk.bwd_workspace_bytes(op, a, b, epi=epi)
+    outs = [(torch.empty_like(a), torch.empty_like(b), zk._workspace(nb, a.device))
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    zk.binary_bwd(op, g, a, b, grad_a=outs[0][0], grad_b=outs[0][1], workspace=outs[0][2],
+                  epi=epi)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for s, o in zip(streams, outs[1:]):
+        zk.binary_bwd(op, g, a, b, grad_a=o[0], grad_b=o[1], workspace=o[2], epi=epi,
+                      stream=s)
+    torch.cuda.synchronize()
+    ref = [host(x).copy() for x in outs[0][:2]]
+    for o in outs[1:]:
+        for x, r in zip(o[:2], ref):
+            assert np.array_equal(host(x).view(np.uint32), r.view(np.uint32))
+    e = orc.EPI_GELU if epi == "gelu" else orc.EPI_NONE
+    ra, rb = orc.bwd(op, g_np, a_np, b_np, epi=e)
+    assert_bwd(ref[0], ra, "grad_a")
+    assert_bwd(ref[1], rb, "grad_b")
+
+
 def test_mass_invariant_gpu():
     rng = np.random.default_rng(71)
     g = rng.standard_normal((64, 130, 64)).astype(np.float32)
