@@ -98,6 +98,12 @@ bool same_view(const zk_desc &x, const zk_desc &y) {
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// The kernels keep binary64 partials in the workspace: 8-byte alignment
+// (hipMalloc and torch allocations are 256-byte aligned).
+bool ws_aligned(const void *ws, size_t need) {
+  return need == 0 || ((uintptr_t)ws & 7u) == 0;
+}
+
 size_t reduce_workspace(const zk_desc &din, int rout, const int64_t *nout);
 
 // Layout of the fused backward's workspace (shapes only):
@@ -283,7 +289,7 @@ zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad, const float *a,
     *workspace_bytes = need;
     return ZK_OK;
   }
-  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  if (*workspace_bytes < need || !ws_aligned(workspace, need)) return ZK_ERR_WORKSPACE;
   const int64_t n = p.c.numel;
   const int64_t na = numel(*da), nb = numel(*db);
   if (n > 0 && (!grad || !a || !b)) return ZK_ERR_NULL;
@@ -344,7 +350,7 @@ zk_status reduce_common(const float *in, const zk_desc *din, int32_t rank_out,
     *workspace_bytes = need;
     return ZK_OK;
   }
-  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  if (*workspace_bytes < need || !ws_aligned(workspace, need)) return ZK_ERR_WORKSPACE;
   int64_t nout = 1;
   for (int k = 0; k < rank_out; ++k) nout *= sizes_out[k];
   if (p.c.numel > 0 && !in) return ZK_ERR_NULL;
@@ -401,7 +407,7 @@ zk_status norm_common(int32_t count, float *const *grads, const int64_t *numels,
     *workspace_bytes = need;
     return ZK_OK;
   }
-  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  if (*workspace_bytes < need || !ws_aligned(workspace, need)) return ZK_ERR_WORKSPACE;
   if (!norm_out) return ZK_ERR_NULL;
   const Ext ew{(uintptr_t)workspace, (uintptr_t)workspace + need};
   const Ext en = ext_dense(norm_out, 1);
@@ -662,7 +668,7 @@ zk_status zk_binary2_bwd(zk_op op1, zk_op op2, const float *grad, const float *a
     *workspace_bytes = need;
     return ZK_OK;
   }
-  if (*workspace_bytes < need) return ZK_ERR_WORKSPACE;
+  if (*workspace_bytes < need || !ws_aligned(workspace, need)) return ZK_ERR_WORKSPACE;
   char *ws = static_cast<char *>(workspace);
   float *tbuf = split && (wa || wb) ? reinterpret_cast<float *>(ws + L.op1 + L.cred) : nullptr;
   const float *up = tbuf ? tbuf : grad;  // upstream gradient of t

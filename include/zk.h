@@ -60,7 +60,8 @@ typedef enum {
                           /* element offset exceeds 2^62                   */
   ZK_ERR_BROADCAST = 5,   /* shapes do not broadcast                        */
   ZK_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
-  ZK_ERR_WORKSPACE = 7,   /* workspace smaller than required                */
+  ZK_ERR_WORKSPACE = 7,   /* workspace smaller than required, or not       */
+                          /* 8-byte aligned                                */
   ZK_ERR_UNSUPPORTED = 8, /* unknown op / epilogue value                    */
   ZK_ERR_HIP = 9,         /* a kernel launch failed                         */
   ZK_ERR_SHAPE = 10       /* reduce target does not broadcast to the input  */
@@ -142,9 +143,11 @@ zk_status zk_binary_fwd(zk_op op, zk_epi epi, const float *a,
  *   workspace      : device scratch owned by the caller.  Pass NULL to query:
  *                    the required size is written to *workspace_bytes and
  *                    nothing is launched.  Otherwise *workspace_bytes is the
- *                    size provided; too small -> ZK_ERR_WORKSPACE.  The size
- *                    depends on the shapes only.  Contents need no
- *                    initialisation and are garbage afterwards.
+ *                    size provided; too small, or a base that is not 8-byte
+ *                    aligned (hipMalloc and torch allocations are), ->
+ *                    ZK_ERR_WORKSPACE.  The size depends on the shapes only.
+ *                    Contents need no initialisation and are garbage
+ *                    afterwards.
  * Sums are accumulated in binary64 in an order fixed by the shapes and
  * rounded once to binary32 (bitwise reproducible run to run).
  * Aliasing: outputs may not overlap each other, `grad`, a, b or the

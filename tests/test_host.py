@@ -155,6 +155,8 @@ def test_backward_validation_errors(L):
                       a=ctypes.c_void_p(FA.value + 4))
     assert st2 == "ZK_OK" and need2 == need
     assert _bwd(2, da, db, ws=ctypes.c_void_p(6 << 20), wsb=need - 1)[0] == "ZK_ERR_WORKSPACE"
+    # binary64 partials need an 8-byte aligned workspace
+    assert _bwd(2, da, db, ws=ctypes.c_void_p((6 << 20) + 4), wsb=need + 8)[0] == "ZK_ERR_WORKSPACE"
     ws = ctypes.c_void_p(6 << 20)
     # outputs overlapping each other, the inputs, the upstream grad or the workspace
     assert _bwd(2, da, db, ws=ws, ga=FO, gb=ctypes.c_void_p(FO.value + 8))[0] == "ZK_ERR_ALIAS"
@@ -245,6 +247,7 @@ def test_reduce_validation_errors(L):
     st, need = red((6,))
     assert st == "ZK_OK" and need > 0
     assert red((6,), ws=FW, wsb=need - 1)[0] == "ZK_ERR_WORKSPACE"
+    assert red((6,), ws=ctypes.c_void_p(FW.value + 4), wsb=need + 8)[0] == "ZK_ERR_WORKSPACE"
     assert red((6,), ws=FW, out=FA)[0] == "ZK_ERR_ALIAS"
     assert red((6,), ws=FW, out=ctypes.c_void_p(FW.value + 8))[0] == "ZK_ERR_ALIAS"
 
@@ -307,6 +310,7 @@ def test_grad_norm_validation_errors(L):
         return zk.STATUS[st]
 
     assert call([FA, FB], [100, 100], wsb=8) == "ZK_ERR_WORKSPACE"
+    assert call([FA, FB], [100, 100], ws=ctypes.c_void_p(FW.value + 4)) == "ZK_ERR_WORKSPACE"
     assert call([FA, None], [100, 100]) == "ZK_ERR_NULL"
     assert call([FA, FB], [100, 100], norm=None) == "ZK_ERR_NULL"
     # overlapping tensors, a tensor over the workspace or over norm_out
