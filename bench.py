@@ -42,7 +42,9 @@ ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
        # ClipGradNorm over the GPT configuration's parameter gradients
        "gpt_loss_mean_clip",
        # per-row statistics: LayerNorm mean / variance, softmax max / sum exp
-       "gpt_row_stats"]
+       "gpt_row_stats",
+       # the attention mask's gradient: scores' gradient summed to [1,1,1024,1024]
+       "attn_mask_grad"]
 ROTATE_BYTES = 1 << 30  # per-workload footprint of the rotating buffer sets
 MAX_SETS = 32
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -335,6 +337,7 @@ def main():
         gen[w + "_fused"] = gen[w]
     gen["gpt_loss_mean_clip"] = Wk.gpt_loss_mean_clip
     gen["gpt_row_stats"] = Wk.gpt_row_stats
+    gen["attn_mask_grad"] = Wk.attn_mask_grad
     log(f"[bench] device {torch.cuda.get_device_name(0)}; spin check "
         f"{spin_seconds(torch) * 1e3:.1f} ms")
     ceiling = copy_ceiling(torch)
@@ -354,7 +357,7 @@ def main():
         else [w for w in args.others.split(",") if w and w != args.workload])
     for w in others:
         big = w.replace("_fused", "") in ("attn_scale_mask", "gpt_residual",
-                                          "strided_transposed")
+                                          "strided_transposed", "attn_mask_grad")
         K = args.other_steps or (40 if big else 400)
         log(f"[bench] workload {w}: {K} steps")
         r = measure(w, gen[w](), K, K // 10, torch)

@@ -484,7 +484,14 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
     const int64_t R0 = c.n[0];
     const int64_t colblocks = ceil_div(c.n[1], 256);
     int64_t rcw = std::min<int64_t>(kColRowsMany, std::max<int64_t>(4, R0 * colblocks / 8192));
-    const int nw = rcw >= kColRowsMany ? kColWavesMany : kColWavesFew;
+    int nw = rcw >= kColRowsMany ? kColWavesMany : kColWavesFew;
+    // Short columns (fewer rows than a block spans, e.g. [128, 1048576]):
+    // kColWavesFew waves (one below that many rows) split the rows evenly,
+    // one partial a column, rather than most waves of a block idling.
+    if (R0 < nw * rcw) {
+      nw = R0 >= kColWavesFew ? kColWavesFew : 1;
+      rcw = std::max<int64_t>(1, ceil_div(R0, nw));
+    }
     while (colblocks * ceil_div(R0, nw * rcw) > kMaxGridBlocks) rcw *= 2;
     rp->chunk = rcw;
     rp->nw = nw;

@@ -141,6 +141,28 @@ class AttnScaleMask(Workload):
         ]
 
 
+class AttnMaskGrad(Workload):
+    """The attention mask's gradient: g[8,16,1024,1024] summed back to the
+    mask's shape [1,1,1024,1024] (a column reduction over 128 rows)."""
+    name = "attn_mask_grad"
+
+    def __init__(self, host=None, b=8, h=16, t=1024):
+        import torch
+        hh = host or W.attn_mask_grad(b, h, t)
+        self.host = hh
+        self.g = torch.from_numpy(hh["g"]).to("cuda")
+        self.target = (1, 1) + tuple(self.g.shape[2:])
+        self.grad_mask = torch.empty(self.target, dtype=torch.float32, device="cuda")
+        self.ws = _ws(zk.reduce_workspace_bytes(self.g, self.target), torch)
+        ng, nm = _n(self.g.shape), _n(self.target)
+        self.calls = [
+            Call("reduce_to_shape(g->[1,1,%d,%d])" % self.target[2:], "bwd",
+                 lambda: zk.reduce_to_shape(self.g, self.target, out=self.grad_mask,
+                                            workspace=self.ws),
+                 [ng], [nm]),
+        ]
+
+
 class StridedTransposed(Workload):
     """a[4096,4096] as a transposed view (strides [1,4096]) * b[4096]."""
     name = "strided_transposed"
@@ -394,6 +416,6 @@ class GPTRowStats(Workload):
 
 
 WORKLOAD_CLASSES = {c.name: c for c in (XYPlusX, MLPBiasGelu, AttnScaleMask,
-                                        StridedTransposed, Rank8, GPTResidual,
+                                        AttnMaskGrad, StridedTransposed, Rank8, GPTResidual,
                                         XYPlusXFused, AttnScaleMaskFused,
                                         GPTResidualFused, GPTLossMeanClip, GPTRowStats)}

@@ -75,6 +75,12 @@ def attn_scale_mask(b=8, h=16, t=1024):
                 g=normal((b, h, t, t), 3003))
 
 
+def attn_mask_grad(b=8, h=16, t=1024):
+    """Upstream gradient of the attention scores, to be summed back to the
+    causal mask's shape [1, 1, t, t] (same seed as attn_scale_mask's g)."""
+    return dict(g=normal((b, h, t, t), 3003))
+
+
 def strided_transposed(n=4096):
     """Storage S[n*n] U(-1,1); a = S viewed [n,n] and transposed, i.e.
     sizes [n,n], strides [1,n]; b[n] U(-1,1); g[n,n] N(0,1)."""

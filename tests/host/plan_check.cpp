@@ -155,6 +155,8 @@ int main() {
           if (rp.chunk < 1) return fail("col rcw", rp.chunk, 0);
           const int64_t P = (c.n[0] + rp.nw * rp.chunk - 1) / (rp.nw * rp.chunk);
           if (rp.partials != P) return fail("col partials", rp.partials, P);
+          // short columns: the one band of rows is split evenly over the waves
+          if (P == 1 && rp.nw * rp.chunk > c.n[0] + rp.nw - 1) return fail("col idle waves", rp.nw, rp.chunk);
           if (((c.n[1] + 255) / 256) * P > kMaxGridBlocks) return fail("col grid", P, 0);
           break;
         }

@@ -535,6 +535,32 @@ def test_full_size_attn_scale_mask(orc):
                        host(wl.grad_scale), 8, full=True)
 
 
+def test_full_size_attn_mask_grad(orc):
+    """The benchmark's mask-gradient call: every one of the 1M outputs of
+    g[8,16,1024,1024] summed to [1,1,1024,1024] against the oracle."""
+    wl = steps.AttnMaskGrad()
+    wl.run()
+    ref = orc.reduce_to_shape(wl.host["g"], wl.target)
+    m = assert_bwd(host(wl.grad_mask), ref, "grad_mask")
+    say(f"  largest error / allowance: {m:.3f}")
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 7, 13, 100, 128, 257])
+def test_short_columns(orc, rows):
+    """Column sums over few rows of many columns (one partial a column, the
+    rows split over the waves of a block), alone and fused with a rule."""
+    rng = np.random.default_rng(1000 + rows)
+    x = rng.standard_normal((rows, 8192)).astype(np.float32)
+    got = host(zk.reduce_to_shape(dev(x), (8192,)))
+    assert_bwd(got, orc.reduce_to_shape(x, (8192,)), f"reduce rows={rows}")
+    b = rng.standard_normal(8192).astype(np.float32)
+    g = rng.standard_normal((rows, 8192)).astype(np.float32)
+    ga, gb = zk.binary_bwd("mul", dev(g), dev(x), dev(b))
+    ra, rb = orc.bwd("mul", g, x, b)
+    assert_bwd(host(ga), ra, "grad_x")
+    assert_bwd(host(gb), rb, "grad_b")
+
+
 def test_full_size_strided(orc):
     wl = steps.StridedTransposed()
     h = wl.host
