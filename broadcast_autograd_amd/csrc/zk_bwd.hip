@@ -259,10 +259,29 @@ struct ColArgs {
   int32_t write_big;
 };
 
-template <int OP, int EPI, int SIDE, int ACC, int NW>
+// One partial a column (short columns, DIRECT kernels): the kernel finishes
+// each sum itself into out (negated when neg, plus acc, divided by div when
+// has_div; rounded once) and no stage 2 runs.
+struct ColDirect {
+  float *out;
+  const float *acc;
+  int32_t neg, has_div;
+  double div;
+};
+
+// The column's result from its one binary64 sum (the arithmetic of
+// k_red_final for a single partial).
+__device__ __forceinline__ float col_direct(const ColDirect &cd, int64_t c, double tot) {
+  double v = cd.neg ? -tot : tot;
+  if (cd.acc) v += (double)cd.acc[c];
+  if (cd.has_div) v = v / cd.div;
+  return (float)v;
+}
+
+template <int OP, int EPI, int SIDE, int ACC, int NW, bool DIRECT>
 __global__ __launch_bounds__(64 * NW) void k_red_col(
     const float *g, const float *big, const float *small, float *gbig,
-    const float *accbig, double *part, ColArgs ca, GcOut gco) {
+    const float *accbig, double *part, ColArgs ca, GcOut gco, ColDirect cd) {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
   // rows in flight per wave: two for the plain rules; one with the GeLU
@@ -352,7 +371,10 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   if constexpr (NW == 1) {
     if (active) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) part[p * ca.K + c + k] = s[k];
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (DIRECT) cd.out[c + k] = col_direct(cd, c + k, s[k]);
+        else part[p * ca.K + c + k] = s[k];
+      }
     }
   } else {
     __shared__ double lds[NW][4][64];
@@ -365,7 +387,8 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
         double tot = lds[0][k][l];
 #pragma unroll
         for (int ww = 1; ww < NW; ++ww) tot += lds[ww][k][l];
-        part[p * ca.K + c + k] = tot;
+        if constexpr (DIRECT) cd.out[c + k] = col_direct(cd, c + k, tot);
+        else part[p * ca.K + c + k] = tot;
       }
     }
   }
@@ -821,13 +844,23 @@ static inline unsigned gridn(int64_t n, int64_t per) {
 
 // red_col waves per block, as planned (kColWavesFew / kColWavesMany).
 template <class Fn>
-static hipError_t with_col_waves(int nw, Fn fn) {
+static hipError_t with_col_waves(int nw, bool direct, Fn fn) {
+  // the planner gives short columns (one partial) kColWavesFew waves
+  if (direct) {
+    if (nw == kColWavesFew) return fn(IC<kColWavesFew>{}, std::true_type{});
+    return hipErrorInvalidValue;
+  }
   switch (nw) {
-    case 1: return fn(IC<1>{});
-    case 4: return fn(IC<4>{});
-    case 16: return fn(IC<16>{});
+    case 1: return fn(IC<1>{}, std::false_type{});
+    case 4: return fn(IC<4>{}, std::false_type{});
+    case 16: return fn(IC<16>{}, std::false_type{});
     default: return hipErrorInvalidValue;
   }
+}
+
+// Short columns finish in stage 1 (k_red_col with DIRECT).
+static bool col_direct_plan(const RedPlan &rp) {
+  return rp.kernel == K_RED_COL && rp.partials == 1 && rp.nw == kColWavesFew;
 }
 
 // One-pass row reduction (red_rowd): stage 1 and the final rounding.
@@ -1228,13 +1261,15 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ca.ss = c.s[1 + sw][1];
             ca.colblocks = (ca.K + 255) / 256;
             ca.write_big = p.fused_big;
+            ColDirect cd{gsmall, accsmall, 0, 0, 0.0};
             unsigned grid = (unsigned)(ca.colblocks * rp.partials);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
-              return with_col_waves(rp.nw, [&](auto Wc) -> hipError_t {
+              return with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
                 constexpr int NW = decltype(Wc)::value;
-                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, NW>), dim3(grid), dim3(64 * NW), 0,
-                          st, g, big, small, gbig, accbig, part, ca, go);
+                constexpr bool D = decltype(Dc)::value;
+                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, NW, D>), dim3(grid), dim3(64 * NW),
+                          0, st, g, big, small, gbig, accbig, part, ca, go, cd);
                 return hipGetLastError();
               });
             });
@@ -1300,6 +1335,7 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
       });
       if (e != hipSuccess) return e;
     }
+    if (col_direct_plan(rp)) continue;  // finished in stage 1
     e = launch_final(rp, part, accsmall, gsmall, st);
     if (e != hipSuccess) return e;
   }
@@ -1340,12 +1376,14 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ca.ss = 0;
           ca.colblocks = (ca.K + 255) / 256;
           ca.write_big = 0;
+          const ColDirect cd{out, acc, neg ? 1 : 0, mean_count >= 0.0 ? 1 : 0, mean_count};
           const unsigned grid = (unsigned)(ca.colblocks * rp.partials);
-          hipError_t e = with_col_waves(rp.nw, [&](auto Wc) -> hipError_t {
+          hipError_t e = with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
             constexpr int NW = decltype(Wc)::value;
-            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, NW>), dim3(grid),
+            constexpr bool D = decltype(Dc)::value;
+            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, NW, D>), dim3(grid),
                       dim3(64 * NW), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ca,
-                      none);
+                      none, cd);
             return hipGetLastError();
           });
           if (e != hipSuccess) return e;
@@ -1379,6 +1417,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
+    if (col_direct_plan(rp)) continue;  // finished in stage 1
     hipError_t e = launch_final(rp, part, acc, out, st, neg, mean_count);
     if (e != hipSuccess) return e;
   }

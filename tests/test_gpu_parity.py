@@ -559,6 +559,14 @@ def test_short_columns(orc, rows):
     ra, rb = orc.bwd("mul", g, x, b)
     assert_bwd(host(ga), ra, "grad_x")
     assert_bwd(host(gb), rb, "grad_b")
+    # accumulated in place onto an existing gradient, and the mean
+    prev = rng.standard_normal(8192).astype(np.float32)
+    gb2 = dev(prev)
+    zk.binary_bwd("mul", dev(g), dev(x), dev(b), need_a=False, grad_b=gb2, acc_b=gb2)
+    _, rb2 = orc.bwd("mul", g, x, b, acc_b=prev, want=(False, True))
+    assert_bwd(host(gb2), rb2, "grad_b += ")
+    got = host(zk.mean_to_shape(dev(x), (8192,)))
+    assert_bwd(got, orc.mean_to_shape(x, (8192,)), f"mean rows={rows}")
 
 
 def test_full_size_strided(orc):
