@@ -65,6 +65,8 @@ SHAPES = [
     ((2, 3, 4, 5, 6), (1, 3, 1, 5, 1), (4, 5, 6)),  # rank 5: generic kernels
     ((3, 1), (1, 4), (2, 3, 4)),             # t repeated into out (split path)
     ((), (5,), (2, 5)),                      # scalar a
+    ((5, 4096), (4096,), (5, 4096)),         # short columns: sums finished in stage 1
+    ((6, 2048), (2048,), (1, 2048)),         # short columns, c a broadcast row
 ]
 
 
