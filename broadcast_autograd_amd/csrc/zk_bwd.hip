@@ -256,6 +256,8 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_generic(
 // the device-scope fences it needs cost more than the second launch.)
 struct ColArgs {
   int64_t R, K, rcw, ss, colblocks;
+  int64_t kmod;  // the small operand's columns: column c reads element c % kmod
+                 // (kmod == K, or a power of two below it for folded rows)
   int32_t write_big;
 };
 
@@ -297,8 +299,10 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   const bool active = c < ca.K;
   float sv[4] = {0.f, 0.f, 0.f, 0.f};
   if (NEED_SMALL && active) {
+    // folded rows: kmod is a power of two dividing 256 and c a multiple of 4
+    const int64_t cm = ca.kmod < ca.K ? (c & (ca.kmod - 1)) : c;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sv[k] = small[(c + k) * ca.ss];
+    for (int k = 0; k < 4; ++k) sv[k] = small[(cm + k) * ca.ss];
   }
   const int64_t r0 = (p * NW + w) * ca.rcw;
   const int64_t r1 = r0 + ca.rcw < ca.R ? r0 + ca.rcw : ca.R;
@@ -1255,14 +1259,15 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
         switch (rp.kernel) {
           case K_RED_COL: {
             ColArgs ca{};
-            ca.R = c.n[0];
-            ca.K = c.n[1];
+            ca.R = c.n[0] / rp.fold;
+            ca.K = c.n[1] * rp.fold;
+            ca.kmod = c.n[1];
             ca.rcw = rp.chunk;
             ca.ss = c.s[1 + sw][1];
             ca.colblocks = (ca.K + 255) / 256;
             ca.write_big = p.fused_big;
             ColDirect cd{gsmall, accsmall, 0, 0, 0.0};
-            unsigned grid = (unsigned)(ca.colblocks * rp.partials);
+            unsigned grid = (unsigned)(ca.colblocks * (rp.partials / rp.fold));
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
               return with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
@@ -1370,14 +1375,15 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
       switch (rp.kernel) {
         case K_RED_COL: {
           ColArgs ca{};
-          ca.R = c.n[0];
-          ca.K = c.n[1];
+          ca.R = c.n[0] / rp.fold;
+          ca.K = c.n[1] * rp.fold;
+          ca.kmod = c.n[1];
           ca.rcw = rp.chunk;
           ca.ss = 0;
           ca.colblocks = (ca.K + 255) / 256;
           ca.write_big = 0;
           const ColDirect cd{out, acc, neg ? 1 : 0, mean_count >= 0.0 ? 1 : 0, mean_count};
-          const unsigned grid = (unsigned)(ca.colblocks * rp.partials);
+          const unsigned grid = (unsigned)(ca.colblocks * (rp.partials / rp.fold));
           hipError_t e = with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
             constexpr int NW = decltype(Wc)::value;
             constexpr bool D = decltype(Dc)::value;

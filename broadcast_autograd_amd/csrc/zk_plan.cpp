@@ -481,8 +481,15 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
     // >= 16 rows and binary64 partials stay within a few % of the call's
     // bytes.  The grid (column groups x partials) stays within the dispatch
     // limit.
-    const int64_t R0 = c.n[0];
-    const int64_t colblocks = ceil_div(c.n[1], 256);
+    // Narrow columns (K < 256 dividing 256, e.g. [4194304, 32]): fold = 256/K
+    // consecutive rows of the dense operands form one row of 256 columns, so
+    // every lane of a wave stays busy; stage 2 then sums the fold copies of
+    // each column along with the partials.
+    int64_t fold = 1;
+    if (c.n[1] < 256 && 256 % c.n[1] == 0 && c.n[0] % (256 / c.n[1]) == 0)
+      fold = 256 / c.n[1];
+    const int64_t R0 = c.n[0] / fold;
+    const int64_t colblocks = ceil_div(c.n[1] * fold, 256);
     int64_t rcw = std::min<int64_t>(kColRowsMany, std::max<int64_t>(4, R0 * colblocks / 8192));
     int nw = rcw >= kColRowsMany ? kColWavesMany : kColWavesFew;
     // Short columns (fewer rows than a block spans, e.g. [128, 1048576]):
@@ -495,7 +502,8 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
     while (colblocks * ceil_div(R0, nw * rcw) > kMaxGridBlocks) rcw *= 2;
     rp->chunk = rcw;
     rp->nw = nw;
-    rp->partials = ceil_div(R0, nw * rcw);
+    rp->fold = (int32_t)fold;
+    rp->partials = ceil_div(R0, nw * rcw) * fold;
     return true;
   }
   if (big_transposed) return false;

@@ -180,6 +180,9 @@ struct RedPlan {
   int64_t chunk = 0;         // rows per wave (COL), rows (TILE) or elements
                              // (ROW/GENERIC) per partial
   int32_t nw = 1;            // COL: waves of a block that share one partial
+  int32_t fold = 1;          // COL: rows of K < 256 columns read as one row of
+                             // fold*K = 256 (stage 1 runs on [R/fold, 256];
+                             // partials counts the fold copies too)
   int64_t red = 0;           // reduced elements per kept element
   size_t ws_offset = 0;      // byte offset of its partials in the workspace
 };

@@ -153,11 +153,16 @@ int main() {
           if (c.n[1] % 4 != 0) return fail("col K%4", c.n[1], 0);
           if (!(rp.nw == 1 || rp.nw == 4 || rp.nw == 16)) return fail("col nw", rp.nw, 0);
           if (rp.chunk < 1) return fail("col rcw", rp.chunk, 0);
-          const int64_t P = (c.n[0] + rp.nw * rp.chunk - 1) / (rp.nw * rp.chunk);
-          if (rp.partials != P) return fail("col partials", rp.partials, P);
+          // narrow columns fold rows into 256-wide ones: fold * K == 256
+          const int64_t f = rp.fold;
+          if (f < 1 || (f > 1 && (c.n[1] * f != 256 || c.n[0] % f != 0)))
+            return fail("col fold", f, c.n[1]);
+          const int64_t R0 = c.n[0] / f, Kw = c.n[1] * f;
+          const int64_t P = (R0 + rp.nw * rp.chunk - 1) / (rp.nw * rp.chunk);
+          if (rp.partials != P * f) return fail("col partials", rp.partials, P * f);
           // short columns: the one band of rows is split evenly over the waves
-          if (P == 1 && rp.nw * rp.chunk > c.n[0] + rp.nw - 1) return fail("col idle waves", rp.nw, rp.chunk);
-          if (((c.n[1] + 255) / 256) * P > kMaxGridBlocks) return fail("col grid", P, 0);
+          if (P == 1 && rp.nw * rp.chunk > R0 + rp.nw - 1) return fail("col idle waves", rp.nw, rp.chunk);
+          if (((Kw + 255) / 256) * P > kMaxGridBlocks) return fail("col grid", P, 0);
           break;
         }
         case K_RED_ROW: {

@@ -545,6 +545,36 @@ def test_full_size_attn_mask_grad(orc):
     say(f"  largest error / allowance: {m:.3f}")
 
 
+@pytest.mark.parametrize("rows,cols", [(4096, 4), (4096, 8), (8192, 32), (2048, 64), (1024, 128),
+                                       (4000, 32), (4001, 32), (96, 128), (65536, 16)])
+def test_narrow_columns(orc, rows, cols):
+    """Column sums of fewer than 256 columns (rows folded into 256-wide ones
+    when the row count allows): reduce, the multiply backward with the small
+    operand's columns repeating across a folded row, GeLU, and acc in place."""
+    rng = np.random.default_rng(zlib.crc32(repr((rows, cols)).encode()))
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    got = host(zk.reduce_to_shape(dev(x), (cols,)))
+    assert_bwd(got, orc.reduce_to_shape(x, (cols,)), f"reduce {rows}x{cols}")
+    b = rng.standard_normal(cols).astype(np.float32)
+    g = rng.standard_normal((rows, cols)).astype(np.float32)
+    ga, gb = zk.binary_bwd("mul", dev(g), dev(x), dev(b))
+    ra, rb = orc.bwd("mul", g, x, b)
+    assert_bwd(host(ga), ra, "grad_x")
+    assert_bwd(host(gb), rb, "grad_b")
+    bias = (0.02 * rng.standard_normal(cols)).astype(np.float32)
+    ga, gb = zk.binary_bwd("add", dev(g), dev(x), dev(bias), epi="gelu")
+    ra, rb = orc.bwd("add", g, x, bias, epi=orc.EPI_GELU)
+    assert_bwd(host(ga), ra, "grad_act (gelu)")
+    assert_bwd(host(gb), rb, "grad_bias (gelu)")
+    prev = rng.standard_normal(cols).astype(np.float32)
+    gb2 = dev(prev)
+    zk.binary_bwd("mul", dev(g), dev(x), dev(b), need_a=False, grad_b=gb2, acc_b=gb2)
+    _, rb2 = orc.bwd("mul", g, x, b, acc_b=prev, want=(False, True))
+    assert_bwd(host(gb2), rb2, "grad_b += ")
+    got = host(zk.mean_to_shape(dev(x), (cols,)))
+    assert_bwd(got, orc.mean_to_shape(x, (cols,)), "mean")
+
+
 @pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 7, 13, 100, 128, 257])
 def test_short_columns(orc, rows):
     """Column sums over few rows of many columns (one partial a column, the
