@@ -36,6 +36,8 @@ constexpr int kColWavesMany = 16;
 // vectors per lane in flight).
 constexpr int64_t kDirMinTerms = 2048;
 constexpr int64_t kDirMaxTerms = 16384;
+// red_rowd for plain row sums ([K, T]) only up to this many elements.
+constexpr int64_t kDirRowSumMaxElems = (int64_t)1 << 24;
 // red_gend: terms per kept element it takes (a wave walks them, 64 at a time).
 constexpr int64_t kGenDirMinTerms = 32;
 constexpr int64_t kGenDirMaxTerms = 4096;

@@ -178,6 +178,9 @@ int main() {
           if (rp.partials != 0 || inner % 4 != 0) return fail("rowd", rp.partials, inner);
           if (rp.kept * rp.red != c.numel) return fail("rowd cover", rp.kept, rp.red);
           if (rp.red < kDirMinTerms || rp.red > kDirMaxTerms) return fail("rowd terms", rp.red, 0);
+          // plain row sums ([K, T]: the reduced run is the whole inner dim) of
+          // many elements go to red_row
+          if (rp.red == inner && c.numel > kDirRowSumMaxElems) return fail("rowd size", c.numel, 0);
           if (!(rp.chunk == 1 || rp.chunk == 2 || rp.chunk == 4) || rp.red > 4096 * rp.chunk)
             return fail("rowd vectors", rp.chunk, rp.red);
           break;
