@@ -1065,6 +1065,45 @@ __global__ __launch_bounds__(kBlk) void k_red_gend(const float *g, const float *
   }
 }
 
+// ------------------------------------------------------------ red_rowseg
+// Sums of the rows of a dense [K, C], C = 4 * lpr < 256 (lpr a power of
+// two): a wave reads 256 consecutive elements a trip (64 / lpr whole rows, lpr
+// lanes a row, one 128-bit vector a lane), adds each lane's four in binary64
+// in a fixed order, then a row's lanes in a butterfly (every lane of the row
+// ends with the same bits); the row's first lane writes the result, negated
+// when asked, plus acc, divided by div for a mean (as k_red_final), rounded
+// once.
+struct RowSegArgs {
+  int64_t K, C;
+  int32_t lpr, lg;  // lanes per row and its log2
+  int32_t neg, has_div;
+  double div;
+};
+
+__global__ __launch_bounds__(kBlk) void k_red_rowseg(const float *in, const float *acc,
+                                                     float *out, RowSegArgs ra) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> ra.lg, q = l & (ra.lpr - 1);
+  const int64_t rpt = 64 >> ra.lg;  // rows a trip
+  const int64_t trips = (ra.K + rpt - 1) / rpt;
+  const int64_t nwaves = ((int64_t)gridDim.x * kBlk) >> 6;
+  for (int64_t t = ((int64_t)blockIdx.x * kBlk + threadIdx.x) >> 6; t < trips; t += nwaves) {
+    const int64_t row = t * rpt + g;
+    double s = 0.0;
+    if (row < ra.K) {
+      const float4 v = ld4_nt(in + row * ra.C + 4 * q);
+      s = (((double)v.x + (double)v.y) + (double)v.z) + (double)v.w;
+    }
+    for (int m = 1; m < ra.lpr; m <<= 1) s += __shfl_xor(s, m, 64);
+    if (q == 0 && row < ra.K) {
+      double v = ra.neg ? -s : s;
+      if (acc) v += (double)acc[row];
+      if (ra.has_div) v = v / ra.div;
+      out[row] = (float)v;
+    }
+  }
+}
+
 static GenArgs make_gen(const Canon &c, int kept_op, int src_op, int a_op,
                         int b_op, const RedPlan &rp) {
   GenArgs ga{};
@@ -1356,6 +1395,24 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
   for (int ri = 0; ri < p.nred; ++ri) {
     const RedPlan &rp = p.red[ri];
     double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + rp.ws_offset);
+    if (rp.kernel == K_RED_ROWSEG) {
+      RowSegArgs ra{};
+      ra.K = rp.kept;
+      ra.C = rp.red;
+      ra.lpr = (int32_t)(rp.red / 4);
+      while ((1 << ra.lg) < ra.lpr) ++ra.lg;
+      if ((1 << ra.lg) != ra.lpr || ra.lpr > 32) return hipErrorInvalidValue;
+      ra.neg = neg ? 1 : 0;
+      ra.has_div = mean_count >= 0.0 ? 1 : 0;
+      ra.div = mean_count;
+      const int64_t trips = (ra.K + (64 >> ra.lg) - 1) / (64 >> ra.lg);
+      ProfScope prof(K_RED_ROWSEG);
+      ZK_LAUNCH(prof, k_red_rowseg, dim3(gridn(trips, kBlk / 64)), dim3(kBlk), 0, st, in, acc,
+                out, ra);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      continue;
+    }
     if (rp.kernel == K_RED_GEND) {
       hipError_t e = launch_gend(rp, c, p.idx64, 4, -1, -1, ZK_ADD, ZK_EPI_NONE, true, 1, in,
                                  nullptr, nullptr, nullptr, nullptr, 0, false, out, acc, neg,

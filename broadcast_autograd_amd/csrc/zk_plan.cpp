@@ -13,7 +13,8 @@ const char *kernel_name(int32_t k) {
       "red_tile",       "red_generic",   "red_final",  "fwd2_row",
       "fwd2_generic",   "bwd_signed",    "copy_row",   "copy_tile",
       "copy_generic",   "norm_part",     "norm_final", "clip_scale",
-      "red_rowd",       "red_gend",      "row_moments", "row_softmax"};
+      "red_rowd",       "red_gend",      "row_moments", "row_softmax",
+      "red_rowseg"};
   if (k < 0 || k >= K_COUNT) return "none";
   return names[k];
 }
@@ -730,7 +731,19 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
   for (int k = 0; k < c.rank; ++k)
     if (c.s[0][k] != c.s[1][k]) src_flat = false;
   RedPlan rp;
-  if (K < c.numel && size_fast(c, 4, -1, false, src_flat, al16(pin), &rp)) {
+  // Short dense rows ([K, C] to [K, 1], C < 256 dividing 256, aligned): a
+  // wave reads 256 / C whole rows at a time (red_rowseg), no partials.
+  if (K < c.numel && src_flat && al16(pin) && c.rank == 2 && kept_mask(c, 4) == 1u &&
+      c.s[4][0] == 1 && c.n[1] >= 4 && c.n[1] < 256 && 256 % c.n[1] == 0) {
+    rp.kernel = K_RED_ROWSEG;
+    rp.kept = c.n[0];
+    rp.red = c.n[1];
+    rp.chunk = 0;
+    rp.partials = 0;
+    rp.which = 1;
+    p->red[p->nred++] = rp;
+    p->vec = 4;
+  } else if (K < c.numel && size_fast(c, 4, -1, false, src_flat, al16(pin), &rp)) {
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;

@@ -185,6 +185,13 @@ int main() {
             return fail("rowd vectors", rp.chunk, rp.red);
           break;
         }
+        case K_RED_ROWSEG: {
+          // dense rows of C = 4 * 2^j < 256 elements, the inner dim reduced
+          if (rp.partials != 0 || rp.kept * rp.red != c.numel || c.rank != 2 || c.n[1] != rp.red)
+            return fail("rowseg", rp.kept, rp.red);
+          if (rp.red < 4 || rp.red >= 256 || 256 % rp.red != 0) return fail("rowseg C", rp.red, 0);
+          break;
+        }
         case K_RED_GEND: {
           if (rp.partials != 0 || rp.kept * rp.red != c.numel) return fail("gend", rp.kept, rp.red);
           if (rp.red < kGenDirMinTerms || rp.red > kGenDirMaxTerms) return fail("gend terms", rp.red, 0);

@@ -545,6 +545,28 @@ def test_full_size_attn_mask_grad(orc):
     say(f"  largest error / allowance: {m:.3f}")
 
 
+@pytest.mark.parametrize("cols", [4, 8, 16, 32, 64, 128])
+@pytest.mark.parametrize("rows", [1, 63, 1001, 65537])
+def test_short_rows(orc, rows, cols):
+    """Row sums of short dense rows (256 / C rows a wave, a butterfly over a
+    row's lanes), as sums and means, in rank 2 and as [rows, 1, C] -> [rows, 1, 1];
+    a misaligned view takes the gather path."""
+    rng = np.random.default_rng(zlib.crc32(repr((rows, cols)).encode()))
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    t = dev(x)
+    ref = orc.reduce_to_shape(x, (rows, 1))
+    assert_bwd(host(zk.reduce_to_shape(t, (rows, 1))), ref, f"sum {rows}x{cols}")
+    assert_bwd(host(zk.mean_to_shape(t, (rows, 1))), orc.mean_to_shape(x, (rows, 1)), "mean")
+    x3 = x.reshape(rows, 1, cols)
+    assert_bwd(host(zk.reduce_to_shape(dev(x3), (rows, 1, 1))),
+               orc.reduce_to_shape(x3, (rows, 1, 1)), "rank 3")
+    if rows > 1:
+        s = rng.standard_normal(rows * cols + 1).astype(np.float32)
+        v, tv, _ = strided_pair(s, (rows, cols), (cols, 1), offset=1)
+        assert_bwd(host(zk.reduce_to_shape(tv, (rows, 1))), orc.reduce_to_shape(v, (rows, 1)),
+                   "misaligned")
+
+
 @pytest.mark.parametrize("rows,cols", [(4096, 4), (4096, 8), (8192, 32), (2048, 64), (1024, 128),
                                        (4000, 32), (4001, 32), (96, 128), (65536, 16)])
 def test_narrow_columns(orc, rows, cols):
