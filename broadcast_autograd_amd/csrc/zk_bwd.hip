@@ -1072,16 +1072,18 @@ __global__ __launch_bounds__(kBlk) void k_red_gend(const float *g, const float *
 // in a fixed order, then a row's lanes in a butterfly (every lane of the row
 // ends with the same bits); the row's first lane writes the result, negated
 // when asked, plus acc, divided by div for a mean (as k_red_final), rounded
-// once.
+// once.  With `part` the row sums are binary64 partials instead (row
+// r1 * K + k is partial r1 of kept element k) for k_red_final.
 struct RowSegArgs {
-  int64_t K, C;
+  int64_t K, C;     // K: rows
   int32_t lpr, lg;  // lanes per row and its log2
   int32_t neg, has_div;
   double div;
 };
 
 __global__ __launch_bounds__(kBlk) void k_red_rowseg(const float *in, const float *acc,
-                                                     float *out, RowSegArgs ra) {
+                                                     float *out, double *part,
+                                                     RowSegArgs ra) {
   const int l = threadIdx.x & 63;
   const int g = l >> ra.lg, q = l & (ra.lpr - 1);
   const int64_t rpt = 64 >> ra.lg;  // rows a trip
@@ -1096,10 +1098,14 @@ __global__ __launch_bounds__(kBlk) void k_red_rowseg(const float *in, const floa
     }
     for (int m = 1; m < ra.lpr; m <<= 1) s += __shfl_xor(s, m, 64);
     if (q == 0 && row < ra.K) {
-      double v = ra.neg ? -s : s;
-      if (acc) v += (double)acc[row];
-      if (ra.has_div) v = v / ra.div;
-      out[row] = (float)v;
+      if (part) {
+        part[row] = s;
+      } else {
+        double v = ra.neg ? -s : s;
+        if (acc) v += (double)acc[row];
+        if (ra.has_div) v = v / ra.div;
+        out[row] = (float)v;
+      }
     }
   }
 }
@@ -1397,20 +1403,26 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
     double *part = reinterpret_cast<double *>(static_cast<char *>(ws) + rp.ws_offset);
     if (rp.kernel == K_RED_ROWSEG) {
       RowSegArgs ra{};
-      ra.K = rp.kept;
-      ra.C = rp.red;
-      ra.lpr = (int32_t)(rp.red / 4);
+      ra.K = c.numel / rp.chunk;  // rows
+      ra.C = rp.chunk;
+      ra.lpr = (int32_t)(rp.chunk / 4);
       while ((1 << ra.lg) < ra.lpr) ++ra.lg;
       if ((1 << ra.lg) != ra.lpr || ra.lpr > 32) return hipErrorInvalidValue;
       ra.neg = neg ? 1 : 0;
       ra.has_div = mean_count >= 0.0 ? 1 : 0;
       ra.div = mean_count;
       const int64_t trips = (ra.K + (64 >> ra.lg) - 1) / (64 >> ra.lg);
-      ProfScope prof(K_RED_ROWSEG);
-      ZK_LAUNCH(prof, k_red_rowseg, dim3(gridn(trips, kBlk / 64)), dim3(kBlk), 0, st, in, acc,
-                out, ra);
+      {
+        ProfScope prof(K_RED_ROWSEG);
+        ZK_LAUNCH(prof, k_red_rowseg, dim3(gridn(trips, kBlk / 64)), dim3(kBlk), 0, st, in,
+                  acc, out, rp.partials > 0 ? part : nullptr, ra);
+      }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+      if (rp.partials > 0) {
+        e = launch_final(rp, part, acc, out, st, neg, mean_count);
+        if (e != hipSuccess) return e;
+      }
       continue;
     }
     if (rp.kernel == K_RED_GEND) {

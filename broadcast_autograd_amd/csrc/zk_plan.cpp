@@ -731,15 +731,20 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
   for (int k = 0; k < c.rank; ++k)
     if (c.s[0][k] != c.s[1][k]) src_flat = false;
   RedPlan rp;
-  // Short dense rows ([K, C] to [K, 1], C < 256 dividing 256, aligned): a
-  // wave reads 256 / C whole rows at a time (red_rowseg), no partials.
-  if (K < c.numel && src_flat && al16(pin) && c.rank == 2 && kept_mask(c, 4) == 1u &&
-      c.s[4][0] == 1 && c.n[1] >= 4 && c.n[1] < 256 && 256 % c.n[1] == 0) {
+  // Short dense rows (C < 256 dividing 256, aligned): a wave reads 256 / C
+  // whole rows at a time (red_rowseg).  [K, C] to [K, 1]: each row sum is the
+  // result (no partials).  [R1, K, C] to [K, 1]: the row sums are binary64
+  // partials [R1, K] for stage 2.
+  const int64_t C = c.n[c.rank - 1];
+  const bool short_rows = K < c.numel && src_flat && al16(pin) && C >= 4 && C < 256 &&
+                          256 % C == 0;
+  if (short_rows && ((c.rank == 2 && kept_mask(c, 4) == 1u && c.s[4][0] == 1) ||
+                     (c.rank == 3 && kept_mask(c, 4) == 2u && c.s[4][1] == 1))) {
     rp.kernel = K_RED_ROWSEG;
-    rp.kept = c.n[0];
-    rp.red = c.n[1];
-    rp.chunk = 0;
-    rp.partials = 0;
+    rp.kept = c.n[c.rank - 2];
+    rp.red = c.numel / rp.kept;
+    rp.chunk = C;
+    rp.partials = c.rank == 3 ? c.n[0] : 0;
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;

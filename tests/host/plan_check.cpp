@@ -186,10 +186,14 @@ int main() {
           break;
         }
         case K_RED_ROWSEG: {
-          // dense rows of C = 4 * 2^j < 256 elements, the inner dim reduced
-          if (rp.partials != 0 || rp.kept * rp.red != c.numel || c.rank != 2 || c.n[1] != rp.red)
-            return fail("rowseg", rp.kept, rp.red);
-          if (rp.red < 4 || rp.red >= 256 || 256 % rp.red != 0) return fail("rowseg C", rp.red, 0);
+          // dense rows of C = 4 * 2^j < 256 elements, the inner dim reduced;
+          // rank 2 finishes in place, rank 3 leaves [R1, K] partials
+          const int64_t C = rp.chunk;
+          if (rp.kept * rp.red != c.numel || c.n[c.rank - 1] != C) return fail("rowseg", rp.kept, C);
+          if (C < 4 || C >= 256 || 256 % C != 0) return fail("rowseg C", C, 0);
+          if (c.rank == 2 ? (rp.partials != 0 || rp.red != C)
+                          : (c.rank != 3 || rp.partials != c.n[0] || rp.kept != c.n[1]))
+            return fail("rowseg partials", rp.partials, c.rank);
           break;
         }
         case K_RED_GEND: {

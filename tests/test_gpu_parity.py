@@ -567,6 +567,19 @@ def test_short_rows(orc, rows, cols):
                    "misaligned")
 
 
+@pytest.mark.parametrize("shape", [(3, 5, 8), (64, 1000, 4), (7, 33, 32), (256, 512, 128),
+                                   (2, 4096, 64)])
+def test_short_rows_middle(orc, shape):
+    """[R1, K, C] -> [K, 1] with short rows: the row sums are binary64
+    partials of stage 2 (sums and means)."""
+    rng = np.random.default_rng(zlib.crc32(repr(shape).encode()))
+    x = rng.standard_normal(shape).astype(np.float32)
+    t = dev(x)
+    tgt = (shape[1], 1)
+    assert_bwd(host(zk.reduce_to_shape(t, tgt)), orc.reduce_to_shape(x, tgt), f"sum {shape}")
+    assert_bwd(host(zk.mean_to_shape(t, tgt)), orc.mean_to_shape(x, tgt), f"mean {shape}")
+
+
 @pytest.mark.parametrize("rows,cols", [(4096, 4), (4096, 8), (8192, 32), (2048, 64), (1024, 128),
                                        (4000, 32), (4001, 32), (96, 128), (65536, 16)])
 def test_narrow_columns(orc, rows, cols):
