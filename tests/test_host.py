@@ -385,6 +385,33 @@ def test_workload_canonical_forms(L, case):
     assert not info["index64"]
 
 
+@pytest.mark.parametrize("shape,target,kernel,partials,ws", [
+    # short columns: one partial a column, finished by red_col (no workspace use)
+    ((128, 1048576), (1048576,), "red_col", 1, None),
+    # narrow columns fold 256/K rows into one: partials count the fold copies
+    ((4194304, 32), (32,), "red_col", 512 * 8, 512 * 8 * 32 * 8),
+    ((33554432, 4), (4,), "red_col", 512 * 64, 512 * 64 * 4 * 8),
+    ((4001, 32), (32,), "red_col", None, None),          # rows not divisible: no fold
+    # plain row sums: a block per row up to 2^24 elements, then red_row
+    ((4096, 2048), (4096, 1), "red_rowd", 0, 0),
+    ((65536, 2048), (65536, 1), "red_row", 1, None),
+    ((64, 128, 256), (128, 1), "red_rowd", 0, None),     # middle pattern stays one pass
+    # short rows: 256 / C rows a wave
+    ((1048576, 128), (1048576, 1), "red_rowseg", 0, 0),
+    ((16777216, 8), (16777216, 1), "red_rowseg", 0, 0),
+    ((256, 4096, 128), (4096, 1), "red_rowseg", 256, 256 * 4096 * 8),
+    ((10, 12), (10, 1), "red_generic", None, None),      # 12 does not divide 256
+])
+def test_reduce_plan_shapes(L, shape, target, kernel, partials, ws):
+    """The planner's choice for the reduction shapes it treats specially."""
+    info = zk.plan_describe("reduce", "add", zk.make_desc(shape), zk.make_desc(target))
+    assert info["kernel"] == kernel
+    if partials is not None:
+        assert info["partials"] == partials
+    if ws is not None:
+        assert info["workspace_bytes"] == ws
+
+
 def test_reduce_plans(L):
     info = zk.plan_describe("reduce", "add", zk.make_desc((32768, 4096)), zk.make_desc((4096,)))
     assert info["kernel"] == "red_col" and info["sizes"] == (32768, 4096)
