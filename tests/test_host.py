@@ -393,12 +393,12 @@ def test_workload_canonical_forms(L, case):
     ((33554432, 4), (4,), "red_col", 512 * 64, 512 * 64 * 4 * 8),
     ((4001, 32), (32,), "red_col", None, None),          # rows not divisible: no fold
     # plain row sums: a block per row up to 2^24 elements, then red_row
-    ((4096, 2048), (4096, 1), "red_rowd", 0, 0),
+    ((4096, 2048), (4096, 1), "red_rowd", 0, None),
     ((65536, 2048), (65536, 1), "red_row", 1, None),
     ((64, 128, 256), (128, 1), "red_rowd", 0, None),     # middle pattern stays one pass
     # short rows: 256 / C rows a wave
-    ((1048576, 128), (1048576, 1), "red_rowseg", 0, 0),
-    ((16777216, 8), (16777216, 1), "red_rowseg", 0, 0),
+    ((1048576, 128), (1048576, 1), "red_rowseg", 0, None),
+    ((16777216, 8), (16777216, 1), "red_rowseg", 0, None),
     ((256, 4096, 128), (4096, 1), "red_rowseg", 256, 256 * 4096 * 8),
     ((10, 12), (10, 1), "red_generic", None, None),      # 12 does not divide 256
 ])
