@@ -1066,7 +1066,7 @@ __global__ __launch_bounds__(kBlk) void k_red_gend(const float *g, const float *
 }
 
 // ------------------------------------------------------------ red_rowseg
-// Sums of the rows of a dense [K, C], C = 4 * lpr < 256 (lpr a power of
+// Sums of the rows of a dense [K, C], C = 4 * lpr <= 256 (lpr a power of
 // two): a wave reads 256 consecutive elements a trip (64 / lpr whole rows, lpr
 // lanes a row, one 128-bit vector a lane), adds each lane's four in binary64
 // in a fixed order, then a row's lanes in a butterfly (every lane of the row
@@ -1407,7 +1407,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
       ra.C = rp.chunk;
       ra.lpr = (int32_t)(rp.chunk / 4);
       while ((1 << ra.lg) < ra.lpr) ++ra.lg;
-      if ((1 << ra.lg) != ra.lpr || ra.lpr > 32) return hipErrorInvalidValue;
+      if ((1 << ra.lg) != ra.lpr || ra.lpr > 64) return hipErrorInvalidValue;
       ra.neg = neg ? 1 : 0;
       ra.has_div = mean_count >= 0.0 ? 1 : 0;
       ra.div = mean_count;

@@ -731,15 +731,18 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
   for (int k = 0; k < c.rank; ++k)
     if (c.s[0][k] != c.s[1][k]) src_flat = false;
   RedPlan rp;
-  // Short dense rows (C < 256 dividing 256, aligned): a wave reads 256 / C
+  // Short dense rows (C <= 256 dividing 256, aligned): a wave reads 256 / C
   // whole rows at a time (red_rowseg).  [K, C] to [K, 1]: each row sum is the
   // result (no partials).  [R1, K, C] to [K, 1]: the row sums are binary64
-  // partials [R1, K] for stage 2.
+  // partials [R1, K] for stage 2, unless red_rowd takes the whole sum in one
+  // pass (R1 * C within its term range).
   const int64_t C = c.n[c.rank - 1];
-  const bool short_rows = K < c.numel && src_flat && al16(pin) && C >= 4 && C < 256 &&
+  const bool short_rows = K < c.numel && src_flat && al16(pin) && C >= 4 && C <= 256 &&
                           256 % C == 0;
+  const bool rowd_range = c.rank == 3 && C == 256 && c.n[0] * C >= kDirMinTerms &&
+                          c.n[0] * C <= kDirMaxTerms;  // red_rowd needs rows of >= 256
   if (short_rows && ((c.rank == 2 && kept_mask(c, 4) == 1u && c.s[4][0] == 1) ||
-                     (c.rank == 3 && kept_mask(c, 4) == 2u && c.s[4][1] == 1))) {
+                     (c.rank == 3 && kept_mask(c, 4) == 2u && c.s[4][1] == 1 && !rowd_range))) {
     rp.kernel = K_RED_ROWSEG;
     rp.kept = c.n[c.rank - 2];
     rp.red = c.numel / rp.kept;

@@ -69,7 +69,7 @@ enum KernelClass : int32_t {
   K_RED_GEND = 21,    // any pattern in one pass: a wave per kept element
   K_ROW_MOMENTS = 22,  // per-row mean and variance, a wave per row
   K_ROW_SOFTMAX = 23,  // per-row max and sum of exponentials, a wave per row
-  K_RED_ROWSEG = 24,   // sums of short dense rows (C < 256), 256/C rows a wave
+  K_RED_ROWSEG = 24,   // sums of short dense rows (C <= 256), 256/C rows a wave
   K_COUNT = 25
 };
 

@@ -190,7 +190,7 @@ int main() {
           // rank 2 finishes in place, rank 3 leaves [R1, K] partials
           const int64_t C = rp.chunk;
           if (rp.kept * rp.red != c.numel || c.n[c.rank - 1] != C) return fail("rowseg", rp.kept, C);
-          if (C < 4 || C >= 256 || 256 % C != 0) return fail("rowseg C", C, 0);
+          if (C < 4 || C > 256 || 256 % C != 0) return fail("rowseg C", C, 0);
           if (c.rank == 2 ? (rp.partials != 0 || rp.red != C)
                           : (c.rank != 3 || rp.partials != c.n[0] || rp.kept != c.n[1]))
             return fail("rowseg partials", rp.partials, c.rank);

@@ -545,7 +545,7 @@ def test_full_size_attn_mask_grad(orc):
     say(f"  largest error / allowance: {m:.3f}")
 
 
-@pytest.mark.parametrize("cols", [4, 8, 16, 32, 64, 128])
+@pytest.mark.parametrize("cols", [4, 8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("rows", [1, 63, 1001, 65537])
 def test_short_rows(orc, rows, cols):
     """Row sums of short dense rows (256 / C rows a wave, a butterfly over a
@@ -568,7 +568,7 @@ def test_short_rows(orc, rows, cols):
 
 
 @pytest.mark.parametrize("shape", [(3, 5, 8), (64, 1000, 4), (7, 33, 32), (256, 512, 128),
-                                   (2, 4096, 64)])
+                                   (2, 4096, 64), (100, 30, 256), (8, 64, 256)])
 def test_short_rows_middle(orc, shape):
     """[R1, K, C] -> [K, 1] with short rows: the row sums are binary64
     partials of stage 2 (sums and means)."""

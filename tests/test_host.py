@@ -401,6 +401,10 @@ def test_workload_canonical_forms(L, case):
     ((16777216, 8), (16777216, 1), "red_rowseg", 0, None),
     ((256, 4096, 128), (4096, 1), "red_rowseg", 256, 256 * 4096 * 8),
     ((10, 12), (10, 1), "red_generic", None, None),      # 12 does not divide 256
+    ((524288, 256), (524288, 1), "red_rowseg", 0, None),
+    ((2048, 256, 256), (256, 1), "red_rowseg", 2048, None),
+    ((8, 64, 256), (64, 1), "red_rowd", 0, None),        # within red_rowd's one pass
+    ((16, 1000, 128), (1000, 1), "red_rowseg", 16, None),  # rows too short for red_rowd
 ])
 def test_reduce_plan_shapes(L, shape, target, kernel, partials, ws):
     """The planner's choice for the reduction shapes it treats specially."""
