@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Effective HBM bandwidth of the broadcasting binary-operator path on one
-MI355X (gfx950): forward + backward of the MLP bias + GeLU workload
-(act[4096,1024] + bias[1024] -> GeLU; backward to act and bias), with the
-other workloads reported beside it.
+MI355X (gfx950): forward + backward of the GPT-scale residual workload
+(out = h[16,2048,4096] * gamma[4096] + resid[16,2048,4096]; backward to h,
+gamma and resid), the largest of the five configurations, with the other
+workloads reported beside it.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -18,8 +19,13 @@ a bounded spin kernel so that the host's enqueue time never shows up between
 the events.  Algorithmic bytes of a call = 4 x (distinct input elements read
 + elements written).
 
-The oracle (plain C, CPU) is timed on the same workload on the host cores as a
-reported baseline only.
+Each configuration is reported with its forward kernels' and its reducing
+backward call's fraction of the 8 TB/s HBM peak, against the targets of 80%
+(forward) and 65% (backward reduce-to-shape).
+
+The oracle (plain C, CPU) is timed on a row slice of the same workload on one
+host core and on all the cores this process may use, as a reported baseline
+only.
 """
 import argparse
 import json
@@ -32,7 +38,14 @@ import numpy as np
 
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 METRIC = "effective HBM GB/s (fwd, fwd+bwd) and % of MI355X HBM peak per config"
-MAIN = "mlp_bias_gelu"
+MAIN = "gpt_residual"
+# the five configurations (4 has two parts) and their workloads
+CONFIGS = {"xy_plus_x": "1", "mlp_bias_gelu": "2", "attn_scale_mask": "3",
+           "strided_transposed": "4a", "rank8_div": "4b", "gpt_residual": "5"}
+TARGETS = {"fwd": 0.80, "bwd_reduce": 0.65}
+MAIN_DESC = ("gpt_residual: out = h[16,2048,4096] * gamma[4096] + resid[16,2048,4096], "
+             "forward (mul, add) + backward (grad_h, grad_gamma reduced over 32768 rows, "
+             "grad_resid)")
 ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
        "rank8_div", "gpt_residual",
        # the three two-operator expressions again, each as one fused call per
@@ -170,26 +183,32 @@ def time_steps(graphs, chunk, K, W, torch):
     return time.perf_counter() - t0
 
 
-def copy_ceiling(torch, nbytes=1 << 30, reps=20):
-    """Practical HBM ceiling: a plain 1 GiB device-to-device tensor copy
-    (read + write), timed the same way (graph, synchronised)."""
+def calibration(torch, nbytes=1 << 30, reps=20):
+    """Practical HBM ceilings: 1 GiB copied device to device (read + write
+    counted) by the library's own streaming copy (zk_materialize of a dense
+    tensor: 128-bit non-temporal loads and stores) and by hipMemcpyAsync
+    (torch's copy_ of a contiguous tensor), each the median of `reps` copies
+    timed with events on the stream it runs on."""
+    from broadcast_autograd_amd import zk
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
     dst = torch.empty_like(src)
-    g = torch.cuda.CUDAGraph()
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        dst.copy_(src)
-    g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        g.replay()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    del src, dst, g
+    out = {}
+    for name, fn in (("zk_copy_16B", lambda: zk.materialize(src, out=dst)),
+                     ("hipMemcpyAsync_DtoD", lambda: dst.copy_(src))):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        out[name] = round(2 * nbytes / float(np.median(ts)) / 1e9, 1)
+    del src, dst
     torch.cuda.empty_cache()
-    return 2 * nbytes / dt / 1e9
+    return out
 
 
 def profile_calls(sets, reps, torch):
@@ -264,10 +283,14 @@ def measure(name, host, K, W, torch, reps=None, check=True):
         us = sum(kern.values())
         calls.append(dict(name=c.name, kind=c.kind, bytes=c.bytes, elements=c.elements, us=us,
                           kernels_us=kern, gbs=c.bytes / (us * 1e-6) / 1e9 if us else None))
+    for cc, c in zip(calls, wl.calls):
+        cc["reduce"] = c.reduce
     fwd_b = sum(c["bytes"] for c in calls if c["kind"] == "fwd")
     bwd_b = sum(c["bytes"] for c in calls if c["kind"] == "bwd")
     fwd_us = sum(c["us"] for c in calls if c["kind"] == "fwd")
     bwd_us = sum(c["us"] for c in calls if c["kind"] == "bwd")
+    red_b = sum(c["bytes"] for c in calls if c["kind"] == "bwd" and c["reduce"])
+    red_us = sum(c["us"] for c in calls if c["kind"] == "bwd" and c["reduce"])
     res = dict(
         workload=name, step_bytes=step_bytes, buffer_sets=len(sets),
         set_bytes=fp, steps=K, warmup=W, seconds=secs,
@@ -276,46 +299,85 @@ def measure(name, host, K, W, torch, reps=None, check=True):
         fwd_kernel_gbs=fwd_b / (fwd_us * 1e-6) / 1e9 if fwd_us else None,
         bwd_kernel_gbs=bwd_b / (bwd_us * 1e-6) / 1e9 if bwd_us else None,
         fwd_bwd_kernel_gbs=(fwd_b + bwd_b) / ((fwd_us + bwd_us) * 1e-6) / 1e9,
+        bwd_reduce_kernel_gbs=red_b / (red_us * 1e-6) / 1e9 if red_us else None,
         calls=calls, profile_reps=reps * len(sets), enqueue_s=enq,
         spin_plus_run_s=spin_total)
-    for k in ("step_gbs", "fwd_kernel_gbs", "bwd_kernel_gbs", "fwd_bwd_kernel_gbs"):
+    for k in ("step_gbs", "fwd_kernel_gbs", "bwd_kernel_gbs", "fwd_bwd_kernel_gbs",
+              "bwd_reduce_kernel_gbs"):
         if res[k] is not None:
             res[k.replace("gbs", "frac")] = res[k] * 1e9 / PEAK_HBM
+    if name in CONFIGS:
+        res["config"] = CONFIGS[name]
+        res["targets"] = {
+            "fwd": {"frac": round(res["fwd_kernel_frac"], 4), "target": TARGETS["fwd"],
+                    "met": res["fwd_kernel_frac"] >= TARGETS["fwd"]},
+            "bwd_reduce": {"frac": round(res["bwd_reduce_kernel_frac"], 4),
+                           "target": TARGETS["bwd_reduce"],
+                           "met": res["bwd_reduce_kernel_frac"] >= TARGETS["bwd_reduce"]}}
     del sets, graphs, chunk
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(host, target_s=12.0):
-    """The oracle on the whole MLP bias + GeLU step, on the host cores."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(target_s=10.0, rows=256):
+    """The oracle on a row slice of the residual workload (h[1,rows,4096],
+    the same per-row work as every one of the full workload's 32768 rows):
+    forward mul and add, backward to h, gamma and resid, repeated for about
+    target_s seconds, once on one thread and once on every core this
+    process may use.  GB/s = the slice step's algorithmic bytes / time."""
     import oracle
-    threads = min(os.cpu_count() or 1, 16)
-    oracle.set_threads(threads)
+    from broadcast_autograd_amd import workloads as Wk
+    host = Wk.gpt_residual(1, rows, 4096)
+    nh, ng = host["h"].size, host["gamma"].size
+    step_bytes = 4 * ((nh + ng + nh) + (3 * nh) + (3 * nh + ng + nh + ng) + (2 * nh))
 
     def step():
-        oracle.fwd("add", host["act"], host["bias"], epi=oracle.EPI_GELU)
-        oracle.bwd("add", host["g"], host["act"], host["bias"], epi=oracle.EPI_GELU)
+        t = oracle.fwd("mul", host["h"], host["gamma"])
+        oracle.fwd("add", t, host["resid"])
+        oracle.bwd("mul", host["g"], host["h"], host["gamma"])
+        oracle.bwd("add", host["g"], t, host["resid"], want=(False, True))
 
-    step()
-    n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < target_s:
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    allc = max(1, min(avail, int(omp))) if omp and omp.isdigit() else avail
+    res = {}
+    for threads in (1, allc):
+        oracle.set_threads(threads)
         step()
-        n += 1
-    dt = (time.perf_counter() - t0) / n
-    return threads, n, dt
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < target_s:
+            step()
+            n += 1
+        dt = (time.perf_counter() - t0) / n
+        res[threads] = (n, dt, step_bytes / dt / 1e9)
+    return res, allc, avail, rows
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=MAIN, choices=ALL)
     ap.add_argument("--others", default="all",
                     help="comma list of other workloads to report, 'all' or 'none'")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--other-steps", type=int, default=None,
                     help="timed steps of each other workload (default 40 for the "
                          "1 GB-scale ones, 400 for the small ones)")
@@ -340,8 +402,8 @@ def main():
     gen["attn_mask_grad"] = Wk.attn_mask_grad
     log(f"[bench] device {torch.cuda.get_device_name(0)}; spin check "
         f"{spin_seconds(torch) * 1e3:.1f} ms")
-    ceiling = copy_ceiling(torch)
-    log(f"[bench] 1 GiB device copy: {ceiling:.1f} GB/s (read + write)")
+    calib = calibration(torch)
+    log(f"[bench] 1 GiB device copies (read + write): {calib}")
     main_host = gen[args.workload]()
     log(f"[bench] main workload {args.workload}: {args.steps} steps")
     res = measure(args.workload, main_host, args.steps, args.warmup, torch)
@@ -365,7 +427,8 @@ def main():
             return "-" if v is None else f"{v:.1f}"
         log(f"[bench]   {r['ms_per_step'] * 1e3:.2f} us/step, {r['step_gbs']:.1f} GB/s; "
             f"fwd kernels {gbs(r['fwd_kernel_gbs'])} GB/s, bwd kernels "
-            f"{gbs(r['bwd_kernel_gbs'])} GB/s")
+            f"{gbs(r['bwd_kernel_gbs'])} GB/s, reducing bwd call "
+            f"{gbs(r['bwd_reduce_kernel_gbs'])} GB/s")
         per[w] = r
 
     # dominant kernel of the main step: the largest total kernel time
@@ -375,22 +438,32 @@ def main():
             if best is None or us > best[2]:
                 best = (c, k, us)
     c, kname, kus = best
-    hbm = c["bytes"] / (kus * 1e-6) / 1e9
+    # the launch's own algorithmic bytes: a reducing call's stage-1 kernel
+    # moves everything but the reduced gradient its stage 2 writes
+    kbytes = c["bytes"]
+    if c["reduce"] and "red_final" in c["kernels_us"] and kname != "red_final":
+        kbytes -= 4 * c["reduce"]
+    hbm = kbytes / (kus * 1e-6) / 1e9
     traffic = read_traffic(args.workload, kname)
     roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM / 1e9,
             "unit": "GB/s", "frac": round(hbm * 1e9 / PEAK_HBM, 4),
             "traffic": traffic, "kernel": kname, "call": c["name"],
-            "bytes_per_launch": c["bytes"], "us_per_launch": round(kus, 3)}
+            "bytes_per_launch": kbytes, "us_per_launch": round(kus, 3)}
 
     cpu = None
     if not args.no_cpu:
         log("[bench] oracle on the host cores ...")
-        threads, n, dt = cpu_baseline(gen[MAIN](), args.cpu_seconds)
-        step_bytes = per[MAIN]["step_bytes"] if MAIN in per else None
-        cpu = {"value": round(step_bytes / dt / 1e9, 3) if step_bytes else None,
-               "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": f"{n} full mlp_bias_gelu steps (act[4096,1024]: forward add+GeLU "
-                         f"and backward to act and bias), {dt * 1e3:.1f} ms each"}
+        res_cpu, allc, avail, rows = cpu_baseline(args.cpu_seconds)
+        n1, dt1, v1 = res_cpu[1]
+        na, dta, va = res_cpu[allc]
+        cpu = {"value": round(va, 4), "unit": "GB/s", "cores": allc, "kind": "oracle",
+               "sample": f"gpt_residual on h[1,{rows},4096] (a {rows}-row slice of the "
+                         f"32768 rows; same per-row work): forward mul and add, backward "
+                         f"to h, gamma and resid; {na} steps of {dta * 1e3:.1f} ms on "
+                         f"{allc} threads, {n1} steps of {dt1 * 1e3:.1f} ms on 1 thread",
+               "one_core": {"value": round(v1, 4), "cores": 1},
+               "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+               "cpus_available": avail}
 
     line = {
         "metric": METRIC,
@@ -405,16 +478,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: y = GeLU(act[4096,1024] + bias[1024]), "
-                               "forward + backward (grad_act, grad_bias)"
-                   if args.workload == MAIN else args.workload,
+        "config": {"workload": MAIN_DESC if args.workload == MAIN else args.workload,
                    "step_bytes": res["step_bytes"],
                    "hbm_peak_frac": round(res["step_frac"], 4),
                    "fwd_kernel_gbs": round(res["fwd_kernel_gbs"], 1),
                    "bwd_kernel_gbs": round(res["bwd_kernel_gbs"], 1),
                    "buffer_sets": res["buffer_sets"],
                    "launch": "hip graphs (one per rotation of buffer sets)",
-                   "copy_ceiling_gbs": round(ceiling, 1)},
+                   "fwd_frac": round(res["fwd_kernel_frac"], 4),
+                   "bwd_reduce_frac": round(res["bwd_reduce_kernel_frac"], 4)
+                   if res.get("bwd_reduce_kernel_frac") is not None else None,
+                   "calibration_copy_gbs": calib},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_config": {w: {k: (round(v, 4) if isinstance(v, float) else v)

@@ -256,8 +256,9 @@ __global__ __launch_bounds__(kBlk) void k_bwd_ew_generic(
 // the device-scope fences it needs cost more than the second launch.)
 struct ColArgs {
   int64_t R, K, rcw, ss, colblocks;
-  int64_t kmod;  // the small operand's columns: column c reads element c % kmod
-                 // (kmod == K, or a power of two below it for folded rows)
+  int64_t bands;  // row bands (partials per fold copy): blocks = colblocks * bands
+  int64_t kmod;   // the small operand's columns: column c reads element c % kmod
+                  // (kmod == K, or a power of two below it for folded rows)
   int32_t write_big;
 };
 
@@ -290,110 +291,93 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   // epilogue, whose arithmetic is long enough per row (measured: the
   // [4096, 1024] GeLU step is ~10% faster than with two)
   constexpr int U = EPI == ZK_EPI_GELU ? 1 : 2;
-  constexpr bool PF = false;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l = threadIdx.x & 63;
-  const int64_t p = blockIdx.x / ca.colblocks;
-  const int64_t cb = blockIdx.x - p * ca.colblocks;
-  const int64_t c = cb * 256 + 4 * l;
-  const bool active = c < ca.K;
-  float sv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (NEED_SMALL && active) {
-    // folded rows: kmod is a power of two dividing 256 and c a multiple of 4
-    const int64_t cm = ca.kmod < ca.K ? (c & (ca.kmod - 1)) : c;
+  __shared__ double lds[NW > 1 ? NW : 1][4][64];
+  // (band p, column group cb) blocks; one per workgroup up to the grid cap,
+  // then with a grid stride (block-uniform, so the LDS barriers stay uniform)
+  const int64_t blocks = ca.colblocks * ca.bands;
+  for (int64_t it = blockIdx.x; it < blocks; it += gridDim.x) {
+    const int64_t p = it / ca.colblocks;
+    const int64_t cb = it - p * ca.colblocks;
+    const int64_t c = cb * 256 + 4 * l;
+    const bool active = c < ca.K;
+    float sv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (NEED_SMALL && active) {
+      // folded rows: kmod is a power of two dividing 256 and c a multiple of 4
+      const int64_t cm = ca.kmod < ca.K ? (c & (ca.kmod - 1)) : c;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sv[k] = small[(cm + k) * ca.ss];
-  }
-  const int64_t r0 = (p * NW + w) * ca.rcw;
-  const int64_t r1 = r0 + ca.rcw < ca.R ? r0 + ca.rcw : ca.R;
-  double s[4] = {0.0, 0.0, 0.0, 0.0};
-  auto load = [&](int64_t rb, float4 *vg, float4 *vb, float4 *va) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t r = rb + u;
-      if (r < r1) {
-        const int64_t i = r * ca.K + c;
-        vg[u] = ld4_nt(g + i);
-        if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
-        if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
-      }
+      for (int k = 0; k < 4; ++k) sv[k] = small[(cm + k) * ca.ss];
     }
-  };
-  auto process = [&](int64_t rb, const float4 *vg, const float4 *vb, const float4 *va) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t r = rb + u;
-      if (r < r1) {
-        const int64_t i = r * ca.K + c;
-        float gv[4], x[4], y[4], tb[4];
-        double ts[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          gv[k] = el(vg[u], k);
-          const float bv = NEED_BIG ? el(vb[u], k) : 0.f;
-          x[k] = SIDE == 0 ? sv[k] : bv;
-          y[k] = SIDE == 0 ? bv : sv[k];
-        }
-        terms2_w<OP, EPI, SIDE, 4>(gv, x, y, ts, tb);
-        float4 ob;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          s[k] += ts[k];
-          float t = tb[k];
-          if constexpr (ACC == 1) t = gv[k] + t;
-          if constexpr (ACC == 2) t = el(va[u], k) + t;
-          el(ob, k) = t;
-        }
-        if (ca.write_big) st4_nt(gbig + i, ob);
-        if (gco.p) gc_store4(gco, i, vg[u]);
-      }
-    }
-  };
-  if (active) {
-    float4 vg[U], vb[U], va[U];
-    if constexpr (PF) {
-      // the next rows' loads are issued before this row's arithmetic
-      if (r0 < r1) load(r0, vg, vb, va);
+    const int64_t r0 = (p * NW + w) * ca.rcw;
+    const int64_t r1 = r0 + ca.rcw < ca.R ? r0 + ca.rcw : ca.R;
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    if (active) {
       for (int64_t rb = r0; rb < r1; rb += U) {
-        float4 ng[U], nb[U], na[U];
-        if (rb + U < r1) load(rb + U, ng, nb, na);
-        process(rb, vg, vb, va);
+        float4 vg[U], vb[U], va[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          vg[u] = ng[u];
-          if constexpr (NEED_BIG) vb[u] = nb[u];
-          if constexpr (ACC == 2) va[u] = na[u];
+          const int64_t r = rb + u;
+          if (r < r1) {
+            const int64_t i = r * ca.K + c;
+            vg[u] = ld4_nt(g + i);
+            if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
+            if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t r = rb + u;
+          if (r < r1) {
+            const int64_t i = r * ca.K + c;
+            float gv[4], x[4], y[4], tb[4];
+            double ts[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              gv[k] = el(vg[u], k);
+              const float bv = NEED_BIG ? el(vb[u], k) : 0.f;
+              x[k] = SIDE == 0 ? sv[k] : bv;
+              y[k] = SIDE == 0 ? bv : sv[k];
+            }
+            terms2_w<OP, EPI, SIDE, 4>(gv, x, y, ts, tb);
+            float4 ob;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              s[k] += ts[k];
+              float t = tb[k];
+              if constexpr (ACC == 1) t = gv[k] + t;
+              if constexpr (ACC == 2) t = el(va[u], k) + t;
+              el(ob, k) = t;
+            }
+            if (ca.write_big) st4_nt(gbig + i, ob);
+            if (gco.p) gc_store4(gco, i, vg[u]);
+          }
+        }
+      }
+    }
+    if constexpr (NW == 1) {
+      if (active) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (DIRECT) cd.out[c + k] = col_direct(cd, c + k, s[k]);
+          else part[p * ca.K + c + k] = s[k];
         }
       }
     } else {
-      for (int64_t rb = r0; rb < r1; rb += U) {
-        load(rb, vg, vb, va);
-        process(rb, vg, vb, va);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lds[w][k][l] = s[k];
+      __syncthreads();
+      if (w == 0 && active) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          double tot = lds[0][k][l];
+#pragma unroll
+          for (int ww = 1; ww < NW; ++ww) tot += lds[ww][k][l];
+          if constexpr (DIRECT) cd.out[c + k] = col_direct(cd, c + k, tot);
+          else part[p * ca.K + c + k] = tot;
+        }
       }
-    }
-  }
-  if constexpr (NW == 1) {
-    if (active) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (DIRECT) cd.out[c + k] = col_direct(cd, c + k, s[k]);
-        else part[p * ca.K + c + k] = s[k];
-      }
-    }
-  } else {
-    __shared__ double lds[NW][4][64];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) lds[w][k][l] = s[k];
-    __syncthreads();
-    if (w == 0 && active) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        double tot = lds[0][k][l];
-#pragma unroll
-        for (int ww = 1; ww < NW; ++ww) tot += lds[ww][k][l];
-        if constexpr (DIRECT) cd.out[c + k] = col_direct(cd, c + k, tot);
-        else part[p * ca.K + c + k] = tot;
-      }
+      __syncthreads();  // lds is rewritten by the block's next (band, group)
     }
   }
 }
@@ -815,6 +799,61 @@ __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
   }
 }
 
+// Stage 2 when a kept element owns C consecutive columns of every partial
+// row ([R1, K, C] -> [K, 1] walked as column sums of [R1, K * C]): out[k] =
+// RN32(sum over p < P, c < C of part[p][k * C + c] (+ acc[k])).  tpk threads
+// (a power of two) per kept element walk its P * C values v = p * C + c
+// (thread q takes v = q + j * tpk, so adjacent threads read adjacent
+// columns), add them in a fixed tree of eight, and the subtotals meet in an
+// LDS tree.
+struct FinColsArgs {
+  int64_t K, P, C, per;  // per: values per thread
+  int32_t tpk, kt, has_acc, neg, has_div;
+  double div;
+};
+
+__global__ __launch_bounds__(kBlk) void k_red_final_cols(const double *part,
+                                                         const float *acc, float *out,
+                                                         FinColsArgs fa) {
+  __shared__ double sh[kBlk];
+  const int t = threadIdx.x;
+  const int q = t % fa.tpk, kk = t / fa.tpk;
+  const int64_t groups = (fa.K + fa.kt - 1) / fa.kt;
+  const uint32_t V = (uint32_t)(fa.P * fa.C), C = (uint32_t)fa.C;  // V < 2^31 (planner)
+  const int64_t row = fa.K * fa.C;
+  for (int64_t kg = blockIdx.x; kg < groups; kg += gridDim.x) {
+    const int64_t k = kg * fa.kt + kk;
+    const bool ok = k < fa.K;
+    double s = 0.0;
+    for (int64_t j0 = 0; j0 < fa.per; j0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t vi = q + (j0 + j) * fa.tpk;
+        v[j] = 0.0;
+        if (ok && j0 + j < fa.per && vi < (int64_t)V) {
+          const uint32_t pp = (uint32_t)vi / C, cc = (uint32_t)vi - pp * C;
+          v[j] = part[(int64_t)pp * row + k * fa.C + cc];
+        }
+      }
+      s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    }
+    sh[t] = s;
+    __syncthreads();
+    for (int off = fa.tpk >> 1; off >= 1; off >>= 1) {
+      if (q < off) sh[t] += sh[t + off];
+      __syncthreads();
+    }
+    if (q == 0 && ok) {
+      double tot = fa.neg ? -sh[t] : sh[t];
+      if (fa.has_acc) tot += (double)acc[k];
+      if (fa.has_div) tot = tot / fa.div;
+      out[k] = (float)tot;
+    }
+    __syncthreads();  // sh is rewritten by the next group
+  }
+}
+
 // ------------------------------------------------------------ bwd_signed
 // gc[i] = sign * g[i] (+ acc[i]) over the dense output layout: the gradient
 // of the second operator's c when no stage-1 kernel streams g for it.
@@ -864,7 +903,21 @@ static hipError_t with_col_waves(int nw, bool direct, Fn fn) {
 
 // Short columns finish in stage 1 (k_red_col with DIRECT).
 static bool col_direct_plan(const RedPlan &rp) {
-  return rp.kernel == K_RED_COL && rp.partials == 1 && rp.nw == kColWavesFew;
+  return rp.kernel == K_RED_COL && rp.partials == 1 && rp.nw == kColWavesFew && rp.csub == 1;
+}
+
+// red_col's arguments for its plan: the [rows, cols] matrix, folded.
+static ColArgs col_args(const RedPlan &rp, int64_t ss, bool write_big) {
+  ColArgs ca{};
+  ca.R = rp.col_rows / rp.fold;
+  ca.K = rp.col_cols * rp.fold;
+  ca.kmod = rp.col_cols;
+  ca.rcw = rp.chunk;
+  ca.ss = ss;
+  ca.colblocks = (ca.K + 255) / 256;
+  ca.bands = rp.partials / rp.fold;
+  ca.write_big = write_big ? 1 : 0;
+  return ca;
 }
 
 // One-pass row reduction (red_rowd): stage 1 and the final rounding.
@@ -910,6 +963,26 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
                                const float *acc, float *out, hipStream_t st,
                                bool neg = false, double mean_count = -1.0) {
   if (rp.kept == 0) return hipSuccess;
+  if (rp.csub > 1) {
+    FinColsArgs fc{};
+    fc.K = rp.kept;
+    fc.P = rp.partials;
+    fc.C = rp.csub;
+    const int64_t V = fc.P * fc.C;
+    int tpk = 1;
+    while (tpk < kBlk && V > 8 * (int64_t)tpk) tpk *= 2;
+    fc.tpk = tpk;
+    fc.kt = kBlk / tpk;
+    fc.per = (V + tpk - 1) / tpk;
+    fc.has_acc = acc != nullptr;
+    fc.neg = neg ? 1 : 0;
+    fc.has_div = mean_count >= 0.0;
+    fc.div = mean_count;
+    ProfScope prof(K_RED_FINAL);
+    ZK_LAUNCH(prof, k_red_final_cols, dim3(gridn(rp.kept, fc.kt)), dim3(kBlk), 0, st, part,
+              acc, out, fc);
+    return hipGetLastError();
+  }
   FinArgs fa{};
   fa.neg = neg ? 1 : 0;
   fa.K = rp.kept;
@@ -1303,16 +1376,9 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
         ProfScope prof(rp.kernel);
         switch (rp.kernel) {
           case K_RED_COL: {
-            ColArgs ca{};
-            ca.R = c.n[0] / rp.fold;
-            ca.K = c.n[1] * rp.fold;
-            ca.kmod = c.n[1];
-            ca.rcw = rp.chunk;
-            ca.ss = c.s[1 + sw][1];
-            ca.colblocks = (ca.K + 255) / 256;
-            ca.write_big = p.fused_big;
+            const ColArgs ca = col_args(rp, c.s[1 + sw][1], p.fused_big);
             ColDirect cd{gsmall, accsmall, 0, 0, 0.0};
-            unsigned grid = (unsigned)(ca.colblocks * (rp.partials / rp.fold));
+            const unsigned grid = gridn(ca.colblocks * ca.bands, 1);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
               return with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
@@ -1443,16 +1509,9 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
       ProfScope prof(rp.kernel);
       switch (rp.kernel) {
         case K_RED_COL: {
-          ColArgs ca{};
-          ca.R = c.n[0] / rp.fold;
-          ca.K = c.n[1] * rp.fold;
-          ca.kmod = c.n[1];
-          ca.rcw = rp.chunk;
-          ca.ss = 0;
-          ca.colblocks = (ca.K + 255) / 256;
-          ca.write_big = 0;
+          const ColArgs ca = col_args(rp, 0, false);
           const ColDirect cd{out, acc, neg ? 1 : 0, mean_count >= 0.0 ? 1 : 0, mean_count};
-          const unsigned grid = (unsigned)(ca.colblocks * (rp.partials / rp.fold));
+          const unsigned grid = gridn(ca.colblocks * ca.bands, 1);
           hipError_t e = with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
             constexpr int NW = decltype(Wc)::value;
             constexpr bool D = decltype(Dc)::value;

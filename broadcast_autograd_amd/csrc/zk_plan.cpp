@@ -450,6 +450,59 @@ static bool size_gend(RedPlan *rp, int64_t K, int64_t red) {
   return true;
 }
 
+// Sizing of a red_col column sum over a dense [rows, cols] matrix (cols a
+// multiple of 4): kept = cols, one partial per band of rows.
+static void size_col(RedPlan *rp, int64_t rows, int64_t cols) {
+  rp->kernel = K_RED_COL;
+  rp->kept = cols;
+  rp->red = rows;
+  rp->col_rows = rows;
+  rp->col_cols = cols;
+  rp->csub = 1;
+  // A wave owns 256 columns and walks rcw rows: enough waves to fill the
+  // chip (~8192), between 4 and 64 rows each.  The waves of a block
+  // combine their sums (kColWavesFew / kColWavesMany), so a partial covers
+  // >= 16 rows and binary64 partials stay within a few % of the call's
+  // bytes.  The number of blocks (column groups x partials) stays within
+  // the dispatch limit where the rows allow it; the kernel walks its blocks
+  // with a grid stride past that.
+  // Narrow columns (cols < 256 dividing 256, e.g. [4194304, 32]): fold =
+  // 256/cols consecutive rows of the dense operands form one row of 256
+  // columns, so every lane of a wave stays busy; stage 2 then sums the fold
+  // copies of each column along with the partials.
+  int64_t fold = 1;
+  if (cols < 256 && 256 % cols == 0 && rows % (256 / cols) == 0) fold = 256 / cols;
+  const int64_t R0 = rows / fold;
+  const int64_t colblocks = ceil_div(cols * fold, 256);
+  int64_t rcw = std::min<int64_t>(kColRowsMany, std::max<int64_t>(4, R0 * colblocks / 8192));
+  int nw = rcw >= kColRowsMany ? kColWavesMany : kColWavesFew;
+  // Short columns (fewer rows than a block spans, e.g. [128, 1048576]):
+  // kColWavesFew waves (one below that many rows) split the rows evenly,
+  // one partial a column, rather than most waves of a block idling.
+  if (R0 < nw * rcw) {
+    nw = R0 >= kColWavesFew ? kColWavesFew : 1;
+    rcw = std::max<int64_t>(1, ceil_div(R0, nw));
+  }
+  // Longer row bands while the grid is above the dispatch limit, down to a
+  // single band (more than 2^30 columns stay above it).
+  while (colblocks * ceil_div(R0, nw * rcw) > kMaxGridBlocks && nw * rcw < R0) rcw *= 2;
+  rp->chunk = rcw;
+  rp->nw = nw;
+  rp->fold = (int32_t)fold;
+  rp->partials = ceil_div(R0, nw * rcw) * fold;
+}
+
+// red_col over [rows, cols] for a sum whose kept elements own C consecutive
+// columns each: stage 2 indexes each kept element's partials * C values with
+// 32 bits, so the plan is taken only below 2^31 of them.
+static bool col_sub_fits(int64_t rows, int64_t cols, int64_t C, RedPlan *rp) {
+  RedPlan q;
+  size_col(&q, rows, cols);
+  if (q.partials * C >= ((int64_t)1 << 31)) return false;
+  *rp = q;
+  return true;
+}
+
 // Try the fast stage-1 classes for the reduced operand stride set `o`
 // (grad layout) with `big` the dense operand id (or -1 if none is read).
 // Requires the source (op 0) to be dense.
@@ -473,38 +526,7 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
     }
     if (big_op >= 0 && !is_flat(c, big_op)) return false;
     if (inner % 4 != 0) return false;
-    rp->kernel = K_RED_COL;
-    rp->kept = c.n[1];
-    rp->red = c.n[0];
-    // A wave owns 256 columns and walks rcw rows: enough waves to fill the
-    // chip (~8192), between 4 and 64 rows each.  The waves of a block
-    // combine their sums (kColWavesFew / kColWavesMany), so a partial covers
-    // >= 16 rows and binary64 partials stay within a few % of the call's
-    // bytes.  The grid (column groups x partials) stays within the dispatch
-    // limit.
-    // Narrow columns (K < 256 dividing 256, e.g. [4194304, 32]): fold = 256/K
-    // consecutive rows of the dense operands form one row of 256 columns, so
-    // every lane of a wave stays busy; stage 2 then sums the fold copies of
-    // each column along with the partials.
-    int64_t fold = 1;
-    if (c.n[1] < 256 && 256 % c.n[1] == 0 && c.n[0] % (256 / c.n[1]) == 0)
-      fold = 256 / c.n[1];
-    const int64_t R0 = c.n[0] / fold;
-    const int64_t colblocks = ceil_div(c.n[1] * fold, 256);
-    int64_t rcw = std::min<int64_t>(kColRowsMany, std::max<int64_t>(4, R0 * colblocks / 8192));
-    int nw = rcw >= kColRowsMany ? kColWavesMany : kColWavesFew;
-    // Short columns (fewer rows than a block spans, e.g. [128, 1048576]):
-    // kColWavesFew waves (one below that many rows) split the rows evenly,
-    // one partial a column, rather than most waves of a block idling.
-    if (R0 < nw * rcw) {
-      nw = R0 >= kColWavesFew ? kColWavesFew : 1;
-      rcw = std::max<int64_t>(1, ceil_div(R0, nw));
-    }
-    while (colblocks * ceil_div(R0, nw * rcw) > kMaxGridBlocks) rcw *= 2;
-    rp->chunk = rcw;
-    rp->nw = nw;
-    rp->fold = (int32_t)fold;
-    rp->partials = ceil_div(R0, nw * rcw) * fold;
+    size_col(rp, c.n[0], c.n[1]);
     return true;
   }
   if (big_transposed) return false;
@@ -551,7 +573,8 @@ static void finish_workspace(BwdPlan *p) {
   size_t off = 0;
   for (int i = 0; i < p->nred; ++i) {
     p->red[i].ws_offset = off;
-    off += round256((size_t)p->red[i].partials * (size_t)p->red[i].kept * 8u);
+    off += round256((size_t)p->red[i].partials * (size_t)p->red[i].kept *
+                    (size_t)p->red[i].csub * 8u);
   }
   p->workspace = off;
 }
@@ -733,21 +756,35 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
   RedPlan rp;
   // Short dense rows (C <= 256 dividing 256, aligned): a wave reads 256 / C
   // whole rows at a time (red_rowseg).  [K, C] to [K, 1]: each row sum is the
-  // result (no partials).  [R1, K, C] to [K, 1]: the row sums are binary64
-  // partials [R1, K] for stage 2, unless red_rowd takes the whole sum in one
-  // pass (R1 * C within its term range).
+  // result (no partials).  [R1, K, C] to [K, 1] with R1 <= C: the row sums are
+  // binary64 partials [R1, K] for stage 2 (at most kRowSegMaxPartials a kept
+  // element, 2 / C of the input's bytes), unless red_rowd takes the whole sum
+  // in one pass (R1 * C within its term range).  With R1 > C the same sum
+  // walks the dense [R1, K * C] matrix as column sums (red_col), whose
+  // partials cover bands of rows, and stage 2 adds each kept element's C
+  // columns along with its partials.
   const int64_t C = c.n[c.rank - 1];
-  const bool short_rows = K < c.numel && src_flat && al16(pin) && C >= 4 && C <= 256 &&
-                          256 % C == 0;
+  const bool dense_al = K < c.numel && src_flat && al16(pin);
+  const bool row2 = c.rank == 2 && kept_mask(c, 4) == 1u && c.s[4][0] == 1;
+  const bool mid3 = c.rank == 3 && kept_mask(c, 4) == 2u && c.s[4][1] == 1;
+  const bool short_rows = dense_al && C >= 4 && C <= 256 && 256 % C == 0;
   const bool rowd_range = c.rank == 3 && C == 256 && c.n[0] * C >= kDirMinTerms &&
                           c.n[0] * C <= kDirMaxTerms;  // red_rowd needs rows of >= 256
-  if (short_rows && ((c.rank == 2 && kept_mask(c, 4) == 1u && c.s[4][0] == 1) ||
-                     (c.rank == 3 && kept_mask(c, 4) == 2u && c.s[4][1] == 1 && !rowd_range))) {
+  const int64_t KC = mid3 ? c.n[1] * C : 0;
+  if (short_rows && (row2 || (mid3 && !rowd_range && c.n[0] <= C))) {
     rp.kernel = K_RED_ROWSEG;
     rp.kept = c.n[c.rank - 2];
     rp.red = c.numel / rp.kept;
     rp.chunk = C;
     rp.partials = c.rank == 3 ? c.n[0] : 0;
+    rp.which = 1;
+    p->red[p->nred++] = rp;
+    p->vec = 4;
+  } else if (dense_al && mid3 && !rowd_range && C % 4 == 0 && C <= 256 &&
+             (KC >= 256 || 256 % KC == 0) && col_sub_fits(c.n[0], KC, C, &rp)) {
+    rp.kept = c.n[1];
+    rp.csub = (int32_t)C;
+    rp.red = c.n[0] * C;
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;

@@ -186,9 +186,18 @@ struct RedPlan {
   int32_t fold = 1;          // COL: rows of K < 256 columns read as one row of
                              // fold*K = 256 (stage 1 runs on [R/fold, 256];
                              // partials counts the fold copies too)
+  int64_t col_rows = 0;      // COL: the [rows, cols] matrix stage 1 walks
+  int64_t col_cols = 0;      //      (before folding)
+  int32_t csub = 1;          // COL: consecutive columns per kept element
+                             // ([R1, K, C] -> [K, 1] walks [R1, K*C]; stage 2
+                             // sums each kept element's C columns too)
   int64_t red = 0;           // reduced elements per kept element
   size_t ws_offset = 0;      // byte offset of its partials in the workspace
 };
+// Rank-3 red_rowseg ([R1, K, C] -> [K, 1], row sums as stage-2 partials) is
+// planned only for R1 <= C, so a kept element has at most this many partials
+// and the partials hold at most 2 / C of the input's bytes.
+constexpr int64_t kRowSegMaxPartials = 256;
 
 struct BwdPlan {
   Canon c;                 // ops: 0 grad, 1 a, 2 b, 3 grad_a, 4 grad_b

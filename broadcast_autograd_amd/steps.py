@@ -22,10 +22,15 @@ def _n(shape):
 
 
 class Call:
-    def __init__(self, name, kind, fn, reads, writes):
+    """One library call of a step.  ``reduce``: the call sums a gradient back
+    to a broadcast operand's shape, and this many reduced elements are
+    written (by the call's last kernel when it has a separate stage 2)."""
+
+    def __init__(self, name, kind, fn, reads, writes, reduce=None):
         self.name, self.kind, self.fn = name, kind, fn
         self.bytes = 4 * (sum(reads) + sum(writes))
         self.elements = max(writes)  # elements of the largest output
+        self.reduce = reduce
 
     def __call__(self):
         return self.fn()
@@ -79,7 +84,7 @@ class XYPlusX(Workload):
             Call("mul_bwd(g;x,y)->grad_x(acc=g),grad_y", "bwd",
                  lambda: zk.binary_bwd("mul", self.g, self.x, self.y, grad_a=self.grad_x,
                                        grad_b=self.grad_y, acc_a=self.g, workspace=self.ws),
-                 [nx, nx, ny], [nx, ny]),
+                 [nx, nx, ny], [nx, ny], reduce=ny),
         ]
 
 
@@ -106,7 +111,7 @@ class MLPBiasGelu(Workload):
                  lambda: zk.binary_bwd("add", self.g, self.act, self.bias,
                                        grad_a=self.grad_act, grad_b=self.grad_bias,
                                        epi="gelu", workspace=self.ws),
-                 [na, na, nb], [na, nb]),
+                 [na, na, nb], [na, nb], reduce=nb),
         ]
 
 
@@ -137,7 +142,7 @@ class AttnScaleMask(Workload):
                  lambda: zk.binary_bwd("mul", self.g, self.scores, self.scale,
                                        grad_a=self.grad_scores, grad_b=self.grad_scale,
                                        workspace=self.ws),
-                 [ns, ns, nc], [ns, nc]),
+                 [ns, ns, nc], [ns, nc], reduce=nc),
         ]
 
 
@@ -159,7 +164,7 @@ class AttnMaskGrad(Workload):
             Call("reduce_to_shape(g->[1,1,%d,%d])" % self.target[2:], "bwd",
                  lambda: zk.reduce_to_shape(self.g, self.target, out=self.grad_mask,
                                             workspace=self.ws),
-                 [ng], [nm]),
+                 [ng], [nm], reduce=nm),
         ]
 
 
@@ -186,7 +191,7 @@ class StridedTransposed(Workload):
             Call("mul_bwd(g;aT,b)->grad_a,grad_b", "bwd",
                  lambda: zk.binary_bwd("mul", self.g, self.a, self.b, grad_a=self.grad_a,
                                        grad_b=self.grad_b, workspace=self.ws),
-                 [na, na, nb], [na, nb]),
+                 [na, na, nb], [na, nb], reduce=nb),
         ]
 
 
@@ -210,7 +215,7 @@ class Rank8(Workload):
             Call("div_bwd(g;a,b)->grad_a,grad_b", "bwd",
                  lambda: zk.binary_bwd("div", self.g, self.a, self.b, grad_a=self.grad_a,
                                        grad_b=self.grad_b, workspace=self.ws),
-                 [na, na, nb], [na, nb]),
+                 [na, na, nb], [na, nb], reduce=nb),
         ]
 
 
@@ -239,7 +244,7 @@ class GPTResidual(Workload):
             Call("mul_bwd(g;h,gamma)->grad_h,grad_gamma", "bwd",
                  lambda: zk.binary_bwd("mul", self.g, self.h, self.gamma, grad_a=self.grad_h,
                                        grad_b=self.grad_gamma, workspace=self.ws),
-                 [nh, nh, ng], [nh, ng]),
+                 [nh, nh, ng], [nh, ng], reduce=ng),
             # add's gradient of t is g itself; resid's is materialised
             Call("add_bwd(g)->grad_resid", "bwd",
                  lambda: zk.binary_bwd("add", self.g, self.t, self.resid, need_a=False,
@@ -278,7 +283,7 @@ class XYPlusXFused(Workload):
                                         need=(True, True, True),
                                         grads=(self.grad_x, self.grad_y, None), tie="a",
                                         workspace=self.ws),
-                 [nx, nx, ny], [nx, ny]),
+                 [nx, nx, ny], [nx, ny], reduce=ny),
         ]
 
 
@@ -307,7 +312,7 @@ class AttnScaleMaskFused(Workload):
                                         self.mask, need=(True, True, False),
                                         grads=(self.grad_scores, self.grad_scale, None),
                                         workspace=self.ws),
-                 [ns, ns, nc], [ns, nc]),
+                 [ns, ns, nc], [ns, nc], reduce=nc),
         ]
 
 
@@ -336,7 +341,7 @@ class GPTResidualFused(Workload):
                  lambda: zk.binary2_bwd("mul", "add", self.g, self.h, self.gamma, self.resid,
                                         grads=(self.grad_h, self.grad_gamma, self.grad_resid),
                                         workspace=self.ws),
-                 [nh, nh, ng], [nh, ng, nh]),
+                 [nh, nh, ng], [nh, ng, nh], reduce=ng),
         ]
 
 

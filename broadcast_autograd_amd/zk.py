@@ -150,6 +150,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _keep(stream, *tensors):
+    """Tensors this wrapper allocated come from torch's caching allocator on
+    the current stream.  When the library runs on another stream, record that
+    use, so that a block freed on return (a workspace) or later is not handed
+    out again before that stream's kernels are done with it."""
+    if stream is None:
+        return
+    import torch
+    if stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -176,6 +191,7 @@ def binary_fwd(op, a, b, out=None, epi="none", stream=None):
     if out is None:
         shape = broadcast_shape(a.shape, b.shape)
         out = torch.empty(shape, dtype=torch.float32, device=a.device)
+        _keep(stream, out)
     da, db = desc_of(a), desc_of(b)
     _check(lib().zk_binary_fwd(_op(op), _epi(epi), _ptr(a), ctypes.byref(da),
                                _ptr(b), ctypes.byref(db), _ptr(out),
@@ -210,8 +226,10 @@ def binary_bwd(op, grad, a, b, need_a=True, need_b=True, grad_a=None,
     import torch
     if need_a and grad_a is None:
         grad_a = torch.empty(a.shape, dtype=torch.float32, device=grad.device)
+        _keep(stream, grad_a)
     if need_b and grad_b is None:
         grad_b = torch.empty(b.shape, dtype=torch.float32, device=grad.device)
+        _keep(stream, grad_b)
     if not need_a:
         grad_a = None
     if not need_b:
@@ -225,6 +243,7 @@ def binary_bwd(op, grad, a, b, need_a=True, need_b=True, grad_a=None,
         _check(L.zk_binary_bwd(*args, None, ctypes.byref(nbytes), None),
                "zk_binary_bwd(query)")
         workspace = _workspace(nbytes.value, grad.device)
+        _keep(stream, workspace)
     nbytes.value = workspace.numel() * workspace.element_size()
     _check(L.zk_binary_bwd(*args, _ptr(workspace), ctypes.byref(nbytes),
                            _stream(stream)), "zk_binary_bwd")
@@ -236,6 +255,7 @@ def scalar_fwd(op, t, s, scalar_first=False, out=None, epi="none", stream=None):
     import torch
     if out is None:
         out = torch.empty(tuple(t.shape), dtype=torch.float32, device=t.device)
+        _keep(stream, out)
     d = desc_of(t)
     _check(lib().zk_scalar_fwd(_op(op), _epi(epi), _ptr(t), ctypes.byref(d), float(s),
                                1 if scalar_first else 0, _ptr(out), _stream(stream)),
@@ -249,6 +269,7 @@ def scalar_bwd(op, grad, t, s, scalar_first=False, grad_t=None, acc_t=None, epi=
     import torch
     if grad_t is None:
         grad_t = torch.empty(tuple(t.shape), dtype=torch.float32, device=grad.device)
+        _keep(stream, grad_t)
     d = desc_of(t)
     _check(lib().zk_scalar_bwd(_op(op), _epi(epi), _ptr(grad), _ptr(t), ctypes.byref(d),
                                float(s), 1 if scalar_first else 0, _ptr(grad_t), _ptr(acc_t),
@@ -261,6 +282,7 @@ def unary_fwd(f, x, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty(tuple(x.shape), dtype=torch.float32, device=x.device)
+        _keep(stream, out)
     d = desc_of(x)
     _check(lib().zk_unary_fwd(_epi(f), _ptr(x), ctypes.byref(d), _ptr(out), _stream(stream)),
            "zk_unary_fwd")
@@ -272,6 +294,7 @@ def unary_bwd(f, grad, x, grad_x=None, acc_x=None, stream=None):
     import torch
     if grad_x is None:
         grad_x = torch.empty(tuple(x.shape), dtype=torch.float32, device=grad.device)
+        _keep(stream, grad_x)
     d = desc_of(x)
     _check(lib().zk_unary_bwd(_epi(f), _ptr(grad), _ptr(x), ctypes.byref(d), _ptr(grad_x),
                               _ptr(acc_x), _stream(stream)), "zk_unary_bwd")
@@ -285,6 +308,7 @@ def materialize(x, shape=None, out=None, stream=None):
     shape = tuple(x.shape) if shape is None else tuple(int(s) for s in shape)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
+        _keep(stream, out)
     d = desc_of(x)
     _check(lib().zk_materialize(_ptr(x), ctypes.byref(d), len(shape), _i64(shape), _ptr(out),
                                 _stream(stream)), "zk_materialize")
@@ -302,6 +326,7 @@ def binary2_fwd(op1, op2, a, b, c, out=None, stream=None):
     if out is None:
         shape = broadcast_shape3(a.shape, b.shape, c.shape)
         out = torch.empty(shape, dtype=torch.float32, device=a.device)
+        _keep(stream, out)
     da, db, dc = desc_of(a), desc_of(b), desc_of(c)
     _check(lib().zk_binary2_fwd(_op(op1), _op(op2), _ptr(a), ctypes.byref(da), _ptr(b),
                                 ctypes.byref(db), _ptr(c), ctypes.byref(dc), _ptr(out),
@@ -338,6 +363,7 @@ def binary2_bwd(op1, op2, grad, a, b, c, need=(True, True, True), grads=(None, N
         g = grads[k]
         if need[k] and g is None and not (k == 2 and tie is not None):
             g = torch.empty(ops[k].shape, dtype=torch.float32, device=grad.device)
+            _keep(stream, g)
         out.append(g if need[k] else None)
     if tie is not None:
         out[2] = out[0] if tie == "a" else out[1]
@@ -351,6 +377,7 @@ def binary2_bwd(op1, op2, grad, a, b, c, need=(True, True, True), grads=(None, N
         _check(L.zk_binary2_bwd(*args, None, ctypes.byref(nbytes), None),
                "zk_binary2_bwd(query)")
         workspace = _workspace(nbytes.value, grad.device)
+        _keep(stream, workspace)
     nbytes.value = workspace.numel() * workspace.element_size()
     _check(L.zk_binary2_bwd(*args, _ptr(workspace), ctypes.byref(nbytes), _stream(stream)),
            "zk_binary2_bwd")
@@ -375,6 +402,7 @@ def reduce_to_shape(x, shape, out=None, workspace=None, stream=None):
     shape = tuple(int(s) for s in shape)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
+        _keep(stream, out)
     d = desc_of(x)
     nbytes = ctypes.c_size_t(0)
     L = lib()
@@ -383,6 +411,7 @@ def reduce_to_shape(x, shape, out=None, workspace=None, stream=None):
                                     _ptr(out), None, ctypes.byref(nbytes), None),
                "zk_reduce_to_shape(query)")
         workspace = _workspace(nbytes.value, x.device)
+        _keep(stream, workspace)
     nbytes.value = workspace.numel() * workspace.element_size()
     _check(L.zk_reduce_to_shape(_ptr(x), ctypes.byref(d), len(shape), _i64(shape),
                                 _ptr(out), _ptr(workspace), ctypes.byref(nbytes),
@@ -397,11 +426,13 @@ def mean_to_shape(x, shape, out=None, workspace=None, stream=None):
     shape = tuple(int(s) for s in shape)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
+        _keep(stream, out)
     d = desc_of(x)
     nbytes = ctypes.c_size_t(0)
     L = lib()
     if workspace is None:
         workspace = _workspace(reduce_workspace_bytes(x, shape), x.device)
+        _keep(stream, workspace)
     nbytes.value = workspace.numel() * workspace.element_size()
     _check(L.zk_mean_to_shape(_ptr(x), ctypes.byref(d), len(shape), _i64(shape),
                               _ptr(out), _ptr(workspace), ctypes.byref(nbytes),
@@ -416,6 +447,7 @@ def mean_bwd(g, shape_in, out=None, stream=None):
     shape_in = tuple(int(s) for s in shape_in)
     if out is None:
         out = torch.empty(shape_in, dtype=torch.float32, device=g.device)
+        _keep(stream, out)
     gs = tuple(g.shape)
     _check(lib().zk_mean_bwd(_ptr(g), len(gs), _i64(gs), len(shape_in), _i64(shape_in),
                              _ptr(out), _stream(stream)), "zk_mean_bwd")
@@ -442,8 +474,10 @@ def _norm_call(tensors, clip, max_norm, norm_out, workspace, stream):
     dev = tensors[0].device if tensors else torch.device("cuda")
     if norm_out is None:
         norm_out = torch.empty((), dtype=torch.float32, device=dev)
+        _keep(stream, norm_out)
     if workspace is None:
         workspace = _workspace(norm_workspace_bytes([t.numel() for t in tensors]), dev)
+        _keep(stream, workspace)
     ptrs, ns = _grad_list(tensors)
     nbytes = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     L = lib()
@@ -482,8 +516,12 @@ def row_moments(x, mean=None, var=None, stream=None):
     """Per-row mean and biased variance of a 2-D tensor with contiguous rows."""
     import torch
     rows, cols, ld = _row_view(x)
-    mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
-    var = torch.empty(rows, dtype=torch.float32, device=x.device) if var is None else var
+    if mean is None:
+        mean = torch.empty(rows, dtype=torch.float32, device=x.device)
+        _keep(stream, mean)
+    if var is None:
+        var = torch.empty(rows, dtype=torch.float32, device=x.device)
+        _keep(stream, var)
     _check(lib().zk_row_moments(_ptr(x), rows, cols, ld, _ptr(mean), _ptr(var),
                                 _stream(stream)), "zk_row_moments")
     return mean, var
@@ -495,8 +533,10 @@ def row_softmax_stats(x, rowmax=None, sumexp=None, stream=None):
     rows, cols, ld = _row_view(x)
     if rowmax is None:
         rowmax = torch.empty(rows, dtype=torch.float32, device=x.device)
+        _keep(stream, rowmax)
     if sumexp is None:
         sumexp = torch.empty(rows, dtype=torch.float32, device=x.device)
+        _keep(stream, sumexp)
     _check(lib().zk_row_softmax_stats(_ptr(x), rows, cols, ld, _ptr(rowmax), _ptr(sumexp),
                                       _stream(stream)), "zk_row_softmax_stats")
     return rowmax, sumexp

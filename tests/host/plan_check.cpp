@@ -145,24 +145,44 @@ int main() {
     for (int i = 0; i < p.nred; ++i) {
       const RedPlan &rp = p.red[i];
       if (rp.kernel >= 0 && rp.kernel < K_COUNT) ++seen[rp.kernel];
-      need += (size_t)rp.partials * (size_t)rp.kept * 8u;
+      need += (size_t)rp.partials * (size_t)rp.kept * (size_t)rp.csub * 8u;
+      if (rp.csub != 1 && rp.kernel != K_RED_COL) return fail("csub", rp.csub, rp.kernel);
+      // a stage-1 class that leaves partials covers every term with >= 1 of them
+      if (rp.red > 0 && (rp.kernel == K_RED_COL || rp.kernel == K_RED_ROW ||
+                         rp.kernel == K_RED_TILE || rp.kernel == K_RED_GENERIC) &&
+          (rp.partials < 1 || rp.chunk < 1))
+        return fail("no partials", rp.partials, rp.chunk);
       const int64_t inner = c.rank > 0 ? c.n[c.rank - 1] : 1;
       switch (rp.kernel) {
         case K_RED_COL: {
-          if (c.rank != 2 || rp.kept != c.n[1] || rp.red != c.n[0]) return fail("col shape", rp.kept, c.rank);
-          if (c.n[1] % 4 != 0) return fail("col K%4", c.n[1], 0);
+          // [rows, cols] column sums: the canonical [R, K], or [R1, K * C] for
+          // [R1, K, C] -> [K, 1] (each kept element owns C columns)
+          if (rp.csub == 1) {
+            if (c.rank != 2 || rp.kept != c.n[1] || rp.red != c.n[0] ||
+                rp.col_rows != c.n[0] || rp.col_cols != c.n[1])
+              return fail("col shape", rp.kept, c.rank);
+          } else {
+            if (c.rank != 3 || rp.csub != c.n[2] || rp.kept != c.n[1] ||
+                rp.col_rows != c.n[0] || rp.col_cols != c.n[1] * c.n[2] ||
+                rp.red != c.n[0] * c.n[2])
+              return fail("col sub shape", rp.csub, c.rank);
+            if (rp.partials * rp.csub >= ((int64_t)1 << 31)) return fail("col sub index", rp.partials, rp.csub);
+          }
+          const int64_t rows = rp.col_rows, cols = rp.col_cols;
+          if (cols % 4 != 0) return fail("col K%4", cols, 0);
           if (!(rp.nw == 1 || rp.nw == 4 || rp.nw == 16)) return fail("col nw", rp.nw, 0);
           if (rp.chunk < 1) return fail("col rcw", rp.chunk, 0);
           // narrow columns fold rows into 256-wide ones: fold * K == 256
           const int64_t f = rp.fold;
-          if (f < 1 || (f > 1 && (c.n[1] * f != 256 || c.n[0] % f != 0)))
-            return fail("col fold", f, c.n[1]);
-          const int64_t R0 = c.n[0] / f, Kw = c.n[1] * f;
+          if (f < 1 || (f > 1 && (cols * f != 256 || rows % f != 0)))
+            return fail("col fold", f, cols);
+          const int64_t R0 = rows / f, Kw = cols * f;
           const int64_t P = (R0 + rp.nw * rp.chunk - 1) / (rp.nw * rp.chunk);
-          if (rp.partials != P * f) return fail("col partials", rp.partials, P * f);
+          if (P < 1 || rp.partials != P * f) return fail("col partials", rp.partials, P * f);
           // short columns: the one band of rows is split evenly over the waves
           if (P == 1 && rp.nw * rp.chunk > R0 + rp.nw - 1) return fail("col idle waves", rp.nw, rp.chunk);
-          if (((Kw + 255) / 256) * P > kMaxGridBlocks) return fail("col grid", P, 0);
+          // the grid stays within the dispatch limit unless one band is left
+          if (P > 1 && ((Kw + 255) / 256) * P > kMaxGridBlocks) return fail("col grid", P, 0);
           break;
         }
         case K_RED_ROW: {
@@ -194,6 +214,9 @@ int main() {
           if (c.rank == 2 ? (rp.partials != 0 || rp.red != C)
                           : (c.rank != 3 || rp.partials != c.n[0] || rp.kept != c.n[1]))
             return fail("rowseg partials", rp.partials, c.rank);
+          // rank 3: at most C (<= 256) row sums a kept element as partials
+          if (rp.partials > C || rp.partials > kRowSegMaxPartials)
+            return fail("rowseg partial bound", rp.partials, C);
           break;
         }
         case K_RED_GEND: {
@@ -274,6 +297,49 @@ int main() {
       default:
         return fail("fwd kernel", f.kernel, 0);
     }
+  }
+  // 5. shapes far beyond the random range: more than 2^30 kept columns, and
+  //    middle sums over many rows of short rows, plan in bounded time with
+  //    at least one partial, within the kernels' index limits
+  {
+    const int64_t big = (int64_t)1 << 31;
+    zk_desc din{}, dk{};
+    din.rank = 2;
+    din.sizes[0] = 2;
+    din.sizes[1] = big;
+    din.strides[0] = big;
+    din.strides[1] = 1;
+    const int64_t tgt[1] = {big};
+    BwdPlan p;
+    if (plan_reduce(din, 1, tgt, 0, 0, &p) != ZK_OK) return fail("huge reduce", 0, 0);
+    if (p.nred != 1 || p.red[0].kernel != K_RED_COL || p.red[0].partials < 1 ||
+        p.red[0].chunk < 1 || p.red[0].kept != big)
+      return fail("huge reduce plan", p.red[0].kernel, p.red[0].partials);
+    dk.rank = 1;
+    dk.sizes[0] = big;
+    dk.strides[0] = 1;
+    BwdPlan q;
+    if (plan_bwd(ZK_MUL, ZK_EPI_NONE, din, dk, true, true, 0, 0, 0, 0, 0, 0, 0, &q) != ZK_OK)
+      return fail("huge bwd", 0, 0);
+    if (q.nred != 1 || q.red[0].kernel != K_RED_COL || q.red[0].partials < 1 ||
+        q.red[0].chunk < 1 || !q.fused_big)
+      return fail("huge bwd plan", q.red[0].kernel, q.red[0].partials);
+    // [2^22, 4, 4] -> [4, 1]: column sums of [2^22, 16] with bounded partials
+    zk_desc m{};
+    m.rank = 3;
+    m.sizes[0] = (int64_t)1 << 22;
+    m.sizes[1] = 4;
+    m.sizes[2] = 4;
+    m.strides[0] = 16;
+    m.strides[1] = 4;
+    m.strides[2] = 1;
+    const int64_t t2[2] = {4, 1};
+    BwdPlan r;
+    if (plan_reduce(m, 2, t2, 0, 0, &r) != ZK_OK) return fail("middle", 0, 0);
+    const RedPlan &rr = r.red[0];
+    if (rr.kernel != K_RED_COL || rr.csub != 4 || rr.partials > 65536 ||
+        r.workspace > ((size_t)64 << 20) / 16)
+      return fail("middle plan", rr.kernel, (long long)r.workspace);
   }
   std::printf("OK\n");
   return 0;

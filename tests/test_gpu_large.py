@@ -79,3 +79,24 @@ def test_backward_and_reductions_past_2_31(orc):
     assert np.all(host(zk.reduce_to_shape(g, (C,))) == np.float32(0.5 * R))
     assert float(host(zk.reduce_to_shape(g.view(-1), ()))) == 0.5 * N
     assert float(host(zk.mean_to_shape(g.view(-1), ()))) == 0.5
+
+
+def test_column_sums_beyond_the_grid_limit():
+    """[2, 2^30 + 1024] summed to its columns: 2^22 + 4 column groups of 256,
+    more than one launch may hold, so red_col walks its blocks with a grid
+    stride.  Column j holds (j mod 4096, 1), so a skipped or misplaced block
+    shows; the sums and the multiply backward's are exact in binary32."""
+    K = (1 << 30) + 1024
+    info = zk.plan_describe("reduce", "add", zk.make_desc((2, K)), zk.make_desc((K,)))
+    assert info["kernel"] == "red_col" and info["partials"] == 1, info
+    col = (torch.arange(K, device="cuda", dtype=torch.int32) % 4096).to(torch.float32)
+    x = torch.stack([col, torch.ones_like(col)])
+    out = torch.full((K,), float("nan"), device="cuda")
+    zk.reduce_to_shape(x, (K,), out=out)
+    assert torch.equal(out, col + 1.0)
+    del out
+    g = torch.full((2, K), 0.5, device="cuda")
+    b = torch.full((K,), 2.0, device="cuda")
+    ga, gb = zk.binary_bwd("mul", g, x, b)
+    assert torch.equal(gb, 0.5 * col + 0.5)     # sum_r g * x[r, j]
+    assert bool((ga == 1.0).all())               # g * b

@@ -466,6 +466,42 @@ def test_determinism_concurrent_streams(orc, case):
     assert_bwd(ref[1], rb, "grad_b")
 
 
+def test_side_stream_allocations_outlive_their_kernels(orc, monkeypatch):
+    """A backward on a side stream with the workspace and gradients left to
+    the binding: those come from torch's allocator on the current stream, so
+    the binding records their use on the side stream.  While that stream is
+    still busy (a spin ahead of the call), a fresh allocation of the same size
+    on the current stream must not get the workspace block back; a write
+    there before synchronising leaves the result intact."""
+    rng = np.random.default_rng(77)
+    a_np = rng.standard_normal((1024, 1024)).astype(np.float32)
+    b_np = rng.standard_normal(1024).astype(np.float32)
+    g_np = rng.standard_normal((1024, 1024)).astype(np.float32)
+    a, b, g = dev(a_np), dev(b_np), dev(g_np)
+    seen = []
+    real = zk._workspace
+
+    def spy(nbytes, device):
+        t = real(nbytes, device)
+        seen.append((t.data_ptr(), t.numel()))
+        return t
+
+    monkeypatch.setattr(zk, "_workspace", spy)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(int(2e8))     # keeps the side stream busy
+    ga, gb = zk.binary_bwd("mul", g, a, b, stream=side)
+    (wp, wn), = seen
+    junk = torch.empty(wn, dtype=torch.uint8, device="cuda")
+    assert junk.data_ptr() != wp, "workspace block reused while its kernels are queued"
+    junk.fill_(0xFF)                    # NaN patterns, on the current stream
+    torch.cuda.synchronize()
+    ra, rb = orc.bwd("mul", g_np, a_np, b_np)
+    assert_bwd(host(ga), ra, "grad_a")
+    assert_bwd(host(gb), rb, "grad_b")
+
+
 def test_mass_invariant_gpu():
     rng = np.random.default_rng(71)
     g = rng.standard_normal((64, 130, 64)).astype(np.float32)
@@ -568,10 +604,15 @@ def test_short_rows(orc, rows, cols):
 
 
 @pytest.mark.parametrize("shape", [(3, 5, 8), (64, 1000, 4), (7, 33, 32), (256, 512, 128),
-                                   (2, 4096, 64), (100, 30, 256), (8, 64, 256)])
+                                   (2, 4096, 64), (100, 30, 256), (8, 64, 256),
+                                   (65536, 4, 4), (1000, 16, 16), (300, 100, 12),
+                                   (4096, 3, 4), (513, 7, 12), (2049, 64, 256), (5, 300, 4)])
 def test_short_rows_middle(orc, shape):
-    """[R1, K, C] -> [K, 1] with short rows: the row sums are binary64
-    partials of stage 2 (sums and means)."""
+    """[R1, K, C] -> [K, 1] with short rows: with R1 <= C the row sums are
+    binary64 partials of stage 2; with more rows the dense [R1, K * C] is
+    summed by columns (folded below 256 columns) and stage 2 adds each kept
+    element's C columns; other narrow shapes take the gather path (sums and
+    means)."""
     rng = np.random.default_rng(zlib.crc32(repr(shape).encode()))
     x = rng.standard_normal(shape).astype(np.float32)
     t = dev(x)

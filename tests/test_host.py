@@ -399,10 +399,14 @@ def test_workload_canonical_forms(L, case):
     # short rows: 256 / C rows a wave
     ((1048576, 128), (1048576, 1), "red_rowseg", 0, None),
     ((16777216, 8), (16777216, 1), "red_rowseg", 0, None),
-    ((256, 4096, 128), (4096, 1), "red_rowseg", 256, 256 * 4096 * 8),
+    # middle sums over more rows than the row length: column sums of
+    # [R1, K * C], stage 2 adding each kept element's C columns
+    ((256, 4096, 128), (4096, 1), "red_col", 1, 4096 * 128 * 8),
+    ((1 << 22, 4, 4), (4, 1), "red_col", 2048 * 16, 2048 * 16 * 16 * 8),
+    ((2, 4096, 128), (4096, 1), "red_rowseg", 2, 2 * 4096 * 8),  # R1 <= C: row sums
     ((10, 12), (10, 1), "red_generic", None, None),      # 12 does not divide 256
     ((524288, 256), (524288, 1), "red_rowseg", 0, None),
-    ((2048, 256, 256), (256, 1), "red_rowseg", 2048, None),
+    ((2048, 256, 256), (256, 1), "red_col", 2, 2 * 65536 * 8),
     ((8, 64, 256), (64, 1), "red_rowd", 0, None),        # within red_rowd's one pass
     ((16, 1000, 128), (1000, 1), "red_rowseg", 16, None),  # rows too short for red_rowd
 ])
@@ -414,6 +418,22 @@ def test_reduce_plan_shapes(L, shape, target, kernel, partials, ws):
         assert info["partials"] == partials
     if ws is not None:
         assert info["workspace_bytes"] == ws
+
+
+def test_plans_beyond_the_grid_limit(L):
+    """More than 2^30 kept columns (the column groups alone exceed the grid
+    limit): planned with one band of rows and at least one partial, for the
+    reduction and the multiply backward (host only, nothing allocated)."""
+    big = 1 << 31
+    info = zk.plan_describe("reduce", "add", zk.make_desc((2, big)), zk.make_desc((big,)))
+    assert info["kernel"] == "red_col" and info["partials"] == 1
+    assert info["workspace_bytes"] == big * 8
+    info = zk.plan_describe("bwd", "mul", zk.make_desc((2, big)), zk.make_desc((big,)))
+    assert info["kernel"] == "red_col" and info["partials"] == 1
+    # [2^22, 4, 4] -> [4, 1]: bounded partials (was 2^22 row sums a kept element)
+    info = zk.plan_describe("reduce", "add", zk.make_desc((1 << 22, 4, 4)),
+                            zk.make_desc((4, 1)))
+    assert info["partials"] <= 65536 and info["workspace_bytes"] <= (64 << 20) // 16
 
 
 def test_reduce_plans(L):
