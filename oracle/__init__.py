@@ -42,7 +42,7 @@ def build(force=True):
     tmp = LIB_PATH + ".tmp"
     cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
            "-msse2", "-mfpmath=sse", "-fopenmp", "-fPIC", "-shared",
-           "-D_GNU_SOURCE", SRC_PATH, "-o", tmp, "-lm"]
+           "-D_GNU_SOURCE", SRC_PATH, "-o", tmp, "-lquadmath", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
@@ -92,6 +92,11 @@ def lib():
         L.or_relu32.restype = ctypes.c_float
         L.or_gelu32.argtypes = [ctypes.c_float]
         L.or_gelu32.restype = ctypes.c_float
+        L.or_gelu32_q.argtypes = [ctypes.c_float]
+        L.or_gelu32_q.restype = ctypes.c_float
+        L.or_gelu_tie_scan.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_double,
+                                       P, I64]
+        L.or_gelu_tie_scan.restype = I64
         L.or_phi_cdf.argtypes = [ctypes.c_double]
         L.or_phi_cdf.restype = ctypes.c_double
         L.or_phi_pdf.argtypes = [ctypes.c_double]
@@ -474,6 +479,22 @@ def relu32(h):
 
 def gelu32(h):
     return np.float32(lib().or_gelu32(float(h)))
+
+
+def gelu32_q(h):
+    """GeLU through the binary128 evaluation alone (the path the oracle takes
+    where binary64 cannot decide the rounding)."""
+    return np.float32(lib().or_gelu32_q(float(h)))
+
+
+def gelu_tie_scan(lo_bits, hi_bits, rel, max_out=1 << 20):
+    """Binary32 arguments (as uint32 bit patterns, bit patterns lo <= u < hi of
+    one sign) whose binary64 GeLU lies within ``rel`` of a binary32 rounding
+    midpoint; returns (patterns found, up to max_out; total count)."""
+    out = np.empty(int(max_out), dtype=np.uint32)
+    n = lib().or_gelu_tie_scan(int(lo_bits), int(hi_bits), float(rel), out.ctypes.data,
+                               int(max_out))
+    return np.sort(out[:min(n, max_out)]), int(n)
 
 
 def phi_cdf(h):

@@ -29,8 +29,11 @@
  * Precision (the pages fix none):
  *   forward  : one IEEE binary32 operation per element, round-to-nearest-even
  *              (built with -ffp-contract=off, SSE, no fast-math)
- *   GeLU     : exact function h*Phi(h), Phi(h) = erfc(-h/sqrt2)/2, evaluated in
- *              binary64 with libm erfc and rounded once to binary32
+ *   GeLU     : exact function h*Phi(h), Phi(h) = erfc(-h/sqrt2)/2, correctly
+ *              rounded to binary32: evaluated in binary64 with libm erfc, and
+ *              again in binary128 (libquadmath) where the binary64 value cannot
+ *              decide the rounding (near a binary32 midpoint, or a result
+ *              below 2^-125)
  *   ReLU     : h for h > 0, NaN for NaN, +0 otherwise; derivative 1 for h > 0,
  *              else 0 (the pages name the activation without a formula)
  *   backward : every term in binary64 from the exact binary32 inputs, summed in
@@ -48,6 +51,7 @@
  * over OUTPUT elements, so results do not depend on the thread count.
  */
 #include <math.h>
+#include <quadmath.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -155,12 +159,90 @@ static float op32(int op, float x, float y) {
 double or_phi_cdf(double h) { return 0.5 * erfc(-h * M_SQRT1_2); }
 double or_phi_pdf(double h) { return exp(-0.5 * h * h) / sqrt(2.0 * M_PI); }
 
-/* GeLU(h) = h * Phi(h), evaluated in binary64, rounded once to binary32.
- * The limits at +-inf are +inf and -0. */
+/* GeLU in binary128 (113-bit significand; libquadmath erfq / erfcq, a few
+ * units of 2^-113 relative), rounded once to binary32:
+ *   h >= -1 : y = h/2 + d, d = (h/2) erf(h/sqrt2) > 0 for h != 0, since
+ *             Phi(h) = (1 + erf(h/sqrt2)) / 2;
+ *   h <  -1 : y = (h/2) erfc(|h|/sqrt2), Phi(h) = erfc(-h/sqrt2) / 2 (the
+ *             sum would cancel there).
+ * In the sum, h/2 is exact and the binary128 addition's own rounding error
+ * e is recovered exactly (two-sum), so y = s + e.  When s is exactly a
+ * binary32 midpoint -- as for h an odd multiple of 2^-149, where h/2 is the
+ * midpoint and d lies far below the last bit of s -- the sign of e decides
+ * the rounding; any other s rounds like y does. */
+static float gelu32_q(float h) {
+  const __float128 H = (__float128)h;
+  const __float128 half = H * 0.5Q;
+  __float128 s, e = 0;
+  if (h >= -1.0f) {
+    const __float128 d = half * erfq(H * M_SQRT1_2q);
+    s = half + d;
+    const __float128 dd = s - half;          /* two-sum (Knuth), exact */
+    e = (half - (s - dd)) + (d - dd);
+  } else {
+    s = half * erfcq(-H * M_SQRT1_2q);
+  }
+  float r = (float)s;                        /* correctly rounded from s */
+  if (e == 0 || (__float128)r == s) return r;
+  const float r2 = nextafterf(r, s > (__float128)r ? INFINITY : -INFINITY);
+  const __float128 mid = ((__float128)r + (__float128)r2) * 0.5Q;  /* exact */
+  if (s != mid) return r;
+  return (e > 0) == (r2 > r) ? r2 : r;       /* the neighbour on e's side */
+}
+
+/* y lies within rel * |y| of the midpoint between its binary32 neighbours. */
+static int near_midpoint32(double y, double rel) {
+  const float f = (float)y;
+  if ((double)f == y) return 0;
+  const double other = (double)nextafterf(f, y > (double)f ? INFINITY : -INFINITY);
+  const double mid = 0.5 * ((double)f + other);  /* exact in binary64 */
+  return fabs(y - mid) <= rel * fabs(y);
+}
+
+/* GeLU(h) = h * Phi(h) rounded once to binary32.  The binary64 evaluation
+ * (libm erfc, relative error far below 1e-12) decides the rounding unless y
+ * lies within 1e-12 of a binary32 midpoint or below 2^-125 (where h/2 itself
+ * can be a midpoint); those go to the binary128 evaluation.  The limits at
+ * +-inf are +inf and -0; GeLU(+-0) = +-0. */
 float or_gelu32(float h) {
+  if (isnan(h)) return h;
   if (isinf(h)) return h > 0 ? h : -0.0f;
-  double hd = (double)h;
-  return (float)(hd * or_phi_cdf(hd));
+  if (h == 0.0f) return h * 0.5f;
+  const double hd = (double)h;
+  const double y = hd * or_phi_cdf(hd);
+  if (fabs(y) >= 0x1p-125 && !near_midpoint32(y, 1e-12)) return (float)y;
+  return gelu32_q(h);
+}
+
+/* The binary128 evaluation alone (for the tests that pin it). */
+float or_gelu32_q(float h) {
+  if (isnan(h)) return h;
+  if (isinf(h)) return h > 0 ? h : -0.0f;
+  if (h == 0.0f) return h * 0.5f;
+  return gelu32_q(h);
+}
+
+/* Binary32 arguments whose binary64 GeLU lies within rel of a binary32
+ * midpoint: scans the bit patterns [lo, hi) of one sign (lo < hi, both in
+ * the same sign half) and writes up to max of them to out, returning how
+ * many were found (which may exceed max). */
+int64_t or_gelu_tie_scan(uint32_t lo, uint32_t hi, double rel, uint32_t *out, int64_t max) {
+  int64_t found = 0;
+#pragma omp parallel for schedule(dynamic, 65536) num_threads(g_threads)
+  for (int64_t u = lo; u < (int64_t)hi; ++u) {
+    const uint32_t bits = (uint32_t)u;
+    float h;
+    memcpy(&h, &bits, 4);
+    if (!isfinite(h) || h == 0.0f) continue;
+    const double hd = (double)h;
+    const double y = hd * or_phi_cdf(hd);
+    if (fabs(y) < 0x1p-125 || !near_midpoint32(y, rel)) continue;
+    int64_t k;
+#pragma omp atomic capture
+    k = found++;
+    if (k < max) out[k] = bits;
+  }
+  return found;
 }
 
 /* ReLU(h): h for h > 0, NaN stays NaN, +0 otherwise. */
