@@ -16,7 +16,7 @@ Each piece is a least-squares fit on a dense grid weighted for relative error
 (near-minimax), computed in binary64 from scipy's erfcx times exp (erfc with
 full relative accuracy), converted from the Chebyshev to the monomial basis
 in d.  Beyond TAB_AMAX (|h| > 6.36) GeLU(h) rounds to h for h > 0, and the
-kernel evaluates negative h there with the device libm.
+kernel evaluates negative h there with its double-double path.
 
 Backward (binary32, tolerance 2e-6): erfcx(u)*(u + K) as a polynomial in s,
 an affine image onto [-1, 1] of t = (u - K)/(u + K), u = |h|/sqrt2 in

@@ -7,7 +7,9 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -140,6 +142,54 @@ size_t reduce_workspace(const zk_desc &din, int rout, const int64_t *nout) {
   return m;
 }
 
+// ------------------------------------------------ debug pointer checks
+// -1: not decided yet (ZK_DEBUG is read at the first consultation).
+std::atomic<int32_t> g_debug{-1};
+
+int32_t debug_mode() {
+  int32_t d = g_debug.load(std::memory_order_relaxed);
+  if (d < 0) {
+    const char *e = std::getenv("ZK_DEBUG");
+    int32_t want = (e && std::strcmp(e, "1") == 0) ? 1 : 0, expect = -1;
+    g_debug.compare_exchange_strong(expect, want, std::memory_order_relaxed);
+    d = g_debug.load(std::memory_order_relaxed);
+  }
+  return d;
+}
+
+// With debug checks on: ZK_OK only when every non-NULL pointer is device
+// memory of the stream's device (or managed memory); no launch otherwise.
+zk_status debug_check_list(void *stream, const void *const *ptrs, size_t n) {
+  if (debug_mode() != 1) return ZK_OK;
+  int dev = -1;
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // leave no error for the caller's next call
+    return ZK_ERR_DEVICE;
+  }
+  std::vector<PtrRecord> recs;
+  recs.reserve(n);
+  for (size_t i = 0; i < n; ++i) {
+    if (!ptrs[i]) continue;
+    hipPointerAttribute_t a{};
+    PtrRecord r{0, kMemUnregistered, -1};
+    if (hipPointerGetAttributes(&a, ptrs[i]) == hipSuccess) {
+      r.known = 1;
+      r.mem_type = a.isManaged ? kMemManaged : (int32_t)a.type;
+      r.device = a.device;
+    } else {
+      (void)hipGetLastError();
+    }
+    recs.push_back(r);
+  }
+  return check_ptr_records(recs.data(), (int)recs.size(), dev);
+}
+
+zk_status debug_check(void *stream, std::initializer_list<const void *> ptrs) {
+  return debug_check_list(stream, ptrs.begin(), ptrs.size());
+}
+
 // ------------------------------------------------ optional kernel timing
 struct Profiler {
   std::mutex mu;
@@ -226,15 +276,22 @@ const char *zk_status_string(zk_status s) {
     case ZK_ERR_BAD_STRIDE: return "negative stride";
     case ZK_ERR_BROADCAST: return "shapes do not broadcast";
     case ZK_ERR_ALIAS: return "an output overlaps an input or another output";
-    case ZK_ERR_WORKSPACE: return "workspace too small";
+    case ZK_ERR_WORKSPACE: return "workspace too small or not 8-byte aligned";
     case ZK_ERR_UNSUPPORTED: return "unsupported op or epilogue";
     case ZK_ERR_HIP: return "HIP launch failed";
     case ZK_ERR_SHAPE: return "target shape does not broadcast to the input";
+    case ZK_ERR_DEVICE: return "a pointer is not device memory of the stream's device";
   }
   return "unknown status";
 }
 
 const char *zk_kernel_name(int32_t k) { return kernel_name(k); }
+
+int32_t zk_set_debug(int32_t mode) {
+  const int32_t before = debug_mode();
+  if (mode == 0 || mode == 1) g_debug.store(mode, std::memory_order_relaxed);
+  return before;
+}
 
 zk_status zk_broadcast_shape(int32_t rank_a, const int64_t *sizes_a,
                              int32_t rank_b, const int64_t *sizes_b,
@@ -265,14 +322,20 @@ zk_status zk_binary_fwd(zk_op op, zk_epi epi, const float *a, const zk_desc *da,
   Ext eo = ext_dense(out, n), ea = ext_of(a, *da), eb = ext_of(b, *db);
   if (ov(eo, ea) && !(out == a && dense_full(*da, n))) return ZK_ERR_ALIAS;
   if (ov(eo, eb) && !(out == b && dense_full(*db, n))) return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {a, b, out}))) return s;
   return hip_status(launch_fwd(p, op, epi, a, b, out, (hipStream_t)stream));
 }
 
-zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad, const float *a,
-                        const zk_desc *da, const float *b, const zk_desc *db,
-                        float *grad_a, const float *acc_a, float *grad_b,
-                        const float *acc_b, void *workspace,
-                        size_t *workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// zk_binary_bwd; lib_ws: the workspace is memory the library owns (left out
+// of the debug pointer check, which asks about caller memory).
+zk_status binary_bwd_impl(zk_op op, zk_epi epi, const float *grad, const float *a,
+                          const zk_desc *da, const float *b, const zk_desc *db,
+                          float *grad_a, const float *acc_a, float *grad_b,
+                          const float *acc_b, void *workspace, size_t *workspace_bytes,
+                          void *stream, bool lib_ws) {
   if (!valid_op(op) || !valid_epi(epi)) return ZK_ERR_UNSUPPORTED;
   if (!workspace_bytes) return ZK_ERR_NULL;
   zk_status s;
@@ -314,8 +377,23 @@ zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad, const float *a,
   if (need && (ov(ews, eg) || ov(ews, ea) || ov(ews, eb) || ov(ews, exa) ||
                       ov(ews, exb)))
     return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {grad, a, b, grad_a, acc_a, grad_b, acc_b,
+                                need && !lib_ws ? workspace : nullptr})))
+    return s;
   return hip_status(launch_bwd(p, op, epi, grad, a, b, grad_a, acc_a, grad_b,
                                acc_b, workspace, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+
+zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad, const float *a,
+                        const zk_desc *da, const float *b, const zk_desc *db,
+                        float *grad_a, const float *acc_a, float *grad_b,
+                        const float *acc_b, void *workspace,
+                        size_t *workspace_bytes, void *stream) {
+  return binary_bwd_impl(op, epi, grad, a, da, b, db, grad_a, acc_a, grad_b, acc_b, workspace,
+                         workspace_bytes, stream, false);
 }
 
 }  // extern "C"
@@ -359,6 +437,9 @@ zk_status reduce_common(const float *in, const zk_desc *din, int32_t rank_out,
   Ext ews;
   if (need) ews = Ext{(uintptr_t)workspace, (uintptr_t)workspace + need};
   if (ov(eo, ei) || ov(eo, ews) || ov(ews, ei)) return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {p.c.numel > 0 ? in : nullptr, nout > 0 ? out : nullptr,
+                                need ? workspace : nullptr})))
+    return s;
   const double count =
       mean ? (double)reduced_count(din->rank, din->sizes, rank_out, sizes_out) : -1.0;
   return hip_status(launch_reduce(p, in, out, workspace, (hipStream_t)stream, nullptr, false,
@@ -416,6 +497,12 @@ zk_status norm_common(int32_t count, float *const *grads, const int64_t *numels,
     if (numels[t] == 0) continue;
     const Ext e = ext_dense(grads[t], numels[t]);
     if (ov(e, ew) || ov(e, en)) return ZK_ERR_ALIAS;
+  }
+  if (debug_mode() == 1) {
+    std::vector<const void *> ptrs{norm_out, need ? workspace : nullptr};
+    for (int t = 0; t < count; ++t)
+      if (numels[t] > 0) ptrs.push_back(grads[t]);
+    if ((s = debug_check_list(stream, ptrs.data(), ptrs.size()))) return s;
   }
   return hip_status(launch_grad_norm(count, grads, numels, norm_out, workspace, clip,
                                      (double)max_norm, (hipStream_t)stream));
@@ -504,6 +591,7 @@ zk_status row_stats_common(int mode, const float *x, int64_t rows, int64_t cols,
   Ext ex;
   if (cols > 0) ex = ext_dense(x, (rows - 1) * ld + cols);
   if (ov(e1, e2) || ov(e1, ex) || ov(e2, ex)) return ZK_ERR_ALIAS;
+  if (zk_status s = debug_check(stream, {cols > 0 ? x : nullptr, o1, o2})) return s;
   return hip_status(launch_row_stats(mode, x, rows, cols, ld, o1, o2, (hipStream_t)stream));
 }
 }  // namespace
@@ -541,6 +629,7 @@ zk_status zk_scalar_fwd(zk_op op, zk_epi epi, const float *t, const zk_desc *dt,
   const int64_t n = p.c.numel;
   if (ov(ext_dense(out, n), ext_of(t, *dt)) && !(out == t && dense_full(*dt, n)))
     return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {t, out}))) return s;
   const ScalarArg sa{sf ? 0 : 1, sv};
   return hip_status(launch_fwd(p, op, epi, pa, pb, out, (hipStream_t)stream, &sa));
 }
@@ -576,6 +665,7 @@ zk_status zk_scalar_bwd(zk_op op, zk_epi epi, const float *grad, const float *t,
   Ext ex = ext_dense(acc_t, n);
   if (ov(eo, eg) || ov(eo, et)) return ZK_ERR_ALIAS;
   if (ov(eo, ex) && acc_t != grad_t) return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {grad, t, grad_t, acc_t}))) return s;
   const ScalarArg sa{sf ? 0 : 1, sv};
   return hip_status(launch_bwd(p, op, epi, grad, pa, pb, ga, xa, gb, xb, nullptr,
                                (hipStream_t)stream, nullptr, nullptr, 1.f, &sa));
@@ -606,6 +696,7 @@ zk_status zk_materialize(const float *in, const zk_desc *din, int32_t rank_out,
   if (p.empty) return ZK_OK;
   if (!in || !out) return ZK_ERR_NULL;
   if (ov(ext_dense(out, p.c.numel), ext_of(in, *din))) return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {in, out}))) return s;
   return hip_status(launch_copy(p, in, out, (hipStream_t)stream));
 }
 
@@ -628,6 +719,7 @@ zk_status zk_binary2_fwd(zk_op op1, zk_op op2, const float *a, const zk_desc *da
   for (int x = 0; x < 3; ++x)
     if (ov(eo, ext_of(in[x], *din[x])) && !(out == in[x] && dense_full(*din[x], n)))
       return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {a, b, c, out}))) return s;
   return hip_status(launch_fwd2(p, op1, op2, a, b, c, out, (hipStream_t)stream));
 }
 
@@ -712,6 +804,9 @@ zk_status zk_binary2_bwd(zk_op op1, zk_op op2, const float *grad, const float *a
     for (int w = 0; w < 3; ++w)
       if (ov(ews, eg) || ov(ews, ea) || ov(ews, eb) || ov(ews, ec) || ov(ews, ex[w]))
         return ZK_ERR_ALIAS;
+  if ((s = debug_check(stream, {grad, a, b, c, grad_a, acc_a, grad_b, acc_b, grad_c, acc_c,
+                                need ? workspace : nullptr})))
+    return s;
   const hipStream_t st = (hipStream_t)stream;
   const float sign = op2 == ZK_SUB ? -1.f : 1.f;
   hipError_t e = hipSuccess;

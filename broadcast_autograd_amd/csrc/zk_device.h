@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "zk_gelu_coeffs.h"
+#include "zk_gelu_exact.h"
 #include "zk_kernels.h"
 
 namespace zk {
@@ -21,24 +22,11 @@ __device__ __forceinline__ float op32(float x, float y) {
   else return x / y;
 }
 
-// Standard normal CDF in binary64 through the device libm erfc (accurate to
-// a few binary64 ulps); the reference path of the forward GeLU.
-__device__ __forceinline__ double phi_cdf(double h) {
-  return 0.5 * erfc(-h * 0.70710678118654752440);
-}
-
-// GeLU through phi_cdf (the path taken near rounding ties, for results
-// below 2^-126 and for arguments outside the table).  Limits: +inf -> +inf,
-// -inf -> -0 (the product inf * 0 would be NaN), NaN -> NaN.
-__device__ __forceinline__ float gelu32_libm_inl(float h) {
-  if (__builtin_isinf(h)) return h > 0.f ? h : -0.0f;
-  const double hd = (double)h;
-  return (float)(hd * phi_cdf(hd));
-}
-// Out-of-line copy for kernels that would otherwise inline it many times.
-__device__ __attribute__((noinline)) float gelu32_libm(float h) {
-  return gelu32_libm_inl(h);
-}
+// GeLU correctly rounded through the double-double evaluation of
+// zk_gelu_exact.h: the path taken near binary32 rounding midpoints, for
+// results below 2^-126 and for arguments outside the table.  Out of line, so
+// that the many kernels reaching it share one copy.
+__device__ __attribute__((noinline)) float gelu32_slow(float h) { return gelu32_exact(h); }
 
 // ------------------------------------------------------------- GeLU fwd
 // GeLU(h) = h Phi(h) = max(h, 0) - |h E(|h|)|/2 with E(a) = erfc(a/sqrt2)
@@ -61,11 +49,11 @@ __device__ __forceinline__ void gelu_tab_load(double *lds) {
 // is rounded when it lies farther than 2^-40 (relative, 2^6 times the error
 // bound) from the midpoint between its two binary32 neighbours, which makes
 // the result the correctly rounded exact value; otherwise bit k of *redo is
-// set and the caller recomputes element k with gelu32_libm.  Also sent
+// set and the caller recomputes element k with gelu32_slow.  Also sent
 // there: results below 2^-126 (binary32 subnormals or zero, including
 // h = +-0) and negative h beyond the table.  Positive h beyond the table
 // gives y = h exactly (GeLU(h) = h (1 - 1e-10) rounds to h); +inf gives
-// +inf and NaN gives NaN; -inf is sent to the libm path.
+// +inf and NaN gives NaN; -inf is sent to the double-double path.
 template <int W>
 __device__ __forceinline__ void gelu32_fast_w(const double *tab, const float (&h)[W],
                                               float (&f)[W], uint32_t &redo) {
@@ -117,13 +105,13 @@ __device__ __forceinline__ void gelu32_fast_w(const double *tab, const float (&h
   }
 }
 
-// One element, with the rare libm path inline.
+// One element, with the rare double-double path.
 __device__ __forceinline__ float gelu32(const double *tab, float h) {
   const float hv[1] = {h};
   float f[1];
   uint32_t redo;
   gelu32_fast_w<1>(tab, hv, f, redo);
-  return redo ? gelu32_libm(h) : f[0];
+  return redo ? gelu32_slow(h) : f[0];
 }
 
 // Phi(h) and the density phi(h) at a binary32 h for the backward, whose
@@ -208,7 +196,7 @@ __device__ __forceinline__ float fwd32(float x, float y, const double *tab) {
   else return h;
 }
 
-// Four elements of a 128-bit vector: r = epi(x (op) y).  The rare libm redo
+// Four elements of a 128-bit vector: r = epi(x (op) y).  The rare slow-path redo
 // of the GeLU is left to the caller (bit k of *redo), which batches it after
 // its stores and so keeps that code out of the hot loop.
 template <int OP, int EPI>

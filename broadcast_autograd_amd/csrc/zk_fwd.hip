@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kBlock) void k_fwd_flat(const float *a,
           vb[u] = ld4_nt(b + i);
         }
       }
-      uint32_t redo_bits = 0;  // bit 4u+k: element needs the GeLU libm path
+      uint32_t redo_bits = 0;  // bit 4u+k: element needs the GeLU double-double path
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t i = base + (int64_t)u * kBlock * 4;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kBlock) void k_fwd_flat(const float *a,
           const int bit = __builtin_ctz(redo_bits);
           redo_bits &= redo_bits - 1;
           const int64_t j = base + (int64_t)(bit >> 2) * kBlock * 4 + (bit & 3);
-          out[j] = gelu32_libm_inl(op32<OP>(a[j], b[j]));
+          out[j] = gelu32_slow(op32<OP>(a[j], b[j]));
         }
       }
     } else {
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(BLK) __attribute__((amdgpu_waves_per_eu(4))) void k
     };
     auto process = [&](I t, const float4 *vb, const float4 *vs) {
       const I base = t * tile + (I)threadIdx.x * 4;
-      uint32_t redo_bits = 0;  // bit 4u+k: element needs the GeLU libm path
+      uint32_t redo_bits = 0;  // bit 4u+k: element needs the GeLU double-double path
       float4 res[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(BLK) __attribute__((amdgpu_waves_per_eu(4))) void k
           else vsm = small[off + (I)k * sin];
           const float vbig = big[i + k];
           const float h = SWAP ? op32<OP>(vsm, vbig) : op32<OP>(vbig, vsm);
-          out[i + k] = gelu32_libm(h);
+          out[i + k] = gelu32_slow(h);
         }
       }
     };

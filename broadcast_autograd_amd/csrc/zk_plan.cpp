@@ -406,6 +406,17 @@ zk_status plan_copy(const zk_desc &din, int rout, const int64_t *nout, uintptr_t
   return ZK_OK;
 }
 
+// ------------------------------------------------------- debug checks
+zk_status check_ptr_records(const PtrRecord *r, int n, int stream_device) {
+  if (stream_device < 0) return ZK_ERR_DEVICE;
+  for (int i = 0; i < n; ++i) {
+    if (!r[i].known) return ZK_ERR_DEVICE;
+    if (r[i].mem_type == kMemManaged) continue;
+    if (r[i].mem_type != kMemDevice || r[i].device != stream_device) return ZK_ERR_DEVICE;
+  }
+  return ZK_OK;
+}
+
 // ------------------------------------------------------------- backward
 
 // Reduction pattern of operand stride set `o` over the canonical dims:

@@ -173,6 +173,21 @@ zk_status plan_fwd2(const zk_desc &da, const zk_desc &db, const zk_desc &dc,
                     uintptr_t pa, uintptr_t pb, uintptr_t pc, uintptr_t pout,
                     Fwd2Plan *p);
 
+// ------------------------------------------------------ debug checks
+// One pointer as the HIP runtime describes it (hipPointerGetAttributes):
+// known = 0 when the runtime could not describe it; mem_type holds the
+// hipMemoryType value (kMemDevice, kMemManaged, ...), device the owner.
+constexpr int32_t kMemUnregistered = 0, kMemHost = 1, kMemDevice = 2, kMemManaged = 3;
+struct PtrRecord {
+  int32_t known;
+  int32_t mem_type;
+  int32_t device;
+};
+// ZK_OK when the stream's device is known (stream_device >= 0) and every
+// record is managed memory or device memory of stream_device; else
+// ZK_ERR_DEVICE.
+zk_status check_ptr_records(const PtrRecord *r, int n, int stream_device);
+
 // --------------------------------------------------------------- backward
 // One stage-1 reduction for one operand's gradient.
 struct RedPlan {

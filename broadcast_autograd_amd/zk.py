@@ -19,7 +19,7 @@ EPIS = {"none": 0, "gelu": 1, "relu": 2}
 STATUS = {0: "ZK_OK", 1: "ZK_ERR_NULL", 2: "ZK_ERR_RANK", 3: "ZK_ERR_BAD_SIZE",
           4: "ZK_ERR_BAD_STRIDE", 5: "ZK_ERR_BROADCAST", 6: "ZK_ERR_ALIAS",
           7: "ZK_ERR_WORKSPACE", 8: "ZK_ERR_UNSUPPORTED", 9: "ZK_ERR_HIP",
-          10: "ZK_ERR_SHAPE"}
+          10: "ZK_ERR_SHAPE", 11: "ZK_ERR_DEVICE"}
 ERR = {v: k for k, v in STATUS.items()}
 
 # exported symbols declared in include/zk.h
@@ -28,7 +28,7 @@ SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
            "zk_scalar_fwd", "zk_scalar_bwd", "zk_unary_fwd", "zk_unary_bwd",
            "zk_mean_to_shape", "zk_mean_bwd", "zk_grad_norm", "zk_clip_grad_norm",
            "zk_row_moments", "zk_row_softmax_stats",
-           "zk_status_string", "zk_plan_describe", "zk_kernel_name",
+           "zk_status_string", "zk_plan_describe", "zk_kernel_name", "zk_set_debug",
            "zk_profile_start", "zk_profile_stop", "zk_profile_read")
 
 
@@ -100,6 +100,7 @@ def lib():
         L.zk_profile_stop.argtypes = []
         L.zk_profile_read.argtypes = [I32, P, P, P]
         L.zk_kernel_name.argtypes = [I32]
+        L.zk_set_debug.argtypes = [I32]
         L.zk_kernel_name.restype = ctypes.c_char_p
         for name in SYMBOLS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int32
@@ -107,6 +108,12 @@ def lib():
         L.zk_kernel_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def set_debug(mode):
+    """Debug pointer checks: 1 on, 0 off, -1 unchanged; returns the previous
+    mode (ZK_DEBUG=1 in the environment turns them on by default)."""
+    return int(lib().zk_set_debug(int(mode)))
 
 
 def _check(code, what):

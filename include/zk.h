@@ -26,7 +26,13 @@
  *     shape, each gradient in its operand's logical shape.
  *   - Pointers are device pointers on the device that owns `stream` (a
  *     hipStream_t passed as void*; NULL means the default stream).  Host
- *     arrays (sizes, descriptors) are read during the call only.
+ *     arrays (sizes, descriptors) are read during the call only.  Inputs on
+ *     another device lead to an illegal memory access (GPU chapter, "kernel
+ *     dispatch": the devices of a call must match); with the environment
+ *     variable ZK_DEBUG=1 (or zk_set_debug(1)) every call first asks the HIP
+ *     runtime about each pointer it will touch and returns ZK_ERR_DEVICE,
+ *     launching nothing, unless all of them are device (or managed) memory
+ *     of the stream's device.
  *   - The library allocates nothing on the device, keeps no pointer after
  *     it returns and never synchronises: results are ready when the stream
  *     reaches them.
@@ -64,7 +70,9 @@ typedef enum {
                           /* 8-byte aligned                                */
   ZK_ERR_UNSUPPORTED = 8, /* unknown op / epilogue value                    */
   ZK_ERR_HIP = 9,         /* a kernel launch failed                         */
-  ZK_ERR_SHAPE = 10       /* reduce target does not broadcast to the input  */
+  ZK_ERR_SHAPE = 10,      /* reduce target does not broadcast to the input  */
+  ZK_ERR_DEVICE = 11      /* (debug checks only) a pointer is not device or */
+                          /* managed memory of the stream's device          */
 } zk_status;
 
 /* out = a (op) b.  Operator chapter, "element-wise operators". */
@@ -74,8 +82,9 @@ typedef enum { ZK_ADD = 0, ZK_SUB = 1, ZK_MUL = 2, ZK_DIV = 3 } zk_op;
  * to binary32 first):
  *   ZK_EPI_GELU: y = GeLU(h) = h * Phi(h), Phi the standard normal CDF (the
  *                activation the GPU chapter, "element-wise" section, and the
- *                GPT chapter's FFN name), evaluated in binary64 and rounded
- *                once to binary32; GeLU' = Phi(h) + h*phi(h).
+ *                GPT chapter's FFN name), correctly rounded to binary32 (a
+ *                binary64 evaluation, redone in double-double where it cannot
+ *                decide the rounding); GeLU' = Phi(h) + h*phi(h).
  *   ZK_EPI_RELU: y = ReLU(h) = h for h > 0, NaN for NaN, +0 otherwise (the
  *                activation of the Module chapter's example MLP); ReLU'(h) = 1 for
  *                h > 0, else 0. */
@@ -387,6 +396,22 @@ zk_status zk_row_softmax_stats(const float *x, int64_t rows, int64_t cols, int64
 
 /* Static, NUL-terminated description of a status code. */
 const char *zk_status_string(zk_status s);
+
+/*
+ * Debug pointer checks (GPU chapter, "kernel dispatch": a call whose
+ * tensors live on different devices faults).  mode 1 turns them on, 0 off,
+ * -1 leaves them as they are; returns the mode in effect before the call.
+ * Until the first zk_set_debug, the mode is 1 when the environment variable
+ * ZK_DEBUG is "1" at the library's first call that consults it, else 0.
+ * While on, every computing call (after validating its arguments) asks
+ * hipPointerGetAttributes about each non-NULL pointer it would read or write
+ * (the workspace too when the call needs one) and hipStreamGetDevice (or,
+ * for the NULL stream, hipGetDevice) about the stream, and returns
+ * ZK_ERR_DEVICE without launching anything unless every pointer is device
+ * memory of the stream's device or managed memory.  Off, no check is made
+ * and no runtime call is added.  Thread-safe (an atomic flag).
+ */
+int32_t zk_set_debug(int32_t mode);
 
 /*
  * Host-only inspection of the launch plan a call would use, for tests and

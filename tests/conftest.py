@@ -19,5 +19,5 @@ def orc():
     import oracle
     if not os.path.exists(oracle.LIB_PATH):
         oracle.build()
-    oracle.set_threads(min(8, os.cpu_count() or 1))
+    oracle.set_threads(min(16, os.cpu_count() or 1))
     return oracle

@@ -1,11 +1,9 @@
 """Helpers for the GPU parity tests: seeded views on both sides and the
 comparison rules.
 
-Forward: bit-exact (any NaN matches any NaN).  GeLU forward: bit-exact, except
-that one unit in the last place is accepted where the exact value lies within
-a relative 1e-12 of the midpoint between the two neighbouring binary32 values
-(both sides round a binary64 evaluation of GeLU; their libm erfc may differ by
-a few binary64 ulps, which only matters at such near-ties).
+Forward: bit-exact (any NaN matches any NaN), the GeLU epilogue included: both
+sides round the exact h * Phi(h) correctly (the oracle through binary128 where
+binary64 cannot decide, the kernels through double-double).
 Backward: |gpu - oracle| <= 2e-6 * sum|terms| + 2^-149 per element, and
 exactly +-0 where that sum is 0.  The 2^-149 term is the spacing of binary32
 subnormals: a binary32 result below 2^-126 cannot carry the relative accuracy
@@ -55,22 +53,20 @@ def assert_bitexact(got, want, what=""):
                              f"{i}: got {got.reshape(-1)[i]} want {want.reshape(-1)[i]}")
 
 
-def assert_gelu_exact(got, want, hval):
-    """Bit-exact GeLU with the documented near-tie exception.  ``hval`` is the
-    binary32 argument h of each element."""
-    import oracle
+def assert_gelu_exact(got, want, hval=None, what="gelu"):
+    """GeLU forward: bit for bit (``hval``, the binary32 arguments, only
+    names the first differing ones).  Returns 0, the number of differences
+    allowed."""
     got = np.asarray(got, dtype=np.float32).reshape(-1)
     want = np.asarray(want, dtype=np.float32).reshape(-1)
-    h = np.asarray(hval, dtype=np.float32).reshape(-1)
     diff = np.flatnonzero((got.view(np.uint32) != want.view(np.uint32)) &
                           ~(np.isnan(got) & np.isnan(want)))
-    for i in diff:
-        gi, wi = got.view(np.int32)[i], want.view(np.int32)[i]
-        assert abs(int(gi) - int(wi)) == 1, (i, got[i], want[i], h[i])
-        exact = float(h[i]) * oracle.phi_cdf(float(h[i]))
-        mid = 0.5 * (float(got[i]) + float(want[i]))
-        assert abs(exact - mid) <= 1e-12 * abs(exact), (i, h[i], exact, mid)
-    return len(diff)
+    if diff.size:
+        i = diff[:5]
+        h = None if hval is None else np.asarray(hval, np.float32).reshape(-1)[i]
+        raise AssertionError(f"{what}: {diff.size} of {got.size} differ; first at {i}: "
+                             f"h {h} got {got[i]} want {want[i]}")
+    return 0
 
 
 def assert_bwd(got, ref, what=""):

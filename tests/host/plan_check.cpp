@@ -341,6 +341,23 @@ int main() {
         r.workspace > ((size_t)64 << 20) / 16)
       return fail("middle plan", rr.kernel, (long long)r.workspace);
   }
+  // 6. debug pointer checks: the decision on synthetic runtime records
+  {
+    const PtrRecord dev0{1, kMemDevice, 0}, dev1{1, kMemDevice, 1}, host{1, kMemHost, 0},
+        unreg{1, kMemUnregistered, -1}, unknown{0, kMemUnregistered, -1},
+        managed{1, kMemManaged, 3};
+    const PtrRecord ok3[3] = {dev0, dev0, managed};
+    if (check_ptr_records(ok3, 3, 0) != ZK_OK) return fail("debug ok", 0, 0);
+    if (check_ptr_records(ok3, 0, 0) != ZK_OK) return fail("debug none", 0, 0);
+    if (check_ptr_records(ok3, 3, -1) != ZK_ERR_DEVICE) return fail("debug no device", 0, 0);
+    for (const PtrRecord &bad : {dev1, host, unreg, unknown}) {
+      const PtrRecord mix[3] = {dev0, bad, dev0};
+      if (check_ptr_records(mix, 3, 0) != ZK_ERR_DEVICE) return fail("debug bad", bad.mem_type, 0);
+    }
+    const PtrRecord on1[2] = {dev1, managed};
+    if (check_ptr_records(on1, 2, 1) != ZK_OK) return fail("debug device 1", 0, 0);
+    if (check_ptr_records(on1, 2, 0) != ZK_ERR_DEVICE) return fail("debug wrong device", 0, 0);
+  }
   std::printf("OK\n");
   return 0;
 }

@@ -2,14 +2,15 @@
 
 GeLU is named by the MLP passages of the "Zero" book (Operator chapter,
 "fusion"; GPT chapter, the feed-forward block) without a formula; both sides
-compute GeLU(h) = h Phi(h) rounded once to binary32 (the oracle from the C
-library's binary64 erfc, the kernels from their own piecewise polynomials
-with a binary64 libm fallback near rounding ties).  Here every one of the
-2,185,232,386 binary32 values in [-10, 10] (both zeros included) goes through
-the MLP layout the benchmark times, act[rows, 1024] + bias[1024] with a zero
-bias, and each result must equal the oracle's bit for bit, apart from the
-documented near-tie exception (results one unit apart where the exact value
-lies within 1e-12 relative of the midpoint between them).
+compute GeLU(h) = h Phi(h) correctly rounded to binary32 (the oracle from the
+C library's binary64 erfc, in binary128 where that cannot decide the
+rounding; the kernels from their own piecewise polynomials, in double-double
+where those cannot).  Here every one of the 2,185,232,386 binary32 values in
+[-10, 10] (both zeros included) goes through the MLP layout the benchmark
+times, act[rows, 1024] + bias[1024] with a zero bias, and each result must
+equal the oracle's bit for bit.  The arguments nearest a rounding midpoint,
+and constructed ones (odd multiples of 2^-149, where h/2 is itself a
+midpoint), also go through every forward kernel class against mpmath.
 
 The backward GeLU'(h) = Phi(h) + h phi(h) is swept over every 16th binary32
 bit pattern in [-14, 14] (every exponent, 2^19 significands of each; past the
@@ -48,7 +49,7 @@ def say(*a):
 def _sweep(orc, sign_bit):
     bias_np = np.zeros(COLS, np.float32)
     bias = dev(bias_np)
-    total = ties = 0
+    total = 0
     for lo in range(0, TEN + 1, CHUNK):
         hi = min(lo + CHUNK, TEN + 1)
         bits = np.arange(lo, hi, dtype=np.uint32) | np.uint32(sign_bit)
@@ -59,13 +60,11 @@ def _sweep(orc, sign_bit):
         h = bits.view(np.float32).reshape(-1, COLS)
         got = host(zk.binary_fwd("add", dev(h), bias, epi="gelu"))
         want = orc.fwd("add", h, bias_np, epi=orc.EPI_GELU)
-        ties += assert_gelu_exact(got.reshape(-1)[:n], want.reshape(-1)[:n],
-                                  h.reshape(-1)[:n])
+        assert_gelu_exact(got.reshape(-1)[:n], want.reshape(-1)[:n], h.reshape(-1)[:n],
+                          f"bits from {lo:#010x}")
         total += n
-        say(f"  bits {lo:#010x}..{hi - 1:#010x} (sign {sign_bit >> 31}): {n} values, "
-            f"near-tie exceptions so far {ties}")
+        say(f"  bits {lo:#010x}..{hi - 1:#010x} (sign {sign_bit >> 31}): {n} values equal")
     assert total == TEN + 1
-    return ties
 
 
 def test_gelu_every_nonnegative_binary32_to_ten(orc):
@@ -74,6 +73,44 @@ def test_gelu_every_nonnegative_binary32_to_ten(orc):
 
 def test_gelu_every_nonpositive_binary32_to_minus_ten(orc):
     _sweep(orc, 0x80000000)
+
+
+def test_gelu_hard_cases_every_forward_kernel():
+    """The near-tie arguments of [-10, 10] and the constructed midpoint cases
+    (tests/gelu_cases.py), plus -inf, +-0 and arguments down to -16, through
+    each forward kernel class that applies the epilogue -- fwd_flat (two
+    dense operands), fwd_row (the bias layout, and the host-scalar path of
+    the stand-alone activation), fwd_tile (a transposed operand), fwd_generic
+    (a gathered operand), fwd2 is not reached (no epilogue) -- against mpmath
+    correctly rounded."""
+    from gelu_cases import constructed_arguments, mp_gelu_f32, near_tie_arguments
+    hs = np.concatenate([near_tie_arguments(), constructed_arguments(),
+                         np.array([-np.inf, 0.0, -0.0, -15.0, -16.0, -14.75], np.float32)])
+    n = hs.size
+    cols = 4
+    rows = -(-n // cols)
+    pad = np.concatenate([hs, np.full(rows * cols - n, 1.0, np.float32)])
+    # GeLU(+-0) = +-0 and GeLU(-inf) = -0 (mpmath has no signed zero)
+    want = np.array([h if h == 0 else (mp_gelu_f32(h) if np.isfinite(h) else np.float32(-0.0))
+                     for h in pad], dtype=np.float32)
+    h2 = pad.reshape(rows, cols)
+    # the epilogue's argument is h - (+0), which is h for every binary32 h
+    # (-0 included; -0 + (+0) would be +0)
+    zrow = torch.zeros(cols, device="cuda")
+    cases = {
+        "fwd_flat": lambda: zk.binary_fwd("sub", dev(h2), torch.zeros(rows, cols, device="cuda"),
+                                          epi="gelu"),
+        "fwd_row": lambda: zk.binary_fwd("sub", dev(h2), zrow, epi="gelu"),
+        "unary": lambda: zk.unary_fwd("gelu", dev(h2)),
+        "fwd_tile": lambda: zk.binary_fwd("sub", dev(np.ascontiguousarray(h2.T)).t(),
+                                          zrow, epi="gelu"),
+        "fwd_generic": lambda: zk.binary_fwd(
+            "sub", torch.as_strided(dev(np.repeat(pad, 2)), (rows, cols), (2 * cols, 2)),
+            torch.zeros(rows, 1, device="cuda"), epi="gelu"),
+    }
+    for name, fn in cases.items():
+        got = host(fn()).reshape(-1)
+        assert_gelu_exact(got, want, pad, name)
 
 
 def _chunks(top, sign_bit, step):

@@ -3,9 +3,8 @@ element by element, on seeded inputs.
 
 Forward: bit-exact.  Backward: |err| <= 2e-6 * sum|terms| per element, plus one
 binary32 subnormal step (2^-149) for results the format cannot resolve finer.
-Small cases run the oracle on every element; the full-size workloads (the
-shapes and launch configuration the benchmark times) are checked on sampled
-positions of the large outputs and on every element of the reduced ones.
+Every case, the full-size workloads included (the shapes and launch
+configuration the benchmark times), is compared on every output element.
 """
 import itertools
 import math
@@ -502,6 +501,49 @@ def test_side_stream_allocations_outlive_their_kernels(orc, monkeypatch):
     assert_bwd(host(gb), rb, "grad_b")
 
 
+def test_debug_checks_accept_device_pointers(orc):
+    """With the debug pointer checks on, every kind of call on device tensors
+    of the current device, on the default stream and on a side stream, runs
+    and returns the same bits as with the checks off."""
+    rng = np.random.default_rng(81)
+    a = dev(rng.standard_normal((256, 512)).astype(np.float32))
+    b = dev(rng.standard_normal(512).astype(np.float32))
+    c = dev(rng.standard_normal((256, 512)).astype(np.float32))
+    g = dev(rng.standard_normal((256, 512)).astype(np.float32))
+
+    def run(stream):
+        gl = [c.clone(), g.clone()]     # clipped in place below
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+        out = [zk.binary_fwd("mul", a, b, epi="gelu", stream=stream)]
+        out += zk.binary_bwd("mul", g, a, b, stream=stream)
+        out.append(zk.reduce_to_shape(a, (1, 512), stream=stream))
+        out.append(zk.mean_to_shape(a, (256, 1), stream=stream))
+        out.append(zk.binary2_fwd("mul", "add", a, b, c, stream=stream))
+        out += zk.binary2_bwd("mul", "add", g, a, b, c, stream=stream)
+        out.append(zk.materialize(a.t(), stream=stream))
+        out.append(zk.scalar_fwd("add", a, 2.5, stream=stream))
+        out.append(zk.unary_bwd("gelu", g, a, stream=stream))
+        out.append(zk.mean_bwd(b, (256, 512), stream=stream))
+        out.append(zk.clip_grad_norm(gl, 1.0, stream=stream))
+        out += gl
+        out += zk.row_moments(a, stream=stream)
+        out += zk.row_softmax_stats(a, stream=stream)
+        return out
+
+    torch.cuda.synchronize()
+    ref = [host(x).copy() for x in run(None)]
+    prev = zk.set_debug(1)
+    try:
+        for stream in (None, torch.cuda.Stream()):
+            got = run(stream)
+            torch.cuda.synchronize()
+            for x, r in zip(got, ref):
+                assert np.array_equal(host(x).view(np.uint32), r.view(np.uint32))
+    finally:
+        zk.set_debug(prev)
+
+
 def test_mass_invariant_gpu():
     rng = np.random.default_rng(71)
     g = rng.standard_normal((64, 130, 64)).astype(np.float32)
@@ -511,39 +553,33 @@ def test_mass_invariant_gpu():
         assert abs(r.sum() - exact) <= 2e-6 * np.abs(g).sum() + 1e-6 * r.size
 
 
-# --------------------------------------------- full sizes, sampled checks
-def _sample(n, k, seed):
-    rng = np.random.default_rng(seed)
-    s = rng.integers(0, n, k, dtype=np.int64)
-    return np.unique(np.concatenate([s, [0, n - 1]]))
+# ------------------------------------ full sizes, every element checked
+def _check_full_fwd(orc, op, a, b, got, what):
+    """Every output element of a full-size forward against the oracle."""
+    say(f"  {what}: {got.size} elements")
+    assert_bitexact(got, orc.fwd(op, a, b), what)
 
 
-def _check_sampled_fwd(orc, op, a, b, got, seed, epi=0):
-    pos = _sample(got.size, 20000, seed)
-    want = orc.fwd_at(op, a, b, pos, epi=epi)
-    if epi:
-        h = orc.fwd_at(op, a, b, pos)
-        assert_gelu_exact(got.reshape(-1)[pos], want, h)
-    else:
-        assert_bitexact(got.reshape(-1)[pos], want, f"sampled fwd {op}")
-
-
-def _check_sampled_bwd(orc, op, which, g, a, b, got, seed, acc=None, epi=0, full=False):
-    n = got.size
-    pos = np.arange(n, dtype=np.int64) if full else _sample(n, 20000, seed)
-    ref = orc.bwd_at(op, which, g, a, b, pos, acc=acc, epi=epi)
-    assert_bwd(got.reshape(-1)[pos], ref, f"sampled bwd {op}/{which}")
+def _check_full_bwd(orc, op, which, g, a, b, got, what, acc=None):
+    """Every element of one full-size gradient against the oracle."""
+    say(f"  {what}: {got.size} elements")
+    want = (which == 0, which == 1)
+    ra, rb = orc.bwd(op, g, a, b, acc_a=acc if which == 0 else None,
+                     acc_b=acc if which == 1 else None, want=want)
+    m = assert_bwd(got, ra if which == 0 else rb, what)
+    say(f"    largest error / allowance {m:.3f}")
 
 
 def test_full_size_xy_plus_x(orc):
     wl = steps.XYPlusX()
     h = wl.host
     wl.run()
-    _check_sampled_fwd(orc, "mul", h["x"], h["y"], host(wl.t), 1)
     t = host(wl.t)
-    _check_sampled_fwd(orc, "add", t, h["x"], host(wl.z), 2)
-    _check_sampled_bwd(orc, "mul", 0, h["g"], h["x"], h["y"], host(wl.grad_x), 3, acc=h["g"])
-    _check_sampled_bwd(orc, "mul", 1, h["g"], h["x"], h["y"], host(wl.grad_y), 4, full=True)
+    _check_full_fwd(orc, "mul", h["x"], h["y"], t, "t = x * y")
+    _check_full_fwd(orc, "add", t, h["x"], host(wl.z), "z = t + x")
+    _check_full_bwd(orc, "mul", 0, h["g"], h["x"], h["y"], host(wl.grad_x), "grad_x",
+                    acc=h["g"])
+    _check_full_bwd(orc, "mul", 1, h["g"], h["x"], h["y"], host(wl.grad_y), "grad_y")
 
 
 def test_full_size_mlp_bias_gelu(orc):
@@ -563,12 +599,14 @@ def test_full_size_attn_scale_mask(orc):
     wl = steps.AttnScaleMask()
     h = wl.host
     wl.run()
-    _check_sampled_fwd(orc, "mul", h["scores"], h["scale"], host(wl.t), 5)
-    _check_sampled_fwd(orc, "add", host(wl.t), h["mask"], host(wl.out), 6)
-    _check_sampled_bwd(orc, "mul", 0, h["g"], h["scores"], h["scale"],
-                       host(wl.grad_scores), 7)
-    _check_sampled_bwd(orc, "mul", 1, h["g"], h["scores"], h["scale"],
-                       host(wl.grad_scale), 8, full=True)
+    t = host(wl.t)
+    _check_full_fwd(orc, "mul", h["scores"], h["scale"], t, "t = scores * scale")
+    _check_full_fwd(orc, "add", t, h["mask"], host(wl.out), "out = t + mask")
+    del t
+    _check_full_bwd(orc, "mul", 0, h["g"], h["scores"], h["scale"], host(wl.grad_scores),
+                    "grad_scores")
+    _check_full_bwd(orc, "mul", 1, h["g"], h["scores"], h["scale"], host(wl.grad_scale),
+                    "grad_scale")
 
 
 def test_full_size_attn_mask_grad(orc):
@@ -680,9 +718,9 @@ def test_full_size_strided(orc):
     h = wl.host
     wl.run()
     va = orc.View(h["a_storage"], h["a_sizes"], h["a_strides"])
-    _check_sampled_fwd(orc, "mul", va, h["b"], host(wl.out), 9)
-    _check_sampled_bwd(orc, "mul", 0, h["g"], va, h["b"], host(wl.grad_a), 10)
-    _check_sampled_bwd(orc, "mul", 1, h["g"], va, h["b"], host(wl.grad_b), 11, full=True)
+    _check_full_fwd(orc, "mul", va, h["b"], host(wl.out), "out = a^T * b")
+    _check_full_bwd(orc, "mul", 0, h["g"], va, h["b"], host(wl.grad_a), "grad_a")
+    _check_full_bwd(orc, "mul", 1, h["g"], va, h["b"], host(wl.grad_b), "grad_b")
 
 
 def test_full_size_gpt_residual(orc):
@@ -690,12 +728,12 @@ def test_full_size_gpt_residual(orc):
     h = wl.host
     wl.run()
     t = host(wl.t)
-    _check_sampled_fwd(orc, "mul", h["h"], h["gamma"], t, 12)
-    _check_sampled_fwd(orc, "add", t, h["resid"], host(wl.out), 13)
-    _check_sampled_bwd(orc, "mul", 0, h["g"], h["h"], h["gamma"], host(wl.grad_h), 14)
-    _check_sampled_bwd(orc, "mul", 1, h["g"], h["h"], h["gamma"], host(wl.grad_gamma), 15,
-                       full=True)
-    _check_sampled_bwd(orc, "add", 1, h["g"], t, h["resid"], host(wl.grad_resid), 16)
+    _check_full_fwd(orc, "mul", h["h"], h["gamma"], t, "t = h * gamma")
+    _check_full_fwd(orc, "add", t, h["resid"], host(wl.out), "out = t + resid")
+    _check_full_bwd(orc, "mul", 0, h["g"], h["h"], h["gamma"], host(wl.grad_h), "grad_h")
+    _check_full_bwd(orc, "mul", 1, h["g"], h["h"], h["gamma"], host(wl.grad_gamma),
+                    "grad_gamma")
+    _check_full_bwd(orc, "add", 1, h["g"], t, h["resid"], host(wl.grad_resid), "grad_resid")
 
 
 # One-pass row reductions (2048..16384 terms per kept element): a block per

@@ -9,6 +9,7 @@ import re
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 from conftest import ROOT
@@ -483,3 +484,98 @@ def test_planner_under_sanitizers():
                    ["-o", exe], check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "OK" in r.stdout, r.stdout + r.stderr
+
+
+def _gelu_exact_host():
+    """The library's double-double GeLU (csrc/zk_gelu_exact.h) built for the
+    host: the same IEEE binary64 operations the kernels run."""
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("no g++")
+    exe = os.path.join(ROOT, "_build", "gelu_exact_check")
+    os.makedirs(os.path.dirname(exe), exist_ok=True)
+    subprocess.run([gxx, "-std=c++17", "-O2", "-ffp-contract=off", "-msse2", "-mfpmath=sse",
+                    "-I", os.path.join(ROOT, "broadcast_autograd_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "host", "gelu_exact_check.cpp"), "-o", exe],
+                   check=True)
+
+    def run(hs):
+        pats = np.asarray(hs, dtype=np.float32).view(np.uint32)
+        r = subprocess.run([exe], input="\n".join(f"{u:08x}" for u in pats), text=True,
+                           capture_output=True, timeout=600, check=True)
+        return np.array([int(x, 16) for x in r.stdout.split()], dtype=np.uint32)
+    return run
+
+
+def test_gelu_exact_path_against_mpmath():
+    """The kernels' double-double GeLU (their path wherever the binary64
+    table cannot round with certainty) is h * Phi(h) correctly rounded: on
+    every near-tie argument of [-10, 10], on constructed midpoint cases
+    (odd multiples of 2^-149 and the like) and on random arguments down to
+    -15, each against mpmath at 400 bits."""
+    from gelu_cases import constructed_arguments, mp_gelu_f32, near_tie_arguments
+    run = _gelu_exact_host()
+    rng = np.random.default_rng(2024)
+    hs = np.concatenate([near_tie_arguments(), constructed_arguments(),
+                         rng.uniform(-15, 7, 400).astype(np.float32),
+                         (rng.standard_normal(100) * 1e-20).astype(np.float32)])
+    got = run(hs)
+    want = np.array([mp_gelu_f32(h) for h in hs], dtype=np.float32).view(np.uint32)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(float(hs[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+def test_gelu_exact_path_against_oracle(orc):
+    """The same path against the oracle on 200k arguments spread over every
+    binade the kernels send to it (tiny, ordinary, near -15, and the limits)."""
+    run = _gelu_exact_host()
+    rng = np.random.default_rng(2025)
+    mags = 2.0 ** rng.uniform(-149, 4, 120000)
+    hs = np.concatenate([(mags * rng.choice([-1, 1], mags.size)).astype(np.float32),
+                         rng.uniform(-15, -6, 40000).astype(np.float32),
+                         rng.uniform(-10, 10, 40000).astype(np.float32),
+                         np.array([0.0, -0.0, np.inf, -np.inf, -15.0, -14.999], np.float32)])
+    got = run(hs).view(np.float32)
+    want = orc.fwd("sub", hs, np.zeros(1, np.float32), epi=orc.EPI_GELU)
+    same = (got.view(np.uint32) == want.view(np.uint32))
+    bad = np.flatnonzero(~same)
+    assert bad.size == 0, [(float(hs[i]), float(got[i]), float(want[i])) for i in bad[:5]]
+
+
+def test_debug_mode_from_environment():
+    """ZK_DEBUG=1 turns the pointer checks on at the first consultation;
+    zk_set_debug overrides it (a fresh process each, no GPU call)."""
+    import sys
+    code = ("from broadcast_autograd_amd import zk; L = zk.lib(); "
+            "print(L.zk_set_debug(-1), L.zk_set_debug(0), L.zk_set_debug(-1), "
+            "L.zk_set_debug(1), L.zk_set_debug(-1))")
+    for env, want in (("1", "1 1 0 0 1"), ("0", "0 0 0 0 1"), (None, "0 0 0 0 1")):
+        e = {k: v for k, v in os.environ.items() if k != "ZK_DEBUG"}
+        if env is not None:
+            e["ZK_DEBUG"] = env
+        r = subprocess.run([sys.executable, "-c", code], env=e, cwd=ROOT, text=True,
+                           capture_output=True, timeout=120, check=True)
+        assert r.stdout.split() == want.split(), (env, r.stdout, r.stderr)
+
+
+def test_debug_check_refuses_without_a_device(L):
+    """With the checks on and no usable GPU (this host), a call is refused with
+    ZK_ERR_DEVICE after validation and before any launch; validation errors
+    still come first.  Skipped where a GPU is present: no test hands a host
+    pointer to a call that could launch."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    a = np.zeros(16, np.float32)
+    d = zk.make_desc((16,))
+    prev = zk.set_debug(1)
+    try:
+        p = a.ctypes.data
+        rc = L.zk_binary_fwd(9, 0, p, ctypes.byref(d), p, ctypes.byref(d), p, None)
+        assert rc == zk.ERR["ZK_ERR_UNSUPPORTED"]  # validation first
+        out = np.zeros(16, np.float32)
+        rc = L.zk_binary_fwd(0, 0, p, ctypes.byref(d), p, ctypes.byref(d), out.ctypes.data, None)
+        assert rc == zk.ERR["ZK_ERR_DEVICE"]
+        assert L.zk_status_string(rc).decode().startswith("a pointer is not device")
+    finally:
+        zk.set_debug(prev)

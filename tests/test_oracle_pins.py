@@ -397,26 +397,11 @@ def test_gelu_pins(orc):
         assert abs(fd - (orc.phi_cdf(h) + h * orc.phi_pdf(h))) < 1e-9
 
 
-def _mp_gelu_f32(h):
-    """GeLU(h) = h * Phi(h) from mpmath at 400 bits, correctly rounded to
-    binary32 (nearest; an exact tie would go to the even neighbour, but none
-    occurs for a binary32 h != 0, since h * Phi(h) is then irrational)."""
-    import mpmath
-    with mpmath.workprec(400):
-        hx = mpmath.mpf(float(h))
-        y = hx * mpmath.ncdf(hx)
-        c = np.float32(float(y))
-        cands = [np.nextafter(c, F32(-np.inf)), c, np.nextafter(c, F32(np.inf))]
-        dist = [abs(mpmath.mpf(float(v)) - y) for v in cands]
-        k = min(range(3), key=lambda i: dist[i])
-        assert sorted(dist)[0] != sorted(dist)[1], ("exact tie", h)
-        return cands[k]
-
-
 def _check_gelu_exact(orc, hs, what):
+    from gelu_cases import mp_gelu_f32
     for h in hs:
         h = F32(h)
-        want = _mp_gelu_f32(h)
+        want = mp_gelu_f32(h)
         for name, fn in (("gelu32", orc.gelu32), ("binary128", orc.gelu32_q)):
             got = fn(h)
             assert got.view(np.uint32) == want.view(np.uint32), \
@@ -427,46 +412,18 @@ def test_gelu_near_ties_correctly_rounded(orc):
     """Every binary32 h in [-10, 10] whose binary64 GeLU lies within 1e-14 of
     a binary32 midpoint (tests/golden/gelu_near_ties.txt, an exhaustive scan):
     the oracle's result equals mpmath's h * Phi(h) correctly rounded."""
-    pats = [int(x, 16) for x in _golden("gelu_near_ties.txt")]
-    assert len(pats) > 100
-    hs = np.array(pats, dtype=np.uint32).view(np.float32)
-    assert np.all(np.abs(hs) <= 10)
+    from gelu_cases import near_tie_arguments
+    hs = near_tie_arguments()
+    assert hs.size > 100 and np.all(np.abs(hs) <= 10)
     _check_gelu_exact(orc, hs, "near tie")
 
 
 def test_gelu_constructed_hard_cases(orc):
-    """Arguments built to sit on or next to binary32 midpoints, each against
-    mpmath: odd multiples of 2^-149 (h/2 is exactly a midpoint and
-    h * Phi(h) = h/2 + h^2 phi(0) + ... lies just above it), normal h whose
-    half is a subnormal midpoint, the run near h = 7.5e-8 where GeLU(h) / (h/2)
-    - 1 = 0.8 h crosses half a binary32 unit, the crossing near h = 5.2 where
-    h - GeLU(h) = h Phi(-h) passes half a unit of h, the switch between the
-    oracle's two binary128 forms at h = -1, and the subnormal results near
-    h = -14."""
-    tiny = 2.0 ** -149
-    hs = [s * k * tiny for k in (1, 3, 5, 7, 2 ** 23 - 1, 2 ** 23 + 1, 12345) for s in (1, -1)]
-    hs += [s * k * tiny for k in (2, 4, 1024) for s in (1, -1)]           # h/2 exact
-    m = np.float32(2.0 ** -126)
-    hs += [s * float(np.nextafter(m, F32(1))) for s in (1, -1)]            # (1 + 2^-23) 2^-126
-    hs += [s * float(F32(1.5) * m + F32(2.0 ** -149)) for s in (1, -1)]
-    # GeLU(h) ~ h/2 (1 + 0.8 h): 0.8 h = 2^-24 near h = 7.45e-8
-    base = int(F32(7.45e-8).view(np.uint32))
-    hs += list(np.arange(base - 48, base + 48, 3, dtype=np.uint32).view(np.float32))
-    # h Phi(-h) = 2^-22 (half a unit of h in [4, 8)) near h = 5.2
-    lo, hi = 5.0, 5.5
-    for _ in range(60):
-        mid = 0.5 * (lo + hi)
-        if mid * orc.phi_cdf(-mid) > 2.0 ** -22:
-            lo = mid
-        else:
-            hi = mid
-    c = int(F32(lo).view(np.uint32))
-    hs += list(np.arange(c - 32, c + 32, dtype=np.uint32).view(np.float32))
-    one = int(F32(1.0).view(np.uint32))
-    hs += [-float(v) for v in np.arange(one - 4, one + 4, dtype=np.uint32).view(np.float32)]
-    hs += list(np.linspace(-14.6, -13.0, 41, dtype=np.float32))
-    _check_gelu_exact(orc, hs, "constructed")
-    # and a spread of ordinary arguments
+    """Arguments built to sit on or next to binary32 midpoints (see
+    gelu_cases.constructed_arguments), and a spread of ordinary ones, each
+    against mpmath."""
+    from gelu_cases import constructed_arguments
+    _check_gelu_exact(orc, constructed_arguments(), "constructed")
     rng = np.random.default_rng(121)
     _check_gelu_exact(orc, rng.uniform(-10, 10, 300).astype(np.float32), "random")
 
