@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzk.so")
 
 SOURCES = ["zk_plan.cpp", "zk_api.cpp", "zk_fwd.hip", "zk_bwd.hip", "zk_norm.hip",
-           "zk_rows.hip"]
+           "zk_rows.hip", "zk_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -276,7 +276,9 @@ const char *zk_status_string(zk_status s) {
     case ZK_ERR_BAD_STRIDE: return "negative stride";
     case ZK_ERR_BROADCAST: return "shapes do not broadcast";
     case ZK_ERR_ALIAS: return "an output overlaps an input or another output";
-    case ZK_ERR_WORKSPACE: return "workspace too small or not 8-byte aligned";
+    case ZK_ERR_WORKSPACE:
+      return "workspace too small or not 8-byte aligned (zk_binary_bwd_noalloc: the call "
+             "needs more than ZK_SCRATCH_BYTES)";
     case ZK_ERR_UNSUPPORTED: return "unsupported op or epilogue";
     case ZK_ERR_HIP: return "HIP launch failed";
     case ZK_ERR_SHAPE: return "target shape does not broadcast to the input";
@@ -329,8 +331,8 @@ zk_status zk_binary_fwd(zk_op op, zk_epi epi, const float *a, const zk_desc *da,
 }  // extern "C"
 
 namespace {
-// zk_binary_bwd; lib_ws: the workspace is memory the library owns (left out
-// of the debug pointer check, which asks about caller memory).
+// zk_binary_bwd; lib_ws: the workspace is the library's own scratch array
+// (left out of the debug pointer check, which asks about caller memory).
 zk_status binary_bwd_impl(zk_op op, zk_epi epi, const float *grad, const float *a,
                           const zk_desc *da, const float *b, const zk_desc *db,
                           float *grad_a, const float *acc_a, float *grad_b,
@@ -394,6 +396,38 @@ zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad, const float *a,
                         size_t *workspace_bytes, void *stream) {
   return binary_bwd_impl(op, epi, grad, a, da, b, db, grad_a, acc_a, grad_b, acc_b, workspace,
                          workspace_bytes, stream, false);
+}
+
+zk_status zk_binary_bwd_noalloc(zk_op op, zk_epi epi, const float *grad, const float *a,
+                                const zk_desc *da, const float *b, const zk_desc *db,
+                                float *grad_a, const float *acc_a, float *grad_b,
+                                const float *acc_b, void *stream) {
+  // the workspace need, from the shapes alone (host planning, nothing launched)
+  size_t need = 0;
+  zk_status s = zk_binary_bwd(op, epi, grad, a, da, b, db, grad_a, acc_a, grad_b, acc_b,
+                              nullptr, &need, nullptr);
+  if (s) return s;
+  if (need > ZK_SCRATCH_BYTES) return ZK_ERR_WORKSPACE;
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return ZK_ERR_DEVICE;
+  }
+  if (stream) {
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return ZK_ERR_DEVICE;
+    }
+    if (sdev != dev) return ZK_ERR_DEVICE;
+  }
+  void *ws = nullptr;
+  if (scratch_on_current_device(&ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return ZK_ERR_HIP;
+  }
+  size_t cap = ZK_SCRATCH_BYTES;
+  return binary_bwd_impl(op, epi, grad, a, da, b, db, grad_a, acc_a, grad_b, acc_b, ws, &cap,
+                         stream, true);
 }
 
 }  // extern "C"

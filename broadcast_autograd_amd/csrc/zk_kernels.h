@@ -109,6 +109,10 @@ size_t norm_workspace(int count, const int64_t *numels);
 hipError_t launch_grad_norm(int count, float *const *g, const int64_t *numels, float *norm_out,
                             void *ws, bool clip, double max_norm, hipStream_t st);
 
+// ---- the library-owned scratch array (zk_scratch.hip): the device address of
+// the current device's copy, looked up on its first use.
+hipError_t scratch_on_current_device(void **ptr);
+
 // ---- per-row statistics (zk_rows.hip): mode 0 mean / variance, mode 1
 // row max / sum of exponentials; rows of `cols` elements at a pitch of ld.
 hipError_t launch_row_stats(int mode, const float *x, int64_t rows, int64_t cols, int64_t ld,

@@ -23,7 +23,7 @@ STATUS = {0: "ZK_OK", 1: "ZK_ERR_NULL", 2: "ZK_ERR_RANK", 3: "ZK_ERR_BAD_SIZE",
 ERR = {v: k for k, v in STATUS.items()}
 
 # exported symbols declared in include/zk.h
-SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd",
+SYMBOLS = ("zk_broadcast_shape", "zk_binary_fwd", "zk_binary_bwd", "zk_binary_bwd_noalloc",
            "zk_reduce_to_shape", "zk_materialize", "zk_binary2_fwd", "zk_binary2_bwd",
            "zk_scalar_fwd", "zk_scalar_bwd", "zk_unary_fwd", "zk_unary_bwd",
            "zk_mean_to_shape", "zk_mean_bwd", "zk_grad_norm", "zk_clip_grad_norm",
@@ -77,6 +77,7 @@ def lib():
         L.zk_broadcast_shape.argtypes = [I32, P, I32, P, P, P]
         L.zk_binary_fwd.argtypes = [I32, I32, P, P, P, P, P, P]
         L.zk_binary_bwd.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.zk_binary_bwd_noalloc.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P]
         L.zk_reduce_to_shape.argtypes = [P, P, I32, P, P, P, P, P]
         L.zk_materialize.argtypes = [P, P, I32, P, P, P]
         F32 = ctypes.c_float

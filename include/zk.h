@@ -170,6 +170,29 @@ zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad,
                         size_t *workspace_bytes, void *stream);
 
 /*
+ * zk_binary_bwd without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The binary64 partial sums go to a device array the
+ * library owns, ZK_SCRATCH_BYTES bytes on each GPU it runs on (held until the
+ * process ends; its address is looked up on the first call on each device).
+ * The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *   Arguments, results, aliasing and errors as zk_binary_bwd, and:
+ *   - a call whose workspace need (what zk_binary_bwd's query reports)
+ *     exceeds ZK_SCRATCH_BYTES returns ZK_ERR_WORKSPACE, launching nothing;
+ *   - `stream` must belong to the current device (else ZK_ERR_DEVICE).
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (two streams, two
+ * host threads) race and give wrong sums; serialise them.  Nothing needs
+ * clearing between calls: every partial is written before it is read.
+ */
+#define ZK_SCRATCH_BYTES ((size_t)8 << 20)
+zk_status zk_binary_bwd_noalloc(zk_op op, zk_epi epi, const float *grad,
+                                const float *a, const zk_desc *da, const float *b,
+                                const zk_desc *db, float *grad_a, const float *acc_a,
+                                float *grad_b, const float *acc_b, void *stream);
+
+/*
  * Sum `in` back to `sizes_out` (Operator chapter, "broadcast": SumToSize),
  * i.e. over every dim where the target is 1 or missing.  The target must
  * broadcast to in's shape with in's shape as the result (else ZK_ERR_SHAPE).

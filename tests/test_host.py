@@ -579,3 +579,29 @@ def test_debug_check_refuses_without_a_device(L):
         assert L.zk_status_string(rc).decode().startswith("a pointer is not device")
     finally:
         zk.set_debug(prev)
+
+
+def test_noalloc_refusals_without_a_device(L):
+    """zk_binary_bwd_noalloc on this GPU-less host: validation errors first,
+    then a workspace need above ZK_SCRATCH_BYTES is ZK_ERR_WORKSPACE (decided
+    from the shapes alone), and a call that fits is refused with ZK_ERR_DEVICE
+    for want of a device.  Skipped where a GPU is present (no test hands a
+    host pointer to a call that could launch)."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    m = ctypes.c_void_p(1 << 20)  # non-NULL markers, never dereferenced here
+    P = lambda k: ctypes.c_void_p(m.value + (k << 36))  # noqa: E731 (disjoint extents)
+    # a transposed [65536, 4096] times [4096]: 1024 partials a column, 32 MiB
+    da = zk.make_desc((65536, 4096), (1, 65536))
+    db = zk.make_desc((4096,))
+    rc = L.zk_binary_bwd_noalloc(9, 0, P(0), P(1), ctypes.byref(da), P(2), ctypes.byref(db),
+                                 P(3), None, P(4), None, None)
+    assert rc == zk.ERR["ZK_ERR_UNSUPPORTED"]
+    rc = L.zk_binary_bwd_noalloc(2, 0, P(0), P(1), ctypes.byref(da), P(2), ctypes.byref(db),
+                                 P(3), None, P(4), None, None)
+    assert rc == zk.ERR["ZK_ERR_WORKSPACE"]
+    ds, dsb = zk.make_desc((64, 256)), zk.make_desc((256,))
+    rc = L.zk_binary_bwd_noalloc(2, 0, P(0), P(1), ctypes.byref(ds), P(2), ctypes.byref(dsb),
+                                 P(3), None, P(4), None, None)
+    assert rc == zk.ERR["ZK_ERR_DEVICE"]
