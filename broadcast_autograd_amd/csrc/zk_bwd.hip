@@ -1253,6 +1253,229 @@ static hipError_t launch_gend(const RedPlan &rp, const Canon &c, bool idx64, int
   });
 }
 
+// -------------------------------------------------------------- red_run
+// A reduction whose two innermost canonical dims form a short contiguous run
+// (L = n0 * n1 elements, 64..256, any mix of kept and reduced) that the
+// source and the full operand walk densely, e.g. the rank-8 pattern
+// [2,3,4,5,6,7,8,9] -> [1,3,1,5,1,7,1,9] (run [8, 9]: 8 reduced x 9 kept).
+// Block kb owns one combination of the outer kept dims and walks every
+// combination of the outer reduced dims (a run each), 1024 / L runs at a time:
+// lane j of a run slot reads element j of each of its runs, so every element
+// is read once, in whole contiguous runs, and a lane always holds the same
+// kept element (its run coordinates' kept part).  The block then adds, for
+// each of its Kin kept elements, the lanes holding it in a fixed order (run
+// coordinates within each slot, then the slots), finishes the sum (sign,
+// acc, divisor; rounded once) and writes it: no partials, no stage 2.  The full operand's
+// gradient is written at every element read.  32-bit offsets (numel < 2^31).
+struct RunArgs {
+  int32_t nk, nr;                                   // outer kept / reduced dims
+  uint32_t kn[kMaxDims], rn[kMaxDims];              // (outer -> inner)
+  FastDiv kfd[kMaxDims], rfd[kMaxDims];
+  int32_t kg[kMaxDims], ksm[kMaxDims], kout[kMaxDims];  // kept dims: source, small, result strides
+  int32_t rg[kMaxDims];                             // reduced dims: source strides
+  int32_t n0, n1, k0, k1;                           // the run's dims, kept flags
+  int32_t sm0, sm1, out0, out1;                     // small / result strides on the run
+  int32_t blocks, runs, slots;
+  int32_t write_big, big_acc;                       // big_acc: 0 none, 1 acc is g, 2 a buffer
+  int32_t neg, has_div;
+  double div;
+};
+constexpr int kRunU = 4;       // runs a lane has in flight
+constexpr int kRunBlk = 1024;  // lanes a block: the rank-8 pattern's 48 runs of 72 in one
+                               // round of loads (14 at once, 4 deep), 105 blocks
+
+template <int OP, int EPI, int WHICH, int IDENT>
+__global__ __launch_bounds__(kRunBlk) void k_red_run(const float *g, const float *a,
+                                                  const float *b, float *gbig,
+                                                  const float *accbig, float *out,
+                                                  const float *acc, RunArgs ra) {
+  constexpr bool RA = !IDENT && (reads_x<OP, EPI, 0>() || reads_x<OP, EPI, 1>());
+  constexpr bool RB = !IDENT && (reads_y<OP, EPI, 0>() || reads_y<OP, EPI, 1>());
+  constexpr bool R_SMALL = WHICH == 0 ? RA : RB;
+  constexpr bool R_BIG = WHICH == 0 ? RB : RA;
+  const float *small = WHICH == 0 ? a : b;
+  const float *big = WHICH == 0 ? b : a;
+  __shared__ double sh[kRunBlk];
+  const int t = threadIdx.x;
+  const int L = ra.n0 * ra.n1;
+  const int slot = t / L, j = t - slot * L;
+  const bool on = slot < ra.slots;
+  const int j0 = j / ra.n1, j1 = j - j0 * ra.n1;
+  const int kin = (ra.k0 ? ra.n0 : 1) * (ra.k1 ? ra.n1 : 1);
+  for (int kb = blockIdx.x; kb < ra.blocks; kb += gridDim.x) {
+    int og = 0, osm = 0, oout = 0;
+    {
+      uint32_t rest = (uint32_t)kb;
+#pragma unroll
+      for (int d = kMaxDims - 1; d >= 0; --d) {
+        if (d < ra.nk) {
+          const uint32_t q = fdiv(ra.kfd[d], rest), c = rest - q * ra.kn[d];
+          og += (int)c * ra.kg[d];
+          osm += (int)c * ra.ksm[d];
+          oout += (int)c * ra.kout[d];
+          rest = q;
+        }
+      }
+    }
+    float sv = 0.f;
+    if (R_SMALL && on) sv = small[osm + j0 * ra.sm0 + j1 * ra.sm1];
+    double s = 0.0;
+    if (on) {
+      for (int r0 = slot; r0 < ra.runs; r0 += ra.slots * kRunU) {
+        int idx[kRunU];
+        float gv[kRunU], bv[kRunU];
+#pragma unroll
+        for (int u = 0; u < kRunU; ++u) {
+          const int r = r0 + u * ra.slots;
+          idx[u] = -1;
+          if (r < ra.runs) {
+            uint32_t rest = (uint32_t)r;
+            int off = og + j;  // the run is dense in the source
+#pragma unroll
+            for (int d = kMaxDims - 1; d >= 0; --d) {
+              if (d < ra.nr) {
+                const uint32_t q = fdiv(ra.rfd[d], rest), c = rest - q * ra.rn[d];
+                off += (int)c * ra.rg[d];
+                rest = q;
+              }
+            }
+            idx[u] = off;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kRunU; ++u) {
+          if (idx[u] >= 0) {
+            gv[u] = g[idx[u]];
+            bv[u] = R_BIG ? big[idx[u]] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kRunU; ++u) {
+          if (idx[u] < 0) continue;
+          if constexpr (IDENT) {
+            s += (double)gv[u];
+          } else {
+            const float x = WHICH == 0 ? sv : bv[u];
+            const float y = WHICH == 0 ? bv[u] : sv;
+            double ts;
+            float tb;
+            terms2<OP, EPI, WHICH>(gv[u], x, y, ts, tb);
+            s += ts;
+            if (ra.write_big) {
+              if (ra.big_acc == 1) tb = gv[u] + tb;
+              else if (ra.big_acc == 2) tb = accbig[idx[u]] + tb;
+              gbig[idx[u]] = tb;
+            }
+          }
+        }
+      }
+    }
+    sh[t] = s;
+    __syncthreads();
+    // Two fixed-order levels: lane (slot, kept element) adds the run lanes of
+    // its slot holding that element, then one lane per kept element adds
+    // the slots' subtotals in slot order.
+    const int na = ra.slots * kin;
+    double v = 0.0;
+    int t0 = 0, t1 = 0;  // the kept element's run coordinates
+    if (t < na) {
+      const int sl = t / kin, tk = t - sl * kin;
+      if (ra.k0 && ra.k1) {
+        t0 = tk / ra.n1;
+        t1 = tk - t0 * ra.n1;
+      } else if (ra.k0) {
+        t0 = tk;
+      } else if (ra.k1) {
+        t1 = tk;
+      }
+      const double *row = sh + sl * L;
+      if (ra.k0 && ra.k1) {
+        v = row[t0 * ra.n1 + t1];
+      } else if (ra.k1) {
+        for (int u0 = 0; u0 < ra.n0; ++u0) v += row[u0 * ra.n1 + t1];
+      } else if (ra.k0) {
+        for (int u1 = 0; u1 < ra.n1; ++u1) v += row[t0 * ra.n1 + u1];
+      } else {
+        for (int u = 0; u < L; ++u) v += row[u];
+      }
+    }
+    __syncthreads();
+    if (t < na) sh[t] = v;
+    __syncthreads();
+    if (t < kin) {
+      double tot = 0.0;
+      for (int sl = 0; sl < ra.slots; ++sl) tot += sh[sl * kin + t];
+      const int k = oout + t0 * ra.out0 + t1 * ra.out1;
+      if (ra.neg) tot = -tot;
+      if (acc) tot += (double)acc[k];
+      if (ra.has_div) tot = tot / ra.div;
+      out[k] = (float)tot;
+    }
+    __syncthreads();  // sh is rewritten for the next block of kept elements
+  }
+}
+
+// One-pass run reduction (red_run).  kept_op: the reduced gradient's stride
+// set; small_op: the reduced operand's own strides (-1: none is read).
+static hipError_t launch_run(const RedPlan &rp, const Canon &c, int kept_op, int small_op,
+                             zk_op op, zk_epi epi, bool ident, int which, const float *g,
+                             const float *a, const float *b, float *gbig, const float *accbig,
+                             int big_acc, bool write_big, float *out, const float *acc,
+                             bool neg, double mean_count, hipStream_t st) {
+  if (rp.kept == 0) return hipSuccess;
+  RunArgs ra{};
+  const int R = c.rank;
+  int64_t blocks = 1, runs = 1;
+  for (int d = 0; d < R - 2; ++d) {
+    const uint32_t n = (uint32_t)c.n[d];
+    if (c.s[kept_op][d] != 0) {
+      ra.kn[ra.nk] = n;
+      ra.kfd[ra.nk] = make_fastdiv(n);
+      ra.kg[ra.nk] = (int32_t)c.s[0][d];
+      ra.ksm[ra.nk] = small_op >= 0 ? (int32_t)c.s[small_op][d] : 0;
+      ra.kout[ra.nk] = (int32_t)c.s[kept_op][d];
+      ++ra.nk;
+      blocks *= n;
+    } else {
+      ra.rn[ra.nr] = n;
+      ra.rfd[ra.nr] = make_fastdiv(n);
+      ra.rg[ra.nr] = (int32_t)c.s[0][d];
+      ++ra.nr;
+      runs *= n;
+    }
+  }
+  ra.n0 = (int32_t)c.n[R - 2];
+  ra.n1 = (int32_t)c.n[R - 1];
+  ra.k0 = c.s[kept_op][R - 2] != 0;
+  ra.k1 = c.s[kept_op][R - 1] != 0;
+  ra.sm0 = small_op >= 0 ? (int32_t)c.s[small_op][R - 2] : 0;
+  ra.sm1 = small_op >= 0 ? (int32_t)c.s[small_op][R - 1] : 0;
+  ra.out0 = (int32_t)c.s[kept_op][R - 2];
+  ra.out1 = (int32_t)c.s[kept_op][R - 1];
+  ra.blocks = (int32_t)blocks;
+  ra.runs = (int32_t)runs;
+  ra.slots = kRunBlk / (ra.n0 * ra.n1);
+  if (ra.slots < 1 || c.s[0][R - 1] != 1 || c.s[0][R - 2] != ra.n1) return hipErrorInvalidValue;
+  ra.write_big = write_big ? 1 : 0;
+  ra.big_acc = big_acc;
+  ra.neg = neg ? 1 : 0;
+  ra.has_div = mean_count >= 0.0 ? 1 : 0;
+  ra.div = mean_count;
+  const unsigned grid = gridn(blocks, 1);
+  ProfScope prof(K_RED_RUN);
+  auto go = [&](auto OPc, auto EPIc, auto Wc, auto IDc) -> hipError_t {
+    constexpr int OP = decltype(OPc)::value, EPI = decltype(EPIc)::value;
+    constexpr int W = decltype(Wc)::value, ID = decltype(IDc)::value;
+    ZK_LAUNCH(prof, (k_red_run<OP, EPI, W, ID>), dim3(grid), dim3(kRunBlk), 0, st, g, a, b, gbig,
+              accbig, out, acc, ra);
+    return hipGetLastError();
+  };
+  if (ident) return go(IC<ZK_ADD>{}, IC<ZK_EPI_NONE>{}, IC<1>{}, IC<1>{});
+  return op_epi(op, epi, [&](auto OPc, auto EPIc) -> hipError_t {
+    return which == 0 ? go(OPc, EPIc, IC<0>{}, IC<0>{}) : go(OPc, EPIc, IC<1>{}, IC<0>{});
+  });
+}
+
 static int acc_mode(const float *acc, const float *g) {
   if (!acc) return 0;
   return acc == g ? 1 : 2;
@@ -1283,7 +1506,6 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
   // kernel that streams all of g in the output layout with 128-bit accesses
   // (or any layout for the scalar element-wise kernel); otherwise it gets a
   // pass of its own at the end.
-  GcOut gco{nullptr, nullptr, c_sign};
   bool gc_done = grad_c == nullptr;
   const bool gc_al = al16p(grad_c) && al16p(acc_c);
   // Element-wise gradients of full-shape operands.
@@ -1348,6 +1570,13 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
          (rp.kernel == K_RED_ROWD && rp.kept > 0))) {
       go = GcOut{grad_c, acc_c, c_sign};
       gc_done = true;
+    }
+    if (rp.kernel == K_RED_RUN) {
+      e = launch_run(rp, c, 3 + sw, 1 + sw, op, epi, false, sw, g, a, b, gbig, accbig,
+                     p.fused_big ? acc_mode(accbig, g) : 0, p.fused_big, gsmall, accsmall, false,
+                     -1.0, st);
+      if (e != hipSuccess) return e;
+      continue;
     }
     if (rp.kernel == K_RED_GEND) {
       e = launch_gend(rp, c, p.idx64, 3 + sw, 1, 2, op, epi, false, sw, g, a, b, gbig, accbig,
@@ -1489,6 +1718,12 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
         e = launch_final(rp, part, acc, out, st, neg, mean_count);
         if (e != hipSuccess) return e;
       }
+      continue;
+    }
+    if (rp.kernel == K_RED_RUN) {
+      hipError_t e = launch_run(rp, c, 4, -1, ZK_ADD, ZK_EPI_NONE, true, 1, in, nullptr, nullptr,
+                                nullptr, nullptr, 0, false, out, acc, neg, mean_count, st);
+      if (e != hipSuccess) return e;
       continue;
     }
     if (rp.kernel == K_RED_GEND) {

@@ -14,7 +14,7 @@ const char *kernel_name(int32_t k) {
       "fwd2_generic",   "bwd_signed",    "copy_row",   "copy_tile",
       "copy_generic",   "norm_part",     "norm_final", "clip_scale",
       "red_rowd",       "red_gend",      "row_moments", "row_softmax",
-      "red_rowseg"};
+      "red_rowseg",     "red_run"};
   if (k < 0 || k >= K_COUNT) return "none";
   return names[k];
 }
@@ -514,6 +514,32 @@ static bool col_sub_fits(int64_t rows, int64_t cols, int64_t C, RedPlan *rp) {
   return true;
 }
 
+// The one-pass run reduction (red_run) when the two innermost canonical dims
+// form a run of kRunMinLen..kRunMaxLen elements that the source (op 0) and,
+// when read, the full operand `big_op` walk densely, and the outer kept dims
+// give at least kRunMinBlocks blocks; false leaves rp alone.  o: the reduced
+// gradient's stride set (0 on reduced dims).
+static bool size_run(const Canon &c, int o, int big_op, bool src_flat, bool idx64,
+                     RedPlan *rp) {
+  if (idx64 || !src_flat || c.rank < 3) return false;
+  if (big_op >= 0 && !is_flat(c, big_op)) return false;
+  const int R = c.rank;
+  const int64_t L = c.n[R - 2] * c.n[R - 1];
+  if (L < kRunMinLen || L > kRunMaxLen) return false;
+  int64_t blocks = 1, runs = 1, kept = 1;
+  for (int k = 0; k < R; ++k) {
+    if (c.s[o][k] != 0) kept *= c.n[k];
+    if (k < R - 2) (c.s[o][k] != 0 ? blocks : runs) *= c.n[k];
+  }
+  if (blocks < kRunMinBlocks || runs < 2) return false;
+  rp->kernel = K_RED_RUN;
+  rp->kept = kept;
+  rp->red = c.numel / kept;
+  rp->chunk = L;
+  rp->partials = 0;
+  return true;
+}
+
 // Try the fast stage-1 classes for the reduced operand stride set `o`
 // (grad layout) with `big` the dense operand id (or -1 if none is read).
 // Requires the source (op 0) to be dense.
@@ -683,6 +709,20 @@ zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
         return ZK_OK;
       }
     }
+    // A short contiguous inner run: one pass reading every element once, that
+    // also writes the full operand's gradient.
+    {
+      RedPlan rr;
+      const int run_big = big_read ? 1 + bw : -1;
+      if ((!big_read || big_full) && (big_full || !big_write) &&
+          size_run(c, 3 + sw, run_big, true, p->idx64, &rr)) {
+        rr.which = sw;
+        p->red[p->nred++] = rr;
+        p->fused_big = big_write;
+        finish_workspace(p);
+        return ZK_OK;
+      }
+    }
     // Moderate term counts: one gather pass that also writes the full
     // operand's gradient.
     {
@@ -803,6 +843,9 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;
+  } else if (K < c.numel && size_run(c, 4, -1, src_flat, p->idx64, &rp)) {
+    rp.which = 1;
+    p->red[p->nred++] = rp;
   } else {
     RedPlan &q = p->red[p->nred++];
     if (!size_gend(&q, K, c.numel / K)) size_generic(&q, K, c.numel / K);

@@ -41,6 +41,12 @@ constexpr int64_t kDirRowSumMaxElems = (int64_t)1 << 24;
 // red_gend: terms per kept element it takes (a wave walks them, 64 at a time).
 constexpr int64_t kGenDirMinTerms = 32;
 constexpr int64_t kGenDirMaxTerms = 4096;
+// red_run: the run (the two innermost canonical dims) holds 64..256 elements
+// (at least one whole run for each 256-lane block), and the outer kept dims
+// give at least this many blocks.
+constexpr int64_t kRunMinLen = 64;
+constexpr int64_t kRunMaxLen = 256;
+constexpr int64_t kRunMinBlocks = 32;
 
 // Kernel classes (ids reported by zk_plan_describe).
 enum KernelClass : int32_t {
@@ -70,7 +76,9 @@ enum KernelClass : int32_t {
   K_ROW_MOMENTS = 22,  // per-row mean and variance, a wave per row
   K_ROW_SOFTMAX = 23,  // per-row max and sum of exponentials, a wave per row
   K_RED_ROWSEG = 24,   // sums of short dense rows (C <= 256), 256/C rows a wave
-  K_COUNT = 25
+  K_RED_RUN = 25,      // two innermost dims a short contiguous run: a block per
+                       // outer kept combination, every element read once, one pass
+  K_COUNT = 26
 };
 
 const char *kernel_name(int32_t k);

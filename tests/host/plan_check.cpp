@@ -224,6 +224,20 @@ int main() {
           if (rp.red < kGenDirMinTerms || rp.red > kGenDirMaxTerms) return fail("gend terms", rp.red, 0);
           break;
         }
+        case K_RED_RUN: {
+          // the two innermost dims form a dense run of 64..256 elements, 32-bit
+          // offsets, at least kRunMinBlocks blocks and two runs a block
+          const int64_t L = c.n[c.rank - 1] * (c.rank >= 2 ? c.n[c.rank - 2] : 1);
+          if (rp.partials != 0 || rp.kept * rp.red != c.numel || rp.chunk != L)
+            return fail("run cover", rp.kept, rp.red);
+          if (c.rank < 3 || L < kRunMinLen || L > kRunMaxLen || p.idx64) return fail("run shape", L, c.rank);
+          if (c.s[0][c.rank - 1] != 1 || c.s[0][c.rank - 2] != c.n[c.rank - 1]) return fail("run dense", 0, 0);
+          const int ko = rp.which == 0 ? 3 : 4;
+          int64_t blocks = 1, runs = 1;
+          for (int k = 0; k < c.rank - 2; ++k) (c.s[ko][k] != 0 ? blocks : runs) *= c.n[k];
+          if (blocks < kRunMinBlocks || runs < 2 || blocks * runs * L != c.numel) return fail("run blocks", blocks, runs);
+          break;
+        }
         case K_RED_TILE: {
           if (c.rank != 2 || c.n[1] % 4 != 0) return fail("tile shape", c.rank, c.n[1]);
           if (rp.partials != (c.n[0] + 63) / 64) return fail("tile partials", rp.partials, 0);
@@ -240,7 +254,7 @@ int main() {
     }
     if (p.workspace < need) return fail("workspace", (long long)p.workspace, (long long)need);
   }
-  for (int k : {K_RED_COL, K_RED_ROW, K_RED_ROWD, K_RED_GEND, K_RED_TILE, K_RED_GENERIC})
+  for (int k : {K_RED_COL, K_RED_ROW, K_RED_ROWD, K_RED_GEND, K_RED_RUN, K_RED_TILE, K_RED_GENERIC})
     if (k != K_RED_TILE && seen[k] == 0) return fail("class never planned", k, 0);
   // 4. forward plans: the dense operand of fwd_row walks the output layout,
   //    128-bit paths only on multiples of 4 and aligned pointers, rank <= 3

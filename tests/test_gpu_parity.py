@@ -792,8 +792,7 @@ def test_one_pass_row_reduction_fused(orc, op2):
 # One-pass gather reductions (32..4096 terms per kept element on patterns
 # the streaming classes do not take): a wave per kept element, also writing
 # the full operand's gradient.
-GEND_SHAPES = [((2, 3, 4, 5, 6, 7, 8, 9), (1, 3, 1, 5, 1, 7, 1, 9)),  # the rank-8 workload
-               ((40, 3, 7), (1, 3, 1)),       # T = 280, inner dim reduced but short
+GEND_SHAPES = [((40, 3, 7), (1, 3, 1)),       # T = 280, inner dim reduced but short
                ((5, 64, 3), (5, 1, 3)),       # middle dim reduced: T = 64
                ((4096, 3), (1, 3)),           # T = 4096, inner 3
                ((33, 5), (1, 5))]             # T = 33
@@ -828,6 +827,55 @@ def test_one_pass_gather_reduction(orc, shapes, op):
     _, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), need_a=False)
     _, rb = orc.bwd(op, g, a, b, want=(False, True))
     assert_bwd(host(gb), rb, f"{op} b only")
+
+
+# One-pass run reductions: the two innermost canonical dims form a short
+# contiguous run ([reduced, kept] or [kept, reduced], 64..256 elements), a
+# block per combination of the outer kept dims reading every element once.
+RUN_SHAPES = [((2, 3, 4, 5, 6, 7, 8, 9), (1, 3, 1, 5, 1, 7, 1, 9)),  # the rank-8 workload: run [8, 9]
+              ((4, 40, 6, 12), (1, 40, 1, 12)),          # run [6 reduced, 12 kept]
+              ((2, 33, 3, 4, 16), (1, 33, 1, 4, 1)),     # run [4 kept, 16 reduced]
+              ((6, 40, 3, 8, 8), (1, 40, 1, 8, 8))]      # run [3 reduced, 64 kept] (8 x 8 merged)
+
+
+@pytest.mark.parametrize("shapes", RUN_SHAPES)
+@pytest.mark.parametrize("op", OPS)
+def test_one_pass_run_reduction(orc, shapes, op):
+    sa, sb = shapes
+    info = zk.plan_describe("bwd", op, zk.make_desc(sa), zk.make_desc(sb))
+    assert info["kernel"] == "red_run", info
+    a, b = _rng_pair(sa, sb, seed=sum(sa) + OPS.index(op) + 7)
+    check_pair(orc, op, a, dev(a), b, dev(b), seed=17)
+    if op in ("add", "mul"):
+        check_pair(orc, op, a, dev(a), b, dev(b), seed=18, epi="gelu")
+    rng = np.random.default_rng(sum(sa) + 3)
+    g = rng.standard_normal(sa).astype(np.float32)
+    acc_a = rng.standard_normal(sa).astype(np.float32)
+    acc_b = rng.standard_normal(sb).astype(np.float32)
+    ga, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), acc_a=dev(g), acc_b=dev(acc_b))
+    ra, rb = orc.bwd(op, g, a, b, acc_a=g, acc_b=acc_b)
+    assert_bwd(host(ga), ra, f"{op} acc_a=g")
+    assert_bwd(host(gb), rb, f"{op} acc_b")
+    xa, xb = dev(acc_a), dev(acc_b)
+    zk.binary_bwd(op, dev(g), dev(a), dev(b), grad_a=xa, acc_a=xa, grad_b=xb, acc_b=xb)
+    ra, rb = orc.bwd(op, g, a, b, acc_a=acc_a, acc_b=acc_b)
+    assert_bwd(host(xa), ra, f"{op} in-place a")
+    assert_bwd(host(xb), rb, f"{op} in-place b")
+    _, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), need_a=False)
+    _, rb = orc.bwd(op, g, a, b, want=(False, True))
+    assert_bwd(host(gb), rb, f"{op} b only")
+    # the same pattern with a as the broadcast operand
+    ga, gb = zk.binary_bwd(op, dev(g), dev(b), dev(a))
+    ra, rb = orc.bwd(op, g, b, a)
+    assert_bwd(host(ga), ra, f"{op} swapped grad_a")
+    assert_bwd(host(gb), rb, f"{op} swapped grad_b")
+    # reduce and mean through the same class, and twice for determinism
+    info = zk.plan_describe("reduce", "add", zk.make_desc(sa), zk.make_desc(sb))
+    assert info["kernel"] == "red_run", info
+    r1 = host(zk.reduce_to_shape(dev(g), sb))
+    assert_bwd(r1, orc.reduce_to_shape(g, sb), "reduce")
+    assert np.array_equal(r1.view(np.uint32), host(zk.reduce_to_shape(dev(g), sb)).view(np.uint32))
+    assert_bwd(host(zk.mean_to_shape(dev(g), sb)), orc.mean_to_shape(g, sb), "mean")
 
 
 def test_one_pass_gather_reduce_mean_and_fused(orc):

@@ -366,7 +366,7 @@ WORKLOAD_PLANS = [
     ("fwd", "div", "none", ((2, 3, 4, 5, 6, 7, 8, 9), None), ((1, 3, 1, 5, 1, 7, 1, 9), None),
      "fwd_generic", (2, 3, 4, 5, 6, 7, 8, 9), (0, 315, 0, 63, 0, 9, 0, 1)),
     ("bwd", "div", "none", ((2, 3, 4, 5, 6, 7, 8, 9), None), ((1, 3, 1, 5, 1, 7, 1, 9), None),
-     "red_gend", (2, 3, 4, 5, 6, 7, 8, 9), (0, 315, 0, 63, 0, 9, 0, 1)),
+     "red_run", (2, 3, 4, 5, 6, 7, 8, 9), (0, 315, 0, 63, 0, 9, 0, 1)),
     ("fwd", "mul", "none", ((16, 2048, 4096), None), ((4096,), None), "fwd_row",
      (32768, 4096), (0, 1)),
     ("fwd", "add", "none", ((16, 2048, 4096), None), ((16, 2048, 4096), None), "fwd_flat",
