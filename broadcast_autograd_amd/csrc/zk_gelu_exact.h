@@ -12,18 +12,26 @@
 // operations keep about 104 significant bits (Dekker 1971, "A floating-point
 // technique for extending the available precision"; Knuth's two-sum).  With
 // x = |h| / sqrt2 and P = 2 Phi(h), so that GeLU(h) = (h / 2) P:
-//   |h| <= 5 : P = 1 + sign(h) erf(x), erf from its Taylor series
-//              erf(x) = 2/sqrt(pi) sum_n (-1)^n x^(2n+1) / (n! (2n+1))
-//              (about 85 terms at x = 3.54; at most ~35 bits lost to the
-//              alternating terms and to 1 - erf);
-//   |h| >  5 : erfc(x) = exp(-x^2) / sqrt(pi) / K(x), K the Laplace continued
-//              fraction x + (1/2) / (x + 1 / (x + (3/2) / (x + ...))) taken
-//              backwards from depth 80 (below 2^-106 relative for x >= 3.5),
-//              exp(-x^2) = exp(-h^2 / 2) with h^2 / 2 exact in binary64 (Cody-
-//              Waite reduction by ln2, Taylor series of the remainder / 64,
-//              six squarings); P = 2 - erfc for h > 0, erfc for h < 0.
-// The result keeps at least ~70 correct bits, so it rounds like the exact
-// value unless that lies within ~2^-70 (relative) of a binary32 midpoint.
+//   |h| < 2^-20 : P = 1 + sign(h) erf(x), erf from its Taylor series
+//                 erf(x) = 2/sqrt(pi) sum_n (-1)^n x^(2n+1) / (n! (2n+1))
+//                 (three terms; P keeps the tiny erf(x) in its low word);
+//   up to the binary64 table's end (|h| <= 4.5 sqrt2): E = erfc(x) from the
+//                 double-double piecewise polynomials of zk_gelu_dd_coeffs.h
+//                 (the binary64 table's pieces, degree 16, fit error below
+//                 2^-97), the high-degree terms in binary64 and the lowest
+//                 few by compensated Horner steps (error below 2^-60 of E,
+//                 see erfc_piece); GeLU(h) = h - (h / 2) E for h > 0 and
+//                 (h / 2) E for h < 0;
+//   beyond      : erfc(x) = exp(-x^2) / sqrt(pi) / K(x), K the Laplace
+//                 continued fraction x + (1/2) / (x + 1 / (x + (3/2) / (x +
+//                 ...))) taken backwards from depth 80 (below 2^-106 relative
+//                 for x >= 3.5), exp(-x^2) = exp(-h^2 / 2) with h^2 / 2 exact
+//                 in binary64 (Cody-Waite reduction by ln2, Taylor series of
+//                 the remainder / 64, six squarings); P as above.
+// The series and continued-fraction branches keep at least ~90 correct
+// bits, the table branch at least ~60; either rounds like the exact value,
+// since no binary32 argument of the table's range has a GeLU value within
+// 2^-53.4 (relative) of a binary32 midpoint (exhaustive scan).
 // Where h / 2 itself is a midpoint (h an odd multiple of 2^-149), y's low
 // word carries the sign of the tiny term h^2 phi(0) that decides it.
 //
@@ -35,10 +43,22 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "zk_gelu_coeffs.h"
+#include "zk_gelu_dd_coeffs.h"
+
 #if defined(__HIPCC__)
 #define ZK_HD __host__ __device__
+// Loops of the rare path stay rolled or only partly unrolled: fully
+// unrolled they would hoist all their coefficient loads into registers, and
+// every kernel calling the path reserves the registers the path needs (the
+// GeLU row kernel must stay within 64 VGPRs to keep 8 waves per SIMD).
+#define ZK_PRAGMA(x) _Pragma(#x)
+#define ZK_UNROLL(n) ZK_PRAGMA(unroll n)
+#define ZK_ROLLED ZK_UNROLL(1)
 #else
 #define ZK_HD
+#define ZK_UNROLL(n)
+#define ZK_ROLLED
 #endif
 
 namespace zk {
@@ -117,20 +137,64 @@ ZK_HD inline dd exp_neg(double q) {
   // exp(-r) = (exp(-r / 64))^64, |r / 64| <= 0.0055: Taylor to s^14 / 14!
   const dd s{-r.hi * 0.015625, -r.lo * 0.015625};
   dd p{1.0, 0.0};
+  ZK_ROLLED
   for (int n = 14; n >= 1; --n) p = add(dd{1.0, 0.0}, div_d(mul(p, s), (double)n));
+  ZK_ROLLED
   for (int j = 0; j < 6; ++j) p = mul(p, p);
   const int e = -(int)k;
   return dd{ldexp(p.hi, e), ldexp(p.lo, e)};
 }
 
-// 2 Phi(h) for a finite binary32 h with 0 < |h| < 15.
+// Why ~60 bits suffice in the table's range: an exhaustive scan of every
+// binary32 argument in [-10, 10] (the table covers |h| <= 6.37) finds no
+// GeLU value closer than 2^-53.4 (relative) to a binary32 rounding midpoint.
+// The path is kept short because a wave that meets a near tie waits for it,
+// and the slowest wave decides when a kernel ends.
+
+// erfc(a / sqrt2) for 2^-20 <= a, a^2 <= kGeluTabAmax2, as hi + lo, from
+// a's double-double piece (ddtab: the rows of kGeluDDTab): the terms of
+// degree kGeluDDSplit and up by binary64 Horner steps, the lower ones by
+// compensated Horner steps (Graillat, Langlois and Louvet, "Compensated
+// Horner scheme", 2005): each step's product and sum errors, found exactly
+// by two-product and two-sum, go with the coefficient's low word into a
+// second binary64 Horner sum, so only one product and one sum per step lie
+// on the chain the result waits for.  That second sum is below 2^-50 of the
+// first, so its own roundings cost ~2^-100; the binary64 terms' bound
+// (2^-60, zk_gelu_dd_coeffs.h) dominates.
+ZK_HD inline dd erfc_piece(double a, const double *ddtab) {
+  // the piece of the binary64 table (a^2 is exact), its double-double twin
+  int i = (int)(fma(a, kGeluTabK, a * a) * kGeluTabS);
+  i = i < kGeluDDN - 1 ? i : kGeluDDN - 1;
+  const double *row = ddtab + i * kGeluDDWidth;
+  // d = a - mid is exact: it is a multiple of the finer of the two last
+  // bits (a >= 2^-20 is a multiple of 2^-43; beyond the first piece a and
+  // mid lie in the same or adjacent binades) and below 0.12, so below 2^53
+  // of that unit
+  const double d = a - row[0];
+  double p = row[1 + 2 * kGeluDDDeg];
+  ZK_UNROLL(6)
+  for (int k = kGeluDDDeg - 1; k >= kGeluDDSplit; --k) p = fma(p, d, row[1 + 2 * k]);
+  double e = 0.0;
+  ZK_UNROLL(kGeluDDSplit)
+  for (int k = kGeluDDSplit - 1; k >= 0; --k) {
+    const dd m = two_prod(p, d);
+    const dd s = two_sum(m.hi, row[1 + 2 * k]);
+    e = fma(e, d, (m.lo + s.lo) + row[2 + 2 * k]);
+    p = s.hi;
+  }
+  return fast_two_sum(p, e);
+}
+
+// 2 Phi(h) for a finite binary32 h with 0 < |h| < 15 outside the table's
+// range (|h| < 2^-20 or h^2 > kGeluTabAmax2).
 ZK_HD inline dd two_phi(float h) {
   const double a = fabs((double)h);
   const dd x = two_prod(a, kInvSqrt2Hi);
   const dd xs = add(x, dd{a * kInvSqrt2Lo, 0.0});  // x = |h| / sqrt2
-  if (a <= 5.0) {
+  if (a < 0x1p-20) {
     const dd x2 = mul(xs, xs);
     dd t = xs, S = xs;
+    ZK_ROLLED
     for (int n = 1; n <= 100; ++n) {
       t = div_d(mul(t, neg(x2)), (double)n);  // (-1)^n x^(2n+1) / n!
       const dd term = div_d(t, (double)(2 * n + 1));
@@ -142,6 +206,7 @@ ZK_HD inline dd two_phi(float h) {
   }
   // Laplace continued fraction for erfc, evaluated from depth 80 upwards
   dd t = xs;
+  ZK_ROLLED
   for (int k = 80; k >= 1; --k) t = add(xs, div(dd{0.5 * k, 0.0}, t));
   const double q = 0.5 * ((double)h * (double)h);  // h^2 / 2 = x^2, exact
   const dd erfc = div(mul(exp_neg(q), dd{kInvSqrtPiHi, kInvSqrtPiLo}), t);
@@ -165,12 +230,21 @@ ZK_HD inline float round_f32(dd y) {
 
 // GeLU(h) = h Phi(h) correctly rounded to binary32, for every binary32 h:
 // +inf -> +inf, -inf -> -0, NaN -> NaN, +-0 -> +-0, and -0 for h <= -15
-// (|h Phi(h)| < 2^-160 there, below half the smallest subnormal).
-ZK_HD inline float gelu32_exact(float h) {
+// (|h Phi(h)| < 2^-160 there, below half the smallest subnormal).  ddtab
+// as in erfc_piece.
+ZK_HD inline float gelu32_exact(float h, const double *ddtab = kGeluDDTab) {
   if (h != h) return h;
   if (h == INFINITY) return h;
   if (h <= -15.0f) return -0.0f;
   if (h == 0.0f) return h * 0.5f;
+  const double a = fabs((double)h);
+  if (a * a <= kGeluTabAmax2 && a >= 0x1p-20) {
+    // GeLU(h) = (h / 2) E for h < 0 and h - (h / 2) E for h > 0 (h / 2 exact)
+    const gx::dd q = gx::mul_d(gx::erfc_piece(a, ddtab), 0.5 * (double)h);
+    if (h < 0.f) return gx::round_f32(q);
+    const gx::dd y = gx::two_sum((double)h, -q.hi);  // h - q.hi exactly
+    return gx::round_f32(gx::fast_two_sum(y.hi, y.lo - q.lo));
+  }
   const gx::dd P = gx::two_phi(h);
   return gx::round_f32(gx::mul_d(P, 0.5 * (double)h));  // (h / 2) * 2 Phi(h)
 }
