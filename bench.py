@@ -63,19 +63,6 @@ MAX_SETS = 32
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "hbm_traffic.fetch_write_counters.txt")
 
-def source_hash():
-    import glob
-    import hashlib
-    h = hashlib.sha256()
-    root = os.path.dirname(os.path.abspath(__file__))
-    # device code, kernel argument blocks and the planner decide the traffic
-    for p in sorted(glob.glob(os.path.join(root, "broadcast_autograd_amd", "csrc", "*"))):
-        if p.endswith((".hip", ".h")) or p.endswith("zk_plan.cpp"):
-            with open(p, "rb") as f:
-                h.update(f.read())
-    return h.hexdigest()
-
-
 def read_traffic(workload, kernel):
     """Counter-measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each
     scaled by a plain copy of known size), or None when the kernels changed
@@ -85,6 +72,7 @@ def read_traffic(workload, kernel):
             lines = f.read().splitlines()
     except OSError:
         return None
+    from broadcast_autograd_amd.profsum import source_hash
     cur = source_hash()
     for ln in lines:
         p = ln.split()
