@@ -60,24 +60,24 @@ ALL = ["xy_plus_x", "mlp_bias_gelu", "attn_scale_mask", "strided_transposed",
        "attn_mask_grad"]
 ROTATE_BYTES = 1 << 30  # per-workload footprint of the rotating buffer sets
 MAX_SETS = 32
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "hbm_traffic.fetch_write_counters.txt")
+# counter summaries whose `traffic` lines give HBM bytes per launch
+TRAFFIC_GLOB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "*.fetch_write_counters.txt")
 
 def read_traffic(workload, kernel):
     """Counter-measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each
     scaled by a plain copy of known size), or None when the kernels changed
     since the counters were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            lines = f.read().splitlines()
-    except OSError:
-        return None
+    import glob
     from broadcast_autograd_amd.profsum import source_hash
-    cur = source_hash()
-    for ln in lines:
-        p = ln.split()
-        if len(p) == 5 and p[0] == "traffic" and p[1] == workload and p[2] == kernel:
-            return int(p[3]) if p[4] == cur else None
+    cur = None
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        with open(path) as f:
+            for ln in f:
+                p = ln.split()
+                if len(p) == 5 and p[0] == "traffic" and p[1] == workload and p[2] == kernel:
+                    cur = cur or source_hash()
+                    return int(p[3]) if p[4] == cur else None
     return None
 
 

@@ -2,7 +2,7 @@
 
     python -m broadcast_autograd_amd.profsum stats DIR [--title T] [--cmd C]
     python -m broadcast_autograd_amd.profsum counters --fetch DIR --write DIR
-        --calib KERNEL:GRID:BYTES [--check KERNEL:GRID:BYTES ...]
+        --calib KERNEL:GRID:BYTES [--check KERNEL:GRID:BYTES[:FIRST_N] ...]
         [--traffic WORKLOAD:CLASS:GRID ...] [--cmd C ...]
     python -m broadcast_autograd_amd.profsum pmc DIR [--per-element GRID:ELEMENTS ...]
 
@@ -13,7 +13,9 @@ dispatch, each counter scaled by what it reads for a copy of known size (the
 calibration kernel and grid; another copy's factors are printed beside them
 as a cross-check), and emits `traffic` lines for the benchmark
 keyed to a hash of the kernel sources.  `pmc` averages any counters per
-(kernel, grid) and, given the elements a grid processes, per element.
+(kernel, grid) and, given the elements a grid processes, per element (an
+SQ_INSTS_* count is of wave instructions, each serving 64 lanes, so per
+element it is 64 times the count over the elements).
 Only the CSV files rocprofv3 writes are read; nothing is executed.
 """
 import argparse
@@ -71,6 +73,8 @@ def cmd_stats(a):
     out = []
     if a.title:
         out.append(f"# {a.title}")
+    for n in a.note or []:
+        out.append(f"# {n}")
     for c in a.cmd or []:
         out.append(f"# command: {c}")
     out.append("# one line per kernel: calls, average / min / max duration (us), share of GPU time")
@@ -86,14 +90,22 @@ def cmd_stats(a):
     print("\n".join(out))
 
 
-def read_counters(d):
-    """{(kernel, grid): {counter: [value per dispatch]}} from a --pmc run."""
-    acc = defaultdict(lambda: defaultdict(list))
+def read_counters(d, first=None):
+    """{(kernel, grid): {counter: [value per dispatch]}} from a --pmc run, in
+    dispatch order; with first = {(kernel, grid): n}, only the first n
+    dispatches of those groups."""
+    rows = []
     for p in find_csv(d, "counter_collection.csv"):
         with open(p, newline="") as f:
             for r in csv.DictReader(f):
-                key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
-                acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                rows.append((int(r["Dispatch_Id"]), (short_name(r["Kernel_Name"]), int(r["Grid_Size"])),
+                             r["Counter_Name"], float(r["Counter_Value"])))
+    rows.sort(key=lambda t: t[0])
+    acc = defaultdict(lambda: defaultdict(list))
+    for _, key, name, v in rows:
+        if first and key in first and len(acc[key][name]) >= first[key]:
+            continue
+        acc[key][name].append(v)
     return acc
 
 
@@ -119,15 +131,23 @@ def cmd_counters(a):
     out.append(f"#   reads FETCH_SIZE {f_cal / 1024:.1f} KiB and WRITE_SIZE {w_cal / 1024:.1f} KiB")
     out.append(f"#   -> scale factors fetch x{ff:.4f}, write x{fw:.4f} (applied below)")
     for chk in a.check or []:
-        k2, g2, b2 = chk.rsplit(":", 2)
-        g2, b2 = int(g2), int(b2)
+        # NAME:GRID:BYTES[:N] -- the first N dispatches of that kernel and grid
+        parts = chk.split(":")
+        n2 = None
+        if len(parts) >= 4 and parts[-1].isdigit() and parts[-2].isdigit() and parts[-3].isdigit():
+            n2 = int(parts[-1])
+            parts = parts[:-1]
+        k2, g2, b2 = ":".join(parts[:-2]), int(parts[-2]), int(parts[-1])
+        sel = {(k2, g2): n2} if n2 else None
+        f2d, w2d = read_counters(a.fetch, sel), read_counters(a.write, sel)
         try:
-            f2 = mean(fetch[(k2, g2)]["FETCH_SIZE"]) * 1024
-            w2 = mean(write[(k2, g2)]["WRITE_SIZE"]) * 1024
+            f2 = mean(f2d[(k2, g2)]["FETCH_SIZE"]) * 1024
+            w2 = mean(w2d[(k2, g2)]["WRITE_SIZE"]) * 1024
         except KeyError:
             sys.exit(f"cross-check kernel {k2} with grid {g2} not found")
-        out.append(f"# cross-check: {k2} grid {g2}, a copy of {b2 // 2} bytes each way, gives "
-                   f"fetch x{(b2 / 2) / f2:.4f}, write x{(b2 / 2) / w2:.4f}")
+        which = f"the first {n2} dispatches of " if n2 else ""
+        out.append(f"# cross-check: {which}{k2} grid {g2}, a copy of {b2 // 2} bytes each way,")
+        out.append(f"#   gives fetch x{(b2 / 2) / f2:.4f}, write x{(b2 / 2) / w2:.4f}")
     h = source_hash()
     out.append(f"# source_sha256 {h}")
     out.append("#")
@@ -159,7 +179,7 @@ def cmd_pmc(a):
         g, n = s.split(":")
         per[int(g)] = int(n)
     names = sorted({c for v in acc.values() for c in v})
-    out = []
+    out = [f"# {n}" for n in a.note or []]
     for c in a.cmd or []:
         out.append(f"# command: {c}")
     out.append("# mean per dispatch (and per element where the grid's element count is given)")
@@ -171,7 +191,12 @@ def cmd_pmc(a):
         for c in names:
             if c in acc[k]:
                 v = mean(acc[k][c])
-                extra = f"   {v / per[k[1]]:.3f} per element" if k[1] in per else ""
+                extra = ""
+                if k[1] in per:
+                    # a wave instruction serves 64 lanes: per element it is
+                    # 64 / elements of the count
+                    f = 64.0 if c.startswith("SQ_INSTS") else 1.0
+                    extra = f"   {v * f / per[k[1]]:.3f} per element"
                 out.append(f"    {c:<28} {v:>16.1f}{extra}")
     print("\n".join(out))
 
@@ -183,6 +208,7 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--title")
     s.add_argument("--cmd", action="append")
+    s.add_argument("--note", action="append")
     s.add_argument("--only")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
@@ -195,6 +221,7 @@ def main(argv=None):
     p.add_argument("dir")
     p.add_argument("--per-element", action="append")
     p.add_argument("--cmd", action="append")
+    p.add_argument("--note", action="append")
     p.add_argument("--only")
     a = ap.parse_args(argv)
     {"stats": cmd_stats, "counters": cmd_counters, "pmc": cmd_pmc}[a.what](a)
