@@ -283,6 +283,51 @@ __global__ __launch_bounds__(BLK) __attribute__((amdgpu_waves_per_eu(4))) void k
   }
 }
 
+// ------------------------------------------------------------- bcrows
+// A dense operand of n0 rows of n1 elements (n1 % 4 == 0) combined with one
+// contiguous row vector that every row shares (the other operand's outer
+// stride is 0, as the attention mask [1,1,S,S] against scores [B,H,S,S]): a
+// lane reads a 16-byte piece of the row vector once and applies it to the
+// same piece of kBcRows rows (n0 % kBcRows == 0), so the shared vector crosses
+// the L2 once per kBcRows rows instead of once per row.  Group g of rows
+// covers rows g * kBcRows ...; vector v of the grid is piece v % (n1 / 4) of
+// group v / (n1 / 4).  One binary32 operation per element, as everywhere.
+constexpr int kBcRows = 2;
+struct BcRowsArgs {
+  int64_t n1;     // row length (elements)
+  int64_t total;  // (n0 / kBcRows) * (n1 / 4) vectors
+  uint32_t vpr;   // n1 / 4, 16-byte pieces per row
+  FastDiv fv;     // divides by vpr (32-bit index path)
+};
+
+template <int OP, int EPI, bool SWAP, typename I>
+__global__ __launch_bounds__(kBlock) void k_fwd_bcrows(const float *big, const float *small,
+                                                       float *out, BcRowsArgs ba) {
+  static_assert(EPI != ZK_EPI_GELU, "the GeLU epilogue takes the row kernel");
+  const I n1 = (I)ba.n1;
+  for (int64_t v64 = (int64_t)blockIdx.x * kBlock + threadIdx.x; v64 < ba.total;
+       v64 += (int64_t)gridDim.x * kBlock) {
+    I g;
+    if constexpr (sizeof(I) == 4) g = (I)fdiv(ba.fv, (uint32_t)v64);
+    else g = (I)(v64 / (int64_t)ba.vpr);
+    const I j = ((I)v64 - g * (I)ba.vpr) * 4;
+    const I i0 = g * (I)kBcRows * n1 + j;
+    float4 x[kBcRows];
+#pragma unroll
+    for (int k = 0; k < kBcRows; ++k) x[k] = ld4_nt(big + i0 + (I)k * n1);
+    const float4 sv = ld4(small + j);
+#pragma unroll
+    for (int k = 0; k < kBcRows; ++k) {
+      float4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        el(r, e) = SWAP ? fwd32<OP, EPI>(el(sv, e), el(x[k], e), nullptr)
+                        : fwd32<OP, EPI>(el(x[k], e), el(sv, e), nullptr);
+      st4_nt(out + i0 + (I)k * n1, r);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ tile
 // out[R, C] row-major; T[i, j] at i + j*ld (transposed view); O[i, j] at
 // i*os0 + j*os1.  64x64 tiles (one per block up to the grid cap): T is read
@@ -777,6 +822,29 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
         if (p.small_mode == SM_ARG)
           return p.vec == 1 ? go_sw(IC<1>{}, IC<SM_ARG>{}) : go_sw(IC<4>{}, IC<SM_ARG>{});
         if (p.vec == 1) return go_sw(IC<1>{}, IC<SM_GATHER>{});
+        if constexpr (EPI != ZK_EPI_GELU) {
+          // rows sharing one contiguous row vector: k_fwd_bcrows
+          const int sm = p.swap ? 1 : 2;
+          if (p.small_mode == SM_CONTIG && c.rank == 2 && c.s[sm][0] == 0 &&
+              c.n[0] % kBcRows == 0 && c.n[1] / 4 < ((int64_t)1 << 31)) {
+            BcRowsArgs ba{};
+            ba.n1 = c.n[1];
+            ba.vpr = (uint32_t)(c.n[1] / 4);
+            ba.total = (c.n[0] / kBcRows) * (c.n[1] / 4);
+            ba.fv = make_fastdiv(ba.vpr);
+            const int64_t need = (ba.total + kBlock - 1) / kBlock;
+            const unsigned grid = (unsigned)(need < kMaxBlocks ? need : kMaxBlocks);
+            auto go_bc = [&](auto SWc, auto Ic) -> hipError_t {
+              constexpr bool SW = decltype(SWc)::value != 0;
+              using I = std::conditional_t<decltype(Ic)::value != 0, int64_t, int32_t>;
+              ZK_LAUNCH(prof, (k_fwd_bcrows<OP, EPI, SW, I>), dim3(grid), dim3(kBlock), 0, st,
+                        p.swap ? b : a, p.swap ? a : b, out, ba);
+              return hipGetLastError();
+            };
+            if (p.idx64) return p.swap ? go_bc(IC<1>{}, IC<1>{}) : go_bc(IC<0>{}, IC<1>{});
+            return p.swap ? go_bc(IC<1>{}, IC<0>{}) : go_bc(IC<0>{}, IC<0>{});
+          }
+        }
         switch (p.small_mode) {
           case SM_BCAST: return go_sw(IC<4>{}, IC<SM_BCAST>{});
           case SM_CONTIG: return go_sw(IC<4>{}, IC<SM_CONTIG>{});
