@@ -284,8 +284,8 @@ __global__ __launch_bounds__(BLK) __attribute__((amdgpu_waves_per_eu(4))) void k
 }
 
 // ------------------------------------------------------------- bcrows
-// A dense operand of n0 rows of n1 elements (n1 % 4 == 0) combined with one
-// contiguous row vector that every row shares (the other operand's outer
+// A dense operand of n0 rows of n1 elements (n1 % 4 == 0, n1 >=
+// kBcRowsMinCols) combined with one contiguous row vector that every row shares (the other operand's outer
 // stride is 0, as the attention mask [1,1,S,S] against scores [B,H,S,S]): a
 // lane reads a 16-byte piece of the row vector once and applies it to the
 // same piece of kBcRows rows (n0 % kBcRows == 0), so the shared vector crosses
@@ -293,6 +293,12 @@ __global__ __launch_bounds__(BLK) __attribute__((amdgpu_waves_per_eu(4))) void k
 // covers rows g * kBcRows ...; vector v of the grid is piece v % (n1 / 4) of
 // group v / (n1 / 4).  One binary32 operation per element, as everywhere.
 constexpr int kBcRows = 2;
+// Only for row vectors of at least this many elements (256 KiB): a short
+// vector stays in each CU's L1 and costs nothing to re-read, and there the
+// paired rows only disturb the stream (measured on MI355X: the 4 MiB mask
+// row, add 174-178 -> 171-172 us; gamma[4096] against h[32768, 4096],
+// 169.8 -> 172.8 us, so that one stays on the row kernel).
+constexpr int64_t kBcRowsMinCols = (int64_t)1 << 16;
 struct BcRowsArgs {
   int64_t n1;     // row length (elements)
   int64_t total;  // (n0 / kBcRows) * (n1 / 4) vectors
@@ -826,7 +832,8 @@ hipError_t launch_fwd(const FwdPlan &p, zk_op op, zk_epi epi, const float *a,
           // rows sharing one contiguous row vector: k_fwd_bcrows
           const int sm = p.swap ? 1 : 2;
           if (p.small_mode == SM_CONTIG && c.rank == 2 && c.s[sm][0] == 0 &&
-              c.n[0] % kBcRows == 0 && c.n[1] / 4 < ((int64_t)1 << 31)) {
+              c.n[0] % kBcRows == 0 && c.n[1] >= kBcRowsMinCols &&
+              c.n[1] / 4 < ((int64_t)1 << 31)) {
             BcRowsArgs ba{};
             ba.n1 = c.n[1];
             ba.vpr = (uint32_t)(c.n[1] / 4);

@@ -64,6 +64,25 @@ def test_forward_past_2_31(orc):
     assert_bitexact(_take(out, pos), orc.fwd_at("add", vs, col_np, pos), "fwd_generic 64-bit")
 
 
+def test_shared_row_vector_past_2_31(orc):
+    """A dense [rows, 65536] operand against a shared row vector, 2^31 +
+    131072 elements: the 64-bit index path of the kernel that applies each
+    piece of the vector to two rows."""
+    cols = 1 << 16
+    rows = ((1 << 31) + 2 * cols) // cols  # even
+    v_np = np.random.default_rng(6).standard_normal(cols).astype(np.float32)
+    a = torch.full((rows, cols), -2.5, device="cuda")
+    info = zk.plan_describe("fwd", "sub", zk.desc_of(a), zk.make_desc((cols,)))
+    assert info["index64"] and info["kernel"] == "fwd_row", info
+    out = zk.binary_fwd("sub", dev(v_np), a)  # the row vector first
+    va = orc.View(np.array([-2.5], np.float32), (rows, cols), (0, 0))
+    n = rows * cols
+    rng = np.random.default_rng(7)
+    pos = np.concatenate([np.array([0, cols - 1, cols, (1 << 31) - 1, 1 << 31, n - 1], np.int64),
+                          rng.integers(0, n, 4000)])
+    assert_bitexact(_take(out, pos), orc.fwd_at("sub", v_np, va, pos), "bcrows 64-bit")
+
+
 def test_backward_and_reductions_past_2_31(orc):
     b_np = np.random.default_rng(5).standard_normal(C).astype(np.float32)
     a = torch.full((R, C), 1.5, device="cuda")

@@ -151,6 +151,25 @@ def test_gelu_epilogue(orc, shapes, op):
     check_pair(orc, op, a, dev(a), b, dev(b), epi="gelu", seed=6)
 
 
+@pytest.mark.parametrize("rows,cols", [(2, 65536), (6, 70000), (7, 65536), (4, 262144),
+                                       (6, 65532), (130, 4096), (1, 8)])
+@pytest.mark.parametrize("epi", ["none", "relu"])
+def test_shared_row_vector(orc, rows, cols, epi):
+    """A dense [rows, cols] operand against one contiguous row vector that
+    every row shares (the attention mask's pattern): an even row count with
+    rows of at least 65536 elements takes the kernel that applies each
+    16-byte piece of the vector to two rows; odd row counts and shorter rows
+    the row kernel.  Both operand orders, every op, bit-exact."""
+    rng = np.random.default_rng(zlib.crc32(repr((rows, cols, epi)).encode()))
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    v = (rng.standard_normal(cols) + 2.0).astype(np.float32)
+    e = orc.EPI_RELU if epi == "relu" else orc.EPI_NONE
+    for op in OPS:
+        for x, y in ((a, v), (v, a)):
+            got = gpu_fwd(op, dev(x), dev(y), epi)
+            assert_bitexact(got, orc.fwd(op, x, y, epi=e), f"{op} {x.shape} {y.shape} {epi}")
+
+
 def test_mlp_bias_gelu_config_layout(orc):
     h = W.mlp_bias_gelu(rows=512)
     check_pair(orc, "add", h["act"], dev(h["act"]), h["bias"], dev(h["bias"]),
