@@ -359,6 +359,47 @@ def test_acc_modes(orc):
         assert_bwd(host(ga), ra2, f"{op} acc=grad")
 
 
+@pytest.mark.parametrize("n", [4096, 1001, 3])
+def test_pass_through_gradients(orc, n):
+    """add's gradients and sub's are g and -g (the rules read no operand):
+    one of them requested alone takes the plain copy kernel; with an
+    accumulator buffer, in place, with the accumulator being g itself (the
+    element-wise kernel), a ragged length (scalar tail) and a misaligned
+    view (the element-wise kernel).  The result is exact: compared bit for
+    bit with the oracle's rounded binary64 sum."""
+    rng = np.random.default_rng(n)
+    a = rng.standard_normal(n).astype(np.float32)
+    b = rng.standard_normal(n).astype(np.float32)
+    g = rng.standard_normal(n).astype(np.float32)
+    acc = rng.standard_normal(n).astype(np.float32)
+    ta, tb, tg = dev(a), dev(b), dev(g)
+    for op in ("add", "sub"):
+        for side in (0, 1):
+            need = (side == 0, side == 1)
+            kw = "acc_a" if side == 0 else "acc_b"
+            gkw = "grad_a" if side == 0 else "grad_b"
+            for mode in ("none", "buffer", "in_place", "g"):
+                args = {}
+                acc_np = None
+                if mode == "buffer":
+                    args[kw], acc_np = dev(acc), acc
+                elif mode == "in_place":
+                    x = dev(acc)
+                    args[kw], args[gkw], acc_np = x, x, acc
+                elif mode == "g":
+                    args[kw], acc_np = tg, g
+                got = zk.binary_bwd(op, tg, ta, tb, need_a=need[0], need_b=need[1], **args)[side]
+                want = orc.bwd(op, g, a, b, want=need,
+                               **({kw: acc_np} if acc_np is not None else {}))[side]
+                assert_bitexact(host(got), want.f32, f"{op} side {side} acc {mode}")
+    # a misaligned view of g: the element-wise kernel
+    big = dev(np.concatenate([np.zeros(1, np.float32), g]))
+    gv = big[1:]
+    got = zk.binary_bwd("sub", gv, ta, tb, need_a=False)[1]
+    want = orc.bwd("sub", g, a, b, want=(False, True))[1]
+    assert_bitexact(host(got), want.f32, "sub side 1 misaligned")
+
+
 def test_both_operands_broadcast(orc):
     rng = np.random.default_rng(51)
     for sa, sb in [((300, 1), (1, 200)), ((5, 1, 7), (1, 6, 1)), ((1, 64), (64, 1))]:
