@@ -117,11 +117,10 @@ def cmd_counters(a):
     fetch, write = read_counters(a.fetch), read_counters(a.write)
     ck, cg, cb = a.calib.rsplit(":", 2)
     cg, cb = int(cg), int(cb)
-    try:
-        f_cal = mean(fetch[(ck, cg)]["FETCH_SIZE"]) * 1024
-        w_cal = mean(write[(ck, cg)]["WRITE_SIZE"]) * 1024
-    except KeyError:
+    if not fetch.get((ck, cg), {}).get("FETCH_SIZE") or not write.get((ck, cg), {}).get("WRITE_SIZE"):
         sys.exit(f"calibration kernel {ck} with grid {cg} not found")
+    f_cal = mean(fetch[(ck, cg)]["FETCH_SIZE"]) * 1024
+    w_cal = mean(write[(ck, cg)]["WRITE_SIZE"]) * 1024
     # the copy reads cb / 2 bytes and writes cb / 2
     ff, fw = (cb / 2) / f_cal, (cb / 2) / w_cal
     out = ["# HBM traffic per dispatch from rocprofv3 hardware counters (MI355X)"]
@@ -140,11 +139,10 @@ def cmd_counters(a):
         k2, g2, b2 = ":".join(parts[:-2]), int(parts[-2]), int(parts[-1])
         sel = {(k2, g2): n2} if n2 else None
         f2d, w2d = read_counters(a.fetch, sel), read_counters(a.write, sel)
-        try:
-            f2 = mean(f2d[(k2, g2)]["FETCH_SIZE"]) * 1024
-            w2 = mean(w2d[(k2, g2)]["WRITE_SIZE"]) * 1024
-        except KeyError:
+        if not f2d.get((k2, g2), {}).get("FETCH_SIZE") or not w2d.get((k2, g2), {}).get("WRITE_SIZE"):
             sys.exit(f"cross-check kernel {k2} with grid {g2} not found")
+        f2 = mean(f2d[(k2, g2)]["FETCH_SIZE"]) * 1024
+        w2 = mean(w2d[(k2, g2)]["WRITE_SIZE"]) * 1024
         which = f"the first {n2} dispatches of " if n2 else ""
         out.append(f"# cross-check: {which}{k2} grid {g2}, a copy of {b2 // 2} bytes each way,")
         out.append(f"#   gives fetch x{(b2 / 2) / f2:.4f}, write x{(b2 / 2) / w2:.4f}")
