@@ -417,8 +417,12 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
 // --------------------------------------------------------------- red_row
 // Rows of R0 contiguous reduced elements; row = r1 * K + k.  Work item =
 // (row, chunk of CL elements); one wave per item.
+// Partials are kept-element major, part[k * P + r1 * NC + ch] (P = R1 * NC
+// of them per kept element): the few kept elements of these sums (16 for the
+// attention scale) each own thousands of partials, which stage 2 then reads
+// in contiguous runs.
 struct RowRedArgs {
-  int64_t R0, K, NC, CL, items, ss;
+  int64_t R0, K, NC, CL, items, ss, P;
   int32_t write_big;
 };
 
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(kBlk) void k_red_row(
       }
     }
     s = wave_sum(s);
-    if (l == 0) part[(r1 * ra.NC + ch) * ra.K + k] = s;
+    if (l == 0) part[k * ra.P + r1 * ra.NC + ch] = s;
   }
 }
 
@@ -789,6 +793,7 @@ __global__ __launch_bounds__(kBlk) void k_red_generic(const float *g,
 // an LDS tree.  Adjacent threads own adjacent k, so loads are coalesced.
 struct FinArgs {
   int64_t K, P, per;  // per: partials per thread
+  int64_t ps, ks;     // partial p of kept element k at part[p * ps + k * ks]
   int32_t tpk, kt, has_acc;
   int32_t neg;  // the terms are the negated partials (exact)
   int32_t has_div;
@@ -811,7 +816,7 @@ __global__ __launch_bounds__(kBlk) void k_red_final(const double *part,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t p = q + (j0 + j) * fa.tpk;
-        v[j] = (ok && j0 + j < fa.per && p < fa.P) ? part[p * fa.K + k] : 0.0;
+        v[j] = (ok && j0 + j < fa.per && p < fa.P) ? part[p * fa.ps + k * fa.ks] : 0.0;
       }
       s += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     }
@@ -1019,10 +1024,16 @@ static hipError_t launch_final(const RedPlan &rp, const double *part,
   fa.neg = neg ? 1 : 0;
   fa.K = rp.kept;
   fa.P = rp.partials;
+  // red_row writes its partials kept-element major ([K][P]), every other
+  // stage 1 partial major ([P][K]).
+  const bool kmajor = rp.kernel == K_RED_ROW;
+  fa.ps = kmajor ? 1 : rp.kept;
+  fa.ks = kmajor ? rp.partials : 1;
   // Threads per kept element: enough that each loads about 8 partials, but
-  // at most 16 once there are many kept elements, so that a wave still reads
-  // runs of >= 16 consecutive k (128 B) from each partial row.
-  const int max_tpk = rp.kept >= 1024 ? 16 : 256;
+  // for [P][K] at most 16 once there are many kept elements, so that a wave
+  // still reads runs of >= 16 consecutive k (128 B) from each partial row
+  // ([K][P] runs are contiguous for any count).
+  const int max_tpk = (kmajor || rp.kept < 1024) ? 256 : 16;
   int tpk = 1;
   while (tpk < max_tpk && rp.partials > 8 * (int64_t)tpk) tpk *= 2;
   fa.tpk = tpk;
@@ -1681,6 +1692,7 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ra.CL = rp.chunk;
             ra.NC = (ra.R0 + ra.CL - 1) / ra.CL;
             ra.items = (c.numel / ra.R0) * ra.NC;
+            ra.P = rp.partials;
             ra.ss = R >= 2 ? c.s[1 + sw][R - 2] : 0;
             ra.write_big = p.fused_big;
             unsigned grid = gridn(ra.items, 4);
@@ -1820,6 +1832,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ra.CL = rp.chunk;
           ra.NC = (ra.R0 + ra.CL - 1) / ra.CL;
           ra.items = (c.numel / ra.R0) * ra.NC;
+          ra.P = rp.partials;
           ra.ss = 0;
           ra.write_big = 0;
           ZK_LAUNCH(prof, (k_red_row<ZK_ADD, ZK_EPI_NONE, 1, 0>), dim3(gridn(ra.items, 4)),
