@@ -321,8 +321,15 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
   // rows in flight per wave: two for the plain rules; one with the GeLU
   // epilogue, whose arithmetic is long enough per row (measured: the
-  // [4096, 1024] GeLU step is ~10% faster than with two)
-  constexpr int U = EPI == ZK_EPI_GELU ? 1 : 2;
+  // [4096, 1024] GeLU step is ~10% faster than with two); four where the
+  // 16-wave blocks of a long column sum (one block a CU) also read the full
+  // operand (the [32768, 4096] multiply backward: 274-276 us against
+  // 274-281, the fused one 391-399 against 391-411; a plain sum of g, which
+  // reads one stream, is 3% slower with four).  Within the 128 VGPRs of a
+  // 16-wave block division takes one row (two spilled), ReLU and a separate
+  // accumulator buffer two.
+  constexpr int U = (EPI == ZK_EPI_GELU || (NW >= 16 && OP == ZK_DIV)) ? 1
+                    : (NW >= 16 && NEED_BIG && EPI == ZK_EPI_NONE && ACC != 2) ? 4 : 2;
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l = threadIdx.x & 63;
   __shared__ double lds[NW > 1 ? NW : 1][4][64];
