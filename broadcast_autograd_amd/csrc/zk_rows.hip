@@ -30,23 +30,29 @@ __device__ __forceinline__ float wave_max_f(float v) {
 }
 
 // exp(d) for a binary64 d <= 0 that is the exact difference of two binary32
-// values: Cody-Waite reduction in binary64 (d = n ln2 + r, |r| <= ln2/2),
-// the hardware base-2 exponential of r log2(e) in binary32 (relative error
-// below 2e-7), scaled back in binary64.  Differences below -745 give 0 and a
-// NaN stays NaN.
+// values, or NaN: d below -746 is taken as -746 (exp is then below half the
+// smallest binary64 subnormal either way, and -inf gives 0), NaN stays NaN.
+// t = d log2(e) in binary64 (|t| <= 1077, error below 2^-42), t = n + f with
+// n = rint(t) and |f| <= 1/2 exact, the hardware base-2 exponential of f in
+// binary32 (f rounded to binary32 and the instruction's own error: relative
+// error below 2e-7 together), scaled by 2^n in binary64.  The integer n is
+// taken from max(n, -1100) so that a NaN converts to a defined value (the
+// NaN still reaches the result through f).
 __device__ __forceinline__ double exp_nonpos(double d) {
-  if (!(d >= -745.0)) return d == d ? 0.0 : d;
-  const double n = rint(d * 1.4426950408889634);
-  const double r = fma(-n, 0.6931471805599453, d);
-  const float e = __builtin_amdgcn_exp2f((float)(r * 1.4426950408889634));
-  return ldexp((double)e, (int)n);
+  d = d < -746.0 ? -746.0 : d;
+  const double t = d * 1.4426950408889634;
+  const double n = rint(t);
+  const float e = __builtin_amdgcn_exp2f((float)(t - n));
+  return ldexp((double)e, (int)fmax(n, -1100.0));
 }
 
 // MODE 0: o1 = mean, o2 = biased variance.  MODE 1: o1 = row max, o2 =
 // sum exp(x - max).  U > 0: RPW rows per wave are held in registers at once
 // (their loads all issued before any arithmetic; VEC: 128-bit loads, element
 // 4(l + 64u) + q; else element l + 64i); U == 0: one row per wave, streamed.
-template <int MODE, int U, int RPW, bool VEC>
+// FULL (with VEC): the rows have exactly 256 U elements, so no element of a
+// lane is out of range.
+template <int MODE, int U, int RPW, bool VEC, bool FULL>
 __global__ __launch_bounds__(kRowsBlk) void k_row_stats(const float *x, float *o1, float *o2,
                                                         RowStatArgs ra) {
   constexpr int WPB = kRowsBlk / 64;
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(kRowsBlk) void k_row_stats(const float *x, float *o
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int64_t j = VEC ? 4 * ((int64_t)l + 64 * (i / 4)) + (i % 4) : (int64_t)l + 64 * i;
-        ok[i] = j < n;
+        ok[i] = FULL || j < n;
       }
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
@@ -72,7 +78,7 @@ __global__ __launch_bounds__(kRowsBlk) void k_row_stats(const float *x, float *o
           for (int u = 0; u < U; ++u) {
             const int64_t j = 4 * ((int64_t)l + 64 * u);
             float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (rok && j + 4 <= n) {
+            if (rok && (FULL || j + 4 <= n)) {
               q = ld4_nt(row + j);
             } else if (rok) {
 #pragma unroll
@@ -122,33 +128,41 @@ __global__ __launch_bounds__(kRowsBlk) void k_row_stats(const float *x, float *o
           }
         }
       } else {
+        // The max ignores NaN.  With a finite max every d = x - max lies in
+        // [-inf, 0] or is NaN, and a NaN element turns the sum into NaN,
+        // which marks the row; a max of +-inf (a +inf element, or only -inf
+        // and NaN elements, or an empty row) takes the rare branch, which
+        // looks for NaN in the registers.  Both branches are wave-uniform.
         float m[RPW];
-        bool nan[RPW];
 #pragma unroll
         for (int rr = 0; rr < RPW; ++rr) {
           m[rr] = -INFINITY;
-          nan[rr] = false;
 #pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            if (ok[i]) {
-              nan[rr] = nan[rr] || v[rr][i] != v[rr][i];
-              m[rr] = fmaxf(m[rr], v[rr][i]);  // ignores NaN; tracked apart
-            }
-          }
+          for (int i = 0; i < NV; ++i)
+            if (ok[i]) m[rr] = fmaxf(m[rr], v[rr][i]);
         }
         double s[RPW];
 #pragma unroll
         for (int rr = 0; rr < RPW; ++rr) {
           m[rr] = wave_max_f(m[rr]);
-          if (__any(nan[rr])) m[rr] = __builtin_nanf("");
-          const double md = (double)m[rr];
-          s[rr] = 0.0;
+          if (__builtin_isfinite(m[rr])) {
+            const double md = (double)m[rr];
+            s[rr] = 0.0;
 #pragma unroll
-          for (int i = 0; i < NV; ++i)
-            if (ok[i]) s[rr] += exp_nonpos((double)v[rr][i] - md);
+            for (int i = 0; i < NV; ++i)
+              if (ok[i]) s[rr] += exp_nonpos((double)v[rr][i] - md);
+            s[rr] = wave_sum(s[rr]);
+            if (s[rr] != s[rr]) m[rr] = __builtin_nanf("");
+          } else {
+            bool nan = false;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) nan = nan || (ok[i] && v[rr][i] != v[rr][i]);
+            if (__any(nan)) m[rr] = __builtin_nanf("");
+            // +inf - +inf, -inf - -inf and NaN - x are NaN: every term of a
+            // non-empty row is NaN or the sum holds one
+            s[rr] = n == 0 ? 0.0 : (double)__builtin_nanf("");
+          }
         }
-#pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) s[rr] = wave_sum(s[rr]);
         if (l == 0) {
 #pragma unroll
           for (int rr = 0; rr < RPW; ++rr) {
@@ -216,10 +230,12 @@ static hipError_t launch_rows_mode(const float *x, int64_t rows, int64_t cols, i
     int64_t blocks = (rows + per_block - 1) / per_block;
     if (blocks > kMaxGridBlocks) blocks = kMaxGridBlocks;
     const dim3 grid((unsigned)blocks), blk(kRowsBlk);
-    if (vec)
-      ZK_LAUNCH(prof, (k_row_stats<MODE, U, RPW, true>), grid, blk, 0, st, x, o1, o2, ra);
+    if (vec && U > 0 && cols == 256 * (int64_t)U)
+      ZK_LAUNCH(prof, (k_row_stats<MODE, U, RPW, true, true>), grid, blk, 0, st, x, o1, o2, ra);
+    else if (vec)
+      ZK_LAUNCH(prof, (k_row_stats<MODE, U, RPW, true, false>), grid, blk, 0, st, x, o1, o2, ra);
     else
-      ZK_LAUNCH(prof, (k_row_stats<MODE, U, RPW, false>), grid, blk, 0, st, x, o1, o2, ra);
+      ZK_LAUNCH(prof, (k_row_stats<MODE, U, RPW, false, false>), grid, blk, 0, st, x, o1, o2, ra);
     return hipGetLastError();
   };
   using std::integral_constant;

@@ -76,13 +76,22 @@ def test_row_stats(orc, cols, layout):
     assert np.array_equal(again.view(np.uint32), host(s).view(np.uint32))
 
 
-def test_row_stats_special_values(orc):
-    x = np.random.default_rng(3).standard_normal((6, 300)).astype(np.float32)
+@pytest.mark.parametrize("cols", [300, 256, 512, 5000])
+def test_row_stats_special_values(orc, cols):
+    """NaN, +-inf and huge values in every row kernel: 256 and 512 columns
+    take the rows that fill every lane, 300 the guarded ones, 5000 the
+    streamed one."""
+    x = np.random.default_rng(3).standard_normal((10, cols)).astype(np.float32)
     x[0, 17] = np.nan
     x[1, :] = -np.inf
     x[2, 3] = np.inf
     x[3, :] = np.float32(-1e9)
     x[4, 0] = np.float32(3e38)
+    x[5, 7], x[5, 200] = np.inf, np.nan
+    x[6, :] = np.nan
+    x[7, ::2] = -np.inf
+    x[8, :] = -np.inf
+    x[8, 100] = np.nan
     t = dev(x)
     mx, s = zk.row_softmax_stats(t)
     rmx, rs = orc.row_softmax_stats(x)
