@@ -568,6 +568,63 @@ __global__ __launch_bounds__(kBlock) void k_fwd2_row(In3 a, In3 b, In3 c, float 
   }
 }
 
+// Fused (a op1 b) op2 c over rows of n1 elements where a is dense, one of b
+// and c is a contiguous row vector that every row shares (outer strides 0,
+// n1 >= kBcRowsMinCols) and the other a scalar per row (inner stride 0):
+// the attention's scores * scale[1,H,1,1] + mask[1,1,S,S].  As in
+// k_fwd_bcrows, a lane applies each 16-byte piece of the shared vector to
+// kBcRows rows.  Row r's scalar sits at (r / nmid) * rs0 + (r % nmid) * rs1
+// (rank 3 [n0, nmid, n1]; rank 2: nmid = 1, rs1 = 0).  VB: b is the vector,
+// c the scalar; else the reverse.  Two binary32 roundings per element, as
+// everywhere.
+struct Bc2Args {
+  int64_t n1;     // row length (elements)
+  int64_t total;  // (rows / kBcRows) * (n1 / 4) vectors
+  uint32_t vpr;   // n1 / 4
+  FastDiv fv;     // divides by vpr
+  uint32_t nmid;  // middle dim of a rank-3 space (1 for rank 2)
+  FastDiv fmid;   // divides by nmid
+  int64_t rs0, rs1;
+};
+
+template <int OP1, int OP2, bool VB, typename I>
+__global__ __launch_bounds__(kBlock) void k_fwd2_bcrows(const float *a, const float *b,
+                                                        const float *c, float *out,
+                                                        Bc2Args ba) {
+  const I n1 = (I)ba.n1;
+  const float *vec = VB ? b : c;
+  const float *sca = VB ? c : b;
+  for (int64_t v64 = (int64_t)blockIdx.x * kBlock + threadIdx.x; v64 < ba.total;
+       v64 += (int64_t)gridDim.x * kBlock) {
+    I g;
+    if constexpr (sizeof(I) == 4) g = (I)fdiv(ba.fv, (uint32_t)v64);
+    else g = (I)(v64 / (int64_t)ba.vpr);
+    const I j = ((I)v64 - g * (I)ba.vpr) * 4;
+    const I r0 = g * (I)kBcRows;
+    float4 x[kBcRows];
+    float sv[kBcRows];
+#pragma unroll
+    for (int k = 0; k < kBcRows; ++k) {
+      const I r = r0 + (I)k;
+      x[k] = ld4_nt(a + r * n1 + j);
+      I q;
+      if constexpr (sizeof(I) == 4) q = (I)fdiv(ba.fmid, (uint32_t)r);
+      else q = r / (I)ba.nmid;
+      sv[k] = sca[q * (I)ba.rs0 + (r - q * (I)ba.nmid) * (I)ba.rs1];
+    }
+    const float4 vv = ld4(vec + j);
+#pragma unroll
+    for (int k = 0; k < kBcRows; ++k) {
+      float4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        el(r, e) = VB ? op32<OP2>(op32<OP1>(el(x[k], e), el(vv, e)), sv[k])
+                      : op32<OP2>(op32<OP1>(el(x[k], e), sv[k]), el(vv, e));
+      st4_nt(out + (r0 + (I)k) * n1 + j, r);
+    }
+  }
+}
+
 template <int OP1, int OP2, typename I>
 __global__ __launch_bounds__(kBlock) void k_fwd2_generic(const float *a, const float *b,
                                                          const float *c, float *out,
@@ -934,6 +991,46 @@ hipError_t launch_fwd2(const Fwd2Plan &p, zk_op op1, zk_op op2, const float *a,
     constexpr int OP2 = decltype(O2)::value;
     ProfScope prof(p.kernel);
     const unsigned grid = grid_of(cn.numel, kBlock * 4);
+    if (p.kernel == K_FWD2_ROW && (cn.rank == 2 || cn.rank == 3) && p.mode[0] == IM_FLAT &&
+        p.mode[2] != IM_SAME_A) {
+      // a shared row vector and a per-row scalar: k_fwd2_bcrows
+      const int R = cn.rank;
+      const int64_t n1 = cn.n[R - 1];
+      auto is_vec = [&](int x) {
+        for (int k = 0; k + 1 < R; ++k)
+          if (cn.s[1 + x][k] != 0) return false;
+        return cn.s[1 + x][R - 1] == 1;
+      };
+      const bool vb = is_vec(1) && cn.s[3][R - 1] == 0;
+      const bool vc = is_vec(2) && cn.s[2][R - 1] == 0;
+      const float *vp = vb ? b : c;
+      const int64_t rows = n1 > 0 ? cn.numel / n1 : 0;
+      if ((vb || vc) && n1 >= kBcRowsMinCols && n1 % 4 == 0 && n1 / 4 < ((int64_t)1 << 31) &&
+          rows % kBcRows == 0 && ((uintptr_t)a & 15u) == 0 && ((uintptr_t)out & 15u) == 0 &&
+          ((uintptr_t)vp & 15u) == 0 && (R == 2 || cn.n[1] < ((int64_t)1 << 31))) {
+        const int so = vb ? 3 : 2;  // the per-row scalar's stride set
+        Bc2Args ba{};
+        ba.n1 = n1;
+        ba.vpr = (uint32_t)(n1 / 4);
+        ba.total = (rows / kBcRows) * (n1 / 4);
+        ba.fv = make_fastdiv(ba.vpr);
+        ba.nmid = R == 3 ? (uint32_t)cn.n[1] : 1u;
+        ba.fmid = make_fastdiv(ba.nmid);
+        ba.rs0 = cn.s[so][0];
+        ba.rs1 = R == 3 ? cn.s[so][1] : 0;
+        const int64_t need = (ba.total + kBlock - 1) / kBlock;
+        const unsigned g2 = (unsigned)(need < kMaxBlocks ? need : kMaxBlocks);
+        auto go = [&](auto VBc, auto Ic) -> hipError_t {
+          constexpr bool VB = decltype(VBc)::value != 0;
+          using I = std::conditional_t<decltype(Ic)::value != 0, int64_t, int32_t>;
+          ZK_LAUNCH(prof, (k_fwd2_bcrows<OP1, OP2, VB, I>), dim3(g2), dim3(kBlock), 0, st, a,
+                    b, c, out, ba);
+          return hipGetLastError();
+        };
+        if (p.idx64) return vb ? go(IC<1>{}, IC<1>{}) : go(IC<0>{}, IC<1>{});
+        return vb ? go(IC<1>{}, IC<0>{}) : go(IC<0>{}, IC<0>{});
+      }
+    }
     if (p.kernel == K_FWD2_ROW) {
       // canonical dims right-aligned onto (c0, c1, c2)
       Space3 sp{};

@@ -174,6 +174,27 @@ def test_fused_determinism():
 
 # ----------------------------------------- full sizes of the fused workloads
 # Every element of every output against the oracle's full fused entry points.
+@pytest.mark.parametrize("shapes", [
+    ((2, 4, 65536), (1, 4, 1), (1, 1, 65536)),   # per-row scalar b, shared vector c (rank 3)
+    ((4, 65536), (65536,), (4, 1)),              # shared vector b, per-row scalar c (rank 2)
+    ((3, 65536), (1, 1), (65536,)),              # odd row count: the row kernel
+    ((2, 4, 65532), (1, 4, 1), (1, 1, 65532)),   # rows below 65536 elements: the row kernel
+])
+@pytest.mark.parametrize("op1", ["add", "sub", "mul", "div"])
+def test_fused_shared_row_vector(orc, shapes, op1):
+    """(a op1 b) op2 c with one small operand a row vector every row shares
+    and the other a scalar per row (the attention's scale and mask): the
+    kernel that applies each piece of the vector to two rows, bit for bit
+    against the oracle's two roundings, op2 add and sub."""
+    rng = np.random.default_rng(zlib.crc32(repr((shapes, op1)).encode()))
+    a = _vals(rng, shapes[0])
+    b = _vals(rng, shapes[1])
+    c = _vals(rng, shapes[2])
+    for op2 in ("add", "sub"):
+        got = host(zk.binary2_fwd(op1, op2, dev(a), dev(b), dev(c)))
+        assert_bitexact(got, orc.fwd2(op1, op2, a, b, c), f"{op1} {op2} {shapes}")
+
+
 def _check_fused(orc, wl, a, b, c, names, tie=None):
     h = wl.host
     say(f"  out: {wl.__dict__[names[3]].numel()} elements")

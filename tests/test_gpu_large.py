@@ -83,6 +83,25 @@ def test_shared_row_vector_past_2_31(orc):
     assert_bitexact(_take(out, pos), orc.fwd_at("sub", v_np, va, pos), "bcrows 64-bit")
 
 
+def test_fused_shared_row_vector_past_2_31(orc):
+    """(a * b) + c with a [rows, 65536] constant, b a shared row vector and c a
+    scalar per row, 2^31 + 131072 elements: the 64-bit index path of the
+    fused kernel that applies each piece of the vector to two rows."""
+    cols = 1 << 16
+    rows = ((1 << 31) + 2 * cols) // cols  # even
+    v_np = np.random.default_rng(8).standard_normal(cols).astype(np.float32)
+    c_np = np.random.default_rng(9).standard_normal((rows, 1)).astype(np.float32)
+    a = torch.full((rows, cols), 0.75, device="cuda")
+    out = zk.binary2_fwd("mul", "add", a, dev(v_np), dev(c_np))
+    va = orc.View(np.array([0.75], np.float32), (rows, cols), (0, 0))
+    n = rows * cols
+    rng = np.random.default_rng(10)
+    pos = np.concatenate([np.array([0, cols - 1, cols, (1 << 31) - 1, 1 << 31, n - 1], np.int64),
+                          rng.integers(0, n, 4000)])
+    assert_bitexact(_take(out, pos), orc.fwd2_at("mul", "add", va, v_np, c_np, pos),
+                    "fused bcrows 64-bit")
+
+
 def test_backward_and_reductions_past_2_31(orc):
     b_np = np.random.default_rng(5).standard_normal(C).astype(np.float32)
     a = torch.full((R, C), 1.5, device="cuda")
