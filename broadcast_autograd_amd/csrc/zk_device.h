@@ -46,7 +46,7 @@ __device__ __forceinline__ void gelu_tab_load(double *lds) {
 }
 
 // GeLU(h) rounded once to binary32 for W arguments.  The binary64 value y
-// is rounded when it lies farther than 2^-40 (relative, 2^6 times the error
+// is rounded when it lies farther than 2^-43 (relative, 2^3 times the error
 // bound) from the midpoint between its two binary32 neighbours, which makes
 // the result the correctly rounded exact value; otherwise bit k of *redo is
 // set and the caller recomputes element k with gelu32_slow.  Also sent
@@ -91,11 +91,14 @@ __device__ __forceinline__ void gelu32_fast_w(const double *tab, const float (&h
     const double y = fma(-0.5, fabs(th), fmax(hd[k], 0.0));  // NaN: fmax gives 0, y NaN
     // Rounding y to binary32 discards the low 29 of its 52 mantissa bits; a
     // midpoint between binary32 neighbours has exactly 2^28 there.  y is
-    // trusted when those bits are more than 2^12 units (2^-40 relative) from
-    // 2^28.
+    // trusted when those bits are more than 2^9 units (2^-43 relative, about
+    // 5x the error bound in those units) from 2^28.  Every element of the
+    // rare path costs its wave the double-double evaluation, so the window
+    // is kept narrow (on the [4096, 1024] forward: ~8 elements a call
+    // instead of ~74 with 2^12 units, 10.4 -> 9.9 us).
     const uint32_t lo = (uint32_t)__double_as_longlong(y);
-    const uint32_t dist = (lo & 0x1fffffffu) - (0x10000000u - 0x1000u);
-    uint32_t near = (uint32_t)(dist < 0x2000u || fabs(y) < 0x1p-126);
+    const uint32_t dist = (lo & 0x1fffffffu) - (0x10000000u - 0x200u);
+    uint32_t near = (uint32_t)(dist < 0x400u || fabs(y) < 0x1p-126);
     float fy = (float)y;
     // Keep the fast value unconditional: left alone, the compiler turns a
     // select on it into a branch per element around the whole evaluation.
