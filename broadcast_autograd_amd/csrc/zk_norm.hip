@@ -85,10 +85,22 @@ __global__ __launch_bounds__(kNormBlk) void k_norm_part(NormTab tab, double *par
 // The square root of the sum of all P partials, in one fixed order (lane l
 // sums partials l, l + 256, ...; then the wave and block trees).  Every
 // block that calls it gets the same bits.  Called by all kNormBlk threads.
+// A lane's loads are issued eight at a time and added in order (a missing
+// one adds +0, which leaves the non-negative sum unchanged), so the clip's
+// every block does not wait for them one by one.
 __device__ __forceinline__ double norm_total(const double *part, int64_t P, double *sh) {
   const int l = threadIdx.x;
   double s = 0.0;
-  for (int64_t i = l; i < P; i += kNormBlk) s += part[i];
+  for (int64_t i0 = l; i0 < P; i0 += 8 * kNormBlk) {
+    double v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t i = i0 + (int64_t)k * kNormBlk;
+      v[k] = i < P ? part[i] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
   s = wave_sum(s);
   if ((l & 63) == 0) sh[l >> 6] = s;
   __syncthreads();
