@@ -427,69 +427,91 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
 // Partials are kept-element major, part[k * P + r1 * NC + ch] (P = R1 * NC
 // of them per kept element): the few kept elements of these sums (16 for the
 // attention scale) each own thousands of partials, which stage 2 then reads
-// in contiguous runs.
+// in contiguous runs.  Blockwise (BW, for NC a multiple of 4): the four
+// waves of a block take four consecutive chunks of one row and add their
+// sums in LDS in wave order, one partial per block,
+// part[k * P + r1 * (NC / 4) + ch / 4].
 struct RowRedArgs {
   int64_t R0, K, NC, CL, items, ss, P;
   int32_t write_big;
 };
 
+// One wave's sum of the terms of work item `item` (not yet summed across
+// lanes); writes the full operand's gradient on the way.
 template <int OP, int EPI, int SIDE, int ACC>
+__device__ __forceinline__ double row_item(const float *g, const float *big,
+                                           const float *small, float *gbig,
+                                           const float *accbig, const RowRedArgs &ra,
+                                           const GcOut &gco, int64_t item, int l,
+                                           int64_t &r1, int64_t &k, int64_t &ch) {
+  constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
+  constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
+  const int64_t row = item / ra.NC;
+  ch = item - row * ra.NC;
+  r1 = row / ra.K;
+  k = row - r1 * ra.K;
+  const float sv = NEED_SMALL ? small[k * ra.ss] : 0.f;
+  const int64_t e0 = row * ra.R0 + ch * ra.CL;
+  const int64_t lim = (ch + 1) * ra.CL < ra.R0 ? (ch + 1) * ra.CL : ra.R0;
+  const int64_t e1 = row * ra.R0 + lim;
+  double s = 0.0;
+  // one vector per lane per trip over short chunks (many waves) streams best
+  for (int64_t i = e0 + 4 * l; i < e1; i += 256) {
+    const float4 vg = ld4_nt(g + i);
+    float4 vb, va;
+    if constexpr (NEED_BIG) vb = ld4_nt(big + i);
+    if constexpr (ACC == 2) va = ld4_nt(accbig + i);
+    float4 ob;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float gv = el(vg, q);
+      const float bv = NEED_BIG ? el(vb, q) : 0.f;
+      const float x = SIDE == 0 ? sv : bv;
+      const float y = SIDE == 0 ? bv : sv;
+      double ts;
+      float tb;
+      terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
+      s += ts;
+      if constexpr (ACC == 1) tb = gv + tb;
+      if constexpr (ACC == 2) tb = el(va, q) + tb;
+      el(ob, q) = tb;
+    }
+    if (ra.write_big) st4_nt(gbig + i, ob);
+    if (gco.p) gc_store4(gco, i, vg);
+  }
+  return s;
+}
+
+template <int OP, int EPI, int SIDE, int ACC, bool BW>
 __global__ __launch_bounds__(kBlk) void k_red_row(
     const float *g, const float *big, const float *small, float *gbig,
     const float *accbig, double *part, RowRedArgs ra, GcOut gco) {
-  constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
-  constexpr bool NEED_SMALL = SIDE == 0 ? any_x<OP, EPI>() : any_y<OP, EPI>();
-  // one vector per lane per trip over short chunks (many waves) streams best
-  constexpr int U = 1;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
-  // items (row, chunk) item = 4 * blockIdx.x + w, then with a grid stride
-  for (int64_t item = (int64_t)blockIdx.x * 4 + w; item < ra.items;
-       item += (int64_t)gridDim.x * 4) {
-    const int64_t row = item / ra.NC, ch = item - row * ra.NC;
-    const int64_t r1 = row / ra.K, k = row - r1 * ra.K;
-    const float sv = NEED_SMALL ? small[k * ra.ss] : 0.f;
-    const int64_t e0 = row * ra.R0 + ch * ra.CL;
-    const int64_t lim = (ch + 1) * ra.CL < ra.R0 ? (ch + 1) * ra.CL : ra.R0;
-    const int64_t e1 = row * ra.R0 + lim;
-    double s = 0.0;
-    for (int64_t eb = e0 + 4 * l; eb < e1; eb += 256 * U) {
-      float4 vg[U], vb[U], va[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = eb + 256 * u;
-        if (i < e1) {
-          vg[u] = ld4_nt(g + i);
-          if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
-          if constexpr (ACC == 2) va[u] = ld4_nt(accbig + i);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t i = eb + 256 * u;
-        if (i < e1) {
-          float4 ob;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float gv = el(vg[u], q);
-            const float bv = NEED_BIG ? el(vb[u], q) : 0.f;
-            const float x = SIDE == 0 ? sv : bv;
-            const float y = SIDE == 0 ? bv : sv;
-            double ts;
-            float tb;
-            terms2<OP, EPI, SIDE>(gv, x, y, ts, tb);
-            s += ts;
-            if constexpr (ACC == 1) tb = gv + tb;
-            if constexpr (ACC == 2) tb = el(va[u], q) + tb;
-            el(ob, q) = tb;
-          }
-          if (ra.write_big) st4_nt(gbig + i, ob);
-          if (gco.p) gc_store4(gco, i, vg[u]);
-        }
-      }
+  int64_t r1, k, ch;
+  if constexpr (!BW) {
+    // items (row, chunk) item = 4 * blockIdx.x + w, then with a grid stride
+    for (int64_t item = (int64_t)blockIdx.x * 4 + w; item < ra.items;
+         item += (int64_t)gridDim.x * 4) {
+      double s = row_item<OP, EPI, SIDE, ACC>(g, big, small, gbig, accbig, ra, gco, item, l,
+                                              r1, k, ch);
+      s = wave_sum(s);
+      if (l == 0) part[k * ra.P + r1 * ra.NC + ch] = s;
     }
-    s = wave_sum(s);
-    if (l == 0) part[k * ra.P + r1 * ra.NC + ch] = s;
+  } else {
+    // items % 4 == 0: every wave of a block has an item, and the block's
+    // trip count is uniform, so the barriers are too
+    __shared__ double sh[4];
+    for (int64_t bi = blockIdx.x; bi < ra.items / 4; bi += gridDim.x) {
+      double s = row_item<OP, EPI, SIDE, ACC>(g, big, small, gbig, accbig, ra, gco, bi * 4 + w,
+                                              l, r1, k, ch);
+      s = wave_sum(s);
+      if (l == 0) sh[w] = s;
+      __syncthreads();
+      if (threadIdx.x == 0)
+        part[k * ra.P + r1 * (ra.NC / 4) + ch / 4] = ((sh[0] + sh[1]) + sh[2]) + sh[3];
+      __syncthreads();  // sh is rewritten by the block's next trip
+    }
   }
 }
 
@@ -1704,9 +1726,13 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ra.write_big = p.fused_big;
             unsigned grid = gridn(ra.items, 4);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
-              ZK_LAUNCH(prof, (k_red_row<OP, EPI, decltype(Sc)::value, decltype(Ac)::value>),
-                        dim3(grid), dim3(kBlk), 0, st, g, big, small, gbig, accbig,
-                        part, ra, go);
+              constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
+              if (rp.nw == 4)
+                ZK_LAUNCH(prof, (k_red_row<OP, EPI, S, A, true>), dim3(grid), dim3(kBlk), 0, st,
+                          g, big, small, gbig, accbig, part, ra, go);
+              else
+                ZK_LAUNCH(prof, (k_red_row<OP, EPI, S, A, false>), dim3(grid), dim3(kBlk), 0, st,
+                          g, big, small, gbig, accbig, part, ra, go);
               return hipGetLastError();
             });
           }
@@ -1842,7 +1868,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           ra.P = rp.partials;
           ra.ss = 0;
           ra.write_big = 0;
-          ZK_LAUNCH(prof, (k_red_row<ZK_ADD, ZK_EPI_NONE, 1, 0>), dim3(gridn(ra.items, 4)),
+          ZK_LAUNCH(prof, (k_red_row<ZK_ADD, ZK_EPI_NONE, 1, 0, false>), dim3(gridn(ra.items, 4)),
                     dim3(kBlk), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ra, none);
           break;
         }

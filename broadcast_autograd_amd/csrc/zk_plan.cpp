@@ -542,9 +542,11 @@ static bool size_run(const Canon &c, int o, int big_op, bool src_flat, bool idx6
 
 // Try the fast stage-1 classes for the reduced operand stride set `o`
 // (grad layout) with `big` the dense operand id (or -1 if none is read).
-// Requires the source (op 0) to be dense.
+// Requires the source (op 0) to be dense.  `streams` counts the full-size
+// arrays stage 1 moves (the upstream gradient, the full operand when read,
+// its gradient when written).
 static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
-                      bool src_flat, bool aligned, RedPlan *rp) {
+                      bool src_flat, bool aligned, int streams, RedPlan *rp) {
   if (!src_flat || !aligned) return false;
   unsigned km = kept_mask(c, o);
   int R = c.rank;
@@ -576,9 +578,15 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
   int64_t rows = c.numel / inner;               // (R1, K) rows
   int64_t K = (R == 1) ? 1 : c.n[R - 2];
   int64_t R1 = rows / K;
-  // Chunks of 256..2048 elements (whole wave trips), about 8192 of them:
-  // short chunks over many waves stream best; partials stay < 0.1% of bytes.
-  int64_t CL = std::min<int64_t>(2048, std::max<int64_t>(256, c.numel / 8192));
+  // Chunks of 256..2048 elements (whole wave trips), about 8192 of them;
+  // partials stay < 0.1% of bytes.  A pass that also reads or writes the
+  // full operand streams best with chunks of 512 (two trips a wave), four
+  // chunks of a row to a block and partial (measured on MI355X: the
+  // [8, 16, 1048576] multiply backward 291 -> 266 us, the add backward
+  // 202 -> 190 us; a plain sum is 2% slower that way and keeps 2048).
+  const bool two_trips = streams >= kRowShortChunkStreams;
+  const int64_t cmax = two_trips ? 512 : 2048;
+  int64_t CL = std::min<int64_t>(cmax, std::max<int64_t>(256, c.numel / 8192));
   // at most 65536 partials per kept element, so that stage 2 stays short
   CL = std::max<int64_t>(CL, ceil_div(R1 * inner, 65536));
   CL = ceil_div(CL, 256) * 256;
@@ -602,7 +610,8 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
   rp->kept = K;
   rp->red = R1 * inner;
   rp->chunk = CL;
-  rp->partials = R1 * NC;
+  rp->nw = (two_trips && NC % 4 == 0) ? 4 : 1;  // waves sharing a partial
+  rp->partials = R1 * NC / rp->nw;
   return true;
 }
 
@@ -700,7 +709,8 @@ zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
       bool aligned = al16(pg) && (!big_read || big_tr || al16(pbig)) &&
                      (!big_write || (al16(pgbig) && al16(paccbig)));
       RedPlan rp;
-      if (size_fast(c, 3 + sw, big_op, big_tr, true, aligned, &rp)) {
+      const int streams = 1 + (big_op >= 0) + big_write;
+      if (size_fast(c, 3 + sw, big_op, big_tr, true, aligned, streams, &rp)) {
         rp.which = sw;
         p->red[p->nred++] = rp;
         p->fused_big = big_write;
@@ -839,7 +849,7 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;
-  } else if (K < c.numel && size_fast(c, 4, -1, false, src_flat, al16(pin), &rp)) {
+  } else if (K < c.numel && size_fast(c, 4, -1, false, src_flat, al16(pin), 1, &rp)) {
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;

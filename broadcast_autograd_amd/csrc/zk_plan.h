@@ -32,6 +32,8 @@ constexpr int64_t kMaxExtent = (int64_t)1 << 62;
 constexpr int kColRowsMany = 64;
 constexpr int kColWavesFew = 4;
 constexpr int kColWavesMany = 16;
+// red_row: passes moving at least this many full-size arrays take 512-element chunks
+constexpr int kRowShortChunkStreams = 2;
 // red_rowd: terms per kept element it takes (a 1024-lane block holds up to 4
 // vectors per lane in flight).
 constexpr int64_t kDirMinTerms = 2048;
@@ -205,7 +207,7 @@ struct RedPlan {
   int64_t partials = 0;      // P: partial sums per kept element
   int64_t chunk = 0;         // rows per wave (COL), rows (TILE) or elements
                              // (ROW/GENERIC) per partial
-  int32_t nw = 1;            // COL: waves of a block that share one partial
+  int32_t nw = 1;            // COL, ROW: waves of a block that share one partial
   int32_t fold = 1;          // COL: rows of K < 256 columns read as one row of
                              // fold*K = 256 (stage 1 runs on [R/fold, 256];
                              // partials counts the fold copies too)

@@ -191,7 +191,9 @@ int main() {
           const int64_t R1 = c.numel / inner / rp.kept;
           const int64_t NC = (inner + rp.chunk - 1) / rp.chunk;
           if (R1 * inner * rp.kept != c.numel) return fail("row cover", R1, rp.kept);
-          if (rp.partials != R1 * NC) return fail("row partials", rp.partials, R1 * NC);
+          // blockwise: four chunks of a row share one partial
+          if (rp.nw != 1 && (rp.nw != 4 || NC % 4 != 0)) return fail("row waves", rp.nw, NC);
+          if (rp.partials != R1 * NC / rp.nw) return fail("row partials", rp.partials, R1 * NC);
           break;
         }
         case K_RED_ROWD: {

@@ -849,6 +849,42 @@ def test_one_pass_row_reduction_fused(orc, op2):
             assert_bwd(host(got), ref, f"fused {op2} grad_{name} c{c.shape}")
 
 
+# Streaming row reductions whose pass also reads or writes the full operand:
+# four chunks of a row to a block, their sums met in LDS (one partial per
+# block) when a row's chunk count divides by 4; else one partial a wave.
+# (shapes, partials per kept element): ragged last chunks, rank 2 and 3,
+# 256- and 512-element chunks.
+ROWB_SHAPES = [(((9, 5, 2000), (5, 1)), 18),      # 8 chunks of 256 a row, last 208
+               (((5, 3, 4000), (3, 1)), 20),      # 16 chunks, last 160
+               (((3, 20480), (3, 1)), 20),        # rank 2, 80 chunks
+               (((7, 3, 2600), (3, 1)), 77),      # 11 chunks a row: one partial a wave
+               (((2, 8, 262144), (8, 1)), 256)]   # 512-element chunks
+
+
+@pytest.mark.parametrize("shapes,parts", ROWB_SHAPES, ids=[str(s[0][0]) for s in ROWB_SHAPES])
+@pytest.mark.parametrize("op", OPS)
+def test_row_reduction_blockwise(orc, shapes, parts, op):
+    sa, sb = shapes
+    info = zk.plan_describe("bwd", op, zk.make_desc(sa), zk.make_desc(sb))
+    assert info["kernel"] == "red_row" and info["partials"] == parts, info
+    a, b = _rng_pair(sa, sb, seed=sum(sa) + OPS.index(op))
+    check_pair(orc, op, a, dev(a), b, dev(b), seed=9)
+    if op in ("add", "mul"):
+        check_pair(orc, op, a, dev(a), b, dev(b), seed=10, epi="gelu")
+    rng = np.random.default_rng(sum(sa) + 1)
+    g = rng.standard_normal(sa).astype(np.float32)
+    acc_a = rng.standard_normal(sa).astype(np.float32)
+    acc_b = rng.standard_normal(sb).astype(np.float32)
+    # separate acc buffers (a third full-size read)
+    ga, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), acc_a=dev(acc_a), acc_b=dev(acc_b))
+    ra, rb = orc.bwd(op, g, a, b, acc_a=acc_a, acc_b=acc_b)
+    assert_bwd(host(ga), ra, f"{op} acc_a")
+    assert_bwd(host(gb), rb, f"{op} acc_b")
+    # the reduced gradient alone (the full operand read, not written)
+    _, gb = zk.binary_bwd(op, dev(g), dev(a), dev(b), need_a=False)
+    assert_bwd(host(gb), orc.bwd(op, g, a, b)[1], f"{op} grad_b alone")
+
+
 # One-pass gather reductions (32..4096 terms per kept element on patterns
 # the streaming classes do not take): a wave per kept element, also writing
 # the full operand's gradient.
