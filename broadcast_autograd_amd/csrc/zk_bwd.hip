@@ -313,7 +313,15 @@ __device__ __forceinline__ float col_direct(const ColDirect &cd, int64_t c, doub
   return (float)v;
 }
 
-template <int OP, int EPI, int SIDE, int ACC, int NW, bool DIRECT>
+// Four rows in flight and interleaved rows (IL) for a 16-wave block that reads
+// the full operand and writes its gradient.
+template <int OP, int EPI, int SIDE, int ACC, int NW>
+constexpr bool col_four_rows() {
+  constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
+  return NW >= 16 && NEED_BIG && EPI == ZK_EPI_NONE && ACC != 2 && OP != ZK_DIV;
+}
+
+template <int OP, int EPI, int SIDE, int ACC, int NW, bool DIRECT, bool IL>
 __global__ __launch_bounds__(64 * NW) void k_red_col(
     const float *g, const float *big, const float *small, float *gbig,
     const float *accbig, double *part, ColArgs ca, GcOut gco, ColDirect cd) {
@@ -325,11 +333,17 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   // 16-wave blocks of a long column sum (one block a CU) also read the full
   // operand (the [32768, 4096] multiply backward: 274-276 us against
   // 274-281, the fused one 391-399 against 391-411; a plain sum of g, which
-  // reads one stream, is 3% slower with four).  Within the 128 VGPRs of a
-  // 16-wave block division takes one row (two spilled), ReLU and a separate
-  // accumulator buffer two.
+  // reads one stream, is 3% slower with four).  Those blocks, when they also
+  // write the full operand's gradient, walk their rows interleaved across
+  // the grid (IL; measured on MI355X: [32768, 4096] 291 -> 283 us,
+  // [65536, 2048] 321 -> 274 us, the fused [32768, 4096] backward 392-399 ->
+  // 380-385 us; plain sums, the division backward and a multiply backward
+  // that only reads the full operand were as fast or slower interleaved).
+  // Within the 128 VGPRs of a 16-wave block division takes one row (two
+  // spilled), ReLU and a separate accumulator buffer two.
   constexpr int U = (EPI == ZK_EPI_GELU || (NW >= 16 && OP == ZK_DIV)) ? 1
                     : (NW >= 16 && NEED_BIG && EPI == ZK_EPI_NONE && ACC != 2) ? 4 : 2;
+  static_assert(!IL || U == 4, "interleaved rows only for the four-row kernels");
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l = threadIdx.x & 63;
   __shared__ double lds[NW > 1 ? NW : 1][4][64];
@@ -348,16 +362,23 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
 #pragma unroll
       for (int k = 0; k < 4; ++k) sv[k] = small[(cm + k) * ca.ss];
     }
-    const int64_t r0 = (p * NW + w) * ca.rcw;
-    const int64_t r1 = r0 + ca.rcw < ca.R ? r0 + ca.rcw : ca.R;
+    // Row walk of wave q = p * NW + w: rows q * rcw ... q * rcw + rcw - 1
+    // (j runs over the rows themselves), or, interleaved (IL), rows q,
+    // q + Q, q + 2Q, ... (Q = bands * NW walkers; j counts the wave's rcw
+    // rows), so that the waves running together read one compact band of
+    // rows of each array.
+    const int64_t q = p * NW + w;
+    const int64_t j0 = IL ? 0 : q * ca.rcw;
+    const int64_t j1 = IL ? ca.rcw : (j0 + ca.rcw < ca.R ? j0 + ca.rcw : ca.R);
+    const int64_t QQ = ca.bands * NW;
     double s[4] = {0.0, 0.0, 0.0, 0.0};
     if (active) {
-      for (int64_t rb = r0; rb < r1; rb += U) {
+      for (int64_t j = j0; j < j1; j += U) {
         float4 vg[U], vb[U], va[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t r = rb + u;
-          if (r < r1) {
+          const int64_t r = IL ? q + (j + u) * QQ : j + u;
+          if (j + u < j1 && (!IL || r < ca.R)) {
             const int64_t i = r * ca.K + c;
             vg[u] = ld4_nt(g + i);
             if constexpr (NEED_BIG) vb[u] = ld4_nt(big + i);
@@ -366,8 +387,8 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t r = rb + u;
-          if (r < r1) {
+          const int64_t r = IL ? q + (j + u) * QQ : j + u;
+          if (j + u < j1 && (!IL || r < ca.R)) {
             const int64_t i = r * ca.K + c;
             float gv[4], x[4], y[4], tb[4];
             double ts[4];
@@ -1707,7 +1728,14 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
               return with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
                 constexpr int NW = decltype(Wc)::value;
                 constexpr bool D = decltype(Dc)::value;
-                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, NW, D>), dim3(grid), dim3(64 * NW),
+                if constexpr (col_four_rows<OP, EPI, S, A, NW>()) {
+                  if (ca.write_big) {
+                    ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, NW, D, true>), dim3(grid),
+                              dim3(64 * NW), 0, st, g, big, small, gbig, accbig, part, ca, go, cd);
+                    return hipGetLastError();
+                  }
+                }
+                ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, NW, D, false>), dim3(grid), dim3(64 * NW),
                           0, st, g, big, small, gbig, accbig, part, ca, go, cd);
                 return hipGetLastError();
               });
@@ -1849,7 +1877,7 @@ hipError_t launch_reduce(const BwdPlan &p, const float *in, float *out,
           hipError_t e = with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
             constexpr int NW = decltype(Wc)::value;
             constexpr bool D = decltype(Dc)::value;
-            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, NW, D>), dim3(grid),
+            ZK_LAUNCH(prof, (k_red_col<ZK_ADD, ZK_EPI_NONE, 1, 0, NW, D, false>), dim3(grid),
                       dim3(64 * NW), 0, st, in, nullptr, nullptr, nullptr, nullptr, part, ca,
                       none, cd);
             return hipGetLastError();
