@@ -313,12 +313,12 @@ __device__ __forceinline__ float col_direct(const ColDirect &cd, int64_t c, doub
   return (float)v;
 }
 
-// Four rows in flight and interleaved rows (IL) for a 16-wave block that reads
-// the full operand and writes its gradient.
-template <int OP, int EPI, int SIDE, int ACC, int NW>
-constexpr bool col_four_rows() {
+// Interleaved rows (IL) for a 16-wave block that reads the full operand and
+// writes its gradient with the plain rules other than division.
+template <int OP, int EPI, int SIDE, int NW>
+constexpr bool col_interleaved() {
   constexpr bool NEED_BIG = SIDE == 0 ? any_y<OP, EPI>() : any_x<OP, EPI>();
-  return NW >= 16 && NEED_BIG && EPI == ZK_EPI_NONE && ACC != 2 && OP != ZK_DIV;
+  return NW >= 16 && NEED_BIG && EPI == ZK_EPI_NONE && OP != ZK_DIV;
 }
 
 template <int OP, int EPI, int SIDE, int ACC, int NW, bool DIRECT, bool IL>
@@ -335,15 +335,16 @@ __global__ __launch_bounds__(64 * NW) void k_red_col(
   // 274-281, the fused one 391-399 against 391-411; a plain sum of g, which
   // reads one stream, is 3% slower with four).  Those blocks, when they also
   // write the full operand's gradient, walk their rows interleaved across
-  // the grid (IL; measured on MI355X: [32768, 4096] 291 -> 283 us,
-  // [65536, 2048] 321 -> 274 us, the fused [32768, 4096] backward 392-399 ->
-  // 380-385 us; plain sums, the division backward and a multiply backward
-  // that only reads the full operand were as fast or slower interleaved).
+  // the grid (IL, also with a separate accumulator buffer; measured on
+  // MI355X: [32768, 4096] 291 -> 283 us, [65536, 2048] 321 -> 274 us, the
+  // fused [32768, 4096] backward 392-399 -> 380-385 us; plain sums, the
+  // division backward and a multiply backward that only reads the full
+  // operand were as fast or slower interleaved).
   // Within the 128 VGPRs of a 16-wave block division takes one row (two
   // spilled), ReLU and a separate accumulator buffer two.
   constexpr int U = (EPI == ZK_EPI_GELU || (NW >= 16 && OP == ZK_DIV)) ? 1
                     : (NW >= 16 && NEED_BIG && EPI == ZK_EPI_NONE && ACC != 2) ? 4 : 2;
-  static_assert(!IL || U == 4, "interleaved rows only for the four-row kernels");
+  static_assert(!IL || col_interleaved<OP, EPI, SIDE, NW>(), "interleaved rows");
   const int w = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l = threadIdx.x & 63;
   __shared__ double lds[NW > 1 ? NW : 1][4][64];
@@ -1728,7 +1729,7 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
               return with_col_waves(rp.nw, col_direct_plan(rp), [&](auto Wc, auto Dc) {
                 constexpr int NW = decltype(Wc)::value;
                 constexpr bool D = decltype(Dc)::value;
-                if constexpr (col_four_rows<OP, EPI, S, A, NW>()) {
+                if constexpr (col_interleaved<OP, EPI, S, NW>()) {
                   if (ca.write_big) {
                     ZK_LAUNCH(prof, (k_red_col<OP, EPI, S, A, NW, D, true>), dim3(grid),
                               dim3(64 * NW), 0, st, g, big, small, gbig, accbig, part, ca, go, cd);

@@ -463,7 +463,7 @@ static bool size_gend(RedPlan *rp, int64_t K, int64_t red) {
 
 // Sizing of a red_col column sum over a dense [rows, cols] matrix (cols a
 // multiple of 4): kept = cols, one partial per band of rows.
-static void size_col(RedPlan *rp, int64_t rows, int64_t cols) {
+static void size_col(RedPlan *rp, int64_t rows, int64_t cols, bool col_il = false) {
   rp->kernel = K_RED_COL;
   rp->kept = cols;
   rp->red = rows;
@@ -494,6 +494,13 @@ static void size_col(RedPlan *rp, int64_t rows, int64_t cols) {
     nw = R0 >= kColWavesFew ? kColWavesFew : 1;
     rcw = std::max<int64_t>(1, ceil_div(R0, nw));
   }
+  // Long columns whose pass reads the full operand and writes its gradient
+  // with the interleaved column kernel (col_il): short row runs, 8 a wave
+  // and 128 a partial, over many blocks (measured on MI355X, with 64: the
+  // fused [32768, 4096] backward 380-385 -> 366-372 us, [32768, 8192]
+  // 578-600 -> 528 us; the division and GeLU backwards, which walk their
+  // rows in order, gained nothing or lost).
+  if (col_il && fold == 1 && nw == kColWavesMany && colblocks >= 8) rcw = kColRowsIL;
   // Longer row bands while the grid is above the dispatch limit, down to a
   // single band (more than 2^30 columns stay above it).
   while (colblocks * ceil_div(R0, nw * rcw) > kMaxGridBlocks && nw * rcw < R0) rcw *= 2;
@@ -546,7 +553,7 @@ static bool size_run(const Canon &c, int o, int big_op, bool src_flat, bool idx6
 // arrays stage 1 moves (the upstream gradient, the full operand when read,
 // its gradient when written).
 static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
-                      bool src_flat, bool aligned, int streams, RedPlan *rp) {
+                      bool src_flat, bool aligned, int streams, bool col_il, RedPlan *rp) {
   if (!src_flat || !aligned) return false;
   unsigned km = kept_mask(c, o);
   int R = c.rank;
@@ -565,7 +572,7 @@ static bool size_fast(const Canon &c, int o, int big_op, bool big_transposed,
     }
     if (big_op >= 0 && !is_flat(c, big_op)) return false;
     if (inner % 4 != 0) return false;
-    size_col(rp, c.n[0], c.n[1]);
+    size_col(rp, c.n[0], c.n[1], col_il);
     return true;
   }
   if (big_transposed) return false;
@@ -710,7 +717,10 @@ zk_status plan_bwd(zk_op op, zk_epi epi, const zk_desc &da, const zk_desc &db,
                      (!big_write || (al16(pgbig) && al16(paccbig)));
       RedPlan rp;
       const int streams = 1 + (big_op >= 0) + big_write;
-      if (size_fast(c, 3 + sw, big_op, big_tr, true, aligned, streams, &rp)) {
+      // the column kernel's interleaved row walk: the full operand read and
+      // its gradient written, no epilogue, not division
+      const bool col_il = big_op >= 0 && big_write && epi == ZK_EPI_NONE && op != ZK_DIV;
+      if (size_fast(c, 3 + sw, big_op, big_tr, true, aligned, streams, col_il, &rp)) {
         rp.which = sw;
         p->red[p->nred++] = rp;
         p->fused_big = big_write;
@@ -849,7 +859,7 @@ zk_status plan_reduce(const zk_desc &din, int rout, const int64_t *nout,
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;
-  } else if (K < c.numel && size_fast(c, 4, -1, false, src_flat, al16(pin), 1, &rp)) {
+  } else if (K < c.numel && size_fast(c, 4, -1, false, src_flat, al16(pin), 1, false, &rp)) {
     rp.which = 1;
     p->red[p->nred++] = rp;
     p->vec = 4;

@@ -796,6 +796,52 @@ def test_full_size_gpt_residual(orc):
     _check_full_bwd(orc, "add", 1, h["g"], t, h["resid"], host(wl.grad_resid), "grad_resid")
 
 
+def test_interleaved_column_sums_acc_modes(orc):
+    """Long columns whose backward reads the full operand and writes its
+    gradient: 16-wave blocks walk their rows interleaved across the grid, 8
+    a wave.  A ragged row count (not a multiple of the 128 rows a partial
+    covers), both sides, and every acc mode of the written gradient (none,
+    acc == upstream grad, a separate buffer, in place)."""
+    R, K = 32768 + 37, 4096
+    info = zk.plan_describe("bwd", "mul", zk.make_desc((R, K)), zk.make_desc((K,)))
+    assert info["kernel"] == "red_col" and info["partials"] == -(-R // 128), info
+    rng = np.random.default_rng(83)
+    a = rng.standard_normal((R, K)).astype(np.float32)
+    b = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    g = rng.standard_normal((R, K)).astype(np.float32)
+    acc = rng.standard_normal((R, K)).astype(np.float32)
+    ta, tb, tg = dev(a), dev(b), dev(g)
+    rb_ref = None
+    for mode in ("none", "grad", "buffer", "inplace"):
+        say(f"  acc mode {mode}")
+        if mode == "none":
+            ga, gb = zk.binary_bwd("mul", tg, ta, tb)
+            want = orc.bwd("mul", g, a, b)
+        elif mode == "grad":
+            ga, gb = zk.binary_bwd("mul", tg, ta, tb, acc_a=tg)
+            want = orc.bwd("mul", g, a, b, acc_a=g)
+        elif mode == "buffer":
+            ga, gb = zk.binary_bwd("mul", tg, ta, tb, acc_a=dev(acc))
+            want = orc.bwd("mul", g, a, b, acc_a=acc)
+        else:
+            ga = dev(acc)
+            _, gb = zk.binary_bwd("mul", tg, ta, tb, grad_a=ga, acc_a=ga)
+            want = orc.bwd("mul", g, a, b, acc_a=acc)
+        assert_bwd(host(ga), want[0], f"grad_a acc {mode}")
+        assert_bwd(host(gb), want[1], f"grad_b acc {mode}")
+        # the reduced gradient does not depend on the other gradient's acc
+        got_b = host(gb)
+        if rb_ref is None:
+            rb_ref = got_b
+        assert np.array_equal(got_b.view(np.int32), rb_ref.view(np.int32)), mode
+        del ga, gb
+    # the small operand first: b's gradient written in full, a's reduced
+    ga, gb = zk.binary_bwd("mul", tg, tb, ta)
+    want = orc.bwd("mul", g, b, a)
+    assert_bwd(host(ga), want[0], "swapped grad_a")
+    assert_bwd(host(gb), want[1], "swapped grad_b")
+
+
 # One-pass row reductions (2048..16384 terms per kept element): a block per
 # kept element finishes the sum itself.  Term counts at and between the
 # limits of 1, 2 and 4 vectors per lane, ragged last vectors, every op with
