@@ -842,6 +842,26 @@ def test_interleaved_column_sums_acc_modes(orc):
     assert_bwd(host(gb), want[1], "swapped grad_b")
 
 
+def test_interleaved_narrow_columns(orc):
+    """The interleaved walk over folded rows: 32 columns read as rows of 256
+    (8 rows each), 524,296 folded rows over 16-wave blocks (a ragged last
+    band), the multiply backward writing the full gradient, with and without
+    acc == upstream grad."""
+    R, K = 4194304 + 64, 32
+    info = zk.plan_describe("bwd", "mul", zk.make_desc((R, K)), zk.make_desc((K,)))
+    assert info["kernel"] == "red_col" and info["partials"] == 8 * -(-(R // 8) // 1024), info
+    rng = np.random.default_rng(89)
+    a = rng.standard_normal((R, K)).astype(np.float32)
+    b = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    g = rng.standard_normal((R, K)).astype(np.float32)
+    ta, tb, tg = dev(a), dev(b), dev(g)
+    for acc in (None, g):
+        ga, gb = zk.binary_bwd("mul", tg, ta, tb, acc_a=None if acc is None else tg)
+        ra, rb = orc.bwd("mul", g, a, b, acc_a=acc)
+        assert_bwd(host(ga), ra, f"grad_a acc {acc is not None}")
+        assert_bwd(host(gb), rb, f"grad_b acc {acc is not None}")
+
+
 # One-pass row reductions (2048..16384 terms per kept element): a block per
 # kept element finishes the sum itself.  Term counts at and between the
 # limits of 1, 2 and 4 vectors per lane, ragged last vectors, every op with

@@ -41,10 +41,12 @@ def _noalloc(op, epi, g, a, b, ga, gb, acc_a=None, acc_b=None, stream=None):
 
 
 # (op, epi, big shape, small shape, smaller big shape, smaller small shape):
-# column sums (16 and 4 waves a block), GeLU column sums, row sums, the
-# transposed tile, a one-pass gather and a gather with partials
+# column sums (16 and 4 waves a block), the interleaved long-column sum whose
+# 256 partials a column fill the scratch exactly, GeLU column sums, row
+# sums, the transposed tile, a one-pass gather and a gather with partials
 CASES = [
     ("mul", "none", (4096, 4096), (4096,), (1000, 2048), (2048,)),
+    ("mul", "none", (32768, 4096), (4096,), (8192, 4096), (4096,)),
     ("add", "gelu", (4096, 1024), (1024,), (300, 512), (512,)),
     ("mul", "none", (8, 16, 65536), (1, 16, 1), (2, 16, 8192), (1, 16, 1)),
     ("div", "none", (2, 3, 4, 5, 6, 7, 8, 9), (1, 3, 1, 5, 1, 7, 1, 9),
