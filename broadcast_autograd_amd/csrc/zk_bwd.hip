@@ -1753,6 +1753,8 @@ hipError_t launch_bwd(const BwdPlan &p, zk_op op, zk_epi epi, const float *g,
             ra.P = rp.partials;
             ra.ss = R >= 2 ? c.s[1 + sw][R - 2] : 0;
             ra.write_big = p.fused_big;
+            // blockwise partials need four chunks a row (the planner's rule)
+            if (rp.nw == 4 && ra.NC % 4 != 0) return hipErrorInvalidValue;
             unsigned grid = gridn(ra.items, 4);
             return side_acc(sw, amode, [&](auto Sc, auto Ac) -> hipError_t {
               constexpr int S = decltype(Sc)::value, A = decltype(Ac)::value;
