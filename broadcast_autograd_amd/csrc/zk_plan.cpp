@@ -495,11 +495,13 @@ static void size_col(RedPlan *rp, int64_t rows, int64_t cols, bool col_il = fals
     rcw = std::max<int64_t>(1, ceil_div(R0, nw));
   }
   // Long columns whose pass reads the full operand and writes its gradient
-  // with the interleaved column kernel (col_il): short row runs, 8 a wave
-  // and 128 a partial, over many blocks (measured on MI355X, with 64: the
-  // fused [32768, 4096] backward 380-385 -> 366-372 us, [32768, 8192]
-  // 578-600 -> 528 us; the division and GeLU backwards, which walk their
-  // rows in order, gained nothing or lost).
+  // with the interleaved column kernel (col_il): short row runs, 4 a wave
+  // (all in flight at once) and 64 a partial, over many blocks (measured on
+  // MI355X: the fused [32768, 4096] backward 380-385 us with 64 rows a wave,
+  // 366-372 with 8, 338-343 with 4; the [32768, 4096] multiply backward's
+  // two stages 274-277, 266-272, 262-265 us; [65536, 2048] 321, 301, 288;
+  // with 2 rows 300-307 us.  The division and GeLU backwards, which walk
+  // their rows in order, gained nothing or lost with 8).
   if (col_il && fold == 1 && nw == kColWavesMany && colblocks >= 8) rcw = kColRowsIL;
   // Longer row bands while the grid is above the dispatch limit, down to a
   // single band (more than 2^30 columns stay above it).

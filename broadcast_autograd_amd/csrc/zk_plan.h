@@ -35,7 +35,7 @@ constexpr int kColWavesMany = 16;
 // red_row: passes moving at least this many full-size arrays take 512-element chunks
 constexpr int kRowShortChunkStreams = 2;
 // red_col: rows a wave for long columns walked by the interleaved kernel
-constexpr int kColRowsIL = 8;
+constexpr int kColRowsIL = 4;
 // red_rowd: terms per kept element it takes (a 1024-lane block holds up to 4
 // vectors per lane in flight).
 constexpr int64_t kDirMinTerms = 2048;

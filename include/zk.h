@@ -186,7 +186,7 @@ zk_status zk_binary_bwd(zk_op op, zk_epi epi, const float *grad,
  * host threads) race and give wrong sums; serialise them.  Nothing needs
  * clearing between calls: every partial is written before it is read.
  */
-#define ZK_SCRATCH_BYTES ((size_t)8 << 20)
+#define ZK_SCRATCH_BYTES ((size_t)16 << 20)
 zk_status zk_binary_bwd_noalloc(zk_op op, zk_epi epi, const float *grad,
                                 const float *a, const zk_desc *da, const float *b,
                                 const zk_desc *db, float *grad_a, const float *acc_a,

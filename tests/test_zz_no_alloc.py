@@ -23,7 +23,7 @@ if not torch.cuda.is_available():
 from broadcast_autograd_amd import zk  # noqa: E402
 from gpu_util import assert_bwd, dev, host  # noqa: E402
 
-SCRATCH_BYTES = 8 << 20  # ZK_SCRATCH_BYTES in include/zk.h
+SCRATCH_BYTES = 16 << 20  # ZK_SCRATCH_BYTES in include/zk.h
 
 
 def say(*a):
@@ -42,7 +42,7 @@ def _noalloc(op, epi, g, a, b, ga, gb, acc_a=None, acc_b=None, stream=None):
 
 # (op, epi, big shape, small shape, smaller big shape, smaller small shape):
 # column sums (16 and 4 waves a block), the interleaved long-column sum whose
-# 256 partials a column fill the scratch exactly, GeLU column sums, row
+# 512 partials a column fill the scratch exactly, GeLU column sums, row
 # sums, the transposed tile, a one-pass gather and a gather with partials
 CASES = [
     ("mul", "none", (4096, 4096), (4096,), (1000, 2048), (2048,)),
