@@ -487,7 +487,8 @@ def test_determinism(orc):
     assert np.array_equal(r[0].view(np.uint32), r[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("case", ["red_col", "red_col_gelu", "red_rowd"])
+@pytest.mark.parametrize("case", ["red_col", "red_col_interleaved", "red_row_blockwise",
+                                  "red_col_gelu", "red_rowd"])
 def test_determinism_concurrent_streams(orc, case):
     """The partition depends on the shapes only: a backward run alone and two
     copies of it running at once on two streams (other occupancy, other
@@ -495,6 +496,10 @@ def test_determinism_concurrent_streams(orc, case):
     rng = np.random.default_rng(zlib.crc32(case.encode()))
     if case == "red_col":
         op, epi, sa, sb = "mul", "none", (2048, 4096), (4096,)
+    elif case == "red_col_interleaved":
+        op, epi, sa, sb = "mul", "none", (32768, 4096), (4096,)
+    elif case == "red_row_blockwise":
+        op, epi, sa, sb = "mul", "none", (2, 8, 262144), (8, 1)
     elif case == "red_col_gelu":
         op, epi, sa, sb = "add", "gelu", (1024, 1024), (1024,)
     else:
