@@ -296,8 +296,9 @@ constexpr int kBcRows = 2;
 // Only for row vectors of at least this many elements (256 KiB): a short
 // vector stays in each CU's L1 and costs nothing to re-read, and there the
 // paired rows only disturb the stream (measured on MI355X: the 4 MiB mask
-// row, add 174-178 -> 171-172 us; gamma[4096] against h[32768, 4096],
-// 169.8 -> 172.8 us, so that one stays on the row kernel).
+// row, add 174-178 -> 167-168 us; gamma[4096] against h[32768, 4096],
+// 170 -> 171-173 us, so that one stays on the row kernel).  Four rows a
+// lane measured 172.7 us on the mask add.
 constexpr int64_t kBcRowsMinCols = (int64_t)1 << 16;
 struct BcRowsArgs {
   int64_t n1;     // row length (elements)
@@ -318,17 +319,19 @@ __global__ __launch_bounds__(kBlock) void k_fwd_bcrows(const float *big, const f
     else g = (I)(v64 / (int64_t)ba.vpr);
     const I j = ((I)v64 - g * (I)ba.vpr) * 4;
     const I i0 = g * (I)kBcRows * n1 + j;
-    float4 x[kBcRows];
-#pragma unroll
-    for (int k = 0; k < kBcRows; ++k) x[k] = ld4_nt(big + i0 + (I)k * n1);
     const float4 sv = ld4(small + j);
+    // The rows one after another: a row's load follows the previous row's
+    // store (out may alias big as far as the compiler knows), so a lane has
+    // one 16-byte vector of the stream in flight; with both rows' loads
+    // issued first the 4 MiB mask add measured 171-172 us against 167-168.
 #pragma unroll
     for (int k = 0; k < kBcRows; ++k) {
+      const float4 x = ld4_nt(big + i0 + (I)k * n1);
       float4 r;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        el(r, e) = SWAP ? fwd32<OP, EPI>(el(sv, e), el(x[k], e), nullptr)
-                        : fwd32<OP, EPI>(el(x[k], e), el(sv, e), nullptr);
+        el(r, e) = SWAP ? fwd32<OP, EPI>(el(sv, e), el(x, e), nullptr)
+                        : fwd32<OP, EPI>(el(x, e), el(sv, e), nullptr);
       st4_nt(out + i0 + (I)k * n1, r);
     }
   }
@@ -601,26 +604,22 @@ __global__ __launch_bounds__(kBlock) void k_fwd2_bcrows(const float *a, const fl
     else g = (I)(v64 / (int64_t)ba.vpr);
     const I j = ((I)v64 - g * (I)ba.vpr) * 4;
     const I r0 = g * (I)kBcRows;
-    float4 x[kBcRows];
-    float sv[kBcRows];
+    const float4 vv = ld4(vec + j);
+    // the rows one after another, as in k_fwd_bcrows
 #pragma unroll
     for (int k = 0; k < kBcRows; ++k) {
       const I r = r0 + (I)k;
-      x[k] = ld4_nt(a + r * n1 + j);
+      const float4 x = ld4_nt(a + r * n1 + j);
       I q;
       if constexpr (sizeof(I) == 4) q = (I)fdiv(ba.fmid, (uint32_t)r);
       else q = r / (I)ba.nmid;
-      sv[k] = sca[q * (I)ba.rs0 + (r - q * (I)ba.nmid) * (I)ba.rs1];
-    }
-    const float4 vv = ld4(vec + j);
-#pragma unroll
-    for (int k = 0; k < kBcRows; ++k) {
-      float4 r;
+      const float sv = sca[q * (I)ba.rs0 + (r - q * (I)ba.nmid) * (I)ba.rs1];
+      float4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        el(r, e) = VB ? op32<OP2>(op32<OP1>(el(x[k], e), el(vv, e)), sv[k])
-                      : op32<OP2>(op32<OP1>(el(x[k], e), sv[k]), el(vv, e));
-      st4_nt(out + (r0 + (I)k) * n1 + j, r);
+        el(o, e) = VB ? op32<OP2>(op32<OP1>(el(x, e), el(vv, e)), sv)
+                      : op32<OP2>(op32<OP1>(el(x, e), sv), el(vv, e));
+      st4_nt(out + r * n1 + j, o);
     }
   }
 }
