@@ -27,7 +27,10 @@
 namespace zk {
 
 constexpr int kNormBlk = 256;
-constexpr int kNormU = 8;  // 128-bit loads in flight per lane
+// 128-bit loads in flight per lane (also in the in-place scaling, where
+// issuing them 1, 2 or 4 at a time measured 24.4, 21.0 and 20.9 us against
+// 20.7 us on the GPT gradient set)
+constexpr int kNormU = 8;
 constexpr int64_t kNormChunk = (int64_t)kNormBlk * 4 * kNormU;
 constexpr int64_t kNormMaxGrid = (int64_t)1 << 22;
 
