@@ -465,6 +465,35 @@ def test_reduce_plans(L):
             assert info["partials"] == 0
 
 
+# (op, epi, full shape, reduced shape, kernel, partials a kept element):
+# a backward that reads the full operand and writes its gradient walks long
+# columns interleaved, 4 rows a wave (64 a partial), and takes 512-element row
+# chunks four to a partial; a plain sum, division, GeLU and folded narrow
+# columns keep the longer runs.
+STREAM_PLANS = [
+    ("mul", "none", (32768, 4096), (4096,), "red_col", 512),
+    ("div", "none", (32768, 4096), (4096,), "red_col", 32),
+    ("add", "gelu", (32768, 4096), (4096,), "red_col", 32),
+    ("mul", "none", (4194304, 32), (32,), "red_col", 4096),
+    ("mul", "none", (2, 8, 262144), (8, 1), "red_row", 256),
+    ("add", "none", (2, 8, 262144), (8, 1), "red_row", 256),
+    ("mul", "none", (7, 3, 2600), (3, 1), "red_row", 77),
+]
+
+
+@pytest.mark.parametrize("op,epi,sa,sb,kernel,partials", STREAM_PLANS)
+def test_stream_count_plans(L, op, epi, sa, sb, kernel, partials):
+    info = zk.plan_describe("bwd", op, zk.make_desc(sa), zk.make_desc(sb), epi=epi)
+    assert (info["kernel"], info["partials"]) == (kernel, partials), info
+    # the same shapes summed alone (one stream) keep the longer runs
+    red = zk.plan_describe("reduce", "add", zk.make_desc(sa), zk.make_desc(sb))
+    assert red["kernel"] == kernel
+    if (op, epi) == ("mul", "none") and len(sa) == 2 and sa[1] >= 2048:
+        assert red["partials"] == 32
+    if kernel == "red_row" and sa[-1] == 262144:
+        assert red["partials"] == 1024
+
+
 def test_index64_threshold(L):
     info = zk.plan_describe("fwd", "add", zk.make_desc((1 << 31,)), zk.make_desc((1,)))
     assert info["index64"]
