@@ -242,7 +242,8 @@ int main() {
         }
         case K_RED_TILE: {
           if (c.rank != 2 || c.n[1] % 4 != 0) return fail("tile shape", c.rank, c.n[1]);
-          if (rp.partials != (c.n[0] + 63) / 64) return fail("tile partials", rp.partials, 0);
+          if (rp.chunk != 64 && rp.chunk != 128) return fail("tile rows", rp.chunk, 0);
+          if (rp.partials != (c.n[0] + rp.chunk - 1) / rp.chunk) return fail("tile partials", rp.partials, 0);
           break;
         }
         case K_RED_GENERIC: {

@@ -621,8 +621,8 @@ def test_noalloc_refusals_without_a_device(L):
         pytest.skip("a GPU is present")
     m = ctypes.c_void_p(1 << 20)  # non-NULL markers, never dereferenced here
     P = lambda k: ctypes.c_void_p(m.value + (k << 36))  # noqa: E731 (disjoint extents)
-    # a transposed [65536, 4096] times [4096]: 1024 partials a column, 32 MiB
-    da = zk.make_desc((65536, 4096), (1, 65536))
+    # a transposed [131072, 4096] times [4096]: 1024 partials a column, 32 MiB
+    da = zk.make_desc((131072, 4096), (1, 131072))
     db = zk.make_desc((4096,))
     rc = L.zk_binary_bwd_noalloc(9, 0, P(0), P(1), ctypes.byref(da), P(2), ctypes.byref(db),
                                  P(3), None, P(4), None, None)

@@ -126,15 +126,15 @@ def test_noalloc_side_stream():
 
 
 def test_noalloc_refuses_more_than_the_scratch():
-    """A transposed operand of 65536 x 4096 leaves 1024 partials a column,
+    """A transposed operand of 131072 x 4096 leaves 1024 partials a column,
     32 MiB: refused with ZK_ERR_WORKSPACE before anything is launched (the
     outputs keep their fill)."""
-    st = torch.empty(4096 * 65536, device="cuda")
-    a = torch.as_strided(st, (65536, 4096), (1, 65536))
+    st = torch.empty(4096 * 131072, device="cuda")
+    a = torch.as_strided(st, (131072, 4096), (1, 131072))
     b = torch.empty(4096, device="cuda")
-    g = torch.empty(65536, 4096, device="cuda")
+    g = torch.empty(131072, 4096, device="cuda")
     assert zk.bwd_workspace_bytes("mul", a, b) > SCRATCH_BYTES
-    ga = torch.full((65536, 4096), 7.0, device="cuda")
+    ga = torch.full((131072, 4096), 7.0, device="cuda")
     gb = torch.full((4096,), 7.0, device="cuda")
     assert _noalloc("mul", "none", g, a, b, ga, gb) == zk.ERR["ZK_ERR_WORKSPACE"]
     torch.cuda.synchronize()
